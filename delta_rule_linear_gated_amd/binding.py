@@ -1,0 +1,224 @@
+"""ctypes binding of ``libdn.so`` (declared in ``include/dn.h``).
+
+Argument marshalling only: every step of the operator runs in the HIP kernels
+behind the C ABI.  PyTorch supplies device memory and the stream.  When the
+library is not built this module raises -- there is no fallback path.
+
+Low level (same names as the C ABI): ``dn_states_bytes``, ``dn_workspace_bytes``,
+``dn_workspace_layout``, ``dn_chunk_fwd``, ``dn_chunk_bwd``, ``dn_status_string``,
+``dn_last_error``.  Convenience: ``chunk_fwd`` / ``chunk_bwd`` allocate outputs
+and workspace with torch and call the above; ``DeltaRule`` is a
+``torch.autograd.Function`` over them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdn.so")
+
+DN_OK, DN_ERR_INVALID, DN_ERR_SHAPE, DN_ERR_DTYPE, DN_ERR_WORKSPACE, DN_ERR_UNSUPPORTED, DN_ERR_HIP = (
+    0, -1, -2, -3, -4, -5, -6)
+DN_F32, DN_BF16 = 0, 1
+DN_GATE_NONE, DN_GATE_SCALAR, DN_GATE_VECTOR = 0, 1, 2
+DN_PASS_FWD, DN_PASS_BWD, DN_PASS_BWD_RECOMPUTE = 0, 1, 2
+
+EXPORTS = ("dn_states_bytes", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
+           "dn_chunk_bwd", "dn_status_string", "dn_last_error")
+
+
+class DnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("gate", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Open libdn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m delta_rule_linear_gated_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    sp = ctypes.POINTER(Shape)
+    L.dn_states_bytes.argtypes = [sp]
+    L.dn_states_bytes.restype = sz
+    L.dn_workspace_bytes.argtypes = [sp, i32]
+    L.dn_workspace_bytes.restype = sz
+    L.dn_workspace_layout.argtypes = [sp, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.dn_workspace_layout.restype = i32
+    L.dn_chunk_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dn_chunk_fwd.restype = i32
+    L.dn_chunk_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dn_chunk_bwd.restype = i32
+    L.dn_status_string.argtypes = [i32]
+    L.dn_status_string.restype = ctypes.c_char_p
+    L.dn_last_error.argtypes = []
+    L.dn_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _check(status: int):
+    if status != DN_OK:
+        L = lib()
+        raise DnError(status, f"{L.dn_status_string(status).decode()}: {L.dn_last_error().decode()}")
+
+
+def make_shape(B, H, T, dk, dv, C, dtype, gate) -> Shape:
+    dt = {torch.float32: DN_F32, torch.bfloat16: DN_BF16, "fp32": DN_F32, "bf16": DN_BF16}.get(dtype, dtype)
+    gt = {None: DN_GATE_NONE, "none": DN_GATE_NONE, "scalar": DN_GATE_SCALAR,
+          "vector": DN_GATE_VECTOR}.get(gate, gate)
+    return Shape(int(B), int(H), int(T), int(dk), int(dv), int(C), int(dt), int(gt))
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+# ------------------------------------------------------------------ C-ABI mirrors
+
+
+def dn_states_bytes(shape: Shape) -> int:
+    return lib().dn_states_bytes(ctypes.byref(shape))
+
+
+def dn_workspace_bytes(shape: Shape, pass_: int) -> int:
+    return lib().dn_workspace_bytes(ctypes.byref(shape), int(pass_))
+
+
+def dn_workspace_layout(shape: Shape, pass_: int):
+    out = (ctypes.c_size_t * 7)()
+    _check(lib().dn_workspace_layout(ctypes.byref(shape), int(pass_), out))
+    return dict(zip(("gam", "T", "P", "lam", "dS1", "states", "total"), list(out)))
+
+
+def dn_status_string(status: int) -> str:
+    return lib().dn_status_string(int(status)).decode()
+
+
+def dn_last_error() -> str:
+    return lib().dn_last_error().decode()
+
+
+def dn_chunk_fwd(shape, q, k, v, beta, g, h0, o, hT, states, ws, ws_bytes, stream=None) -> int:
+    """Raw call; returns the dn_status (no exception)."""
+    return lib().dn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                              _ptr(h0), _ptr(o), _ptr(hT), _ptr(states), _ptr(ws), int(ws_bytes),
+                              _stream(stream))
+
+
+def dn_chunk_bwd(shape, q, k, v, beta, g, h0, dout, dhT, states, dq, dk, dv, dbeta, dg, dh0, ws,
+                 ws_bytes, stream=None) -> int:
+    """Raw call; returns the dn_status (no exception)."""
+    return lib().dn_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                              _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(states), _ptr(dq), _ptr(dk),
+                              _ptr(dv), _ptr(dbeta), _ptr(dg), _ptr(dh0), _ptr(ws), int(ws_bytes),
+                              _stream(stream))
+
+
+# ------------------------------------------------------------------ convenience
+
+
+def _gate_kind(g, dk):
+    if g is None:
+        return DN_GATE_NONE
+    return DN_GATE_VECTOR if g.dim() == 4 else DN_GATE_SCALAR
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def shape_of(q, v, g, C) -> Shape:
+    B, H, T, dk = q.shape
+    return make_shape(B, H, T, dk, v.shape[-1], C, q.dtype, _gate_kind(g, dk))
+
+
+def workspace(shape: Shape, pass_: int, device) -> torch.Tensor:
+    n = dn_workspace_bytes(shape, pass_)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def chunk_fwd(q, k, v, beta, g=None, h0=None, C=64, save_states=True, want_hT=True, ws=None,
+              stream=None):
+    """Returns (o, hT or None, states or None)."""
+    _contig(q, k, v, beta, g, h0)
+    sh = shape_of(q, v, g, C)
+    o = torch.empty_like(v)
+    hT = torch.empty(q.shape[0], q.shape[1], v.shape[-1], q.shape[-1], dtype=torch.float32,
+                     device=q.device) if want_hT else None
+    states = None
+    if save_states:
+        nt = (q.shape[2] + C - 1) // C
+        states = torch.empty(q.shape[0], q.shape[1], nt, v.shape[-1], q.shape[-1], dtype=q.dtype,
+                             device=q.device)
+    if ws is None:
+        ws = workspace(sh, DN_PASS_FWD, q.device)
+    _check(dn_chunk_fwd(sh, q, k, v, beta, g, h0, o, hT, states, ws, ws.numel(), stream))
+    return o, hT, states
+
+
+def chunk_bwd(q, k, v, beta, g, h0, do, dhT=None, states=None, C=64, want_dh0=True, ws=None,
+              stream=None):
+    """Returns dict dq, dk, dv, dbeta, dg (None without a gate), dh0 (or None)."""
+    _contig(q, k, v, beta, g, h0, do, dhT, states)
+    sh = shape_of(q, v, g, C)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dbeta = torch.empty_like(beta)
+    dg = None if g is None else torch.empty_like(g)
+    dh0 = torch.empty(q.shape[0], q.shape[1], v.shape[-1], q.shape[-1], dtype=torch.float32,
+                      device=q.device) if want_dh0 else None
+    if ws is None:
+        ws = workspace(sh, DN_PASS_BWD if states is not None else DN_PASS_BWD_RECOMPUTE, q.device)
+    _check(dn_chunk_bwd(sh, q, k, v, beta, g, h0, do, dhT, states, dq, dk, dv, dbeta, dg, dh0, ws,
+                        ws.numel(), stream))
+    return {"dq": dq, "dk": dk, "dv": dv, "dbeta": dbeta, "dg": dg, "dh0": dh0}
+
+
+class DeltaRule(torch.autograd.Function):
+    """o, hT = DeltaRule.apply(q, k, v, beta, g, h0, C, recompute)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, beta, g, h0, C=64, recompute=False):
+        o, hT, states = chunk_fwd(q, k, v, beta, g, h0, C=C, save_states=not recompute)
+        ctx.C = C
+        ctx.save_for_backward(q, k, v, beta, g, h0, states)
+        return o, hT
+
+    @staticmethod
+    def backward(ctx, do, dhT):
+        q, k, v, beta, g, h0, states = ctx.saved_tensors
+        gr = chunk_bwd(q, k, v, beta, g, h0, do.contiguous(),
+                       None if dhT is None else dhT.contiguous(), states, C=ctx.C)
+        return gr["dq"], gr["dk"], gr["dv"], gr["dbeta"], gr["dg"], (gr["dh0"] if h0 is not None else None), None, None

@@ -1,0 +1,288 @@
+// dn_api.cpp -- the C ABI (include/dn.h): host-side validation, workspace
+// carving and dispatch to the kernel launchers.  Pure host code: every check
+// runs before the first HIP call, so a bad call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <utility>
+#include <vector>
+
+#include "../../include/dn.h"
+#include "dn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dn_status fail(dn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+struct Dims {
+    size_t BH, T, NT, dk, dv, E, gw;
+};
+
+dn_status check_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
+    if (!s) return fail(DN_ERR_INVALID, "shape is NULL");
+    if (s->B < 0 || s->H < 0 || s->T < 0) return fail(DN_ERR_SHAPE, "B, H, T must be >= 0");
+    if (s->dk <= 0 || s->dv <= 0) return fail(DN_ERR_SHAPE, "dk and dv must be > 0");
+    if (s->C <= 0) return fail(DN_ERR_SHAPE, "chunk size C must be > 0");
+    if (s->dtype != DN_F32 && s->dtype != DN_BF16) return fail(DN_ERR_DTYPE, "unknown dtype %d", s->dtype);
+    if (s->gate < DN_GATE_NONE || s->gate > DN_GATE_VECTOR) return fail(DN_ERR_INVALID, "unknown gate %d", s->gate);
+    if ((long long)s->B * s->H > 65535) return fail(DN_ERR_UNSUPPORTED, "B*H must be <= 65535");
+    if (s->C != 16 && s->C != 32 && s->C != 64) return fail(DN_ERR_UNSUPPORTED, "C must be 16, 32 or 64");
+    if (s->dk != s->dv) return fail(DN_ERR_UNSUPPORTED, "dk must equal dv");
+    if (s->dk != 16 && s->dk != 32 && s->dk != 64 && s->dk != 128)
+        return fail(DN_ERR_UNSUPPORTED, "dk must be 16, 32, 64 or 128");
+    pr->B = s->B;
+    pr->H = s->H;
+    pr->T = s->T;
+    pr->dk = s->dk;
+    pr->dv = s->dv;
+    pr->C = s->C;
+    pr->bf16 = s->dtype == DN_BF16;
+    pr->gate = s->gate;
+    pr->BV = 0;
+    if (!dn::supported(*pr))
+        return fail(DN_ERR_UNSUPPORTED, "no kernel for dtype=%s gate=%d C=%d d=%d (LDS budget)",
+                    pr->bf16 ? "bf16" : "fp32", s->gate, s->C, s->dk);
+    pr->BV = dn::pick_bv(*pr);
+    d->BH = (size_t)s->B * s->H;
+    d->T = (size_t)s->T;
+    d->NT = s->T > 0 ? ((size_t)s->T + s->C - 1) / s->C : 0;
+    d->dk = (size_t)s->dk;
+    d->dv = (size_t)s->dv;
+    d->E = pr->bf16 ? 2 : 4;
+    d->gw = s->gate == DN_GATE_VECTOR ? (size_t)s->dk : 1;
+    return DN_OK;
+}
+
+struct Buf {
+    const char* name;
+    const void* p;
+    size_t bytes;
+    bool output;
+};
+
+// Required pointers must be non-NULL when non-empty; all must be 16-byte
+// aligned; outputs may not overlap anything else.
+dn_status check_buffers(const std::vector<Buf>& bufs) {
+    for (const Buf& b : bufs) {
+        if (b.bytes == 0 || !b.p) continue;
+        if (reinterpret_cast<uintptr_t>(b.p) % 16 != 0)
+            return fail(DN_ERR_INVALID, "%s is not 16-byte aligned", b.name);
+    }
+    for (size_t i = 0; i < bufs.size(); ++i) {
+        const Buf& a = bufs[i];
+        if (!a.p || a.bytes == 0) continue;
+        for (size_t j = i + 1; j < bufs.size(); ++j) {
+            const Buf& b = bufs[j];
+            if (!b.p || b.bytes == 0 || (!a.output && !b.output)) continue;
+            const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), a1 = a0 + a.bytes;
+            const uintptr_t b0 = reinterpret_cast<uintptr_t>(b.p), b1 = b0 + b.bytes;
+            if (a0 < b1 && b0 < a1) return fail(DN_ERR_INVALID, "%s overlaps %s", a.name, b.name);
+        }
+    }
+    return DN_OK;
+}
+
+dn_status need(const void* p, size_t bytes, const char* name) {
+    if (bytes > 0 && !p) return fail(DN_ERR_INVALID, "%s is NULL", name);
+    return DN_OK;
+}
+
+#define DN_TRY(expr)                      \
+    do {                                  \
+        const dn_status st_ = (expr);     \
+        if (st_ != DN_OK) return st_;     \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t dn_states_bytes(const dn_shape* shape) {
+    dn::Problem pr;
+    Dims d;
+    if (check_shape(shape, &pr, &d) != DN_OK) return 0;
+    return d.BH * d.NT * d.dv * d.dk * d.E;
+}
+
+size_t dn_workspace_bytes(const dn_shape* shape, int pass) {
+    dn::Problem pr;
+    Dims d;
+    if (pass < DN_PASS_FWD || pass > DN_PASS_BWD_RECOMPUTE) return 0;
+    if (check_shape(shape, &pr, &d) != DN_OK) return 0;
+    return dn::ws_layout(pr, pass != DN_PASS_FWD, pass == DN_PASS_BWD_RECOMPUTE).total;
+}
+
+dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[7]) {
+    dn::Problem pr;
+    Dims d;
+    if (!offsets) return fail(DN_ERR_INVALID, "offsets is NULL");
+    if (pass < DN_PASS_FWD || pass > DN_PASS_BWD_RECOMPUTE) return fail(DN_ERR_INVALID, "unknown pass %d", pass);
+    DN_TRY(check_shape(shape, &pr, &d));
+    const dn::WsLayout w = dn::ws_layout(pr, pass != DN_PASS_FWD, pass == DN_PASS_BWD_RECOMPUTE);
+    offsets[0] = w.gam;
+    offsets[1] = w.Tm;
+    offsets[2] = w.Pm;
+    offsets[3] = w.lam;
+    offsets[4] = w.dS1;
+    offsets[5] = w.states;
+    offsets[6] = w.total;
+    return DN_OK;
+}
+
+dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
+                       const float* beta, const float* g, const float* h0, void* o, float* hT,
+                       void* states, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = '\0';
+    dn::Problem pr;
+    Dims d;
+    DN_TRY(check_shape(shape, &pr, &d));
+    const size_t nk = d.BH * d.T * d.dk * d.E, nv = d.BH * d.T * d.dv * d.E;
+    const size_t nb = d.BH * d.T * 4, ng = pr.gate == DN_GATE_NONE ? 0 : d.BH * d.T * d.gw * 4;
+    const size_t ns = d.BH * d.dv * d.dk * 4, nst = d.BH * d.NT * d.dv * d.dk * d.E;
+    if (pr.gate == DN_GATE_NONE && g) return fail(DN_ERR_INVALID, "g must be NULL without a gate");
+    DN_TRY(need(q, nk, "q"));
+    DN_TRY(need(k, nk, "k"));
+    DN_TRY(need(v, nv, "v"));
+    DN_TRY(need(beta, nb, "beta"));
+    DN_TRY(need(g, ng, "g"));
+    DN_TRY(need(o, nv, "o"));
+    const dn::WsLayout w = dn::ws_layout(pr, false, false);
+    if (ws_bytes < w.total) return fail(DN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+    DN_TRY(need(ws, w.total, "workspace"));
+    DN_TRY(check_buffers({{"q", q, nk, false},
+                          {"k", k, nk, false},
+                          {"v", v, nv, false},
+                          {"beta", beta, nb, false},
+                          {"g", g, ng, false},
+                          {"h0", h0, ns, false},
+                          {"o", o, nv, true},
+                          {"hT", hT, ns, true},
+                          {"states", states, nst, true},
+                          {"workspace", ws, w.total, true}}));
+    dn::Params p{};
+    p.BH = (int)d.BH;
+    p.T = (int)d.T;
+    p.NT = (int)d.NT;
+    p.DKr = (int)d.dk;
+    p.DVr = (int)d.dv;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.beta = beta;
+    p.g = g;
+    p.h0 = h0;
+    p.o = o;
+    p.hT = hT;
+    p.states = states;
+    char* wb = static_cast<char*>(ws);
+    p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(wb + w.gam);
+    p.Tm = wb + w.Tm;
+    p.Pm = wb + w.Pm;
+    const hipError_t e = dn::launch_forward(pr, p, states != nullptr, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return DN_OK;
+}
+
+dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, const void* v,
+                       const float* beta, const float* g, const float* h0, const void* dout,
+                       const float* dhT, const void* states, void* dq, void* dk, void* dv,
+                       float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes,
+                       void* stream) {
+    g_err[0] = '\0';
+    dn::Problem pr;
+    Dims d;
+    DN_TRY(check_shape(shape, &pr, &d));
+    const size_t nk = d.BH * d.T * d.dk * d.E, nv = d.BH * d.T * d.dv * d.E;
+    const size_t nb = d.BH * d.T * 4, ng = pr.gate == DN_GATE_NONE ? 0 : d.BH * d.T * d.gw * 4;
+    const size_t ns = d.BH * d.dv * d.dk * 4, nst = d.BH * d.NT * d.dv * d.dk * d.E;
+    if (pr.gate == DN_GATE_NONE && (g || dg)) return fail(DN_ERR_INVALID, "g and dg must be NULL without a gate");
+    DN_TRY(need(q, nk, "q"));
+    DN_TRY(need(k, nk, "k"));
+    DN_TRY(need(v, nv, "v"));
+    DN_TRY(need(beta, nb, "beta"));
+    DN_TRY(need(g, ng, "g"));
+    DN_TRY(need(dout, nv, "dout"));
+    DN_TRY(need(dq, nk, "dq"));
+    DN_TRY(need(dk, nk, "dk"));
+    DN_TRY(need(dv, nv, "dv"));
+    DN_TRY(need(dbeta, nb, "dbeta"));
+    DN_TRY(need(dg, ng, "dg"));
+    const bool have_states = states != nullptr;
+    const dn::WsLayout w = dn::ws_layout(pr, true, !have_states);
+    if (ws_bytes < w.total) return fail(DN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
+    DN_TRY(need(ws, w.total, "workspace"));
+    DN_TRY(check_buffers({{"q", q, nk, false},
+                          {"k", k, nk, false},
+                          {"v", v, nv, false},
+                          {"beta", beta, nb, false},
+                          {"g", g, ng, false},
+                          {"h0", h0, ns, false},
+                          {"dout", dout, nv, false},
+                          {"dhT", dhT, ns, false},
+                          {"states", states, nst, false},
+                          {"dq", dq, nk, true},
+                          {"dk", dk, nk, true},
+                          {"dv", dv, nv, true},
+                          {"dbeta", dbeta, nb, true},
+                          {"dg", dg, ng, true},
+                          {"dh0", dh0, ns, true},
+                          {"workspace", ws, w.total, true}}));
+    dn::Params p{};
+    p.BH = (int)d.BH;
+    p.T = (int)d.T;
+    p.NT = (int)d.NT;
+    p.DKr = (int)d.dk;
+    p.DVr = (int)d.dv;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.dout = dout;
+    p.beta = beta;
+    p.g = g;
+    p.h0 = h0;
+    p.dhT = dhT;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dbeta = dbeta;
+    p.dg = dg;
+    p.dh0 = dh0;
+    char* wb = static_cast<char*>(ws);
+    p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(wb + w.gam);
+    p.Tm = wb + w.Tm;
+    p.Pm = wb + w.Pm;
+    p.lam = wb + w.lam;
+    p.dS1 = wb + w.dS1;
+    p.states = have_states ? const_cast<void*>(states) : static_cast<void*>(wb + w.states);
+    const hipError_t e = dn::launch_backward(pr, p, have_states, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return DN_OK;
+}
+
+const char* dn_status_string(dn_status status) {
+    switch (status) {
+        case DN_OK: return "ok";
+        case DN_ERR_INVALID: return "invalid argument";
+        case DN_ERR_SHAPE: return "invalid shape";
+        case DN_ERR_DTYPE: return "invalid dtype";
+        case DN_ERR_WORKSPACE: return "workspace too small";
+        case DN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case DN_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* dn_last_error(void) { return g_err; }
+
+}  // extern "C"

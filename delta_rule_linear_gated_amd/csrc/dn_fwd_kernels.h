@@ -1,0 +1,346 @@
+// dn_fwd_kernels.h -- forward-pass kernels of the chunkwise gated delta rule.
+//
+// Per head the state S (d_v x d_k) evolves as
+//     S_t = S_{t-1} Diag(e^{g_t}) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t
+// (ReWY abstract: DeltaNet / GDN / KDA; SFDA summary "Kernarchitektur",
+// transposed, zero phase).  The sequence is cut into chunks of C steps.  Inside
+// a chunk, with gam the in-chunk cumulative log-decay, Gam = e^gam and S0 the
+// state entering the chunk (SFDA summary, "Der konstruktive Chunk-WY-Theorem":
+// the chunk's transition product is the decay product minus a rank <= C
+// correction with a triangular core; "Zentrale Beitraege": exact affine chunk
+// transfer):
+//     A   = strictly-lower( diag(beta) (K Gam)(K / Gam)^T )     pairwise decays e^{gam_t - gam_s}
+//     P   = lower( (Q Gam)(K / Gam)^T )
+//     T   = (I + A)^{-1}                                         (forward substitution)
+//     U   = T diag(beta) (V - (K Gam) S0^T)                      the chunk's corrected writes
+//     O   = (Q Gam) S0^T + P U
+//     S1  = S0 Diag(Gam_C) + U^T (K Gam_C / Gam)
+// prep_kernel builds gam, T and P for every chunk in parallel; fwd_state_kernel
+// walks the chunks of one head (one d_v block of it) in order, keeping S in
+// MFMA accumulators, and writes O as it goes.
+//
+// Gates: kGateNone (DeltaNet), kGateScalar (GDN: pairwise decays applied as
+// e^{gam_t - gam_s} on the C x C scores, never above 1 for g <= 0), kGateVector
+// (KDA: per-channel decays, factored through a per-chunk centre gam_C / 2 so
+// that K e^{gam - centre} and K e^{centre - gam} stay within e^{+-|gam_C|/2} --
+// the centred contraction of the ReWY abstract).
+#pragma once
+
+#include "dn_device.h"
+#include "dn_internal.h"
+
+namespace dn {
+
+template <int GATE, int DK> struct GateLayout {
+    static constexpr int GW = GATE == kGateVector ? DK : 1;  // gam values per step
+};
+
+// Loads the chunk's cumulative log-decay into gam_s (rows >= valid repeat the
+// last valid row) and beta into beta_s (0 for rows >= valid).
+template <int GATE, int C, int DK>
+__device__ __forceinline__ void load_gam_beta(float* gam_s, float* beta_s, const float* __restrict__ gam_ws,
+                                              const float* __restrict__ beta, int valid) {
+    constexpr int GW = GateLayout<GATE, DK>::GW;
+    for (int t = threadIdx.x; t < C; t += kThreads) beta_s[t] = t < valid ? beta[t] : 0.f;
+    if (GATE == kGateNone) return;
+    for (int idx = threadIdx.x; idx < C * GW; idx += kThreads) {
+        const int t = idx / GW, c = idx % GW;
+        const int tt = t < valid ? t : valid - 1;
+        gam_s[idx] = gam_ws[tt * GW + c];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prep_kernel: grid (NT, BH), one chunk per workgroup.
+template <typename TI, int GATE, int C, int DK>
+__global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
+    constexpr int LDK = DK + Pad<TI>::value;
+    constexpr int LDA = C + 4;
+    constexpr int GW = GateLayout<GATE, DK>::GW;
+    constexpr bool VEC = GATE == kGateVector;
+    __shared__ float gam_s[C * GW];
+    __shared__ float beta_s[C];
+    __shared__ __align__(16) TI Kp[C * LDK];               // K, or K e^{gam - centre}
+    __shared__ __align__(16) TI Km[VEC ? C * LDK : 16];    // K e^{centre - gam} (vector gate)
+    __shared__ __align__(16) TI Qp[C * LDK];               // Q, or Q e^{gam - centre}
+    __shared__ __align__(16) float A_s[C * LDA];
+
+    const int n = blockIdx.x, bh = blockIdx.y;
+    const int t0 = n * C;
+    const int valid = min(C, p.T - t0);
+    const long row0 = (long)bh * p.T + t0;
+    const TI* __restrict__ q = static_cast<const TI*>(p.q) + row0 * DK;
+    const TI* __restrict__ k = static_cast<const TI*>(p.k) + row0 * DK;
+    const float* __restrict__ beta = p.beta + row0;
+
+    // -- cumulative log-decay within the chunk
+    if (GATE == kGateScalar) {
+        if (wave_id() == 0) {
+            const int t = lane_id();
+            float x = (t < valid) ? p.g[row0 + t] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (t >= off) x += y;
+            }
+            if (t < C) {
+                gam_s[t] = x;
+                if (t < valid) p.gam[row0 + t] = x;
+            }
+        }
+    } else if (GATE == kGateVector) {
+        for (int c = threadIdx.x; c < DK; c += kThreads) {
+            float acc = 0.f;
+            for (int t = 0; t < C; ++t) {
+                if (t < valid) acc += p.g[(row0 + t) * DK + c];
+                gam_s[t * DK + c] = acc;
+                if (t < valid) p.gam[(row0 + t) * DK + c] = acc;
+            }
+        }
+    }
+    for (int t = threadIdx.x; t < C; t += kThreads) beta_s[t] = t < valid ? beta[t] : 0.f;
+    __syncthreads();
+
+    // -- stage K and Q (centred per-channel factors for the vector gate)
+    if (VEC) {
+        const float* gl = gam_s + (valid - 1) * DK;  // gam_C
+        stage<TI, C, DK, false>(Kp, LDK, k, DK, valid, [&](int r, int c, float x) {
+            return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]);
+        });
+        stage<TI, C, DK, false>(Km, LDK, k, DK, valid, [&](int r, int c, float x) {
+            return x * fexp(0.5f * gl[c] - gam_s[r * DK + c]);
+        });
+        stage<TI, C, DK, false>(Qp, LDK, q, DK, valid, [&](int r, int c, float x) {
+            return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]);
+        });
+    } else {
+        stage_copy<TI, C, DK, false>(Kp, LDK, k, DK, valid);
+        stage_copy<TI, C, DK, false>(Qp, LDK, q, DK, valid);
+    }
+    __syncthreads();
+
+    // -- gated Gram matrices: A (strict lower, scaled by beta_t) and P (lower)
+    const TI* KmP = VEC ? Km : Kp;
+    TI* __restrict__ Pout = static_cast<TI*>(p.Pm) + ((long)bh * p.NT + n) * C * C;
+    {
+        using TL = Tiles<C, C>;
+        f32x4 acc[TL::PER];
+#pragma unroll
+        for (int j = 0; j < TL::PER; ++j) {
+            if (!TL::valid(j)) continue;
+            const bool upper = TL::n0(j) > TL::m0(j);
+            acc[j] = zero4();
+            if (!upper) acc[j] = tile_nt<TI, DK>(Kp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, acc[j]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = TL::row(j, i), s = TL::col(j);
+                float a = 0.f;
+                if (s < t) {
+                    a = beta_s[t] * acc[j][i];
+                    if (GATE == kGateScalar) a *= fexp(gam_s[t] - gam_s[s]);
+                }
+                A_s[t * LDA + s] = a;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TL::PER; ++j) {
+            if (!TL::valid(j)) continue;
+            const bool upper = TL::n0(j) > TL::m0(j);
+            acc[j] = zero4();
+            if (!upper) acc[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, acc[j]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = TL::row(j, i), s = TL::col(j);
+                float pv = 0.f;
+                if (s <= t) {
+                    pv = acc[j][i];
+                    if (GATE == kGateScalar) pv *= fexp(gam_s[t] - gam_s[s]);
+                }
+                Pout[t * C + s] = from_f<TI>(pv);
+            }
+        }
+    }
+    __syncthreads();
+
+    // -- T = (I + A)^{-1}: column c of T solves (I + A) x = e_c by forward
+    //    substitution; lane c of wave 0 owns column c, A rows are LDS broadcasts.
+    if (wave_id() == 0) {
+        const int c = lane_id();
+        float x[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            float acc = (i == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < i; ++j) acc -= A_s[i * LDA + j] * x[j];
+            x[i] = acc;
+        }
+        if (c < C) {
+            TI* __restrict__ Tout = static_cast<TI*>(p.Tm) + ((long)bh * p.NT + n) * C * C;
+#pragma unroll
+            for (int i = 0; i < C; ++i) Tout[i * C + c] = from_f<TI>(x[i]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fwd_state_kernel: grid (DV / BV, BH).  Walks the chunks of one head in order
+// for one block of BV state rows (rows of S are independent: each row only
+// mixes with itself through the key dimension).
+//   SAVE    : write the bf16/fp32 state entering each chunk to p.states
+//   OUTPUT  : write O and hT (off for the recompute pass of the backward)
+template <typename TI, int GATE, int C, int DK, int BV, bool SAVE, bool OUTPUT>
+__global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
+    constexpr int PAD = Pad<TI>::value;
+    constexpr int LDK = DK + PAD;
+    constexpr int LDC = C + PAD;
+    constexpr int LDV = BV + PAD;
+    constexpr int GW = GateLayout<GATE, DK>::GW;
+    constexpr int DV = 0;  // (unused; the runtime d_v is p.DVr)
+    (void)DV;
+    __shared__ float gam_s[C * GW];
+    __shared__ float beta_s[C];
+    __shared__ __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
+    __shared__ __align__(16) TI Qg[C * LDK];     // Q Gam            [t][c]
+    __shared__ __align__(16) TI Kg[C * LDK];     // K Gam            [t][c]
+    __shared__ __align__(16) TI KdT[DK * LDC];   // (K Gam_C / Gam)^T [c][t]
+    __shared__ __align__(16) TI Vb[C * LDV];     // V block          [t][v]
+    __shared__ __align__(16) TI Tl[C * LDC];     // T                [t][s]
+    __shared__ __align__(16) TI Pl[C * LDC];     // P                [t][s]
+    __shared__ __align__(16) TI RT[BV * LDC];    // R^T              [v][t]
+    __shared__ __align__(16) TI UT[BV * LDC];    // U^T              [v][t]
+
+    const int DVr = p.DVr;
+    const int bh = blockIdx.y;
+    const int v0 = blockIdx.x * BV;
+    using TS = Tiles<BV, DK>;
+    f32x4 S[TS::PER];
+#pragma unroll
+    for (int j = 0; j < TS::PER; ++j) {
+        S[j] = zero4();
+        if (p.h0 && TS::valid(j)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[j][i] = p.h0[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)];
+        }
+    }
+
+    for (int n = 0; n < p.NT; ++n) {
+        const int t0 = n * C;
+        const int valid = min(C, p.T - t0);
+        const long row0 = (long)bh * p.T + t0;
+        // (a) state operand (and the saved copy)
+        TI* __restrict__ sv = SAVE ? static_cast<TI*>(p.states) + (((long)bh * p.NT + n) * DVr + v0) * DK : nullptr;
+#pragma unroll
+        for (int j = 0; j < TS::PER; ++j) {
+            if (!TS::valid(j)) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = TS::row(j, i), c = TS::col(j);
+                const TI x = from_f<TI>(S[j][i]);
+                Ss[r * LDK + c] = x;
+                if (SAVE) sv[r * DK + c] = x;
+            }
+        }
+        // (b) chunk tiles
+        load_gam_beta<GATE, C, DK>(gam_s, beta_s, p.gam + row0 * GW, p.beta + row0, valid);
+        __syncthreads();
+        const TI* __restrict__ q = static_cast<const TI*>(p.q) + row0 * DK;
+        const TI* __restrict__ k = static_cast<const TI*>(p.k) + row0 * DK;
+        const TI* __restrict__ v = static_cast<const TI*>(p.v) + row0 * DVr + v0;
+        const float* gl = gam_s + (valid - 1) * GW;
+        auto gam_at = [&](int r, int c) -> float {
+            if (GATE == kGateNone) return 0.f;
+            return GATE == kGateVector ? gam_s[r * DK + c] : gam_s[r];
+        };
+        auto gl_at = [&](int c) -> float {
+            if (GATE == kGateNone) return 0.f;
+            return GATE == kGateVector ? gl[c] : gl[0];
+        };
+        if (GATE == kGateNone) {
+            stage_copy<TI, C, DK, false>(Qg, LDK, q, DK, valid);
+            stage_copy<TI, C, DK, false>(Kg, LDK, k, DK, valid);
+            stage_copy<TI, C, DK, true>(KdT, LDC, k, DK, valid);
+        } else {
+            stage<TI, C, DK, false>(Qg, LDK, q, DK, valid, [&](int r, int c, float x) { return x * fexp(gam_at(r, c)); });
+            stage<TI, C, DK, false>(Kg, LDK, k, DK, valid, [&](int r, int c, float x) { return x * fexp(gam_at(r, c)); });
+            stage<TI, C, DK, true>(KdT, LDC, k, DK, valid,
+                                   [&](int r, int c, float x) { return x * fexp(gl_at(c) - gam_at(r, c)); });
+        }
+        stage_copy<TI, C, BV, false>(Vb, LDV, v, DVr, valid);
+        const long cc = ((long)bh * p.NT + n) * C * C;
+        stage_copy<TI, C, C, false>(Tl, LDC, static_cast<const TI*>(p.Tm) + cc, C, C);
+        stage_copy<TI, C, C, false>(Pl, LDC, static_cast<const TI*>(p.Pm) + cc, C, C);
+        __syncthreads();
+
+        // (c) X = (K Gam) S0^T ;  R = diag(beta) (V - X)  -> R^T
+        using TX = Tiles<C, BV>;
+        {
+            f32x4 X[TX::PER];
+            zero_acc<C, BV>(X);
+            gemm_nt<TI, C, BV, DK>(X, Kg, LDK, Ss, LDK);
+#pragma unroll
+            for (int j = 0; j < TX::PER; ++j) {
+                if (!TX::valid(j)) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TX::row(j, i), c = TX::col(j);
+                    RT[c * LDC + t] = from_f<TI>(beta_s[t] * (to_f(Vb[t * LDV + c]) - X[j][i]));
+                }
+            }
+        }
+        __syncthreads();
+        // (d) U = T R  -> U^T
+        {
+            f32x4 U[TX::PER];
+            zero_acc<C, BV>(U);
+            gemm_nt<TI, C, BV, C>(U, Tl, LDC, RT, LDC);
+#pragma unroll
+            for (int j = 0; j < TX::PER; ++j) {
+                if (!TX::valid(j)) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) UT[TX::col(j) * LDC + TX::row(j, i)] = from_f<TI>(U[j][i]);
+            }
+        }
+        __syncthreads();
+        // (e) O = (Q Gam) S0^T + P U
+        if (OUTPUT) {
+            f32x4 O[TX::PER];
+            zero_acc<C, BV>(O);
+            gemm_nt<TI, C, BV, DK>(O, Qg, LDK, Ss, LDK);
+            gemm_nt<TI, C, BV, C>(O, Pl, LDC, UT, LDC);
+            TI* __restrict__ o = static_cast<TI*>(p.o) + row0 * DVr + v0;
+#pragma unroll
+            for (int j = 0; j < TX::PER; ++j) {
+                if (!TX::valid(j)) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TX::row(j, i);
+                    if (t < valid) o[(long)t * DVr + TX::col(j)] = from_f<TI>(O[j][i]);
+                }
+            }
+        }
+        // (f) S1 = S0 Diag(Gam_C) + U^T (K Gam_C / Gam)
+#pragma unroll
+        for (int j = 0; j < TS::PER; ++j) {
+            if (!TS::valid(j)) continue;
+            if (GATE != kGateNone) {
+                const float f = fexp(gl_at(TS::col(j)));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[j][i] *= f;
+            }
+        }
+        gemm_nt<TI, BV, DK, C>(S, UT, LDC, KdT, LDC);
+        __syncthreads();
+    }
+    if (OUTPUT && p.hT) {
+#pragma unroll
+        for (int j = 0; j < TS::PER; ++j) {
+            if (!TS::valid(j)) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p.hT[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)] = S[j][i];
+        }
+    }
+}
+
+}  // namespace dn

@@ -1,0 +1,71 @@
+// dn_internal.h -- what the C-ABI layer and the kernels share: the problem
+// descriptor, the workspace layout and the launch entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dn {
+
+enum Gate { kGateNone = 0, kGateScalar = 1, kGateVector = 2 };
+
+// Everything a launch needs.  Element pointers are device pointers; the
+// element type of q/k/v/o/dO/dq/dk/dv/states/T/P/lambda/dS1 is the I/O type
+// (fp32 or bf16).  Layouts are row-major:
+//   q, k, dq, dk        [BH][T][DK]         v, o, dO, dv        [BH][T][DV]
+//   beta, dbeta         [BH][T]   fp32      g, dg  [BH][T] or [BH][T][DK]  fp32
+//   h0, hT, dh0, dhT    [BH][DV][DK] fp32   states              [BH][NT][DV][DK]
+// workspace:
+//   gam   fp32 in-chunk cumulative log-decay, same layout as g
+//   Tm    [BH][NT][C][C]   (I + A)^{-1} of each chunk
+//   Pm    [BH][NT][C][C]   causal intra-chunk score matrix of each chunk
+//   lam   [BH][NT][C][DV]  triangular-residual adjoint (backward only)
+//   dS1   [BH][NT][DV][DK] state cotangent leaving each chunk (backward only)
+struct Params {
+    int BH, T, NT, DKr, DVr;  // runtime copies (the kernels also get them as template args)
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* beta;
+    const float* g;
+    const float* h0;
+    const float* dhT;
+    void* o;
+    float* hT;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dbeta;
+    float* dg;
+    float* dh0;
+    void* states;  // read by the backward, written by the forward
+    float* gam;
+    void* Tm;
+    void* Pm;
+    void* lam;
+    void* dS1;
+};
+
+struct Problem {
+    int B, H, T, dk, dv, C;
+    int bf16;   // 1: bf16 I/O, 0: fp32 I/O
+    int gate;   // Gate
+    int BV;     // d_v block of the sequential kernels
+};
+
+// Workspace carving.  Offsets in bytes from the workspace base; every region
+// starts on a 256-byte boundary.
+struct WsLayout {
+    size_t gam, Tm, Pm, lam, dS1, states, total;
+};
+WsLayout ws_layout(const Problem& pr, bool backward, bool need_states);
+
+// Kernel launch sequences (all enqueue on `stream`, none synchronises).
+hipError_t launch_forward(const Problem& pr, const Params& p, bool save_states, hipStream_t stream);
+hipError_t launch_backward(const Problem& pr, const Params& p, bool have_states, hipStream_t stream);
+bool supported(const Problem& pr);
+int pick_bv(const Problem& pr);
+
+}  // namespace dn

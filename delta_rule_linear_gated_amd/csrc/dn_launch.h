@@ -1,0 +1,134 @@
+// dn_launch.h -- launch templates shared by the per-variant translation units
+// (one per pass x I/O type x gate, compiled in parallel).
+#pragma once
+
+#include "dn_bwd_kernels.h"
+#include "dn_fwd_kernels.h"
+#include "dn_internal.h"
+
+namespace dn {
+
+typedef hipError_t (*LaunchFn)(const Problem&, const Params&, bool, hipStream_t);
+
+// Entry points defined by dn_{fwd,bwd}_{bf16,f32}_g{0,1,2}.hip.
+#define DN_DECLARE_VARIANT(PASS, DT, G) \
+    hipError_t launch_##PASS##_##DT##_g##G(const Problem&, const Params&, bool, hipStream_t);
+DN_DECLARE_VARIANT(fwd, bf16, 0) DN_DECLARE_VARIANT(fwd, bf16, 1) DN_DECLARE_VARIANT(fwd, bf16, 2)
+DN_DECLARE_VARIANT(fwd, f32, 0) DN_DECLARE_VARIANT(fwd, f32, 1) DN_DECLARE_VARIANT(fwd, f32, 2)
+DN_DECLARE_VARIANT(bwd, bf16, 0) DN_DECLARE_VARIANT(bwd, bf16, 1) DN_DECLARE_VARIANT(bwd, bf16, 2)
+DN_DECLARE_VARIANT(bwd, f32, 0) DN_DECLARE_VARIANT(bwd, f32, 1) DN_DECLARE_VARIANT(bwd, f32, 2)
+
+constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Static LDS of each kernel (bytes), mirrored from the kernels' declarations
+// so that configurations that cannot fit are never instantiated.
+template <typename TI, int GATE, int C, int DK> constexpr size_t prep_lds() {
+    constexpr size_t E = sizeof(TI);
+    constexpr int LDK = DK + Pad<TI>::value;
+    constexpr int GW = GateLayout<GATE, DK>::GW;
+    return 4 * (C * GW + C + C * (C + 4)) + E * C * LDK * (GATE == kGateVector ? 3 : 2) + 64;
+}
+template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_state_lds() {
+    constexpr size_t E = sizeof(TI);
+    constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
+    constexpr int GW = GateLayout<GATE, DK>::GW;
+    return 4 * (C * GW + C) + E * (BV * LDK + 2 * C * LDK + DK * LDC + C * LDV + 4 * C * LDC);
+}
+template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t bwd_state_lds() {
+    constexpr size_t E = sizeof(TI);
+    constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P;
+    constexpr int GW = GateLayout<GATE, DK>::GW;
+    return 4 * (C * GW + C) + E * (BV * LDK + C * LDK + 2 * C * LDC + 3 * BV * LDC + 2 * DK * LDC);
+}
+constexpr size_t kLdsMax = 160 * 1024;
+
+// bwd_chunk's layout asserts are only meaningful when the configuration fits;
+// evaluate its TOTAL lazily through this helper.
+template <typename TI, int GATE, int C, int D> struct Fits {
+    static constexpr int BV = D < 64 ? D : 64;
+    static constexpr bool small = prep_lds<TI, GATE, C, D>() <= kLdsMax &&
+                                  fwd_state_lds<TI, GATE, C, D, BV>() <= kLdsMax &&
+                                  bwd_state_lds<TI, GATE, C, D, BV>() <= kLdsMax;
+    // fp32 at D = 128 cannot hold the backward's tiles
+    static constexpr bool value = small && !(sizeof(TI) == 4 && D > 64) &&
+                                  !(sizeof(TI) == 4 && D == 64 && GATE == kGateVector && C == 64);
+};
+
+template <typename TI, int GATE, int C, int D>
+hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t stream) {
+    if constexpr (!Fits<TI, GATE, C, D>::value) {
+        return hipErrorInvalidConfiguration;
+    } else {
+        constexpr int BV = D < 64 ? D : 64;
+        const int BH = pr.B * pr.H;
+        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        if (save)
+            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, true>), dim3(D / BV, BH),
+                               dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, true>), dim3(D / BV, BH),
+                               dim3(kThreads), 0, stream, p);
+        return hipGetLastError();
+    }
+}
+
+template <typename TI, int GATE, int C, int D>
+hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStream_t stream) {
+    if constexpr (!Fits<TI, GATE, C, D>::value) {
+        return hipErrorInvalidConfiguration;
+    } else {
+        constexpr int BV = D < 64 ? D : 64;
+        const int BH = pr.B * pr.H;
+        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        if (!have_states)
+            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, false>), dim3(D / BV, BH),
+                               dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3(D / BV, BH), dim3(kThreads), 0,
+                           stream, p);
+        hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        return hipGetLastError();
+    }
+}
+
+template <typename TI, int GATE, int C, int D> bool fits_rt() { return Fits<TI, GATE, C, D>::value; }
+
+// Dispatch over (dtype, gate, C, D).  F is a functor template wrapper.
+#define DN_DISPATCH_D(TI, GATE, C, FN, ...)                                      \
+    switch (pr.dk) {                                                             \
+        case 16: return FN<TI, GATE, C, 16>(__VA_ARGS__);                        \
+        case 32: return FN<TI, GATE, C, 32>(__VA_ARGS__);                        \
+        case 64: return FN<TI, GATE, C, 64>(__VA_ARGS__);                        \
+        case 128: return FN<TI, GATE, C, 128>(__VA_ARGS__);                      \
+        default: break;                                                          \
+    }
+#define DN_DISPATCH_C(TI, GATE, FN, ...)                                         \
+    switch (pr.C) {                                                              \
+        case 16: DN_DISPATCH_D(TI, GATE, 16, FN, __VA_ARGS__) break;             \
+        case 32: DN_DISPATCH_D(TI, GATE, 32, FN, __VA_ARGS__) break;             \
+        case 64: DN_DISPATCH_D(TI, GATE, 64, FN, __VA_ARGS__) break;             \
+        default: break;                                                          \
+    }
+#define DN_DISPATCH_G(TI, FN, ...)                                               \
+    switch (pr.gate) {                                                           \
+        case kGateNone: DN_DISPATCH_C(TI, kGateNone, FN, __VA_ARGS__) break;     \
+        case kGateScalar: DN_DISPATCH_C(TI, kGateScalar, FN, __VA_ARGS__) break; \
+        case kGateVector: DN_DISPATCH_C(TI, kGateVector, FN, __VA_ARGS__) break; \
+        default: break;                                                          \
+    }
+#define DN_DISPATCH(FN, ...)                                                     \
+    if (pr.bf16) {                                                               \
+        DN_DISPATCH_G(bf16, FN, __VA_ARGS__)                                     \
+    } else {                                                                     \
+        DN_DISPATCH_G(float, FN, __VA_ARGS__)                                    \
+    }
+
+
+// Defines launch_<PASS>_<DT>_g<G>: dispatch over (C, D) for one I/O type and gate.
+#define DN_DEFINE_VARIANT(PASS, DT, TI, G)                                                        \
+    hipError_t launch_##PASS##_##DT##_g##G(const Problem& pr, const Params& p, bool flag,         \
+                                           hipStream_t stream) {                                  \
+        DN_DISPATCH_C(TI, G, PASS##_impl, pr, p, flag, stream)                                    \
+        return hipErrorInvalidConfiguration;                                                      \
+    }
+
+}  // namespace dn

@@ -1,0 +1,152 @@
+/*
+ * dn.h -- C ABI of the chunkwise gated delta-rule operator for AMD MI355X (gfx950).
+ *
+ * The operator (per batch element and head; the state S is d_v x d_k):
+ *
+ *     S_t = S_{t-1} Diag(exp(g_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,     o_t = S_t q_t
+ *
+ * with S_0 = h0 and hT = S_T.  g_t is the natural-log decay: absent (DeltaNet),
+ * one scalar per step (Gated DeltaNet) or one value per key channel (Kimi Delta
+ * Attention).  Sources:
+ *   - ReWY abstract (paperdot listing): delta-rule linear attention for DeltaNet,
+ *     GDN and KDA; chunkwise evaluation; a backward in which the chunk correction
+ *     is differentiated as one triangular residual system (no inverse adjoint),
+ *     centred contractions for vector gates and key-gradient reuse for scalar
+ *     gates; exact in exact arithmetic; fp32 working matrices.
+ *   - SFDA technical summary (gist.science), "Kernarchitektur": the update
+ *     S_t = (I - beta k k*) Lambda_t S_{t-1} + beta k v*, which with zero phase is
+ *     KDA; this header uses its transpose (S is d_v x d_k, o = S q).
+ *     "Der konstruktive Chunk-WY-Theorem" / "Zentrale Beitraege": chunk products
+ *     in WY form and the exact affine chunk transfer used by the forward.
+ *   - KLA abstract (thelatestinai): GDN as gated decay plus delta-rule residual
+ *     write; the Kaczmarz step beta_t = eta_t / (||k_t||^2 + eps) changes only
+ *     the beta input, so callers compute it before calling.
+ *   - Fast Weight Attention abstract (papers.fzhiy.net): read-after-write output,
+ *     o_t reads the state after step t's write.
+ * There is no query scale.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer, 16-byte aligned, dense and
+ *     row-major in the layout given below.  The caller owns all memory.  The
+ *     library never allocates, frees or synchronises: it validates the
+ *     arguments on the host, then enqueues kernels on `stream` (a hipStream_t;
+ *     NULL = the default stream) and returns.
+ *   - Outputs must not overlap inputs, each other or the workspace.
+ *   - On any error nothing is enqueued, a negative dn_status is returned and
+ *     dn_last_error() describes it.  No C++ exception crosses this boundary.
+ *   - NaN / Inf in the inputs propagate to the outputs; they are not errors.
+ *   - The library keeps no state between calls except the per-thread error text;
+ *     calls from several host threads are safe.  Two calls that share a
+ *     workspace must be ordered on one stream.
+ *
+ * Layouts (BH = B * H, NT = ceil(T / C)); "io" is the element type chosen by
+ * dn_shape.dtype (fp32 or bf16), everything marked fp32 is always fp32:
+ *     q, k, dq, dk       io   [B][H][T][dk]
+ *     v, o, dout, dv     io   [B][H][T][dv]
+ *     beta, dbeta        fp32 [B][H][T]
+ *     g, dg              fp32 [B][H][T] (DN_GATE_SCALAR) or [B][H][T][dk] (DN_GATE_VECTOR)
+ *     h0, hT, dh0, dhT   fp32 [B][H][dv][dk]
+ *     states             io   [B][H][NT][dv][dk]   state entering each chunk
+ * The saved states are kept in the io type: the kernels use the state as a
+ * matrix-core operand in that type, so the backward reads exactly the operand
+ * values the forward used; the running state itself and hT are fp32.
+ */
+#ifndef DN_H
+#define DN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DN_OK = 0,
+    DN_ERR_INVALID = -1,      /* NULL / misaligned / overlapping pointer, bad enum */
+    DN_ERR_SHAPE = -2,        /* negative or inconsistent sizes */
+    DN_ERR_DTYPE = -3,        /* unknown dtype */
+    DN_ERR_WORKSPACE = -4,    /* workspace missing or smaller than dn_workspace_bytes() */
+    DN_ERR_UNSUPPORTED = -5,  /* valid but not implemented (see dn_shape) */
+    DN_ERR_HIP = -6           /* the HIP runtime refused a launch */
+} dn_status;
+
+typedef enum { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
+
+typedef enum { DN_GATE_NONE = 0, DN_GATE_SCALAR = 1, DN_GATE_VECTOR = 2 } dn_gate;
+
+/* Which call a workspace is sized for. */
+typedef enum {
+    DN_PASS_FWD = 0,           /* dn_chunk_fwd (states saved or not) */
+    DN_PASS_BWD = 1,           /* dn_chunk_bwd with the forward's saved states */
+    DN_PASS_BWD_RECOMPUTE = 2  /* dn_chunk_bwd with states == NULL (states recomputed) */
+} dn_pass;
+
+/*
+ * Problem shape.  Supported: B, H, T >= 0 with B*H <= 65535; dk == dv in
+ * {16, 32, 64, 128} (fp32: dk <= 64); C in {16, 32, 64}; any T (a last,
+ * shorter chunk is handled exactly); fp32 with a vector gate needs C <= 32 at
+ * dk = 64.  Anything else returns DN_ERR_UNSUPPORTED.
+ */
+typedef struct {
+    int32_t B, H, T, dk, dv, C;
+    int32_t dtype;  /* dn_dtype */
+    int32_t gate;   /* dn_gate  */
+} dn_shape;
+
+/* Bytes of `states` for this shape: B*H*ceil(T/C)*dv*dk*sizeof(io).  0 on bad shape. */
+size_t dn_states_bytes(const dn_shape* shape);
+
+/* Workspace bytes the given pass needs (0 on bad shape).  Workspace contents
+ * are scratch: nothing is carried from one call to the next. */
+size_t dn_workspace_bytes(const dn_shape* shape, int pass);
+
+/*
+ * Forward pass (chunkwise: per-chunk WY/UT construction with a unit-lower-
+ * triangular solve, the inter-chunk state recurrence, the causal intra-chunk
+ * output -- ReWY abstract; SFDA summary, chunk-WY theorem and affine transfer).
+ *   inputs : q, k, v, beta; g (must be NULL iff gate == DN_GATE_NONE);
+ *            h0 (NULL = zero initial state)
+ *   outputs: o; hT (NULL = not wanted); states (NULL = not saved, i.e. the
+ *            recomputation policy: dn_chunk_bwd is then called with
+ *            states == NULL)
+ *   ws     : device workspace of ws_bytes >= dn_workspace_bytes(shape, DN_PASS_FWD)
+ */
+dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
+                       const float* beta, const float* g, const float* h0, void* o, float* hT,
+                       void* states, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward pass in the reduced ReWY form: vector-Jacobian products of
+ * L = <O, dout> + <hT, dhT> with respect to every input.
+ *   inputs : q, k, v, beta, g, h0 as given to dn_chunk_fwd; dout; dhT (NULL =
+ *            zero); states from dn_chunk_fwd, or NULL to recompute them here
+ *   outputs: dq, dk, dv, dbeta; dg (must be NULL iff gate == DN_GATE_NONE;
+ *            same layout as g); dh0 (NULL = not wanted)
+ *   ws     : >= dn_workspace_bytes(shape, states ? DN_PASS_BWD : DN_PASS_BWD_RECOMPUTE)
+ */
+dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, const void* v,
+                       const float* beta, const float* g, const float* h0, const void* dout,
+                       const float* dhT, const void* states, void* dq, void* dk, void* dv,
+                       float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Static description of a status code. */
+const char* dn_status_string(dn_status status);
+
+/* Detail text of the last error on the calling thread ("" if none). */
+const char* dn_last_error(void);
+
+/*
+ * Diagnostics: byte offsets of the workspace regions a pass uses, in the order
+ * {cumulative log-decay, (I+A)^{-1} per chunk, intra-chunk scores per chunk,
+ * triangular-residual adjoint, state cotangent per chunk, recomputed states,
+ * total}.  Returns DN_OK or an error for a bad shape / pass.
+ */
+dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[7]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DN_H */

@@ -97,21 +97,22 @@ def _chunk_backward(Q, K, V, beta, G, S0, dO, dS1, c):
     dgam += WP.sum(axis=1) - WP.sum(axis=0)
     # gamma = cumsum(G): dG is the reverse cumulative sum of dgam
     dG = np.cumsum(dgam[::-1], axis=0)[::-1]
-    return dQ, dK, dV, dbeta, dG, dS0
+    return dQ, dK, dV, dbeta, dG, dS0, lam
 
 
 def _split(T, C):
     return [(t0, min(t0 + C, T)) for t0 in range(0, T, C)]
 
 
-def forward(q, k, v, beta, g=None, h0=None, C=16):
+def forward(q, k, v, beta, g=None, h0=None, C=16, trace=None):
     """Chunked forward of one head or of [B,H,...] batches.  Returns (o, hT, states)
-    where states[n] is the state entering chunk n."""
+    where states[n] is the state entering chunk n.  For one head, ``trace`` (a
+    list) receives per chunk a dict with gam, T = (I + A)^{-1}, Pm and U."""
     q = np.asarray(q, np.float64)
     if q.ndim == 4:
         B, H = q.shape[:2]
         outs = [forward(q[b, h], k[b, h], v[b, h], beta[b, h],
-                        None if g is None else g[b, h], None if h0 is None else h0[b, h], C)
+                        None if g is None else g[b, h], None if h0 is None else h0[b, h], C, trace)
                 for b in range(B) for h in range(H)]
         o = np.stack([x[0] for x in outs]).reshape(B, H, *outs[0][0].shape)
         hT = np.stack([x[1] for x in outs]).reshape(B, H, *outs[0][1].shape)
@@ -126,21 +127,27 @@ def forward(q, k, v, beta, g=None, h0=None, C=16):
     states = []
     for t0, t1 in _split(T, C):
         states.append(S.copy())
-        O, S, _ = _chunk_forward(q[t0:t1], k[t0:t1], v[t0:t1], beta[t0:t1], G[t0:t1], S)
+        O, S, cache = _chunk_forward(q[t0:t1], k[t0:t1], v[t0:t1], beta[t0:t1], G[t0:t1], S)
         o[t0:t1] = O
+        if trace is not None:
+            L = t1 - t0
+            trace.append(dict(gam=cache["gam"], T=np.linalg.inv(np.eye(L) + cache["A"]),
+                              Pm=cache["Pm"], U=cache["U"]))
     return o, S, np.array(states).reshape(len(states), dv, dk)
 
 
-def backward(q, k, v, beta, g, h0, do, dhT=None, C=16):
+def backward(q, k, v, beta, g, h0, do, dhT=None, C=16, trace=None):
     """Chunked reverse mode (ReWY form) of one head or of [B,H,...] batches.
     Returns dict dq, dk, dv, dbeta, dg (None without a gate, [T] for a scalar
-    gate, [T, dk] for a vector gate), dh0."""
+    gate, [T, dk] for a vector gate), dh0.  For one head, ``trace`` (a dict)
+    receives per chunk, in chunk order, "dS1" (the state cotangent leaving the
+    chunk) and "lam" (the solution of (I + A)^T lam = dU)."""
     q = np.asarray(q, np.float64)
     if q.ndim == 4:
         B, H = q.shape[:2]
         res = [backward(q[b, h], k[b, h], v[b, h], beta[b, h], None if g is None else g[b, h],
                         None if h0 is None else h0[b, h], do[b, h],
-                        None if dhT is None else dhT[b, h], C)
+                        None if dhT is None else dhT[b, h], C, trace)
                for b in range(B) for h in range(H)]
         out = {}
         for name in res[0]:
@@ -166,10 +173,16 @@ def backward(q, k, v, beta, g, h0, do, dhT=None, C=16):
     dvv = np.zeros_like(v)
     db = np.zeros_like(beta)
     dG = np.zeros((T, dk))
+    dS1s, lams = [], []
     for (t0, t1), (S0, cache) in reversed(list(zip(spans, saved))):
+        dS1s.append(dS)
         r = _chunk_backward(q[t0:t1], k[t0:t1], v[t0:t1], beta[t0:t1], G[t0:t1], S0,
                             do[t0:t1], dS, cache)
-        dq[t0:t1], dkk[t0:t1], dvv[t0:t1], db[t0:t1], dG[t0:t1], dS = r
+        dq[t0:t1], dkk[t0:t1], dvv[t0:t1], db[t0:t1], dG[t0:t1], dS = r[:6]
+        lams.append(r[6])
+    if trace is not None:
+        trace["dS1"] = dS1s[::-1]
+        trace["lam"] = lams[::-1]
     if g is None:
         dg = None
     elif np.asarray(g).ndim == 1:

@@ -1,0 +1,77 @@
+"""Shared helpers of the parity tests: run the HIP path through the C ABI and the
+fp64 oracle on the same rounded inputs, and compare them."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from delta_rule_linear_gated_amd import binding as B
+from delta_rule_linear_gated_amd import workloads as W
+
+# Tolerances of the parity bar: max |gpu - oracle| / max |oracle| per tensor.
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+OUTPUTS = ("o", "hT", "dq", "dk", "dv", "dbeta", "dg", "dh0")
+
+
+def nthreads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(x - ref))) if ref.size else 0.0
+    return num / den if den > 0 else num
+
+
+def gpu_run(w: W.Workload, inp: dict, policy: str | None = None, dhT=True):
+    """fwd + bwd on the GPU through the C ABI.  Returns a dict of CPU tensors."""
+    policy = policy or w.policy
+    d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
+    o, hT, states = B.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], C=w.C,
+                                save_states=(policy == "save"))
+    gr = B.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["do"],
+                     d["dhT"] if dhT else None, states, C=w.C)
+    torch.cuda.synchronize()
+    out = {"o": o, "hT": hT, **gr, "states": states}
+    return {n: (None if t is None else t.cpu()) for n, t in out.items()}
+
+
+def oracle_run(inp: dict, heads=None, dhT=True):
+    """fp64 oracle on the same rounded inputs (optionally only some (b, h) heads)."""
+    f = {n: W.to_f64(t, heads) for n, t in inp.items()}
+    o, hT = oracle.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], nthreads=nthreads())
+    gr = oracle.backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], f["do"],
+                         f["dhT"] if dhT else None, nthreads=nthreads())
+    return {"o": o, "hT": hT, **gr}
+
+
+def select(t, heads):
+    if t is None or heads is None:
+        return t
+    return torch.stack([t[b, h] for b, h in heads])[None]
+
+
+def compare(gpu: dict, ref: dict, tol: float, heads=None, label=""):
+    errs = {}
+    for n in OUTPUTS:
+        if ref.get(n) is None:
+            assert gpu.get(n) is None, n
+            continue
+        x = select(gpu[n], heads)
+        assert torch.isfinite(x.float()).all(), f"{label} {n} has non-finite values"
+        errs[n] = rel_err(x.to(torch.float64).numpy(), ref[n])
+    say(f"{label} errors: " + ", ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, f"{label} over tolerance {tol}: {bad}"
+    return errs

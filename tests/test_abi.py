@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/dn.h declares, sizes its buffers, and rejects bad calls on the host
+before any HIP call (so no test here launches anything)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from delta_rule_linear_gated_amd import binding as B
+from delta_rule_linear_gated_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "dn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dn_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for st in (B.DN_OK, B.DN_ERR_INVALID, B.DN_ERR_SHAPE, B.DN_ERR_DTYPE, B.DN_ERR_WORKSPACE,
+               B.DN_ERR_UNSUPPORTED, B.DN_ERR_HIP):
+        assert B.dn_status_string(st) not in ("", "unknown status")
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_sizes_of_the_workloads(name):
+    w = W.CONFIGS[name]
+    sh = B.make_shape(w.B, w.H, w.T, w.dk, w.dv, w.C, w.dtype, w.gate)
+    E = 2 if w.dtype == "bf16" else 4
+    NT = -(-w.T // w.C)
+    assert B.dn_states_bytes(sh) == w.B * w.H * NT * w.dv * w.dk * E
+    f = B.dn_workspace_bytes(sh, B.DN_PASS_FWD)
+    b = B.dn_workspace_bytes(sh, B.DN_PASS_BWD)
+    r = B.dn_workspace_bytes(sh, B.DN_PASS_BWD_RECOMPUTE)
+    assert 0 < f < b < r
+    lay = B.dn_workspace_layout(sh, B.DN_PASS_BWD_RECOMPUTE)
+    assert lay["total"] == r
+    offs = [lay[k] for k in ("gam", "T", "P", "lam", "dS1", "states", "total")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert r - b >= B.dn_states_bytes(sh)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation first
+
+
+def fwd(sh, **over):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, h0=None, o=FAKE * 6, hT=None,
+             states=None, ws=FAKE * 7, ws_bytes=1 << 40)
+    a.update(over)
+    return B.dn_chunk_fwd(sh, a["q"], a["k"], a["v"], a["beta"], a["g"], a["h0"], a["o"], a["hT"],
+                          a["states"], a["ws"], a["ws_bytes"], 0)
+
+
+def bwd(sh, **over):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, h0=None, dout=FAKE * 8,
+             dhT=None, states=None, dq=FAKE * 9, dk=FAKE * 10, dv=FAKE * 11, dbeta=FAKE * 12,
+             dg=FAKE * 13, dh0=None, ws=FAKE * 14, ws_bytes=1 << 40)
+    a.update(over)
+    return B.dn_chunk_bwd(sh, *(a[n] for n in ("q", "k", "v", "beta", "g", "h0", "dout", "dhT", "states",
+                                               "dq", "dk", "dv", "dbeta", "dg", "dh0", "ws", "ws_bytes")), 0)
+
+
+SMALL = dict(B=1, H=1, T=64, dk=16, dv=16, C=16, dtype="bf16", gate="scalar")
+
+
+def sh_of(**over):
+    d = dict(SMALL)
+    d.update(over)
+    return B.make_shape(**d)
+
+
+def test_validation_errors_forward():
+    assert fwd(sh_of(T=-1)) == B.DN_ERR_SHAPE
+    assert fwd(sh_of(dk=0)) == B.DN_ERR_SHAPE
+    assert fwd(sh_of(dtype=7)) == B.DN_ERR_DTYPE
+    assert fwd(sh_of(gate=3)) == B.DN_ERR_INVALID
+    assert fwd(sh_of(C=48)) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh_of(dk=16, dv=32)) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh_of(dk=96, dv=96)) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh_of(dk=128, dv=128, C=64, dtype="fp32")) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh_of(B=300, H=300)) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh_of(), q=None) == B.DN_ERR_INVALID
+    assert fwd(sh_of(), g=None) == B.DN_ERR_INVALID
+    assert fwd(sh_of(gate="none")) == B.DN_ERR_INVALID                 # g given without a gate
+    assert fwd(sh_of(), q=FAKE + 8) == B.DN_ERR_INVALID                # misaligned
+    assert fwd(sh_of(), ws_bytes=16) == B.DN_ERR_WORKSPACE
+    assert fwd(sh_of(), o=FAKE * 3) == B.DN_ERR_INVALID                # output aliases v
+    assert fwd(sh_of(), o=FAKE * 7) == B.DN_ERR_INVALID                # output aliases workspace
+    assert "overlaps" in B.dn_last_error()
+    assert fwd(sh_of(), v=None) == B.DN_ERR_INVALID
+    L = B.lib()
+    assert L.dn_chunk_fwd(None, None, None, None, None, None, None, None, None, None, None, 0, None) == B.DN_ERR_INVALID
+
+
+def test_validation_errors_backward():
+    assert bwd(sh_of(), dq=None) == B.DN_ERR_INVALID
+    assert bwd(sh_of(), dg=None) == B.DN_ERR_INVALID
+    assert bwd(sh_of(gate="none"), g=None) == B.DN_ERR_INVALID         # dg given without a gate
+    assert bwd(sh_of(), ws_bytes=1024) == B.DN_ERR_WORKSPACE
+    assert bwd(sh_of(), dk=FAKE * 9) == B.DN_ERR_INVALID               # dk aliases dq
+    assert bwd(sh_of(), dq=FAKE) == B.DN_ERR_INVALID                   # dq aliases q
+    assert bwd(sh_of(T=-5)) == B.DN_ERR_SHAPE
+
+
+def test_workspace_grows_with_recompute():
+    sh = sh_of(T=4096, dk=128, dv=128, C=64)
+    assert B.dn_workspace_bytes(sh, B.DN_PASS_BWD_RECOMPUTE) - B.dn_workspace_bytes(sh, B.DN_PASS_BWD) \
+        >= B.dn_states_bytes(sh)
+    assert B.dn_workspace_bytes(sh, 9) == 0
