@@ -27,7 +27,8 @@ DN_GATE_NONE, DN_GATE_SCALAR, DN_GATE_VECTOR = 0, 1, 2
 DN_PASS_FWD, DN_PASS_BWD, DN_PASS_BWD_RECOMPUTE = 0, 1, 2
 
 EXPORTS = ("dn_states_bytes", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
-           "dn_chunk_bwd", "dn_status_string", "dn_last_error")
+           "dn_chunk_bwd", "dn_status_string", "dn_last_error", "dn_profile_enable",
+           "dn_profile_collect")
 
 
 class DnError(RuntimeError):
@@ -69,6 +70,11 @@ def lib():
     L.dn_status_string.restype = ctypes.c_char_p
     L.dn_last_error.argtypes = []
     L.dn_last_error.restype = ctypes.c_char_p
+    L.dn_profile_enable.argtypes = [i32]
+    L.dn_profile_enable.restype = i32
+    L.dn_profile_collect.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int), i32]
+    L.dn_profile_collect.restype = i32
     _lib = L
     return L
 
@@ -125,6 +131,24 @@ def dn_status_string(status: int) -> str:
 
 def dn_last_error() -> str:
     return lib().dn_last_error().decode()
+
+
+def dn_profile_enable(on: bool) -> None:
+    _check(lib().dn_profile_enable(1 if on else 0))
+
+
+def dn_profile_collect(max_kernels: int = 16) -> dict:
+    """{kernel name: (total ms, launches)} of the launches since the last collect."""
+    names = ctypes.create_string_buffer(32 * max_kernels)
+    ms = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int * max_kernels)()
+    n = lib().dn_profile_collect(names, ms, cnt, max_kernels)
+    raw = names.raw
+    out = {}
+    for i in range(n):
+        nm = raw[32 * i: 32 * i + 32].split(b"\0", 1)[0].decode()
+        out[nm] = (ms[i], cnt[i])
+    return out
 
 
 def dn_chunk_fwd(shape, q, k, v, beta, g, h0, o, hT, states, ws, ws_bytes, stream=None) -> int:

@@ -31,9 +31,9 @@ COMMON = [
 
 
 def sources() -> list[str]:
-    """dn_api.cpp plus every .hip unit (the per-variant kernel units and dn_launch.hip)."""
+    """dn_api.cpp, dn_profile.cpp and every .hip unit (the per-variant kernel units and dn_launch.hip)."""
     hips = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
-    return ["dn_api.cpp", *hips]
+    return ["dn_api.cpp", "dn_profile.cpp", *hips]
 
 
 def _compile(src: str) -> str:

@@ -33,14 +33,17 @@
 namespace dn {
 
 // ---------------------------------------------------------------------------
-// bwd_state_kernel: grid (DV / BV, BH), chunks walked from last to first.
+// bwd_state_kernel: grid (DV / BV, BH), chunks walked from last to first; the
+// global tiles of chunk n - 1 are loaded into registers while chunk n is
+// computed.  The workspace holds T^T and P^T here (prep_kernel<..., true>).
 template <typename TI, int GATE, int C, int DK, int BV>
 __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     constexpr int PAD = Pad<TI>::value;
     constexpr int LDK = DK + PAD;
     constexpr int LDC = C + PAD;
     constexpr int GW = GateLayout<GATE, DK>::GW;
-    __shared__ float gam_s[C * GW];
+    __shared__ float gam_s[GATE == kGateVector ? C * DK : 4];
+    __shared__ float rowf[2 * C];
     __shared__ float beta_s[C];
     __shared__ __align__(16) TI dSs[BV * LDK];   // dS1 operand     [v][c]
     __shared__ __align__(16) TI Kd[C * LDK];     // K Gam_C / Gam   [t][c]
@@ -60,12 +63,30 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < TS::PER; ++j) {
         dS[j] = zero4();
-        if (p.dhT && TS::valid(j)) {
+        if (p.dhT && TS::active()) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 dS[j][i] = p.dhT[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)];
         }
     }
+
+    RegB<TI, C, DK> rq, rk;
+    RegB<TI, C, BV> rdo;
+    RegN<TI, C, C> rPT, rTT;
+    GateRegs<GATE, C, DK> rg;
+    auto prefetch = [&](int n) {
+        const int t0 = n * C;
+        const int valid = min(C, p.T - t0);
+        const long row0 = (long)bh * p.T + t0;
+        const long cc = ((long)bh * p.NT + n) * C * C;
+        rg.load(p.gam + row0 * GW, p.beta + row0, valid);
+        rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
+        rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
+        rdo.load(static_cast<const TI*>(p.dout) + row0 * DVr + v0, DVr, valid);
+        rPT.load(static_cast<const TI*>(p.Pm) + cc, C, C);
+        rTT.load(static_cast<const TI*>(p.Tm) + cc, C, C);
+    };
+    prefetch(p.NT - 1);
 
     for (int n = p.NT - 1; n >= 0; --n) {
         const int t0 = n * C;
@@ -73,47 +94,36 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         const long row0 = (long)bh * p.T + t0;
         // (a) dS1 of this chunk: operand copy and workspace copy
         TI* __restrict__ dsv = static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK;
+        if (TS::active()) {
 #pragma unroll
-        for (int j = 0; j < TS::PER; ++j) {
-            if (!TS::valid(j)) continue;
+            for (int j = 0; j < TS::PER; ++j) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = TS::row(j, i), c = TS::col(j);
-                const TI x = from_f<TI>(dS[j][i]);
-                dSs[r * LDK + c] = x;
-                dsv[r * DK + c] = x;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = TS::row(j, i), c = TS::col(j);
+                    const TI x = from_f<TI>(dS[j][i]);
+                    dSs[r * LDK + c] = x;
+                    dsv[r * DK + c] = x;
+                }
             }
         }
-        // (b) chunk tiles
-        load_gam_beta<GATE, C, DK>(gam_s, beta_s, p.gam + row0 * GW, p.beta + row0, valid);
+        // (b) commit this chunk's tiles
+        rg.commit(rowf, gam_s, beta_s);
         __syncthreads();
-        const TI* __restrict__ q = static_cast<const TI*>(p.q) + row0 * DK;
-        const TI* __restrict__ k = static_cast<const TI*>(p.k) + row0 * DK;
-        const TI* __restrict__ dO = static_cast<const TI*>(p.dout) + row0 * DVr + v0;
-        const float* gl = gam_s + (valid - 1) * GW;
-        auto gam_at = [&](int r, int c) -> float {
-            if (GATE == kGateNone) return 0.f;
-            return GATE == kGateVector ? gam_s[r * DK + c] : gam_s[r];
-        };
-        auto gl_at = [&](int c) -> float {
-            if (GATE == kGateNone) return 0.f;
-            return GATE == kGateVector ? gl[c] : gl[0];
-        };
+        const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (GATE == kGateNone) {
-            stage_copy<TI, C, DK, false>(Kd, LDK, k, DK, valid);
-            stage_copy<TI, C, DK, true>(QgT, LDC, q, DK, valid);
-            stage_copy<TI, C, DK, true>(KgT, LDC, k, DK, valid);
+            rk.store_n(Kd, LDK, Identity());
+            rq.store_t(QgT, LDC, Identity());
+            rk.store_t(KgT, LDC, Identity());
         } else {
-            stage<TI, C, DK, false>(Kd, LDK, k, DK, valid,
-                                    [&](int r, int c, float x) { return x * fexp(gl_at(c) - gam_at(r, c)); });
-            stage<TI, C, DK, true>(QgT, LDC, q, DK, valid, [&](int r, int c, float x) { return x * fexp(gam_at(r, c)); });
-            stage<TI, C, DK, true>(KgT, LDC, k, DK, valid, [&](int r, int c, float x) { return x * fexp(gam_at(r, c)); });
+            rk.store_n(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
+            rq.store_t(QgT, LDC, [&](int r, int c, float x) { return x * gf.G(r, c); });
+            rk.store_t(KgT, LDC, [&](int r, int c, float x) { return x * gf.G(r, c); });
         }
-        stage_copy<TI, C, BV, true>(dOT, LDC, dO, DVr, valid);
-        const long cc = ((long)bh * p.NT + n) * C * C;
-        stage_copy<TI, C, C, true>(PT, LDC, static_cast<const TI*>(p.Pm) + cc, C, C);
-        stage_copy<TI, C, C, true>(TT, LDC, static_cast<const TI*>(p.Tm) + cc, C, C);
+        rdo.store_t(dOT, LDC, Identity());
+        rPT.store(PT, LDC);
+        rTT.store(TT, LDC);
         __syncthreads();
+        if (n > 0) prefetch(n - 1);
 
         using TX = Tiles<C, BV>;
         // (c) dU = P^T dO + Kd dS1^T  -> dU^T
@@ -122,11 +132,12 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
             zero_acc<C, BV>(dU);
             gemm_nt<TI, C, BV, C>(dU, PT, LDC, dOT, LDC);
             gemm_nt<TI, C, BV, DK>(dU, Kd, LDK, dSs, LDK);
+            if (TX::active()) {
 #pragma unroll
-            for (int j = 0; j < TX::PER; ++j) {
-                if (!TX::valid(j)) continue;
+                for (int j = 0; j < TX::PER; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dUT[TX::col(j) * LDC + TX::row(j, i)] = from_f<TI>(dU[j][i]);
+                    for (int i = 0; i < 4; ++i) dUT[TX::col(j) * LDC + TX::row(j, i)] = from_f<TI>(dU[j][i]);
+                }
             }
         }
         __syncthreads();
@@ -137,37 +148,38 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
             gemm_nt<TI, C, BV, C>(L, TT, LDC, dUT, LDC);
             TI* __restrict__ lam = static_cast<TI*>(p.lam) + ((long)bh * p.NT + n) * C * DVr + v0;
             TI* __restrict__ dv = static_cast<TI*>(p.dv) + row0 * DVr + v0;
+            if (TX::active()) {
 #pragma unroll
-            for (int j = 0; j < TX::PER; ++j) {
-                if (!TX::valid(j)) continue;
+                for (int j = 0; j < TX::PER; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TX::row(j, i), c = TX::col(j);
-                    const float l = L[j][i];
-                    const float bl = beta_s[t] * l;
-                    lam[(long)t * DVr + c] = from_f<TI>(l);
-                    if (t < valid) dv[(long)t * DVr + c] = from_f<TI>(bl);
-                    bLT[c * LDC + t] = from_f<TI>(-bl);
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = TX::row(j, i), c = TX::col(j);
+                        const float l = L[j][i];
+                        const float bl = beta_s[t] * l;
+                        lam[(long)t * DVr + c] = from_f<TI>(l);
+                        if (t < valid) dv[(long)t * DVr + c] = from_f<TI>(bl);
+                        bLT[c * LDC + t] = from_f<TI>(-bl);
+                    }
                 }
             }
         }
         __syncthreads();
         // (e) dS0 = dS1 Diag(Gam_C) + dO^T (Q Gam) - (beta lambda)^T (K Gam)
+        if (GATE != kGateNone && TS::active()) {
 #pragma unroll
-        for (int j = 0; j < TS::PER; ++j) {
-            if (!TS::valid(j) || GATE == kGateNone) continue;
-            const float f = fexp(gl_at(TS::col(j)));
+            for (int j = 0; j < TS::PER; ++j) {
+                const float f = gf.GC(TS::col(j));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dS[j][i] *= f;
+                for (int i = 0; i < 4; ++i) dS[j][i] *= f;
+            }
         }
         gemm_nt<TI, BV, DK, C>(dS, dOT, LDC, QgT, LDC);
         gemm_nt<TI, BV, DK, C>(dS, bLT, LDC, KgT, LDC);
         __syncthreads();
     }
-    if (p.dh0) {
+    if (p.dh0 && TS::active()) {
 #pragma unroll
         for (int j = 0; j < TS::PER; ++j) {
-            if (!TS::valid(j)) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 p.dh0[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)] = dS[j][i];
@@ -220,10 +232,13 @@ struct BwdChunkSmem {
     static constexpr size_t GAM = al(F_END1);                        // gam  [C][GW]
     static constexpr size_t BETA = GAM + al(C * GW * 4);             // beta [C]
     static constexpr size_t RED_R = BETA + al(C * 4);                // row partials [D/16][C]
+    static constexpr int SPLIT = kThreads / D > 0 ? kThreads / D : 1;
+    static constexpr int REDC_ROWS = (C / 16) > SPLIT ? (C / 16) : SPLIT;
     static constexpr size_t RED_C = RED_R + al((D / 16) * C * 4);    // column partials [C/16][D]
-    static constexpr size_t LASTS = RED_C + al((C / 16) * D * 4);    // sum_v S0 dS1 per channel [D]
+    static constexpr size_t LASTS = RED_C + al(REDC_ROWS * D * 4);   // sum_v S0 dS1 per channel [D]
     static constexpr size_t DBR = LASTS + al(D * 4);                 // dbeta partial [C]
-    static constexpr size_t TOTAL = DBR + al(C * 4);
+    static constexpr size_t ROWF = DBR + al(C * 4);                  // scalar gate row factors [2][C]
+    static constexpr size_t TOTAL = ROWF + al(2 * C * 4);
     // d gam of the vector gate [C][D] fp32, written once every phase-C tile is dead
     static constexpr size_t DGB = BIG;
     static_assert(GATE != kGateVector || DGB + C * D * 4 <= TOTAL, "d gam buffer");
@@ -236,6 +251,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     using L = BwdChunkSmem<TI, GATE, C, D>;
     constexpr int LD = L::LD, LC = L::LC, GW = L::GW;
     constexpr bool VEC = GATE == kGateVector;
+    constexpr bool SCA = GATE == kGateScalar;
     __shared__ __align__(16) char smem[L::TOTAL];
     TI* lamb = reinterpret_cast<TI*>(smem + L::LAM);
     TI* Ub = reinterpret_cast<TI*>(smem + L::UB);
@@ -246,6 +262,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     float* red_c = reinterpret_cast<float*>(smem + L::RED_C);
     float* lastS = reinterpret_cast<float*>(smem + L::LASTS);
     float* dbr = reinterpret_cast<float*>(smem + L::DBR);
+    float* rowf = reinterpret_cast<float*>(smem + L::ROWF);   // scalar gate: e^{gam_t}, e^{gam_C - gam_t}
     float* dgb = reinterpret_cast<float*>(smem + L::DGB);
 
     const int n = blockIdx.x, bh = blockIdx.y;
@@ -261,53 +278,90 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     const TI* __restrict__ dS1g = static_cast<const TI*>(p.dS1) + chunk * D * D;
     const TI* __restrict__ lamg = static_cast<const TI*>(p.lam) + chunk * C * D;
 
-    load_gam_beta<GATE, C, D>(gam_s, beta_s, p.gam + row0 * GW, p.beta + row0, valid);
-    __syncthreads();
-    const float* gl = gam_s + (valid - 1) * GW;
-    auto gam_at = [&](int r, int c) -> float {
-        if (GATE == kGateNone) return 0.f;
-        return VEC ? gam_s[r * D + c] : gam_s[r];
-    };
-    auto gl_at = [&](int c) -> float {
-        if (GATE == kGateNone) return 0.f;
-        return VEC ? gl[c] : gl[0];
-    };
     using TO = Tiles<C, D>;   // every C x D output of this kernel uses this tile map
     using TCC = Tiles<C, C>;
 
-    // ---------------- phase A: X = (K Gam) S0^T, R, U = T R, dbeta_R
+    // ---------------- prologue: gate, beta, row factors, sum_v S0 dS1, k at this lane's elements
+    load_gam_beta<GATE, C, D>(gam_s, beta_s, p.gam + row0 * GW, p.beta + row0, valid);
+    {
+        // sum over v of S0[v][c] dS1[v][c] (gradient of S0 Diag(Gam_C) with respect to gam_C)
+        constexpr int SPLIT = kThreads / D > 0 ? kThreads / D : 1;
+        float* part = red_c;  // [SPLIT][D] scratch, consumed below before red_c is used again
+        for (int idx = threadIdx.x; idx < D * SPLIT; idx += kThreads) {
+            const int c = idx % D, h = idx / D;
+            float acc = 0.f;
+            for (int vv = h; vv < D; vv += SPLIT) acc += to_f(S0g[(long)vv * D + c]) * to_f(dS1g[(long)vv * D + c]);
+            part[h * D + c] = acc;
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < D; c += kThreads) {
+            float acc = 0.f;
+            for (int h = 0; h < SPLIT; ++h) acc += part[h * D + c];
+            lastS[c] = acc;
+        }
+    }
+    if (SCA) {
+        for (int t = threadIdx.x; t < C; t += kThreads) {
+            const float gl0 = gam_s[valid - 1];
+            rowf[t] = fexp(gam_s[t]);
+            rowf[C + t] = fexp(gl0 - gam_s[t]);
+        }
+    }
+    float kv[TO::PER][4];
+#pragma unroll
+    for (int j = 0; j < TO::PER; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = TO::row(j, i);
+            kv[j][i] = (TO::active() && t < valid) ? to_f(k[(long)t * D + TO::col(j)]) : 0.f;
+        }
+    __syncthreads();
+    const float* gl = gam_s + (valid - 1) * GW;
+    // per-element decay factors: Gm = e^{gam}, Gd = e^{gam_C - gam}; vector gate also
+    // fp = e^{gam - centre}, fm = e^{centre - gam} with centre = gam_C / 2
+    auto Gm = [&](int t, int c) -> float {
+        if (GATE == kGateNone) return 1.f;
+        return SCA ? rowf[t] : fexp(gam_s[t * D + c]);
+    };
+    auto Gd = [&](int t, int c) -> float {
+        if (GATE == kGateNone) return 1.f;
+        return SCA ? rowf[C + t] : fexp(gl[c] - gam_s[t * D + c]);
+    };
+
+    // ---------------- phase A: X = (K Gam) S0^T, R = beta (V - X), U = T R, dbeta_R
     {
         TI* Kg = reinterpret_cast<TI*>(smem + L::A_KG);
         TI* S0 = reinterpret_cast<TI*>(smem + L::A_S0);
         TI* RT = reinterpret_cast<TI*>(smem + L::A_RT);
         TI* Tl = reinterpret_cast<TI*>(smem + L::A_T);
-        if (GATE == kGateNone)
-            stage_copy<TI, C, D, false>(Kg, LD, k, D, valid);
+        if (VEC)
+            stage<TI, C, D, false>(Kg, LD, k, D, valid, [&](int r, int c, float x) { return x * fexp(gam_s[r * D + c]); });
         else
-            stage<TI, C, D, false>(Kg, LD, k, D, valid, [&](int r, int c, float x) { return x * fexp(gam_at(r, c)); });
+            stage_copy<TI, C, D, false>(Kg, LD, k, D, valid);   // scalar: Gam_t applied to X's rows
         stage_copy<TI, D, D, false>(S0, LD, S0g, D, D);
         stage_copy<TI, C, D, false>(lamb, LD, lamg, D, C);
-        stage_copy<TI, C, C, false>(Tl, LC, static_cast<const TI*>(p.Tm) + chunk * C * C, C, C);
+        stage_copy<TI, C, C, true>(Tl, LC, static_cast<const TI*>(p.Tm) + chunk * C * C, C, C);  // ws holds T^T
         __syncthreads();
         f32x4 X[TO::PER];
         zero_acc<C, D>(X);
         gemm_nt<TI, C, D, D>(X, Kg, LD, S0, LD);
+        if (TO::active()) {
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
-            float part[4];
+            for (int j = 0; j < TO::PER; ++j) {
+                float part[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TO::row(j, i), c = TO::col(j);
-                const float vv = t < valid ? to_f(v[(long)t * D + c]) : 0.f;
-                const float xr = vv - X[j][i];
-                part[i] = to_f(lamb[t * LD + c]) * xr;
-                RT[c * LC + t] = from_f<TI>(beta_s[t] * xr);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TO::row(j, i), c = TO::col(j);
+                    const float vv = t < valid ? to_f(v[(long)t * D + c]) : 0.f;
+                    const float xr = vv - (SCA ? rowf[t] : 1.f) * X[j][i];
+                    part[i] = to_f(lamb[t * LD + c]) * xr;
+                    RT[c * LC + t] = from_f<TI>(beta_s[t] * xr);
+                }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float s = row16_sum(part[i]);
-                if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s;
+                for (int i = 0; i < 4; ++i) {
+                    const float s = row16_sum(part[i]);
+                    if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s;
+                }
             }
         }
         __syncthreads();
@@ -320,19 +374,22 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         zero_acc<C, D>(U);
         gemm_nt<TI, C, D, C>(U, Tl, LC, RT, LC);
         __syncthreads();  // T (over dO) and RT dead after this point
+        if (TO::active()) {
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
+            for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Ub[TO::row(j, i) * LD + TO::col(j)] = from_f<TI>(U[j][i]);
+                for (int i = 0; i < 4; ++i) Ub[TO::row(j, i) * LD + TO::col(j)] = from_f<TI>(U[j][i]);
         }
     }
 
-    // ---------------- phase D: dQg = dO S0, dKg = -beta lambda S0, dKd = U dS1
-    f32x4 dq[TO::PER], dk[TO::PER], dgm[TO::PER];
+    // ---------------- phase D: dO S0, lambda S0, U dS1 (contractions over d_v)
+    // dq accumulates dL/dq, dk dL/dk, dkp the part of dL/dk reached through
+    // factors e^{+gam} (K Gam, K e^{gam - centre}); the rest of dk came through
+    // e^{-gam} factors, so d gam = q.dq + k.(2 dkp - dk) + the gam_C terms.
+    f32x4 dq[TO::PER], dk[TO::PER], dkp[TO::PER];
     zero_acc<C, D>(dq);
     zero_acc<C, D>(dk);
-    zero_acc<C, D>(dgm);
+    zero_acc<C, D>(dkp);
     {
         TI* S0T = reinterpret_cast<TI*>(smem + L::D_S0T);
         TI* dS1T = reinterpret_cast<TI*>(smem + L::D_DS1T);
@@ -340,62 +397,44 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         stage_copy<TI, D, D, true>(dS1T, LD, dS1g, D, D);
         stage_copy<TI, C, D, false>(dOb, LD, dO, D, valid);
         __syncthreads();
-        // sum_v S0[v][c] dS1[v][c] (the Gam_C gradient of S0 Diag(Gam_C))
-        for (int c = threadIdx.x; c < D; c += kThreads) {
-            float s = 0.f;
-            for (int vv = 0; vv < D; ++vv) s += to_f(S0T[c * LD + vv]) * to_f(dS1T[c * LD + vv]);
-            lastS[c] = s;
-        }
         f32x4 tmp[TO::PER];
         zero_acc<C, D>(tmp);
         gemm_nt<TI, C, D, D>(tmp, dOb, LD, S0T, LD);
+        if (TO::active()) {
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
+            for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TO::row(j, i), c = TO::col(j);
-                const float G = GATE == kGateNone ? 1.f : fexp(gam_at(t, c));
-                const float qq = t < valid ? to_f(q[(long)t * D + c]) : 0.f;
-                dq[j][i] = tmp[j][i] * G;
-                dgm[j][i] = tmp[j][i] * qq * G;
-            }
+                for (int i = 0; i < 4; ++i) dq[j][i] = tmp[j][i] * Gm(TO::row(j, i), TO::col(j));
         }
         zero_acc<C, D>(tmp);
         gemm_nt<TI, C, D, D>(tmp, lamb, LD, S0T, LD);
+        if (TO::active()) {
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
+            for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TO::row(j, i), c = TO::col(j);
-                const float G = GATE == kGateNone ? 1.f : fexp(gam_at(t, c));
-                const float kk = t < valid ? to_f(k[(long)t * D + c]) : 0.f;
-                const float dKg = -beta_s[t] * tmp[j][i];
-                dk[j][i] = dKg * G;
-                dgm[j][i] += dKg * kk * G;
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TO::row(j, i);
+                    const float x = -beta_s[t] * tmp[j][i] * Gm(t, TO::col(j));
+                    dk[j][i] = x;
+                    dkp[j][i] = x;
+                }
         }
         zero_acc<C, D>(tmp);
         gemm_nt<TI, C, D, D>(tmp, Ub, LD, dS1T, LD);
-        // column partial sums of Kd * dKd for the gam_C gradient
+        if (TO::active()) {
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
-            float colp = 0.f;
+            for (int j = 0; j < TO::PER; ++j) {
+                float colp = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TO::row(j, i), c = TO::col(j);
-                const float e = GATE == kGateNone ? 1.f : fexp(gl_at(c) - gam_at(t, c));
-                const float kk = t < valid ? to_f(k[(long)t * D + c]) : 0.f;
-                dk[j][i] += tmp[j][i] * e;
-                const float kd = kk * e * tmp[j][i];
-                dgm[j][i] -= kd;
-                colp += kd;
+                for (int i = 0; i < 4; ++i) {
+                    const float x = tmp[j][i] * Gd(TO::row(j, i), TO::col(j));
+                    dk[j][i] += x;
+                    colp += kv[j][i] * x;   // Kd * dKd, summed over rows for the gam_C term
+                }
+                colp += __shfl_xor(colp, 16);
+                colp += __shfl_xor(colp, 32);
+                if (lane_id() < 16) red_c[(TO::m0(j) / 16) * D + TO::col(j)] = colp;
             }
-            colp += __shfl_xor(colp, 16);
-            colp += __shfl_xor(colp, 32);
-            if (lane_id() < 16) red_c[(TO::m0(j) / 16) * D + TO::col(j)] = colp;
         }
         __syncthreads();  // S0T / dS1T dead
     }
@@ -407,40 +446,40 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         TI* dP = reinterpret_cast<TI*>(smem + L::B_DP);
         TI* dPT = reinterpret_cast<TI*>(smem + L::B_DPT);
         f32x4 acc[TCC::PER];
+        if (TCC::active()) {
 #pragma unroll
-        for (int j = 0; j < TCC::PER; ++j) {
-            if (!TCC::valid(j)) continue;
-            const bool upper = TCC::n0(j) > TCC::m0(j);
-            acc[j] = zero4();
-            if (!upper) acc[j] = tile_nt<TI, D>(lamb + TCC::m0(j) * LD, LD, Ub + TCC::n0(j) * LD, LD, acc[j]);
+            for (int j = 0; j < TCC::PER; ++j) {
+                const bool upper = TCC::n0(j) > TCC::m0(j);
+                acc[j] = zero4();
+                if (!upper) acc[j] = tile_nt<TI, D>(lamb + TCC::m0(j) * LD, LD, Ub + TCC::n0(j) * LD, LD, acc[j]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TCC::row(j, i), s = TCC::col(j);
-                float a = 0.f;
-                if (s < t) {
-                    a = -acc[j][i];  // dA = -lambda U^T
-                    if (GATE == kGateScalar) a *= fexp(gam_s[t] - gam_s[s]);
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TCC::row(j, i), s = TCC::col(j);
+                    float a = 0.f;
+                    if (s < t) {
+                        a = -acc[j][i];  // dA = -lambda U^T
+                        if (SCA) a *= fexp(gam_s[t] - gam_s[s]);
+                    }
+                    dA[t * LC + s] = from_f<TI>(a);
+                    dAT[s * LC + t] = from_f<TI>(beta_s[t] * a);
                 }
-                dA[t * LC + s] = from_f<TI>(a);
-                dAT[s * LC + t] = from_f<TI>(beta_s[t] * a);
             }
-        }
 #pragma unroll
-        for (int j = 0; j < TCC::PER; ++j) {
-            if (!TCC::valid(j)) continue;
-            const bool upper = TCC::n0(j) > TCC::m0(j);
-            acc[j] = zero4();
-            if (!upper) acc[j] = tile_nt<TI, D>(dOb + TCC::m0(j) * LD, LD, Ub + TCC::n0(j) * LD, LD, acc[j]);
+            for (int j = 0; j < TCC::PER; ++j) {
+                const bool upper = TCC::n0(j) > TCC::m0(j);
+                acc[j] = zero4();
+                if (!upper) acc[j] = tile_nt<TI, D>(dOb + TCC::m0(j) * LD, LD, Ub + TCC::n0(j) * LD, LD, acc[j]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TCC::row(j, i), s = TCC::col(j);
-                float a = 0.f;
-                if (s <= t) {
-                    a = acc[j][i];
-                    if (GATE == kGateScalar) a *= fexp(gam_s[t] - gam_s[s]);
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TCC::row(j, i), s = TCC::col(j);
+                    float a = 0.f;
+                    if (s <= t) {
+                        a = acc[j][i];
+                        if (SCA) a *= fexp(gam_s[t] - gam_s[s]);
+                    }
+                    dP[t * LC + s] = from_f<TI>(a);
+                    dPT[s * LC + t] = from_f<TI>(a);
                 }
-                dP[t * LC + s] = from_f<TI>(a);
-                dPT[s * LC + t] = from_f<TI>(a);
             }
         }
         __syncthreads();  // lambda, U, dO dead
@@ -456,93 +495,86 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         TI* KlT = VEC ? reinterpret_cast<TI*>(smem + L::C_KLT) : KrT;
         TI* QlT = reinterpret_cast<TI*>(smem + L::C_QLT);
         if (VEC) {
-            stage<TI, C, D, true>(KrT, LC, k, D, valid,
-                                  [&](int r, int c, float x) { return x * fexp(0.5f * gl[c] - gam_s[r * D + c]); });
-            stage<TI, C, D, true>(KlT, LC, k, D, valid,
-                                  [&](int r, int c, float x) { return x * fexp(gam_s[r * D + c] - 0.5f * gl[c]); });
-            stage<TI, C, D, true>(QlT, LC, q, D, valid,
-                                  [&](int r, int c, float x) { return x * fexp(gam_s[r * D + c] - 0.5f * gl[c]); });
+            stage_t<TI, C, D>(KrT, LC, k, D, valid,
+                              [&](int r, int c, float x) { return x * fexp(0.5f * gl[c] - gam_s[r * D + c]); });
+            stage_t<TI, C, D>(KlT, LC, k, D, valid,
+                              [&](int r, int c, float x) { return x * fexp(gam_s[r * D + c] - 0.5f * gl[c]); });
+            stage_t<TI, C, D>(QlT, LC, q, D, valid,
+                              [&](int r, int c, float x) { return x * fexp(gam_s[r * D + c] - 0.5f * gl[c]); });
         } else {
             stage_copy<TI, C, D, true>(KrT, LC, k, D, valid);
             stage_copy<TI, C, D, true>(QlT, LC, q, D, valid);
         }
         __syncthreads();
+        auto fpl = [&](int t, int c) -> float { return VEC ? fexp(gam_s[t * D + c] - 0.5f * gl[c]) : 1.f; };
         float dbA[TO::PER][4];
         f32x4 tmp[TO::PER];
         // Y = dA~ Kr :  dK+ = beta Y, dbeta_A = sum_c K+ Y
         zero_acc<C, D>(tmp);
         gemm_nt<TI, C, D, C>(tmp, dA, LC, KrT, LC);
+        if (TO::active()) {
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
+            for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TO::row(j, i), c = TO::col(j);
-                const float kk = t < valid ? to_f(k[(long)t * D + c]) : 0.f;
-                const float fp = VEC ? fexp(gam_s[t * D + c] - 0.5f * gl[c]) : 1.f;
-                const float kp = kk * fp;
-                const float y = tmp[j][i];
-                dbA[j][i] = kp * y;
-                dk[j][i] += beta_s[t] * y * fp;
-                dgm[j][i] += kp * beta_s[t] * y;
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TO::row(j, i);
+                    const float fp = fpl(t, TO::col(j));
+                    const float y = tmp[j][i];
+                    dbA[j][i] = kv[j][i] * fp * y;
+                    const float x = beta_s[t] * y * fp;
+                    dk[j][i] += x;
+                    dkp[j][i] += x;
+                }
         }
-        // Z = (beta dA~)^T Kl :  dK- += Z
+        // Z = (beta dA~)^T Kl and W = dP~^T Ql : both reach k through e^{-gam}
         zero_acc<C, D>(tmp);
         gemm_nt<TI, C, D, C>(tmp, dAT, LC, KlT, LC);
-        // W = dP~^T Ql :  dK- += W
         gemm_nt<TI, C, D, C>(tmp, dPT, LC, QlT, LC);
+        if (TO::active()) {
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
+            for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TO::row(j, i), c = TO::col(j);
-                const float kk = t < valid ? to_f(k[(long)t * D + c]) : 0.f;
-                const float fm = VEC ? fexp(0.5f * gl[c] - gam_s[t * D + c]) : 1.f;
-                dk[j][i] += tmp[j][i] * fm;
-                dgm[j][i] -= kk * fm * tmp[j][i];
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const float fm = VEC ? 1.f / fpl(TO::row(j, i), TO::col(j)) : 1.f;
+                    dk[j][i] += tmp[j][i] * fm;
+                }
         }
         // dQ+ = dP~ Kr
         zero_acc<C, D>(tmp);
         gemm_nt<TI, C, D, C>(tmp, dP, LC, KrT, LC);
+        if (TO::active()) {
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
+            for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TO::row(j, i), c = TO::col(j);
-                const float qq = t < valid ? to_f(q[(long)t * D + c]) : 0.f;
-                const float fp = VEC ? fexp(gam_s[t * D + c] - 0.5f * gl[c]) : 1.f;
-                dq[j][i] += tmp[j][i] * fp;
-                dgm[j][i] += qq * fp * tmp[j][i];
-            }
+                for (int i = 0; i < 4; ++i) dq[j][i] += tmp[j][i] * fpl(TO::row(j, i), TO::col(j));
         }
+
         // -------- finish: dq, dk, dbeta, dg
         TI* __restrict__ dqo = static_cast<TI*>(p.dq) + row0 * D;
         TI* __restrict__ dko = static_cast<TI*>(p.dk) + row0 * D;
+        float dgm[TO::PER][4];
+        if (TO::active()) {
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
+            for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TO::row(j, i), c = TO::col(j);
-                if (t < valid) {
-                    dqo[(long)t * D + c] = from_f<TI>(dq[j][i]);
-                    dko[(long)t * D + c] = from_f<TI>(dk[j][i]);
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TO::row(j, i), c = TO::col(j);
+                    float qq = 0.f;
+                    if (t < valid) {
+                        dqo[(long)t * D + c] = from_f<TI>(dq[j][i]);
+                        dko[(long)t * D + c] = from_f<TI>(dk[j][i]);
+                        if (GATE != kGateNone) qq = to_f(q[(long)t * D + c]);
+                    }
+                    dgm[j][i] = qq * dq[j][i] + kv[j][i] * (2.f * dkp[j][i] - dk[j][i]);
                 }
-            }
-        }
-        // dbeta = dbeta_R + rowsum(K+ Y)
+            // dbeta = dbeta_R + rowsum(K+ Y)
 #pragma unroll
-        for (int j = 0; j < TO::PER; ++j) {
-            if (!TO::valid(j)) continue;
+            for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float s = row16_sum(dbA[j][i]);
-                if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s;
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const float s = row16_sum(dbA[j][i]);
+                    if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s;
+                }
         }
         __syncthreads();
         for (int t = threadIdx.x; t < valid; t += kThreads) {
@@ -554,11 +586,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         __syncthreads();
         // d gam: elementwise terms + the gam_C terms on the last valid row
         if (VEC) {
+            if (TO::active()) {
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j) {
-                if (!TO::valid(j)) continue;
+                for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dgb[TO::row(j, i) * D + TO::col(j)] = dgm[j][i];
+                    for (int i = 0; i < 4; ++i) dgb[TO::row(j, i) * D + TO::col(j)] = dgm[j][i];
             }
             __syncthreads();
             for (int c = threadIdx.x; c < D; c += kThreads) {
@@ -571,18 +603,18 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 }
             }
         } else {
+            if (TO::active()) {
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j) {
-                if (!TO::valid(j)) continue;
+                for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float s = row16_sum(dgm[j][i]);
-                    if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s;
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        const float s = row16_sum(dgm[j][i]);
+                        if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s;
+                    }
             }
             __syncthreads();
             if (wave_id() == 0) {
-                // last-row total: sum_c (Gam_C lastS[c] + column partials)
+                // last-row total: sum_c (Gam_C lastS[c] + column partials of Kd dKd)
                 float part = 0.f;
                 for (int c = lane_id(); c < D; c += 64) {
                     float x = fexp(gl[0]) * lastS[c];

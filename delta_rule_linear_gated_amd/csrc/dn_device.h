@@ -43,38 +43,53 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // ---------------------------------------------------------------------------
-// One K-step of a 16x16 tile.  a/b point at the tile's first row, at column k0.
+// One K-step of a 16x16 tile: load() fetches this lane's fragment of a tile
+// whose first row is at p (row stride ld, at column k0 already), op() is the
+// MFMA.  step() = both.
 template <typename T, int KS> struct Mma;
 
 template <> struct Mma<bf16, 32> {
     static constexpr int kStep = 32;
-    __device__ __forceinline__ static f32x4 step(const bf16* a, int lda, const bf16* b, int ldb,
-                                                 f32x4 acc) {
+    typedef bf16x8 Frag;
+    __device__ __forceinline__ static Frag load(const bf16* p, int ld) {
         const int l = lane_id();
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(a + (l & 15) * lda + 8 * (l >> 4));
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(b + (l & 15) * ldb + 8 * (l >> 4));
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+        return *reinterpret_cast<const bf16x8*>(p + (l & 15) * ld + 8 * (l >> 4));
+    }
+    __device__ __forceinline__ static f32x4 op(Frag a, Frag b, f32x4 acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 step(const bf16* a, int lda, const bf16* b, int ldb, f32x4 acc) {
+        return op(load(a, lda), load(b, ldb), acc);
     }
 };
 
 template <> struct Mma<bf16, 16> {
     static constexpr int kStep = 16;
-    __device__ __forceinline__ static f32x4 step(const bf16* a, int lda, const bf16* b, int ldb,
-                                                 f32x4 acc) {
+    typedef i16x4 Frag;
+    __device__ __forceinline__ static Frag load(const bf16* p, int ld) {
         const int l = lane_id();
-        const i16x4 av = *reinterpret_cast<const i16x4*>(a + (l & 15) * lda + 4 * (l >> 4));
-        const i16x4 bv = *reinterpret_cast<const i16x4*>(b + (l & 15) * ldb + 4 * (l >> 4));
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+        return *reinterpret_cast<const i16x4*>(p + (l & 15) * ld + 4 * (l >> 4));
+    }
+    __device__ __forceinline__ static f32x4 op(Frag a, Frag b, f32x4 acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 step(const bf16* a, int lda, const bf16* b, int ldb, f32x4 acc) {
+        return op(load(a, lda), load(b, ldb), acc);
     }
 };
 
 template <> struct Mma<float, 4> {
     static constexpr int kStep = 4;
-    __device__ __forceinline__ static f32x4 step(const float* a, int lda, const float* b, int ldb,
-                                                 f32x4 acc) {
+    typedef float Frag;
+    __device__ __forceinline__ static Frag load(const float* p, int ld) {
         const int l = lane_id();
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(a[(l & 15) * lda + (l >> 4)],
-                                                    b[(l & 15) * ldb + (l >> 4)], acc, 0, 0, 0);
+        return p[(l & 15) * ld + (l >> 4)];
+    }
+    __device__ __forceinline__ static f32x4 op(Frag a, Frag b, f32x4 acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 step(const float* a, int lda, const float* b, int ldb, f32x4 acc) {
+        return op(load(a, lda), load(b, ldb), acc);
     }
 };
 
@@ -107,16 +122,33 @@ __device__ __forceinline__ f32x4 tile_nt(const T* A, int lda, const T* B, int ld
     }
 }
 
-// Static distribution of the 16x16 tiles of an M x N output over the 4 waves:
-// wave w owns tiles w, w + 4, w + 8, ... (row-major tile order).
+// Static distribution of the 16x16 tiles of an M x N output over the 4 waves.
+// The waves form a WM x WN grid; each owns an RM x RN block of tiles, so one
+// K step loads RM A-fragments and RN B-fragments for RM*RN MFMAs.  Outputs of
+// fewer than 4 tiles give one tile to each of the first waves.
 template <int M, int N> struct Tiles {
     static_assert(M % 16 == 0 && N % 16 == 0, "tile dims");
     static constexpr int TM = M / 16, TN = N / 16, NT = TM * TN;
-    static constexpr int PER = (NT + kWaves - 1) / kWaves;
-    __device__ __forceinline__ static int tile(int j) { return wave_id() + kWaves * j; }
-    __device__ __forceinline__ static bool valid(int j) { return tile(j) < NT; }
-    __device__ __forceinline__ static int m0(int j) { return (tile(j) / TN) * 16; }
-    __device__ __forceinline__ static int n0(int j) { return (tile(j) % TN) * 16; }
+    static constexpr int pick_wm() {
+        if (NT < kWaves) return TM;
+        int best = 0, cost = 1 << 30;
+        for (int wm = 1; wm <= kWaves; wm *= 2) {
+            const int wn = kWaves / wm;
+            if (TM % wm || TN % wn) continue;
+            const int c = TM / wm + TN / wn;
+            if (c < cost) { cost = c; best = wm; }
+        }
+        return best;
+    }
+    static constexpr int WM = pick_wm();
+    static constexpr int WN = NT < kWaves ? TN : kWaves / WM;
+    static constexpr int RM = TM / WM, RN = TN / WN;
+    static constexpr int PER = RM * RN;
+    static_assert(WM > 0 && WM * WN <= kWaves && RM * WM == TM && RN * WN == TN, "tile grid");
+    __device__ __forceinline__ static bool active() { return wave_id() < WM * WN; }
+    __device__ __forceinline__ static bool valid(int) { return active(); }
+    __device__ __forceinline__ static int m0(int j) { return ((wave_id() / WN) * RM + j / RN) * 16; }
+    __device__ __forceinline__ static int n0(int j) { return ((wave_id() % WN) * RN + j % RN) * 16; }
     // row / column of accumulator element i of this lane
     __device__ __forceinline__ static int row(int j, int i) { return m0(j) + 4 * (lane_id() >> 4) + i; }
     __device__ __forceinline__ static int col(int j) { return n0(j) + (lane_id() & 15); }
@@ -126,10 +158,30 @@ template <int M, int N> struct Tiles {
 template <typename T, int M, int N, int K, int NACC>
 __device__ __forceinline__ void gemm_nt(f32x4 (&acc)[NACC], const T* A, int lda, const T* B, int ldb) {
     using TL = Tiles<M, N>;
+    using MM = typename MmaFor<T, K>::type;
     static_assert(NACC == TL::PER, "accumulator count");
+    if (!TL::active()) return;
+    const T* a0 = A + TL::m0(0) * lda;
+    const T* b0 = B + TL::n0(0) * ldb;
+    if constexpr (sizeof(T) == 2 && MM::kStep == 16) {
+        // see tile_nt: 16x16x16 chains never inherit another shape's accumulator
 #pragma unroll
-    for (int j = 0; j < TL::PER; ++j) {
-        if (TL::valid(j)) acc[j] = tile_nt<T, K>(A + TL::m0(j) * lda, lda, B + TL::n0(j) * ldb, ldb, acc[j]);
+        for (int j = 0; j < NACC; ++j)
+            acc[j] = tile_nt<T, K>(A + TL::m0(j) * lda, lda, B + TL::n0(j) * ldb, ldb, acc[j]);
+    } else {
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += MM::kStep) {
+            typename MM::Frag fa[TL::RM], fb[TL::RN];
+#pragma unroll
+            for (int im = 0; im < TL::RM; ++im) fa[im] = MM::load(a0 + im * 16 * lda + k0, lda);
+#pragma unroll
+            for (int in = 0; in < TL::RN; ++in) fb[in] = MM::load(b0 + in * 16 * ldb + k0, ldb);
+#pragma unroll
+            for (int im = 0; im < TL::RM; ++im)
+#pragma unroll
+                for (int in = 0; in < TL::RN; ++in)
+                    acc[im * TL::RN + in] = MM::op(fa[im], fb[in], acc[im * TL::RN + in]);
+        }
     }
 }
 
@@ -143,10 +195,19 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NACC]) {
 // ---------------------------------------------------------------------------
 // Global -> LDS staging of a ROWS x COLS row-major tile (global row stride gld),
 // rows >= valid_rows are zero.  f(r, c, x) maps each value (as float) before it
-// is rounded to T.  TRANS stores lds[c * ldl + r] instead of lds[r * ldl + c].
+// is rounded to T.  TRANS stores lds[c * ldl + r] instead of lds[r * ldl + c]
+// (through stage_t below).
+template <typename T, int ROWS, int COLS, class F>
+__device__ __forceinline__ void stage_t(T* lds, int ldl, const T* __restrict__ g, long gld, int valid_rows,
+                                        F f);
+
 template <typename T, int ROWS, int COLS, bool TRANS, class F>
 __device__ __forceinline__ void stage(T* lds, int ldl, const T* __restrict__ g, long gld,
                                       int valid_rows, F f) {
+    if constexpr (TRANS) {
+        stage_t<T, ROWS, COLS>(lds, ldl, g, gld, valid_rows, f);
+        return;
+    }
     constexpr int VW = 16 / sizeof(T);
     static_assert(COLS % VW == 0, "cols");
     constexpr int NV = ROWS * COLS / VW;
@@ -163,11 +224,43 @@ __device__ __forceinline__ void stage(T* lds, int ldl, const T* __restrict__ g, 
 #pragma unroll
             for (int e = 0; e < VW; ++e) vals[e] = from_f<T>(0.f);
         }
-        if (!TRANS) {
-            *reinterpret_cast<uint4*>(lds + r * ldl + c0) = *reinterpret_cast<const uint4*>(vals);
-        } else {
+        *reinterpret_cast<uint4*>(lds + r * ldl + c0) = *reinterpret_cast<const uint4*>(vals);
+    }
+}
+
+// Transposing staging: lds[c * ldl + r] = f(r, c, g[r * gld + c]) for a
+// ROWS x COLS row-major global tile.  Each thread moves one VW x VW block
+// (VW = 16 bytes of elements): VW 16-byte row loads, a register transpose, VW
+// 16-byte LDS stores.  Lanes walk the row blocks first, so one load instruction
+// reads whole 128-byte row segments and one store instruction writes
+// consecutive 16-byte pieces of an LDS row.  Rows >= valid_rows read as zero.
+template <typename T, int ROWS, int COLS, class F>
+__device__ __forceinline__ void stage_t(T* lds, int ldl, const T* __restrict__ g, long gld, int valid_rows,
+                                        F f) {
+    constexpr int VW = 16 / sizeof(T);
+    static_assert(ROWS % VW == 0 && COLS % VW == 0, "block");
+    constexpr int BR = ROWS / VW, BC = COLS / VW, NB = BR * BC;
+    for (int b = threadIdx.x; b < NB; b += kThreads) {
+        const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+        T v[VW][VW];
 #pragma unroll
-            for (int e = 0; e < VW; ++e) lds[(c0 + e) * ldl + r] = vals[e];
+        for (int i = 0; i < VW; ++i) {
+            if (r0 + i < valid_rows) {
+                const uint4 raw = *reinterpret_cast<const uint4*>(g + (long)(r0 + i) * gld + c0);
+                const T* src = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+                for (int e = 0; e < VW; ++e) v[i][e] = src[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VW; ++e) v[i][e] = from_f<T>(0.f);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VW; ++e) {
+            T out[VW];
+#pragma unroll
+            for (int i = 0; i < VW; ++i) out[i] = from_f<T>(f(r0 + i, c0 + e, to_f(v[i][e])));
+            *reinterpret_cast<uint4*>(lds + (c0 + e) * ldl + r0) = *reinterpret_cast<const uint4*>(out);
         }
     }
 }
@@ -180,8 +273,123 @@ struct Identity {
 template <typename T, int ROWS, int COLS, bool TRANS>
 __device__ __forceinline__ void stage_copy(T* lds, int ldl, const T* __restrict__ g, long gld,
                                            int valid_rows) {
-    stage<T, ROWS, COLS, TRANS>(lds, ldl, g, gld, valid_rows, Identity());
+    if constexpr (TRANS)
+        stage_t<T, ROWS, COLS>(lds, ldl, g, gld, valid_rows, Identity());
+    else
+        stage<T, ROWS, COLS, false>(lds, ldl, g, gld, valid_rows, Identity());
 }
+
+// ---------------------------------------------------------------------------
+// Register-staged tiles: load() issues every global load of a tile at once
+// (no waits), a later store*() maps, rounds and writes it to LDS.  Issuing the
+// loads of the next chunk before computing the current one hides their latency.
+//
+// RegN: row-major thread mapping (16-byte vectors, consecutive lanes along a
+// row), for natural-layout stores.
+template <typename T, int ROWS, int COLS> struct RegN {
+    static constexpr int VW = 16 / sizeof(T), VPR = COLS / VW, NV = ROWS * VPR;
+    static constexpr int PER = (NV + kThreads - 1) / kThreads;
+    static_assert(COLS % VW == 0, "cols");
+    uint4 r[PER];
+    // rows >= valid are zero
+    __device__ __forceinline__ void load(const T* __restrict__ g, long gld, int valid) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            const int row = idx / VPR, c0 = (idx % VPR) * VW;
+            r[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (idx < NV && row < valid) r[i] = *reinterpret_cast<const uint4*>(g + row * gld + c0);
+        }
+    }
+    // rows >= valid repeat row valid - 1 (for cumulative quantities)
+    __device__ __forceinline__ void load_clamped(const T* __restrict__ g, long gld, int valid) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            const int row = idx / VPR, c0 = (idx % VPR) * VW;
+            r[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (idx < NV) r[i] = *reinterpret_cast<const uint4*>(g + (row < valid ? row : valid - 1) * gld + c0);
+        }
+    }
+    template <class F> __device__ __forceinline__ void store(T* lds, int ldl, F f) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            if (idx >= NV) continue;
+            const int row = idx / VPR, c0 = (idx % VPR) * VW;
+            const T* src = reinterpret_cast<const T*>(&r[i]);
+            T out[VW];
+#pragma unroll
+            for (int e = 0; e < VW; ++e) out[e] = from_f<T>(f(row, c0 + e, to_f(src[e])));
+            *reinterpret_cast<uint4*>(lds + row * ldl + c0) = *reinterpret_cast<const uint4*>(out);
+        }
+    }
+    __device__ __forceinline__ void store(T* lds, int ldl) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            if (idx >= NV) continue;
+            const int row = idx / VPR, c0 = (idx % VPR) * VW;
+            *reinterpret_cast<uint4*>(lds + row * ldl + c0) = r[i];
+        }
+    }
+};
+
+// RegB: VW x VW blocks per thread (lanes walk row blocks first), for
+// transposed stores (register transpose) and, when the same data is also
+// needed untransposed, natural stores from the same registers.
+template <typename T, int ROWS, int COLS> struct RegB {
+    static constexpr int VW = 16 / sizeof(T), BR = ROWS / VW, BC = COLS / VW, NB = BR * BC;
+    static constexpr int PER = (NB + kThreads - 1) / kThreads;
+    static_assert(ROWS % VW == 0 && COLS % VW == 0, "block");
+    uint4 r[PER][VW];
+    __device__ __forceinline__ void load(const T* __restrict__ g, long gld, int valid) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int b = threadIdx.x + i * kThreads;
+            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                r[i][e] = make_uint4(0u, 0u, 0u, 0u);
+                if (b < NB && r0 + e < valid) r[i][e] = *reinterpret_cast<const uint4*>(g + (r0 + e) * gld + c0);
+            }
+        }
+    }
+    // lds[c * ldl + r] = f(r, c, x)
+    template <class F> __device__ __forceinline__ void store_t(T* lds, int ldl, F f) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int b = threadIdx.x + i * kThreads;
+            if (b >= NB) continue;
+            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                T out[VW];
+#pragma unroll
+                for (int k = 0; k < VW; ++k)
+                    out[k] = from_f<T>(f(r0 + k, c0 + e, to_f(reinterpret_cast<const T*>(&r[i][k])[e])));
+                *reinterpret_cast<uint4*>(lds + (c0 + e) * ldl + r0) = *reinterpret_cast<const uint4*>(out);
+            }
+        }
+    }
+    // lds[r * ldl + c] = f(r, c, x)
+    template <class F> __device__ __forceinline__ void store_n(T* lds, int ldl, F f) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int b = threadIdx.x + i * kThreads;
+            if (b >= NB) continue;
+            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                const T* src = reinterpret_cast<const T*>(&r[i][e]);
+                T out[VW];
+#pragma unroll
+                for (int k = 0; k < VW; ++k) out[k] = from_f<T>(f(r0 + e, c0 + k, to_f(src[k])));
+                *reinterpret_cast<uint4*>(lds + (r0 + e) * ldl + c0) = *reinterpret_cast<const uint4*>(out);
+            }
+        }
+    }
+};
 
 // Sum over the 16 lanes that share (lane >> 4): the lanes holding one output row.
 __device__ __forceinline__ float row16_sum(float x) {

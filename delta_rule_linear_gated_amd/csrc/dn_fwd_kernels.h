@@ -26,6 +26,8 @@
 // the centred contraction of the ReWY abstract).
 #pragma once
 
+#include <type_traits>
+
 #include "dn_device.h"
 #include "dn_internal.h"
 
@@ -51,8 +53,9 @@ __device__ __forceinline__ void load_gam_beta(float* gam_s, float* beta_s, const
 }
 
 // ---------------------------------------------------------------------------
-// prep_kernel: grid (NT, BH), one chunk per workgroup.
-template <typename TI, int GATE, int C, int DK>
+// prep_kernel: grid (NT, BH), one chunk per workgroup.  TRANS_OUT stores T^T
+// and P^T instead of T and P (the layout the reverse pass reads).
+template <typename TI, int GATE, int C, int DK, bool TRANS_OUT>
 __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
     constexpr int LDK = DK + Pad<TI>::value;
     constexpr int LDA = C + 4;
@@ -156,7 +159,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
                     pv = acc[j][i];
                     if (GATE == kGateScalar) pv *= fexp(gam_s[t] - gam_s[s]);
                 }
-                Pout[t * C + s] = from_f<TI>(pv);
+                if (TRANS_OUT)
+                    Pout[s * C + t] = from_f<TI>(pv);
+                else
+                    Pout[t * C + s] = from_f<TI>(pv);
             }
         }
     }
@@ -176,18 +182,80 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
         }
         if (c < C) {
             TI* __restrict__ Tout = static_cast<TI*>(p.Tm) + ((long)bh * p.NT + n) * C * C;
+            if (TRANS_OUT) {
 #pragma unroll
-            for (int i = 0; i < C; ++i) Tout[i * C + c] = from_f<TI>(x[i]);
+                for (int i = 0; i < C; ++i) Tout[c * C + i] = from_f<TI>(x[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < C; ++i) Tout[i * C + c] = from_f<TI>(x[i]);
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
+// Per-chunk gate data held in registers between prefetch and commit, and the
+// decay factors it leaves in LDS:
+//   scalar gate: rowf[t] = e^{gam_t}, rowf[C + t] = e^{gam_C - gam_t}
+//   vector gate: gam_s[t][c] (factors computed per element from it)
+template <int GATE, int C, int DK> struct GateRegs {
+    static constexpr bool VEC = GATE == kGateVector;
+    RegN<float, VEC ? C : 4, VEC ? DK : 4> gv;   // vector gate: the chunk's gam rows
+    float gs = 0.f, gC = 0.f, b = 0.f;          // scalar gate: gam_t, gam_C; beta_t (thread t < C)
+    __device__ __forceinline__ void load(const float* __restrict__ gam, const float* __restrict__ beta,
+                                         int valid) {
+        const int t = threadIdx.x;
+        if (t < C) b = t < valid ? beta[t] : 0.f;
+        if (GATE == kGateScalar && t < C) {
+            gs = gam[t < valid ? t : valid - 1];
+            gC = gam[valid - 1];
+        }
+        if (VEC) gv.load_clamped(gam, DK, valid);
+    }
+    __device__ __forceinline__ void commit(float* rowf, float* gam_s, float* beta_s) const {
+        const int t = threadIdx.x;
+        if (t < C) beta_s[t] = b;
+        if (GATE == kGateScalar && t < C) {
+            rowf[t] = fexp(gs);
+            rowf[C + t] = fexp(gC - gs);
+        }
+        if (VEC) gv.store(gam_s, DK);
+    }
+};
+
+// Decay factors read back from LDS after GateRegs::commit.
+template <int GATE, int C, int DK> struct GateLds {
+    const float* rowf;
+    const float* gam_s;
+    int last;  // valid - 1
+    // e^{gam[t][c]}
+    __device__ __forceinline__ float G(int t, int c) const {
+        if (GATE == kGateNone) return 1.f;
+        if (GATE == kGateScalar) return rowf[t];
+        return fexp(gam_s[t * DK + c]);
+    }
+    // e^{gam_C[c] - gam[t][c]}
+    __device__ __forceinline__ float Gd(int t, int c) const {
+        if (GATE == kGateNone) return 1.f;
+        if (GATE == kGateScalar) return rowf[C + t];
+        return fexp(gam_s[last * DK + c] - gam_s[t * DK + c]);
+    }
+    // e^{gam_C[c]}
+    __device__ __forceinline__ float GC(int c) const {
+        if (GATE == kGateNone) return 1.f;
+        if (GATE == kGateScalar) return rowf[last];
+        return fexp(gam_s[last * DK + c]);
+    }
+};
+
+// ---------------------------------------------------------------------------
 // fwd_state_kernel: grid (DV / BV, BH).  Walks the chunks of one head in order
 // for one block of BV state rows (rows of S are independent: each row only
-// mixes with itself through the key dimension).
-//   SAVE    : write the bf16/fp32 state entering each chunk to p.states
-//   OUTPUT  : write O and hT (off for the recompute pass of the backward)
+// mixes with itself through the key dimension).  The global tiles of chunk
+// n + 1 are loaded into registers while chunk n is computed.
+//   SAVE    : write the state entering each chunk (I/O type) to p.states
+//   OUTPUT  : write O and hT.  Off for the recompute pass of the backward, where
+//             the workspace holds T^T (and P is not needed).
 template <typename TI, int GATE, int C, int DK, int BV, bool SAVE, bool OUTPUT>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     constexpr int PAD = Pad<TI>::value;
@@ -195,9 +263,8 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     constexpr int LDC = C + PAD;
     constexpr int LDV = BV + PAD;
     constexpr int GW = GateLayout<GATE, DK>::GW;
-    constexpr int DV = 0;  // (unused; the runtime d_v is p.DVr)
-    (void)DV;
-    __shared__ float gam_s[C * GW];
+    __shared__ float gam_s[GATE == kGateVector ? C * DK : 4];
+    __shared__ float rowf[2 * C];
     __shared__ float beta_s[C];
     __shared__ __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
     __shared__ __align__(16) TI Qg[C * LDK];     // Q Gam            [t][c]
@@ -217,12 +284,33 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < TS::PER; ++j) {
         S[j] = zero4();
-        if (p.h0 && TS::valid(j)) {
+        if (p.h0 && TS::active()) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 S[j][i] = p.h0[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)];
         }
     }
+
+    // registers of the next chunk
+    RegN<TI, C, DK> rq;
+    RegB<TI, C, DK> rk;
+    RegN<TI, C, BV> rv;
+    std::conditional_t<OUTPUT, RegN<TI, C, C>, RegB<TI, C, C>> rT;
+    RegN<TI, OUTPUT ? C : 16, OUTPUT ? C : 16> rP;
+    GateRegs<GATE, C, DK> rg;
+    auto prefetch = [&](int n) {
+        const int t0 = n * C;
+        const int valid = min(C, p.T - t0);
+        const long row0 = (long)bh * p.T + t0;
+        const long cc = ((long)bh * p.NT + n) * C * C;
+        rg.load(p.gam + row0 * GW, p.beta + row0, valid);
+        rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
+        rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
+        rv.load(static_cast<const TI*>(p.v) + row0 * DVr + v0, DVr, valid);
+        rT.load(static_cast<const TI*>(p.Tm) + cc, C, C);
+        if constexpr (OUTPUT) rP.load(static_cast<const TI*>(p.Pm) + cc, C, C);
+    };
+    prefetch(0);
 
     for (int n = 0; n < p.NT; ++n) {
         const int t0 = n * C;
@@ -230,47 +318,40 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         const long row0 = (long)bh * p.T + t0;
         // (a) state operand (and the saved copy)
         TI* __restrict__ sv = SAVE ? static_cast<TI*>(p.states) + (((long)bh * p.NT + n) * DVr + v0) * DK : nullptr;
+        if (TS::active()) {
 #pragma unroll
-        for (int j = 0; j < TS::PER; ++j) {
-            if (!TS::valid(j)) continue;
+            for (int j = 0; j < TS::PER; ++j) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = TS::row(j, i), c = TS::col(j);
-                const TI x = from_f<TI>(S[j][i]);
-                Ss[r * LDK + c] = x;
-                if (SAVE) sv[r * DK + c] = x;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = TS::row(j, i), c = TS::col(j);
+                    const TI x = from_f<TI>(S[j][i]);
+                    Ss[r * LDK + c] = x;
+                    if (SAVE) sv[r * DK + c] = x;
+                }
             }
         }
-        // (b) chunk tiles
-        load_gam_beta<GATE, C, DK>(gam_s, beta_s, p.gam + row0 * GW, p.beta + row0, valid);
+        // (b) commit this chunk's tiles to LDS
+        rg.commit(rowf, gam_s, beta_s);
         __syncthreads();
-        const TI* __restrict__ q = static_cast<const TI*>(p.q) + row0 * DK;
-        const TI* __restrict__ k = static_cast<const TI*>(p.k) + row0 * DK;
-        const TI* __restrict__ v = static_cast<const TI*>(p.v) + row0 * DVr + v0;
-        const float* gl = gam_s + (valid - 1) * GW;
-        auto gam_at = [&](int r, int c) -> float {
-            if (GATE == kGateNone) return 0.f;
-            return GATE == kGateVector ? gam_s[r * DK + c] : gam_s[r];
-        };
-        auto gl_at = [&](int c) -> float {
-            if (GATE == kGateNone) return 0.f;
-            return GATE == kGateVector ? gl[c] : gl[0];
-        };
+        const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (GATE == kGateNone) {
-            stage_copy<TI, C, DK, false>(Qg, LDK, q, DK, valid);
-            stage_copy<TI, C, DK, false>(Kg, LDK, k, DK, valid);
-            stage_copy<TI, C, DK, true>(KdT, LDC, k, DK, valid);
+            rq.store(Qg, LDK);
+            rk.store_n(Kg, LDK, Identity());
+            rk.store_t(KdT, LDC, Identity());
         } else {
-            stage<TI, C, DK, false>(Qg, LDK, q, DK, valid, [&](int r, int c, float x) { return x * fexp(gam_at(r, c)); });
-            stage<TI, C, DK, false>(Kg, LDK, k, DK, valid, [&](int r, int c, float x) { return x * fexp(gam_at(r, c)); });
-            stage<TI, C, DK, true>(KdT, LDC, k, DK, valid,
-                                   [&](int r, int c, float x) { return x * fexp(gl_at(c) - gam_at(r, c)); });
+            rq.store(Qg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
+            rk.store_n(Kg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
+            rk.store_t(KdT, LDC, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
         }
-        stage_copy<TI, C, BV, false>(Vb, LDV, v, DVr, valid);
-        const long cc = ((long)bh * p.NT + n) * C * C;
-        stage_copy<TI, C, C, false>(Tl, LDC, static_cast<const TI*>(p.Tm) + cc, C, C);
-        stage_copy<TI, C, C, false>(Pl, LDC, static_cast<const TI*>(p.Pm) + cc, C, C);
+        rv.store(Vb, LDV);
+        if constexpr (OUTPUT) {
+            rT.store(Tl, LDC);
+            rP.store(Pl, LDC);
+        } else {
+            rT.store_t(Tl, LDC, Identity());
+        }
         __syncthreads();
+        if (n + 1 < p.NT) prefetch(n + 1);
 
         // (c) X = (K Gam) S0^T ;  R = diag(beta) (V - X)  -> R^T
         using TX = Tiles<C, BV>;
@@ -278,13 +359,14 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             f32x4 X[TX::PER];
             zero_acc<C, BV>(X);
             gemm_nt<TI, C, BV, DK>(X, Kg, LDK, Ss, LDK);
+            if (TX::active()) {
 #pragma unroll
-            for (int j = 0; j < TX::PER; ++j) {
-                if (!TX::valid(j)) continue;
+                for (int j = 0; j < TX::PER; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TX::row(j, i), c = TX::col(j);
-                    RT[c * LDC + t] = from_f<TI>(beta_s[t] * (to_f(Vb[t * LDV + c]) - X[j][i]));
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = TX::row(j, i), c = TX::col(j);
+                        RT[c * LDC + t] = from_f<TI>(beta_s[t] * (to_f(Vb[t * LDV + c]) - X[j][i]));
+                    }
                 }
             }
         }
@@ -294,11 +376,12 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             f32x4 U[TX::PER];
             zero_acc<C, BV>(U);
             gemm_nt<TI, C, BV, C>(U, Tl, LDC, RT, LDC);
+            if (TX::active()) {
 #pragma unroll
-            for (int j = 0; j < TX::PER; ++j) {
-                if (!TX::valid(j)) continue;
+                for (int j = 0; j < TX::PER; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) UT[TX::col(j) * LDC + TX::row(j, i)] = from_f<TI>(U[j][i]);
+                    for (int i = 0; i < 4; ++i) UT[TX::col(j) * LDC + TX::row(j, i)] = from_f<TI>(U[j][i]);
+                }
             }
         }
         __syncthreads();
@@ -309,22 +392,22 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             gemm_nt<TI, C, BV, DK>(O, Qg, LDK, Ss, LDK);
             gemm_nt<TI, C, BV, C>(O, Pl, LDC, UT, LDC);
             TI* __restrict__ o = static_cast<TI*>(p.o) + row0 * DVr + v0;
+            if (TX::active()) {
 #pragma unroll
-            for (int j = 0; j < TX::PER; ++j) {
-                if (!TX::valid(j)) continue;
+                for (int j = 0; j < TX::PER; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TX::row(j, i);
-                    if (t < valid) o[(long)t * DVr + TX::col(j)] = from_f<TI>(O[j][i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = TX::row(j, i);
+                        if (t < valid) o[(long)t * DVr + TX::col(j)] = from_f<TI>(O[j][i]);
+                    }
                 }
             }
         }
         // (f) S1 = S0 Diag(Gam_C) + U^T (K Gam_C / Gam)
+        if (GATE != kGateNone && TS::active()) {
 #pragma unroll
-        for (int j = 0; j < TS::PER; ++j) {
-            if (!TS::valid(j)) continue;
-            if (GATE != kGateNone) {
-                const float f = fexp(gl_at(TS::col(j)));
+            for (int j = 0; j < TS::PER; ++j) {
+                const float f = gf.GC(TS::col(j));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[j][i] *= f;
             }
@@ -332,10 +415,9 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         gemm_nt<TI, BV, DK, C>(S, UT, LDC, KdT, LDC);
         __syncthreads();
     }
-    if (OUTPUT && p.hT) {
+    if (OUTPUT && p.hT && TS::active()) {
 #pragma unroll
         for (int j = 0; j < TS::PER; ++j) {
-            if (!TS::valid(j)) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 p.hT[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)] = S[j][i];

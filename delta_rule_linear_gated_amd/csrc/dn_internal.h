@@ -68,4 +68,8 @@ hipError_t launch_backward(const Problem& pr, const Params& p, bool have_states,
 bool supported(const Problem& pr);
 int pick_bv(const Problem& pr);
 
+// Optional per-kernel timing (dn_profile.cpp); no-ops unless enabled.
+void prof_begin(hipStream_t stream, const char* name);
+void prof_end(hipStream_t stream);
+
 }  // namespace dn

@@ -61,13 +61,17 @@ hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t s
     } else {
         constexpr int BV = D < 64 ? D : 64;
         const int BH = pr.B * pr.H;
-        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        prof_begin(stream, "prep");
+        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D, false>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        prof_end(stream);
+        prof_begin(stream, "fwd_state");
         if (save)
             hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, true>), dim3(D / BV, BH),
                                dim3(kThreads), 0, stream, p);
         else
             hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, true>), dim3(D / BV, BH),
                                dim3(kThreads), 0, stream, p);
+        prof_end(stream);
         return hipGetLastError();
     }
 }
@@ -79,13 +83,22 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
     } else {
         constexpr int BV = D < 64 ? D : 64;
         const int BH = pr.B * pr.H;
-        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
-        if (!have_states)
+        prof_begin(stream, "prep_bwd");
+        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D, true>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        prof_end(stream);
+        if (!have_states) {
+            prof_begin(stream, "fwd_state_recompute");
             hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, false>), dim3(D / BV, BH),
                                dim3(kThreads), 0, stream, p);
+            prof_end(stream);
+        }
+        prof_begin(stream, "bwd_state");
         hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3(D / BV, BH), dim3(kThreads), 0,
                            stream, p);
+        prof_end(stream);
+        prof_begin(stream, "bwd_chunk");
         hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        prof_end(stream);
         return hipGetLastError();
     }
 }

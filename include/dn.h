@@ -145,6 +145,18 @@ const char* dn_last_error(void);
  */
 dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[7]);
 
+/*
+ * Diagnostics: per-kernel timing.  dn_profile_enable(1) makes every later
+ * launch record a pair of hipEvents on its stream (creating two event objects
+ * per launch); dn_profile_enable(0) stops it.  dn_profile_collect waits for
+ * the recorded events, writes up to max_kernels entries -- the kernel name
+ * (NUL-terminated, at most 31 characters, in names[32*i ...]), its summed
+ * milliseconds and its launch count -- releases the events and returns the
+ * number of entries.  Any output pointer may be NULL.
+ */
+dn_status dn_profile_enable(int on);
+int dn_profile_collect(char* names, double* total_ms, int* launches, int max_kernels);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,8 +59,9 @@ def test_workspace_intermediates(case):
             ref = np.concatenate([c["gam"] if gate == "vector" else c["gam"][:, :1] for c in tr])
             say(f"  head {h} gam err {rel_err(gam, ref):.2e}")
             assert rel_err(gam, ref) < 1e-5
-        Tm = region(lay["T"], 2 * NT * C * C, et).reshape(2, NT, C, C)[h]
-        Pm = region(lay["P"], 2 * NT * C * C, et).reshape(2, NT, C, C)[h]
+        # the backward's workspace holds T^T and P^T (the layout the reverse pass reads)
+        Tm = region(lay["T"], 2 * NT * C * C, et).reshape(2, NT, C, C)[h].transpose(0, 2, 1)
+        Pm = region(lay["P"], 2 * NT * C * C, et).reshape(2, NT, C, C)[h].transpose(0, 2, 1)
         lam = region(lay["lam"], 2 * NT * C * d, et).reshape(2, NT, C, d)[h]
         dS1 = region(lay["dS1"], 2 * NT * d * d, et).reshape(2, NT, d, d)[h]
         st = states.cpu().to(torch.float64).numpy()[0, h]
