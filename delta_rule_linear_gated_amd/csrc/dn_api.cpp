@@ -10,7 +10,7 @@
 #include <utility>
 #include <vector>
 
-#include "../../include/dn.h"
+#include "dn.h"
 #include "dn_internal.h"
 
 namespace {

@@ -41,8 +41,10 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     constexpr int PAD = Pad<TI>::value;
     constexpr int LDK = DK + PAD;
     constexpr int LDC = C + PAD;
+    constexpr int LDV = BV + PAD;
     constexpr int GW = GateLayout<GATE, DK>::GW;
-    __shared__ float gam_s[GATE == kGateVector ? C * DK : 4];
+    constexpr bool VEC = GATE == kGateVector;
+    __shared__ float gam_s[VEC ? C * DK : C];
     __shared__ float rowf[2 * C];
     __shared__ float beta_s[C];
     __shared__ __align__(16) TI dSs[BV * LDK];   // dS1 operand     [v][c]
@@ -54,6 +56,11 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     __shared__ __align__(16) TI KgT[DK * LDC];   // (K Gam)^T       [c][t]
     __shared__ __align__(16) TI dUT[BV * LDC];   // dU^T            [v][t]
     __shared__ __align__(16) TI bLT[BV * LDC];   // -(beta lambda)^T [v][t]
+    // lambda / dv write-back tiles [C][LDV]: Kd and P^T are dead once dU is formed
+    constexpr bool DB_IN_PT = C >= BV;
+    __shared__ __align__(16) TI DbSep[DB_IN_PT ? 8 : C * LDV];
+    TI* Lb = Kd;
+    TI* Db = DB_IN_PT ? PT : DbSep;
 
     const int DVr = p.DVr;
     const int bh = blockIdx.y;
@@ -92,18 +99,21 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
         const long row0 = (long)bh * p.T + t0;
-        // (a) dS1 of this chunk: operand copy and workspace copy
-        TI* __restrict__ dsv = static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK;
+        // write back lambda and dv of the chunk done last iteration (a full chunk of
+        // work after they were formed); the sync keeps commit() off their tiles
+        if (n + 1 < p.NT) {
+            const long rp = (long)bh * p.T + (n + 1) * C;
+            lds_to_global<TI, C, BV>(static_cast<TI*>(p.lam) + ((long)bh * p.NT + n + 1) * C * DVr + v0, DVr, Lb,
+                                     LDV, C);
+            lds_to_global<TI, C, BV>(static_cast<TI*>(p.dv) + rp * DVr + v0, DVr, Db, LDV, min(C, p.T - (n + 1) * C));
+            __syncthreads();
+        }
+        // (a) dS1 of this chunk: operand copy (written to the workspace from LDS below)
         if (TS::active()) {
 #pragma unroll
             for (int j = 0; j < TS::PER; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = TS::row(j, i), c = TS::col(j);
-                    const TI x = from_f<TI>(dS[j][i]);
-                    dSs[r * LDK + c] = x;
-                    dsv[r * DK + c] = x;
-                }
+                for (int i = 0; i < 4; ++i) dSs[TS::row(j, i) * LDK + TS::col(j)] = from_f<TI>(dS[j][i]);
             }
         }
         // (b) commit this chunk's tiles
@@ -124,6 +134,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         rTT.store(TT, LDC);
         __syncthreads();
         if (n > 0) prefetch(n - 1);
+        lds_to_global<TI, BV, DK>(static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, dSs, LDK,
+                                  BV);
 
         using TX = Tiles<C, BV>;
         // (c) dU = P^T dO + Kd dS1^T  -> dU^T
@@ -146,18 +158,21 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
             f32x4 L[TX::PER];
             zero_acc<C, BV>(L);
             gemm_nt<TI, C, BV, C>(L, TT, LDC, dUT, LDC);
-            TI* __restrict__ lam = static_cast<TI*>(p.lam) + ((long)bh * p.NT + n) * C * DVr + v0;
-            TI* __restrict__ dv = static_cast<TI*>(p.dv) + row0 * DVr + v0;
             if (TX::active()) {
+                float bt[TX::PER][4];   // LDS reads first, then the writes
+#pragma unroll
+                for (int j = 0; j < TX::PER; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bt[j][i] = beta_s[TX::row(j, i)];
 #pragma unroll
                 for (int j = 0; j < TX::PER; ++j) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int t = TX::row(j, i), c = TX::col(j);
                         const float l = L[j][i];
-                        const float bl = beta_s[t] * l;
-                        lam[(long)t * DVr + c] = from_f<TI>(l);
-                        if (t < valid) dv[(long)t * DVr + c] = from_f<TI>(bl);
+                        const float bl = bt[j][i] * l;
+                        Lb[t * LDV + c] = from_f<TI>(l);
+                        Db[t * LDV + c] = from_f<TI>(bl);
                         bLT[c * LDC + t] = from_f<TI>(-bl);
                     }
                 }
@@ -177,6 +192,10 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         gemm_nt<TI, BV, DK, C>(dS, bLT, LDC, KgT, LDC);
         __syncthreads();
     }
+    if (p.NT > 0) {   // lambda and dv of chunk 0
+        lds_to_global<TI, C, BV>(static_cast<TI*>(p.lam) + (long)bh * p.NT * C * DVr + v0, DVr, Lb, LDV, C);
+        lds_to_global<TI, C, BV>(static_cast<TI*>(p.dv) + (long)bh * p.T * DVr + v0, DVr, Db, LDV, min(C, p.T));
+    }
     if (p.dh0 && TS::active()) {
 #pragma unroll
         for (int j = 0; j < TS::PER; ++j) {
@@ -189,80 +208,93 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
 
 // ---------------------------------------------------------------------------
 // bwd_chunk_kernel: grid (NT, BH); every chunk finished independently.
-// D = d_k = d_v.  LDS is carved by phase (see the offsets below).
+// D = d_k = d_v.  The d_v dimension is streamed in blocks of VB columns: the
+// block's S0 rows, dS1 rows, lambda, dO and V columns are loaded into registers
+// one block ahead and committed to LDS while the previous block computes
+//     X_b = (K Gam) S0_b^T,  R_b = beta (V_b - X_b),  U_b = T R_b
+//     dQg += dO_b S0_b,  dKg += lambda_b S0_b,  dKd += U_b dS1_b
+//     dA  += lambda_b U_b^T,  dP += dO_b U_b^T
+// after which the key-gradient products (phase C) finish dq, dk, dbeta, dg.
 template <typename TI, int GATE, int C, int D>
 struct BwdChunkSmem {
     static constexpr int PAD = Pad<TI>::value;
-    static constexpr int LD = D + PAD;   // rows of D elements
-    static constexpr int LC = C + PAD;   // rows of C elements
+    static constexpr int VB = D >= 32 ? 32 : D;   // d_v block
+    static constexpr int NVB = D / VB;
+    static constexpr int LD = D + PAD;            // rows of D elements
+    static constexpr int LC = C + PAD;            // rows of C elements
+    static constexpr int LVB = VB + PAD;          // rows of VB elements
     static constexpr int GW = GateLayout<GATE, D>::GW;
     static constexpr size_t E = sizeof(TI);
     static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
-    static constexpr size_t CxD = al(C * LD * E);    // [C][D] tile
-    static constexpr size_t DxD = al(D * LD * E);    // [D][D] tile
-    static constexpr size_t DxC = al(D * LC * E);    // [D][C] tile
-    static constexpr size_t CxC = al(C * LC * E);    // [C][C] tile
-    // persistent
-    static constexpr size_t LAM = 0;                 // lambda  [t][v]   phases A, D, B
-    static constexpr size_t UB = LAM + CxD;          // U       [t][v]   phases A, D, B
-    static constexpr size_t DOB = UB + CxD;          // dO      [t][v]   phases D, B (T in phase A)
-    static constexpr size_t BIG = DOB + CxD;
-    // phase A
-    static constexpr size_t A_KG = BIG;              // K Gam   [t][c]
-    static constexpr size_t A_S0 = A_KG + CxD;       // S0      [v][c]
-    static constexpr size_t A_RT = A_S0 + DxD;       // R^T     [v][t]
-    static constexpr size_t A_END = A_RT + DxC;
-    static constexpr size_t A_T = DOB;               // T       [t][s]
-    // phase D
-    static constexpr size_t D_S0T = BIG;             // S0^T    [c][v]
-    static constexpr size_t D_DS1T = D_S0T + DxD;    // dS1^T   [c][v]
-    static constexpr size_t D_END = D_DS1T + DxD;
-    // phase B/C
-    static constexpr size_t B_DA = BIG;              // dA~     [t][s]
-    static constexpr size_t B_DAT = B_DA + CxC;      // dA~^T beta  [s][t]
-    static constexpr size_t B_DP = B_DAT + CxC;      // dP~     [t][s]
-    static constexpr size_t B_DPT = B_DP + CxC;      // dP~^T   [s][t]
-    static constexpr size_t C_KRT = 0;               // (K or K e^{c-gam})^T  [c][s]   (over LAM/UB)
-    static constexpr size_t C_KLT = C_KRT + DxC;     // (K e^{gam-c})^T        [c][t]   (vector only)
-    static constexpr size_t C_QLT = B_DPT + CxC;     // (Q or Q e^{gam-c})^T  [c][t]
-    static constexpr size_t C_END = C_QLT + DxC;
+    // persistent through the d_v loop
+    static constexpr size_t KG = 0;                                  // K (or K Gam)   [C][LD]
+    static constexpr size_t TL = KG + al(C * LD * E);                // T              [C][LC]
+    static constexpr size_t LOOP = TL + al(C * LC * E);
+    // d_v loop, one block
+    static constexpr size_t S0B = LOOP;                              // S0 rows        [VB][LD]
+    static constexpr size_t S0BT = S0B + al(VB * LD * E);            // S0 block^T     [D][LVB]
+    static constexpr size_t DS1T = S0BT + al(D * LVB * E);           // dS1 block^T    [D][LVB]
+    static constexpr size_t LAMB = DS1T + al(D * LVB * E);           // lambda block   [C][LVB]
+    static constexpr size_t DOB = LAMB + al(C * LVB * E);            // dO block       [C][LVB]
+    static constexpr size_t VBL = DOB + al(C * LVB * E);             // V block        [C][LVB]
+    static constexpr size_t RTB = VBL + al(C * LVB * E);             // R block^T      [VB][LC]
+    static constexpr size_t UB = RTB + al(VB * LC * E);              // U block        [C][LVB]
+    static constexpr size_t LOOP_END = UB + al(C * LVB * E);
+    // phase C (aliases everything above once the loop is done)
+    static constexpr size_t DA = 0;                                  // dA~            [C][LC]
+    static constexpr size_t DAT = DA + al(C * LC * E);               // beta dA~^T     [C][LC]
+    static constexpr size_t DP = DAT + al(C * LC * E);               // dP~            [C][LC]
+    static constexpr size_t DPT = DP + al(C * LC * E);               // dP~^T          [C][LC]
+    static constexpr size_t KRT = DPT + al(C * LC * E);              // (K or K e^{c-gam})^T [D][LC]
+    static constexpr size_t QLT = KRT + al(D * LC * E);              // (Q or Q e^{gam-c})^T [D][LC]
+    static constexpr size_t KLT = QLT + al(D * LC * E);              // (K e^{gam-c})^T (vector) [D][LC]
+    static constexpr size_t C_END = GATE == kGateVector ? KLT + al(D * LC * E) : KLT;
+    static constexpr size_t BIG_END = LOOP_END > C_END ? LOOP_END : C_END;
     // small fp32 arrays
-    static constexpr size_t F_END0 = A_END > D_END ? A_END : D_END;
-    static constexpr size_t F_END1 = F_END0 > C_END ? F_END0 : C_END;
-    static constexpr size_t GAM = al(F_END1);                        // gam  [C][GW]
-    static constexpr size_t BETA = GAM + al(C * GW * 4);             // beta [C]
-    static constexpr size_t RED_R = BETA + al(C * 4);                // row partials [D/16][C]
+    static constexpr size_t GAM = al(BIG_END);                                    // gam [C][D] or [C]
+    static constexpr size_t ROWF = GAM + al(GATE == kGateVector ? C * D * 4 : C * 4);  // [2][C] (scalar)
+    static constexpr size_t BETA = ROWF + al(2 * C * 4);                          // [C]
+    static constexpr size_t RED_R = BETA + al(C * 4);                             // [D/16][C]
+    // column partials: [C/16][D] (Kd dKd) and [SPLIT][D] (sum_v S0 dS1, SPLIT threads per column)
     static constexpr int SPLIT = kThreads / D > 0 ? kThreads / D : 1;
     static constexpr int REDC_ROWS = (C / 16) > SPLIT ? (C / 16) : SPLIT;
-    static constexpr size_t RED_C = RED_R + al((D / 16) * C * 4);    // column partials [C/16][D]
-    static constexpr size_t LASTS = RED_C + al(REDC_ROWS * D * 4);   // sum_v S0 dS1 per channel [D]
-    static constexpr size_t DBR = LASTS + al(D * 4);                 // dbeta partial [C]
-    static constexpr size_t ROWF = DBR + al(C * 4);                  // scalar gate row factors [2][C]
-    static constexpr size_t TOTAL = ROWF + al(2 * C * 4);
-    // d gam of the vector gate [C][D] fp32, written once every phase-C tile is dead
-    static constexpr size_t DGB = BIG;
-    static_assert(GATE != kGateVector || DGB + C * D * 4 <= TOTAL, "d gam buffer");
-    static_assert(C_KLT + DxC <= BIG || GATE != kGateVector, "K+ tile must fit below BIG");
+    static constexpr size_t RED_C = RED_R + al((D / 16) * C * 4);                 // [REDC_ROWS][D]
+    static constexpr size_t LASTS = RED_C + al(REDC_ROWS * D * 4);                // [D]
+    static constexpr size_t DBR = LASTS + al(D * 4);                              // [C]
+    static constexpr size_t TOTAL = DBR + al(C * 4);
+    // dq / dk write-back tiles [C][LD] each at offset 0; d gam of the vector gate
+    // [C][D] fp32 after them, written once every phase-C tile is dead
+    static constexpr size_t DGB = al(2 * C * LD * E);
+    static_assert(GATE != kGateVector || DGB + C * D * 4 <= BIG_END, "d gam buffer");
+    static_assert(2 * C * LD * E <= BIG_END, "write-back tiles");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
 template <typename TI, int GATE, int C, int D>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     using L = BwdChunkSmem<TI, GATE, C, D>;
-    constexpr int LD = L::LD, LC = L::LC, GW = L::GW;
+    constexpr int LD = L::LD, LC = L::LC, LVB = L::LVB, GW = L::GW;
+    constexpr int VB = L::VB, NVB = L::NVB;
     constexpr bool VEC = GATE == kGateVector;
     constexpr bool SCA = GATE == kGateScalar;
     __shared__ __align__(16) char smem[L::TOTAL];
-    TI* lamb = reinterpret_cast<TI*>(smem + L::LAM);
-    TI* Ub = reinterpret_cast<TI*>(smem + L::UB);
-    TI* dOb = reinterpret_cast<TI*>(smem + L::DOB);
+    TI* KG = reinterpret_cast<TI*>(smem + L::KG);
+    TI* TLs = reinterpret_cast<TI*>(smem + L::TL);
+    TI* S0B = reinterpret_cast<TI*>(smem + L::S0B);
+    TI* S0BT = reinterpret_cast<TI*>(smem + L::S0BT);
+    TI* DS1T = reinterpret_cast<TI*>(smem + L::DS1T);
+    TI* LAMB = reinterpret_cast<TI*>(smem + L::LAMB);
+    TI* DOB = reinterpret_cast<TI*>(smem + L::DOB);
+    TI* VBL = reinterpret_cast<TI*>(smem + L::VBL);
+    TI* RTB = reinterpret_cast<TI*>(smem + L::RTB);
+    TI* UB = reinterpret_cast<TI*>(smem + L::UB);
     float* gam_s = reinterpret_cast<float*>(smem + L::GAM);
+    float* rowf = reinterpret_cast<float*>(smem + L::ROWF);
     float* beta_s = reinterpret_cast<float*>(smem + L::BETA);
     float* red_r = reinterpret_cast<float*>(smem + L::RED_R);
     float* red_c = reinterpret_cast<float*>(smem + L::RED_C);
     float* lastS = reinterpret_cast<float*>(smem + L::LASTS);
     float* dbr = reinterpret_cast<float*>(smem + L::DBR);
-    float* rowf = reinterpret_cast<float*>(smem + L::ROWF);   // scalar gate: e^{gam_t}, e^{gam_C - gam_t}
     float* dgb = reinterpret_cast<float*>(smem + L::DGB);
 
     const int n = blockIdx.x, bh = blockIdx.y;
@@ -278,240 +310,234 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     const TI* __restrict__ dS1g = static_cast<const TI*>(p.dS1) + chunk * D * D;
     const TI* __restrict__ lamg = static_cast<const TI*>(p.lam) + chunk * C * D;
 
-    using TO = Tiles<C, D>;   // every C x D output of this kernel uses this tile map
-    using TCC = Tiles<C, C>;
+    using TO = Tiles<C, D>;    // C x D outputs: dq, dk
+    using TCC = Tiles<C, C>;   // dA, dP
+    using TX = Tiles<C, VB>;   // X_b, U_b
 
-    // ---------------- prologue: gate, beta, row factors, sum_v S0 dS1, k at this lane's elements
-    load_gam_beta<GATE, C, D>(gam_s, beta_s, p.gam + row0 * GW, p.beta + row0, valid);
-    {
-        // sum over v of S0[v][c] dS1[v][c] (gradient of S0 Diag(Gam_C) with respect to gam_C)
-        constexpr int SPLIT = kThreads / D > 0 ? kThreads / D : 1;
-        float* part = red_c;  // [SPLIT][D] scratch, consumed below before red_c is used again
-        for (int idx = threadIdx.x; idx < D * SPLIT; idx += kThreads) {
-            const int c = idx % D, h = idx / D;
-            float acc = 0.f;
-            for (int vv = h; vv < D; vv += SPLIT) acc += to_f(S0g[(long)vv * D + c]) * to_f(dS1g[(long)vv * D + c]);
-            part[h * D + c] = acc;
-        }
-        __syncthreads();
-        for (int c = threadIdx.x; c < D; c += kThreads) {
-            float acc = 0.f;
-            for (int h = 0; h < SPLIT; ++h) acc += part[h * D + c];
-            lastS[c] = acc;
-        }
-    }
-    if (SCA) {
-        for (int t = threadIdx.x; t < C; t += kThreads) {
-            const float gl0 = gam_s[valid - 1];
-            rowf[t] = fexp(gam_s[t]);
-            rowf[C + t] = fexp(gl0 - gam_s[t]);
-        }
-    }
-    float kv[TO::PER][4];
-#pragma unroll
-    for (int j = 0; j < TO::PER; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = TO::row(j, i);
-            kv[j][i] = (TO::active() && t < valid) ? to_f(k[(long)t * D + TO::col(j)]) : 0.f;
-        }
+    // ---------------- prologue: gate, K, T, the first d_v block, k at this lane's elements
+    GateRegs<GATE, C, D> rg;
+    rg.load(p.gam + row0 * GW, p.beta + row0, valid);
+    RegN<TI, C, D> rK;
+    rK.load(k, D, valid);
+    RegB<TI, C, C> rT;   // the workspace holds T^T; the transposed store gives T
+    rT.load(static_cast<const TI*>(p.Tm) + chunk * C * C, C, C);
+    RegB<TI, VB, D> rS0, rdS1;
+    RegN<TI, C, VB> rlam, rdo, rv;
+    auto load_block = [&](int b) {
+        const int v0 = b * VB;
+        rS0.load(S0g + (long)v0 * D, D, VB);
+        rdS1.load(dS1g + (long)v0 * D, D, VB);
+        rlam.load(lamg + v0, D, C);
+        rdo.load(dO + v0, D, valid);
+        rv.load(v + v0, D, valid);
+    };
+    load_block(0);
+    rg.commit(rowf, gam_s, beta_s);
     __syncthreads();
-    const float* gl = gam_s + (valid - 1) * GW;
-    // per-element decay factors: Gm = e^{gam}, Gd = e^{gam_C - gam}; vector gate also
-    // fp = e^{gam - centre}, fm = e^{centre - gam} with centre = gam_C / 2
-    auto Gm = [&](int t, int c) -> float {
-        if (GATE == kGateNone) return 1.f;
-        return SCA ? rowf[t] : fexp(gam_s[t * D + c]);
+    const GateLds<GATE, C, D> gf{rowf, gam_s, valid - 1};
+    if (VEC)
+        rK.store(KG, LD, [&](int r, int c, float x) { return x * gf.G(r, c); });
+    else
+        rK.store(KG, LD);   // scalar: Gam_t is applied to X's rows
+    rT.store_t(TLs, LC, Identity());
+    auto commit_block = [&]() {
+        rS0.store_n(S0B, LD, Identity());
+        rS0.store_t(S0BT, LVB, Identity());
+        rdS1.store_t(DS1T, LVB, Identity());
+        rlam.store(LAMB, LVB);
+        rdo.store(DOB, LVB);
+        rv.store(VBL, LVB);
     };
-    auto Gd = [&](int t, int c) -> float {
-        if (GATE == kGateNone) return 1.f;
-        return SCA ? rowf[C + t] : fexp(gl[c] - gam_s[t * D + c]);
-    };
+    commit_block();
+    __syncthreads();
 
-    // ---------------- phase A: X = (K Gam) S0^T, R = beta (V - X), U = T R, dbeta_R
-    {
-        TI* Kg = reinterpret_cast<TI*>(smem + L::A_KG);
-        TI* S0 = reinterpret_cast<TI*>(smem + L::A_S0);
-        TI* RT = reinterpret_cast<TI*>(smem + L::A_RT);
-        TI* Tl = reinterpret_cast<TI*>(smem + L::A_T);
-        if (VEC)
-            stage<TI, C, D, false>(Kg, LD, k, D, valid, [&](int r, int c, float x) { return x * fexp(gam_s[r * D + c]); });
-        else
-            stage_copy<TI, C, D, false>(Kg, LD, k, D, valid);   // scalar: Gam_t applied to X's rows
-        stage_copy<TI, D, D, false>(S0, LD, S0g, D, D);
-        stage_copy<TI, C, D, false>(lamb, LD, lamg, D, C);
-        stage_copy<TI, C, C, true>(Tl, LC, static_cast<const TI*>(p.Tm) + chunk * C * C, C, C);  // ws holds T^T
+    // ---------------- d_v loop
+    f32x4 dq[TO::PER], dkp[TO::PER], dkm[TO::PER], dA[TCC::PER], dP[TCC::PER];
+    zero_acc<C, D>(dq);
+    zero_acc<C, D>(dkp);
+    zero_acc<C, D>(dkm);
+    zero_acc<C, C>(dA);
+    zero_acc<C, C>(dP);
+    float dbr_part[TX::PER][4] = {};
+    float lastS_acc = 0.f;   // sum_v S0[v][c] dS1[v][c] for c = threadIdx.x % D (split over threads)
+    constexpr int SPLIT = L::SPLIT;
+#pragma unroll 1
+    for (int b = 0; b < NVB; ++b) {
+        if (b + 1 < NVB) load_block(b + 1);
+        // X_b = (K Gam) S0_b^T and the two S0 contractions
+        f32x4 X[TX::PER];
+        zero_acc<C, VB>(X);
+        gemm_nt<TI, C, VB, D>(X, KG, LD, S0B, LD);
+        gemm_nt<TI, C, D, VB>(dq, DOB, LVB, S0BT, LVB);
+        gemm_nt<TI, C, D, VB>(dkp, LAMB, LVB, S0BT, LVB);
+        if (threadIdx.x < D * SPLIT) {
+            const int c = threadIdx.x % D, h = threadIdx.x / D;
+            for (int vv = h; vv < VB; vv += SPLIT) lastS_acc += to_f(S0BT[c * LVB + vv]) * to_f(DS1T[c * LVB + vv]);
+        }
+        if (TX::active()) {
+            float rb[TX::PER][4];   // LDS reads first, then the writes
+#pragma unroll
+            for (int j = 0; j < TX::PER; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TX::row(j, i), c = TX::col(j);
+                    const float xr = to_f(VBL[t * LVB + c]) - (SCA ? rowf[t] : 1.f) * X[j][i];
+                    dbr_part[j][i] += to_f(LAMB[t * LVB + c]) * xr;
+                    rb[j][i] = beta_s[t] * xr;
+                }
+#pragma unroll
+            for (int j = 0; j < TX::PER; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) RTB[TX::col(j) * LC + TX::row(j, i)] = from_f<TI>(rb[j][i]);
+        }
         __syncthreads();
-        f32x4 X[TO::PER];
-        zero_acc<C, D>(X);
-        gemm_nt<TI, C, D, D>(X, Kg, LD, S0, LD);
-        if (TO::active()) {
+        // U_b = T R_b
+        {
+            f32x4 U[TX::PER];
+            zero_acc<C, VB>(U);
+            gemm_nt<TI, C, VB, C>(U, TLs, LC, RTB, LC);
+            if (TX::active()) {
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j) {
-                float part[4];
+                for (int j = 0; j < TX::PER; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TO::row(j, i), c = TO::col(j);
-                    const float vv = t < valid ? to_f(v[(long)t * D + c]) : 0.f;
-                    const float xr = vv - (SCA ? rowf[t] : 1.f) * X[j][i];
-                    part[i] = to_f(lamb[t * LD + c]) * xr;
-                    RT[c * LC + t] = from_f<TI>(beta_s[t] * xr);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float s = row16_sum(part[i]);
-                    if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s;
-                }
+                    for (int i = 0; i < 4; ++i) UB[TX::row(j, i) * LVB + TX::col(j)] = from_f<TI>(U[j][i]);
             }
         }
         __syncthreads();
-        for (int t = threadIdx.x; t < C; t += kThreads) {
-            float s = 0.f;
-            for (int b = 0; b < D / 16; ++b) s += red_r[b * C + t];
-            dbr[t] = s;
-        }
-        f32x4 U[TO::PER];
-        zero_acc<C, D>(U);
-        gemm_nt<TI, C, D, C>(U, Tl, LC, RT, LC);
-        __syncthreads();  // T (over dO) and RT dead after this point
-        if (TO::active()) {
-#pragma unroll
-            for (int j = 0; j < TO::PER; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Ub[TO::row(j, i) * LD + TO::col(j)] = from_f<TI>(U[j][i]);
+        gemm_nt<TI, C, D, VB>(dkm, UB, LVB, DS1T, LVB);
+        gemm_nt<TI, C, C, VB>(dA, LAMB, LVB, UB, LVB);
+        gemm_nt<TI, C, C, VB>(dP, DOB, LVB, UB, LVB);
+        __syncthreads();
+        if (b + 1 < NVB) {
+            commit_block();
+            __syncthreads();
         }
     }
 
-    // ---------------- phase D: dO S0, lambda S0, U dS1 (contractions over d_v)
-    // dq accumulates dL/dq, dk dL/dk, dkp the part of dL/dk reached through
-    // factors e^{+gam} (K Gam, K e^{gam - centre}); the rest of dk came through
-    // e^{-gam} factors, so d gam = q.dq + k.(2 dkp - dk) + the gam_C terms.
-    f32x4 dq[TO::PER], dk[TO::PER], dkp[TO::PER];
-    zero_acc<C, D>(dq);
-    zero_acc<C, D>(dk);
-    zero_acc<C, D>(dkp);
-    {
-        TI* S0T = reinterpret_cast<TI*>(smem + L::D_S0T);
-        TI* dS1T = reinterpret_cast<TI*>(smem + L::D_DS1T);
-        stage_copy<TI, D, D, true>(S0T, LD, S0g, D, D);
-        stage_copy<TI, D, D, true>(dS1T, LD, dS1g, D, D);
-        stage_copy<TI, C, D, false>(dOb, LD, dO, D, valid);
-        __syncthreads();
-        f32x4 tmp[TO::PER];
-        zero_acc<C, D>(tmp);
-        gemm_nt<TI, C, D, D>(tmp, dOb, LD, S0T, LD);
-        if (TO::active()) {
+    // q and k for the key-gradient products (loads in flight during the epilogues below)
+    RegB<TI, C, D> rq, rk;
+    rq.load(q, D, valid);
+    rk.load(k, D, valid);
+
+    // ---------------- dbeta_R, sum_v S0 dS1, and the d_v-contraction epilogues
+    if (TX::active()) {
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j)
+        for (int j = 0; j < TX::PER; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dq[j][i] = tmp[j][i] * Gm(TO::row(j, i), TO::col(j));
+            for (int i = 0; i < 4; ++i) {
+                const float s = row16_sum(dbr_part[j][i]);
+                if ((lane_id() & 15) == 0) red_r[(TX::n0(j) / 16) * C + TX::row(j, i)] = s;
+            }
+    }
+    if (threadIdx.x < D * SPLIT) red_c[(threadIdx.x / D) * D + threadIdx.x % D] = lastS_acc;
+    __syncthreads();   // red_r / red_c partials complete
+    for (int t = threadIdx.x; t < C; t += kThreads) {
+        float s = 0.f;
+        for (int b = 0; b < VB / 16; ++b) s += red_r[b * C + t];
+        dbr[t] = s;
+    }
+    for (int c = threadIdx.x; c < D; c += kThreads) {
+        float s = 0.f;
+        for (int h = 0; h < SPLIT; ++h) s += red_c[h * D + c];
+        lastS[c] = s;
+    }
+    __syncthreads();   // red_c is reused below
+    // dq = Gam dQg ; dk+ = -beta Gam dKg ; dk- = Gd dKd
+    if (TO::active()) {
+#pragma unroll
+        for (int j = 0; j < TO::PER; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = TO::row(j, i), c = TO::col(j);
+                const float G = gf.G(t, c);
+                dq[j][i] *= G;
+                dkp[j][i] *= -beta_s[t] * G;
+                dkm[j][i] *= gf.Gd(t, c);
+            }
         }
-        zero_acc<C, D>(tmp);
-        gemm_nt<TI, C, D, D>(tmp, lamb, LD, S0T, LD);
+    }
+    __syncthreads();   // d_v-loop tiles dead
+
+    // ---------------- phase B: dA~ and dP~ into LDS
+    {
+        TI* DAs = reinterpret_cast<TI*>(smem + L::DA);
+        TI* DATs = reinterpret_cast<TI*>(smem + L::DAT);
+        TI* DPs = reinterpret_cast<TI*>(smem + L::DP);
+        TI* DPTs = reinterpret_cast<TI*>(smem + L::DPT);
+        if (TCC::active()) {
+            float bt[TCC::PER][4];   // LDS reads first, then the writes
+#pragma unroll
+            for (int j = 0; j < TCC::PER; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TCC::row(j, i), s2 = TCC::col(j);
+                    const float e = (SCA && s2 <= t) ? fexp(gam_s[t] - gam_s[s2]) : 1.f;
+                    dP[j][i] = s2 <= t ? dP[j][i] * e : 0.f;
+                    dA[j][i] = s2 < t ? -dA[j][i] * e : 0.f;   // dA = -lambda U^T
+                    bt[j][i] = beta_s[t];
+                }
+#pragma unroll
+            for (int j = 0; j < TCC::PER; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TCC::row(j, i), s2 = TCC::col(j);
+                    DAs[t * LC + s2] = from_f<TI>(dA[j][i]);
+                    DATs[s2 * LC + t] = from_f<TI>(bt[j][i] * dA[j][i]);
+                    DPs[t * LC + s2] = from_f<TI>(dP[j][i]);
+                    DPTs[s2 * LC + t] = from_f<TI>(dP[j][i]);
+                }
+        }
+    }
+
+    // ---------------- phase C: key-gradient products
+    {
+        const TI* DAs = reinterpret_cast<const TI*>(smem + L::DA);
+        const TI* DATs = reinterpret_cast<const TI*>(smem + L::DAT);
+        const TI* DPs = reinterpret_cast<const TI*>(smem + L::DP);
+        const TI* DPTs = reinterpret_cast<const TI*>(smem + L::DPT);
+        TI* KrT = reinterpret_cast<TI*>(smem + L::KRT);
+        TI* QlT = reinterpret_cast<TI*>(smem + L::QLT);
+        TI* KlT = VEC ? reinterpret_cast<TI*>(smem + L::KLT) : KrT;
+        const float* gl = gam_s + (valid - 1) * GW;
+        // fp = e^{gam - centre} (vector gate; 1 otherwise), centre = gam_C / 2
+        auto fpl = [&](int t, int c) -> float { return VEC ? fexp(gam_s[t * D + c] - 0.5f * gl[c]) : 1.f; };
+        if (VEC) {
+            rk.store_t(KrT, LC, [&](int r, int c, float x) { return x / fpl(r, c); });
+            rk.store_t(KlT, LC, [&](int r, int c, float x) { return x * fpl(r, c); });
+            rq.store_t(QlT, LC, [&](int r, int c, float x) { return x * fpl(r, c); });
+        } else {
+            rk.store_t(KrT, LC, Identity());
+            rq.store_t(QlT, LC, Identity());
+        }
+        __syncthreads();
+        // k and q at this lane's elements, read back from the staged tiles; the
+        // gam_C column sums of Kd dKd (dk- holds only the Kd path so far)
+        float kv[TO::PER][4], qv[TO::PER][4];
         if (TO::active()) {
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = TO::row(j, i);
-                    const float x = -beta_s[t] * tmp[j][i] * Gm(t, TO::col(j));
-                    dk[j][i] = x;
-                    dkp[j][i] = x;
+                    const int t = TO::row(j, i), c = TO::col(j);
+                    const float fp = fpl(t, c);
+                    kv[j][i] = to_f(KrT[c * LC + t]) * fp;
+                    qv[j][i] = to_f(QlT[c * LC + t]) / fp;
                 }
-        }
-        zero_acc<C, D>(tmp);
-        gemm_nt<TI, C, D, D>(tmp, Ub, LD, dS1T, LD);
-        if (TO::active()) {
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j) {
                 float colp = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = tmp[j][i] * Gd(TO::row(j, i), TO::col(j));
-                    dk[j][i] += x;
-                    colp += kv[j][i] * x;   // Kd * dKd, summed over rows for the gam_C term
-                }
+                for (int i = 0; i < 4; ++i) colp += kv[j][i] * dkm[j][i];
                 colp += __shfl_xor(colp, 16);
                 colp += __shfl_xor(colp, 32);
                 if (lane_id() < 16) red_c[(TO::m0(j) / 16) * D + TO::col(j)] = colp;
             }
         }
-        __syncthreads();  // S0T / dS1T dead
-    }
-
-    // ---------------- phase B: dA~ and dP~ from lambda U^T and dO U^T
-    {
-        TI* dA = reinterpret_cast<TI*>(smem + L::B_DA);
-        TI* dAT = reinterpret_cast<TI*>(smem + L::B_DAT);
-        TI* dP = reinterpret_cast<TI*>(smem + L::B_DP);
-        TI* dPT = reinterpret_cast<TI*>(smem + L::B_DPT);
-        f32x4 acc[TCC::PER];
-        if (TCC::active()) {
-#pragma unroll
-            for (int j = 0; j < TCC::PER; ++j) {
-                const bool upper = TCC::n0(j) > TCC::m0(j);
-                acc[j] = zero4();
-                if (!upper) acc[j] = tile_nt<TI, D>(lamb + TCC::m0(j) * LD, LD, Ub + TCC::n0(j) * LD, LD, acc[j]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TCC::row(j, i), s = TCC::col(j);
-                    float a = 0.f;
-                    if (s < t) {
-                        a = -acc[j][i];  // dA = -lambda U^T
-                        if (SCA) a *= fexp(gam_s[t] - gam_s[s]);
-                    }
-                    dA[t * LC + s] = from_f<TI>(a);
-                    dAT[s * LC + t] = from_f<TI>(beta_s[t] * a);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < TCC::PER; ++j) {
-                const bool upper = TCC::n0(j) > TCC::m0(j);
-                acc[j] = zero4();
-                if (!upper) acc[j] = tile_nt<TI, D>(dOb + TCC::m0(j) * LD, LD, Ub + TCC::n0(j) * LD, LD, acc[j]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TCC::row(j, i), s = TCC::col(j);
-                    float a = 0.f;
-                    if (s <= t) {
-                        a = acc[j][i];
-                        if (SCA) a *= fexp(gam_s[t] - gam_s[s]);
-                    }
-                    dP[t * LC + s] = from_f<TI>(a);
-                    dPT[s * LC + t] = from_f<TI>(a);
-                }
-            }
-        }
-        __syncthreads();  // lambda, U, dO dead
-    }
-
-    // ---------------- phase C: key-gradient products
-    {
-        const TI* dA = reinterpret_cast<const TI*>(smem + L::B_DA);
-        const TI* dAT = reinterpret_cast<const TI*>(smem + L::B_DAT);
-        const TI* dP = reinterpret_cast<const TI*>(smem + L::B_DP);
-        const TI* dPT = reinterpret_cast<const TI*>(smem + L::B_DPT);
-        TI* KrT = reinterpret_cast<TI*>(smem + L::C_KRT);
-        TI* KlT = VEC ? reinterpret_cast<TI*>(smem + L::C_KLT) : KrT;
-        TI* QlT = reinterpret_cast<TI*>(smem + L::C_QLT);
-        if (VEC) {
-            stage_t<TI, C, D>(KrT, LC, k, D, valid,
-                              [&](int r, int c, float x) { return x * fexp(0.5f * gl[c] - gam_s[r * D + c]); });
-            stage_t<TI, C, D>(KlT, LC, k, D, valid,
-                              [&](int r, int c, float x) { return x * fexp(gam_s[r * D + c] - 0.5f * gl[c]); });
-            stage_t<TI, C, D>(QlT, LC, q, D, valid,
-                              [&](int r, int c, float x) { return x * fexp(gam_s[r * D + c] - 0.5f * gl[c]); });
-        } else {
-            stage_copy<TI, C, D, true>(KrT, LC, k, D, valid);
-            stage_copy<TI, C, D, true>(QlT, LC, q, D, valid);
-        }
-        __syncthreads();
-        auto fpl = [&](int t, int c) -> float { return VEC ? fexp(gam_s[t * D + c] - 0.5f * gl[c]) : 1.f; };
         float dbA[TO::PER][4];
         f32x4 tmp[TO::PER];
         // Y = dA~ Kr :  dK+ = beta Y, dbeta_A = sum_c K+ Y
         zero_acc<C, D>(tmp);
-        gemm_nt<TI, C, D, C>(tmp, dA, LC, KrT, LC);
+        gemm_nt<TI, C, D, C>(tmp, DAs, LC, KrT, LC);
         if (TO::active()) {
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j)
@@ -521,27 +547,22 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                     const float fp = fpl(t, TO::col(j));
                     const float y = tmp[j][i];
                     dbA[j][i] = kv[j][i] * fp * y;
-                    const float x = beta_s[t] * y * fp;
-                    dk[j][i] += x;
-                    dkp[j][i] += x;
+                    dkp[j][i] += beta_s[t] * y * fp;
                 }
         }
         // Z = (beta dA~)^T Kl and W = dP~^T Ql : both reach k through e^{-gam}
         zero_acc<C, D>(tmp);
-        gemm_nt<TI, C, D, C>(tmp, dAT, LC, KlT, LC);
-        gemm_nt<TI, C, D, C>(tmp, dPT, LC, QlT, LC);
+        gemm_nt<TI, C, D, C>(tmp, DATs, LC, KlT, LC);
+        gemm_nt<TI, C, D, C>(tmp, DPTs, LC, QlT, LC);
         if (TO::active()) {
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float fm = VEC ? 1.f / fpl(TO::row(j, i), TO::col(j)) : 1.f;
-                    dk[j][i] += tmp[j][i] * fm;
-                }
+                for (int i = 0; i < 4; ++i) dkm[j][i] += tmp[j][i] / fpl(TO::row(j, i), TO::col(j));
         }
         // dQ+ = dP~ Kr
         zero_acc<C, D>(tmp);
-        gemm_nt<TI, C, D, C>(tmp, dP, LC, KrT, LC);
+        gemm_nt<TI, C, D, C>(tmp, DPs, LC, KrT, LC);
         if (TO::active()) {
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j)
@@ -549,38 +570,37 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 for (int i = 0; i < 4; ++i) dq[j][i] += tmp[j][i] * fpl(TO::row(j, i), TO::col(j));
         }
 
-        // -------- finish: dq, dk, dbeta, dg
-        TI* __restrict__ dqo = static_cast<TI*>(p.dq) + row0 * D;
-        TI* __restrict__ dko = static_cast<TI*>(p.dk) + row0 * D;
+        // -------- finish: dq, dk = dk+ + dk-, dbeta, d gam = q.dq + k.(dk+ - dk-)
         float dgm[TO::PER][4];
+        __syncthreads();   // phase-C tiles dead: dq / dk go through LDS for coalesced stores
+        TI* dqs = reinterpret_cast<TI*>(smem + L::DA);
+        TI* dks = dqs + C * LD;
         if (TO::active()) {
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = TO::row(j, i), c = TO::col(j);
-                    float qq = 0.f;
-                    if (t < valid) {
-                        dqo[(long)t * D + c] = from_f<TI>(dq[j][i]);
-                        dko[(long)t * D + c] = from_f<TI>(dk[j][i]);
-                        if (GATE != kGateNone) qq = to_f(q[(long)t * D + c]);
-                    }
-                    dgm[j][i] = qq * dq[j][i] + kv[j][i] * (2.f * dkp[j][i] - dk[j][i]);
+                    dqs[t * LD + c] = from_f<TI>(dq[j][i]);
+                    dks[t * LD + c] = from_f<TI>(dkp[j][i] + dkm[j][i]);
+                    dgm[j][i] = qv[j][i] * dq[j][i] + kv[j][i] * (dkp[j][i] - dkm[j][i]);
                 }
             // dbeta = dbeta_R + rowsum(K+ Y)
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float s = row16_sum(dbA[j][i]);
-                    if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s;
+                    const float s2 = row16_sum(dbA[j][i]);
+                    if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s2;
                 }
         }
         __syncthreads();
+        lds_to_global<TI, C, D>(static_cast<TI*>(p.dq) + row0 * D, D, dqs, LD, valid);
+        lds_to_global<TI, C, D>(static_cast<TI*>(p.dk) + row0 * D, D, dks, LD, valid);
         for (int t = threadIdx.x; t < valid; t += kThreads) {
-            float s = dbr[t];
-            for (int b = 0; b < D / 16; ++b) s += red_r[b * C + t];
-            p.dbeta[row0 + t] = s;
+            float s2 = dbr[t];
+            for (int b = 0; b < D / 16; ++b) s2 += red_r[b * C + t];
+            p.dbeta[row0 + t] = s2;
         }
         if (GATE == kGateNone) return;
         __syncthreads();
@@ -608,8 +628,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 for (int j = 0; j < TO::PER; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float s = row16_sum(dgm[j][i]);
-                        if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s;
+                        const float s2 = row16_sum(dgm[j][i]);
+                        if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s2;
                     }
             }
             __syncthreads();
@@ -617,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 // last-row total: sum_c (Gam_C lastS[c] + column partials of Kd dKd)
                 float part = 0.f;
                 for (int c = lane_id(); c < D; c += 64) {
-                    float x = fexp(gl[0]) * lastS[c];
+                    float x = gf.GC(c) * lastS[c];
                     for (int b = 0; b < C / 16; ++b) x += red_c[b * D + c];
                     part += x;
                 }

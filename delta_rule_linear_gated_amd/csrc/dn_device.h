@@ -280,10 +280,16 @@ __device__ __forceinline__ void stage_copy(T* lds, int ldl, const T* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Register-staged tiles: load() issues every global load of a tile at once
-// (no waits), a later store*() maps, rounds and writes it to LDS.  Issuing the
-// loads of the next chunk before computing the current one hides their latency.
+// Register-staged tiles: load() issues every global load of a tile at once, a
+// later store*() maps, rounds and writes it to LDS.  Issuing the loads of the
+// next chunk before computing the current one hides their latency.
 //
+// Loads are branch-free: addresses are clamped into the tile (rows >= valid
+// read row valid - 1, surplus threads re-read the last vector) and the zeroing
+// of rows >= valid happens at store time.  A load under a branch makes the
+// compiler wait for it at the end of the branch, which serialises the tile.
+__device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
+
 // RegN: row-major thread mapping (16-byte vectors, consecutive lanes along a
 // row), for natural-layout stores.
 template <typename T, int ROWS, int COLS> struct RegN {
@@ -291,37 +297,48 @@ template <typename T, int ROWS, int COLS> struct RegN {
     static constexpr int PER = (NV + kThreads - 1) / kThreads;
     static_assert(COLS % VW == 0, "cols");
     uint4 r[PER];
-    // rows >= valid are zero
+    int valid_ = ROWS;
+    __device__ __forceinline__ static int idx_of(int i) {
+        const int idx = threadIdx.x + i * kThreads;
+        return idx < NV ? idx : NV - 1;
+    }
+    // rows >= valid store as zero
     __device__ __forceinline__ void load(const T* __restrict__ g, long gld, int valid) {
+        valid_ = valid;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int idx = threadIdx.x + i * kThreads;
+            const int idx = idx_of(i);
             const int row = idx / VPR, c0 = (idx % VPR) * VW;
-            r[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (idx < NV && row < valid) r[i] = *reinterpret_cast<const uint4*>(g + row * gld + c0);
+            r[i] = *reinterpret_cast<const uint4*>(g + (row < valid ? row : valid - 1) * gld + c0);
         }
     }
-    // rows >= valid repeat row valid - 1 (for cumulative quantities)
+    // rows >= valid store as row valid - 1 (for cumulative quantities)
     __device__ __forceinline__ void load_clamped(const T* __restrict__ g, long gld, int valid) {
+        load(g, gld, valid);
+        valid_ = ROWS;
+    }
+    // Two-phase: every output vector is formed (f may read LDS) before any is
+    // written, so f's LDS reads are not ordered behind this tile's LDS writes.
+    template <class F> __device__ __forceinline__ void store(T* lds, int ldl, F f) const {
+        uint4 outv[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int idx = threadIdx.x + i * kThreads;
+            const int idx = idx_of(i);
             const int row = idx / VPR, c0 = (idx % VPR) * VW;
-            r[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (idx < NV) r[i] = *reinterpret_cast<const uint4*>(g + (row < valid ? row : valid - 1) * gld + c0);
+            const T* src = reinterpret_cast<const T*>(&r[i]);
+            T* out = reinterpret_cast<T*>(&outv[i]);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                const float y = f(row, c0 + e, to_f(src[e]));   // unconditional: no branch around f's LDS reads
+                out[e] = from_f<T>(row < valid_ ? y : 0.f);
+            }
         }
-    }
-    template <class F> __device__ __forceinline__ void store(T* lds, int ldl, F f) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int idx = threadIdx.x + i * kThreads;
             if (idx >= NV) continue;
             const int row = idx / VPR, c0 = (idx % VPR) * VW;
-            const T* src = reinterpret_cast<const T*>(&r[i]);
-            T out[VW];
-#pragma unroll
-            for (int e = 0; e < VW; ++e) out[e] = from_f<T>(f(row, c0 + e, to_f(src[e])));
-            *reinterpret_cast<uint4*>(lds + row * ldl + c0) = *reinterpret_cast<const uint4*>(out);
+            *reinterpret_cast<uint4*>(lds + row * ldl + c0) = outv[i];
         }
     }
     __device__ __forceinline__ void store(T* lds, int ldl) const {
@@ -330,7 +347,7 @@ template <typename T, int ROWS, int COLS> struct RegN {
             const int idx = threadIdx.x + i * kThreads;
             if (idx >= NV) continue;
             const int row = idx / VPR, c0 = (idx % VPR) * VW;
-            *reinterpret_cast<uint4*>(lds + row * ldl + c0) = r[i];
+            *reinterpret_cast<uint4*>(lds + row * ldl + c0) = row < valid_ ? r[i] : zero_u4();
         }
     }
 };
@@ -343,53 +360,93 @@ template <typename T, int ROWS, int COLS> struct RegB {
     static constexpr int PER = (NB + kThreads - 1) / kThreads;
     static_assert(ROWS % VW == 0 && COLS % VW == 0, "block");
     uint4 r[PER][VW];
+    int valid_ = ROWS;
     __device__ __forceinline__ void load(const T* __restrict__ g, long gld, int valid) {
+        valid_ = valid;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int b = threadIdx.x + i * kThreads;
+            int b = threadIdx.x + i * kThreads;
+            b = b < NB ? b : NB - 1;
             const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
 #pragma unroll
             for (int e = 0; e < VW; ++e) {
-                r[i][e] = make_uint4(0u, 0u, 0u, 0u);
-                if (b < NB && r0 + e < valid) r[i][e] = *reinterpret_cast<const uint4*>(g + (r0 + e) * gld + c0);
+                const int row = r0 + e < valid ? r0 + e : valid - 1;
+                r[i][e] = *reinterpret_cast<const uint4*>(g + row * gld + c0);
             }
         }
     }
-    // lds[c * ldl + r] = f(r, c, x)
+    // lds[c * ldl + r] = f(r, c, x).  Two-phase like RegN::store.
     template <class F> __device__ __forceinline__ void store_t(T* lds, int ldl, F f) const {
+        uint4 outv[PER][VW];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            int b = threadIdx.x + i * kThreads;
+            b = b < NB ? b : NB - 1;
+            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                T* out = reinterpret_cast<T*>(&outv[i][e]);
+#pragma unroll
+                for (int k = 0; k < VW; ++k) {
+                    const float y = f(r0 + k, c0 + e, to_f(reinterpret_cast<const T*>(&r[i][k])[e]));
+                    out[k] = from_f<T>(r0 + k < valid_ ? y : 0.f);
+                }
+            }
+        }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int b = threadIdx.x + i * kThreads;
             if (b >= NB) continue;
             const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
 #pragma unroll
-            for (int e = 0; e < VW; ++e) {
-                T out[VW];
-#pragma unroll
-                for (int k = 0; k < VW; ++k)
-                    out[k] = from_f<T>(f(r0 + k, c0 + e, to_f(reinterpret_cast<const T*>(&r[i][k])[e])));
-                *reinterpret_cast<uint4*>(lds + (c0 + e) * ldl + r0) = *reinterpret_cast<const uint4*>(out);
-            }
+            for (int e = 0; e < VW; ++e) *reinterpret_cast<uint4*>(lds + (c0 + e) * ldl + r0) = outv[i][e];
         }
     }
-    // lds[r * ldl + c] = f(r, c, x)
+    // lds[r * ldl + c] = f(r, c, x).  Two-phase like RegN::store.
     template <class F> __device__ __forceinline__ void store_n(T* lds, int ldl, F f) const {
+        uint4 outv[PER][VW];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int b = threadIdx.x + i * kThreads;
-            if (b >= NB) continue;
+            int b = threadIdx.x + i * kThreads;
+            b = b < NB ? b : NB - 1;
             const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
 #pragma unroll
             for (int e = 0; e < VW; ++e) {
                 const T* src = reinterpret_cast<const T*>(&r[i][e]);
-                T out[VW];
+                T* out = reinterpret_cast<T*>(&outv[i][e]);
 #pragma unroll
-                for (int k = 0; k < VW; ++k) out[k] = from_f<T>(f(r0 + e, c0 + k, to_f(src[k])));
-                *reinterpret_cast<uint4*>(lds + (r0 + e) * ldl + c0) = *reinterpret_cast<const uint4*>(out);
+                for (int k = 0; k < VW; ++k) {
+                    const float y = f(r0 + e, c0 + k, to_f(src[k]));
+                    out[k] = from_f<T>(r0 + e < valid_ ? y : 0.f);
+                }
             }
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int b = threadIdx.x + i * kThreads;
+            if (b >= NB) continue;
+            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+#pragma unroll
+            for (int e = 0; e < VW; ++e) *reinterpret_cast<uint4*>(lds + (r0 + e) * ldl + c0) = outv[i][e];
         }
     }
 };
+
+// Coalesced write-back of a ROWS x COLS tile held in LDS (row stride ldl) to
+// global memory (row stride gld), 16 bytes per thread and store; rows >=
+// valid_rows are not written.
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ void lds_to_global(T* __restrict__ g, long gld, const T* lds, int ldl, int valid_rows) {
+    constexpr int VW = 16 / sizeof(T), VPR = COLS / VW, NV = ROWS * VPR;
+    static_assert(COLS % VW == 0, "cols");
+#pragma unroll
+    for (int i = 0; i < (NV + kThreads - 1) / kThreads; ++i) {
+        const int idx = threadIdx.x + i * kThreads;
+        const int row = idx / VPR, c0 = (idx % VPR) * VW;
+        if (idx < NV && row < valid_rows)
+            *reinterpret_cast<uint4*>(g + row * gld + c0) = *reinterpret_cast<const uint4*>(lds + row * ldl + c0);
+    }
+}
 
 // Sum over the 16 lanes that share (lane >> 4): the lanes holding one output row.
 __device__ __forceinline__ float row16_sum(float x) {

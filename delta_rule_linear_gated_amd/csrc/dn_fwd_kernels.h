@@ -37,21 +37,6 @@ template <int GATE, int DK> struct GateLayout {
     static constexpr int GW = GATE == kGateVector ? DK : 1;  // gam values per step
 };
 
-// Loads the chunk's cumulative log-decay into gam_s (rows >= valid repeat the
-// last valid row) and beta into beta_s (0 for rows >= valid).
-template <int GATE, int C, int DK>
-__device__ __forceinline__ void load_gam_beta(float* gam_s, float* beta_s, const float* __restrict__ gam_ws,
-                                              const float* __restrict__ beta, int valid) {
-    constexpr int GW = GateLayout<GATE, DK>::GW;
-    for (int t = threadIdx.x; t < C; t += kThreads) beta_s[t] = t < valid ? beta[t] : 0.f;
-    if (GATE == kGateNone) return;
-    for (int idx = threadIdx.x; idx < C * GW; idx += kThreads) {
-        const int t = idx / GW, c = idx % GW;
-        const int tt = t < valid ? t : valid - 1;
-        gam_s[idx] = gam_ws[tt * GW + c];
-    }
-}
-
 // ---------------------------------------------------------------------------
 // prep_kernel: grid (NT, BH), one chunk per workgroup.  TRANS_OUT stores T^T
 // and P^T instead of T and P (the layout the reverse pass reads).
@@ -128,42 +113,37 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
     {
         using TL = Tiles<C, C>;
         f32x4 acc[TL::PER];
+        f32x4 accp[TL::PER];
 #pragma unroll
         for (int j = 0; j < TL::PER; ++j) {
-            if (!TL::valid(j)) continue;
-            const bool upper = TL::n0(j) > TL::m0(j);
             acc[j] = zero4();
-            if (!upper) acc[j] = tile_nt<TI, DK>(Kp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, acc[j]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TL::row(j, i), s = TL::col(j);
-                float a = 0.f;
-                if (s < t) {
-                    a = beta_s[t] * acc[j][i];
-                    if (GATE == kGateScalar) a *= fexp(gam_s[t] - gam_s[s]);
-                }
-                A_s[t * LDA + s] = a;
-            }
+            accp[j] = zero4();
+            if (!TL::valid(j) || TL::n0(j) > TL::m0(j)) continue;   // strictly upper tiles are zero
+            acc[j] = tile_nt<TI, DK>(Kp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, acc[j]);
+            accp[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, accp[j]);
         }
+        // gate factors and masks (LDS reads only), then the stores
+        if (TL::active()) {
 #pragma unroll
-        for (int j = 0; j < TL::PER; ++j) {
-            if (!TL::valid(j)) continue;
-            const bool upper = TL::n0(j) > TL::m0(j);
-            acc[j] = zero4();
-            if (!upper) acc[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, acc[j]);
+            for (int j = 0; j < TL::PER; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = TL::row(j, i), s = TL::col(j);
-                float pv = 0.f;
-                if (s <= t) {
-                    pv = acc[j][i];
-                    if (GATE == kGateScalar) pv *= fexp(gam_s[t] - gam_s[s]);
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TL::row(j, i), s = TL::col(j);
+                    const float e = (GATE == kGateScalar && s <= t) ? fexp(gam_s[t] - gam_s[s]) : 1.f;
+                    acc[j][i] = s < t ? beta_s[t] * acc[j][i] * e : 0.f;
+                    accp[j][i] = s <= t ? accp[j][i] * e : 0.f;
                 }
-                if (TRANS_OUT)
-                    Pout[s * C + t] = from_f<TI>(pv);
-                else
-                    Pout[t * C + s] = from_f<TI>(pv);
-            }
+#pragma unroll
+            for (int j = 0; j < TL::PER; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = TL::row(j, i), s = TL::col(j);
+                    A_s[t * LDA + s] = acc[j][i];
+                    if (TRANS_OUT)
+                        Pout[s * C + t] = from_f<TI>(accp[j][i]);
+                    else
+                        Pout[t * C + s] = from_f<TI>(accp[j][i]);
+                }
         }
     }
     __syncthreads();
@@ -196,28 +176,33 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // Per-chunk gate data held in registers between prefetch and commit, and the
 // decay factors it leaves in LDS:
-//   scalar gate: rowf[t] = e^{gam_t}, rowf[C + t] = e^{gam_C - gam_t}
+//   scalar gate: rowf[t] = e^{gam_t}, rowf[C + t] = e^{gam_C - gam_t}, gam_s[t]
 //   vector gate: gam_s[t][c] (factors computed per element from it)
 template <int GATE, int C, int DK> struct GateRegs {
     static constexpr bool VEC = GATE == kGateVector;
     RegN<float, VEC ? C : 4, VEC ? DK : 4> gv;   // vector gate: the chunk's gam rows
     float gs = 0.f, gC = 0.f, b = 0.f;          // scalar gate: gam_t, gam_C; beta_t (thread t < C)
+    int valid_ = C;
+    // branch-free: row indices are clamped into the chunk, masking happens in commit()
     __device__ __forceinline__ void load(const float* __restrict__ gam, const float* __restrict__ beta,
                                          int valid) {
+        valid_ = valid;
         const int t = threadIdx.x;
-        if (t < C) b = t < valid ? beta[t] : 0.f;
-        if (GATE == kGateScalar && t < C) {
-            gs = gam[t < valid ? t : valid - 1];
+        const int tt = t < valid ? t : valid - 1;
+        b = beta[tt];
+        if (GATE == kGateScalar) {
+            gs = gam[tt];
             gC = gam[valid - 1];
         }
         if (VEC) gv.load_clamped(gam, DK, valid);
     }
     __device__ __forceinline__ void commit(float* rowf, float* gam_s, float* beta_s) const {
         const int t = threadIdx.x;
-        if (t < C) beta_s[t] = b;
+        if (t < C) beta_s[t] = t < valid_ ? b : 0.f;
         if (GATE == kGateScalar && t < C) {
             rowf[t] = fexp(gs);
             rowf[C + t] = fexp(gC - gs);
+            gam_s[t] = gs;
         }
         if (VEC) gv.store(gam_s, DK);
     }
@@ -227,7 +212,8 @@ template <int GATE, int C, int DK> struct GateRegs {
 template <int GATE, int C, int DK> struct GateLds {
     const float* rowf;
     const float* gam_s;
-    int last;  // valid - 1
+    int last;                  // valid - 1
+    const float* gl = nullptr; // vector gate: a copy of row `last` of gam_s, if gam_s is reused
     // e^{gam[t][c]}
     __device__ __forceinline__ float G(int t, int c) const {
         if (GATE == kGateNone) return 1.f;
@@ -244,7 +230,7 @@ template <int GATE, int C, int DK> struct GateLds {
     __device__ __forceinline__ float GC(int c) const {
         if (GATE == kGateNone) return 1.f;
         if (GATE == kGateScalar) return rowf[last];
-        return fexp(gam_s[last * DK + c]);
+        return fexp(gl ? gl[c] : gam_s[last * DK + c]);
     }
 };
 
@@ -263,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     constexpr int LDC = C + PAD;
     constexpr int LDV = BV + PAD;
     constexpr int GW = GateLayout<GATE, DK>::GW;
-    __shared__ float gam_s[GATE == kGateVector ? C * DK : 4];
+    __shared__ float gam_s[GATE == kGateVector ? C * DK : C];
     __shared__ float rowf[2 * C];
     __shared__ float beta_s[C];
     __shared__ __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
@@ -273,7 +259,9 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     __shared__ __align__(16) TI Vb[C * LDV];     // V block          [t][v]
     __shared__ __align__(16) TI Tl[C * LDC];     // T                [t][s]
     __shared__ __align__(16) TI Pl[C * LDC];     // P                [t][s]
-    __shared__ __align__(16) TI RT[BV * LDC];    // R^T              [v][t]
+    // R^T [v][t]; after (d) it holds the chunk's O [t][v] until the next iteration writes it back
+    constexpr int RT_ELEMS = BV * LDC > C * LDV ? BV * LDC : C * LDV;
+    __shared__ __align__(16) TI RT[RT_ELEMS];
     __shared__ __align__(16) TI UT[BV * LDC];    // U^T              [v][t]
 
     const int DVr = p.DVr;
@@ -316,18 +304,16 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
         const long row0 = (long)bh * p.T + t0;
-        // (a) state operand (and the saved copy)
-        TI* __restrict__ sv = SAVE ? static_cast<TI*>(p.states) + (((long)bh * p.NT + n) * DVr + v0) * DK : nullptr;
+        // write back the previous chunk's O (a full chunk of work after it was formed,
+        // so the stores never sit just ahead of a wait on this chunk's loads)
+        if (OUTPUT && n > 0)
+            lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + (row0 - C) * DVr + v0, DVr, RT, LDV, C);
+        // (a) state operand (saved from LDS below)
         if (TS::active()) {
 #pragma unroll
             for (int j = 0; j < TS::PER; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = TS::row(j, i), c = TS::col(j);
-                    const TI x = from_f<TI>(S[j][i]);
-                    Ss[r * LDK + c] = x;
-                    if (SAVE) sv[r * DK + c] = x;
-                }
+                for (int i = 0; i < 4; ++i) Ss[TS::row(j, i) * LDK + TS::col(j)] = from_f<TI>(S[j][i]);
             }
         }
         // (b) commit this chunk's tiles to LDS
@@ -352,6 +338,9 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         }
         __syncthreads();
         if (n + 1 < p.NT) prefetch(n + 1);
+        if (SAVE)
+            lds_to_global<TI, BV, DK>(static_cast<TI*>(p.states) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, Ss,
+                                      LDK, BV);
 
         // (c) X = (K Gam) S0^T ;  R = diag(beta) (V - X)  -> R^T
         using TX = Tiles<C, BV>;
@@ -360,14 +349,19 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             zero_acc<C, BV>(X);
             gemm_nt<TI, C, BV, DK>(X, Kg, LDK, Ss, LDK);
             if (TX::active()) {
+                // all LDS reads, then all LDS writes (see RegN::store)
+                float rv_[TX::PER][4];
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) {
+                for (int j = 0; j < TX::PER; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int t = TX::row(j, i), c = TX::col(j);
-                        RT[c * LDC + t] = from_f<TI>(beta_s[t] * (to_f(Vb[t * LDV + c]) - X[j][i]));
+                        rv_[j][i] = beta_s[t] * (to_f(Vb[t * LDV + c]) - X[j][i]);
                     }
-                }
+#pragma unroll
+                for (int j = 0; j < TX::PER; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) RT[TX::col(j) * LDC + TX::row(j, i)] = from_f<TI>(rv_[j][i]);
             }
         }
         __syncthreads();
@@ -385,21 +379,17 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             }
         }
         __syncthreads();
-        // (e) O = (Q Gam) S0^T + P U
+        // (e) O = (Q Gam) S0^T + P U   (into RT, dead since (d); written back next iteration)
         if (OUTPUT) {
             f32x4 O[TX::PER];
             zero_acc<C, BV>(O);
             gemm_nt<TI, C, BV, DK>(O, Qg, LDK, Ss, LDK);
             gemm_nt<TI, C, BV, C>(O, Pl, LDC, UT, LDC);
-            TI* __restrict__ o = static_cast<TI*>(p.o) + row0 * DVr + v0;
             if (TX::active()) {
 #pragma unroll
                 for (int j = 0; j < TX::PER; ++j) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = TX::row(j, i);
-                        if (t < valid) o[(long)t * DVr + TX::col(j)] = from_f<TI>(O[j][i]);
-                    }
+                    for (int i = 0; i < 4; ++i) RT[TX::row(j, i) * LDV + TX::col(j)] = from_f<TI>(O[j][i]);
                 }
             }
         }
@@ -414,6 +404,11 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         }
         gemm_nt<TI, BV, DK, C>(S, UT, LDC, KdT, LDC);
         __syncthreads();
+    }
+    if (OUTPUT && p.NT > 0) {
+        const int t0 = (p.NT - 1) * C;
+        lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + ((long)bh * p.T + t0) * DVr + v0, DVr, RT, LDV,
+                                 min(C, p.T - t0));
     }
     if (OUTPUT && p.hT && TS::active()) {
 #pragma unroll

@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/dn.h"
+#include "dn.h"
 #include "dn_internal.h"
 
 namespace dn {
