@@ -23,7 +23,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
 // LDS row padding (elements) that keeps row starts 16-byte aligned and shifts
@@ -122,10 +122,10 @@ __device__ __forceinline__ f32x4 tile_nt(const T* A, int lda, const T* B, int ld
     }
 }
 
-// Static distribution of the 16x16 tiles of an M x N output over the 4 waves.
+// Static distribution of the 16x16 tiles of an M x N output over the waves.
 // The waves form a WM x WN grid; each owns an RM x RN block of tiles, so one
 // K step loads RM A-fragments and RN B-fragments for RM*RN MFMAs.  Outputs of
-// fewer than 4 tiles give one tile to each of the first waves.
+// fewer tiles than waves give one tile to each of the first waves.
 template <int M, int N> struct Tiles {
     static_assert(M % 16 == 0 && N % 16 == 0, "tile dims");
     static constexpr int TM = M / 16, TN = N / 16, NT = TM * TN;
@@ -352,24 +352,44 @@ template <typename T, int ROWS, int COLS> struct RegN {
     }
 };
 
-// RegB: VW x VW blocks per thread (lanes walk row blocks first), for
+// RegB: BRW x VW blocks per thread (lanes walk row blocks first), for
 // transposed stores (register transpose) and, when the same data is also
-// needed untransposed, natural stores from the same registers.
+// needed untransposed, natural stores from the same registers.  Global loads
+// are 16-byte row pieces; a transposed store writes BRW elements (BRW x
+// sizeof(T) bytes) of an LDS row.  BRW is the tallest block (VW, VW/2 or VW/4
+// rows) that still gives every thread a block, so the tile is spread over the
+// workgroup instead of piling 8 x 16 bytes on a few threads.
+template <int BYTES> struct VecOf;
+template <> struct VecOf<16> { typedef uint4 type; };
+template <> struct VecOf<8> { typedef uint2 type; };
+template <> struct VecOf<4> { typedef uint32_t type; };
+
 template <typename T, int ROWS, int COLS> struct RegB {
-    static constexpr int VW = 16 / sizeof(T), BR = ROWS / VW, BC = COLS / VW, NB = BR * BC;
+    static constexpr int VW = 16 / sizeof(T);
+    static constexpr int pick_brw() {
+        int b = VW;
+        while (b > 1 && b * sizeof(T) > 4 && (ROWS / b) * (COLS / VW) < kThreads && ROWS % (b / 2) == 0) b /= 2;
+        return b;
+    }
+    static constexpr int BRW = pick_brw();
+    static constexpr int BR = ROWS / BRW, BC = COLS / VW, NB = BR * BC;
     static constexpr int PER = (NB + kThreads - 1) / kThreads;
-    static_assert(ROWS % VW == 0 && COLS % VW == 0, "block");
-    uint4 r[PER][VW];
+    static_assert(ROWS % BRW == 0 && COLS % VW == 0, "block");
+    typedef typename VecOf<BRW * sizeof(T)>::type TV;   // one transposed-row piece
+    uint4 r[PER][BRW];
     int valid_ = ROWS;
+    __device__ __forceinline__ static int blk(int i) {
+        const int b = threadIdx.x + i * kThreads;
+        return b < NB ? b : NB - 1;
+    }
     __device__ __forceinline__ void load(const T* __restrict__ g, long gld, int valid) {
         valid_ = valid;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            int b = threadIdx.x + i * kThreads;
-            b = b < NB ? b : NB - 1;
-            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+            const int b = blk(i);
+            const int r0 = (b % BR) * BRW, c0 = (b / BR) * VW;
 #pragma unroll
-            for (int e = 0; e < VW; ++e) {
+            for (int e = 0; e < BRW; ++e) {
                 const int row = r0 + e < valid ? r0 + e : valid - 1;
                 r[i][e] = *reinterpret_cast<const uint4*>(g + row * gld + c0);
             }
@@ -377,17 +397,16 @@ template <typename T, int ROWS, int COLS> struct RegB {
     }
     // lds[c * ldl + r] = f(r, c, x).  Two-phase like RegN::store.
     template <class F> __device__ __forceinline__ void store_t(T* lds, int ldl, F f) const {
-        uint4 outv[PER][VW];
+        TV outv[PER][VW];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            int b = threadIdx.x + i * kThreads;
-            b = b < NB ? b : NB - 1;
-            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+            const int b = blk(i);
+            const int r0 = (b % BR) * BRW, c0 = (b / BR) * VW;
 #pragma unroll
             for (int e = 0; e < VW; ++e) {
                 T* out = reinterpret_cast<T*>(&outv[i][e]);
 #pragma unroll
-                for (int k = 0; k < VW; ++k) {
+                for (int k = 0; k < BRW; ++k) {
                     const float y = f(r0 + k, c0 + e, to_f(reinterpret_cast<const T*>(&r[i][k])[e]));
                     out[k] = from_f<T>(r0 + k < valid_ ? y : 0.f);
                 }
@@ -397,21 +416,20 @@ template <typename T, int ROWS, int COLS> struct RegB {
         for (int i = 0; i < PER; ++i) {
             const int b = threadIdx.x + i * kThreads;
             if (b >= NB) continue;
-            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+            const int r0 = (b % BR) * BRW, c0 = (b / BR) * VW;
 #pragma unroll
-            for (int e = 0; e < VW; ++e) *reinterpret_cast<uint4*>(lds + (c0 + e) * ldl + r0) = outv[i][e];
+            for (int e = 0; e < VW; ++e) *reinterpret_cast<TV*>(lds + (c0 + e) * ldl + r0) = outv[i][e];
         }
     }
     // lds[r * ldl + c] = f(r, c, x).  Two-phase like RegN::store.
     template <class F> __device__ __forceinline__ void store_n(T* lds, int ldl, F f) const {
-        uint4 outv[PER][VW];
+        uint4 outv[PER][BRW];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            int b = threadIdx.x + i * kThreads;
-            b = b < NB ? b : NB - 1;
-            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+            const int b = blk(i);
+            const int r0 = (b % BR) * BRW, c0 = (b / BR) * VW;
 #pragma unroll
-            for (int e = 0; e < VW; ++e) {
+            for (int e = 0; e < BRW; ++e) {
                 const T* src = reinterpret_cast<const T*>(&r[i][e]);
                 T* out = reinterpret_cast<T*>(&outv[i][e]);
 #pragma unroll
@@ -425,9 +443,9 @@ template <typename T, int ROWS, int COLS> struct RegB {
         for (int i = 0; i < PER; ++i) {
             const int b = threadIdx.x + i * kThreads;
             if (b >= NB) continue;
-            const int r0 = (b % BR) * VW, c0 = (b / BR) * VW;
+            const int r0 = (b % BR) * BRW, c0 = (b / BR) * VW;
 #pragma unroll
-            for (int e = 0; e < VW; ++e) *reinterpret_cast<uint4*>(lds + (r0 + e) * ldl + c0) = outv[i][e];
+            for (int e = 0; e < BRW; ++e) *reinterpret_cast<uint4*>(lds + (r0 + e) * ldl + c0) = outv[i][e];
         }
     }
 };
