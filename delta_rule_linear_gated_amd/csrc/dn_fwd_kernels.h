@@ -38,20 +38,122 @@ template <int GATE, int DK> struct GateLayout {
 };
 
 // ---------------------------------------------------------------------------
+// 16 x 16 fp32 block product on the matrix cores, row-major operands:
+//     acc += A[16][16] * B[16][16]
+// (v_mfma_f32_16x16x4_f32: lane l holds A[l & 15][k0 + (l >> 4)] and
+// B[k0 + (l >> 4)][l & 15]; the result is D[4 (l >> 4) + i][l & 15].)
+__device__ __forceinline__ f32x4 mm16_nn(const float* A, int lda, const float* B, int ldb, f32x4 acc) {
+    const int l = lane_id();
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(l & 15) * lda + k0 + (l >> 4)], B[(k0 + (l >> 4)) * ldb + (l & 15)],
+                                                   acc, 0, 0, 0);
+    return acc;
+}
+
+// T = (I + A)^{-1} for a strictly lower C x C matrix A (fp32 in LDS, row
+// stride ld), written to Ts (fp32, row stride ld).  With 16 x 16 blocks:
+//   diagonal blocks  T_bb = (I + A_bb)^{-1}: forward substitution, all blocks at
+//                    once on wave 0 (lane = block * 16 + column);
+//   off-diagonal     T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, filled by distance
+//                    i - j = 1, 2, ...; one wave per block, fp32 MFMA;
+//   above the block diagonal T is zero.
+// Ysc is per-wave scratch for one 16 x 16 fp32 block.  Ends with a barrier.
+template <int C>
+__device__ __forceinline__ void unit_lower_inverse(const float* A, float* Ts, int ld, float* Ysc) {
+    constexpr int NBK = C / 16;
+    // zero the strictly-upper blocks
+    for (int idx = threadIdx.x; idx < C * C; idx += kThreads) {
+        const int r = idx / C, c = idx % C;
+        if ((c >> 4) > (r >> 4)) Ts[r * ld + c] = 0.f;
+    }
+    if (wave_id() == 0) {
+        const int l = lane_id(), b = l >> 4, c = l & 15;
+        if (b < NBK) {
+            const float* Ab = A + (16 * b) * ld + 16 * b;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
+            // right-looking: once x_j is final, remove its contribution from the rows below
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                float a[16];
+#pragma unroll
+                for (int i = jj + 1; i < 16; ++i) a[i] = Ab[i * ld + jj];
+#pragma unroll
+                for (int i = jj + 1; i < 16; ++i) x[i] -= a[i] * x[jj];
+            }
+            float* Tb = Ts + (16 * b) * ld + 16 * b;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Tb[i * ld + c] = x[i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int dist = 1; dist < NBK; ++dist) {
+        const int jb = wave_id();
+        if (jb < NBK - dist) {
+            const int ib = jb + dist;
+            float* Y = Ysc + wave_id() * 256;
+            f32x4 y = zero4();
+            for (int kb = jb; kb < ib; ++kb)
+                y = mm16_nn(A + (16 * ib) * ld + 16 * kb, ld, Ts + (16 * kb) * ld + 16 * jb, ld, y);
+            const int l = lane_id();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Y[(4 * (l >> 4) + i) * 16 + (l & 15)] = y[i];
+            // (the same wave reads Y back: LDS operations of one wave complete in order)
+            f32x4 t = zero4();
+            t = mm16_nn(Ts + (16 * ib) * ld + 16 * ib, ld, Y, 16, t);
+            float* Tij = Ts + (16 * ib) * ld + 16 * jb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Tij[(4 * (l >> 4) + i) * ld + (l & 15)] = -t[i];
+        }
+        __syncthreads();
+    }
+}
+
+// LDS carving of prep_kernel.  R0 holds the staged K / Q tiles until the Gram
+// products are done, then the fp32 inverse, its block scratch and the P tile.
+template <typename TI, int GATE, int C, int DK> struct PrepSmem {
+    static constexpr bool VEC = GATE == kGateVector;
+    static constexpr int LDK = DK + Pad<TI>::value;
+    static constexpr int LDA = C + 4;                   // fp32 C x C rows
+    static constexpr int LC = C + Pad<TI>::value;       // I/O-type C x C rows
+    static constexpr int GW = GateLayout<GATE, DK>::GW;
+    static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+    static constexpr size_t KP = 0;
+    static constexpr size_t KM = KP + al(C * LDK * sizeof(TI));
+    static constexpr size_t QP = KM + (VEC ? al(C * LDK * sizeof(TI)) : 0);
+    static constexpr size_t R0_END = QP + al(C * LDK * sizeof(TI));
+    static constexpr size_t TS = 0;                     // fp32 [C][LDA]
+    static constexpr size_t YSC = TS + al(C * LDA * 4); // fp32 [C/16][256]
+    static constexpr size_t PS = YSC + al((C / 16) * 256 * 4);   // TI [C][LC]
+    static constexpr size_t R0B_END = PS + al(C * LC * sizeof(TI));
+    static constexpr size_t R0 = R0_END > R0B_END ? R0_END : R0B_END;
+    static constexpr size_t AS = R0;                    // fp32 [C][LDA]
+    static constexpr size_t GAM = AS + al(C * LDA * 4);
+    static constexpr size_t BETA = GAM + al(C * GW * 4);
+    static constexpr size_t TOTAL = BETA + al(C * 4);
+};
+
+// ---------------------------------------------------------------------------
 // prep_kernel: grid (NT, BH), one chunk per workgroup.  TRANS_OUT stores T^T
 // and P^T instead of T and P (the layout the reverse pass reads).
 template <typename TI, int GATE, int C, int DK, bool TRANS_OUT>
 __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
-    constexpr int LDK = DK + Pad<TI>::value;
-    constexpr int LDA = C + 4;
-    constexpr int GW = GateLayout<GATE, DK>::GW;
-    constexpr bool VEC = GATE == kGateVector;
-    __shared__ float gam_s[C * GW];
-    __shared__ float beta_s[C];
-    __shared__ __align__(16) TI Kp[C * LDK];               // K, or K e^{gam - centre}
-    __shared__ __align__(16) TI Km[VEC ? C * LDK : 16];    // K e^{centre - gam} (vector gate)
-    __shared__ __align__(16) TI Qp[C * LDK];               // Q, or Q e^{gam - centre}
-    __shared__ __align__(16) float A_s[C * LDA];
+    using L = PrepSmem<TI, GATE, C, DK>;
+    constexpr int LDK = L::LDK, LDA = L::LDA, LC = L::LC, GW = L::GW;
+    constexpr bool VEC = L::VEC;
+    __shared__ __align__(16) char smem[L::TOTAL];
+    TI* Kp = reinterpret_cast<TI*>(smem + L::KP);   // K, or K e^{gam - centre}
+    TI* Km = reinterpret_cast<TI*>(smem + L::KM);   // K e^{centre - gam} (vector gate)
+    TI* Qp = reinterpret_cast<TI*>(smem + L::QP);   // Q, or Q e^{gam - centre}
+    float* Ts = reinterpret_cast<float*>(smem + L::TS);
+    float* Ysc = reinterpret_cast<float*>(smem + L::YSC);
+    TI* Ps = reinterpret_cast<TI*>(smem + L::PS);
+    float* A_s = reinterpret_cast<float*>(smem + L::AS);
+    float* gam_s = reinterpret_cast<float*>(smem + L::GAM);
+    float* beta_s = reinterpret_cast<float*>(smem + L::BETA);
 
     const int n = blockIdx.x, bh = blockIdx.y;
     const int t0 = n * C;
@@ -60,12 +162,16 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
     const TI* __restrict__ q = static_cast<const TI*>(p.q) + row0 * DK;
     const TI* __restrict__ k = static_cast<const TI*>(p.k) + row0 * DK;
     const float* __restrict__ beta = p.beta + row0;
+    RegN<TI, C, DK> rq, rk;
+    rq.load(q, DK, valid);
+    rk.load(k, DK, valid);
 
     // -- cumulative log-decay within the chunk
     if (GATE == kGateScalar) {
         if (wave_id() == 0) {
             const int t = lane_id();
-            float x = (t < valid) ? p.g[row0 + t] : 0.f;
+            const float g = p.g[row0 + (t < valid ? t : valid - 1)];
+            float x = t < valid ? g : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off);
@@ -86,34 +192,26 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
             }
         }
     }
-    for (int t = threadIdx.x; t < C; t += kThreads) beta_s[t] = t < valid ? beta[t] : 0.f;
+    for (int t = threadIdx.x; t < C; t += kThreads) beta_s[t] = beta[t < valid ? t : valid - 1] * (t < valid ? 1.f : 0.f);
     __syncthreads();
 
     // -- stage K and Q (centred per-channel factors for the vector gate)
     if (VEC) {
         const float* gl = gam_s + (valid - 1) * DK;  // gam_C
-        stage<TI, C, DK, false>(Kp, LDK, k, DK, valid, [&](int r, int c, float x) {
-            return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]);
-        });
-        stage<TI, C, DK, false>(Km, LDK, k, DK, valid, [&](int r, int c, float x) {
-            return x * fexp(0.5f * gl[c] - gam_s[r * DK + c]);
-        });
-        stage<TI, C, DK, false>(Qp, LDK, q, DK, valid, [&](int r, int c, float x) {
-            return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]);
-        });
+        rk.store(Kp, LDK, [&](int r, int c, float x) { return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]); });
+        rk.store(Km, LDK, [&](int r, int c, float x) { return x * fexp(0.5f * gl[c] - gam_s[r * DK + c]); });
+        rq.store(Qp, LDK, [&](int r, int c, float x) { return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]); });
     } else {
-        stage_copy<TI, C, DK, false>(Kp, LDK, k, DK, valid);
-        stage_copy<TI, C, DK, false>(Qp, LDK, q, DK, valid);
+        rk.store(Kp, LDK);
+        rq.store(Qp, LDK);
     }
     __syncthreads();
 
     // -- gated Gram matrices: A (strict lower, scaled by beta_t) and P (lower)
     const TI* KmP = VEC ? Km : Kp;
-    TI* __restrict__ Pout = static_cast<TI*>(p.Pm) + ((long)bh * p.NT + n) * C * C;
     {
         using TL = Tiles<C, C>;
-        f32x4 acc[TL::PER];
-        f32x4 accp[TL::PER];
+        f32x4 acc[TL::PER], accp[TL::PER];
 #pragma unroll
         for (int j = 0; j < TL::PER; ++j) {
             acc[j] = zero4();
@@ -122,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
             acc[j] = tile_nt<TI, DK>(Kp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, acc[j]);
             accp[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, accp[j]);
         }
-        // gate factors and masks (LDS reads only), then the stores
+        // gate factors and masks (LDS reads only)
         if (TL::active()) {
 #pragma unroll
             for (int j = 0; j < TL::PER; ++j)
@@ -133,6 +231,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
                     acc[j][i] = s < t ? beta_s[t] * acc[j][i] * e : 0.f;
                     accp[j][i] = s <= t ? accp[j][i] * e : 0.f;
                 }
+        }
+        __syncthreads();   // K / Q tiles dead: R0 becomes the inverse's and P's space
+        if (TL::active()) {
 #pragma unroll
             for (int j = 0; j < TL::PER; ++j)
 #pragma unroll
@@ -140,35 +241,29 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
                     const int t = TL::row(j, i), s = TL::col(j);
                     A_s[t * LDA + s] = acc[j][i];
                     if (TRANS_OUT)
-                        Pout[s * C + t] = from_f<TI>(accp[j][i]);
+                        Ps[s * LC + t] = from_f<TI>(accp[j][i]);
                     else
-                        Pout[t * C + s] = from_f<TI>(accp[j][i]);
+                        Ps[t * LC + s] = from_f<TI>(accp[j][i]);
                 }
         }
     }
     __syncthreads();
+    const long cc = ((long)bh * p.NT + n) * C * C;
+    lds_to_global<TI, C, C>(static_cast<TI*>(p.Pm) + cc, C, Ps, LC, C);
 
-    // -- T = (I + A)^{-1}: column c of T solves (I + A) x = e_c by forward
-    //    substitution; lane c of wave 0 owns column c, A rows are LDS broadcasts.
-    if (wave_id() == 0) {
-        const int c = lane_id();
-        float x[C];
+    // -- T = (I + A)^{-1}
+    unit_lower_inverse<C>(A_s, Ts, LDA, Ysc);
+
+    // -- T (or T^T) to the workspace, 16 bytes per store
+    {
+        constexpr int VW = 16 / sizeof(TI), VPR = C / VW, NV = C * VPR;
+        TI* __restrict__ Tout = static_cast<TI*>(p.Tm) + cc;
+        for (int idx = threadIdx.x; idx < NV; idx += kThreads) {
+            const int r = idx / VPR, c0 = (idx % VPR) * VW;
+            TI out[VW];
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            float acc = (i == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int j = 0; j < i; ++j) acc -= A_s[i * LDA + j] * x[j];
-            x[i] = acc;
-        }
-        if (c < C) {
-            TI* __restrict__ Tout = static_cast<TI*>(p.Tm) + ((long)bh * p.NT + n) * C * C;
-            if (TRANS_OUT) {
-#pragma unroll
-                for (int i = 0; i < C; ++i) Tout[c * C + i] = from_f<TI>(x[i]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < C; ++i) Tout[i * C + c] = from_f<TI>(x[i]);
-            }
+            for (int e = 0; e < VW; ++e) out[e] = from_f<TI>(TRANS_OUT ? Ts[(c0 + e) * LDA + r] : Ts[r * LDA + c0 + e]);
+            *reinterpret_cast<uint4*>(Tout + r * C + c0) = *reinterpret_cast<const uint4*>(out);
         }
     }
 }

@@ -23,10 +23,7 @@ constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 // Static LDS of each kernel (bytes), mirrored from the kernels' declarations
 // so that configurations that cannot fit are never instantiated.
 template <typename TI, int GATE, int C, int DK> constexpr size_t prep_lds() {
-    constexpr size_t E = sizeof(TI);
-    constexpr int LDK = DK + Pad<TI>::value;
-    constexpr int GW = GateLayout<GATE, DK>::GW;
-    return 4 * (C * GW + C + C * (C + 4)) + E * C * LDK * (GATE == kGateVector ? 3 : 2) + 64;
+    return PrepSmem<TI, GATE, C, DK>::TOTAL;
 }
 template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_state_lds() {
     constexpr size_t E = sizeof(TI);
