@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--policy", default=None, choices=[None, "save", "recompute"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-recompute-leg", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run --steps device-to-device copies of MIB MiB "
+                         "(a known-size reference for the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -90,6 +93,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "launches": max(1, args.steps)}), flush=True)
+        return
     B.lib()  # fail loudly if the HIP library is missing
     w = W.CONFIGS[args.workload]
     policy = args.policy or w.policy
@@ -186,6 +199,17 @@ def main():
                         "algorithmic_bytes_per_launch": int(by * units),
                         "algorithmic_flops_per_launch": int(fl * units),
                         "achieved_gbs": round(ach_gbs, 1), "avg_launch_ms": round(avg_s * 1e3, 4)}
+
+    # measured HBM traffic of the dominant kernel, from the committed rocprofv3
+    # summary of this workload -- only while the kernel sources are unchanged
+    if roofline is not None:
+        from delta_rule_linear_gated_amd import profiling
+        summ = profiling.load_summary(os.path.join(ROOT, "profiles", f"{w.name}_all_kernels_rocprof.md"))
+        if summ and summ.get("source_sha256") == profiling.source_digest():
+            rec = summ["kernels"].get(roofline["kernel"], {})
+            if "bytes" in rec:
+                roofline["traffic"] = rec["bytes"]
+                roofline["traffic_source"] = f"profiles/{w.name}_all_kernels_rocprof.md"
 
     other = None
     if not args.no_recompute_leg and w.B * w.H * w.T > 0:

@@ -1,0 +1,157 @@
+"""Summaries of rocprofv3 output for the operator's kernels.
+
+``python -m delta_rule_linear_gated_amd.profiling summarize ...`` turns the CSV
+output of a ``--kernel-trace --stats`` run and of ``--pmc FETCH_SIZE`` /
+``--pmc WRITE_SIZE`` runs (plus the same counters over a device copy of known
+size) into a short markdown summary with an embedded JSON block.  bench.py
+reads that block to report the measured HBM traffic of its dominant kernel,
+and only while the kernel sources still hash to the digest recorded in it.
+
+Counter scaling: each counter is divided by what it reads for the reference
+copy (bytes moved / counter value), so a kernel's traffic is
+``FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale`` (KiB -> bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources (csrc/*), in name order."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if os.path.isfile(path):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_key(name: str) -> str:
+    """Map a demangled rocprofv3 kernel name to the names dn_profile_collect uses."""
+    if "prep_kernel" in name:
+        return "prep_bwd" if re.search(r"true>\(", name) else "prep"
+    if "fwd_state_kernel" in name:
+        return "fwd_state" if re.search(r"true, true>\(", name) or re.search(r"false, true>\(", name) \
+            else "fwd_state_recompute"
+    for k in ("bwd_state", "bwd_chunk"):
+        if k + "_kernel" in name:
+            return k
+    if "copyBuffer" in name or "elementwise" in name:
+        return "copy"
+    return name
+
+
+def _csv(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    hits = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def counter_means(d):
+    """{kernel key: mean counter value per dispatch} of one --pmc run."""
+    acc = collections.defaultdict(list)
+    for r in _csv(_find(d, "counter_collection.csv")):
+        acc[kernel_key(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def copy_value(d):
+    """Counter value of the copy kernel dispatches (the largest-valued copy kernel)."""
+    best = 0.0
+    for r in _csv(_find(d, "counter_collection.csv")):
+        if kernel_key(r["Kernel_Name"]) == "copy":
+            best = max(best, float(r["Counter_Value"]))
+    return best
+
+
+def summarize(args) -> str:
+    stats = _csv(_find(args.trace, "kernel_stats.csv"))
+    fetch = counter_means(args.fetch)
+    write = counter_means(args.write)
+    copy_kib = args.copy_mib * 1024.0
+    fetch_scale = copy_kib / copy_value(args.copy_fetch)
+    write_scale = copy_kib / copy_value(args.copy_write)
+    kern = {}
+    for r in stats:
+        k = kernel_key(r["Name"])
+        if k == "copy":
+            continue
+        f = fetch.get(k)
+        w = write.get(k)
+        rec = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+               "share": float(r["Percentage"]) / 100.0}
+        if f is not None and w is not None:
+            rec.update(fetch_kib=f, write_kib=w,
+                       bytes=int((f * fetch_scale + w * write_scale) * 1024))
+        kern[k] = rec
+    data = {"workload": args.workload, "source_sha256": source_digest(),
+            "fetch_scale": fetch_scale, "write_scale": write_scale, "copy_mib": args.copy_mib,
+            "kernels": kern}
+    lines = [f"# {args.title}", "", "Commands (from /tmp, TMPDIR=/tmp):", ""]
+    for c in args.command:
+        lines.append(f"    {c}")
+    lines += ["", "| kernel | calls | avg us | share | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |",
+              "|---|---|---|---|---|---|---|"]
+    for k, r in kern.items():
+        lines.append(f"| {k} | {r['calls']} | {r['avg_us']:.1f} | {r['share']:.3f} | "
+                     f"{r.get('fetch_kib', float('nan')):.0f} | {r.get('write_kib', float('nan')):.0f} | "
+                     f"{r.get('bytes', 0):,} |")
+    lines += ["", f"Copy calibration ({args.copy_mib} MiB read + written per copy): FETCH_SIZE scale "
+              f"{fetch_scale:.4f}, WRITE_SIZE scale {write_scale:.4f} (true KiB per counted KiB).", "",
+              "```json", json.dumps(data, indent=1), "```", ""]
+    return "\n".join(lines)
+
+
+def load_summary(path):
+    """The JSON block of a summary written by ``summarize`` (None if absent)."""
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"```json\n(.*?)\n```", txt, re.S)
+    return json.loads(m.group(1)) if m else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("summarize")
+    s.add_argument("--trace", required=True)
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--copy-fetch", required=True)
+    s.add_argument("--copy-write", required=True)
+    s.add_argument("--copy-mib", type=float, required=True)
+    s.add_argument("--workload", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", action="append", default=[])
+    s.add_argument("--out", required=True)
+    sub.add_parser("digest")
+    a = ap.parse_args()
+    if a.cmd == "digest":
+        print(source_digest())
+        return
+    txt = summarize(a)
+    with open(a.out, "w") as f:
+        f.write(txt)
+    print(txt)
+
+
+if __name__ == "__main__":
+    main()

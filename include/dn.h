@@ -35,7 +35,8 @@
  *   - On any error nothing is enqueued, a negative dn_status is returned and
  *     dn_last_error() describes it.  No C++ exception crosses this boundary.
  *   - NaN / Inf in the inputs propagate to the outputs; they are not errors.
- *   - The library keeps no state between calls except the per-thread error text;
+ *   - The library keeps no state between calls except the per-thread error text
+ *     and, while dn_profile_enable(1) is in effect, the recorded timing events;
  *     calls from several host threads are safe.  Two calls that share a
  *     workspace must be ordered on one stream.
  *
