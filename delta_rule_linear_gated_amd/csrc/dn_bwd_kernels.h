@@ -63,8 +63,9 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     TI* Db = DB_IN_PT ? PT : DbSep;
 
     const int DVr = p.DVr;
-    const int bh = blockIdx.y;
-    const int v0 = blockIdx.x * BV;
+    int bh, vblk;
+    head_and_block(DVr / BV, p.BH, bh, vblk);
+    const int v0 = vblk * BV;
     using TS = Tiles<BV, DK>;
     f32x4 dS[TS::PER];
 #pragma unroll

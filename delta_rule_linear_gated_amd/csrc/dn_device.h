@@ -466,6 +466,24 @@ __device__ __forceinline__ void lds_to_global(T* __restrict__ g, long gld, const
     }
 }
 
+// Workgroup -> (head, d_v block) for the sequential kernels (1-D grid of
+// nblk * BH workgroups).  Workgroups are handed to the 8 XCDs round-robin by
+// id, and each XCD has its own L2; the d_v blocks of one head read the same
+// q / k / T / P tiles, so they are given ids that are equal mod 8 (same XCD,
+// shared L2).  Falls back to the plain order when BH is not a multiple of 8.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void head_and_block(int nblk, int BH, int& bh, int& blk) {
+    const int id = blockIdx.x;
+    if (BH % kXcds == 0) {
+        const int x = id % kXcds, k = id / kXcds;
+        bh = (k / nblk) * kXcds + x;
+        blk = k % nblk;
+    } else {
+        bh = id / nblk;
+        blk = id % nblk;
+    }
+}
+
 // Sum over the 16 lanes that share (lane >> 4): the lanes holding one output row.
 __device__ __forceinline__ float row16_sum(float x) {
     x += __shfl_xor(x, 1);

@@ -360,8 +360,9 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     __shared__ __align__(16) TI UT[BV * LDC];    // U^T              [v][t]
 
     const int DVr = p.DVr;
-    const int bh = blockIdx.y;
-    const int v0 = blockIdx.x * BV;
+    int bh, vblk;
+    head_and_block(DVr / BV, p.BH, bh, vblk);
+    const int v0 = vblk * BV;
     using TS = Tiles<BV, DK>;
     f32x4 S[TS::PER];
 #pragma unroll

@@ -65,10 +65,10 @@ hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t s
         prof_end(stream);
         prof_begin(stream, "fwd_state");
         if (save)
-            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, true>), dim3(D / BV, BH),
+            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, true>), dim3((D / BV) * BH),
                                dim3(kThreads), 0, stream, p);
         else
-            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, true>), dim3(D / BV, BH),
+            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, true>), dim3((D / BV) * BH),
                                dim3(kThreads), 0, stream, p);
         prof_end(stream);
         return hipGetLastError();
@@ -87,12 +87,12 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
         prof_end(stream);
         if (!have_states) {
             prof_begin(stream, "fwd_state_recompute");
-            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, false>), dim3(D / BV, BH),
+            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, false>), dim3((D / BV) * BH),
                                dim3(kThreads), 0, stream, p);
             prof_end(stream);
         }
         prof_begin(stream, "bwd_state");
-        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3(D / BV, BH), dim3(kThreads), 0,
+        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3((D / BV) * BH), dim3(kThreads), 0,
                            stream, p);
         prof_end(stream);
         prof_begin(stream, "bwd_chunk");
