@@ -99,7 +99,6 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     for (int n = p.NT - 1; n >= 0; --n) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
-        const long row0 = (long)bh * p.T + t0;
         // write back lambda and dv of the chunk done last iteration (a full chunk of
         // work after they were formed); the sync keeps commit() off their tiles
         if (n + 1 < p.NT) {
@@ -255,18 +254,19 @@ struct BwdChunkSmem {
     static constexpr size_t GAM = al(BIG_END);                                    // gam [C][D] or [C]
     static constexpr size_t ROWF = GAM + al(GATE == kGateVector ? C * D * 4 : C * 4);  // [2][C] (scalar)
     static constexpr size_t BETA = ROWF + al(2 * C * 4);                          // [C]
-    static constexpr size_t RED_R = BETA + al(C * 4);                             // [D/16][C]
-    // column partials: [C/16][D] (Kd dKd) and [SPLIT][D] (sum_v S0 dS1, SPLIT threads per column)
-    static constexpr int SPLIT = kThreads / D > 0 ? kThreads / D : 1;
-    static constexpr int REDC_ROWS = (C / 16) > SPLIT ? (C / 16) : SPLIT;
-    static constexpr size_t RED_C = RED_R + al((D / 16) * C * 4);                 // [REDC_ROWS][D]
-    static constexpr size_t LASTS = RED_C + al(REDC_ROWS * D * 4);                // [D]
+    static constexpr size_t RED_R = BETA + al(C * 4);                             // [D/16][C] row partials
+    static constexpr size_t RED_C = RED_R + al((D / 16) * C * 4);                 // [C/16][D] column partials
+    static constexpr size_t LASTS = RED_C + al((C / 16) * D * 4);                 // [D]
     static constexpr size_t DBR = LASTS + al(D * 4);                              // [C]
     static constexpr size_t TOTAL = DBR + al(C * 4);
     // dq / dk write-back tiles [C][LD] each at offset 0; d gam of the vector gate
     // [C][D] fp32 after them, written once every phase-C tile is dead
     static constexpr size_t DGB = al(2 * C * LD * E);
     static_assert(GATE != kGateVector || DGB + C * D * 4 <= BIG_END, "d gam buffer");
+    // per-thread partials of sum_v S0 dS1 [row blocks of the S0 register tile][D] fp32,
+    // at offset 0 right after the d_v loop
+    using RS = RegB<TI, VB, D>;
+    static_assert(RS::BR * D * 4 <= BIG_END, "S0 dS1 partials");
     static_assert(2 * C * LD * E <= BIG_END, "write-back tiles");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -333,6 +333,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         rv.load(v + v0, D, valid);
     };
     load_block(0);
+    // sum_v S0[v][c] dS1[v][c] over this thread's rows of every block
+    float ls[L::RS::PER][L::RS::VW] = {};
     rg.commit(rowf, gam_s, beta_s);
     __syncthreads();
     const GateLds<GATE, C, D> gf{rowf, gam_s, valid - 1};
@@ -342,6 +344,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         rK.store(KG, LD);   // scalar: Gam_t is applied to X's rows
     rT.store_t(TLs, LC, Identity());
     auto commit_block = [&]() {
+        rS0.dot_rows(rdS1, ls);
         rS0.store_n(S0B, LD, Identity());
         rS0.store_t(S0BT, LVB, Identity());
         rdS1.store_t(DS1T, LVB, Identity());
@@ -360,8 +363,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     zero_acc<C, C>(dA);
     zero_acc<C, C>(dP);
     float dbr_part[TX::PER][4] = {};
-    float lastS_acc = 0.f;   // sum_v S0[v][c] dS1[v][c] for c = threadIdx.x % D (split over threads)
-    constexpr int SPLIT = L::SPLIT;
 #pragma unroll 1
     for (int b = 0; b < NVB; ++b) {
         if (b + 1 < NVB) load_block(b + 1);
@@ -371,10 +372,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         gemm_nt<TI, C, VB, D>(X, KG, LD, S0B, LD);
         gemm_nt<TI, C, D, VB>(dq, DOB, LVB, S0BT, LVB);
         gemm_nt<TI, C, D, VB>(dkp, LAMB, LVB, S0BT, LVB);
-        if (threadIdx.x < D * SPLIT) {
-            const int c = threadIdx.x % D, h = threadIdx.x / D;
-            for (int vv = h; vv < VB; vv += SPLIT) lastS_acc += to_f(S0BT[c * LVB + vv]) * to_f(DS1T[c * LVB + vv]);
-        }
         if (TX::active()) {
             float rb[TX::PER][4];   // LDS reads first, then the writes
 #pragma unroll
@@ -421,28 +418,38 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     rk.load(k, D, valid);
 
     // ---------------- dbeta_R, sum_v S0 dS1, and the d_v-contraction epilogues
+    float* lsred = reinterpret_cast<float*>(smem);   // d_v-loop tiles are dead
     if (TX::active()) {
 #pragma unroll
-        for (int j = 0; j < TX::PER; ++j)
+        for (int im = 0; im < TX::RM; ++im)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float s = row16_sum(dbr_part[j][i]);
-                if ((lane_id() & 15) == 0) red_r[(TX::n0(j) / 16) * C + TX::row(j, i)] = s;
+                float s = 0.f;
+#pragma unroll
+                for (int in = 0; in < TX::RN; ++in) s += dbr_part[im * TX::RN + in][i];
+                s = row16_sum(s);
+                if ((lane_id() & 15) == 0) red_r[TX::cg() * C + TX::row(im * TX::RN, i)] = s;
             }
     }
-    if (threadIdx.x < D * SPLIT) red_c[(threadIdx.x / D) * D + threadIdx.x % D] = lastS_acc;
-    __syncthreads();   // red_r / red_c partials complete
+#pragma unroll
+    for (int i = 0; i < L::RS::PER; ++i) {
+        if (L::RS::owns(i)) {
+#pragma unroll
+            for (int k = 0; k < L::RS::VW; ++k) lsred[L::RS::rowblk(i) * D + L::RS::col0(i) + k] = ls[i][k];
+        }
+    }
+    __syncthreads();   // row and column partials complete
     for (int t = threadIdx.x; t < C; t += kThreads) {
         float s = 0.f;
-        for (int b = 0; b < VB / 16; ++b) s += red_r[b * C + t];
+        for (int b = 0; b < TX::WN; ++b) s += red_r[b * C + t];
         dbr[t] = s;
     }
     for (int c = threadIdx.x; c < D; c += kThreads) {
         float s = 0.f;
-        for (int h = 0; h < SPLIT; ++h) s += red_c[h * D + c];
+        for (int h = 0; h < L::RS::BR; ++h) s += lsred[h * D + c];
         lastS[c] = s;
     }
-    __syncthreads();   // red_c is reused below
+    __syncthreads();   // red_r and the partials are reused below
     // dq = Gam dQg ; dk+ = -beta Gam dKg ; dk- = Gd dKd
     if (TO::active()) {
 #pragma unroll
@@ -457,7 +464,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             }
         }
     }
-    __syncthreads();   // d_v-loop tiles dead
 
     // ---------------- phase B: dA~ and dP~ into LDS
     {
@@ -525,13 +531,15 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                     qv[j][i] = to_f(QlT[c * LC + t]) / fp;
                 }
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j) {
+            for (int in = 0; in < TO::RN; ++in) {
                 float colp = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) colp += kv[j][i] * dkm[j][i];
+                for (int im = 0; im < TO::RM; ++im)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) colp += kv[im * TO::RN + in][i] * dkm[im * TO::RN + in][i];
                 colp += __shfl_xor(colp, 16);
                 colp += __shfl_xor(colp, 32);
-                if (lane_id() < 16) red_c[(TO::m0(j) / 16) * D + TO::col(j)] = colp;
+                if (lane_id() < 16) red_c[TO::rg() * D + TO::col(in)] = colp;
             }
         }
         float dbA[TO::PER][4];
@@ -588,11 +596,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 }
             // dbeta = dbeta_R + rowsum(K+ Y)
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j)
+            for (int im = 0; im < TO::RM; ++im)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float s2 = row16_sum(dbA[j][i]);
-                    if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s2;
+                    float s2 = 0.f;
+#pragma unroll
+                    for (int in = 0; in < TO::RN; ++in) s2 += dbA[im * TO::RN + in][i];
+                    s2 = row16_sum(s2);
+                    if ((lane_id() & 15) == 0) red_r[TO::cg() * C + TO::row(im * TO::RN, i)] = s2;
                 }
         }
         __syncthreads();
@@ -600,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         lds_to_global<TI, C, D>(static_cast<TI*>(p.dk) + row0 * D, D, dks, LD, valid);
         for (int t = threadIdx.x; t < valid; t += kThreads) {
             float s2 = dbr[t];
-            for (int b = 0; b < D / 16; ++b) s2 += red_r[b * C + t];
+            for (int b = 0; b < TO::WN; ++b) s2 += red_r[b * C + t];
             p.dbeta[row0 + t] = s2;
         }
         if (GATE == kGateNone) return;
@@ -616,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             __syncthreads();
             for (int c = threadIdx.x; c < D; c += kThreads) {
                 float last = fexp(gl[c]) * lastS[c];
-                for (int b = 0; b < C / 16; ++b) last += red_c[b * D + c];
+                for (int b = 0; b < TO::WM; ++b) last += red_c[b * D + c];
                 float acc = 0.f;
                 for (int t = valid - 1; t >= 0; --t) {
                     acc += dgb[t * D + c] + (t == valid - 1 ? last : 0.f);
@@ -626,11 +637,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         } else {
             if (TO::active()) {
 #pragma unroll
-                for (int j = 0; j < TO::PER; ++j)
+                for (int im = 0; im < TO::RM; ++im)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float s2 = row16_sum(dgm[j][i]);
-                        if ((lane_id() & 15) == 0) red_r[(TO::n0(j) / 16) * C + TO::row(j, i)] = s2;
+                        float s2 = 0.f;
+#pragma unroll
+                        for (int in = 0; in < TO::RN; ++in) s2 += dgm[im * TO::RN + in][i];
+                        s2 = row16_sum(s2);
+                        if ((lane_id() & 15) == 0) red_r[TO::cg() * C + TO::row(im * TO::RN, i)] = s2;
                     }
             }
             __syncthreads();
@@ -639,7 +653,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 float part = 0.f;
                 for (int c = lane_id(); c < D; c += 64) {
                     float x = gf.GC(c) * lastS[c];
-                    for (int b = 0; b < C / 16; ++b) x += red_c[b * D + c];
+                    for (int b = 0; b < TO::WM; ++b) x += red_c[b * D + c];
                     part += x;
                 }
 #pragma unroll
@@ -647,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 const int t = lane_id();
                 float x = 0.f;
                 if (t < valid) {
-                    for (int b = 0; b < D / 16; ++b) x += red_r[b * C + t];
+                    for (int b = 0; b < TO::WN; ++b) x += red_r[b * C + t];
                     if (t == valid - 1) x += part;
                 }
                 // reverse inclusive scan over t: dg_t = sum_{s >= t} x_s

@@ -146,6 +146,9 @@ template <int M, int N> struct Tiles {
     static constexpr int PER = RM * RN;
     static_assert(WM > 0 && WM * WN <= kWaves && RM * WM == TM && RN * WN == TN, "tile grid");
     __device__ __forceinline__ static bool active() { return wave_id() < WM * WN; }
+    // the wave's column group (0..WN-1; its RN tiles share rows) and row group (0..WM-1)
+    __device__ __forceinline__ static int cg() { return wave_id() % WN; }
+    __device__ __forceinline__ static int rg() { return wave_id() / WN; }
     __device__ __forceinline__ static bool valid(int) { return active(); }
     __device__ __forceinline__ static int m0(int j) { return ((wave_id() / WN) * RM + j / RN) * 16; }
     __device__ __forceinline__ static int n0(int j) { return ((wave_id() % WN) * RN + j % RN) * 16; }
@@ -395,6 +398,24 @@ template <typename T, int ROWS, int COLS> struct RegB {
             }
         }
     }
+    // Blocks this thread owns (threads past the last block hold a duplicate).
+    __device__ __forceinline__ static bool owns(int i) { return threadIdx.x + i * kThreads < NB; }
+    __device__ __forceinline__ static int col0(int i) { return (blk(i) / BR) * VW; }
+    __device__ __forceinline__ static int rowblk(int i) { return blk(i) % BR; }
+    // acc[i][k] += sum over the block's rows r of this[r][c] * o[r][c], c = col0(i) + k,
+    // for two tiles loaded with the same shape (so the same thread mapping).
+    // Every row counts: for tiles loaded with valid = ROWS.
+    __device__ __forceinline__ void dot_rows(const RegB& o, float (&acc)[PER][VW]) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int e = 0; e < BRW; ++e) {
+                const T* x = reinterpret_cast<const T*>(&r[i][e]);
+                const T* y = reinterpret_cast<const T*>(&o.r[i][e]);
+#pragma unroll
+                for (int k = 0; k < VW; ++k) acc[i][k] += to_f(x[k]) * to_f(y[k]);
+            }
+    }
     // lds[c * ldl + r] = f(r, c, x).  Two-phase like RegN::store.
     template <class F> __device__ __forceinline__ void store_t(T* lds, int ldl, F f) const {
         TV outv[PER][VW];
@@ -484,12 +505,23 @@ __device__ __forceinline__ void head_and_block(int nblk, int BH, int& bh, int& b
     }
 }
 
-// Sum over the 16 lanes that share (lane >> 4): the lanes holding one output row.
+// x as seen from another lane of the same row of 16 lanes, by a DPP control:
+// quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2),
+// row_half_mirror = 0x141 (lane i of 8 <- 7 - i), row_mirror = 0x140 (i of 16 <- 15 - i).
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes that share (lane >> 4): the lanes holding one output
+// row of an MFMA tile.  Butterfly over lane ^ 1, lane ^ 2, then the other
+// quad of the 8 and the other 8 of the 16 (every lane of a quad / an 8 holds
+// the same partial by then); DPP moves, no LDS traffic.  Every lane of the
+// wave must be active.
 __device__ __forceinline__ float row16_sum(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    x += dpp_f<0x140>(x);
     return x;
 }
 

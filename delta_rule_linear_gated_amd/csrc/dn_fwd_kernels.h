@@ -142,7 +142,7 @@ template <typename TI, int GATE, int C, int DK> struct PrepSmem {
 template <typename TI, int GATE, int C, int DK, bool TRANS_OUT>
 __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
     using L = PrepSmem<TI, GATE, C, DK>;
-    constexpr int LDK = L::LDK, LDA = L::LDA, LC = L::LC, GW = L::GW;
+    constexpr int LDK = L::LDK, LDA = L::LDA, LC = L::LC;
     constexpr bool VEC = L::VEC;
     __shared__ __align__(16) char smem[L::TOTAL];
     TI* Kp = reinterpret_cast<TI*>(smem + L::KP);   // K, or K e^{gam - centre}
