@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     constexpr bool VEC = GATE == kGateVector;
     __shared__ float gam_s[VEC ? C * DK : C];
     __shared__ float rowf[2 * C];
-    __shared__ float beta_s[C];
+    __shared__ __align__(16) float beta_s[C];
     __shared__ __align__(16) TI dSs[BV * LDK];   // dS1 operand     [v][c]
     __shared__ __align__(16) TI Kd[C * LDK];     // K Gam_C / Gam   [t][c]
     __shared__ __align__(16) TI PT[C * LDC];     // P^T             [t][s]
@@ -66,16 +66,13 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     int bh, vblk;
     head_and_block(DVr / BV, p.BH, bh, vblk);
     const int v0 = vblk * BV;
-    using TS = Tiles<BV, DK>;
+    // dS held transposed, dS^T [c][v] tiles (4 consecutive keys of one row v per lane)
+    using TS = Tiles<DK, BV>;
     f32x4 dS[TS::PER];
 #pragma unroll
     for (int j = 0; j < TS::PER; ++j) {
         dS[j] = zero4();
-        if (p.dhT && TS::active()) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dS[j][i] = p.dhT[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)];
-        }
+        if (p.dhT && TS::active()) dS[j] = ld4<float>(p.dhT + ((long)bh * DVr + v0 + TS::col(j)) * DK + TS::row(j, 0));
     }
 
     RegB<TI, C, DK> rq, rk;
@@ -111,10 +108,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         // (a) dS1 of this chunk: operand copy (written to the workspace from LDS below)
         if (TS::active()) {
 #pragma unroll
-            for (int j = 0; j < TS::PER; ++j) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dSs[TS::row(j, i) * LDK + TS::col(j)] = from_f<TI>(dS[j][i]);
-            }
+            for (int j = 0; j < TS::PER; ++j) st4<TI>(dSs + TS::col(j) * LDK + TS::row(j, 0), dS[j]);
         }
         // (b) commit this chunk's tiles
         rg.commit(rowf, gam_s, beta_s);
@@ -146,50 +140,43 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
             gemm_nt<TI, C, BV, DK>(dU, Kd, LDK, dSs, LDK);
             if (TX::active()) {
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dUT[TX::col(j) * LDC + TX::row(j, i)] = from_f<TI>(dU[j][i]);
-                }
+                for (int j = 0; j < TX::PER; ++j) st4<TI>(dUT + TX::col(j) * LDC + TX::row(j, 0), dU[j]);
             }
         }
         __syncthreads();
-        // (d) lambda = T^T dU ; dv = beta lambda ; keep -(beta lambda)^T
+        // (d) lambda^T = dU^T T ; dv = beta lambda ; keep -(beta lambda)^T.  lambda^T
+        //     tiles give a lane 4 consecutive v of one row t of lambda and dv
         {
-            f32x4 L[TX::PER];
-            zero_acc<C, BV>(L);
-            gemm_nt<TI, C, BV, C>(L, TT, LDC, dUT, LDC);
-            if (TX::active()) {
-                float bt[TX::PER][4];   // LDS reads first, then the writes
+            using TL = Tiles<BV, C>;
+            f32x4 L[TL::PER];
+            zero_acc<BV, C>(L);
+            gemm_nt<TI, BV, C, C>(L, dUT, LDC, TT, LDC);
+            if (TL::active()) {
+                float bt[TL::PER];   // LDS reads first, then the writes
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j)
+                for (int j = 0; j < TL::PER; ++j) bt[j] = beta_s[TL::col(j)];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) bt[j][i] = beta_s[TX::row(j, i)];
+                for (int j = 0; j < TL::PER; ++j) {
+                    const int t = TL::col(j), c = TL::row(j, 0);
+                    const f32x4 bl = bt[j] * L[j];
+                    st4<TI>(Lb + t * LDV + c, L[j]);
+                    st4<TI>(Db + t * LDV + c, bl);
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = TX::row(j, i), c = TX::col(j);
-                        const float l = L[j][i];
-                        const float bl = bt[j][i] * l;
-                        Lb[t * LDV + c] = from_f<TI>(l);
-                        Db[t * LDV + c] = from_f<TI>(bl);
-                        bLT[c * LDC + t] = from_f<TI>(-bl);
-                    }
+                    for (int i = 0; i < 4; ++i) bLT[(c + i) * LDC + t] = from_f<TI>(-bl[i]);
                 }
             }
         }
         __syncthreads();
-        // (e) dS0 = dS1 Diag(Gam_C) + dO^T (Q Gam) - (beta lambda)^T (K Gam)
+        // (e) dS0^T = Diag(Gam_C) dS1^T + (Q Gam)^T dO - (K Gam)^T (beta lambda)
         if (GATE != kGateNone && TS::active()) {
 #pragma unroll
             for (int j = 0; j < TS::PER; ++j) {
-                const float f = gf.GC(TS::col(j));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dS[j][i] *= f;
+                for (int i = 0; i < 4; ++i) dS[j][i] *= gf.GC(TS::row(j, i));
             }
         }
-        gemm_nt<TI, BV, DK, C>(dS, dOT, LDC, QgT, LDC);
-        gemm_nt<TI, BV, DK, C>(dS, bLT, LDC, KgT, LDC);
+        gemm_nt<TI, DK, BV, C>(dS, QgT, LDC, dOT, LDC);
+        gemm_nt<TI, DK, BV, C>(dS, KgT, LDC, bLT, LDC);
         __syncthreads();
     }
     if (p.NT > 0) {   // lambda and dv of chunk 0
@@ -198,11 +185,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     }
     if (p.dh0 && TS::active()) {
 #pragma unroll
-        for (int j = 0; j < TS::PER; ++j) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p.dh0[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)] = dS[j][i];
-        }
+        for (int j = 0; j < TS::PER; ++j)
+            st4<float>(p.dh0 + ((long)bh * DVr + v0 + TS::col(j)) * DK + TS::row(j, 0), dS[j]);
     }
 }
 

@@ -195,6 +195,24 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NACC]) {
     for (int j = 0; j < NACC; ++j) acc[j] = zero4();
 }
 
+// Four consecutive elements p[0..3] (16-byte aligned for fp32, 8-byte for bf16):
+// one vector store / load.  An accumulator tile gives each lane 4 consecutive
+// rows of one column, so these move a lane's 4 values of a tile whose LDS (or
+// global) layout is transposed with respect to the tile.
+template <typename T> struct Vec4;
+template <> struct Vec4<float> { typedef f32x4 type; };
+template <> struct Vec4<bf16> { typedef __attribute__((ext_vector_type(4))) __bf16 type; };
+
+template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {
+    typename Vec4<T>::type v = {from_f<T>(a), from_f<T>(b), from_f<T>(c), from_f<T>(d)};
+    *reinterpret_cast<typename Vec4<T>::type*>(p) = v;
+}
+template <typename T> __device__ __forceinline__ void st4(T* p, f32x4 x) { st4<T>(p, x[0], x[1], x[2], x[3]); }
+template <typename T> __device__ __forceinline__ f32x4 ld4(const T* p) {
+    const typename Vec4<T>::type v = *reinterpret_cast<const typename Vec4<T>::type*>(p);
+    return f32x4{to_f(v[0]), to_f(v[1]), to_f(v[2]), to_f(v[3])};
+}
+
 // ---------------------------------------------------------------------------
 // Global -> LDS staging of a ROWS x COLS row-major tile (global row stride gld),
 // rows >= valid_rows are zero.  f(r, c, x) maps each value (as float) before it

@@ -346,12 +346,12 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     constexpr int GW = GateLayout<GATE, DK>::GW;
     __shared__ float gam_s[GATE == kGateVector ? C * DK : C];
     __shared__ float rowf[2 * C];
-    __shared__ float beta_s[C];
+    __shared__ __align__(16) float beta_s[C];
     __shared__ __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
     __shared__ __align__(16) TI Qg[C * LDK];     // Q Gam            [t][c]
     __shared__ __align__(16) TI Kg[C * LDK];     // K Gam            [t][c]
     __shared__ __align__(16) TI KdT[DK * LDC];   // (K Gam_C / Gam)^T [c][t]
-    __shared__ __align__(16) TI Vb[C * LDV];     // V block          [t][v]
+    __shared__ __align__(16) TI VbT[BV * LDC];   // V block^T        [v][t]
     __shared__ __align__(16) TI Tl[C * LDC];     // T                [t][s]
     __shared__ __align__(16) TI Pl[C * LDC];     // P                [t][s]
     // R^T [v][t]; after (d) it holds the chunk's O [t][v] until the next iteration writes it back
@@ -363,22 +363,20 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     int bh, vblk;
     head_and_block(DVr / BV, p.BH, bh, vblk);
     const int v0 = vblk * BV;
-    using TS = Tiles<BV, DK>;
+    // the state is held transposed, S^T [c][v] tiles: a lane's 4 values are 4
+    // consecutive keys c of one row v of S (one vector store into S0's [v][c] copy)
+    using TS = Tiles<DK, BV>;
     f32x4 S[TS::PER];
 #pragma unroll
     for (int j = 0; j < TS::PER; ++j) {
         S[j] = zero4();
-        if (p.h0 && TS::active()) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[j][i] = p.h0[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)];
-        }
+        if (p.h0 && TS::active()) S[j] = ld4<float>(p.h0 + ((long)bh * DVr + v0 + TS::col(j)) * DK + TS::row(j, 0));
     }
 
     // registers of the next chunk
     RegN<TI, C, DK> rq;
     RegB<TI, C, DK> rk;
-    RegN<TI, C, BV> rv;
+    RegB<TI, C, BV> rv;
     std::conditional_t<OUTPUT, RegN<TI, C, C>, RegB<TI, C, C>> rT;
     RegN<TI, OUTPUT ? C : 16, OUTPUT ? C : 16> rP;
     GateRegs<GATE, C, DK> rg;
@@ -407,10 +405,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         // (a) state operand (saved from LDS below)
         if (TS::active()) {
 #pragma unroll
-            for (int j = 0; j < TS::PER; ++j) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Ss[TS::row(j, i) * LDK + TS::col(j)] = from_f<TI>(S[j][i]);
-            }
+            for (int j = 0; j < TS::PER; ++j) st4<TI>(Ss + TS::col(j) * LDK + TS::row(j, 0), S[j]);
         }
         // (b) commit this chunk's tiles to LDS
         rg.commit(rowf, gam_s, beta_s);
@@ -425,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             rk.store_n(Kg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
             rk.store_t(KdT, LDC, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
         }
-        rv.store(Vb, LDV);
+        rv.store_t(VbT, LDC, Identity());
         if constexpr (OUTPUT) {
             rT.store(Tl, LDC);
             rP.store(Pl, LDC);
@@ -445,19 +440,16 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             zero_acc<C, BV>(X);
             gemm_nt<TI, C, BV, DK>(X, Kg, LDK, Ss, LDK);
             if (TX::active()) {
-                // all LDS reads, then all LDS writes (see RegN::store)
-                float rv_[TX::PER][4];
+                // all LDS reads, then all LDS writes (see RegN::store); a lane's 4 rows t
+                // are consecutive in V^T, beta and R^T
+                f32x4 rv_[TX::PER];
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j)
+                for (int j = 0; j < TX::PER; ++j) {
+                    const int t = TX::row(j, 0), c = TX::col(j);
+                    rv_[j] = ld4<float>(beta_s + t) * (ld4<TI>(VbT + c * LDC + t) - X[j]);
+                }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = TX::row(j, i), c = TX::col(j);
-                        rv_[j][i] = beta_s[t] * (to_f(Vb[t * LDV + c]) - X[j][i]);
-                    }
-#pragma unroll
-                for (int j = 0; j < TX::PER; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) RT[TX::col(j) * LDC + TX::row(j, i)] = from_f<TI>(rv_[j][i]);
+                for (int j = 0; j < TX::PER; ++j) st4<TI>(RT + TX::col(j) * LDC + TX::row(j, 0), rv_[j]);
             }
         }
         __syncthreads();
@@ -468,37 +460,32 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             gemm_nt<TI, C, BV, C>(U, Tl, LDC, RT, LDC);
             if (TX::active()) {
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) UT[TX::col(j) * LDC + TX::row(j, i)] = from_f<TI>(U[j][i]);
-                }
+                for (int j = 0; j < TX::PER; ++j) st4<TI>(UT + TX::col(j) * LDC + TX::row(j, 0), U[j]);
             }
         }
         __syncthreads();
-        // (e) O = (Q Gam) S0^T + P U   (into RT, dead since (d); written back next iteration)
+        // (e) O^T = S0 (Q Gam)^T + U^T P^T   (O into RT, dead since (d); written back
+        //     next iteration; O^T tiles give a lane 4 consecutive v of one row t of O)
         if (OUTPUT) {
-            f32x4 O[TX::PER];
-            zero_acc<C, BV>(O);
-            gemm_nt<TI, C, BV, DK>(O, Qg, LDK, Ss, LDK);
-            gemm_nt<TI, C, BV, C>(O, Pl, LDC, UT, LDC);
-            if (TX::active()) {
+            using TOT = Tiles<BV, C>;
+            f32x4 OT[TOT::PER];
+            zero_acc<BV, C>(OT);
+            gemm_nt<TI, BV, C, DK>(OT, Ss, LDK, Qg, LDK);
+            gemm_nt<TI, BV, C, C>(OT, UT, LDC, Pl, LDC);
+            if (TOT::active()) {
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) RT[TX::row(j, i) * LDV + TX::col(j)] = from_f<TI>(O[j][i]);
-                }
+                for (int j = 0; j < TOT::PER; ++j) st4<TI>(RT + TOT::col(j) * LDV + TOT::row(j, 0), OT[j]);
             }
         }
-        // (f) S1 = S0 Diag(Gam_C) + U^T (K Gam_C / Gam)
+        // (f) S1^T = Diag(Gam_C) S0^T + (K Gam_C / Gam)^T U
         if (GATE != kGateNone && TS::active()) {
 #pragma unroll
             for (int j = 0; j < TS::PER; ++j) {
-                const float f = gf.GC(TS::col(j));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[j][i] *= f;
+                for (int i = 0; i < 4; ++i) S[j][i] *= gf.GC(TS::row(j, i));
             }
         }
-        gemm_nt<TI, BV, DK, C>(S, UT, LDC, KdT, LDC);
+        gemm_nt<TI, DK, BV, C>(S, KdT, LDC, UT, LDC);
         __syncthreads();
     }
     if (OUTPUT && p.NT > 0) {
@@ -508,11 +495,8 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     }
     if (OUTPUT && p.hT && TS::active()) {
 #pragma unroll
-        for (int j = 0; j < TS::PER; ++j) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p.hT[((long)bh * DVr + v0 + TS::row(j, i)) * DK + TS::col(j)] = S[j][i];
-        }
+        for (int j = 0; j < TS::PER; ++j)
+            st4<float>(p.hT + ((long)bh * DVr + v0 + TS::col(j)) * DK + TS::row(j, 0), S[j]);
     }
 }
 

@@ -30,7 +30,7 @@ template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_sta
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
     constexpr int G = GATE == kGateVector ? C * DK : C;
     constexpr int RT = BV * LDC > C * LDV ? BV * LDC : C * LDV;
-    return 4 * (G + 3 * C) + E * (BV * LDK + 2 * C * LDK + DK * LDC + C * LDV + 2 * C * LDC + BV * LDC + RT) + 64;
+    return 4 * (G + 3 * C) + E * (BV * LDK + 2 * C * LDK + DK * LDC + BV * LDC + 2 * C * LDC + BV * LDC + RT) + 64;
 }
 template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t bwd_state_lds() {
     constexpr size_t E = sizeof(TI);
