@@ -44,7 +44,7 @@ def kernel_budget(name: str, C: int, d: int, E: int, gw: int, saved: bool):
     contractions it performs (triangles halved) and the tensors it must read and
     write once.  E = bytes per I/O element, gw = gate values per step."""
     sc = C * 4 * (1 + gw)                     # beta + gate (or d gam) per chunk, fp32
-    if name == "prep":
+    if name in ("prep", "prep_recompute"):
         fl = 2 * (C * (C - 1) / 2 * d + C * (C + 1) / 2 * d) + C ** 3 / 3
         by = 2 * C * d * E + sc + C * gw * 4 + 2 * C * C * E
     elif name in ("fwd_state", "fwd_state_recompute"):
@@ -120,7 +120,7 @@ def main():
         bufs = dict(
             o=torch.empty_like(v),
             hT=torch.empty(w.B, w.H, w.dv, w.dk, device=dev),
-            states=(torch.empty(w.B, w.H, NT, w.dv, w.dk, dtype=q.dtype, device=dev) if pol == "save" else None),
+            states=(B.saved_buffer(sh, dev) if pol == "save" else None),
             wsf=B.workspace(sh, B.DN_PASS_FWD, dev),
             wsb=B.workspace(sh, B.DN_PASS_BWD if pol == "save" else B.DN_PASS_BWD_RECOMPUTE, dev),
             dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),

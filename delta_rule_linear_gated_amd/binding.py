@@ -4,9 +4,9 @@ Argument marshalling only: every step of the operator runs in the HIP kernels
 behind the C ABI.  PyTorch supplies device memory and the stream.  When the
 library is not built this module raises -- there is no fallback path.
 
-Low level (same names as the C ABI): ``dn_states_bytes``, ``dn_workspace_bytes``,
-``dn_workspace_layout``, ``dn_chunk_fwd``, ``dn_chunk_bwd``, ``dn_status_string``,
-``dn_last_error``.  Convenience: ``chunk_fwd`` / ``chunk_bwd`` allocate outputs
+Low level (same names as the C ABI): ``dn_states_bytes``, ``dn_states_layout``,
+``dn_workspace_bytes``, ``dn_workspace_layout``, ``dn_chunk_fwd``, ``dn_chunk_bwd``,
+``dn_status_string``, ``dn_last_error``.  Convenience: ``chunk_fwd`` / ``chunk_bwd`` allocate outputs
 and workspace with torch and call the above; ``DeltaRule`` is a
 ``torch.autograd.Function`` over them.
 """
@@ -26,7 +26,7 @@ DN_F32, DN_BF16 = 0, 1
 DN_GATE_NONE, DN_GATE_SCALAR, DN_GATE_VECTOR = 0, 1, 2
 DN_PASS_FWD, DN_PASS_BWD, DN_PASS_BWD_RECOMPUTE = 0, 1, 2
 
-EXPORTS = ("dn_states_bytes", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
+EXPORTS = ("dn_states_bytes", "dn_states_layout", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
            "dn_chunk_bwd", "dn_status_string", "dn_last_error", "dn_profile_enable",
            "dn_profile_collect")
 
@@ -62,6 +62,8 @@ def lib():
     L.dn_workspace_bytes.restype = sz
     L.dn_workspace_layout.argtypes = [sp, i32, ctypes.POINTER(ctypes.c_size_t)]
     L.dn_workspace_layout.restype = i32
+    L.dn_states_layout.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
+    L.dn_states_layout.restype = i32
     L.dn_chunk_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dn_chunk_fwd.restype = i32
     L.dn_chunk_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -113,6 +115,12 @@ def _stream(stream):
 
 def dn_states_bytes(shape: Shape) -> int:
     return lib().dn_states_bytes(ctypes.byref(shape))
+
+
+def dn_states_layout(shape: Shape):
+    out = (ctypes.c_size_t * 5)()
+    _check(lib().dn_states_layout(ctypes.byref(shape), out))
+    return dict(zip(("states", "T", "P", "gam", "total"), list(out)))
 
 
 def dn_workspace_bytes(shape: Shape, pass_: int) -> int:
@@ -192,19 +200,44 @@ def workspace(shape: Shape, pass_: int, device) -> torch.Tensor:
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
+def saved_buffer(shape: Shape, device) -> torch.Tensor:
+    """Byte buffer for the forward's saved states, T, P and log-decay."""
+    return torch.empty(max(dn_states_bytes(shape), 1), dtype=torch.uint8, device=device)
+
+
+def saved_regions(buf: torch.Tensor, shape: Shape) -> dict:
+    """Views of a saved buffer: states [B,H,NT,dv,dk], T and P [B,H,NT,C,C] (io
+    type), gam like g (fp32; None without a gate)."""
+    lay = dn_states_layout(shape)
+    io = torch.bfloat16 if shape.dtype == DN_BF16 else torch.float32
+    E = 2 if shape.dtype == DN_BF16 else 4
+    B, H, T, dk, dv, C = shape.B, shape.H, shape.T, shape.dk, shape.dv, shape.C
+    NT = -(-T // C) if T > 0 else 0
+
+    def view(off, dims, dt, e):
+        n = 1
+        for x in dims:
+            n *= x
+        return buf[off:off + n * e].view(dt).reshape(dims)
+
+    out = {"states": view(lay["states"], (B, H, NT, dv, dk), io, E),
+           "T": view(lay["T"], (B, H, NT, C, C), io, E),
+           "P": view(lay["P"], (B, H, NT, C, C), io, E), "gam": None}
+    if shape.gate != DN_GATE_NONE:
+        gw = (dk,) if shape.gate == DN_GATE_VECTOR else ()
+        out["gam"] = view(lay["gam"], (B, H, T) + gw, torch.float32, 4)
+    return out
+
+
 def chunk_fwd(q, k, v, beta, g=None, h0=None, C=64, save_states=True, want_hT=True, ws=None,
               stream=None):
-    """Returns (o, hT or None, states or None)."""
+    """Returns (o, hT or None, saved buffer or None); saved_regions() views the buffer."""
     _contig(q, k, v, beta, g, h0)
     sh = shape_of(q, v, g, C)
     o = torch.empty_like(v)
     hT = torch.empty(q.shape[0], q.shape[1], v.shape[-1], q.shape[-1], dtype=torch.float32,
                      device=q.device) if want_hT else None
-    states = None
-    if save_states:
-        nt = (q.shape[2] + C - 1) // C
-        states = torch.empty(q.shape[0], q.shape[1], nt, v.shape[-1], q.shape[-1], dtype=q.dtype,
-                             device=q.device)
+    states = saved_buffer(sh, q.device) if save_states else None
     if ws is None:
         ws = workspace(sh, DN_PASS_FWD, q.device)
     _check(dn_chunk_fwd(sh, q, k, v, beta, g, h0, o, hT, states, ws, ws.numel(), stream))

@@ -112,7 +112,21 @@ size_t dn_states_bytes(const dn_shape* shape) {
     dn::Problem pr;
     Dims d;
     if (check_shape(shape, &pr, &d) != DN_OK) return 0;
-    return d.BH * d.NT * d.dv * d.dk * d.E;
+    return dn::saved_layout(pr).total;
+}
+
+dn_status dn_states_layout(const dn_shape* shape, size_t offsets[5]) {
+    dn::Problem pr;
+    Dims d;
+    if (!offsets) return fail(DN_ERR_INVALID, "offsets is NULL");
+    DN_TRY(check_shape(shape, &pr, &d));
+    const dn::SavedLayout l = dn::saved_layout(pr);
+    offsets[0] = l.states;
+    offsets[1] = l.Tm;
+    offsets[2] = l.Pm;
+    offsets[3] = l.gam;
+    offsets[4] = l.total;
+    return DN_OK;
 }
 
 size_t dn_workspace_bytes(const dn_shape* shape, int pass) {
@@ -120,7 +134,7 @@ size_t dn_workspace_bytes(const dn_shape* shape, int pass) {
     Dims d;
     if (pass < DN_PASS_FWD || pass > DN_PASS_BWD_RECOMPUTE) return 0;
     if (check_shape(shape, &pr, &d) != DN_OK) return 0;
-    return dn::ws_layout(pr, pass != DN_PASS_FWD, pass == DN_PASS_BWD_RECOMPUTE).total;
+    return dn::ws_layout(pr, pass).total;
 }
 
 dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[7]) {
@@ -129,7 +143,7 @@ dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[7]
     if (!offsets) return fail(DN_ERR_INVALID, "offsets is NULL");
     if (pass < DN_PASS_FWD || pass > DN_PASS_BWD_RECOMPUTE) return fail(DN_ERR_INVALID, "unknown pass %d", pass);
     DN_TRY(check_shape(shape, &pr, &d));
-    const dn::WsLayout w = dn::ws_layout(pr, pass != DN_PASS_FWD, pass == DN_PASS_BWD_RECOMPUTE);
+    const dn::WsLayout w = dn::ws_layout(pr, pass);
     offsets[0] = w.gam;
     offsets[1] = w.Tm;
     offsets[2] = w.Pm;
@@ -149,7 +163,9 @@ dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, cons
     DN_TRY(check_shape(shape, &pr, &d));
     const size_t nk = d.BH * d.T * d.dk * d.E, nv = d.BH * d.T * d.dv * d.E;
     const size_t nb = d.BH * d.T * 4, ng = pr.gate == DN_GATE_NONE ? 0 : d.BH * d.T * d.gw * 4;
-    const size_t ns = d.BH * d.dv * d.dk * 4, nst = d.BH * d.NT * d.dv * d.dk * d.E;
+    const size_t ns = d.BH * d.dv * d.dk * 4;
+    const dn::SavedLayout sl = dn::saved_layout(pr);
+    const size_t nst = sl.total;
     if (pr.gate == DN_GATE_NONE && g) return fail(DN_ERR_INVALID, "g must be NULL without a gate");
     DN_TRY(need(q, nk, "q"));
     DN_TRY(need(k, nk, "k"));
@@ -157,7 +173,7 @@ dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, cons
     DN_TRY(need(beta, nb, "beta"));
     DN_TRY(need(g, ng, "g"));
     DN_TRY(need(o, nv, "o"));
-    const dn::WsLayout w = dn::ws_layout(pr, false, false);
+    const dn::WsLayout w = dn::ws_layout(pr, DN_PASS_FWD);
     if (ws_bytes < w.total) return fail(DN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
     DN_TRY(need(ws, w.total, "workspace"));
     DN_TRY(check_buffers({{"q", q, nk, false},
@@ -185,10 +201,12 @@ dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, cons
     p.o = o;
     p.hT = hT;
     p.states = states;
-    char* wb = static_cast<char*>(ws);
-    p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(wb + w.gam);
-    p.Tm = wb + w.Tm;
-    p.Pm = wb + w.Pm;
+    // gam, T and P go with the saved states when there are any (the backward reads
+    // them there), else into the workspace
+    char* wb = states ? static_cast<char*>(states) : static_cast<char*>(ws);
+    p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(wb + (states ? sl.gam : w.gam));
+    p.Tm = wb + (states ? sl.Tm : w.Tm);
+    p.Pm = wb + (states ? sl.Pm : w.Pm);
     const hipError_t e = dn::launch_forward(pr, p, states != nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;
@@ -205,7 +223,9 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
     DN_TRY(check_shape(shape, &pr, &d));
     const size_t nk = d.BH * d.T * d.dk * d.E, nv = d.BH * d.T * d.dv * d.E;
     const size_t nb = d.BH * d.T * 4, ng = pr.gate == DN_GATE_NONE ? 0 : d.BH * d.T * d.gw * 4;
-    const size_t ns = d.BH * d.dv * d.dk * 4, nst = d.BH * d.NT * d.dv * d.dk * d.E;
+    const size_t ns = d.BH * d.dv * d.dk * 4;
+    const dn::SavedLayout sl = dn::saved_layout(pr);
+    const size_t nst = sl.total;
     if (pr.gate == DN_GATE_NONE && (g || dg)) return fail(DN_ERR_INVALID, "g and dg must be NULL without a gate");
     DN_TRY(need(q, nk, "q"));
     DN_TRY(need(k, nk, "k"));
@@ -219,7 +239,7 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
     DN_TRY(need(dbeta, nb, "dbeta"));
     DN_TRY(need(dg, ng, "dg"));
     const bool have_states = states != nullptr;
-    const dn::WsLayout w = dn::ws_layout(pr, true, !have_states);
+    const dn::WsLayout w = dn::ws_layout(pr, have_states ? DN_PASS_BWD : DN_PASS_BWD_RECOMPUTE);
     if (ws_bytes < w.total) return fail(DN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w.total);
     DN_TRY(need(ws, w.total, "workspace"));
     DN_TRY(check_buffers({{"q", q, nk, false},
@@ -259,12 +279,20 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
     p.dg = dg;
     p.dh0 = dh0;
     char* wb = static_cast<char*>(ws);
-    p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(wb + w.gam);
-    p.Tm = wb + w.Tm;
-    p.Pm = wb + w.Pm;
+    char* sb = have_states ? static_cast<char*>(const_cast<void*>(states)) : nullptr;
     p.lam = wb + w.lam;
     p.dS1 = wb + w.dS1;
-    p.states = have_states ? const_cast<void*>(states) : static_cast<void*>(wb + w.states);
+    if (have_states) {   // the forward's saved states, gam, T and P
+        p.states = sb + sl.states;
+        p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(sb + sl.gam);
+        p.Tm = sb + sl.Tm;
+        p.Pm = sb + sl.Pm;
+    } else {             // recomputed into the workspace
+        p.states = wb + w.states;
+        p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(wb + w.gam);
+        p.Tm = wb + w.Tm;
+        p.Pm = wb + w.Pm;
+    }
     const hipError_t e = dn::launch_backward(pr, p, have_states, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;

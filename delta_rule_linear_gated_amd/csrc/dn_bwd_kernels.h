@@ -35,7 +35,7 @@ namespace dn {
 // ---------------------------------------------------------------------------
 // bwd_state_kernel: grid (DV / BV, BH), chunks walked from last to first; the
 // global tiles of chunk n - 1 are loaded into registers while chunk n is
-// computed.  The workspace holds T^T and P^T here (prep_kernel<..., true>).
+// computed.  T and P (row-major) are transposed on their way into LDS.
 template <typename TI, int GATE, int C, int DK, int BV>
 __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     constexpr int PAD = Pad<TI>::value;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
 
     RegB<TI, C, DK> rq, rk;
     RegB<TI, C, BV> rdo;
-    RegN<TI, C, C> rPT, rTT;
+    RegB<TI, C, C> rP, rT;
     GateRegs<GATE, C, DK> rg;
     auto prefetch = [&](int n) {
         const int t0 = n * C;
@@ -88,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
         rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
         rdo.load(static_cast<const TI*>(p.dout) + row0 * DVr + v0, DVr, valid);
-        rPT.load(static_cast<const TI*>(p.Pm) + cc, C, C);
-        rTT.load(static_cast<const TI*>(p.Tm) + cc, C, C);
+        rP.load(static_cast<const TI*>(p.Pm) + cc, C, C);
+        rT.load(static_cast<const TI*>(p.Tm) + cc, C, C);
     };
     prefetch(p.NT - 1);
 
@@ -124,8 +124,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
             rk.store_t(KgT, LDC, [&](int r, int c, float x) { return x * gf.G(r, c); });
         }
         rdo.store_t(dOT, LDC, Identity());
-        rPT.store(PT, LDC);
-        rTT.store(TT, LDC);
+        rP.store_t(PT, LDC, Identity());
+        rT.store_t(TT, LDC, Identity());
         __syncthreads();
         if (n > 0) prefetch(n - 1);
         lds_to_global<TI, BV, DK>(static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, dSs, LDK,
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     rg.load(p.gam + row0 * GW, p.beta + row0, valid);
     RegN<TI, C, D> rK;
     rK.load(k, D, valid);
-    RegB<TI, C, C> rT;   // the workspace holds T^T; the transposed store gives T
+    RegN<TI, C, C> rT;
     rT.load(static_cast<const TI*>(p.Tm) + chunk * C * C, C, C);
     RegB<TI, VB, D> rS0, rdS1;
     RegN<TI, C, VB> rlam, rdo, rv;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         rK.store(KG, LD, [&](int r, int c, float x) { return x * gf.G(r, c); });
     else
         rK.store(KG, LD);   // scalar: Gam_t is applied to X's rows
-    rT.store_t(TLs, LC, Identity());
+    rT.store(TLs, LC);
     auto commit_block = [&]() {
         rS0.dot_rows(rdS1, ls);
         rS0.store_n(S0B, LD, Identity());

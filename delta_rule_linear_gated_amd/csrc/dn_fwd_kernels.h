@@ -137,9 +137,9 @@ template <typename TI, int GATE, int C, int DK> struct PrepSmem {
 };
 
 // ---------------------------------------------------------------------------
-// prep_kernel: grid (NT, BH), one chunk per workgroup.  TRANS_OUT stores T^T
-// and P^T instead of T and P (the layout the reverse pass reads).
-template <typename TI, int GATE, int C, int DK, bool TRANS_OUT>
+// prep_kernel: grid (NT, BH), one chunk per workgroup: gam, P and T of the
+// chunk (T and P row-major; the reverse pass transposes them while staging).
+template <typename TI, int GATE, int C, int DK>
 __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
     using L = PrepSmem<TI, GATE, C, DK>;
     constexpr int LDK = L::LDK, LDA = L::LDA, LC = L::LC;
@@ -240,10 +240,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
                 for (int i = 0; i < 4; ++i) {
                     const int t = TL::row(j, i), s = TL::col(j);
                     A_s[t * LDA + s] = acc[j][i];
-                    if (TRANS_OUT)
-                        Ps[s * LC + t] = from_f<TI>(accp[j][i]);
-                    else
-                        Ps[t * LC + s] = from_f<TI>(accp[j][i]);
+                    Ps[t * LC + s] = from_f<TI>(accp[j][i]);
                 }
         }
     }
@@ -254,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
     // -- T = (I + A)^{-1}
     unit_lower_inverse<C>(A_s, Ts, LDA, Ysc);
 
-    // -- T (or T^T) to the workspace, 16 bytes per store
+    // -- T to global memory, 16 bytes per store
     {
         constexpr int VW = 16 / sizeof(TI), VPR = C / VW, NV = C * VPR;
         TI* __restrict__ Tout = static_cast<TI*>(p.Tm) + cc;
@@ -262,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
             const int r = idx / VPR, c0 = (idx % VPR) * VW;
             TI out[VW];
 #pragma unroll
-            for (int e = 0; e < VW; ++e) out[e] = from_f<TI>(TRANS_OUT ? Ts[(c0 + e) * LDA + r] : Ts[r * LDA + c0 + e]);
+            for (int e = 0; e < VW; ++e) out[e] = from_f<TI>(Ts[r * LDA + c0 + e]);
             *reinterpret_cast<uint4*>(Tout + r * C + c0) = *reinterpret_cast<const uint4*>(out);
         }
     }
@@ -335,8 +332,8 @@ template <int GATE, int C, int DK> struct GateLds {
 // mixes with itself through the key dimension).  The global tiles of chunk
 // n + 1 are loaded into registers while chunk n is computed.
 //   SAVE    : write the state entering each chunk (I/O type) to p.states
-//   OUTPUT  : write O and hT.  Off for the recompute pass of the backward, where
-//             the workspace holds T^T (and P is not needed).
+//   OUTPUT  : write O and hT.  Off for the recompute pass of the backward (P is
+//             not needed there).
 template <typename TI, int GATE, int C, int DK, int BV, bool SAVE, bool OUTPUT>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     constexpr int PAD = Pad<TI>::value;
@@ -377,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     RegN<TI, C, DK> rq;
     RegB<TI, C, DK> rk;
     RegB<TI, C, BV> rv;
-    std::conditional_t<OUTPUT, RegN<TI, C, C>, RegB<TI, C, C>> rT;
+    RegN<TI, C, C> rT;
     RegN<TI, OUTPUT ? C : 16, OUTPUT ? C : 16> rP;
     GateRegs<GATE, C, DK> rg;
     auto prefetch = [&](int n) {
@@ -421,12 +418,8 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             rk.store_t(KdT, LDC, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
         }
         rv.store_t(VbT, LDC, Identity());
-        if constexpr (OUTPUT) {
-            rT.store(Tl, LDC);
-            rP.store(Pl, LDC);
-        } else {
-            rT.store_t(Tl, LDC, Identity());
-        }
+        rT.store(Tl, LDC);
+        if constexpr (OUTPUT) rP.store(Pl, LDC);
         __syncthreads();
         if (n + 1 < p.NT) prefetch(n + 1);
         if (SAVE)

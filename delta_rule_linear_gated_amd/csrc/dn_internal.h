@@ -16,12 +16,15 @@ enum Gate { kGateNone = 0, kGateScalar = 1, kGateVector = 2 };
 //   q, k, dq, dk        [BH][T][DK]         v, o, dO, dv        [BH][T][DV]
 //   beta, dbeta         [BH][T]   fp32      g, dg  [BH][T] or [BH][T][DK]  fp32
 //   h0, hT, dh0, dhT    [BH][DV][DK] fp32   states              [BH][NT][DV][DK]
-// workspace:
+// per-chunk quantities of the forward, kept in the caller's saved buffer when
+// the forward saves (the backward then reads them there) and in the workspace
+// otherwise:
 //   gam   fp32 in-chunk cumulative log-decay, same layout as g
 //   Tm    [BH][NT][C][C]   (I + A)^{-1} of each chunk
 //   Pm    [BH][NT][C][C]   causal intra-chunk score matrix of each chunk
-//   lam   [BH][NT][C][DV]  triangular-residual adjoint (backward only)
-//   dS1   [BH][NT][DV][DK] state cotangent leaving each chunk (backward only)
+// workspace of the backward:
+//   lam   [BH][NT][C][DV]  triangular-residual adjoint
+//   dS1   [BH][NT][DV][DK] state cotangent leaving each chunk
 struct Params {
     int BH, T, NT, DKr, DVr;  // runtime copies (the kernels also get them as template args)
     const void* q;
@@ -55,12 +58,19 @@ struct Problem {
     int BV;     // d_v block of the sequential kernels
 };
 
-// Workspace carving.  Offsets in bytes from the workspace base; every region
-// starts on a 256-byte boundary.
+// Workspace carving per pass (0 forward, 1 backward with saved data, 2 backward
+// recomputing it).  Offsets in bytes from the workspace base; every region
+// starts on a 256-byte boundary; regions a pass does not use have size 0.
 struct WsLayout {
     size_t gam, Tm, Pm, lam, dS1, states, total;
 };
-WsLayout ws_layout(const Problem& pr, bool backward, bool need_states);
+WsLayout ws_layout(const Problem& pr, int pass);
+
+// The forward's saved buffer: chunk-entry states, T, P, gam (same alignment).
+struct SavedLayout {
+    size_t states, Tm, Pm, gam, total;
+};
+SavedLayout saved_layout(const Problem& pr);
 
 // Kernel launch sequences (all enqueue on `stream`, none synchronises).
 hipError_t launch_forward(const Problem& pr, const Params& p, bool save_states, hipStream_t stream);

@@ -61,7 +61,7 @@ hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t s
         constexpr int BV = D < 64 ? D : 64;
         const int BH = pr.B * pr.H;
         prof_begin(stream, "prep");
-        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D, false>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
         prof_end(stream);
         prof_begin(stream, "fwd_state");
         if (save)
@@ -82,10 +82,10 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
     } else {
         constexpr int BV = D < 64 ? D : 64;
         const int BH = pr.B * pr.H;
-        prof_begin(stream, "prep_bwd");
-        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D, true>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
-        prof_end(stream);
-        if (!have_states) {
+        if (!have_states) {   // recomputation policy: gam, T, P and the states into the workspace
+            prof_begin(stream, "prep_recompute");
+            hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+            prof_end(stream);
             prof_begin(stream, "fwd_state_recompute");
             hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, false>), dim3((D / BV) * BH),
                                dim3(kThreads), 0, stream, p);

@@ -33,27 +33,54 @@ bool supported(const Problem& pr) {
     return false;
 }
 
-WsLayout ws_layout(const Problem& pr, bool backward, bool need_states) {
-    WsLayout w{};
+namespace {
+struct Sizes {
+    size_t gam, cc, lam, st;
+};
+Sizes sizes(const Problem& pr) {
     const size_t E = pr.bf16 ? 2 : 4;
     const size_t BH = (size_t)pr.B * pr.H;
     const size_t NT = pr.T > 0 ? ((size_t)pr.T + pr.C - 1) / pr.C : 0;
     const size_t gw = pr.gate == kGateVector ? (size_t)pr.dk : 1;
+    Sizes z;
+    z.gam = al256(pr.gate == kGateNone ? 0 : BH * pr.T * gw * 4);
+    z.cc = al256(BH * NT * pr.C * pr.C * E);
+    z.lam = al256(BH * NT * pr.C * pr.dv * E);
+    z.st = al256(BH * NT * (size_t)pr.dv * pr.dk * E);
+    return z;
+}
+}  // namespace
+
+WsLayout ws_layout(const Problem& pr, int pass) {
+    const Sizes z = sizes(pr);
+    const bool chunk_data = pass != 1;   // forward, or a backward that recomputes
+    WsLayout w{};
     size_t off = 0;
     w.gam = off;
-    off += al256(pr.gate == kGateNone ? 0 : BH * pr.T * gw * 4);
+    if (chunk_data) off += z.gam;
     w.Tm = off;
-    off += al256(BH * NT * pr.C * pr.C * E);
+    if (chunk_data) off += z.cc;
     w.Pm = off;
-    off += al256(BH * NT * pr.C * pr.C * E);
+    if (chunk_data) off += z.cc;
     w.lam = off;
-    if (backward) off += al256(BH * NT * pr.C * pr.dv * E);
+    if (pass != 0) off += z.lam;
     w.dS1 = off;
-    if (backward) off += al256(BH * NT * (size_t)pr.dv * pr.dk * E);
+    if (pass != 0) off += z.st;
     w.states = off;
-    if (need_states) off += al256(BH * NT * (size_t)pr.dv * pr.dk * E);
+    if (pass == 2) off += z.st;
     w.total = off;
     return w;
+}
+
+SavedLayout saved_layout(const Problem& pr) {
+    const Sizes z = sizes(pr);
+    SavedLayout l{};
+    l.states = 0;
+    l.Tm = z.st;
+    l.Pm = l.Tm + z.cc;
+    l.gam = l.Pm + z.cc;
+    l.total = l.gam + z.gam;
+    return l;
 }
 
 hipError_t launch_forward(const Problem& pr, const Params& p, bool save_states, hipStream_t stream) {

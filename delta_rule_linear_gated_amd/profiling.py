@@ -40,7 +40,7 @@ def source_digest() -> str:
 def kernel_key(name: str) -> str:
     """Map a demangled rocprofv3 kernel name to the names dn_profile_collect uses."""
     if "prep_kernel" in name:
-        return "prep_bwd" if re.search(r"true>\(", name) else "prep"
+        return "prep"
     if "fwd_state_kernel" in name:
         return "fwd_state" if re.search(r"true, true>\(", name) or re.search(r"false, true>\(", name) \
             else "fwd_state_recompute"

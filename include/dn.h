@@ -47,10 +47,17 @@
  *     beta, dbeta        fp32 [B][H][T]
  *     g, dg              fp32 [B][H][T] (DN_GATE_SCALAR) or [B][H][T][dk] (DN_GATE_VECTOR)
  *     h0, hT, dh0, dhT   fp32 [B][H][dv][dk]
- *     states             io   [B][H][NT][dv][dk]   state entering each chunk
- * The saved states are kept in the io type: the kernels use the state as a
- * matrix-core operand in that type, so the backward reads exactly the operand
- * values the forward used; the running state itself and hT are fp32.
+ *     states             the forward's saved buffer, four regions at the byte
+ *                        offsets dn_states_layout() gives (each 256-byte aligned):
+ *                          io   [B][H][NT][dv][dk]  state entering each chunk
+ *                          io   [B][H][NT][C][C]    (I + A)^{-1} of each chunk
+ *                          io   [B][H][NT][C][C]    causal intra-chunk scores
+ *                          fp32 like g              in-chunk cumulative log-decay
+ *                                                   (absent without a gate)
+ * The saved quantities are kept in the types the kernels use them in (the state
+ * and the per-chunk matrices are matrix-core operands in the io type), so the
+ * backward reads exactly the operand values the forward used; the running
+ * state itself and hT are fp32.
  */
 #ifndef DN_H
 #define DN_H
@@ -79,7 +86,7 @@ typedef enum { DN_GATE_NONE = 0, DN_GATE_SCALAR = 1, DN_GATE_VECTOR = 2 } dn_gat
 /* Which call a workspace is sized for. */
 typedef enum {
     DN_PASS_FWD = 0,           /* dn_chunk_fwd (states saved or not) */
-    DN_PASS_BWD = 1,           /* dn_chunk_bwd with the forward's saved states */
+    DN_PASS_BWD = 1,           /* dn_chunk_bwd with the forward's saved buffer */
     DN_PASS_BWD_RECOMPUTE = 2  /* dn_chunk_bwd with states == NULL (states recomputed) */
 } dn_pass;
 
@@ -95,8 +102,13 @@ typedef struct {
     int32_t gate;   /* dn_gate  */
 } dn_shape;
 
-/* Bytes of `states` for this shape: B*H*ceil(T/C)*dv*dk*sizeof(io).  0 on bad shape. */
+/* Bytes of the saved buffer `states` for this shape (the four regions listed
+ * under Layouts, each rounded up to 256 bytes).  0 on bad shape. */
 size_t dn_states_bytes(const dn_shape* shape);
+
+/* Byte offsets of the regions of `states`: {chunk-entry states, (I + A)^{-1},
+ * intra-chunk scores, cumulative log-decay, total}.  DN_OK or a shape error. */
+dn_status dn_states_layout(const dn_shape* shape, size_t offsets[5]);
 
 /* Workspace bytes the given pass needs (0 on bad shape).  Workspace contents
  * are scratch: nothing is carried from one call to the next. */
@@ -108,7 +120,8 @@ size_t dn_workspace_bytes(const dn_shape* shape, int pass);
  * output -- ReWY abstract; SFDA summary, chunk-WY theorem and affine transfer).
  *   inputs : q, k, v, beta; g (must be NULL iff gate == DN_GATE_NONE);
  *            h0 (NULL = zero initial state)
- *   outputs: o; hT (NULL = not wanted); states (NULL = not saved, i.e. the
+ *   outputs: o; hT (NULL = not wanted); states (dn_states_bytes(shape) bytes:
+ *            what the backward reuses; NULL = not saved, i.e. the
  *            recomputation policy: dn_chunk_bwd is then called with
  *            states == NULL)
  *   ws     : device workspace of ws_bytes >= dn_workspace_bytes(shape, DN_PASS_FWD)
@@ -121,7 +134,8 @@ dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, cons
  * Backward pass in the reduced ReWY form: vector-Jacobian products of
  * L = <O, dout> + <hT, dhT> with respect to every input.
  *   inputs : q, k, v, beta, g, h0 as given to dn_chunk_fwd; dout; dhT (NULL =
- *            zero); states from dn_chunk_fwd, or NULL to recompute them here
+ *            zero); states as written by dn_chunk_fwd (the backward then skips
+ *            the per-chunk preparation), or NULL to recompute everything here
  *   outputs: dq, dk, dv, dbeta; dg (must be NULL iff gate == DN_GATE_NONE;
  *            same layout as g); dh0 (NULL = not wanted)
  *   ws     : >= dn_workspace_bytes(shape, states ? DN_PASS_BWD : DN_PASS_BWD_RECOMPUTE)
@@ -142,7 +156,10 @@ const char* dn_last_error(void);
  * Diagnostics: byte offsets of the workspace regions a pass uses, in the order
  * {cumulative log-decay, (I+A)^{-1} per chunk, intra-chunk scores per chunk,
  * triangular-residual adjoint, state cotangent per chunk, recomputed states,
- * total}.  Returns DN_OK or an error for a bad shape / pass.
+ * total}; a region the pass does not use has zero size (the next offset is
+ * equal).  DN_PASS_FWD places the first three there only when the forward
+ * saves nothing; DN_PASS_BWD takes them from the saved buffer.  Returns DN_OK
+ * or an error for a bad shape / pass.
  */
 dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[7]);
 

@@ -43,7 +43,10 @@ def gpu_run(w: W.Workload, inp: dict, policy: str | None = None, dhT=True):
     gr = B.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["do"],
                      d["dhT"] if dhT else None, states, C=w.C)
     torch.cuda.synchronize()
-    out = {"o": o, "hT": hT, **gr, "states": states}
+    out = {"o": o, "hT": hT, **gr}
+    if states is not None:   # the saved buffer's regions (not its alignment gaps)
+        sv = B.saved_regions(states, B.shape_of(d["q"], d["v"], d["g"], w.C))
+        out.update({"states": sv["states"], "saved_T": sv["T"], "saved_P": sv["P"], "saved_gam": sv["gam"]})
     return {n: (None if t is None else t.cpu()) for n, t in out.items()}
 
 

@@ -39,16 +39,30 @@ def test_sizes_of_the_workloads(name):
     sh = B.make_shape(w.B, w.H, w.T, w.dk, w.dv, w.C, w.dtype, w.gate)
     E = 2 if w.dtype == "bf16" else 4
     NT = -(-w.T // w.C)
-    assert B.dn_states_bytes(sh) == w.B * w.H * NT * w.dv * w.dk * E
+    gw = 0 if w.gate == "none" else (w.dk if w.gate == "vector" else 1)
+    al = lambda x: -(-x // 256) * 256
+    sl = B.dn_states_layout(sh)
+    # saved buffer: chunk-entry states, T, P (io type), cumulative log-decay (fp32)
+    assert sl["states"] == 0
+    assert sl["T"] == al(w.B * w.H * NT * w.dv * w.dk * E)
+    assert sl["P"] - sl["T"] == sl["gam"] - sl["P"] == al(w.B * w.H * NT * w.C * w.C * E)
+    assert sl["total"] - sl["gam"] == al(w.B * w.H * w.T * gw * 4)
+    assert B.dn_states_bytes(sh) == sl["total"]
     f = B.dn_workspace_bytes(sh, B.DN_PASS_FWD)
     b = B.dn_workspace_bytes(sh, B.DN_PASS_BWD)
     r = B.dn_workspace_bytes(sh, B.DN_PASS_BWD_RECOMPUTE)
-    assert 0 < f < b < r
+    assert 0 < f and 0 < b < r
     lay = B.dn_workspace_layout(sh, B.DN_PASS_BWD_RECOMPUTE)
     assert lay["total"] == r
     offs = [lay[k] for k in ("gam", "T", "P", "lam", "dS1", "states", "total")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert r - b >= B.dn_states_bytes(sh)
+    # the recomputing backward holds in its workspace what the saved buffer carries
+    assert r - b == B.dn_states_bytes(sh)
+    # with a saved buffer the backward's workspace holds only lambda and dS1
+    lb = B.dn_workspace_layout(sh, B.DN_PASS_BWD)
+    assert lb["gam"] == lb["T"] == lb["P"] == lb["lam"] == 0 and lb["states"] == lb["total"] == b
+    # the forward's workspace holds gam, T, P (used when it saves nothing)
+    assert f == sl["total"] - sl["T"]
 
 
 FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation first
@@ -116,5 +130,5 @@ def test_validation_errors_backward():
 def test_workspace_grows_with_recompute():
     sh = sh_of(T=4096, dk=128, dv=128, C=64)
     assert B.dn_workspace_bytes(sh, B.DN_PASS_BWD_RECOMPUTE) - B.dn_workspace_bytes(sh, B.DN_PASS_BWD) \
-        >= B.dn_states_bytes(sh)
+        == B.dn_states_bytes(sh)
     assert B.dn_workspace_bytes(sh, 9) == 0

@@ -1,7 +1,8 @@
-"""Parity of the per-chunk intermediates the HIP path leaves in its workspace
-(cumulative log-decay, (I + A)^{-1}, intra-chunk scores, saved states, the
-triangular-residual adjoint lambda and the state cotangent per chunk) with the
-fp64 chunked evaluation of the oracle.  A mismatch here names the stage that
+"""Parity of the per-chunk intermediates the HIP path leaves in the forward's
+saved buffer (cumulative log-decay, (I + A)^{-1}, intra-chunk scores, chunk-entry
+states) and in the backward's workspace (the triangular-residual adjoint lambda
+and the state cotangent per chunk) with the fp64 chunked evaluation of the
+oracle.  A mismatch here names the stage that
 is wrong when an end-to-end parity test fails."""
 import numpy as np
 import pytest
@@ -54,17 +55,18 @@ def test_workspace_intermediates(case):
         chunked.backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], f["do"], f["dhT"], C=C,
                          trace=trb)
         _, _, st_ref = chunked.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], C=C)
+        sv = B.saved_regions(states, sh)
         if gate != "none":
-            gam = region(lay["gam"], 2 * T * gw, torch.float32).reshape(2, T, gw)[h]
+            gam = sv["gam"][0, h].cpu().to(torch.float64).numpy().reshape(T, gw)
             ref = np.concatenate([c["gam"] if gate == "vector" else c["gam"][:, :1] for c in tr])
             say(f"  head {h} gam err {rel_err(gam, ref):.2e}")
             assert rel_err(gam, ref) < 1e-5
-        # the backward's workspace holds T^T and P^T (the layout the reverse pass reads)
-        Tm = region(lay["T"], 2 * NT * C * C, et).reshape(2, NT, C, C)[h].transpose(0, 2, 1)
-        Pm = region(lay["P"], 2 * NT * C * C, et).reshape(2, NT, C, C)[h].transpose(0, 2, 1)
+        # T and P as the forward saved them (row-major), lambda and dS1 from the backward's workspace
+        Tm = sv["T"][0, h].cpu().to(torch.float64).numpy()
+        Pm = sv["P"][0, h].cpu().to(torch.float64).numpy()
         lam = region(lay["lam"], 2 * NT * C * d, et).reshape(2, NT, C, d)[h]
         dS1 = region(lay["dS1"], 2 * NT * d * d, et).reshape(2, NT, d, d)[h]
-        st = states.cpu().to(torch.float64).numpy()[0, h]
+        st = sv["states"][0, h].cpu().to(torch.float64).numpy()
         for n in range(NT):
             L = tr[n]["T"].shape[0]
             errs = dict(T=rel_err(Tm[n, :L, :L], tr[n]["T"]), P=rel_err(Pm[n, :L, :L], tr[n]["Pm"]),

@@ -68,7 +68,7 @@ def test_bitwise_deterministic(gate):
     inp = W.make_inputs(w)
     a = gpu_run(w, inp)
     b = gpu_run(w, inp)
-    for n in ("o", "hT", "dq", "dk", "dv", "dbeta", "dg", "dh0", "states"):
+    for n in ("o", "hT", "dq", "dk", "dv", "dbeta", "dg", "dh0", "states", "saved_T", "saved_P", "saved_gam"):
         assert torch.equal(a[n], b[n]), n
 
 
