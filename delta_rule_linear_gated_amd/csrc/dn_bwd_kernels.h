@@ -199,6 +199,11 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
 //     dQg += dO_b S0_b,  dKg += lambda_b S0_b,  dKd += U_b dS1_b
 //     dA  += lambda_b U_b^T,  dP += dO_b U_b^T
 // after which the key-gradient products (phase C) finish dq, dk, dbeta, dg.
+// Every LDS tile keeps its natural (global) layout; operands contracted over
+// their leading index are read with the transposing LDS load.  The products are
+// accumulated transposed where that gives a lane 4 consecutive elements of a
+// row of the stored result (X^T, U^T, dq^T, dk^T, dA^T, dP^T), so results go
+// to LDS with one vector store per tile.
 template <typename TI, int GATE, int C, int D>
 struct BwdChunkSmem {
     static constexpr int PAD = Pad<TI>::value;
@@ -208,35 +213,33 @@ struct BwdChunkSmem {
     static constexpr int LC = C + PAD;            // rows of C elements
     static constexpr int LVB = VB + PAD;          // rows of VB elements
     static constexpr int GW = GateLayout<GATE, D>::GW;
+    static constexpr bool VEC = GATE == kGateVector;
     static constexpr size_t E = sizeof(TI);
     static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
-    // persistent through the d_v loop
+    // persistent through the d_v loop (K also through phase C without a vector gate)
     static constexpr size_t KG = 0;                                  // K (or K Gam)   [C][LD]
     static constexpr size_t TL = KG + al(C * LD * E);                // T              [C][LC]
     static constexpr size_t LOOP = TL + al(C * LC * E);
     // d_v loop, one block
     static constexpr size_t S0B = LOOP;                              // S0 rows        [VB][LD]
-    static constexpr size_t S0BT = S0B + al(VB * LD * E);            // S0 block^T     [D][LVB]
-    static constexpr size_t DS1T = S0BT + al(D * LVB * E);           // dS1 block^T    [D][LVB]
-    static constexpr size_t LAMB = DS1T + al(D * LVB * E);           // lambda block   [C][LVB]
+    static constexpr size_t DS1B = S0B + al(VB * LD * E);            // dS1 rows       [VB][LD]
+    static constexpr size_t LAMB = DS1B + al(VB * LD * E);           // lambda block   [C][LVB]
     static constexpr size_t DOB = LAMB + al(C * LVB * E);            // dO block       [C][LVB]
-    static constexpr size_t VBL = DOB + al(C * LVB * E);             // V block        [C][LVB]
-    static constexpr size_t RTB = VBL + al(C * LVB * E);             // R block^T      [VB][LC]
-    static constexpr size_t UB = RTB + al(VB * LC * E);              // U block        [C][LVB]
-    static constexpr size_t LOOP_END = UB + al(C * LVB * E);
-    // phase C (aliases everything above once the loop is done)
-    static constexpr size_t DA = 0;                                  // dA~            [C][LC]
-    static constexpr size_t DAT = DA + al(C * LC * E);               // beta dA~^T     [C][LC]
-    static constexpr size_t DP = DAT + al(C * LC * E);               // dP~            [C][LC]
-    static constexpr size_t DPT = DP + al(C * LC * E);               // dP~^T          [C][LC]
-    static constexpr size_t KRT = DPT + al(C * LC * E);              // (K or K e^{c-gam})^T [D][LC]
-    static constexpr size_t QLT = KRT + al(D * LC * E);              // (Q or Q e^{gam-c})^T [D][LC]
-    static constexpr size_t KLT = QLT + al(D * LC * E);              // (K e^{gam-c})^T (vector) [D][LC]
-    static constexpr size_t C_END = GATE == kGateVector ? KLT + al(D * LC * E) : KLT;
+    static constexpr size_t VBL = DOB + al(C * LVB * E);             // V block, then U block [C][LVB]
+    static constexpr size_t RB = VBL + al(C * LVB * E);              // R block        [C][LVB]
+    static constexpr size_t LOOP_END = RB + al(C * LVB * E);
+    // phase C (over the d_v-loop tiles)
+    static constexpr size_t DA = LOOP;                               // dA~            [C][LC]
+    static constexpr size_t DAB = DA + al(C * LC * E);               // beta_t dA~     [C][LC]
+    static constexpr size_t DP = DAB + al(C * LC * E);               // dP~            [C][LC]
+    static constexpr size_t QL = DP + al(C * LC * E);                // Q (Q e^{gam-c}) [C][LD]
+    static constexpr size_t KR = QL + al(C * LD * E);                // K e^{c-gam}    [C][LD] (vector)
+    static constexpr size_t KL = KR + al(C * LD * E);                // K e^{gam-c}    [C][LD] (vector)
+    static constexpr size_t C_END = VEC ? KL + al(C * LD * E) : KR;
     static constexpr size_t BIG_END = LOOP_END > C_END ? LOOP_END : C_END;
     // small fp32 arrays
     static constexpr size_t GAM = al(BIG_END);                                    // gam [C][D] or [C]
-    static constexpr size_t ROWF = GAM + al(GATE == kGateVector ? C * D * 4 : C * 4);  // [2][C] (scalar)
+    static constexpr size_t ROWF = GAM + al(VEC ? C * D * 4 : C * 4);             // [2][C] (scalar)
     static constexpr size_t BETA = ROWF + al(2 * C * 4);                          // [C]
     static constexpr size_t RED_R = BETA + al(C * 4);                             // [D/16][C] row partials
     static constexpr size_t RED_C = RED_R + al((D / 16) * C * 4);                 // [C/16][D] column partials
@@ -246,11 +249,11 @@ struct BwdChunkSmem {
     // dq / dk write-back tiles [C][LD] each at offset 0; d gam of the vector gate
     // [C][D] fp32 after them, written once every phase-C tile is dead
     static constexpr size_t DGB = al(2 * C * LD * E);
-    static_assert(GATE != kGateVector || DGB + C * D * 4 <= BIG_END, "d gam buffer");
+    static_assert(!VEC || DGB + C * D * 4 <= BIG_END, "d gam buffer");
     // per-thread partials of sum_v S0 dS1 [row blocks of the S0 register tile][D] fp32,
-    // at offset 0 right after the d_v loop
+    // over the dead d_v-loop tiles right after the loop
     using RS = RegB<TI, VB, D>;
-    static_assert(RS::BR * D * 4 <= BIG_END, "S0 dS1 partials");
+    static_assert(LOOP + RS::BR * D * 4 <= BIG_END, "S0 dS1 partials");
     static_assert(2 * C * LD * E <= BIG_END, "write-back tiles");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -266,13 +269,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     TI* KG = reinterpret_cast<TI*>(smem + L::KG);
     TI* TLs = reinterpret_cast<TI*>(smem + L::TL);
     TI* S0B = reinterpret_cast<TI*>(smem + L::S0B);
-    TI* S0BT = reinterpret_cast<TI*>(smem + L::S0BT);
-    TI* DS1T = reinterpret_cast<TI*>(smem + L::DS1T);
+    TI* DS1B = reinterpret_cast<TI*>(smem + L::DS1B);
     TI* LAMB = reinterpret_cast<TI*>(smem + L::LAMB);
     TI* DOB = reinterpret_cast<TI*>(smem + L::DOB);
     TI* VBL = reinterpret_cast<TI*>(smem + L::VBL);
-    TI* RTB = reinterpret_cast<TI*>(smem + L::RTB);
-    TI* UB = reinterpret_cast<TI*>(smem + L::UB);
+    TI* UB = VBL;   // V is dead once R is formed; U is dead before the next block's V
+    TI* RB = reinterpret_cast<TI*>(smem + L::RB);
     float* gam_s = reinterpret_cast<float*>(smem + L::GAM);
     float* rowf = reinterpret_cast<float*>(smem + L::ROWF);
     float* beta_s = reinterpret_cast<float*>(smem + L::BETA);
@@ -295,11 +297,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     const TI* __restrict__ dS1g = static_cast<const TI*>(p.dS1) + chunk * D * D;
     const TI* __restrict__ lamg = static_cast<const TI*>(p.lam) + chunk * C * D;
 
-    using TO = Tiles<C, D>;    // C x D outputs: dq, dk
-    using TCC = Tiles<C, C>;   // dA, dP
-    using TX = Tiles<C, VB>;   // X_b, U_b
+    using TO = Tiles<D, C>;    // dq^T, dk^T         [c][t]
+    using TCC = Tiles<C, C>;   // dA^T, dP^T         [s][t]
+    using TX = Tiles<VB, C>;   // X_b^T, U_b^T       [v][t]
 
-    // ---------------- prologue: gate, K, T, the first d_v block, k at this lane's elements
+    // ---------------- prologue: gate, K, T, the first d_v block
     GateRegs<GATE, C, D> rg;
     rg.load(p.gam + row0 * GW, p.beta + row0, valid);
     RegN<TI, C, D> rK;
@@ -330,8 +332,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     auto commit_block = [&]() {
         rS0.dot_rows(rdS1, ls);
         rS0.store_n(S0B, LD, Identity());
-        rS0.store_t(S0BT, LVB, Identity());
-        rdS1.store_t(DS1T, LVB, Identity());
+        rdS1.store_n(DS1B, LD, Identity());
         rlam.store(LAMB, LVB);
         rdo.store(DOB, LVB);
         rv.store(VBL, LVB);
@@ -341,54 +342,49 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
 
     // ---------------- d_v loop
     f32x4 dq[TO::PER], dkp[TO::PER], dkm[TO::PER], dA[TCC::PER], dP[TCC::PER];
-    zero_acc<C, D>(dq);
-    zero_acc<C, D>(dkp);
-    zero_acc<C, D>(dkm);
+    zero_acc<D, C>(dq);
+    zero_acc<D, C>(dkp);
+    zero_acc<D, C>(dkm);
     zero_acc<C, C>(dA);
     zero_acc<C, C>(dP);
-    float dbr_part[TX::PER][4] = {};
+    float dbr_part[TX::PER] = {};   // sum over this lane's 4 v of lambda (V - X) at row t = TX::col(j)
 #pragma unroll 1
     for (int b = 0; b < NVB; ++b) {
         if (b + 1 < NVB) load_block(b + 1);
-        // X_b = (K Gam) S0_b^T and the two S0 contractions
+        // X_b^T = S0_b (K Gam)^T and the two S0 contractions (S0 rows read as [k][m])
         f32x4 X[TX::PER];
-        zero_acc<C, VB>(X);
-        gemm_nt<TI, C, VB, D>(X, KG, LD, S0B, LD);
-        gemm_nt<TI, C, D, VB>(dq, DOB, LVB, S0BT, LVB);
-        gemm_nt<TI, C, D, VB>(dkp, LAMB, LVB, S0BT, LVB);
+        zero_acc<VB, C>(X);
+        gemm<TI, VB, C, D, false, false>(X, S0B, LD, KG, LD);
+        gemm<TI, D, C, VB, true, false>(dq, S0B, LD, DOB, LVB);
+        gemm<TI, D, C, VB, true, false>(dkp, S0B, LD, LAMB, LVB);
         if (TX::active()) {
-            float rb[TX::PER][4];   // LDS reads first, then the writes
+            f32x4 rb[TX::PER];   // LDS reads first, then the writes
 #pragma unroll
-            for (int j = 0; j < TX::PER; ++j)
+            for (int j = 0; j < TX::PER; ++j) {
+                const int t = TX::col(j), c = TX::row(j, 0);
+                const f32x4 xr = ld4<TI>(VBL + t * LVB + c) - (SCA ? rowf[t] : 1.f) * X[j];
+                const f32x4 lm = ld4<TI>(LAMB + t * LVB + c);
+                dbr_part[j] += lm[0] * xr[0] + lm[1] * xr[1] + lm[2] * xr[2] + lm[3] * xr[3];
+                rb[j] = beta_s[t] * xr;
+            }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TX::row(j, i), c = TX::col(j);
-                    const float xr = to_f(VBL[t * LVB + c]) - (SCA ? rowf[t] : 1.f) * X[j][i];
-                    dbr_part[j][i] += to_f(LAMB[t * LVB + c]) * xr;
-                    rb[j][i] = beta_s[t] * xr;
-                }
-#pragma unroll
-            for (int j = 0; j < TX::PER; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) RTB[TX::col(j) * LC + TX::row(j, i)] = from_f<TI>(rb[j][i]);
+            for (int j = 0; j < TX::PER; ++j) st4<TI>(RB + TX::col(j) * LVB + TX::row(j, 0), rb[j]);
         }
         __syncthreads();
-        // U_b = T R_b
+        // U_b^T = R_b^T T^T  (R rows read as [k][m])
         {
             f32x4 U[TX::PER];
-            zero_acc<C, VB>(U);
-            gemm_nt<TI, C, VB, C>(U, TLs, LC, RTB, LC);
+            zero_acc<VB, C>(U);
+            gemm<TI, VB, C, C, true, false>(U, RB, LVB, TLs, LC);
             if (TX::active()) {
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) UB[TX::row(j, i) * LVB + TX::col(j)] = from_f<TI>(U[j][i]);
+                for (int j = 0; j < TX::PER; ++j) st4<TI>(UB + TX::col(j) * LVB + TX::row(j, 0), U[j]);
             }
         }
         __syncthreads();
-        gemm_nt<TI, C, D, VB>(dkm, UB, LVB, DS1T, LVB);
-        gemm_nt<TI, C, C, VB>(dA, LAMB, LVB, UB, LVB);
-        gemm_nt<TI, C, C, VB>(dP, DOB, LVB, UB, LVB);
+        gemm<TI, D, C, VB, true, false>(dkm, DS1B, LD, UB, LVB);
+        gemm<TI, C, C, VB, false, false>(dA, UB, LVB, LAMB, LVB);
+        gemm<TI, C, C, VB, false, false>(dP, UB, LVB, DOB, LVB);
         __syncthreads();
         if (b + 1 < NVB) {
             commit_block();
@@ -396,36 +392,34 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         }
     }
 
-    // q and k for the key-gradient products (loads in flight during the epilogues below)
-    RegB<TI, C, D> rq, rk;
+    // q (and k for the vector gate) for the key-gradient products (loads in flight
+    // during the epilogues below)
+    RegN<TI, C, D> rq, rk;
     rq.load(q, D, valid);
-    rk.load(k, D, valid);
+    if (VEC) rk.load(k, D, valid);
 
     // ---------------- dbeta_R, sum_v S0 dS1, and the d_v-contraction epilogues
-    float* lsred = reinterpret_cast<float*>(smem);   // d_v-loop tiles are dead
+    float* lsred = reinterpret_cast<float*>(smem + L::LOOP);   // d_v-loop tiles are dead
     if (TX::active()) {
 #pragma unroll
-        for (int im = 0; im < TX::RM; ++im)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float s = 0.f;
-#pragma unroll
-                for (int in = 0; in < TX::RN; ++in) s += dbr_part[im * TX::RN + in][i];
-                s = row16_sum(s);
-                if ((lane_id() & 15) == 0) red_r[TX::cg() * C + TX::row(im * TX::RN, i)] = s;
-            }
+        for (int j = 0; j < TX::PER; ++j) {
+            float s = dbr_part[j];
+            s += __shfl_xor(s, 16);
+            s += __shfl_xor(s, 32);
+            if (lane_id() < 16) red_r[(TX::m0(j) / 16) * C + TX::col(j)] = s;
+        }
     }
 #pragma unroll
     for (int i = 0; i < L::RS::PER; ++i) {
         if (L::RS::owns(i)) {
 #pragma unroll
-            for (int k = 0; k < L::RS::VW; ++k) lsred[L::RS::rowblk(i) * D + L::RS::col0(i) + k] = ls[i][k];
+            for (int kk = 0; kk < L::RS::VW; ++kk) lsred[L::RS::rowblk(i) * D + L::RS::col0(i) + kk] = ls[i][kk];
         }
     }
     __syncthreads();   // row and column partials complete
     for (int t = threadIdx.x; t < C; t += kThreads) {
         float s = 0.f;
-        for (int b = 0; b < TX::WN; ++b) s += red_r[b * C + t];
+        for (int b = 0; b < VB / 16; ++b) s += red_r[b * C + t];
         dbr[t] = s;
     }
     for (int c = threadIdx.x; c < D; c += kThreads) {
@@ -434,168 +428,169 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         lastS[c] = s;
     }
     __syncthreads();   // red_r and the partials are reused below
-    // dq = Gam dQg ; dk+ = -beta Gam dKg ; dk- = Gd dKd
+    // dq = Gam dQg ; dk+ = -beta Gam dKg ; dk- = Gd dKd   (element c = row, t = col)
     if (TO::active()) {
 #pragma unroll
         for (int j = 0; j < TO::PER; ++j) {
+            const int t = TO::col(j);
+            const float bt = beta_s[t];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = TO::row(j, i), c = TO::col(j);
+                const int c = TO::row(j, i);
                 const float G = gf.G(t, c);
                 dq[j][i] *= G;
-                dkp[j][i] *= -beta_s[t] * G;
+                dkp[j][i] *= -bt * G;
                 dkm[j][i] *= gf.Gd(t, c);
             }
         }
     }
 
-    // ---------------- phase B: dA~ and dP~ into LDS
+    // ---------------- phase B: dA~, beta dA~ and dP~ into LDS (element s = row, t = col)
     {
         TI* DAs = reinterpret_cast<TI*>(smem + L::DA);
-        TI* DATs = reinterpret_cast<TI*>(smem + L::DAT);
+        TI* DABs = reinterpret_cast<TI*>(smem + L::DAB);
         TI* DPs = reinterpret_cast<TI*>(smem + L::DP);
-        TI* DPTs = reinterpret_cast<TI*>(smem + L::DPT);
         if (TCC::active()) {
-            float bt[TCC::PER][4];   // LDS reads first, then the writes
+            f32x4 a[TCC::PER], ab[TCC::PER], pp[TCC::PER];   // LDS reads first, then the writes
 #pragma unroll
-            for (int j = 0; j < TCC::PER; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TCC::row(j, i), s2 = TCC::col(j);
-                    const float e = (SCA && s2 <= t) ? fexp(gam_s[t] - gam_s[s2]) : 1.f;
-                    dP[j][i] = s2 <= t ? dP[j][i] * e : 0.f;
-                    dA[j][i] = s2 < t ? -dA[j][i] * e : 0.f;   // dA = -lambda U^T
-                    bt[j][i] = beta_s[t];
-                }
-#pragma unroll
-            for (int j = 0; j < TCC::PER; ++j)
+            for (int j = 0; j < TCC::PER; ++j) {
+                const int t = TCC::col(j);
+                const float bt = beta_s[t];
+                const float gt = SCA ? gam_s[t] : 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int t = TCC::row(j, i), s2 = TCC::col(j);
-                    DAs[t * LC + s2] = from_f<TI>(dA[j][i]);
-                    DATs[s2 * LC + t] = from_f<TI>(bt[j][i] * dA[j][i]);
-                    DPs[t * LC + s2] = from_f<TI>(dP[j][i]);
-                    DPTs[s2 * LC + t] = from_f<TI>(dP[j][i]);
+                    const int s2 = TCC::row(j, i);
+                    const float e = (SCA && s2 <= t) ? fexp(gt - gam_s[s2]) : 1.f;
+                    pp[j][i] = s2 <= t ? dP[j][i] * e : 0.f;
+                    a[j][i] = s2 < t ? -dA[j][i] * e : 0.f;   // dA = -lambda U^T
+                    ab[j][i] = bt * a[j][i];
                 }
+            }
+#pragma unroll
+            for (int j = 0; j < TCC::PER; ++j) {
+                const int off = TCC::col(j) * LC + TCC::row(j, 0);
+                st4<TI>(DAs + off, a[j]);
+                st4<TI>(DABs + off, ab[j]);
+                st4<TI>(DPs + off, pp[j]);
+            }
         }
     }
 
     // ---------------- phase C: key-gradient products
     {
         const TI* DAs = reinterpret_cast<const TI*>(smem + L::DA);
-        const TI* DATs = reinterpret_cast<const TI*>(smem + L::DAT);
+        const TI* DABs = reinterpret_cast<const TI*>(smem + L::DAB);
         const TI* DPs = reinterpret_cast<const TI*>(smem + L::DP);
-        const TI* DPTs = reinterpret_cast<const TI*>(smem + L::DPT);
-        TI* KrT = reinterpret_cast<TI*>(smem + L::KRT);
-        TI* QlT = reinterpret_cast<TI*>(smem + L::QLT);
-        TI* KlT = VEC ? reinterpret_cast<TI*>(smem + L::KLT) : KrT;
+        TI* Ql = reinterpret_cast<TI*>(smem + L::QL);
+        // K rows: the loop's K tile without a vector gate, else K e^{c - gam} / K e^{gam - c}
+        TI* Kr = VEC ? reinterpret_cast<TI*>(smem + L::KR) : KG;
+        TI* Kl = VEC ? reinterpret_cast<TI*>(smem + L::KL) : KG;
         const float* gl = gam_s + (valid - 1) * GW;
         // fp = e^{gam - centre} (vector gate; 1 otherwise), centre = gam_C / 2
         auto fpl = [&](int t, int c) -> float { return VEC ? fexp(gam_s[t * D + c] - 0.5f * gl[c]) : 1.f; };
+        auto fp4 = [&](int t, int c0) -> f32x4 {
+            if constexpr (VEC) {
+                const f32x4 g4 = ld4<float>(gam_s + t * D + c0), c4 = ld4<float>(gl + c0);
+                return f32x4{fexp(g4[0] - 0.5f * c4[0]), fexp(g4[1] - 0.5f * c4[1]), fexp(g4[2] - 0.5f * c4[2]),
+                             fexp(g4[3] - 0.5f * c4[3])};
+            } else {
+                return f32x4{1.f, 1.f, 1.f, 1.f};
+            }
+        };
         if (VEC) {
-            rk.store_t(KrT, LC, [&](int r, int c, float x) { return x / fpl(r, c); });
-            rk.store_t(KlT, LC, [&](int r, int c, float x) { return x * fpl(r, c); });
-            rq.store_t(QlT, LC, [&](int r, int c, float x) { return x * fpl(r, c); });
+            rk.store(Kr, LD, [&](int r, int c, float x) { return x / fpl(r, c); });
+            rk.store(Kl, LD, [&](int r, int c, float x) { return x * fpl(r, c); });
+            rq.store(Ql, LD, [&](int r, int c, float x) { return x * fpl(r, c); });
         } else {
-            rk.store_t(KrT, LC, Identity());
-            rq.store_t(QlT, LC, Identity());
+            rq.store(Ql, LD);
         }
         __syncthreads();
-        // k and q at this lane's elements, read back from the staged tiles; the
-        // gam_C column sums of Kd dKd (dk- holds only the Kd path so far)
-        float kv[TO::PER][4], qv[TO::PER][4];
+        // k and q at this lane's elements (4 consecutive c of row t), read back from the
+        // staged tiles; the gam_C column sums of Kd dKd (dk- holds only the Kd path so far)
+        f32x4 kv[TO::PER], qv[TO::PER];
         if (TO::active()) {
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TO::row(j, i), c = TO::col(j);
-                    const float fp = fpl(t, c);
-                    kv[j][i] = to_f(KrT[c * LC + t]) * fp;
-                    qv[j][i] = to_f(QlT[c * LC + t]) / fp;
-                }
-#pragma unroll
-            for (int in = 0; in < TO::RN; ++in) {
-                float colp = 0.f;
-#pragma unroll
-                for (int im = 0; im < TO::RM; ++im)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) colp += kv[im * TO::RN + in][i] * dkm[im * TO::RN + in][i];
-                colp += __shfl_xor(colp, 16);
-                colp += __shfl_xor(colp, 32);
-                if (lane_id() < 16) red_c[TO::rg() * D + TO::col(in)] = colp;
+            for (int j = 0; j < TO::PER; ++j) {
+                const int t = TO::col(j), c0 = TO::row(j, 0);
+                const f32x4 fp = fp4(t, c0);
+                kv[j] = ld4<TI>(Kr + t * LD + c0) * fp;
+                qv[j] = ld4<TI>(Ql + t * LD + c0) / fp;
             }
-        }
-        float dbA[TO::PER][4];
-        f32x4 tmp[TO::PER];
-        // Y = dA~ Kr :  dK+ = beta Y, dbeta_A = sum_c K+ Y
-        zero_acc<C, D>(tmp);
-        gemm_nt<TI, C, D, C>(tmp, DAs, LC, KrT, LC);
-        if (TO::active()) {
-#pragma unroll
-            for (int j = 0; j < TO::PER; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TO::row(j, i);
-                    const float fp = fpl(t, TO::col(j));
-                    const float y = tmp[j][i];
-                    dbA[j][i] = kv[j][i] * fp * y;
-                    dkp[j][i] += beta_s[t] * y * fp;
-                }
-        }
-        // Z = (beta dA~)^T Kl and W = dP~^T Ql : both reach k through e^{-gam}
-        zero_acc<C, D>(tmp);
-        gemm_nt<TI, C, D, C>(tmp, DATs, LC, KlT, LC);
-        gemm_nt<TI, C, D, C>(tmp, DPTs, LC, QlT, LC);
-        if (TO::active()) {
-#pragma unroll
-            for (int j = 0; j < TO::PER; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dkm[j][i] += tmp[j][i] / fpl(TO::row(j, i), TO::col(j));
-        }
-        // dQ+ = dP~ Kr
-        zero_acc<C, D>(tmp);
-        gemm_nt<TI, C, D, C>(tmp, DPs, LC, KrT, LC);
-        if (TO::active()) {
-#pragma unroll
-            for (int j = 0; j < TO::PER; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dq[j][i] += tmp[j][i] * fpl(TO::row(j, i), TO::col(j));
-        }
-
-        // -------- finish: dq, dk = dk+ + dk-, dbeta, d gam = q.dq + k.(dk+ - dk-)
-        float dgm[TO::PER][4];
-        __syncthreads();   // phase-C tiles dead: dq / dk go through LDS for coalesced stores
-        TI* dqs = reinterpret_cast<TI*>(smem + L::DA);
-        TI* dks = dqs + C * LD;
-        if (TO::active()) {
-#pragma unroll
-            for (int j = 0; j < TO::PER; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = TO::row(j, i), c = TO::col(j);
-                    dqs[t * LD + c] = from_f<TI>(dq[j][i]);
-                    dks[t * LD + c] = from_f<TI>(dkp[j][i] + dkm[j][i]);
-                    dgm[j][i] = qv[j][i] * dq[j][i] + kv[j][i] * (dkp[j][i] - dkm[j][i]);
-                }
-            // dbeta = dbeta_R + rowsum(K+ Y)
+            // column sums over t (the 16 lanes of a tile row, the wave's RN tiles) per c
 #pragma unroll
             for (int im = 0; im < TO::RM; ++im)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float s2 = 0.f;
+                    float colp = 0.f;
 #pragma unroll
-                    for (int in = 0; in < TO::RN; ++in) s2 += dbA[im * TO::RN + in][i];
-                    s2 = row16_sum(s2);
-                    if ((lane_id() & 15) == 0) red_r[TO::cg() * C + TO::row(im * TO::RN, i)] = s2;
+                    for (int in = 0; in < TO::RN; ++in)
+                        colp += kv[im * TO::RN + in][i] * dkm[im * TO::RN + in][i];
+                    colp = row16_sum(colp);
+                    if ((lane_id() & 15) == 0) red_c[TO::cg() * D + TO::row(im * TO::RN, i)] = colp;
                 }
+        }
+        float dbA[TO::PER];   // sum over this lane's 4 c of K+ Y at row t = TO::col(j)
+        f32x4 tmp[TO::PER];
+        // Y^T = Kr^T dA~^T :  dK+ = beta Y, dbeta_A = sum_c K+ Y
+        zero_acc<D, C>(tmp);
+        gemm<TI, D, C, C, true, false>(tmp, Kr, LD, DAs, LC);
+        if (TO::active()) {
+#pragma unroll
+            for (int j = 0; j < TO::PER; ++j) {
+                const int t = TO::col(j);
+                const f32x4 fp = fp4(t, TO::row(j, 0));
+                const f32x4 yf = tmp[j] * fp;
+                const f32x4 d4 = kv[j] * yf;
+                dbA[j] = d4[0] + d4[1] + d4[2] + d4[3];
+                dkp[j] += beta_s[t] * yf;
+            }
+        }
+        // Z^T = Kl^T (beta dA~) and W^T = Ql^T dP~ : both reach k through e^{-gam}
+        zero_acc<D, C>(tmp);
+        gemm<TI, D, C, C, true, true>(tmp, Kl, LD, DABs, LC);
+        gemm<TI, D, C, C, true, true>(tmp, Ql, LD, DPs, LC);
+        if (TO::active()) {
+#pragma unroll
+            for (int j = 0; j < TO::PER; ++j) dkm[j] += tmp[j] / fp4(TO::col(j), TO::row(j, 0));
+        }
+        // dQ+^T = Kr^T dP~^T
+        zero_acc<D, C>(tmp);
+        gemm<TI, D, C, C, true, false>(tmp, Kr, LD, DPs, LC);
+        if (TO::active()) {
+#pragma unroll
+            for (int j = 0; j < TO::PER; ++j) dq[j] += tmp[j] * fp4(TO::col(j), TO::row(j, 0));
+        }
+
+        // -------- finish: dq, dk = dk+ + dk-, dbeta, d gam = q.dq + k.(dk+ - dk-)
+        f32x4 dgm[TO::PER];
+        __syncthreads();   // phase-C tiles dead: dq / dk go through LDS for coalesced stores
+        TI* dqs = reinterpret_cast<TI*>(smem);
+        TI* dks = dqs + C * LD;
+        if (TO::active()) {
+#pragma unroll
+            for (int j = 0; j < TO::PER; ++j) {
+                const int off = TO::col(j) * LD + TO::row(j, 0);
+                st4<TI>(dqs + off, dq[j]);
+                st4<TI>(dks + off, dkp[j] + dkm[j]);
+                dgm[j] = qv[j] * dq[j] + kv[j] * (dkp[j] - dkm[j]);
+            }
+            // dbeta = dbeta_R + rowsum(K+ Y): sums over c (4 per lane, 4 lane groups, RM tiles)
+#pragma unroll
+            for (int in = 0; in < TO::RN; ++in) {
+                float s2 = 0.f;
+#pragma unroll
+                for (int im = 0; im < TO::RM; ++im) s2 += dbA[im * TO::RN + in];
+                s2 += __shfl_xor(s2, 16);
+                s2 += __shfl_xor(s2, 32);
+                if (lane_id() < 16) red_r[TO::rg() * C + TO::col(in)] = s2;
+            }
         }
         __syncthreads();
         lds_to_global<TI, C, D>(static_cast<TI*>(p.dq) + row0 * D, D, dqs, LD, valid);
         lds_to_global<TI, C, D>(static_cast<TI*>(p.dk) + row0 * D, D, dks, LD, valid);
         for (int t = threadIdx.x; t < valid; t += kThreads) {
             float s2 = dbr[t];
-            for (int b = 0; b < TO::WN; ++b) s2 += red_r[b * C + t];
+            for (int b = 0; b < TO::WM; ++b) s2 += red_r[b * C + t];
             p.dbeta[row0 + t] = s2;
         }
         if (GATE == kGateNone) return;
@@ -604,14 +599,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         if (VEC) {
             if (TO::active()) {
 #pragma unroll
-                for (int j = 0; j < TO::PER; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dgb[TO::row(j, i) * D + TO::col(j)] = dgm[j][i];
+                for (int j = 0; j < TO::PER; ++j) st4<float>(dgb + TO::col(j) * D + TO::row(j, 0), dgm[j]);
             }
             __syncthreads();
             for (int c = threadIdx.x; c < D; c += kThreads) {
                 float last = fexp(gl[c]) * lastS[c];
-                for (int b = 0; b < TO::WM; ++b) last += red_c[b * D + c];
+                for (int b = 0; b < TO::WN; ++b) last += red_c[b * D + c];
                 float acc = 0.f;
                 for (int t = valid - 1; t >= 0; --t) {
                     acc += dgb[t * D + c] + (t == valid - 1 ? last : 0.f);
@@ -621,15 +614,17 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         } else {
             if (TO::active()) {
 #pragma unroll
-                for (int im = 0; im < TO::RM; ++im)
+                for (int in = 0; in < TO::RN; ++in) {
+                    float s2 = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float s2 = 0.f;
-#pragma unroll
-                        for (int in = 0; in < TO::RN; ++in) s2 += dgm[im * TO::RN + in][i];
-                        s2 = row16_sum(s2);
-                        if ((lane_id() & 15) == 0) red_r[TO::cg() * C + TO::row(im * TO::RN, i)] = s2;
+                    for (int im = 0; im < TO::RM; ++im) {
+                        const f32x4 x = dgm[im * TO::RN + in];
+                        s2 += x[0] + x[1] + x[2] + x[3];
                     }
+                    s2 += __shfl_xor(s2, 16);
+                    s2 += __shfl_xor(s2, 32);
+                    if (lane_id() < 16) red_r[TO::rg() * C + TO::col(in)] = s2;
+                }
             }
             __syncthreads();
             if (wave_id() == 0) {
@@ -637,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 float part = 0.f;
                 for (int c = lane_id(); c < D; c += 64) {
                     float x = gf.GC(c) * lastS[c];
-                    for (int b = 0; b < TO::WM; ++b) x += red_c[b * D + c];
+                    for (int b = 0; b < TO::WN; ++b) x += red_c[b * D + c];
                     part += x;
                 }
 #pragma unroll
@@ -645,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 const int t = lane_id();
                 float x = 0.f;
                 if (t < valid) {
-                    for (int b = 0; b < TO::WN; ++b) x += red_r[b * C + t];
+                    for (int b = 0; b < TO::WM; ++b) x += red_r[b * C + t];
                     if (t == valid - 1) x += part;
                 }
                 // reverse inclusive scan over t: dg_t = sum_{s >= t} x_s

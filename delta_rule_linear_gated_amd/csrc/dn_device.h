@@ -2,9 +2,12 @@
 // chunkwise gated delta rule: element types, MFMA tile products over LDS,
 // global->LDS staging, small wave reductions.
 //
-// Every dense contraction of the chunk form is written as an "NT" product
+// Every dense contraction of the chunk form is written as a product
 //     D[m][n] += sum_k A[m][k] * B[n][k]
-// with BOTH operands stored K-contiguous in LDS (A as [m][k], B as [n][k]).
+// with each operand stored in LDS either K-contiguous (A as [m][k], B as
+// [n][k]) or transposed (A as [k][m], B as [k][n]); a transposed bf16 operand
+// is read with ds_read_b64_tr_b16, which hands each lane 4 consecutive K values
+// of one row out of 4 rows x 16 columns read by its group of 16 lanes.
 // A 16x16 output tile is computed by one wave64 with
 //   bf16 : v_mfma_f32_16x16x32_bf16 (K step 32) or 16x16x16bf16_1k (K step 16)
 //   fp32 : v_mfma_f32_16x16x4_f32   (K step 4)
@@ -48,12 +51,30 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // MFMA.  step() = both.
 template <typename T, int KS> struct Mma;
 
+// ds_read_b64_tr_b16 at p: within each group of 16 lanes, output lane j gets
+// element j % 4 of the 8-byte pieces read by lanes 4k + j / 4 (k = 0..3).  With
+// lane i of a group reading row r0 + i / 4, columns c0 + 4 (i % 4) .. + 3 of a
+// row-major array, lane j receives column c0 + j of rows r0 .. r0 + 3.
+__device__ __forceinline__ i16x4 tr16_b64(const bf16* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
 template <> struct Mma<bf16, 32> {
     static constexpr int kStep = 32;
     typedef bf16x8 Frag;
     __device__ __forceinline__ static Frag load(const bf16* p, int ld) {
         const int l = lane_id();
         return *reinterpret_cast<const bf16x8*>(p + (l & 15) * ld + 8 * (l >> 4));
+    }
+    // The same fragment from a transposed operand: p at row k0, column m0 of a
+    // [k][m] array.  Lane l gets column m0 + (l & 15), rows k0 + 8 (l >> 4) + 0..7.
+    __device__ __forceinline__ static Frag load_t(const bf16* p, int ld) {
+        const int l = lane_id(), i = l & 15;
+        const bf16* a = p + (8 * (l >> 4) + (i >> 2)) * ld + 4 * (i & 3);
+        const i16x4 lo = tr16_b64(a), hi = tr16_b64(a + 4 * ld);
+        const i16x4 v[2] = {lo, hi};
+        return *reinterpret_cast<const bf16x8*>(v);
     }
     __device__ __forceinline__ static f32x4 op(Frag a, Frag b, f32x4 acc) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
@@ -70,6 +91,11 @@ template <> struct Mma<bf16, 16> {
         const int l = lane_id();
         return *reinterpret_cast<const i16x4*>(p + (l & 15) * ld + 4 * (l >> 4));
     }
+    // transposed operand ([k][m], p at row k0, column m0): rows k0 + 4 (l >> 4) + 0..3
+    __device__ __forceinline__ static Frag load_t(const bf16* p, int ld) {
+        const int l = lane_id(), i = l & 15;
+        return tr16_b64(p + (4 * (l >> 4) + (i >> 2)) * ld + 4 * (i & 3));
+    }
     __device__ __forceinline__ static f32x4 op(Frag a, Frag b, f32x4 acc) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
     }
@@ -84,6 +110,11 @@ template <> struct Mma<float, 4> {
     __device__ __forceinline__ static Frag load(const float* p, int ld) {
         const int l = lane_id();
         return p[(l & 15) * ld + (l >> 4)];
+    }
+    // transposed operand ([k][m], p at row k0, column m0)
+    __device__ __forceinline__ static Frag load_t(const float* p, int ld) {
+        const int l = lane_id();
+        return p[(l >> 4) * ld + (l & 15)];
     }
     __device__ __forceinline__ static f32x4 op(Frag a, Frag b, f32x4 acc) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
@@ -184,6 +215,52 @@ __device__ __forceinline__ void gemm_nt(f32x4 (&acc)[NACC], const T* A, int lda,
 #pragma unroll
                 for (int in = 0; in < TL::RN; ++in)
                     acc[im * TL::RN + in] = MM::op(fa[im], fb[in], acc[im * TL::RN + in]);
+        }
+    }
+}
+
+// acc[j] += A * B^T over the tiles this wave owns, with A stored [M][K] (TA =
+// false) or [K][M] (TA = true) and B stored [N][K] (TB = false) or [K][N] (TB =
+// true).  gemm<..., false, false> is gemm_nt.
+template <typename T, int M, int N, int K, bool TA, bool TB, int NACC>
+__device__ __forceinline__ void gemm(f32x4 (&acc)[NACC], const T* A, int lda, const T* B, int ldb) {
+    using TL = Tiles<M, N>;
+    using MM = typename MmaFor<T, K>::type;
+    static_assert(NACC == TL::PER, "accumulator count");
+    static_assert(K % MM::kStep == 0, "K must be a multiple of the MFMA K step");
+    if (!TL::active()) return;
+    auto fa = [&](int im, int k0) {
+        const int m = TL::m0(0) + im * 16;
+        return TA ? MM::load_t(A + k0 * lda + m, lda) : MM::load(A + m * lda + k0, lda);
+    };
+    auto fb = [&](int in, int k0) {
+        const int n = TL::n0(0) + in * 16;
+        return TB ? MM::load_t(B + k0 * ldb + n, ldb) : MM::load(B + n * ldb + k0, ldb);
+    };
+    if constexpr (sizeof(T) == 2 && MM::kStep == 16) {
+        // 16x16x16 chains never inherit another shape's accumulator (see tile_nt)
+#pragma unroll
+        for (int im = 0; im < TL::RM; ++im)
+#pragma unroll
+            for (int in = 0; in < TL::RN; ++in) {
+                f32x4 part = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < K; k0 += MM::kStep) part = MM::op(fa(im, k0), fb(in, k0), part);
+                acc[im * TL::RN + in] = acc[im * TL::RN + in] + part;
+            }
+    } else {
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += MM::kStep) {
+            typename MM::Frag a[TL::RM], b[TL::RN];
+#pragma unroll
+            for (int im = 0; im < TL::RM; ++im) a[im] = fa(im, k0);
+#pragma unroll
+            for (int in = 0; in < TL::RN; ++in) b[in] = fb(in, k0);
+#pragma unroll
+            for (int im = 0; im < TL::RM; ++im)
+#pragma unroll
+                for (int in = 0; in < TL::RN; ++in)
+                    acc[im * TL::RN + in] = MM::op(a[im], b[in], acc[im * TL::RN + in]);
         }
     }
 }
