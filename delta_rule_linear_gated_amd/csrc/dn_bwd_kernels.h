@@ -35,7 +35,9 @@ namespace dn {
 // ---------------------------------------------------------------------------
 // bwd_state_kernel: grid (DV / BV, BH), chunks walked from last to first; the
 // global tiles of chunk n - 1 are loaded into registers while chunk n is
-// computed.  T and P (row-major) are transposed on their way into LDS.
+// computed.  Every tile is kept in its natural layout (T and P as saved, row
+// major); operands contracted over their leading index are read with the
+// transposing LDS load.
 template <typename TI, int GATE, int C, int DK, int BV>
 __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     constexpr int PAD = Pad<TI>::value;
@@ -49,18 +51,19 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     __shared__ __align__(16) float beta_s[C];
     __shared__ __align__(16) TI dSs[BV * LDK];   // dS1 operand     [v][c]
     __shared__ __align__(16) TI Kd[C * LDK];     // K Gam_C / Gam   [t][c]
-    __shared__ __align__(16) TI PT[C * LDC];     // P^T             [t][s]
-    __shared__ __align__(16) TI TT[C * LDC];     // T^T             [t][s]
-    __shared__ __align__(16) TI dOT[BV * LDC];   // dO^T block      [v][t]
-    __shared__ __align__(16) TI QgT[DK * LDC];   // (Q Gam)^T       [c][t]
-    __shared__ __align__(16) TI KgT[DK * LDC];   // (K Gam)^T       [c][t]
+    __shared__ __align__(16) TI Kn[C * LDK];     // -K Gam          [t][c]
+    __shared__ __align__(16) TI Qg[C * LDK];     // Q Gam           [t][c]
+    __shared__ __align__(16) TI Pl[C * LDC];     // P               [s][t]
+    __shared__ __align__(16) TI Tl[C * LDC];     // T               [s][t]
+    __shared__ __align__(16) TI dOb[C * LDV];    // dO block        [t][v]
     __shared__ __align__(16) TI dUT[BV * LDC];   // dU^T            [v][t]
-    __shared__ __align__(16) TI bLT[BV * LDC];   // -(beta lambda)^T [v][t]
-    // lambda / dv write-back tiles [C][LDV]: Kd and P^T are dead once dU is formed
-    constexpr bool DB_IN_PT = C >= BV;
-    __shared__ __align__(16) TI DbSep[DB_IN_PT ? 8 : C * LDV];
+    // lambda and dv = beta lambda [t][v], written back a chunk later: lambda over
+    // Kd (dead once dU is formed), dv over P when it fits (dead as well), and dv
+    // is also the operand of the dS update
+    constexpr bool DB_IN_P = C >= BV;
+    __shared__ __align__(16) TI DbSep[DB_IN_P ? 8 : C * LDV];
     TI* Lb = Kd;
-    TI* Db = DB_IN_PT ? PT : DbSep;
+    TI* Db = DB_IN_P ? Pl : DbSep;
 
     const int DVr = p.DVr;
     int bh, vblk;
@@ -75,9 +78,9 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         if (p.dhT && TS::active()) dS[j] = ld4<float>(p.dhT + ((long)bh * DVr + v0 + TS::col(j)) * DK + TS::row(j, 0));
     }
 
-    RegB<TI, C, DK> rq, rk;
-    RegB<TI, C, BV> rdo;
-    RegB<TI, C, C> rP, rT;
+    RegN<TI, C, DK> rq, rk;
+    RegN<TI, C, BV> rdo;
+    RegN<TI, C, C> rP, rT;
     GateRegs<GATE, C, DK> rg;
     auto prefetch = [&](int n) {
         const int t0 = n * C;
@@ -93,6 +96,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     };
     prefetch(p.NT - 1);
 
+    using TX = Tiles<C, BV>;    // dU  [t][v]
+    using TL = Tiles<BV, C>;    // lambda^T [v][t]
     for (int n = p.NT - 1; n >= 0; --n) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
@@ -115,54 +120,49 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         __syncthreads();
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (GATE == kGateNone) {
-            rk.store_n(Kd, LDK, Identity());
-            rq.store_t(QgT, LDC, Identity());
-            rk.store_t(KgT, LDC, Identity());
+            rk.store(Kd, LDK);
+            rk.store(Kn, LDK, [](int, int, float x) { return -x; });
+            rq.store(Qg, LDK);
         } else {
-            rk.store_n(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
-            rq.store_t(QgT, LDC, [&](int r, int c, float x) { return x * gf.G(r, c); });
-            rk.store_t(KgT, LDC, [&](int r, int c, float x) { return x * gf.G(r, c); });
+            rk.store(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
+            rk.store(Kn, LDK, [&](int r, int c, float x) { return -x * gf.G(r, c); });
+            rq.store(Qg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
         }
-        rdo.store_t(dOT, LDC, Identity());
-        rP.store_t(PT, LDC, Identity());
-        rT.store_t(TT, LDC, Identity());
+        rdo.store(dOb, LDV);
+        rP.store(Pl, LDC);
+        rT.store(Tl, LDC);
         __syncthreads();
         if (n > 0) prefetch(n - 1);
         lds_to_global<TI, BV, DK>(static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, dSs, LDK,
                                   BV);
 
-        using TX = Tiles<C, BV>;
-        // (c) dU = P^T dO + Kd dS1^T  -> dU^T
+        // (c) dU = P^T dO + Kd dS1^T  -> dU^T   (P and dO read as [k][m] / [k][n])
         {
             f32x4 dU[TX::PER];
             zero_acc<C, BV>(dU);
-            gemm_nt<TI, C, BV, C>(dU, PT, LDC, dOT, LDC);
-            gemm_nt<TI, C, BV, DK>(dU, Kd, LDK, dSs, LDK);
+            gemm<TI, C, BV, C, true, true>(dU, Pl, LDC, dOb, LDV);
+            gemm<TI, C, BV, DK, false, false>(dU, Kd, LDK, dSs, LDK);
             if (TX::active()) {
 #pragma unroll
                 for (int j = 0; j < TX::PER; ++j) st4<TI>(dUT + TX::col(j) * LDC + TX::row(j, 0), dU[j]);
             }
         }
         __syncthreads();
-        // (d) lambda^T = dU^T T ; dv = beta lambda ; keep -(beta lambda)^T.  lambda^T
-        //     tiles give a lane 4 consecutive v of one row t of lambda and dv
+        // (d) lambda^T = dU^T T ; dv = beta lambda.  lambda^T tiles give a lane 4
+        //     consecutive v of one row t of lambda and dv
         {
-            using TL = Tiles<BV, C>;
-            f32x4 L[TL::PER];
-            zero_acc<BV, C>(L);
-            gemm_nt<TI, BV, C, C>(L, dUT, LDC, TT, LDC);
+            f32x4 Lm[TL::PER];
+            zero_acc<BV, C>(Lm);
+            gemm<TI, BV, C, C, false, true>(Lm, dUT, LDC, Tl, LDC);
             if (TL::active()) {
                 float bt[TL::PER];   // LDS reads first, then the writes
 #pragma unroll
                 for (int j = 0; j < TL::PER; ++j) bt[j] = beta_s[TL::col(j)];
 #pragma unroll
                 for (int j = 0; j < TL::PER; ++j) {
-                    const int t = TL::col(j), c = TL::row(j, 0);
-                    const f32x4 bl = bt[j] * L[j];
-                    st4<TI>(Lb + t * LDV + c, L[j]);
-                    st4<TI>(Db + t * LDV + c, bl);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) bLT[(c + i) * LDC + t] = from_f<TI>(-bl[i]);
+                    const int off = TL::col(j) * LDV + TL::row(j, 0);
+                    st4<TI>(Lb + off, Lm[j]);
+                    st4<TI>(Db + off, bt[j] * Lm[j]);
                 }
             }
         }
@@ -175,8 +175,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
                 for (int i = 0; i < 4; ++i) dS[j][i] *= gf.GC(TS::row(j, i));
             }
         }
-        gemm_nt<TI, DK, BV, C>(dS, QgT, LDC, dOT, LDC);
-        gemm_nt<TI, DK, BV, C>(dS, KgT, LDC, bLT, LDC);
+        gemm<TI, DK, BV, C, true, true>(dS, Qg, LDK, dOb, LDV);
+        gemm<TI, DK, BV, C, true, true>(dS, Kn, LDK, Db, LDV);
         __syncthreads();
     }
     if (p.NT > 0) {   // lambda and dv of chunk 0

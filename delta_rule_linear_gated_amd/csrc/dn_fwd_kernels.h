@@ -341,20 +341,21 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     constexpr int LDC = C + PAD;
     constexpr int LDV = BV + PAD;
     constexpr int GW = GateLayout<GATE, DK>::GW;
+    // every tile in its natural layout; operands contracted over their leading
+    // index are read with the transposing LDS load
     __shared__ float gam_s[GATE == kGateVector ? C * DK : C];
     __shared__ float rowf[2 * C];
     __shared__ __align__(16) float beta_s[C];
     __shared__ __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
-    __shared__ __align__(16) TI Qg[C * LDK];     // Q Gam            [t][c]
-    __shared__ __align__(16) TI Kg[C * LDK];     // K Gam            [t][c]
-    __shared__ __align__(16) TI KdT[DK * LDC];   // (K Gam_C / Gam)^T [c][t]
-    __shared__ __align__(16) TI VbT[BV * LDC];   // V block^T        [v][t]
-    __shared__ __align__(16) TI Tl[C * LDC];     // T                [t][s]
-    __shared__ __align__(16) TI Pl[C * LDC];     // P                [t][s]
-    // R^T [v][t]; after (d) it holds the chunk's O [t][v] until the next iteration writes it back
-    constexpr int RT_ELEMS = BV * LDC > C * LDV ? BV * LDC : C * LDV;
-    __shared__ __align__(16) TI RT[RT_ELEMS];
-    __shared__ __align__(16) TI UT[BV * LDC];    // U^T              [v][t]
+    __shared__ __align__(16) TI Qg[C * LDK];     // Q Gam             [t][c]
+    __shared__ __align__(16) TI Kg[C * LDK];     // K Gam             [t][c]
+    __shared__ __align__(16) TI Kd[C * LDK];     // K Gam_C / Gam     [t][c]
+    __shared__ __align__(16) TI Vb[C * LDV];     // V block           [t][v]
+    __shared__ __align__(16) TI Tl[C * LDC];     // T                 [t][s]
+    __shared__ __align__(16) TI Pl[C * LDC];     // P                 [t][s]
+    // R [t][v]; after (d) it holds the chunk's O [t][v] until the next iteration writes it back
+    __shared__ __align__(16) TI Rb[C * LDV];
+    __shared__ __align__(16) TI Ub[C * LDV];     // U                 [t][v]
 
     const int DVr = p.DVr;
     int bh, vblk;
@@ -371,9 +372,8 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     }
 
     // registers of the next chunk
-    RegN<TI, C, DK> rq;
-    RegB<TI, C, DK> rk;
-    RegB<TI, C, BV> rv;
+    RegN<TI, C, DK> rq, rk;
+    RegN<TI, C, BV> rv;
     RegN<TI, C, C> rT;
     RegN<TI, OUTPUT ? C : 16, OUTPUT ? C : 16> rP;
     GateRegs<GATE, C, DK> rg;
@@ -391,6 +391,9 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     };
     prefetch(0);
 
+    // X^T, U^T and O^T tiles [v][t]: a lane holds 4 consecutive v of one row t of
+    // R, U and O (one vector LDS access each)
+    using TX = Tiles<BV, C>;
     for (int n = 0; n < p.NT; ++n) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         // write back the previous chunk's O (a full chunk of work after it was formed,
         // so the stores never sit just ahead of a wait on this chunk's loads)
         if (OUTPUT && n > 0)
-            lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + (row0 - C) * DVr + v0, DVr, RT, LDV, C);
+            lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + (row0 - C) * DVr + v0, DVr, Rb, LDV, C);
         // (a) state operand (saved from LDS below)
         if (TS::active()) {
 #pragma unroll
@@ -410,14 +413,14 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (GATE == kGateNone) {
             rq.store(Qg, LDK);
-            rk.store_n(Kg, LDK, Identity());
-            rk.store_t(KdT, LDC, Identity());
+            rk.store(Kg, LDK);
+            rk.store(Kd, LDK);
         } else {
             rq.store(Qg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
-            rk.store_n(Kg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
-            rk.store_t(KdT, LDC, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
+            rk.store(Kg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
+            rk.store(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
         }
-        rv.store_t(VbT, LDC, Identity());
+        rv.store(Vb, LDV);
         rT.store(Tl, LDC);
         if constexpr (OUTPUT) rP.store(Pl, LDC);
         __syncthreads();
@@ -426,51 +429,46 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             lds_to_global<TI, BV, DK>(static_cast<TI*>(p.states) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, Ss,
                                       LDK, BV);
 
-        // (c) X = (K Gam) S0^T ;  R = diag(beta) (V - X)  -> R^T
-        using TX = Tiles<C, BV>;
+        // (c) X^T = S0 (K Gam)^T ;  R = diag(beta) (V - X)
         {
             f32x4 X[TX::PER];
-            zero_acc<C, BV>(X);
-            gemm_nt<TI, C, BV, DK>(X, Kg, LDK, Ss, LDK);
+            zero_acc<BV, C>(X);
+            gemm<TI, BV, C, DK, false, false>(X, Ss, LDK, Kg, LDK);
             if (TX::active()) {
-                // all LDS reads, then all LDS writes (see RegN::store); a lane's 4 rows t
-                // are consecutive in V^T, beta and R^T
-                f32x4 rv_[TX::PER];
+                f32x4 r[TX::PER];   // all LDS reads, then all LDS writes (see RegN::store)
 #pragma unroll
                 for (int j = 0; j < TX::PER; ++j) {
-                    const int t = TX::row(j, 0), c = TX::col(j);
-                    rv_[j] = ld4<float>(beta_s + t) * (ld4<TI>(VbT + c * LDC + t) - X[j]);
+                    const int t = TX::col(j), c = TX::row(j, 0);
+                    r[j] = beta_s[t] * (ld4<TI>(Vb + t * LDV + c) - X[j]);
                 }
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) st4<TI>(RT + TX::col(j) * LDC + TX::row(j, 0), rv_[j]);
+                for (int j = 0; j < TX::PER; ++j) st4<TI>(Rb + TX::col(j) * LDV + TX::row(j, 0), r[j]);
             }
         }
         __syncthreads();
-        // (d) U = T R  -> U^T
+        // (d) U^T = R^T T^T  (R read as [k][m])
         {
             f32x4 U[TX::PER];
-            zero_acc<C, BV>(U);
-            gemm_nt<TI, C, BV, C>(U, Tl, LDC, RT, LDC);
+            zero_acc<BV, C>(U);
+            gemm<TI, BV, C, C, true, false>(U, Rb, LDV, Tl, LDC);
             if (TX::active()) {
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) st4<TI>(UT + TX::col(j) * LDC + TX::row(j, 0), U[j]);
+                for (int j = 0; j < TX::PER; ++j) st4<TI>(Ub + TX::col(j) * LDV + TX::row(j, 0), U[j]);
             }
         }
         __syncthreads();
-        // (e) O^T = S0 (Q Gam)^T + U^T P^T   (O into RT, dead since (d); written back
-        //     next iteration; O^T tiles give a lane 4 consecutive v of one row t of O)
+        // (e) O^T = S0 (Q Gam)^T + U^T P^T   (O into Rb, dead since (d); written back next iteration)
         if (OUTPUT) {
-            using TOT = Tiles<BV, C>;
-            f32x4 OT[TOT::PER];
+            f32x4 OT[TX::PER];
             zero_acc<BV, C>(OT);
-            gemm_nt<TI, BV, C, DK>(OT, Ss, LDK, Qg, LDK);
-            gemm_nt<TI, BV, C, C>(OT, UT, LDC, Pl, LDC);
-            if (TOT::active()) {
+            gemm<TI, BV, C, DK, false, false>(OT, Ss, LDK, Qg, LDK);
+            gemm<TI, BV, C, C, true, false>(OT, Ub, LDV, Pl, LDC);
+            if (TX::active()) {
 #pragma unroll
-                for (int j = 0; j < TOT::PER; ++j) st4<TI>(RT + TOT::col(j) * LDV + TOT::row(j, 0), OT[j]);
+                for (int j = 0; j < TX::PER; ++j) st4<TI>(Rb + TX::col(j) * LDV + TX::row(j, 0), OT[j]);
             }
         }
-        // (f) S1^T = Diag(Gam_C) S0^T + (K Gam_C / Gam)^T U
+        // (f) S1^T = Diag(Gam_C) S0^T + (K Gam_C / Gam)^T U   (both read as [k][m] / [k][n])
         if (GATE != kGateNone && TS::active()) {
 #pragma unroll
             for (int j = 0; j < TS::PER; ++j) {
@@ -478,12 +476,12 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
                 for (int i = 0; i < 4; ++i) S[j][i] *= gf.GC(TS::row(j, i));
             }
         }
-        gemm_nt<TI, DK, BV, C>(S, KdT, LDC, UT, LDC);
+        gemm<TI, DK, BV, C, true, true>(S, Kd, LDK, Ub, LDV);
         __syncthreads();
     }
     if (OUTPUT && p.NT > 0) {
         const int t0 = (p.NT - 1) * C;
-        lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + ((long)bh * p.T + t0) * DVr + v0, DVr, RT, LDV,
+        lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + ((long)bh * p.T + t0) * DVr + v0, DVr, Rb, LDV,
                                  min(C, p.T - t0));
     }
     if (OUTPUT && p.hT && TS::active()) {

@@ -29,14 +29,13 @@ template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_sta
     constexpr size_t E = sizeof(TI);
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
     constexpr int G = GATE == kGateVector ? C * DK : C;
-    constexpr int RT = BV * LDC > C * LDV ? BV * LDC : C * LDV;
-    return 4 * (G + 3 * C) + E * (BV * LDK + 2 * C * LDK + DK * LDC + BV * LDC + 2 * C * LDC + BV * LDC + RT) + 64;
+    return 4 * (G + 3 * C) + E * (BV * LDK + 3 * C * LDK + 3 * C * LDV + 2 * C * LDC) + 64;
 }
 template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t bwd_state_lds() {
     constexpr size_t E = sizeof(TI);
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
     constexpr int G = GATE == kGateVector ? C * DK : C;
-    return 4 * (G + 3 * C) + E * (BV * LDK + C * LDK + 2 * C * LDC + 3 * BV * LDC + 2 * DK * LDC) +
+    return 4 * (G + 3 * C) + E * (BV * LDK + 3 * C * LDK + 2 * C * LDC + C * LDV + BV * LDC) +
            (C >= BV ? 16 : E * C * LDV) + 64;
 }
 constexpr size_t kLdsMax = 160 * 1024;
