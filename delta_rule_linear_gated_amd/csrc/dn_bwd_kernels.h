@@ -308,17 +308,22 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     rK.load(k, D, valid);
     RegN<TI, C, C> rT;
     rT.load(static_cast<const TI*>(p.Tm) + chunk * C * C, C, C);
-    RegB<TI, VB, D> rS0, rdS1;
-    RegN<TI, C, VB> rlam, rdo, rv;
-    auto load_block = [&](int b) {
+    // two register sets: the loads of block b + 2 are issued when block b is
+    // committed, so two blocks of loads are in flight during the loop
+    struct BlockRegs {
+        RegB<TI, VB, D> S0, dS1;
+        RegN<TI, C, VB> lam, dO, V;
+    } rb[2];
+    auto load_block = [&](BlockRegs& r, int b) {
         const int v0 = b * VB;
-        rS0.load(S0g + (long)v0 * D, D, VB);
-        rdS1.load(dS1g + (long)v0 * D, D, VB);
-        rlam.load(lamg + v0, D, C);
-        rdo.load(dO + v0, D, valid);
-        rv.load(v + v0, D, valid);
+        r.S0.load(S0g + (long)v0 * D, D, VB);
+        r.dS1.load(dS1g + (long)v0 * D, D, VB);
+        r.lam.load(lamg + v0, D, C);
+        r.dO.load(dO + v0, D, valid);
+        r.V.load(v + v0, D, valid);
     };
-    load_block(0);
+    load_block(rb[0], 0);
+    if (NVB > 1) load_block(rb[1], 1);
     // sum_v S0[v][c] dS1[v][c] over this thread's rows of every block
     float ls[L::RS::PER][L::RS::VW] = {};
     rg.commit(rowf, gam_s, beta_s);
@@ -329,16 +334,17 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     else
         rK.store(KG, LD);   // scalar: Gam_t is applied to X's rows
     rT.store(TLs, LC);
-    auto commit_block = [&]() {
-        rS0.dot_rows(rdS1, ls);
-        rS0.store_n(S0B, LD, Identity());
-        rdS1.store_n(DS1B, LD, Identity());
-        rlam.store(LAMB, LVB);
-        rdo.store(DOB, LVB);
-        rv.store(VBL, LVB);
+    auto commit_block = [&](BlockRegs& r) {
+        r.S0.dot_rows(r.dS1, ls);
+        r.S0.store_n(S0B, LD, Identity());
+        r.dS1.store_n(DS1B, LD, Identity());
+        r.lam.store(LAMB, LVB);
+        r.dO.store(DOB, LVB);
+        r.V.store(VBL, LVB);
     };
-    commit_block();
+    commit_block(rb[0]);
     __syncthreads();
+    if (NVB > 2) load_block(rb[0], 2);
 
     // ---------------- d_v loop
     f32x4 dq[TO::PER], dkp[TO::PER], dkm[TO::PER], dA[TCC::PER], dP[TCC::PER];
@@ -348,9 +354,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     zero_acc<C, C>(dA);
     zero_acc<C, C>(dP);
     float dbr_part[TX::PER] = {};   // sum over this lane's 4 v of lambda (V - X) at row t = TX::col(j)
-#pragma unroll 1
+#pragma unroll
     for (int b = 0; b < NVB; ++b) {
-        if (b + 1 < NVB) load_block(b + 1);
         // X_b^T = S0_b (K Gam)^T and the two S0 contractions (S0 rows read as [k][m])
         f32x4 X[TX::PER];
         zero_acc<VB, C>(X);
@@ -387,8 +392,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         gemm<TI, C, C, VB, false, false>(dP, UB, LVB, DOB, LVB);
         __syncthreads();
         if (b + 1 < NVB) {
-            commit_block();
+            commit_block(rb[(b + 1) & 1]);
             __syncthreads();
+            if (b + 3 < NVB) load_block(rb[(b + 1) & 1], b + 3);
         }
     }
 
