@@ -241,19 +241,22 @@ struct BwdChunkSmem {
     static constexpr size_t GAM = al(BIG_END);                                    // gam [C][D] or [C]
     static constexpr size_t ROWF = GAM + al(VEC ? C * D * 4 : C * 4);             // [2][C] (scalar)
     static constexpr size_t BETA = ROWF + al(2 * C * 4);                          // [C]
-    static constexpr size_t RED_R = BETA + al(C * 4);                             // [D/16][C] row partials
-    static constexpr size_t RED_C = RED_R + al((D / 16) * C * 4);                 // [C/16][D] column partials
+    static constexpr size_t RED_R = BETA + al(C * 4);                             // [D/16][C] row partials (dbeta_A)
+    static constexpr size_t RED_G = RED_R + al((D / 16) * C * 4);                 // [D/16][C] row partials (d gam)
+    static constexpr size_t RED_B = RED_G + al((D / 16) * C * 4);                 // [VB/16][C] row partials (dbeta_R)
+    static constexpr size_t RED_C = RED_B + al((VB / 16) * C * 4);                // [C/16][D] column partials
     static constexpr size_t LASTS = RED_C + al((C / 16) * D * 4);                 // [D]
-    static constexpr size_t DBR = LASTS + al(D * 4);                              // [C]
-    static constexpr size_t TOTAL = DBR + al(C * 4);
+    static constexpr size_t PART = LASTS + al(D * 4);                             // [D/64 rounded up]
+    static constexpr size_t TOTAL = PART + 256;
     // dq / dk write-back tiles [C][LD] each at offset 0; d gam of the vector gate
     // [C][D] fp32 after them, written once every phase-C tile is dead
     static constexpr size_t DGB = al(2 * C * LD * E);
     static_assert(!VEC || DGB + C * D * 4 <= BIG_END, "d gam buffer");
     // per-thread partials of sum_v S0 dS1 [row blocks of the S0 register tile][D] fp32,
-    // over the dead d_v-loop tiles right after the loop
+    // beside the write-back tiles (and d gam)
     using RS = RegB<TI, VB, D>;
-    static_assert(LOOP + RS::BR * D * 4 <= BIG_END, "S0 dS1 partials");
+    static constexpr size_t LSRED = VEC ? DGB + al(C * D * 4) : DGB;
+    static_assert(LSRED + RS::BR * D * 4 <= BIG_END, "S0 dS1 partials");
     static_assert(2 * C * LD * E <= BIG_END, "write-back tiles");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -279,9 +282,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     float* rowf = reinterpret_cast<float*>(smem + L::ROWF);
     float* beta_s = reinterpret_cast<float*>(smem + L::BETA);
     float* red_r = reinterpret_cast<float*>(smem + L::RED_R);
+    float* red_g = reinterpret_cast<float*>(smem + L::RED_G);
+    float* red_b = reinterpret_cast<float*>(smem + L::RED_B);
+    float* part_s = reinterpret_cast<float*>(smem + L::PART);
     float* red_c = reinterpret_cast<float*>(smem + L::RED_C);
     float* lastS = reinterpret_cast<float*>(smem + L::LASTS);
-    float* dbr = reinterpret_cast<float*>(smem + L::DBR);
     float* dgb = reinterpret_cast<float*>(smem + L::DGB);
 
     const int n = blockIdx.x, bh = blockIdx.y;
@@ -404,36 +409,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     rq.load(q, D, valid);
     if (VEC) rk.load(k, D, valid);
 
-    // ---------------- dbeta_R, sum_v S0 dS1, and the d_v-contraction epilogues
-    float* lsred = reinterpret_cast<float*>(smem + L::LOOP);   // d_v-loop tiles are dead
-    if (TX::active()) {
-#pragma unroll
-        for (int j = 0; j < TX::PER; ++j) {
-            float s = dbr_part[j];
-            s += __shfl_xor(s, 16);
-            s += __shfl_xor(s, 32);
-            if (lane_id() < 16) red_r[(TX::m0(j) / 16) * C + TX::col(j)] = s;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < L::RS::PER; ++i) {
-        if (L::RS::owns(i)) {
-#pragma unroll
-            for (int kk = 0; kk < L::RS::VW; ++kk) lsred[L::RS::rowblk(i) * D + L::RS::col0(i) + kk] = ls[i][kk];
-        }
-    }
-    __syncthreads();   // row and column partials complete
-    for (int t = threadIdx.x; t < C; t += kThreads) {
-        float s = 0.f;
-        for (int b = 0; b < VB / 16; ++b) s += red_r[b * C + t];
-        dbr[t] = s;
-    }
-    for (int c = threadIdx.x; c < D; c += kThreads) {
-        float s = 0.f;
-        for (int h = 0; h < L::RS::BR; ++h) s += lsred[h * D + c];
-        lastS[c] = s;
-    }
-    __syncthreads();   // red_r and the partials are reused below
     // dq = Gam dQg ; dk+ = -beta Gam dKg ; dk- = Gd dKd   (element c = row, t = col)
     if (TO::active()) {
 #pragma unroll
@@ -568,10 +543,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         }
 
         // -------- finish: dq, dk = dk+ + dk-, dbeta, d gam = q.dq + k.(dk+ - dk-)
-        f32x4 dgm[TO::PER];
         __syncthreads();   // phase-C tiles dead: dq / dk go through LDS for coalesced stores
         TI* dqs = reinterpret_cast<TI*>(smem);
         TI* dks = dqs + C * LD;
+        float* lsred = reinterpret_cast<float*>(smem + L::LSRED);
+        f32x4 dgm[TO::PER];
         if (TO::active()) {
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j) {
@@ -580,81 +556,120 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 st4<TI>(dks + off, dkp[j] + dkm[j]);
                 dgm[j] = qv[j] * dq[j] + kv[j] * (dkp[j] - dkm[j]);
             }
-            // dbeta = dbeta_R + rowsum(K+ Y): sums over c (4 per lane, 4 lane groups, RM tiles)
+            // row partials over c (4 per lane, 4 lane groups, RM tiles) of K+ Y (dbeta)
+            // and, for the scalar gate, of d gam
 #pragma unroll
             for (int in = 0; in < TO::RN; ++in) {
-                float s2 = 0.f;
+                float sb = 0.f, sg = 0.f;
 #pragma unroll
-                for (int im = 0; im < TO::RM; ++im) s2 += dbA[im * TO::RN + in];
-                s2 += __shfl_xor(s2, 16);
-                s2 += __shfl_xor(s2, 32);
-                if (lane_id() < 16) red_r[TO::rg() * C + TO::col(in)] = s2;
+                for (int im = 0; im < TO::RM; ++im) {
+                    sb += dbA[im * TO::RN + in];
+                    const f32x4 x = dgm[im * TO::RN + in];
+                    sg += x[0] + x[1] + x[2] + x[3];
+                }
+                sb += __shfl_xor(sb, 16);
+                sb += __shfl_xor(sb, 32);
+                if (SCA) {
+                    sg += __shfl_xor(sg, 16);
+                    sg += __shfl_xor(sg, 32);
+                }
+                if (lane_id() < 16) {
+                    red_r[TO::rg() * C + TO::col(in)] = sb;
+                    if (SCA) red_g[TO::rg() * C + TO::col(in)] = sg;
+                }
+            }
+        }
+        // dbeta_R row partials over v (X^T tiles: 4 v per lane, 4 lane groups)
+        if (TX::active()) {
+#pragma unroll
+            for (int j = 0; j < TX::PER; ++j) {
+                float sr = dbr_part[j];
+                sr += __shfl_xor(sr, 16);
+                sr += __shfl_xor(sr, 32);
+                if (lane_id() < 16) red_b[(TX::m0(j) / 16) * C + TX::col(j)] = sr;
+            }
+        }
+        // per-thread partials of sum_v S0 dS1 (gate terms only)
+        if (GATE != kGateNone) {
+#pragma unroll
+            for (int i = 0; i < L::RS::PER; ++i) {
+                if (L::RS::owns(i)) {
+#pragma unroll
+                    for (int kk = 0; kk < L::RS::VW; kk += 4)
+                        st4<float>(lsred + L::RS::rowblk(i) * D + L::RS::col0(i) + kk,
+                                   f32x4{ls[i][kk], ls[i][kk + 1], ls[i][kk + 2], ls[i][kk + 3]});
+                }
             }
         }
         __syncthreads();
         lds_to_global<TI, C, D>(static_cast<TI*>(p.dq) + row0 * D, D, dqs, LD, valid);
         lds_to_global<TI, C, D>(static_cast<TI*>(p.dk) + row0 * D, D, dks, LD, valid);
         for (int t = threadIdx.x; t < valid; t += kThreads) {
-            float s2 = dbr[t];
+            float s2 = 0.f;
+            for (int b = 0; b < VB / 16; ++b) s2 += red_b[b * C + t];
             for (int b = 0; b < TO::WM; ++b) s2 += red_r[b * C + t];
             p.dbeta[row0 + t] = s2;
         }
-        if (GATE == kGateNone) return;
-        __syncthreads();
-        // d gam: elementwise terms + the gam_C terms on the last valid row
-        if (VEC) {
-            if (TO::active()) {
-#pragma unroll
-                for (int j = 0; j < TO::PER; ++j) st4<float>(dgb + TO::col(j) * D + TO::row(j, 0), dgm[j]);
-            }
-            __syncthreads();
-            for (int c = threadIdx.x; c < D; c += kThreads) {
-                float last = fexp(gl[c]) * lastS[c];
-                for (int b = 0; b < TO::WN; ++b) last += red_c[b * D + c];
-                float acc = 0.f;
-                for (int t = valid - 1; t >= 0; --t) {
-                    acc += dgb[t * D + c] + (t == valid - 1 ? last : 0.f);
-                    p.dg[(row0 + t) * D + c] = acc;
+        if constexpr (GATE != kGateNone) {
+            // gam_C terms: lastS[c] = sum_v S0 dS1 and the Kd dKd column sums; for the
+            // scalar gate their total over c, one partial per wave
+            if (wave_id() < (D + 63) / 64) {
+                const int c = threadIdx.x;
+                float x = 0.f;
+                if (c < D) {
+                    float ssum = 0.f;
+                    for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * D + c];
+                    float cs = 0.f;
+                    for (int b = 0; b < TO::WN; ++b) cs += red_c[b * D + c];
+                    lastS[c] = ssum;
+                    x = gf.GC(c) * ssum + cs;
+                    if (VEC) lastS[c] = fexp(gl[c]) * ssum + cs;   // the whole last-row term of channel c
+                }
+                if (SCA) {
+                    x = row16_sum(x);
+                    const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0)) +
+                                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16)) +
+                                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32)) +
+                                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+                    if (lane_id() == 0) part_s[wave_id()] = tot;
                 }
             }
-        } else {
-            if (TO::active()) {
+            __syncthreads();
+            // d gam: elementwise terms + the gam_C terms on the last valid row
+            if (VEC) {
+                if (TO::active()) {
 #pragma unroll
-                for (int in = 0; in < TO::RN; ++in) {
-                    float s2 = 0.f;
-#pragma unroll
-                    for (int im = 0; im < TO::RM; ++im) {
-                        const f32x4 x = dgm[im * TO::RN + in];
-                        s2 += x[0] + x[1] + x[2] + x[3];
+                    for (int j = 0; j < TO::PER; ++j) st4<float>(dgb + TO::col(j) * D + TO::row(j, 0), dgm[j]);
+                }
+                __syncthreads();
+                for (int c = threadIdx.x; c < D; c += kThreads) {
+                    const float last = lastS[c];
+                    float acc = 0.f;
+                    for (int t = valid - 1; t >= 0; --t) {
+                        acc += dgb[t * D + c] + (t == valid - 1 ? last : 0.f);
+                        p.dg[(row0 + t) * D + c] = acc;
                     }
-                    s2 += __shfl_xor(s2, 16);
-                    s2 += __shfl_xor(s2, 32);
-                    if (lane_id() < 16) red_r[TO::rg() * C + TO::col(in)] = s2;
                 }
-            }
-            __syncthreads();
-            if (wave_id() == 0) {
-                // last-row total: sum_c (Gam_C lastS[c] + column partials of Kd dKd)
-                float part = 0.f;
-                for (int c = lane_id(); c < D; c += 64) {
-                    float x = gf.GC(c) * lastS[c];
-                    for (int b = 0; b < TO::WN; ++b) x += red_c[b * D + c];
-                    part += x;
-                }
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+            } else if (wave_id() == 0) {
                 const int t = lane_id();
                 float x = 0.f;
                 if (t < valid) {
-                    for (int b = 0; b < TO::WM; ++b) x += red_r[b * C + t];
-                    if (t == valid - 1) x += part;
+                    for (int b = 0; b < TO::WM; ++b) x += red_g[b * C + t];
+                    if (t == valid - 1)
+                        for (int w = 0; w < (D + 63) / 64; ++w) x += part_s[w];
                 }
-                // reverse inclusive scan over t: dg_t = sum_{s >= t} x_s
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float y = __shfl_down(x, off);
-                    if (t + off < 64) x += y;
-                }
+                // reverse inclusive scan over the 64 lanes, dg_t = sum_{s >= t} x_s: within
+                // each row of 16 lanes by DPP row shifts (lane i adds lane i + n of its row,
+                // 0 past the row end), then the totals of the later rows
+                x += dpp_f<0x101>(x);
+                x += dpp_f<0x102>(x);
+                x += dpp_f<0x104>(x);
+                x += dpp_f<0x108>(x);
+                const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+                const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+                const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+                const int row = t >> 4;
+                x += (row < 1 ? r1 : 0.f) + (row < 2 ? r2 : 0.f) + (row < 3 ? r3 : 0.f);
                 if (t < valid) p.dg[row0 + t] = x;
             }
         }
