@@ -49,11 +49,9 @@ dn_status check_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
     pr->C = s->C;
     pr->bf16 = s->dtype == DN_BF16;
     pr->gate = s->gate;
-    pr->BV = 0;
     if (!dn::supported(*pr))
         return fail(DN_ERR_UNSUPPORTED, "no kernel for dtype=%s gate=%d C=%d d=%d (LDS budget)",
                     pr->bf16 ? "bf16" : "fp32", s->gate, s->C, s->dk);
-    pr->BV = dn::pick_bv(*pr);
     d->BH = (size_t)s->B * s->H;
     d->T = (size_t)s->T;
     d->NT = s->T > 0 ? ((size_t)s->T + s->C - 1) / s->C : 0;

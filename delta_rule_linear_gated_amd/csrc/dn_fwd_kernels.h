@@ -131,9 +131,12 @@ template <typename TI, int GATE, int C, int DK> struct PrepSmem {
     static constexpr size_t R0B_END = PS + al(C * LC * sizeof(TI));
     static constexpr size_t R0 = R0_END > R0B_END ? R0_END : R0B_END;
     static constexpr size_t AS = R0;                    // fp32 [C][LDA]
+    // vector gate: segment totals of the per-channel cumsum [NSEG][DK] fp32
+    static constexpr int NSEG = (kThreads / DK) < C ? (kThreads / DK) : C;
     static constexpr size_t GAM = AS + al(C * LDA * 4);
     static constexpr size_t BETA = GAM + al(C * GW * 4);
-    static constexpr size_t TOTAL = BETA + al(C * 4);
+    static constexpr size_t TOT = BETA + al(C * 4);
+    static constexpr size_t TOTAL = TOT + (VEC ? al(NSEG * DK * 4) : 0);
 };
 
 // ---------------------------------------------------------------------------
@@ -183,12 +186,34 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
             }
         }
     } else if (GATE == kGateVector) {
-        for (int c = threadIdx.x; c < DK; c += kThreads) {
-            float acc = 0.f;
-            for (int t = 0; t < C; ++t) {
-                if (t < valid) acc += p.g[(row0 + t) * DK + c];
-                gam_s[t * DK + c] = acc;
-                if (t < valid) p.gam[(row0 + t) * DK + c] = acc;
+        // per-channel cumsum in two levels: NSEG segments of RS rows per channel, one
+        // thread each (branch-free loads of its RS rows, a local prefix sum), then the
+        // totals of the earlier segments
+        constexpr int NSEG = L::NSEG, RS = C / NSEG;
+        float* tot = reinterpret_cast<float*>(smem + L::TOT);
+        const int c = threadIdx.x % DK, seg = threadIdx.x / DK;
+        float x[RS];
+        if (seg < NSEG) {
+#pragma unroll
+            for (int r = 0; r < RS; ++r) {
+                const int t = seg * RS + r;
+                const float gv = p.g[(row0 + (t < valid ? t : valid - 1)) * DK + c];
+                x[r] = t < valid ? gv : 0.f;
+            }
+#pragma unroll
+            for (int r = 1; r < RS; ++r) x[r] += x[r - 1];
+            tot[seg * DK + c] = x[RS - 1];
+        }
+        __syncthreads();
+        if (seg < NSEG) {
+            float off = 0.f;
+            for (int s2 = 0; s2 < seg; ++s2) off += tot[s2 * DK + c];
+#pragma unroll
+            for (int r = 0; r < RS; ++r) {
+                const int t = seg * RS + r;
+                const float y = x[r] + off;
+                gam_s[t * DK + c] = y;
+                if (t < valid) p.gam[(row0 + t) * DK + c] = y;
             }
         }
     }

@@ -55,7 +55,6 @@ struct Problem {
     int B, H, T, dk, dv, C;
     int bf16;   // 1: bf16 I/O, 0: fp32 I/O
     int gate;   // Gate
-    int BV;     // d_v block of the sequential kernels
 };
 
 // Workspace carving per pass (0 forward, 1 backward with saved data, 2 backward
@@ -76,7 +75,6 @@ SavedLayout saved_layout(const Problem& pr);
 hipError_t launch_forward(const Problem& pr, const Params& p, bool save_states, hipStream_t stream);
 hipError_t launch_backward(const Problem& pr, const Params& p, bool have_states, hipStream_t stream);
 bool supported(const Problem& pr);
-int pick_bv(const Problem& pr);
 
 // Optional per-kernel timing (dn_profile.cpp); no-ops unless enabled.
 void prof_begin(hipStream_t stream, const char* name);

@@ -2,6 +2,8 @@
 // (one per pass x I/O type x gate, compiled in parallel).
 #pragma once
 
+#include <atomic>
+
 #include "dn_bwd_kernels.h"
 #include "dn_fwd_kernels.h"
 #include "dn_internal.h"
@@ -52,23 +54,79 @@ template <typename TI, int GATE, int C, int D> struct Fits {
                                   !(sizeof(TI) == 4 && D == 64 && GATE == kGateVector && C == 64);
 };
 
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// d_v block of the sequential kernels: the widest of 64, 32, 16 (at most D) whose
+// grid of (D / BV) * BH workgroups still gives every compute unit one; the
+// narrowest when none does (few heads: more, shorter chains per chunk).
+template <int D> int state_block(int BH) {
+    const int cus = device_cus();
+    for (int bv = D < 64 ? D : 64; bv >= 16; bv /= 2)
+        if ((D / bv) * BH >= cus) return bv;
+    return D < 16 ? D : 16;
+}
+
+template <typename TI, int GATE, int C, int D, int BV>
+void launch_fwd_state(const Params& p, int BH, bool save, bool output, hipStream_t stream) {
+    const dim3 grid((D / BV) * BH), block(kThreads);
+    if (output) {
+        if (save)
+            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, true>), grid, block, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, false>), grid, block, 0, stream, p);
+    }
+}
+
+template <typename TI, int GATE, int C, int D>
+void fwd_state(const Params& p, int BH, bool save, bool output, hipStream_t stream) {
+    const int bv = state_block<D>(BH);
+    if (bv >= 64 && D >= 64)
+        launch_fwd_state<TI, GATE, C, D, (D < 64 ? D : 64)>(p, BH, save, output, stream);
+    else if (bv >= 32 && D >= 32)
+        launch_fwd_state<TI, GATE, C, D, (D < 32 ? D : 32)>(p, BH, save, output, stream);
+    else
+        launch_fwd_state<TI, GATE, C, D, 16>(p, BH, save, output, stream);
+}
+
+template <typename TI, int GATE, int C, int D>
+void bwd_state(const Params& p, int BH, hipStream_t stream) {
+    const int bv = state_block<D>(BH);
+    const dim3 block(kThreads);
+    if (bv >= 64 && D >= 64) {
+        constexpr int BV = D < 64 ? D : 64;
+        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3((D / BV) * BH), block, 0, stream, p);
+    } else if (bv >= 32 && D >= 32) {
+        constexpr int BV = D < 32 ? D : 32;
+        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3((D / BV) * BH), block, 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, 16>), dim3((D / 16) * BH), block, 0, stream, p);
+    }
+}
+
 template <typename TI, int GATE, int C, int D>
 hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t stream) {
     if constexpr (!Fits<TI, GATE, C, D>::value) {
         return hipErrorInvalidConfiguration;
     } else {
-        constexpr int BV = D < 64 ? D : 64;
         const int BH = pr.B * pr.H;
         prof_begin(stream, "prep");
         hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
         prof_end(stream);
         prof_begin(stream, "fwd_state");
-        if (save)
-            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, true>), dim3((D / BV) * BH),
-                               dim3(kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, true>), dim3((D / BV) * BH),
-                               dim3(kThreads), 0, stream, p);
+        fwd_state<TI, GATE, C, D>(p, BH, save, true, stream);
         prof_end(stream);
         return hipGetLastError();
     }
@@ -79,20 +137,17 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
     if constexpr (!Fits<TI, GATE, C, D>::value) {
         return hipErrorInvalidConfiguration;
     } else {
-        constexpr int BV = D < 64 ? D : 64;
         const int BH = pr.B * pr.H;
         if (!have_states) {   // recomputation policy: gam, T, P and the states into the workspace
             prof_begin(stream, "prep_recompute");
             hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
             prof_end(stream);
             prof_begin(stream, "fwd_state_recompute");
-            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, false>), dim3((D / BV) * BH),
-                               dim3(kThreads), 0, stream, p);
+            fwd_state<TI, GATE, C, D>(p, BH, true, false, stream);
             prof_end(stream);
         }
         prof_begin(stream, "bwd_state");
-        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3((D / BV) * BH), dim3(kThreads), 0,
-                           stream, p);
+        bwd_state<TI, GATE, C, D>(p, BH, stream);
         prof_end(stream);
         prof_begin(stream, "bwd_chunk");
         hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);

@@ -25,8 +25,6 @@ const LaunchFn kBwd[2][3] = {{launch_bwd_f32_g0, launch_bwd_f32_g1, launch_bwd_f
 
 }  // namespace
 
-int pick_bv(const Problem& pr) { return pr.dv < 64 ? pr.dv : 64; }
-
 bool supported(const Problem& pr) {
     if (pr.dk != pr.dv) return false;
     DN_DISPATCH(fits_rt)
