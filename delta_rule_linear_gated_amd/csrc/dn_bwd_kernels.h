@@ -57,13 +57,10 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     __shared__ __align__(16) TI Tl[C * LDC];     // T               [s][t]
     __shared__ __align__(16) TI dOb[C * LDV];    // dO block        [t][v]
     __shared__ __align__(16) TI dUT[BV * LDC];   // dU^T            [v][t]
-    // lambda and dv = beta lambda [t][v], written back a chunk later: lambda over
-    // Kd (dead once dU is formed), dv over P when it fits (dead as well), and dv
-    // is also the operand of the dS update
-    constexpr bool DB_IN_P = C >= BV;
-    __shared__ __align__(16) TI DbSep[DB_IN_P ? 8 : C * LDV];
-    TI* Lb = Kd;
-    TI* Db = DB_IN_P ? Pl : DbSep;
+    // lambda and dv = beta lambda [t][v], written back a chunk later (dv is also the
+    // operand of the dS update)
+    __shared__ __align__(16) TI Lb[C * LDV];
+    __shared__ __align__(16) TI Db[C * LDV];
 
     const int DVr = p.DVr;
     int bh, vblk;
@@ -88,6 +85,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         const long row0 = (long)bh * p.T + t0;
         const long cc = ((long)bh * p.NT + n) * C * C;
         rg.load(p.gam + row0 * GW, p.beta + row0, valid);
+        __builtin_amdgcn_sched_barrier(0);   // gate first, then the tiles, in order (see RegN)
         rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
         rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
         rdo.load(static_cast<const TI*>(p.dout) + row0 * DVr + v0, DVr, valid);
@@ -101,15 +99,6 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     for (int n = p.NT - 1; n >= 0; --n) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
-        // write back lambda and dv of the chunk done last iteration (a full chunk of
-        // work after they were formed); the sync keeps commit() off their tiles
-        if (n + 1 < p.NT) {
-            const long rp = (long)bh * p.T + (n + 1) * C;
-            lds_to_global<TI, C, BV>(static_cast<TI*>(p.lam) + ((long)bh * p.NT + n + 1) * C * DVr + v0, DVr, Lb,
-                                     LDV, C);
-            lds_to_global<TI, C, BV>(static_cast<TI*>(p.dv) + rp * DVr + v0, DVr, Db, LDV, min(C, p.T - (n + 1) * C));
-            __syncthreads();
-        }
         // (a) dS1 of this chunk: operand copy (written to the workspace from LDS below)
         if (TS::active()) {
 #pragma unroll
@@ -131,10 +120,18 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         rdo.store(dOb, LDV);
         rP.store(Pl, LDC);
         rT.store(Tl, LDC);
+        // lambda and dv of the chunk done last iteration (in Lb / Db until (d) below)
+        if (n + 1 < p.NT) {
+            const long rp = (long)bh * p.T + (n + 1) * C;
+            lds_to_global<TI, C, BV>(static_cast<TI*>(p.lam) + ((long)bh * p.NT + n + 1) * C * DVr + v0, DVr, Lb,
+                                     LDV, C);
+            lds_to_global<TI, C, BV>(static_cast<TI*>(p.dv) + rp * DVr + v0, DVr, Db, LDV, min(C, p.T - (n + 1) * C));
+        }
         __syncthreads();
-        if (n > 0) prefetch(n - 1);
         lds_to_global<TI, BV, DK>(static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, dSs, LDK,
                                   BV);
+        // the next chunk's loads last and unconditional (see the forward state kernel)
+        prefetch(n > 0 ? n - 1 : 0);
 
         // (c) dU = P^T dO + Kd dS1^T  -> dU^T   (P and dO read as [k][m] / [k][n])
         {

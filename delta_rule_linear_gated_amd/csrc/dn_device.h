@@ -388,8 +388,22 @@ __device__ __forceinline__ void stage_copy(T* lds, int ldl, const T* __restrict_
 // compiler wait for it at the end of the branch, which serialises the tile.
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// A loaded register passed through an empty asm: no use of it can be scheduled
+// above this point.  Applied where a prefetched tile is consumed; otherwise the
+// compiler may start reformatting the next chunk's tile right after its load
+// (in the previous iteration), which makes the wave wait for the load there.
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+__device__ __forceinline__ uint4 pin(const uint4& v) {
+    u32x4 x = {v.x, v.y, v.z, v.w};
+    asm volatile("" : "+v"(x));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // RegN: row-major thread mapping (16-byte vectors, consecutive lanes along a
-// row), for natural-layout stores.
+// row), for natural-layout stores.  Loads are issued in program order (a
+// scheduling barrier after each): a prefetch before a loop and the one inside
+// it then issue identically, and the wait counts merged at the loop head stay
+// precise instead of waiting for every outstanding load and store.
 template <typename T, int ROWS, int COLS> struct RegN {
     static constexpr int VW = 16 / sizeof(T), VPR = COLS / VW, NV = ROWS * VPR;
     static constexpr int PER = (NV + kThreads - 1) / kThreads;
@@ -408,6 +422,7 @@ template <typename T, int ROWS, int COLS> struct RegN {
             const int idx = idx_of(i);
             const int row = idx / VPR, c0 = (idx % VPR) * VW;
             r[i] = *reinterpret_cast<const uint4*>(g + (row < valid ? row : valid - 1) * gld + c0);
+            __builtin_amdgcn_sched_barrier(0);   // fixed issue order (see the note above)
         }
     }
     // rows >= valid store as row valid - 1 (for cumulative quantities)
@@ -423,7 +438,8 @@ template <typename T, int ROWS, int COLS> struct RegN {
         for (int i = 0; i < PER; ++i) {
             const int idx = idx_of(i);
             const int row = idx / VPR, c0 = (idx % VPR) * VW;
-            const T* src = reinterpret_cast<const T*>(&r[i]);
+            const uint4 ri = pin(r[i]);
+            const T* src = reinterpret_cast<const T*>(&ri);
             T* out = reinterpret_cast<T*>(&outv[i]);
 #pragma unroll
             for (int e = 0; e < VW; ++e) {
@@ -445,7 +461,7 @@ template <typename T, int ROWS, int COLS> struct RegN {
             const int idx = threadIdx.x + i * kThreads;
             if (idx >= NV) continue;
             const int row = idx / VPR, c0 = (idx % VPR) * VW;
-            *reinterpret_cast<uint4*>(lds + row * ldl + c0) = row < valid_ ? r[i] : zero_u4();
+            *reinterpret_cast<uint4*>(lds + row * ldl + c0) = row < valid_ ? pin(r[i]) : zero_u4();
         }
     }
 };
@@ -490,6 +506,7 @@ template <typename T, int ROWS, int COLS> struct RegB {
             for (int e = 0; e < BRW; ++e) {
                 const int row = r0 + e < valid ? r0 + e : valid - 1;
                 r[i][e] = *reinterpret_cast<const uint4*>(g + row * gld + c0);
+                __builtin_amdgcn_sched_barrier(0);   // fixed issue order (see RegN)
             }
         }
     }
@@ -505,8 +522,9 @@ template <typename T, int ROWS, int COLS> struct RegB {
         for (int i = 0; i < PER; ++i)
 #pragma unroll
             for (int e = 0; e < BRW; ++e) {
-                const T* x = reinterpret_cast<const T*>(&r[i][e]);
-                const T* y = reinterpret_cast<const T*>(&o.r[i][e]);
+                const uint4 a = pin(r[i][e]), b = pin(o.r[i][e]);
+                const T* x = reinterpret_cast<const T*>(&a);
+                const T* y = reinterpret_cast<const T*>(&b);
 #pragma unroll
                 for (int k = 0; k < VW; ++k) acc[i][k] += to_f(x[k]) * to_f(y[k]);
             }
@@ -514,6 +532,11 @@ template <typename T, int ROWS, int COLS> struct RegB {
     // lds[c * ldl + r] = f(r, c, x).  Two-phase like RegN::store.
     template <class F> __device__ __forceinline__ void store_t(T* lds, int ldl, F f) const {
         TV outv[PER][VW];
+        uint4 rr[PER][BRW];
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int k = 0; k < BRW; ++k) rr[i][k] = pin(r[i][k]);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int b = blk(i);
@@ -523,7 +546,7 @@ template <typename T, int ROWS, int COLS> struct RegB {
                 T* out = reinterpret_cast<T*>(&outv[i][e]);
 #pragma unroll
                 for (int k = 0; k < BRW; ++k) {
-                    const float y = f(r0 + k, c0 + e, to_f(reinterpret_cast<const T*>(&r[i][k])[e]));
+                    const float y = f(r0 + k, c0 + e, to_f(reinterpret_cast<const T*>(&rr[i][k])[e]));
                     out[k] = from_f<T>(r0 + k < valid_ ? y : 0.f);
                 }
             }
@@ -546,7 +569,8 @@ template <typename T, int ROWS, int COLS> struct RegB {
             const int r0 = (b % BR) * BRW, c0 = (b / BR) * VW;
 #pragma unroll
             for (int e = 0; e < BRW; ++e) {
-                const T* src = reinterpret_cast<const T*>(&r[i][e]);
+                const uint4 ri = pin(r[i][e]);
+                const T* src = reinterpret_cast<const T*>(&ri);
                 T* out = reinterpret_cast<T*>(&outv[i][e]);
 #pragma unroll
                 for (int k = 0; k < VW; ++k) {

@@ -307,9 +307,12 @@ template <int GATE, int C, int DK> struct GateRegs {
         const int t = threadIdx.x;
         const int tt = t < valid ? t : valid - 1;
         b = beta[tt];
+        __builtin_amdgcn_sched_barrier(0);   // fixed issue order (see RegN)
         if (GATE == kGateScalar) {
             gs = gam[tt];
+            __builtin_amdgcn_sched_barrier(0);
             gC = gam[valid - 1];
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (VEC) gv.load_clamped(gam, DK, valid);
     }
@@ -408,6 +411,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         const long row0 = (long)bh * p.T + t0;
         const long cc = ((long)bh * p.NT + n) * C * C;
         rg.load(p.gam + row0 * GW, p.beta + row0, valid);
+        __builtin_amdgcn_sched_barrier(0);   // gate first, then the tiles, in order (see RegN)
         rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
         rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
         rv.load(static_cast<const TI*>(p.v) + row0 * DVr + v0, DVr, valid);
@@ -423,10 +427,6 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
         const long row0 = (long)bh * p.T + t0;
-        // write back the previous chunk's O (a full chunk of work after it was formed,
-        // so the stores never sit just ahead of a wait on this chunk's loads)
-        if (OUTPUT && n > 0)
-            lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + (row0 - C) * DVr + v0, DVr, Rb, LDV, C);
         // (a) state operand (saved from LDS below)
         if (TS::active()) {
 #pragma unroll
@@ -448,11 +448,19 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         rv.store(Vb, LDV);
         rT.store(Tl, LDC);
         if constexpr (OUTPUT) rP.store(Pl, LDC);
+        // the previous chunk's O (in Rb until (c) below overwrites it)
+        if (OUTPUT && n > 0)
+            lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + (row0 - C) * DVr + v0, DVr, Rb, LDV, C);
         __syncthreads();
-        if (n + 1 < p.NT) prefetch(n + 1);
         if (SAVE)
             lds_to_global<TI, BV, DK>(static_cast<TI*>(p.states) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, Ss,
                                       LDK, BV);
+        // The next chunk's loads come after every global store of the iteration and
+        // unconditionally (the last chunk reloads itself): the wait counts at the loop
+        // head are merged over the first entry (the loads alone) and the back edge,
+        // and only with the loads last on both do they stay exact instead of waiting
+        // for every outstanding load and store.
+        prefetch(n + 1 < p.NT ? n + 1 : n);
 
         // (c) X^T = S0 (K Gam)^T ;  R = diag(beta) (V - X)
         {

@@ -37,18 +37,19 @@ template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t bwd_sta
     constexpr size_t E = sizeof(TI);
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
     constexpr int G = GATE == kGateVector ? C * DK : C;
-    return 4 * (G + 3 * C) + E * (BV * LDK + 3 * C * LDK + 2 * C * LDC + C * LDV + BV * LDC) +
-           (C >= BV ? 16 : E * C * LDV) + 64;
+    return 4 * (G + 3 * C) + E * (BV * LDK + 3 * C * LDK + 2 * C * LDC + 3 * C * LDV + BV * LDC) + 64;
 }
 constexpr size_t kLdsMax = 160 * 1024;
 
 // bwd_chunk's layout asserts are only meaningful when the configuration fits;
 // evaluate its TOTAL lazily through this helper.
+// A d_v block BV of the sequential kernels is usable when both fit in LDS.
+template <typename TI, int GATE, int C, int D, int BV> constexpr bool state_fits() {
+    return BV <= D && fwd_state_lds<TI, GATE, C, D, BV>() <= kLdsMax && bwd_state_lds<TI, GATE, C, D, BV>() <= kLdsMax;
+}
 template <typename TI, int GATE, int C, int D> struct Fits {
-    static constexpr int BV = D < 64 ? D : 64;
-    static constexpr bool small = prep_lds<TI, GATE, C, D>() <= kLdsMax &&
-                                  fwd_state_lds<TI, GATE, C, D, BV>() <= kLdsMax &&
-                                  bwd_state_lds<TI, GATE, C, D, BV>() <= kLdsMax;
+    static constexpr int BVMIN = D < 16 ? D : 16;
+    static constexpr bool small = prep_lds<TI, GATE, C, D>() <= kLdsMax && state_fits<TI, GATE, C, D, BVMIN>();
     // fp32 at D = 128 cannot hold the backward's tiles
     static constexpr bool value = small && !(sizeof(TI) == 4 && D > 64) &&
                                   !(sizeof(TI) == 4 && D == 64 && GATE == kGateVector && C == 64);
@@ -67,53 +68,59 @@ inline int device_cus() {
     return v;
 }
 
-// d_v block of the sequential kernels: the widest of 64, 32, 16 (at most D) whose
-// grid of (D / BV) * BH workgroups still gives every compute unit one; the
-// narrowest when none does (few heads: more, shorter chains per chunk).
-template <int D> int state_block(int BH) {
+// d_v block of the sequential kernels: the widest of 64, 32, 16 (at most D, and
+// fitting in LDS) whose grid of (D / BV) * BH workgroups still gives every
+// compute unit one; the narrowest when none does (few heads: more, shorter
+// chains per chunk).
+template <typename TI, int GATE, int C, int D> int state_block(int BH) {
     const int cus = device_cus();
-    for (int bv = D < 64 ? D : 64; bv >= 16; bv /= 2)
-        if ((D / bv) * BH >= cus) return bv;
-    return D < 16 ? D : 16;
-}
-
-template <typename TI, int GATE, int C, int D, int BV>
-void launch_fwd_state(const Params& p, int BH, bool save, bool output, hipStream_t stream) {
-    const dim3 grid((D / BV) * BH), block(kThreads);
-    if (output) {
-        if (save)
-            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, true>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, true>), grid, block, 0, stream, p);
-    } else {
-        hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, false>), grid, block, 0, stream, p);
+    const bool ok[3] = {state_fits<TI, GATE, C, D, 64>(), state_fits<TI, GATE, C, D, 32>(),
+                        state_fits<TI, GATE, C, D, 16>()};
+    const int bvs[3] = {64, 32, 16};
+    int last = D < 16 ? D : 16;
+    for (int i = 0; i < 3; ++i) {
+        if (!ok[i]) continue;
+        last = bvs[i];
+        if ((D / bvs[i]) * BH >= cus) return bvs[i];
     }
+    return last;
 }
 
-template <typename TI, int GATE, int C, int D>
-void fwd_state(const Params& p, int BH, bool save, bool output, hipStream_t stream) {
-    const int bv = state_block<D>(BH);
-    if (bv >= 64 && D >= 64)
-        launch_fwd_state<TI, GATE, C, D, (D < 64 ? D : 64)>(p, BH, save, output, stream);
-    else if (bv >= 32 && D >= 32)
-        launch_fwd_state<TI, GATE, C, D, (D < 32 ? D : 32)>(p, BH, save, output, stream);
+// OUTPUT is a template argument so that the forward and the backward units each
+// instantiate only the variants they launch.
+template <typename TI, int GATE, int C, int D, int BV, bool OUTPUT>
+void launch_fwd_state(const Params& p, int BH, bool save, hipStream_t stream) {
+    const dim3 grid((D / BV) * BH), block(kThreads);
+    if (!OUTPUT || save)
+        hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, OUTPUT>), grid, block, 0, stream, p);
     else
-        launch_fwd_state<TI, GATE, C, D, 16>(p, BH, save, output, stream);
+        hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, true>), grid, block, 0, stream, p);
+}
+
+template <typename TI, int GATE, int C, int D, bool OUTPUT>
+void fwd_state(const Params& p, int BH, bool save, hipStream_t stream) {
+    const int bv = state_block<TI, GATE, C, D>(BH);
+    if constexpr (state_fits<TI, GATE, C, D, 64>())
+        if (bv == 64) return launch_fwd_state<TI, GATE, C, D, 64, OUTPUT>(p, BH, save, stream);
+    if constexpr (state_fits<TI, GATE, C, D, 32>())
+        if (bv == 32) return launch_fwd_state<TI, GATE, C, D, 32, OUTPUT>(p, BH, save, stream);
+    if constexpr (state_fits<TI, GATE, C, D, 16>())
+        launch_fwd_state<TI, GATE, C, D, 16, OUTPUT>(p, BH, save, stream);
+}
+
+template <typename TI, int GATE, int C, int D, int BV> void launch_bwd_state(const Params& p, int BH, hipStream_t stream) {
+    hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3((D / BV) * BH), dim3(kThreads), 0, stream, p);
 }
 
 template <typename TI, int GATE, int C, int D>
 void bwd_state(const Params& p, int BH, hipStream_t stream) {
-    const int bv = state_block<D>(BH);
-    const dim3 block(kThreads);
-    if (bv >= 64 && D >= 64) {
-        constexpr int BV = D < 64 ? D : 64;
-        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3((D / BV) * BH), block, 0, stream, p);
-    } else if (bv >= 32 && D >= 32) {
-        constexpr int BV = D < 32 ? D : 32;
-        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3((D / BV) * BH), block, 0, stream, p);
-    } else {
-        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, 16>), dim3((D / 16) * BH), block, 0, stream, p);
-    }
+    const int bv = state_block<TI, GATE, C, D>(BH);
+    if constexpr (state_fits<TI, GATE, C, D, 64>())
+        if (bv == 64) return launch_bwd_state<TI, GATE, C, D, 64>(p, BH, stream);
+    if constexpr (state_fits<TI, GATE, C, D, 32>())
+        if (bv == 32) return launch_bwd_state<TI, GATE, C, D, 32>(p, BH, stream);
+    if constexpr (state_fits<TI, GATE, C, D, 16>())
+        launch_bwd_state<TI, GATE, C, D, 16>(p, BH, stream);
 }
 
 template <typename TI, int GATE, int C, int D>
@@ -126,7 +133,7 @@ hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t s
         hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
         prof_end(stream);
         prof_begin(stream, "fwd_state");
-        fwd_state<TI, GATE, C, D>(p, BH, save, true, stream);
+        fwd_state<TI, GATE, C, D, true>(p, BH, save, stream);
         prof_end(stream);
         return hipGetLastError();
     }
@@ -143,7 +150,7 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
             hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
             prof_end(stream);
             prof_begin(stream, "fwd_state_recompute");
-            fwd_state<TI, GATE, C, D>(p, BH, true, false, stream);
+            fwd_state<TI, GATE, C, D, false>(p, BH, true, stream);
             prof_end(stream);
         }
         prof_begin(stream, "bwd_state");
