@@ -46,21 +46,28 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     constexpr int LDV = BV + PAD;
     constexpr int GW = GateLayout<GATE, DK>::GW;
     constexpr bool VEC = GATE == kGateVector;
+    constexpr bool SCA = GATE == kGateScalar;
+    // A scalar gate is a row scaling: Q and K stay unscaled (K staged once) and the
+    // decays go to the C x BV operands -- e^{gam_C - gam_t} to the K dS1^T part of
+    // dU, e^{gam_t} to copies of dO and of -beta lambda for the dS update.  The
+    // vector gate scales Q and K per element.
     __shared__ float gam_s[VEC ? C * DK : C];
-    __shared__ float rowf[2 * C];
+    __shared__ __align__(16) float rowf[2 * C];
     __shared__ __align__(16) float beta_s[C];
     __shared__ __align__(16) TI dSs[BV * LDK];   // dS1 operand     [v][c]
-    __shared__ __align__(16) TI Kd[C * LDK];     // K Gam_C / Gam   [t][c]
-    __shared__ __align__(16) TI Kn[C * LDK];     // -K Gam          [t][c]
-    __shared__ __align__(16) TI Qg[C * LDK];     // Q Gam           [t][c]
+    __shared__ __align__(16) TI Kd[C * LDK];     // K (vector gate: K Gam_C / Gam)  [t][c]
+    __shared__ __align__(16) TI Kn[VEC ? C * LDK : 8];   // -K Gam (vector gate)    [t][c]
+    __shared__ __align__(16) TI Qg[C * LDK];     // Q (vector gate: Q Gam)          [t][c]
     __shared__ __align__(16) TI Pl[C * LDC];     // P               [s][t]
     __shared__ __align__(16) TI Tl[C * LDC];     // T               [s][t]
     __shared__ __align__(16) TI dOb[C * LDV];    // dO block        [t][v]
+    __shared__ __align__(16) TI dOg[SCA ? C * LDV : 8];  // dO Gam (scalar gate)    [t][v]
     __shared__ __align__(16) TI dUT[BV * LDC];   // dU^T            [v][t]
-    // lambda and dv = beta lambda [t][v], written back a chunk later (dv is also the
-    // operand of the dS update)
+    // lambda and dv = beta lambda [t][v], written back a chunk later; without a
+    // vector gate the dS update takes -beta lambda (Gam) from Dn, else dv itself
     __shared__ __align__(16) TI Lb[C * LDV];
     __shared__ __align__(16) TI Db[C * LDV];
+    __shared__ __align__(16) TI Dn[VEC ? 8 : C * LDV];
 
     const int DVr = p.DVr;
     int bh, vblk;
@@ -108,16 +115,16 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         rg.commit(rowf, gam_s, beta_s);
         __syncthreads();
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
-        if (GATE == kGateNone) {
-            rk.store(Kd, LDK);
-            rk.store(Kn, LDK, [](int, int, float x) { return -x; });
-            rq.store(Qg, LDK);
-        } else {
+        if (VEC) {
             rk.store(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
             rk.store(Kn, LDK, [&](int r, int c, float x) { return -x * gf.G(r, c); });
             rq.store(Qg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
+        } else {
+            rk.store(Kd, LDK);
+            rq.store(Qg, LDK);
         }
         rdo.store(dOb, LDV);
+        if (SCA) rdo.store(dOg, LDV, [&](int r, int, float x) { return x * rowf[r]; });
         rP.store(Pl, LDC);
         rT.store(Tl, LDC);
         // lambda and dv of the chunk done last iteration (in Lb / Db until (d) below)
@@ -137,8 +144,12 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         {
             f32x4 dU[TX::PER];
             zero_acc<C, BV>(dU);
-            gemm<TI, C, BV, C, true, true>(dU, Pl, LDC, dOb, LDV);
             gemm<TI, C, BV, DK, false, false>(dU, Kd, LDK, dSs, LDK);
+            if (SCA && TX::active()) {   // rows t of K dS1^T times e^{gam_C - gam_t}
+#pragma unroll
+                for (int j = 0; j < TX::PER; ++j) dU[j] *= ld4<float>(rowf + C + TX::row(j, 0));
+            }
+            gemm<TI, C, BV, C, true, true>(dU, Pl, LDC, dOb, LDV);
             if (TX::active()) {
 #pragma unroll
                 for (int j = 0; j < TX::PER; ++j) st4<TI>(dUT + TX::col(j) * LDC + TX::row(j, 0), dU[j]);
@@ -157,9 +168,10 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
                 for (int j = 0; j < TL::PER; ++j) bt[j] = beta_s[TL::col(j)];
 #pragma unroll
                 for (int j = 0; j < TL::PER; ++j) {
-                    const int off = TL::col(j) * LDV + TL::row(j, 0);
+                    const int t = TL::col(j), off = t * LDV + TL::row(j, 0);
                     st4<TI>(Lb + off, Lm[j]);
                     st4<TI>(Db + off, bt[j] * Lm[j]);
+                    if (!VEC) st4<TI>(Dn + off, (-(SCA ? rowf[t] : 1.f) * bt[j]) * Lm[j]);
                 }
             }
         }
@@ -172,8 +184,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
                 for (int i = 0; i < 4; ++i) dS[j][i] *= gf.GC(TS::row(j, i));
             }
         }
-        gemm<TI, DK, BV, C, true, true>(dS, Qg, LDK, dOb, LDV);
-        gemm<TI, DK, BV, C, true, true>(dS, Kn, LDK, Db, LDV);
+        gemm<TI, DK, BV, C, true, true>(dS, Qg, LDK, SCA ? dOg : dOb, LDV);
+        gemm<TI, DK, BV, C, true, true>(dS, VEC ? Kn : Kd, LDK, VEC ? Db : Dn, LDV);
         __syncthreads();
     }
     if (p.NT > 0) {   // lambda and dv of chunk 0

@@ -369,21 +369,28 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     constexpr int LDC = C + PAD;
     constexpr int LDV = BV + PAD;
     constexpr int GW = GateLayout<GATE, DK>::GW;
-    // every tile in its natural layout; operands contracted over their leading
-    // index are read with the transposing LDS load
-    __shared__ float gam_s[GATE == kGateVector ? C * DK : C];
+    constexpr bool VEC = GATE == kGateVector;
+    constexpr bool SCA = GATE == kGateScalar;
+    // Every tile in its natural layout; operands contracted over their leading
+    // index are read with the transposing LDS load.  A scalar gate is a row
+    // scaling, so Q and K stay unscaled (staged once) and the decays are applied
+    // to the C x BV results instead: e^{gam_t} to X and to the Q S0^T part of O,
+    // e^{gam_C - gam_t} to a second copy of U that feeds the state update.  The
+    // per-channel vector gate scales Q and K per element.
+    __shared__ float gam_s[VEC ? C * DK : C];
     __shared__ float rowf[2 * C];
     __shared__ __align__(16) float beta_s[C];
     __shared__ __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
-    __shared__ __align__(16) TI Qg[C * LDK];     // Q Gam             [t][c]
-    __shared__ __align__(16) TI Kg[C * LDK];     // K Gam             [t][c]
-    __shared__ __align__(16) TI Kd[C * LDK];     // K Gam_C / Gam     [t][c]
+    __shared__ __align__(16) TI Qg[C * LDK];     // Q (vector gate: Q Gam)            [t][c]
+    __shared__ __align__(16) TI Kg[C * LDK];     // K (vector gate: K Gam)            [t][c]
+    __shared__ __align__(16) TI Kd[VEC ? C * LDK : 8];   // K Gam_C / Gam (vector gate) [t][c]
     __shared__ __align__(16) TI Vb[C * LDV];     // V block           [t][v]
     __shared__ __align__(16) TI Tl[C * LDC];     // T                 [t][s]
     __shared__ __align__(16) TI Pl[C * LDC];     // P                 [t][s]
     // R [t][v]; after (d) it holds the chunk's O [t][v] until the next iteration writes it back
     __shared__ __align__(16) TI Rb[C * LDV];
     __shared__ __align__(16) TI Ub[C * LDV];     // U                 [t][v]
+    __shared__ __align__(16) TI Ud[SCA ? C * LDV : 8];   // U Gam_C / Gam (scalar gate) [t][v]
 
     const int DVr = p.DVr;
     int bh, vblk;
@@ -436,14 +443,13 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         rg.commit(rowf, gam_s, beta_s);
         __syncthreads();
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
-        if (GATE == kGateNone) {
-            rq.store(Qg, LDK);
-            rk.store(Kg, LDK);
-            rk.store(Kd, LDK);
-        } else {
+        if (VEC) {
             rq.store(Qg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
             rk.store(Kg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
             rk.store(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
+        } else {
+            rq.store(Qg, LDK);
+            rk.store(Kg, LDK);
         }
         rv.store(Vb, LDV);
         rT.store(Tl, LDC);
@@ -472,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
 #pragma unroll
                 for (int j = 0; j < TX::PER; ++j) {
                     const int t = TX::col(j), c = TX::row(j, 0);
-                    r[j] = beta_s[t] * (ld4<TI>(Vb + t * LDV + c) - X[j]);
+                    r[j] = beta_s[t] * (ld4<TI>(Vb + t * LDV + c) - (SCA ? rowf[t] : 1.f) * X[j]);
                 }
 #pragma unroll
                 for (int j = 0; j < TX::PER; ++j) st4<TI>(Rb + TX::col(j) * LDV + TX::row(j, 0), r[j]);
@@ -486,7 +492,11 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             gemm<TI, BV, C, C, true, false>(U, Rb, LDV, Tl, LDC);
             if (TX::active()) {
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) st4<TI>(Ub + TX::col(j) * LDV + TX::row(j, 0), U[j]);
+                for (int j = 0; j < TX::PER; ++j) {
+                    const int t = TX::col(j), off = t * LDV + TX::row(j, 0);
+                    st4<TI>(Ub + off, U[j]);
+                    if (SCA) st4<TI>(Ud + off, rowf[C + t] * U[j]);
+                }
             }
         }
         __syncthreads();
@@ -495,6 +505,10 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             f32x4 OT[TX::PER];
             zero_acc<BV, C>(OT);
             gemm<TI, BV, C, DK, false, false>(OT, Ss, LDK, Qg, LDK);
+            if (SCA && TX::active()) {
+#pragma unroll
+                for (int j = 0; j < TX::PER; ++j) OT[j] *= rowf[TX::col(j)];
+            }
             gemm<TI, BV, C, C, true, false>(OT, Ub, LDV, Pl, LDC);
             if (TX::active()) {
 #pragma unroll
@@ -509,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
                 for (int i = 0; i < 4; ++i) S[j][i] *= gf.GC(TS::row(j, i));
             }
         }
-        gemm<TI, DK, BV, C, true, true>(S, Kd, LDK, Ub, LDV);
+        gemm<TI, DK, BV, C, true, true>(S, VEC ? Kd : Kg, LDK, SCA ? Ud : Ub, LDV);
         __syncthreads();
     }
     if (OUTPUT && p.NT > 0) {

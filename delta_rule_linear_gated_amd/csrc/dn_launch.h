@@ -31,13 +31,18 @@ template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_sta
     constexpr size_t E = sizeof(TI);
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
     constexpr int G = GATE == kGateVector ? C * DK : C;
-    return 4 * (G + 3 * C) + E * (BV * LDK + 3 * C * LDK + 3 * C * LDV + 2 * C * LDC) + 64;
+    constexpr int NK = GATE == kGateVector ? 3 : 2;   // Q, K (+ K Gam_C / Gam)
+    constexpr int NV = GATE == kGateScalar ? 4 : 3;   // V, R, U (+ U Gam_C / Gam)
+    return 4 * (G + 3 * C) + E * (BV * LDK + NK * C * LDK + NV * C * LDV + 2 * C * LDC) + 96;
 }
 template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t bwd_state_lds() {
     constexpr size_t E = sizeof(TI);
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
     constexpr int G = GATE == kGateVector ? C * DK : C;
-    return 4 * (G + 3 * C) + E * (BV * LDK + 3 * C * LDK + 2 * C * LDC + 3 * C * LDV + BV * LDC) + 64;
+    constexpr int NK = GATE == kGateVector ? 3 : 2;   // K, Q (+ -K Gam)
+    // dO, lambda, dv, then -beta lambda (Gam) without a vector gate, dO Gam with a scalar one
+    constexpr int NV = GATE == kGateVector ? 3 : (GATE == kGateScalar ? 5 : 4);
+    return 4 * (G + 3 * C) + E * (BV * LDK + NK * C * LDK + 2 * C * LDC + NV * C * LDV + BV * LDC) + 128;
 }
 constexpr size_t kLdsMax = 160 * 1024;
 
