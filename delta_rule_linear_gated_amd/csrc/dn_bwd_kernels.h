@@ -229,13 +229,15 @@ struct BwdChunkSmem {
     static constexpr size_t KG = 0;                                  // K (or K Gam)   [C][LD]
     static constexpr size_t TL = KG + al(C * LD * E);                // T              [C][LC]
     static constexpr size_t LOOP = TL + al(C * LC * E);
-    // d_v loop, one block
-    static constexpr size_t S0B = LOOP;                              // S0 rows        [VB][LD]
+    // d_v loop: two buffers of one block's tiles (offsets within a buffer), so the
+    // next block is committed while this one computes
+    static constexpr size_t S0B = 0;                                 // S0 rows        [VB][LD]
     static constexpr size_t DS1B = S0B + al(VB * LD * E);            // dS1 rows       [VB][LD]
     static constexpr size_t LAMB = DS1B + al(VB * LD * E);           // lambda block   [C][LVB]
     static constexpr size_t DOB = LAMB + al(C * LVB * E);            // dO block       [C][LVB]
     static constexpr size_t VBL = DOB + al(C * LVB * E);             // V block, then U block [C][LVB]
-    static constexpr size_t RB = VBL + al(C * LVB * E);              // R block        [C][LVB]
+    static constexpr size_t BLK = VBL + al(C * LVB * E);
+    static constexpr size_t RB = LOOP + 2 * BLK;                     // R block        [C][LVB]
     static constexpr size_t LOOP_END = RB + al(C * LVB * E);
     // phase C (over the d_v-loop tiles)
     static constexpr size_t DA = LOOP;                               // dA~            [C][LC]
@@ -280,12 +282,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     __shared__ __align__(16) char smem[L::TOTAL];
     TI* KG = reinterpret_cast<TI*>(smem + L::KG);
     TI* TLs = reinterpret_cast<TI*>(smem + L::TL);
-    TI* S0B = reinterpret_cast<TI*>(smem + L::S0B);
-    TI* DS1B = reinterpret_cast<TI*>(smem + L::DS1B);
-    TI* LAMB = reinterpret_cast<TI*>(smem + L::LAMB);
-    TI* DOB = reinterpret_cast<TI*>(smem + L::DOB);
-    TI* VBL = reinterpret_cast<TI*>(smem + L::VBL);
-    TI* UB = VBL;   // V is dead once R is formed; U is dead before the next block's V
+    // tiles of block-buffer i (V and then U share a slot: V is dead once R is formed)
+    auto blk = [&](int i, size_t off) { return reinterpret_cast<TI*>(smem + L::LOOP + i * L::BLK + off); };
     TI* RB = reinterpret_cast<TI*>(smem + L::RB);
     float* gam_s = reinterpret_cast<float*>(smem + L::GAM);
     float* rowf = reinterpret_cast<float*>(smem + L::ROWF);
@@ -348,15 +346,15 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     else
         rK.store(KG, LD);   // scalar: Gam_t is applied to X's rows
     rT.store(TLs, LC);
-    auto commit_block = [&](BlockRegs& r) {
+    auto commit_block = [&](BlockRegs& r, int i) {
         r.S0.dot_rows(r.dS1, ls);
-        r.S0.store_n(S0B, LD, Identity());
-        r.dS1.store_n(DS1B, LD, Identity());
-        r.lam.store(LAMB, LVB);
-        r.dO.store(DOB, LVB);
-        r.V.store(VBL, LVB);
+        r.S0.store_n(blk(i, L::S0B), LD, Identity());
+        r.dS1.store_n(blk(i, L::DS1B), LD, Identity());
+        r.lam.store(blk(i, L::LAMB), LVB);
+        r.dO.store(blk(i, L::DOB), LVB);
+        r.V.store(blk(i, L::VBL), LVB);
     };
-    commit_block(rb[0]);
+    commit_block(rb[0], 0);
     __syncthreads();
     if (NVB > 2) load_block(rb[0], 2);
 
@@ -370,6 +368,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     float dbr_part[TX::PER] = {};   // sum over this lane's 4 v of lambda (V - X) at row t = TX::col(j)
 #pragma unroll
     for (int b = 0; b < NVB; ++b) {
+        TI* S0B = blk(b & 1, L::S0B);
+        TI* DS1B = blk(b & 1, L::DS1B);
+        TI* LAMB = blk(b & 1, L::LAMB);
+        TI* DOB = blk(b & 1, L::DOB);
+        TI* VBL = blk(b & 1, L::VBL);
+        TI* UB = VBL;
         // X_b^T = S0_b (K Gam)^T and the two S0 contractions (S0 rows read as [k][m])
         f32x4 X[TX::PER];
         zero_acc<VB, C>(X);
@@ -377,19 +381,25 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         gemm<TI, D, C, VB, true, false>(dq, S0B, LD, DOB, LVB);
         gemm<TI, D, C, VB, true, false>(dkp, S0B, LD, LAMB, LVB);
         if (TX::active()) {
-            f32x4 rb[TX::PER];   // LDS reads first, then the writes
+            f32x4 rr[TX::PER];   // LDS reads first, then the writes
 #pragma unroll
             for (int j = 0; j < TX::PER; ++j) {
                 const int t = TX::col(j), c = TX::row(j, 0);
                 const f32x4 xr = ld4<TI>(VBL + t * LVB + c) - (SCA ? rowf[t] : 1.f) * X[j];
                 const f32x4 lm = ld4<TI>(LAMB + t * LVB + c);
                 dbr_part[j] += lm[0] * xr[0] + lm[1] * xr[1] + lm[2] * xr[2] + lm[3] * xr[3];
-                rb[j] = beta_s[t] * xr;
+                rr[j] = beta_s[t] * xr;
             }
 #pragma unroll
-            for (int j = 0; j < TX::PER; ++j) st4<TI>(RB + TX::col(j) * LVB + TX::row(j, 0), rb[j]);
+            for (int j = 0; j < TX::PER; ++j) st4<TI>(RB + TX::col(j) * LVB + TX::row(j, 0), rr[j]);
         }
         __syncthreads();
+        // block b + 1 into the other buffer (free since block b - 1 ended), read after
+        // the two barriers below
+        if (b + 1 < NVB) {
+            commit_block(rb[(b + 1) & 1], (b + 1) & 1);
+            if (b + 3 < NVB) load_block(rb[(b + 1) & 1], b + 3);
+        }
         // U_b^T = R_b^T T^T  (R rows read as [k][m])
         {
             f32x4 U[TX::PER];
@@ -405,11 +415,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         gemm<TI, C, C, VB, false, false>(dA, UB, LVB, LAMB, LVB);
         gemm<TI, C, C, VB, false, false>(dP, UB, LVB, DOB, LVB);
         __syncthreads();
-        if (b + 1 < NVB) {
-            commit_block(rb[(b + 1) & 1]);
-            __syncthreads();
-            if (b + 3 < NVB) load_block(rb[(b + 1) & 1], b + 3);
-        }
     }
 
     // q (and k for the vector gate) for the key-gradient products (loads in flight
