@@ -378,8 +378,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         f32x4 X[TX::PER];
         zero_acc<VB, C>(X);
         gemm<TI, VB, C, D, false, false>(X, S0B, LD, KG, LD);
-        gemm<TI, D, C, VB, true, false>(dq, S0B, LD, DOB, LVB);
-        gemm<TI, D, C, VB, true, false>(dkp, S0B, LD, LAMB, LVB);
+        gemm2<TI, D, C, VB, true, false>(dq, dkp, S0B, LD, DOB, LAMB, LVB);
         if (TX::active()) {
             f32x4 rr[TX::PER];   // LDS reads first, then the writes
 #pragma unroll
@@ -412,8 +411,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         }
         __syncthreads();
         gemm<TI, D, C, VB, true, false>(dkm, DS1B, LD, UB, LVB);
-        gemm<TI, C, C, VB, false, false>(dA, UB, LVB, LAMB, LVB);
-        gemm<TI, C, C, VB, false, false>(dP, UB, LVB, DOB, LVB);
+        gemm2<TI, C, C, VB, false, false>(dA, dP, UB, LVB, LAMB, DOB, LVB);
         __syncthreads();
     }
 

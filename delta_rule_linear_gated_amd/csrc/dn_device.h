@@ -265,6 +265,48 @@ __device__ __forceinline__ void gemm(f32x4 (&acc)[NACC], const T* A, int lda, co
     }
 }
 
+// Two products with the same A: acc1 += A * B1^T, acc2 += A * B2^T (layouts as in
+// gemm), each A fragment read once for both.
+template <typename T, int M, int N, int K, bool TA, bool TB, int NACC>
+__device__ __forceinline__ void gemm2(f32x4 (&acc1)[NACC], f32x4 (&acc2)[NACC], const T* A, int lda, const T* B1,
+                                      const T* B2, int ldb) {
+    using TL = Tiles<M, N>;
+    using MM = typename MmaFor<T, K>::type;
+    static_assert(NACC == TL::PER, "accumulator count");
+    if constexpr (sizeof(T) == 2 && MM::kStep == 16) {
+        gemm<T, M, N, K, TA, TB>(acc1, A, lda, B1, ldb);
+        gemm<T, M, N, K, TA, TB>(acc2, A, lda, B2, ldb);
+    } else {
+        if (!TL::active()) return;
+        auto fa = [&](int im, int k0) {
+            const int m = TL::m0(0) + im * 16;
+            return TA ? MM::load_t(A + k0 * lda + m, lda) : MM::load(A + m * lda + k0, lda);
+        };
+        auto fb = [&](const T* B, int in, int k0) {
+            const int n = TL::n0(0) + in * 16;
+            return TB ? MM::load_t(B + k0 * ldb + n, ldb) : MM::load(B + n * ldb + k0, ldb);
+        };
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += MM::kStep) {
+            typename MM::Frag a[TL::RM], b1[TL::RN], b2[TL::RN];
+#pragma unroll
+            for (int im = 0; im < TL::RM; ++im) a[im] = fa(im, k0);
+#pragma unroll
+            for (int in = 0; in < TL::RN; ++in) {
+                b1[in] = fb(B1, in, k0);
+                b2[in] = fb(B2, in, k0);
+            }
+#pragma unroll
+            for (int im = 0; im < TL::RM; ++im)
+#pragma unroll
+                for (int in = 0; in < TL::RN; ++in) {
+                    acc1[im * TL::RN + in] = MM::op(a[im], b1[in], acc1[im * TL::RN + in]);
+                    acc2[im * TL::RN + in] = MM::op(a[im], b2[in], acc2[im * TL::RN + in]);
+                }
+        }
+    }
+}
+
 template <int M, int N, int NACC>
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NACC]) {
     static_assert(NACC == Tiles<M, N>::PER, "accumulator count");
@@ -641,6 +683,17 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += dpp_f<0x4E>(x);
     x += dpp_f<0x141>(x);
     x += dpp_f<0x140>(x);
+    return x;
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8 or 16), every
+// lane of a group getting the total (the DPP steps of row16_sum).
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group");
+    if (N >= 2) x += dpp_f<0xB1>(x);
+    if (N >= 4) x += dpp_f<0x4E>(x);
+    if (N >= 8) x += dpp_f<0x141>(x);
+    if (N >= 16) x += dpp_f<0x140>(x);
     return x;
 }
 
