@@ -27,7 +27,7 @@ DN_GATE_NONE, DN_GATE_SCALAR, DN_GATE_VECTOR = 0, 1, 2
 DN_PASS_FWD, DN_PASS_BWD, DN_PASS_BWD_RECOMPUTE = 0, 1, 2
 
 EXPORTS = ("dn_states_bytes", "dn_states_layout", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
-           "dn_chunk_bwd", "dn_status_string", "dn_last_error", "dn_profile_enable",
+           "dn_chunk_bwd", "dn_recurrent_fwd", "dn_status_string", "dn_last_error", "dn_profile_enable",
            "dn_profile_collect")
 
 
@@ -64,6 +64,8 @@ def lib():
     L.dn_workspace_layout.restype = i32
     L.dn_states_layout.argtypes = [sp, ctypes.POINTER(ctypes.c_size_t)]
     L.dn_states_layout.restype = i32
+    L.dn_recurrent_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.dn_recurrent_fwd.restype = i32
     L.dn_chunk_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dn_chunk_fwd.restype = i32
     L.dn_chunk_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -175,6 +177,12 @@ def dn_chunk_bwd(shape, q, k, v, beta, g, h0, dout, dhT, states, dq, dk, dv, dbe
                               _stream(stream))
 
 
+def dn_recurrent_fwd(shape, q, k, v, beta, g, state, o, stream=None) -> int:
+    """Raw call; returns the dn_status (no exception)."""
+    return lib().dn_recurrent_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                  _ptr(state), _ptr(o), _stream(stream))
+
+
 # ------------------------------------------------------------------ convenience
 
 
@@ -261,6 +269,17 @@ def chunk_bwd(q, k, v, beta, g, h0, do, dhT=None, states=None, C=64, want_dh0=Tr
     _check(dn_chunk_bwd(sh, q, k, v, beta, g, h0, do, dhT, states, dq, dk, dv, dbeta, dg, dh0, ws,
                         ws.numel(), stream))
     return {"dq": dq, "dk": dk, "dv": dv, "dbeta": dbeta, "dg": dg, "dh0": dh0}
+
+
+def recurrent_fwd(q, k, v, beta, g, state, stream=None):
+    """T recurrent steps (decode); `state` (fp32 [B,H,dv,dk]) is updated in place.
+    Returns o."""
+    _contig(q, k, v, beta, g, state)
+    B, H, T, dk = q.shape
+    sh = make_shape(B, H, T, dk, v.shape[-1], 64, q.dtype, _gate_kind(g, dk))
+    o = torch.empty_like(v)
+    _check(dn_recurrent_fwd(sh, q, k, v, beta, g, state, o, stream))
+    return o
 
 
 class DeltaRule(torch.autograd.Function):

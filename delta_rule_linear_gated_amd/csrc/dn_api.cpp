@@ -296,6 +296,63 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
     return DN_OK;
 }
 
+dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, float* state, void* o, void* stream) {
+    g_err[0] = '\0';
+    if (!shape) return fail(DN_ERR_INVALID, "shape is NULL");
+    const dn_shape* s = shape;
+    if (s->B < 0 || s->H < 0 || s->T < 0) return fail(DN_ERR_SHAPE, "B, H, T must be >= 0");
+    if (s->dtype != DN_F32 && s->dtype != DN_BF16) return fail(DN_ERR_DTYPE, "unknown dtype %d", s->dtype);
+    if (s->gate < DN_GATE_NONE || s->gate > DN_GATE_VECTOR) return fail(DN_ERR_INVALID, "unknown gate %d", s->gate);
+    if (s->dk != 16 && s->dk != 32 && s->dk != 64 && s->dk != 128)
+        return fail(DN_ERR_UNSUPPORTED, "dk must be 16, 32, 64 or 128");
+    if (s->dv <= 0 || s->dv % 16 != 0) return fail(DN_ERR_UNSUPPORTED, "dv must be a positive multiple of 16");
+    if ((long long)s->B * s->H * (s->dv / 16) > 0x7fffffffLL) return fail(DN_ERR_UNSUPPORTED, "B*H*dv/16 too large");
+    const size_t BH = (size_t)s->B * s->H, T = (size_t)s->T, E = s->dtype == DN_BF16 ? 2 : 4;
+    const size_t gw = s->gate == DN_GATE_VECTOR ? (size_t)s->dk : 1;
+    const size_t nk = BH * T * s->dk * E, nv = BH * T * s->dv * E, nb = BH * T * 4;
+    const size_t ng = s->gate == DN_GATE_NONE ? 0 : BH * T * gw * 4, ns = BH * s->dv * s->dk * 4;
+    if (s->gate == DN_GATE_NONE && g) return fail(DN_ERR_INVALID, "g must be NULL without a gate");
+    DN_TRY(need(q, nk, "q"));
+    DN_TRY(need(k, nk, "k"));
+    DN_TRY(need(v, nv, "v"));
+    DN_TRY(need(beta, nb, "beta"));
+    DN_TRY(need(g, ng, "g"));
+    DN_TRY(need(state, ns, "state"));
+    DN_TRY(need(o, nv, "o"));
+    DN_TRY(check_buffers({{"q", q, nk, false},
+                          {"k", k, nk, false},
+                          {"v", v, nv, false},
+                          {"beta", beta, nb, false},
+                          {"g", g, ng, false},
+                          {"state", state, ns, true},
+                          {"o", o, nv, true}}));
+    dn::Problem pr{};
+    pr.B = s->B;
+    pr.H = s->H;
+    pr.T = s->T;
+    pr.dk = s->dk;
+    pr.dv = s->dv;
+    pr.C = s->C;
+    pr.bf16 = s->dtype == DN_BF16;
+    pr.gate = s->gate;
+    dn::Params p{};
+    p.BH = (int)BH;
+    p.T = s->T;
+    p.DKr = s->dk;
+    p.DVr = s->dv;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.beta = beta;
+    p.g = g;
+    p.hT = state;
+    p.o = o;
+    const hipError_t e = dn::launch_recurrent(pr, p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return DN_OK;
+}
+
 const char* dn_status_string(dn_status status) {
     switch (status) {
         case DN_OK: return "ok";

@@ -74,6 +74,8 @@ SavedLayout saved_layout(const Problem& pr);
 // Kernel launch sequences (all enqueue on `stream`, none synchronises).
 hipError_t launch_forward(const Problem& pr, const Params& p, bool save_states, hipStream_t stream);
 hipError_t launch_backward(const Problem& pr, const Params& p, bool have_states, hipStream_t stream);
+// Recurrent form: T steps per head, state p.hT (fp32, in place), outputs p.o.
+hipError_t launch_recurrent(const Problem& pr, const Params& p, hipStream_t stream);
 bool supported(const Problem& pr);
 
 // Optional per-kernel timing (dn_profile.cpp); no-ops unless enabled.

@@ -146,6 +146,23 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
                        float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes,
                        void* stream);
 
+/*
+ * Recurrent evaluation (decode): the T steps of the recurrence for every batch
+ * element and head, one token at a time (the recurrent form of the Fast Weight
+ * Attention abstract; the decode setting of the KLA abstract), with the state
+ * updated in place.  Same per-step arithmetic as the chunkwise forward.
+ *   shape  : B, H, T (steps; 0 is a no-op), dk in {16, 32, 64, 128}, dv a
+ *            positive multiple of 16 (may differ from dk), dtype, gate; C unused
+ *   inputs : q, k [B][H][T][dk], v [B][H][T][dv] (io); beta [B][H][T] fp32; g as
+ *            for dn_chunk_fwd (NULL iff gate == DN_GATE_NONE)
+ *   state  : fp32 [B][H][dv][dk]: the state before step 1 on entry, after step T
+ *            on return (in place; it may not overlap any other argument)
+ *   outputs: o [B][H][T][dv] (io)
+ * Validation and errors as for dn_chunk_fwd; no workspace.
+ */
+dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, float* state, void* o, void* stream);
+
 /* Static description of a status code. */
 const char* dn_status_string(dn_status status);
 

@@ -132,3 +132,23 @@ def test_workspace_grows_with_recompute():
     assert B.dn_workspace_bytes(sh, B.DN_PASS_BWD_RECOMPUTE) - B.dn_workspace_bytes(sh, B.DN_PASS_BWD) \
         == B.dn_states_bytes(sh)
     assert B.dn_workspace_bytes(sh, 9) == 0
+
+
+def rec(sh, **over):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, state=FAKE * 6, o=FAKE * 7)
+    a.update(over)
+    return B.dn_recurrent_fwd(sh, a["q"], a["k"], a["v"], a["beta"], a["g"], a["state"], a["o"], 0)
+
+
+def test_validation_errors_recurrent():
+    assert rec(sh_of(T=-1)) == B.DN_ERR_SHAPE
+    assert rec(sh_of(dtype=7)) == B.DN_ERR_DTYPE
+    assert rec(sh_of(gate=3)) == B.DN_ERR_INVALID
+    assert rec(sh_of(dk=48, dv=48)) == B.DN_ERR_UNSUPPORTED
+    assert rec(sh_of(dv=24)) == B.DN_ERR_UNSUPPORTED                   # dv not a multiple of 16
+    assert rec(sh_of(), q=None) == B.DN_ERR_INVALID
+    assert rec(sh_of(), state=None) == B.DN_ERR_INVALID
+    assert rec(sh_of(gate="none")) == B.DN_ERR_INVALID                 # g given without a gate
+    assert rec(sh_of(), o=FAKE * 6) == B.DN_ERR_INVALID                # o aliases the state
+    assert rec(sh_of(), state=FAKE + 8) == B.DN_ERR_INVALID            # misaligned
+    assert "state" in B.dn_last_error() or "aligned" in B.dn_last_error()
