@@ -71,6 +71,12 @@ def parse():
     ap.add_argument("--policy", default=None, choices=[None, "save", "recompute"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-recompute-leg", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="instead of fwd+bwd, time the recurrent (decode) entry point: --decode-batch "
+                         "sequences with the workload's heads and dims, --decode-tokens tokens per "
+                         "sequence and call, the fp32 state updated in place")
+    ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--decode-tokens", type=int, default=1)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run --steps device-to-device copies of MIB MiB "
                          "(a known-size reference for the HBM byte counters) and exit")
@@ -105,6 +111,9 @@ def main():
         return
     B.lib()  # fail loudly if the HIP library is missing
     w = W.CONFIGS[args.workload]
+    if args.decode:
+        decode_bench(args, w)
+        return
     policy = args.policy or w.policy
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -232,6 +241,88 @@ def main():
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / peak, 4),
         "algorithmic_gflop_per_step": round(fl_th * w.token_heads / 1e9, 2),
         "roofline": roofline, "kernels": per_kernel, "other_policy": other, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def decode_bench(args, w0):
+    """Decode throughput of dn_recurrent_fwd: one call advances every sequence of a
+    serving batch by --decode-tokens tokens.  HBM-bound: each call reads and writes
+    the fp32 state once (2 dv dk 4 bytes per head) plus the tokens' q, k, v, beta, g
+    and o."""
+    import torch
+
+    from delta_rule_linear_gated_amd import binding as B
+    from delta_rule_linear_gated_amd import workloads as W
+
+    w = W.custom(args.decode_batch, w0.H, args.decode_tokens, w0.dk, w0.dv, w0.C, w0.gate, w0.dtype,
+                 h0_std=0.5, seed=w0.seed, name=f"decode_{w0.name}")
+    dev = torch.device("cuda:0")
+    print(f"[bench] decode: generating {w.describe()}", file=sys.stderr, flush=True)
+    inp_cpu = W.make_inputs(w, cotangents=False)
+    inp = {n: (None if t is None else t.to(dev)) for n, t in inp_cpu.items()}
+    q, k, v, beta, g = (inp[n] for n in ("q", "k", "v", "beta", "g"))
+    state = inp["h0"].clone()
+    o = torch.empty_like(v)
+    sh = B.make_shape(w.B, w.H, w.T, w.dk, w.dv, w.C, w.dtype, w.gate)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        st = B.dn_recurrent_fwd(sh, q, k, v, beta, g, state, o, stream)
+        if st != B.DN_OK:
+            raise B.DnError(st, B.dn_last_error())
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    B.dn_profile_collect()
+    B.dn_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    B.dn_profile_enable(False)
+    kern = B.dn_profile_collect()
+    E = 2 if w.dtype == "bf16" else 4
+    gw = w.dk if w.gate == "vector" else (0 if w.gate == "none" else 1)
+    heads = w.B * w.H
+    by = heads * (2 * w.dv * w.dk * 4 + w.T * ((2 * w.dk + 2 * w.dv) * E + 4 * (1 + gw)))
+    fl = heads * w.T * 8 * w.dv * w.dk     # decay, S k, rank-one update, S q
+    tot, n = kern.get("recurrent", (0.0, 0))
+    roofline = None
+    if n:
+        avg_s = tot / n / 1e3
+        ach = by / avg_s / 1e9
+        roofline = {"kernel": "recurrent", "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "algorithmic_bytes_per_launch": int(by), "algorithmic_flops_per_launch": int(fl),
+                    "avg_launch_ms": round(avg_s * 1e3, 4)}
+    tokens = w.B * w.T
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build_oracle()
+        f = {nm: W.to_f64(t) for nm, t in inp_cpu.items()}
+        threads = min(16, os.cpu_count() or 1)
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], nthreads=threads)
+            reps += 1
+            if time.perf_counter() - t0 > 2.0:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        cpu = {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole batch ({w.B * w.H} heads x {w.T} token(s)), fp64, {reps} repetitions"}
+    line = {
+        "metric": "decode tokens/s (recurrent form, state in place)", "value": round(tokens / (ms / 1e3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"decode: gate={w.gate} B={w.B} H={w.H} dk={w.dk} dv={w.dv}, {w.T} token(s) "
+                               f"per sequence and call", "global_batch": w.B, "seq_len": w.T, "heads": w.H,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
