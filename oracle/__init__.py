@@ -130,3 +130,33 @@ def backward(q, k, v, beta, g, h0, do, dhT=None, gate=None, nthreads=0):
     if rc != 0:
         raise RuntimeError("dn_oracle_bwd failed")
     return {"dq": dq, "dk": dkk, "dv": dvv, "dbeta": db, "dg": dg, "dh0": dh0}
+
+
+# --------------------------------------------------------------------------- Kaczmarz step
+# KLA abstract: the Kaczmarz (normalised least-squares) step of the delta rule sets
+# beta_t = eta_t / (||k_t||^2 + eps); nothing else in the recurrence changes.
+
+
+def kaczmarz_beta(eta, k, eps):
+    """beta_t = eta_t / (||k_t||^2 + eps), fp64."""
+    eta, k = _f64(eta), _f64(k)
+    return eta / (np.sum(k * k, axis=-1) + eps)
+
+
+def kaczmarz_forward(q, k, v, eta, g=None, h0=None, eps=1e-6, gate=None, nthreads=0):
+    """``forward`` with beta = kaczmarz_beta(eta, k, eps)."""
+    return forward(q, k, v, kaczmarz_beta(eta, k, eps), g, h0, gate=gate, nthreads=nthreads)
+
+
+def kaczmarz_backward(q, k, v, eta, g, h0, do, dhT=None, eps=1e-6, gate=None, nthreads=0):
+    """Reverse mode through beta = eta / n, n = ||k||^2 + eps (chain rule on top of
+    ``backward``): d eta = d beta / n and dk gains -2 (d beta) beta k / n.
+    Returns the dict of ``backward`` with "deta" in place of "dbeta"."""
+    k64 = _f64(k)
+    n = np.sum(k64 * k64, axis=-1) + eps
+    beta = _f64(eta) / n
+    gr = backward(q, k, v, beta, g, h0, do, dhT, gate=gate, nthreads=nthreads)
+    db = gr.pop("dbeta")
+    gr["deta"] = db / n
+    gr["dk"] = gr["dk"] - (2.0 * db * beta / n)[..., None] * k64
+    return gr

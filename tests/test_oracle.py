@@ -100,6 +100,49 @@ def test_finite_differences(gate):
         assert rel(gr[gname], fd) < 1e-7, (gate, gname, rel(gr[gname], fd))
 
 
+
+def _loss_kacz(c, eps, **over):
+    d = dict(c)
+    d.update(over)
+    o, hT = oracle.kaczmarz_forward(d["q"], d["k"], d["v"], d["eta"], d["g"], d["h0"], eps=eps)
+    return np.sum(o * d["do"]) + np.sum(hT * d["dhT"])
+
+
+@pytest.mark.parametrize("gate", [1, 2])
+def test_finite_differences_kaczmarz(gate):
+    """The Kaczmarz chain rule (d eta and the extra dk term) against central
+    differences of the Kaczmarz forward, with unnormalised keys so ||k|| matters."""
+    c = rand_case(41 + gate, T=6, gate=gate)
+    r = np.random.default_rng(5 + gate)
+    c["k"] = r.standard_normal(c["k"].shape) * 1.3
+    c["eta"] = 1 / (1 + np.exp(-r.standard_normal(c["beta"].shape)))
+    eps = 1e-3
+    gr = oracle.kaczmarz_backward(c["q"], c["k"], c["v"], c["eta"], c["g"], c["h0"], c["do"], c["dhT"], eps=eps)
+    h = 1e-6
+    for inp, gname in [("eta", "deta"), ("k", "dk"), ("q", "dq")]:
+        x = c[inp]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xp[idx] += h
+            xm = x.copy()
+            xm[idx] -= h
+            fd[idx] = (_loss_kacz(c, eps, **{inp: xp}) - _loss_kacz(c, eps, **{inp: xm})) / (2 * h)
+        assert rel(gr[gname], fd) < 1e-7, (gate, gname, rel(gr[gname], fd))
+
+
+def test_kaczmarz_step_projects_onto_the_key():
+    """With g = 0 and eta = 1 one Kaczmarz step solves S k = v exactly (the KLA
+    abstract's normalised least-squares step): o for q = k is v up to eps."""
+    r = np.random.default_rng(8)
+    dk, dv = 5, 3
+    k = r.standard_normal((1, 1, 1, dk)) * 2.0
+    v = r.standard_normal((1, 1, 1, dv))
+    h0 = r.standard_normal((1, 1, dv, dk))
+    eps = 1e-12
+    o, hT = oracle.kaczmarz_forward(k, k, v, np.ones((1, 1, 1)), None, h0, eps=eps)
+    assert np.max(np.abs(o[0, 0, 0] - v[0, 0, 0])) < 1e-9
+
 # --------------------------------------------------------------------------- brute force
 
 
