@@ -39,14 +39,15 @@ def algorithmic_flops_per_token_head(C: int, dk: int, dv: int) -> float:
     return (2 * C * (dk + dv) + 6 * dk * dv + C * C / 3) + (4 * C * (dk + dv) + 12 * dk * dv)
 
 
-def kernel_budget(name: str, C: int, d: int, E: int, gw: int, saved: bool):
+def kernel_budget(name: str, C: int, d: int, E: int, gw: int, saved: bool, kz: bool = False):
     """Algorithmic (flops, HBM bytes) of one kernel per chunk and head: the
     contractions it performs (triangles halved) and the tensors it must read and
-    write once.  E = bytes per I/O element, gw = gate values per step."""
+    write once.  E = bytes per I/O element, gw = gate values per step, kz = the
+    Kaczmarz step (prep writes beta and 1 / (||k||^2 + eps), bwd_chunk reads the latter)."""
     sc = C * 4 * (1 + gw)                     # beta + gate (or d gam) per chunk, fp32
     if name in ("prep", "prep_recompute"):
-        fl = 2 * (C * (C - 1) / 2 * d + C * (C + 1) / 2 * d) + C ** 3 / 3
-        by = 2 * C * d * E + sc + C * gw * 4 + 2 * C * C * E
+        fl = 2 * (C * (C - 1) / 2 * d + C * (C + 1) / 2 * d) + C ** 3 / 3 + (2 * C * d if kz else 0)
+        by = 2 * C * d * E + sc + C * gw * 4 + 2 * C * C * E + (2 * C * 4 if kz else 0)
     elif name in ("fwd_state", "fwd_state_recompute"):
         fl = 2 * (3 * C * d * d + C * C * d)
         by = (3 if name == "fwd_state" else 2) * C * d * E + 2 * C * C * E + sc
@@ -57,6 +58,7 @@ def kernel_budget(name: str, C: int, d: int, E: int, gw: int, saved: bool):
     elif name == "bwd_chunk":
         fl = 2 * (4 * C * d * d + 3.5 * C * C * d)
         by = 4 * C * d * E + 2 * d * d * E + C * d * E + C * C * E + sc + 2 * C * d * E + sc
+        by += C * 4 if kz else 0
     else:
         return None
     return fl, by
@@ -121,7 +123,7 @@ def main():
     inp_cpu = W.make_inputs(w)
     inp = {n: (None if t is None else t.to(dev)) for n, t in inp_cpu.items()}
     q, k, v, beta, g, h0, do, dhT = (inp[n] for n in ("q", "k", "v", "beta", "g", "h0", "do", "dhT"))
-    sh = B.shape_of(q, v, g, w.C)
+    sh = B.shape_of(q, v, g, w.C, w.kaczmarz_eps)   # Kaczmarz workloads: beta carries eta
     E = 2 if w.dtype == "bf16" else 4
     NT = -(-w.T // w.C)
 
@@ -189,7 +191,7 @@ def main():
     roofline = None
     if kern:
         dom = max(kern, key=lambda n: kern[n][0])
-        fl, by = kernel_budget(dom, w.C, w.dk, E, gw, policy == "save")
+        fl, by = kernel_budget(dom, w.C, w.dk, E, gw, policy == "save", w.kla)
         units = w.B * w.H * NT                      # chunk-heads per launch
         avg_s = kern[dom][0] / kern[dom][1] / 1e3
         ach_gbs = by * units / avg_s / 1e9
@@ -236,7 +238,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: gate={w.gate} B={w.B} H={w.H} T={w.T} dk={w.dk} dv={w.dv} "
-                               f"C={w.C} policy={policy}, fwd+bwd",
+                               f"C={w.C} policy={policy}, fwd+bwd"
+                               + (f", Kaczmarz step in-kernel (eps={w.kaczmarz_eps:g})" if w.kla else ""),
                    "global_batch": w.B, "seq_len": w.T, "heads": w.H, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / peak, 4),
         "algorithmic_gflop_per_step": round(fl_th * w.token_heads / 1e9, 2),
@@ -256,7 +259,7 @@ def decode_bench(args, w0):
     from delta_rule_linear_gated_amd import workloads as W
 
     w = W.custom(args.decode_batch, w0.H, args.decode_tokens, w0.dk, w0.dv, w0.C, w0.gate, w0.dtype,
-                 h0_std=0.5, seed=w0.seed, name=f"decode_{w0.name}")
+                 h0_std=0.5, kla=w0.kla, seed=w0.seed, name=f"decode_{w0.name}", kz_eps=w0.kz_eps)
     dev = torch.device("cuda:0")
     print(f"[bench] decode: generating {w.describe()}", file=sys.stderr, flush=True)
     inp_cpu = W.make_inputs(w, cotangents=False)
@@ -264,7 +267,7 @@ def decode_bench(args, w0):
     q, k, v, beta, g = (inp[n] for n in ("q", "k", "v", "beta", "g"))
     state = inp["h0"].clone()
     o = torch.empty_like(v)
-    sh = B.make_shape(w.B, w.H, w.T, w.dk, w.dv, w.C, w.dtype, w.gate)
+    sh = B.make_shape(w.B, w.H, w.T, w.dk, w.dv, w.C, w.dtype, w.gate, w.kaczmarz_eps)
     stream = torch.cuda.current_stream(dev)
 
     def call():
@@ -308,7 +311,11 @@ def decode_bench(args, w0):
         t0 = time.perf_counter()
         reps = 0
         while True:
-            oracle.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], nthreads=threads)
+            if w.kla:
+                oracle.kaczmarz_forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], eps=w.kaczmarz_eps,
+                                        nthreads=threads)
+            else:
+                oracle.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], nthreads=threads)
             reps += 1
             if time.perf_counter() - t0 > 2.0:
                 break
@@ -343,9 +350,14 @@ def cpu_baseline(w, inp_cpu):
     f = {n: W.to_f64(t, heads) for n, t in inp_cpu.items()}
     print(f"[bench] cpu baseline: oracle on {nheads} heads x T={w.T}, {threads} threads", file=sys.stderr,
           flush=True)
+    args = (f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"])
     t0 = time.perf_counter()
-    oracle.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], nthreads=threads)
-    oracle.backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], f["do"], f["dhT"], nthreads=threads)
+    if w.kla:   # Kaczmarz step: beta carries eta
+        oracle.kaczmarz_forward(*args, eps=w.kaczmarz_eps, nthreads=threads)
+        oracle.kaczmarz_backward(*args, f["do"], f["dhT"], eps=w.kaczmarz_eps, nthreads=threads)
+    else:
+        oracle.forward(*args, nthreads=threads)
+        oracle.backward(*args, f["do"], f["dhT"], nthreads=threads)
     dt = time.perf_counter() - t0
     tok = nheads * w.T / w.H  # tokens of all heads: the sample covers nheads/H batch rows
     return {"value": round(tok / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",

@@ -25,6 +25,7 @@ DN_OK, DN_ERR_INVALID, DN_ERR_SHAPE, DN_ERR_DTYPE, DN_ERR_WORKSPACE, DN_ERR_UNSU
 DN_F32, DN_BF16 = 0, 1
 DN_GATE_NONE, DN_GATE_SCALAR, DN_GATE_VECTOR = 0, 1, 2
 DN_PASS_FWD, DN_PASS_BWD, DN_PASS_BWD_RECOMPUTE = 0, 1, 2
+DN_FLAG_KACZMARZ = 1
 
 EXPORTS = ("dn_states_bytes", "dn_states_layout", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
            "dn_chunk_bwd", "dn_recurrent_fwd", "dn_status_string", "dn_last_error", "dn_profile_enable",
@@ -40,7 +41,8 @@ class DnError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("C", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("gate", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("gate", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("eps", ctypes.c_float)]
 
 
 _lib = None
@@ -97,11 +99,13 @@ def _check(status: int):
         raise DnError(status, f"{L.dn_status_string(status).decode()}: {L.dn_last_error().decode()}")
 
 
-def make_shape(B, H, T, dk, dv, C, dtype, gate) -> Shape:
+def make_shape(B, H, T, dk, dv, C, dtype, gate, kaczmarz_eps=None) -> Shape:
+    """``kaczmarz_eps`` not None sets DN_FLAG_KACZMARZ with that eps (beta then carries eta)."""
     dt = {torch.float32: DN_F32, torch.bfloat16: DN_BF16, "fp32": DN_F32, "bf16": DN_BF16}.get(dtype, dtype)
     gt = {None: DN_GATE_NONE, "none": DN_GATE_NONE, "scalar": DN_GATE_SCALAR,
           "vector": DN_GATE_VECTOR}.get(gate, gate)
-    return Shape(int(B), int(H), int(T), int(dk), int(dv), int(C), int(dt), int(gt))
+    flags, eps = (0, 0.0) if kaczmarz_eps is None else (DN_FLAG_KACZMARZ, float(kaczmarz_eps))
+    return Shape(int(B), int(H), int(T), int(dk), int(dv), int(C), int(dt), int(gt), flags, eps)
 
 
 def _stream(stream):
@@ -120,9 +124,9 @@ def dn_states_bytes(shape: Shape) -> int:
 
 
 def dn_states_layout(shape: Shape):
-    out = (ctypes.c_size_t * 5)()
+    out = (ctypes.c_size_t * 6)()
     _check(lib().dn_states_layout(ctypes.byref(shape), out))
-    return dict(zip(("states", "T", "P", "gam", "total"), list(out)))
+    return dict(zip(("states", "T", "P", "gam", "kz", "total"), list(out)))
 
 
 def dn_workspace_bytes(shape: Shape, pass_: int) -> int:
@@ -130,9 +134,9 @@ def dn_workspace_bytes(shape: Shape, pass_: int) -> int:
 
 
 def dn_workspace_layout(shape: Shape, pass_: int):
-    out = (ctypes.c_size_t * 7)()
+    out = (ctypes.c_size_t * 8)()
     _check(lib().dn_workspace_layout(ctypes.byref(shape), int(pass_), out))
-    return dict(zip(("gam", "T", "P", "lam", "dS1", "states", "total"), list(out)))
+    return dict(zip(("gam", "T", "P", "lam", "dS1", "states", "kz", "total"), list(out)))
 
 
 def dn_status_string(status: int) -> str:
@@ -198,9 +202,9 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
-def shape_of(q, v, g, C) -> Shape:
+def shape_of(q, v, g, C, kaczmarz_eps=None) -> Shape:
     B, H, T, dk = q.shape
-    return make_shape(B, H, T, dk, v.shape[-1], C, q.dtype, _gate_kind(g, dk))
+    return make_shape(B, H, T, dk, v.shape[-1], C, q.dtype, _gate_kind(g, dk), kaczmarz_eps)
 
 
 def workspace(shape: Shape, pass_: int, device) -> torch.Tensor:
@@ -215,7 +219,8 @@ def saved_buffer(shape: Shape, device) -> torch.Tensor:
 
 def saved_regions(buf: torch.Tensor, shape: Shape) -> dict:
     """Views of a saved buffer: states [B,H,NT,dv,dk], T and P [B,H,NT,C,C] (io
-    type), gam like g (fp32; None without a gate)."""
+    type), gam like g (fp32; None without a gate), and with the Kaczmarz flag
+    kz_beta and kz_rn [B,H,T] (fp32; else None)."""
     lay = dn_states_layout(shape)
     io = torch.bfloat16 if shape.dtype == DN_BF16 else torch.float32
     E = 2 if shape.dtype == DN_BF16 else 4
@@ -230,18 +235,22 @@ def saved_regions(buf: torch.Tensor, shape: Shape) -> dict:
 
     out = {"states": view(lay["states"], (B, H, NT, dv, dk), io, E),
            "T": view(lay["T"], (B, H, NT, C, C), io, E),
-           "P": view(lay["P"], (B, H, NT, C, C), io, E), "gam": None}
+           "P": view(lay["P"], (B, H, NT, C, C), io, E), "gam": None, "kz_beta": None, "kz_rn": None}
     if shape.gate != DN_GATE_NONE:
         gw = (dk,) if shape.gate == DN_GATE_VECTOR else ()
         out["gam"] = view(lay["gam"], (B, H, T) + gw, torch.float32, 4)
+    if shape.flags & DN_FLAG_KACZMARZ:
+        out["kz_beta"] = view(lay["kz"], (B, H, T), torch.float32, 4)
+        out["kz_rn"] = view(lay["kz"] + B * H * T * 4, (B, H, T), torch.float32, 4)
     return out
 
 
 def chunk_fwd(q, k, v, beta, g=None, h0=None, C=64, save_states=True, want_hT=True, ws=None,
-              stream=None):
-    """Returns (o, hT or None, saved buffer or None); saved_regions() views the buffer."""
+              stream=None, kaczmarz_eps=None):
+    """Returns (o, hT or None, saved buffer or None); saved_regions() views the buffer.
+    With ``kaczmarz_eps`` set, ``beta`` is eta (Kaczmarz step)."""
     _contig(q, k, v, beta, g, h0)
-    sh = shape_of(q, v, g, C)
+    sh = shape_of(q, v, g, C, kaczmarz_eps)
     o = torch.empty_like(v)
     hT = torch.empty(q.shape[0], q.shape[1], v.shape[-1], q.shape[-1], dtype=torch.float32,
                      device=q.device) if want_hT else None
@@ -253,10 +262,11 @@ def chunk_fwd(q, k, v, beta, g=None, h0=None, C=64, save_states=True, want_hT=Tr
 
 
 def chunk_bwd(q, k, v, beta, g, h0, do, dhT=None, states=None, C=64, want_dh0=True, ws=None,
-              stream=None):
-    """Returns dict dq, dk, dv, dbeta, dg (None without a gate), dh0 (or None)."""
+              stream=None, kaczmarz_eps=None):
+    """Returns dict dq, dk, dv, dbeta, dg (None without a gate), dh0 (or None).  With
+    ``kaczmarz_eps`` set, ``beta`` is eta and "dbeta" holds d eta."""
     _contig(q, k, v, beta, g, h0, do, dhT, states)
-    sh = shape_of(q, v, g, C)
+    sh = shape_of(q, v, g, C, kaczmarz_eps)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -271,24 +281,27 @@ def chunk_bwd(q, k, v, beta, g, h0, do, dhT=None, states=None, C=64, want_dh0=Tr
     return {"dq": dq, "dk": dk, "dv": dv, "dbeta": dbeta, "dg": dg, "dh0": dh0}
 
 
-def recurrent_fwd(q, k, v, beta, g, state, stream=None):
+def recurrent_fwd(q, k, v, beta, g, state, stream=None, kaczmarz_eps=None):
     """T recurrent steps (decode); `state` (fp32 [B,H,dv,dk]) is updated in place.
-    Returns o."""
+    Returns o.  With ``kaczmarz_eps`` set, ``beta`` is eta."""
     _contig(q, k, v, beta, g, state)
     B, H, T, dk = q.shape
-    sh = make_shape(B, H, T, dk, v.shape[-1], 64, q.dtype, _gate_kind(g, dk))
+    sh = make_shape(B, H, T, dk, v.shape[-1], 64, q.dtype, _gate_kind(g, dk), kaczmarz_eps)
     o = torch.empty_like(v)
     _check(dn_recurrent_fwd(sh, q, k, v, beta, g, state, o, stream))
     return o
 
 
 class DeltaRule(torch.autograd.Function):
-    """o, hT = DeltaRule.apply(q, k, v, beta, g, h0, C, recompute)."""
+    """o, hT = DeltaRule.apply(q, k, v, beta, g, h0, C, recompute, kaczmarz_eps); with
+    kaczmarz_eps set, the fourth argument is eta."""
 
     @staticmethod
-    def forward(ctx, q, k, v, beta, g, h0, C=64, recompute=False):
-        o, hT, states = chunk_fwd(q, k, v, beta, g, h0, C=C, save_states=not recompute)
+    def forward(ctx, q, k, v, beta, g, h0, C=64, recompute=False, kaczmarz_eps=None):
+        o, hT, states = chunk_fwd(q, k, v, beta, g, h0, C=C, save_states=not recompute,
+                                  kaczmarz_eps=kaczmarz_eps)
         ctx.C = C
+        ctx.kz = kaczmarz_eps
         ctx.save_for_backward(q, k, v, beta, g, h0, states)
         return o, hT
 
@@ -296,5 +309,6 @@ class DeltaRule(torch.autograd.Function):
     def backward(ctx, do, dhT):
         q, k, v, beta, g, h0, states = ctx.saved_tensors
         gr = chunk_bwd(q, k, v, beta, g, h0, do.contiguous(),
-                       None if dhT is None else dhT.contiguous(), states, C=ctx.C)
-        return gr["dq"], gr["dk"], gr["dv"], gr["dbeta"], gr["dg"], (gr["dh0"] if h0 is not None else None), None, None
+                       None if dhT is None else dhT.contiguous(), states, C=ctx.C, kaczmarz_eps=ctx.kz)
+        return (gr["dq"], gr["dk"], gr["dv"], gr["dbeta"], gr["dg"], (gr["dh0"] if h0 is not None else None),
+                None, None, None)

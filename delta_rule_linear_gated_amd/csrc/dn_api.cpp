@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -25,6 +26,19 @@ dn_status fail(dn_status st, const char* fmt, ...) {
     return st;
 }
 
+#define DN_TRY(expr)                      \
+    do {                                  \
+        const dn_status st_ = (expr);     \
+        if (st_ != DN_OK) return st_;     \
+    } while (0)
+
+dn_status check_flags(const dn_shape* s) {
+    if (s->flags & ~DN_FLAG_KACZMARZ) return fail(DN_ERR_INVALID, "unknown flags 0x%x", s->flags);
+    if ((s->flags & DN_FLAG_KACZMARZ) && !(std::isfinite(s->eps) && s->eps >= 0.f))
+        return fail(DN_ERR_INVALID, "Kaczmarz eps must be finite and >= 0");
+    return DN_OK;
+}
+
 struct Dims {
     size_t BH, T, NT, dk, dv, E, gw;
 };
@@ -36,6 +50,7 @@ dn_status check_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
     if (s->C <= 0) return fail(DN_ERR_SHAPE, "chunk size C must be > 0");
     if (s->dtype != DN_F32 && s->dtype != DN_BF16) return fail(DN_ERR_DTYPE, "unknown dtype %d", s->dtype);
     if (s->gate < DN_GATE_NONE || s->gate > DN_GATE_VECTOR) return fail(DN_ERR_INVALID, "unknown gate %d", s->gate);
+    DN_TRY(check_flags(s));
     if ((long long)s->B * s->H > 65535) return fail(DN_ERR_UNSUPPORTED, "B*H must be <= 65535");
     if (s->C != 16 && s->C != 32 && s->C != 64) return fail(DN_ERR_UNSUPPORTED, "C must be 16, 32 or 64");
     if (s->dk != s->dv) return fail(DN_ERR_UNSUPPORTED, "dk must equal dv");
@@ -49,6 +64,7 @@ dn_status check_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
     pr->C = s->C;
     pr->bf16 = s->dtype == DN_BF16;
     pr->gate = s->gate;
+    pr->kz = (s->flags & DN_FLAG_KACZMARZ) ? 1 : 0;
     if (!dn::supported(*pr))
         return fail(DN_ERR_UNSUPPORTED, "no kernel for dtype=%s gate=%d C=%d d=%d (LDS budget)",
                     pr->bf16 ? "bf16" : "fp32", s->gate, s->C, s->dk);
@@ -91,16 +107,21 @@ dn_status check_buffers(const std::vector<Buf>& bufs) {
     return DN_OK;
 }
 
+// Kaczmarz flag: the caller's beta argument is eta; prep writes beta_t and
+// 1 / (||k_t||^2 + eps) to `region` and every later kernel reads beta there.
+void set_kaczmarz(dn::Params* p, char* region, const Dims& d, float eps) {
+    p->eta = p->beta;
+    p->kb = reinterpret_cast<float*>(region);
+    p->krn = p->kb + d.BH * d.T;
+    p->beta = p->kb;
+    p->eps = eps;
+    p->kz = 1;
+}
+
 dn_status need(const void* p, size_t bytes, const char* name) {
     if (bytes > 0 && !p) return fail(DN_ERR_INVALID, "%s is NULL", name);
     return DN_OK;
 }
-
-#define DN_TRY(expr)                      \
-    do {                                  \
-        const dn_status st_ = (expr);     \
-        if (st_ != DN_OK) return st_;     \
-    } while (0)
 
 }  // namespace
 
@@ -113,7 +134,7 @@ size_t dn_states_bytes(const dn_shape* shape) {
     return dn::saved_layout(pr).total;
 }
 
-dn_status dn_states_layout(const dn_shape* shape, size_t offsets[5]) {
+dn_status dn_states_layout(const dn_shape* shape, size_t offsets[6]) {
     dn::Problem pr;
     Dims d;
     if (!offsets) return fail(DN_ERR_INVALID, "offsets is NULL");
@@ -123,7 +144,8 @@ dn_status dn_states_layout(const dn_shape* shape, size_t offsets[5]) {
     offsets[1] = l.Tm;
     offsets[2] = l.Pm;
     offsets[3] = l.gam;
-    offsets[4] = l.total;
+    offsets[4] = l.kz;
+    offsets[5] = l.total;
     return DN_OK;
 }
 
@@ -135,7 +157,7 @@ size_t dn_workspace_bytes(const dn_shape* shape, int pass) {
     return dn::ws_layout(pr, pass).total;
 }
 
-dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[7]) {
+dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[8]) {
     dn::Problem pr;
     Dims d;
     if (!offsets) return fail(DN_ERR_INVALID, "offsets is NULL");
@@ -148,7 +170,8 @@ dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[7]
     offsets[3] = w.lam;
     offsets[4] = w.dS1;
     offsets[5] = w.states;
-    offsets[6] = w.total;
+    offsets[6] = w.kz;
+    offsets[7] = w.total;
     return DN_OK;
 }
 
@@ -205,6 +228,7 @@ dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, cons
     p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(wb + (states ? sl.gam : w.gam));
     p.Tm = wb + (states ? sl.Tm : w.Tm);
     p.Pm = wb + (states ? sl.Pm : w.Pm);
+    if (pr.kz) set_kaczmarz(&p, wb + (states ? sl.kz : w.kz), d, shape->eps);
     const hipError_t e = dn::launch_forward(pr, p, states != nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;
@@ -285,11 +309,13 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
         p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(sb + sl.gam);
         p.Tm = sb + sl.Tm;
         p.Pm = sb + sl.Pm;
+        if (pr.kz) set_kaczmarz(&p, sb + sl.kz, d, shape->eps);
     } else {             // recomputed into the workspace
         p.states = wb + w.states;
         p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(wb + w.gam);
         p.Tm = wb + w.Tm;
         p.Pm = wb + w.Pm;
+        if (pr.kz) set_kaczmarz(&p, wb + w.kz, d, shape->eps);
     }
     const hipError_t e = dn::launch_backward(pr, p, have_states, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
@@ -304,6 +330,7 @@ dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, 
     if (s->B < 0 || s->H < 0 || s->T < 0) return fail(DN_ERR_SHAPE, "B, H, T must be >= 0");
     if (s->dtype != DN_F32 && s->dtype != DN_BF16) return fail(DN_ERR_DTYPE, "unknown dtype %d", s->dtype);
     if (s->gate < DN_GATE_NONE || s->gate > DN_GATE_VECTOR) return fail(DN_ERR_INVALID, "unknown gate %d", s->gate);
+    DN_TRY(check_flags(s));
     if (s->dk != 16 && s->dk != 32 && s->dk != 64 && s->dk != 128)
         return fail(DN_ERR_UNSUPPORTED, "dk must be 16, 32, 64 or 128");
     if (s->dv <= 0 || s->dv % 16 != 0) return fail(DN_ERR_UNSUPPORTED, "dv must be a positive multiple of 16");
@@ -336,6 +363,7 @@ dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, 
     pr.C = s->C;
     pr.bf16 = s->dtype == DN_BF16;
     pr.gate = s->gate;
+    pr.kz = (s->flags & DN_FLAG_KACZMARZ) ? 1 : 0;
     dn::Params p{};
     p.BH = (int)BH;
     p.T = s->T;
@@ -348,6 +376,11 @@ dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, 
     p.g = g;
     p.hT = state;
     p.o = o;
+    if (pr.kz) {   // the step size is formed per step in the kernel
+        p.eta = beta;
+        p.eps = s->eps;
+        p.kz = 1;
+    }
     const hipError_t e = dn::launch_recurrent(pr, p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;

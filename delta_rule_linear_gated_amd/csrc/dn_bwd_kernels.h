@@ -258,7 +258,8 @@ struct BwdChunkSmem {
     static constexpr size_t RED_C = RED_B + al((VB / 16) * C * 4);                // [C/16][D] column partials
     static constexpr size_t LASTS = RED_C + al((C / 16) * D * 4);                 // [D]
     static constexpr size_t PART = LASTS + al(D * 4);                             // [D/64 rounded up]
-    static constexpr size_t TOTAL = PART + 256;
+    static constexpr size_t KCO = PART + 256;                                     // [C] Kaczmarz dk coefficients
+    static constexpr size_t TOTAL = KCO + al(C * 4);
     // dq / dk write-back tiles [C][LD] each at offset 0; d gam of the vector gate
     // [C][D] fp32 after them, written once every phase-C tile is dead
     static constexpr size_t DGB = al(2 * C * LD * E);
@@ -295,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     float* red_c = reinterpret_cast<float*>(smem + L::RED_C);
     float* lastS = reinterpret_cast<float*>(smem + L::LASTS);
     float* dgb = reinterpret_cast<float*>(smem + L::DGB);
+    float* kco = reinterpret_cast<float*>(smem + L::KCO);
 
     const int n = blockIdx.x, bh = blockIdx.y;
     const int t0 = n * C;
@@ -555,17 +557,21 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         }
 
         // -------- finish: dq, dk = dk+ + dk-, dbeta, d gam = q.dq + k.(dk+ - dk-)
+        // (Kaczmarz step: dk also gets -2 dbeta_t beta_t k_t / (||k_t||^2 + eps), once
+        // dbeta_t is reduced, and dbeta becomes d eta = dbeta / (||k_t||^2 + eps))
         __syncthreads();   // phase-C tiles dead: dq / dk go through LDS for coalesced stores
         TI* dqs = reinterpret_cast<TI*>(smem);
         TI* dks = dqs + C * LD;
         float* lsred = reinterpret_cast<float*>(smem + L::LSRED);
-        f32x4 dgm[TO::PER];
+        const bool kz = p.kz != 0;
+        f32x4 dgm[TO::PER], dkt[TO::PER];
         if (TO::active()) {
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j) {
                 const int off = TO::col(j) * LD + TO::row(j, 0);
+                dkt[j] = dkp[j] + dkm[j];
                 st4<TI>(dqs + off, dq[j]);
-                st4<TI>(dks + off, dkp[j] + dkm[j]);
+                if (!kz) st4<TI>(dks + off, dkt[j]);
                 dgm[j] = qv[j] * dq[j] + kv[j] * (dkp[j] - dkm[j]);
             }
             // row partials over c (4 per lane, 4 lane groups, RM tiles) of K+ Y (dbeta)
@@ -614,14 +620,30 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             }
         }
         __syncthreads();
-        lds_to_global<TI, C, D>(static_cast<TI*>(p.dq) + row0 * D, D, dqs, LD, valid);
-        lds_to_global<TI, C, D>(static_cast<TI*>(p.dk) + row0 * D, D, dks, LD, valid);
         for (int t = threadIdx.x; t < valid; t += kThreads) {
             float s2 = 0.f;
             for (int b = 0; b < VB / 16; ++b) s2 += red_b[b * C + t];
             for (int b = 0; b < TO::WM; ++b) s2 += red_r[b * C + t];
+            if (kz) {
+                const float rn = p.krn[row0 + t];
+                kco[t] = -2.f * s2 * beta_s[t] * rn;
+                s2 *= rn;
+            }
             p.dbeta[row0 + t] = s2;
         }
+        if (kz) {
+            __syncthreads();
+            if (TO::active()) {
+#pragma unroll
+                for (int j = 0; j < TO::PER; ++j) {
+                    const int t = TO::col(j);
+                    st4<TI>(dks + t * LD + TO::row(j, 0), dkt[j] + (t < valid ? kco[t] : 0.f) * kv[j]);
+                }
+            }
+            __syncthreads();
+        }
+        lds_to_global<TI, C, D>(static_cast<TI*>(p.dq) + row0 * D, D, dqs, LD, valid);
+        lds_to_global<TI, C, D>(static_cast<TI*>(p.dk) + row0 * D, D, dks, LD, valid);
         if constexpr (GATE != kGateNone) {
             // gam_C terms: lastS[c] = sum_v S0 dS1 and the Kd dKd column sums; for the
             // scalar gate their total over c, one partial per wave

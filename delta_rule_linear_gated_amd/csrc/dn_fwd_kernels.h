@@ -217,7 +217,35 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
             }
         }
     }
-    for (int t = threadIdx.x; t < C; t += kThreads) beta_s[t] = beta[t < valid ? t : valid - 1] * (t < valid ? 1.f : 0.f);
+    if (p.kz) {
+        // Kaczmarz step (KLA abstract): beta_t = eta_t / (||k_t||^2 + eps) from the
+        // key rows in registers; a row's vectors sit in one aligned group of VPR lanes
+        using RK = RegN<TI, C, DK>;
+#pragma unroll
+        for (int i = 0; i < RK::PER; ++i) {
+            const uint4 ri = rk.r[i];
+            const TI* src = reinterpret_cast<const TI*>(&ri);
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < RK::VW; ++e) {
+                const float x = to_f(src[e]);
+                ss += x * x;
+            }
+            ss = group_sum<RK::VPR>(ss);
+            const int idx = threadIdx.x + i * kThreads, row = idx / RK::VPR;
+            if (idx < RK::NV && idx % RK::VPR == 0) {
+                const float rn = 1.f / (ss + p.eps);
+                const float b = row < valid ? p.eta[row0 + row] * rn : 0.f;
+                beta_s[row] = b;
+                if (row < valid) {
+                    p.kb[row0 + row] = b;
+                    p.krn[row0 + row] = rn;
+                }
+            }
+        }
+    } else {
+        for (int t = threadIdx.x; t < C; t += kThreads) beta_s[t] = beta[t < valid ? t : valid - 1] * (t < valid ? 1.f : 0.f);
+    }
     __syncthreads();
 
     // -- stage K and Q (centred per-channel factors for the vector gate)

@@ -22,6 +22,8 @@ enum Gate { kGateNone = 0, kGateScalar = 1, kGateVector = 2 };
 //   gam   fp32 in-chunk cumulative log-decay, same layout as g
 //   Tm    [BH][NT][C][C]   (I + A)^{-1} of each chunk
 //   Pm    [BH][NT][C][C]   causal intra-chunk score matrix of each chunk
+//   kb    [BH][T] fp32     Kaczmarz step beta_t = eta_t / (||k_t||^2 + eps)
+//   krn   [BH][T] fp32     1 / (||k_t||^2 + eps)   (both only with the flag)
 // workspace of the backward:
 //   lam   [BH][NT][C][DV]  triangular-residual adjoint
 //   dS1   [BH][NT][DV][DK] state cotangent leaving each chunk
@@ -31,7 +33,8 @@ struct Params {
     const void* k;
     const void* v;
     const void* dout;
-    const float* beta;
+    const float* beta;   // beta_t as the kernels use it (kb with the Kaczmarz flag)
+    const float* eta;    // Kaczmarz flag: the caller's eta (read by prep and the recurrent kernel)
     const float* g;
     const float* h0;
     const float* dhT;
@@ -49,25 +52,31 @@ struct Params {
     void* Pm;
     void* lam;
     void* dS1;
+    float* kb;    // Kaczmarz flag: written by prep, read through `beta` afterwards
+    float* krn;
+    float eps;
+    int kz;       // 1: Kaczmarz step (beta from eta and the keys)
 };
 
 struct Problem {
     int B, H, T, dk, dv, C;
     int bf16;   // 1: bf16 I/O, 0: fp32 I/O
     int gate;   // Gate
+    int kz;     // Kaczmarz step flag
 };
 
 // Workspace carving per pass (0 forward, 1 backward with saved data, 2 backward
 // recomputing it).  Offsets in bytes from the workspace base; every region
 // starts on a 256-byte boundary; regions a pass does not use have size 0.
 struct WsLayout {
-    size_t gam, Tm, Pm, lam, dS1, states, total;
+    size_t gam, Tm, Pm, lam, dS1, states, kz, total;
 };
 WsLayout ws_layout(const Problem& pr, int pass);
 
-// The forward's saved buffer: chunk-entry states, T, P, gam (same alignment).
+// The forward's saved buffer: chunk-entry states, T, P, gam, Kaczmarz data
+// (kb then krn) (same alignment).
 struct SavedLayout {
-    size_t states, Tm, Pm, gam, total;
+    size_t states, Tm, Pm, gam, kz, total;
 };
 SavedLayout saved_layout(const Problem& pr);
 

@@ -33,7 +33,7 @@ bool supported(const Problem& pr) {
 
 namespace {
 struct Sizes {
-    size_t gam, cc, lam, st;
+    size_t gam, cc, lam, st, kz;
 };
 Sizes sizes(const Problem& pr) {
     const size_t E = pr.bf16 ? 2 : 4;
@@ -45,6 +45,7 @@ Sizes sizes(const Problem& pr) {
     z.cc = al256(BH * NT * pr.C * pr.C * E);
     z.lam = al256(BH * NT * pr.C * pr.dv * E);
     z.st = al256(BH * NT * (size_t)pr.dv * pr.dk * E);
+    z.kz = pr.kz ? al256(2 * BH * pr.T * 4) : 0;
     return z;
 }
 }  // namespace
@@ -66,6 +67,8 @@ WsLayout ws_layout(const Problem& pr, int pass) {
     if (pass != 0) off += z.st;
     w.states = off;
     if (pass == 2) off += z.st;
+    w.kz = off;
+    if (chunk_data) off += z.kz;
     w.total = off;
     return w;
 }
@@ -77,7 +80,8 @@ SavedLayout saved_layout(const Problem& pr) {
     l.Tm = z.st;
     l.Pm = l.Tm + z.cc;
     l.gam = l.Pm + z.cc;
-    l.total = l.gam + z.gam;
+    l.kz = l.gam + z.gam;
+    l.total = l.kz + z.kz;
     return l;
 }
 

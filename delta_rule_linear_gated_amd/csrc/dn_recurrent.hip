@@ -32,7 +32,7 @@ template <typename TI, int GATE, int DK> struct StepIn {
             q[e] = to_f(qp[e]);
         }
         v = to_f(static_cast<const TI*>(p.v)[tok * p.DVr + v_row]);
-        beta = p.beta[tok];
+        beta = p.kz ? p.eta[tok] : p.beta[tok];
         if (GATE == kGateScalar) a[0] = p.g[tok];
         if (GATE == kGateVector) {
 #pragma unroll
@@ -82,7 +82,14 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < E; ++e) pk += s[e] * cur.k[e];
         pk = row16_sum(pk);
-        const float u = cur.beta * (cur.v - pk);
+        float beta = cur.beta;
+        if (p.kz) {   // Kaczmarz step (KLA abstract): beta_t = eta_t / (||k_t||^2 + eps)
+            float kk = 0.f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) kk += cur.k[e] * cur.k[e];
+            beta /= row16_sum(kk) + p.eps;
+        }
+        const float u = beta * (cur.v - pk);
         float oq = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {

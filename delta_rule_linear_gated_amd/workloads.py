@@ -14,9 +14,9 @@ Distributions (per head, per step):
   h0    = h0_std * N(0, 1)  (None when h0_std == 0)  fp32 [B,H,dv,dk]
   dO    ~ N(0, 1) in the I/O dtype; dhT ~ N(0, 1) fp32
 The long-context workload uses the Kaczmarz step of the KLA abstract: keys are
-left unnormalised and beta = eta / (||k~||^2 + 1e-6) with eta = sigmoid(N(0, 1))
-and k~ the rounded key (computed in fp64, rounded to fp32) -- an input-side
-preprocessing, the operator itself is unchanged.
+left unnormalised and the step input is eta = sigmoid(N(0, 1)) (fp32, returned
+under "beta"), which the operator turns into beta_t = eta_t / (||k_t||^2 + eps)
+with eps = ``Workload.kaczmarz_eps`` (1e-6 unless a custom workload sets it).
 
 Rounding: fp64 -> fp32 (round to nearest), then fp32 -> bf16 (round to nearest
 even) for bf16 workloads.
@@ -47,6 +47,12 @@ class Workload:
     kla: bool = False
     policy: str = "save"          # "save": forward keeps per-chunk states; "recompute"
     seed: int = 1
+    kz_eps: float = 1e-6          # eps of the Kaczmarz step (kla workloads)
+
+    @property
+    def kaczmarz_eps(self):
+        """eps of the Kaczmarz step (its "beta" input is then eta), else None."""
+        return self.kz_eps if self.kla else None
 
     @property
     def token_heads(self) -> int:
@@ -105,7 +111,8 @@ def make_inputs(w: Workload, seed: int | None = None, cotangents: bool = True,
                 device: str | torch.device = "cpu") -> dict:
     """Draw one batch of inputs for workload ``w``.
 
-    Returns a dict of torch tensors (on ``device``): q, k, v (I/O dtype), beta,
+    Returns a dict of torch tensors (on ``device``): q, k, v (I/O dtype), beta
+    (eta when ``w.kaczmarz_eps`` is set),
     g (None / [B,H,T] / [B,H,T,dk]), h0 (None or [B,H,dv,dk]) in fp32, and, when
     ``cotangents``, do (I/O dtype) and dhT (fp32).  Every tensor has its own
     random stream, so a workload is reproducible tensor by tensor."""
@@ -121,14 +128,8 @@ def make_inputs(w: Workload, seed: int | None = None, cotangents: bool = True,
     out["k"] = _round(k, w.dtype)
     del k
     out["v"] = _round(_rng(s, 2).standard_normal((B, H, T, dv)), w.dtype)
-    if w.kla:
-        eta = _sigmoid(_rng(s, 3).standard_normal((B, H, T)))
-        kr = out["k"].to(torch.float64).numpy()
-        beta = eta / (np.sum(kr * kr, axis=-1) + 1e-6)
-        del kr
-    else:
-        beta = _sigmoid(_rng(s, 3).standard_normal((B, H, T)))
-    out["beta"] = _round(beta, "fp32")
+    # beta, or eta for the Kaczmarz step (same distribution)
+    out["beta"] = _round(_sigmoid(_rng(s, 3).standard_normal((B, H, T))), "fp32")
     if w.gate == "none":
         out["g"] = None
     elif w.gate == "scalar":
@@ -150,9 +151,9 @@ def make_inputs(w: Workload, seed: int | None = None, cotangents: bool = True,
 
 
 def custom(B, H, T, dk, dv, C, gate="scalar", dtype="bf16", h0_std=0.0, kla=False,
-           policy="save", seed=7, name="custom") -> Workload:
+           policy="save", seed=7, name="custom", kz_eps=1e-6) -> Workload:
     """A workload of any shape, with the same distributions."""
-    return Workload(name, B, H, T, dk, dv, C, gate, dtype, h0_std, kla, policy, seed)
+    return Workload(name, B, H, T, dk, dv, C, gate, dtype, h0_std, kla, policy, seed, kz_eps)
 
 
 def to_f64(t, heads=None) -> np.ndarray | None:

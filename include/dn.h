@@ -20,7 +20,8 @@
  *     in WY form and the exact affine chunk transfer used by the forward.
  *   - KLA abstract (thelatestinai): GDN as gated decay plus delta-rule residual
  *     write; the Kaczmarz step beta_t = eta_t / (||k_t||^2 + eps) changes only
- *     the beta input, so callers compute it before calling.
+ *     the step size.  Callers either pass beta themselves or set
+ *     DN_FLAG_KACZMARZ and pass eta in its place (see dn_shape).
  *   - Fast Weight Attention abstract (papers.fzhiy.net): read-after-write output,
  *     o_t reads the state after step t's write.
  * There is no query scale.
@@ -54,6 +55,8 @@
  *                          io   [B][H][NT][C][C]    causal intra-chunk scores
  *                          fp32 like g              in-chunk cumulative log-decay
  *                                                   (absent without a gate)
+ *                          fp32 [2][B][H][T]        DN_FLAG_KACZMARZ only: beta_t,
+ *                                                   then 1 / (||k_t||^2 + eps)
  * The saved quantities are kept in the types the kernels use them in (the state
  * and the per-chunk matrices are matrix-core operands in the io type), so the
  * backward reads exactly the operand values the forward used; the running
@@ -91,24 +94,40 @@ typedef enum {
 } dn_pass;
 
 /*
+ * Kaczmarz step size (KLA abstract): with this flag the `beta` argument of every
+ * entry point carries eta [B][H][T] fp32 and the operator uses
+ *     beta_t = eta_t / (||k_t||^2 + eps)
+ * with ||k_t||^2 summed in fp32 over the keys as given (io type).  The backward
+ * then writes d eta (= d beta / (||k_t||^2 + eps)) to `dbeta`, and dk includes
+ * the path through the step size, -2 (d beta_t) beta_t k_t / (||k_t||^2 + eps).
+ * A zero key with eps == 0 gives Inf / NaN like any other division by zero.
+ */
+#define DN_FLAG_KACZMARZ 1u
+
+/*
  * Problem shape.  Supported: B, H, T >= 0 with B*H <= 65535; dk == dv in
  * {16, 32, 64, 128} (fp32: dk <= 64); C in {16, 32, 64}; any T (a last,
  * shorter chunk is handled exactly); fp32 with a vector gate needs C <= 32 at
- * dk = 64.  Anything else returns DN_ERR_UNSUPPORTED.
+ * dk = 64.  flags: 0 or DN_FLAG_KACZMARZ (other bits: DN_ERR_INVALID); eps:
+ * read only with DN_FLAG_KACZMARZ, finite and >= 0.  Anything else returns
+ * DN_ERR_UNSUPPORTED.
  */
 typedef struct {
     int32_t B, H, T, dk, dv, C;
-    int32_t dtype;  /* dn_dtype */
-    int32_t gate;   /* dn_gate  */
+    int32_t dtype;   /* dn_dtype */
+    int32_t gate;    /* dn_gate  */
+    uint32_t flags;  /* DN_FLAG_* */
+    float eps;       /* Kaczmarz denominator offset */
 } dn_shape;
 
-/* Bytes of the saved buffer `states` for this shape (the four regions listed
- * under Layouts, each rounded up to 256 bytes).  0 on bad shape. */
+/* Bytes of the saved buffer `states` for this shape (the regions listed under
+ * Layouts, each rounded up to 256 bytes).  0 on bad shape. */
 size_t dn_states_bytes(const dn_shape* shape);
 
 /* Byte offsets of the regions of `states`: {chunk-entry states, (I + A)^{-1},
- * intra-chunk scores, cumulative log-decay, total}.  DN_OK or a shape error. */
-dn_status dn_states_layout(const dn_shape* shape, size_t offsets[5]);
+ * intra-chunk scores, cumulative log-decay, Kaczmarz step data, total}; an
+ * absent region has zero size.  DN_OK or a shape error. */
+dn_status dn_states_layout(const dn_shape* shape, size_t offsets[6]);
 
 /* Workspace bytes the given pass needs (0 on bad shape).  Workspace contents
  * are scratch: nothing is carried from one call to the next. */
@@ -118,8 +137,8 @@ size_t dn_workspace_bytes(const dn_shape* shape, int pass);
  * Forward pass (chunkwise: per-chunk WY/UT construction with a unit-lower-
  * triangular solve, the inter-chunk state recurrence, the causal intra-chunk
  * output -- ReWY abstract; SFDA summary, chunk-WY theorem and affine transfer).
- *   inputs : q, k, v, beta; g (must be NULL iff gate == DN_GATE_NONE);
- *            h0 (NULL = zero initial state)
+ *   inputs : q, k, v, beta (eta with DN_FLAG_KACZMARZ); g (must be NULL iff
+ *            gate == DN_GATE_NONE); h0 (NULL = zero initial state)
  *   outputs: o; hT (NULL = not wanted); states (dn_states_bytes(shape) bytes:
  *            what the backward reuses; NULL = not saved, i.e. the
  *            recomputation policy: dn_chunk_bwd is then called with
@@ -136,8 +155,9 @@ dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, cons
  *   inputs : q, k, v, beta, g, h0 as given to dn_chunk_fwd; dout; dhT (NULL =
  *            zero); states as written by dn_chunk_fwd (the backward then skips
  *            the per-chunk preparation), or NULL to recompute everything here
- *   outputs: dq, dk, dv, dbeta; dg (must be NULL iff gate == DN_GATE_NONE;
- *            same layout as g); dh0 (NULL = not wanted)
+ *   outputs: dq, dk, dv, dbeta (d eta with DN_FLAG_KACZMARZ); dg (must be
+ *            NULL iff gate == DN_GATE_NONE; same layout as g); dh0 (NULL = not
+ *            wanted)
  *   ws     : >= dn_workspace_bytes(shape, states ? DN_PASS_BWD : DN_PASS_BWD_RECOMPUTE)
  */
 dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, const void* v,
@@ -153,8 +173,9 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
  * updated in place.  Same per-step arithmetic as the chunkwise forward.
  *   shape  : B, H, T (steps; 0 is a no-op), dk in {16, 32, 64, 128}, dv a
  *            positive multiple of 16 (may differ from dk), dtype, gate; C unused
- *   inputs : q, k [B][H][T][dk], v [B][H][T][dv] (io); beta [B][H][T] fp32; g as
- *            for dn_chunk_fwd (NULL iff gate == DN_GATE_NONE)
+ *   inputs : q, k [B][H][T][dk], v [B][H][T][dv] (io); beta [B][H][T] fp32 (eta
+ *            with DN_FLAG_KACZMARZ); g as for dn_chunk_fwd (NULL iff gate ==
+ *            DN_GATE_NONE)
  *   state  : fp32 [B][H][dv][dk]: the state before step 1 on entry, after step T
  *            on return (in place; it may not overlap any other argument)
  *   outputs: o [B][H][T][dv] (io)
@@ -173,12 +194,12 @@ const char* dn_last_error(void);
  * Diagnostics: byte offsets of the workspace regions a pass uses, in the order
  * {cumulative log-decay, (I+A)^{-1} per chunk, intra-chunk scores per chunk,
  * triangular-residual adjoint, state cotangent per chunk, recomputed states,
- * total}; a region the pass does not use has zero size (the next offset is
- * equal).  DN_PASS_FWD places the first three there only when the forward
- * saves nothing; DN_PASS_BWD takes them from the saved buffer.  Returns DN_OK
- * or an error for a bad shape / pass.
+ * Kaczmarz step data (as in the saved buffer), total}; a region the pass does
+ * not use has zero size (the next offset is equal).  DN_PASS_FWD places the
+ * per-chunk data there only when the forward saves nothing; DN_PASS_BWD takes
+ * it from the saved buffer.  Returns DN_OK or an error for a bad shape / pass.
  */
-dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[7]);
+dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[8]);
 
 /*
  * Diagnostics: per-kernel timing.  dn_profile_enable(1) makes every later

@@ -35,27 +35,37 @@ def rel_err(x, ref):
 
 
 def gpu_run(w: W.Workload, inp: dict, policy: str | None = None, dhT=True):
-    """fwd + bwd on the GPU through the C ABI.  Returns a dict of CPU tensors."""
+    """fwd + bwd on the GPU through the C ABI (with the Kaczmarz flag when the
+    workload has one: inp["beta"] is then eta).  Returns a dict of CPU tensors."""
     policy = policy or w.policy
+    kz = w.kaczmarz_eps
     d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
     o, hT, states = B.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], C=w.C,
-                                save_states=(policy == "save"))
+                                save_states=(policy == "save"), kaczmarz_eps=kz)
     gr = B.chunk_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["h0"], d["do"],
-                     d["dhT"] if dhT else None, states, C=w.C)
+                     d["dhT"] if dhT else None, states, C=w.C, kaczmarz_eps=kz)
     torch.cuda.synchronize()
     out = {"o": o, "hT": hT, **gr}
     if states is not None:   # the saved buffer's regions (not its alignment gaps)
-        sv = B.saved_regions(states, B.shape_of(d["q"], d["v"], d["g"], w.C))
-        out.update({"states": sv["states"], "saved_T": sv["T"], "saved_P": sv["P"], "saved_gam": sv["gam"]})
+        sv = B.saved_regions(states, B.shape_of(d["q"], d["v"], d["g"], w.C, kz))
+        out.update({"states": sv["states"], "saved_T": sv["T"], "saved_P": sv["P"], "saved_gam": sv["gam"],
+                    "saved_kz_beta": sv["kz_beta"], "saved_kz_rn": sv["kz_rn"]})
     return {n: (None if t is None else t.cpu()) for n, t in out.items()}
 
 
-def oracle_run(inp: dict, heads=None, dhT=True):
-    """fp64 oracle on the same rounded inputs (optionally only some (b, h) heads)."""
+def oracle_run(inp: dict, heads=None, dhT=True, kaczmarz_eps=None):
+    """fp64 oracle on the same rounded inputs (optionally only some (b, h) heads).
+    With ``kaczmarz_eps``, inp["beta"] is eta and "dbeta" holds d eta."""
     f = {n: W.to_f64(t, heads) for n, t in inp.items()}
-    o, hT = oracle.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], nthreads=nthreads())
-    gr = oracle.backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], f["do"],
-                         f["dhT"] if dhT else None, nthreads=nthreads())
+    args = (f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"])
+    dh = f["dhT"] if dhT else None
+    if kaczmarz_eps is None:
+        o, hT = oracle.forward(*args, nthreads=nthreads())
+        gr = oracle.backward(*args, f["do"], dh, nthreads=nthreads())
+    else:
+        o, hT = oracle.kaczmarz_forward(*args, eps=kaczmarz_eps, nthreads=nthreads())
+        gr = oracle.kaczmarz_backward(*args, f["do"], dh, eps=kaczmarz_eps, nthreads=nthreads())
+        gr["dbeta"] = gr.pop("deta")
     return {"o": o, "hT": hT, **gr}
 
 

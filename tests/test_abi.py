@@ -36,7 +36,7 @@ def test_status_strings():
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
 def test_sizes_of_the_workloads(name):
     w = W.CONFIGS[name]
-    sh = B.make_shape(w.B, w.H, w.T, w.dk, w.dv, w.C, w.dtype, w.gate)
+    sh = B.make_shape(w.B, w.H, w.T, w.dk, w.dv, w.C, w.dtype, w.gate, w.kaczmarz_eps)
     E = 2 if w.dtype == "bf16" else 4
     NT = -(-w.T // w.C)
     gw = 0 if w.gate == "none" else (w.dk if w.gate == "vector" else 1)
@@ -46,7 +46,9 @@ def test_sizes_of_the_workloads(name):
     assert sl["states"] == 0
     assert sl["T"] == al(w.B * w.H * NT * w.dv * w.dk * E)
     assert sl["P"] - sl["T"] == sl["gam"] - sl["P"] == al(w.B * w.H * NT * w.C * w.C * E)
-    assert sl["total"] - sl["gam"] == al(w.B * w.H * w.T * gw * 4)
+    assert sl["kz"] - sl["gam"] == al(w.B * w.H * w.T * gw * 4)
+    # Kaczmarz step: beta and 1 / (||k||^2 + eps) per token (fp32)
+    assert sl["total"] - sl["kz"] == (al(2 * w.B * w.H * w.T * 4) if w.kla else 0)
     assert B.dn_states_bytes(sh) == sl["total"]
     f = B.dn_workspace_bytes(sh, B.DN_PASS_FWD)
     b = B.dn_workspace_bytes(sh, B.DN_PASS_BWD)
@@ -54,13 +56,13 @@ def test_sizes_of_the_workloads(name):
     assert 0 < f and 0 < b < r
     lay = B.dn_workspace_layout(sh, B.DN_PASS_BWD_RECOMPUTE)
     assert lay["total"] == r
-    offs = [lay[k] for k in ("gam", "T", "P", "lam", "dS1", "states", "total")]
+    offs = [lay[k] for k in ("gam", "T", "P", "lam", "dS1", "states", "kz", "total")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     # the recomputing backward holds in its workspace what the saved buffer carries
     assert r - b == B.dn_states_bytes(sh)
     # with a saved buffer the backward's workspace holds only lambda and dS1
     lb = B.dn_workspace_layout(sh, B.DN_PASS_BWD)
-    assert lb["gam"] == lb["T"] == lb["P"] == lb["lam"] == 0 and lb["states"] == lb["total"] == b
+    assert lb["gam"] == lb["T"] == lb["P"] == lb["lam"] == 0 and lb["states"] == lb["kz"] == lb["total"] == b
     # the forward's workspace holds gam, T, P (used when it saves nothing)
     assert f == sl["total"] - sl["T"]
 
@@ -125,6 +127,24 @@ def test_validation_errors_backward():
     assert bwd(sh_of(), dk=FAKE * 9) == B.DN_ERR_INVALID               # dk aliases dq
     assert bwd(sh_of(), dq=FAKE) == B.DN_ERR_INVALID                   # dq aliases q
     assert bwd(sh_of(T=-5)) == B.DN_ERR_SHAPE
+
+
+def test_validation_errors_kaczmarz():
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert fwd(sh_of(kaczmarz_eps=eps)) == B.DN_ERR_INVALID and "eps" in B.dn_last_error()
+        assert bwd(sh_of(kaczmarz_eps=eps)) == B.DN_ERR_INVALID
+        assert rec(sh_of(kaczmarz_eps=eps)) == B.DN_ERR_INVALID
+    sh = sh_of()
+    sh.flags = 2
+    assert fwd(sh) == B.DN_ERR_INVALID and "flags" in B.dn_last_error()
+    assert B.dn_states_bytes(sh) == 0
+    # eps is ignored without the flag; with it the saved buffer gains the step data
+    sh = sh_of()
+    sh.eps = float("nan")
+    assert B.dn_states_bytes(sh) == B.dn_states_bytes(sh_of()) > 0
+    kz = sh_of(kaczmarz_eps=0.0)
+    assert B.dn_states_bytes(kz) - B.dn_states_bytes(sh_of()) == 512   # 2 x 64 fp32
+    assert B.dn_workspace_bytes(kz, B.DN_PASS_BWD) == B.dn_workspace_bytes(sh_of(), B.DN_PASS_BWD)
 
 
 def test_workspace_grows_with_recompute():

@@ -24,7 +24,7 @@ def test_workload_full_size(name):
     say(f"[parity] {w.describe()}")
     inp = W.make_inputs(w)
     gpu = gpu_run(w, inp)
-    ref = oracle_run(inp)
+    ref = oracle_run(inp, kaczmarz_eps=w.kaczmarz_eps)
     compare(gpu, ref, TOL[w.dtype], label=name)
 
 
