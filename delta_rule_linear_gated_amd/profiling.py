@@ -81,8 +81,25 @@ def copy_value(d):
     return best
 
 
+def timed_means(d, steps, warmup):
+    """{kernel key: mean duration (us) of its launches in the timed steps} from the
+    kernel trace: a kernel launched n times over warmup + steps steps has its last
+    n * steps / (warmup + steps) launches in the timed region (the warmup launches
+    also see the clock ramp up, so the all-launch average runs high)."""
+    acc = collections.defaultdict(list)
+    rows = sorted(_csv(_find(d, "kernel_trace.csv")), key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
+        acc[kernel_key(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = {}
+    for k, v in acc.items():
+        n = max(1, round(len(v) * steps / (steps + warmup)))
+        out[k] = sum(v[-n:]) / n
+    return out
+
+
 def summarize(args) -> str:
     stats = _csv(_find(args.trace, "kernel_stats.csv"))
+    timed = timed_means(args.trace, args.steps, args.warmup) if args.steps else {}
     fetch = counter_means(args.fetch)
     write = counter_means(args.write)
     copy_kib = args.copy_mib * 1024.0
@@ -97,6 +114,8 @@ def summarize(args) -> str:
         w = write.get(k)
         rec = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
                "share": float(r["Percentage"]) / 100.0}
+        if k in timed:
+            rec["timed_avg_us"] = timed[k]
         if f is not None and w is not None:
             rec.update(fetch_kib=f, write_kib=w,
                        bytes=int((f * fetch_scale + w * write_scale) * 1024))
@@ -107,10 +126,11 @@ def summarize(args) -> str:
     lines = [f"# {args.title}", "", "Commands (from /tmp, TMPDIR=/tmp):", ""]
     for c in args.command:
         lines.append(f"    {c}")
-    lines += ["", "| kernel | calls | avg us | share | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |",
-              "|---|---|---|---|---|---|---|"]
+    lines += ["", "| kernel | calls | avg us (all) | avg us (timed steps) | share | FETCH_SIZE KiB | WRITE_SIZE KiB "
+              "| HBM bytes (scaled) |", "|---|---|---|---|---|---|---|---|"]
     for k, r in kern.items():
-        lines.append(f"| {k} | {r['calls']} | {r['avg_us']:.1f} | {r['share']:.3f} | "
+        lines.append(f"| {k} | {r['calls']} | {r['avg_us']:.1f} | {r.get('timed_avg_us', float('nan')):.1f} | "
+                     f"{r['share']:.3f} | "
                      f"{r.get('fetch_kib', float('nan')):.0f} | {r.get('write_kib', float('nan')):.0f} | "
                      f"{r.get('bytes', 0):,} |")
     lines += ["", f"Copy calibration ({args.copy_mib} MiB read + written per copy): FETCH_SIZE scale "
@@ -141,6 +161,8 @@ def main():
     s.add_argument("--workload", required=True)
     s.add_argument("--title", required=True)
     s.add_argument("--command", action="append", default=[])
+    s.add_argument("--steps", type=int, default=0, help="timed steps of the traced bench run")
+    s.add_argument("--warmup", type=int, default=0, help="warmup steps of the traced bench run")
     s.add_argument("--out", required=True)
     sub.add_parser("digest")
     a = ap.parse_args()
