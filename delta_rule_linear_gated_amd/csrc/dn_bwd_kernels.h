@@ -414,7 +414,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         __syncthreads();
         gemm<TI, D, C, VB, true, false>(dkm, DS1B, LD, UB, LVB);
         gemm2<TI, C, C, VB, false, false>(dA, dP, UB, LVB, LAMB, DOB, LVB);
-        __syncthreads();
+        // no barrier here: the next writes into this buffer (the commit of block
+        // b + 2) and into RB come after the next block's first barrier
     }
 
     // q (and k for the vector gate) for the key-gradient products (loads in flight
@@ -441,6 +442,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     }
 
     // ---------------- phase B: dA~, beta dA~ and dP~ into LDS (element s = row, t = col)
+    __syncthreads();   // the last block's tiles, which phase B overwrites, are dead
     {
         TI* DAs = reinterpret_cast<TI*>(smem + L::DA);
         TI* DABs = reinterpret_cast<TI*>(smem + L::DAB);

@@ -390,6 +390,16 @@ template <int GATE, int C, int DK> struct GateLds {
 //   SAVE    : write the state entering each chunk (I/O type) to p.states
 //   OUTPUT  : write O and hT.  Off for the recompute pass of the backward (P is
 //             not needed there).
+// Static LDS of fwd_state_kernel (bytes), mirrored from its declarations.
+template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_state_lds() {
+    constexpr size_t E = sizeof(TI);
+    constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
+    constexpr int G = GATE == kGateVector ? C * DK : C;
+    constexpr int NK = GATE == kGateVector ? 3 : 2;   // Q, K (+ K Gam_C / Gam)
+    constexpr int NV = GATE == kGateScalar ? 3 : 2;   // V (then U), R (+ U Gam_C / Gam)
+    return 4 * (G + 3 * C) + E * (BV * LDK + NK * C * LDK + NV * C * LDV + 2 * C * LDC) + 96;
+}
+
 template <typename TI, int GATE, int C, int DK, int BV, bool SAVE, bool OUTPUT>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     constexpr int PAD = Pad<TI>::value;
@@ -412,12 +422,12 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     __shared__ __align__(16) TI Qg[C * LDK];     // Q (vector gate: Q Gam)            [t][c]
     __shared__ __align__(16) TI Kg[C * LDK];     // K (vector gate: K Gam)            [t][c]
     __shared__ __align__(16) TI Kd[VEC ? C * LDK : 8];   // K Gam_C / Gam (vector gate) [t][c]
-    __shared__ __align__(16) TI Vb[C * LDV];     // V block           [t][v]
+    __shared__ __align__(16) TI Vb[C * LDV];     // V block [t][v]; after (c) U [t][v]
     __shared__ __align__(16) TI Tl[C * LDC];     // T                 [t][s]
     __shared__ __align__(16) TI Pl[C * LDC];     // P                 [t][s]
     // R [t][v]; after (d) it holds the chunk's O [t][v] until the next iteration writes it back
     __shared__ __align__(16) TI Rb[C * LDV];
-    __shared__ __align__(16) TI Ub[C * LDV];     // U                 [t][v]
+    TI* const Ub = Vb;                           // V is dead once R is formed
     __shared__ __align__(16) TI Ud[SCA ? C * LDV : 8];   // U Gam_C / Gam (scalar gate) [t][v]
 
     const int DVr = p.DVr;

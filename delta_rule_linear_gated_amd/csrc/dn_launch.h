@@ -27,14 +27,6 @@ constexpr size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 template <typename TI, int GATE, int C, int DK> constexpr size_t prep_lds() {
     return PrepSmem<TI, GATE, C, DK>::TOTAL;
 }
-template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_state_lds() {
-    constexpr size_t E = sizeof(TI);
-    constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
-    constexpr int G = GATE == kGateVector ? C * DK : C;
-    constexpr int NK = GATE == kGateVector ? 3 : 2;   // Q, K (+ K Gam_C / Gam)
-    constexpr int NV = GATE == kGateScalar ? 4 : 3;   // V, R, U (+ U Gam_C / Gam)
-    return 4 * (G + 3 * C) + E * (BV * LDK + NK * C * LDK + NV * C * LDV + 2 * C * LDC) + 96;
-}
 template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t bwd_state_lds() {
     constexpr size_t E = sizeof(TI);
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
