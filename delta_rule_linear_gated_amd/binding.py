@@ -25,7 +25,7 @@ DN_OK, DN_ERR_INVALID, DN_ERR_SHAPE, DN_ERR_DTYPE, DN_ERR_WORKSPACE, DN_ERR_UNSU
 DN_F32, DN_BF16 = 0, 1
 DN_GATE_NONE, DN_GATE_SCALAR, DN_GATE_VECTOR = 0, 1, 2
 DN_PASS_FWD, DN_PASS_BWD, DN_PASS_BWD_RECOMPUTE = 0, 1, 2
-DN_FLAG_KACZMARZ = 1
+DN_FLAG_KACZMARZ, DN_FLAG_NO_SCAN = 1, 2
 
 EXPORTS = ("dn_states_bytes", "dn_states_layout", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
            "dn_chunk_bwd", "dn_recurrent_fwd", "dn_status_string", "dn_last_error", "dn_profile_enable",
@@ -99,12 +99,15 @@ def _check(status: int):
         raise DnError(status, f"{L.dn_status_string(status).decode()}: {L.dn_last_error().decode()}")
 
 
-def make_shape(B, H, T, dk, dv, C, dtype, gate, kaczmarz_eps=None) -> Shape:
-    """``kaczmarz_eps`` not None sets DN_FLAG_KACZMARZ with that eps (beta then carries eta)."""
+def make_shape(B, H, T, dk, dv, C, dtype, gate, kaczmarz_eps=None, no_scan=False) -> Shape:
+    """``kaczmarz_eps`` not None sets DN_FLAG_KACZMARZ with that eps (beta then carries eta);
+    ``no_scan`` sets DN_FLAG_NO_SCAN (one sequential state pass, never the chunk-parallel scan)."""
     dt = {torch.float32: DN_F32, torch.bfloat16: DN_BF16, "fp32": DN_F32, "bf16": DN_BF16}.get(dtype, dtype)
     gt = {None: DN_GATE_NONE, "none": DN_GATE_NONE, "scalar": DN_GATE_SCALAR,
           "vector": DN_GATE_VECTOR}.get(gate, gate)
     flags, eps = (0, 0.0) if kaczmarz_eps is None else (DN_FLAG_KACZMARZ, float(kaczmarz_eps))
+    if no_scan:
+        flags |= DN_FLAG_NO_SCAN
     return Shape(int(B), int(H), int(T), int(dk), int(dv), int(C), int(dt), int(gt), flags, eps)
 
 
@@ -134,9 +137,9 @@ def dn_workspace_bytes(shape: Shape, pass_: int) -> int:
 
 
 def dn_workspace_layout(shape: Shape, pass_: int):
-    out = (ctypes.c_size_t * 8)()
+    out = (ctypes.c_size_t * 10)()
     _check(lib().dn_workspace_layout(ctypes.byref(shape), int(pass_), out))
-    return dict(zip(("gam", "T", "P", "lam", "dS1", "states", "kz", "total"), list(out)))
+    return dict(zip(("gam", "T", "P", "lam", "dS1", "states", "kz", "seg_end", "seg_start", "total"), list(out)))
 
 
 def dn_status_string(status: int) -> str:
@@ -202,9 +205,9 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
-def shape_of(q, v, g, C, kaczmarz_eps=None) -> Shape:
+def shape_of(q, v, g, C, kaczmarz_eps=None, no_scan=False) -> Shape:
     B, H, T, dk = q.shape
-    return make_shape(B, H, T, dk, v.shape[-1], C, q.dtype, _gate_kind(g, dk), kaczmarz_eps)
+    return make_shape(B, H, T, dk, v.shape[-1], C, q.dtype, _gate_kind(g, dk), kaczmarz_eps, no_scan)
 
 
 def workspace(shape: Shape, pass_: int, device) -> torch.Tensor:
@@ -246,11 +249,11 @@ def saved_regions(buf: torch.Tensor, shape: Shape) -> dict:
 
 
 def chunk_fwd(q, k, v, beta, g=None, h0=None, C=64, save_states=True, want_hT=True, ws=None,
-              stream=None, kaczmarz_eps=None):
+              stream=None, kaczmarz_eps=None, no_scan=False):
     """Returns (o, hT or None, saved buffer or None); saved_regions() views the buffer.
     With ``kaczmarz_eps`` set, ``beta`` is eta (Kaczmarz step)."""
     _contig(q, k, v, beta, g, h0)
-    sh = shape_of(q, v, g, C, kaczmarz_eps)
+    sh = shape_of(q, v, g, C, kaczmarz_eps, no_scan)
     o = torch.empty_like(v)
     hT = torch.empty(q.shape[0], q.shape[1], v.shape[-1], q.shape[-1], dtype=torch.float32,
                      device=q.device) if want_hT else None
@@ -262,11 +265,11 @@ def chunk_fwd(q, k, v, beta, g=None, h0=None, C=64, save_states=True, want_hT=Tr
 
 
 def chunk_bwd(q, k, v, beta, g, h0, do, dhT=None, states=None, C=64, want_dh0=True, ws=None,
-              stream=None, kaczmarz_eps=None):
+              stream=None, kaczmarz_eps=None, no_scan=False):
     """Returns dict dq, dk, dv, dbeta, dg (None without a gate), dh0 (or None).  With
     ``kaczmarz_eps`` set, ``beta`` is eta and "dbeta" holds d eta."""
     _contig(q, k, v, beta, g, h0, do, dhT, states)
-    sh = shape_of(q, v, g, C, kaczmarz_eps)
+    sh = shape_of(q, v, g, C, kaczmarz_eps, no_scan)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)

@@ -33,7 +33,7 @@ dn_status fail(dn_status st, const char* fmt, ...) {
     } while (0)
 
 dn_status check_flags(const dn_shape* s) {
-    if (s->flags & ~DN_FLAG_KACZMARZ) return fail(DN_ERR_INVALID, "unknown flags 0x%x", s->flags);
+    if (s->flags & ~(DN_FLAG_KACZMARZ | DN_FLAG_NO_SCAN)) return fail(DN_ERR_INVALID, "unknown flags 0x%x", s->flags);
     if ((s->flags & DN_FLAG_KACZMARZ) && !(std::isfinite(s->eps) && s->eps >= 0.f))
         return fail(DN_ERR_INVALID, "Kaczmarz eps must be finite and >= 0");
     return DN_OK;
@@ -65,6 +65,7 @@ dn_status check_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
     pr->bf16 = s->dtype == DN_BF16;
     pr->gate = s->gate;
     pr->kz = (s->flags & DN_FLAG_KACZMARZ) ? 1 : 0;
+    pr->no_scan = (s->flags & DN_FLAG_NO_SCAN) ? 1 : 0;
     if (!dn::supported(*pr))
         return fail(DN_ERR_UNSUPPORTED, "no kernel for dtype=%s gate=%d C=%d d=%d (LDS budget)",
                     pr->bf16 ? "bf16" : "fp32", s->gate, s->C, s->dk);
@@ -118,6 +119,15 @@ void set_kaczmarz(dn::Params* p, char* region, const Dims& d, float eps) {
     p->kz = 1;
 }
 
+// The scan plan and its buffers (in the workspace; unused when nseg == 1).
+void set_scan(dn::Params* p, const dn::Problem& pr, char* ws, const dn::WsLayout& w) {
+    const dn::ScanPlan sp = dn::scan_plan(pr);
+    p->nseg = sp.nseg;
+    p->seg_len = sp.seg_len;
+    p->seg_end = reinterpret_cast<float*>(ws + w.seg_end);
+    p->seg_start = reinterpret_cast<float*>(ws + w.seg_start);
+}
+
 dn_status need(const void* p, size_t bytes, const char* name) {
     if (bytes > 0 && !p) return fail(DN_ERR_INVALID, "%s is NULL", name);
     return DN_OK;
@@ -157,7 +167,7 @@ size_t dn_workspace_bytes(const dn_shape* shape, int pass) {
     return dn::ws_layout(pr, pass).total;
 }
 
-dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[8]) {
+dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[10]) {
     dn::Problem pr;
     Dims d;
     if (!offsets) return fail(DN_ERR_INVALID, "offsets is NULL");
@@ -171,7 +181,9 @@ dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[8]
     offsets[4] = w.dS1;
     offsets[5] = w.states;
     offsets[6] = w.kz;
-    offsets[7] = w.total;
+    offsets[7] = w.seg_end;
+    offsets[8] = w.seg_start;
+    offsets[9] = w.total;
     return DN_OK;
 }
 
@@ -229,6 +241,7 @@ dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, cons
     p.Tm = wb + (states ? sl.Tm : w.Tm);
     p.Pm = wb + (states ? sl.Pm : w.Pm);
     if (pr.kz) set_kaczmarz(&p, wb + (states ? sl.kz : w.kz), d, shape->eps);
+    set_scan(&p, pr, static_cast<char*>(ws), w);
     const hipError_t e = dn::launch_forward(pr, p, states != nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;
@@ -317,6 +330,7 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
         p.Pm = wb + w.Pm;
         if (pr.kz) set_kaczmarz(&p, wb + w.kz, d, shape->eps);
     }
+    set_scan(&p, pr, wb, w);
     const hipError_t e = dn::launch_backward(pr, p, have_states, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;

@@ -33,12 +33,20 @@
 namespace dn {
 
 // ---------------------------------------------------------------------------
-// bwd_state_kernel: grid (DV / BV, BH), chunks walked from last to first; the
-// global tiles of chunk n - 1 are loaded into registers while chunk n is
-// computed.  Every tile is kept in its natural layout (T and P as saved, row
-// major); operands contracted over their leading index are read with the
-// transposing LDS load.
-template <typename TI, int GATE, int C, int DK, int BV>
+// bwd_state_kernel: grid (rows / BV) * nseg * BH, the chunks of one segment
+// walked from last to first; the global tiles of chunk n - 1 are loaded into
+// registers while chunk n is computed.  Every tile is kept in its natural
+// layout (T and P as saved, row major); operands contracted over their leading
+// index are read with the transposing LDS load.
+//   SUMMARY: segment summary of the chunk-parallel scan, the mirror image of the
+//            forward's: dS through the segment from zero (the last segment from
+//            dhT), plus DK rows that start as the identity and see dO = 0 and end
+//            as the transpose of the segment's transition matrix
+//            (dS_start = dS_end P_s^T + dS_start|zero end); end states to
+//            p.seg_end, nothing else written.
+// Otherwise, with segments, a segment starts from the dS the combine left in
+// p.seg_start (the last from dhT) and writes lambda, dv and dS1 of its chunks.
+template <typename TI, int GATE, int C, int DK, int BV, bool SUMMARY = false>
 __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     constexpr int PAD = Pad<TI>::value;
     constexpr int LDK = DK + PAD;
@@ -70,17 +78,31 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     __shared__ __align__(16) TI Dn[VEC ? 8 : C * LDV];
 
     const int DVr = p.DVr;
-    int bh, vblk;
-    head_and_block(DVr / BV, p.BH, bh, vblk);
+    const int rows = DVr + (SUMMARY ? DK : 0);
+    const int nblk = rows / BV;
+    int bh, sb;
+    head_and_block(nblk * p.nseg, p.BH, bh, sb);
+    const int seg = sb / nblk, vblk = sb - seg * nblk;
     const int v0 = vblk * BV;
+    const bool trans = SUMMARY && v0 >= DVr;   // rows of the transposed transition
+    if (trans && (seg == 0 || seg == p.nseg - 1)) return;
+    const int n0 = seg * p.seg_len, n1 = min(p.NT, n0 + p.seg_len);
+    const bool last = seg == p.nseg - 1;
     // dS held transposed, dS^T [c][v] tiles (4 consecutive keys of one row v per lane)
     using TS = Tiles<DK, BV>;
     f32x4 dS[TS::PER];
+    const float* init = last ? (trans ? nullptr : (p.dhT ? p.dhT + (long)bh * DVr * DK : nullptr))
+                             : (SUMMARY ? nullptr : p.seg_start + ((long)bh * p.nseg + seg) * DVr * DK);
 #pragma unroll
     for (int j = 0; j < TS::PER; ++j) {
         dS[j] = zero4();
-        if (p.dhT && TS::active()) dS[j] = ld4<float>(p.dhT + ((long)bh * DVr + v0 + TS::col(j)) * DK + TS::row(j, 0));
+        if (init && TS::active()) dS[j] = ld4<float>(init + (long)(v0 + TS::col(j)) * DK + TS::row(j, 0));
+        if (trans && TS::active()) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dS[j][i] = TS::row(j, i) == v0 - DVr + TS::col(j) ? 1.f : 0.f;
+        }
     }
+    const int vcol = trans ? 0 : v0;   // (transition rows load a valid dO block and zero it)
 
     RegN<TI, C, DK> rq, rk;
     RegN<TI, C, BV> rdo;
@@ -95,15 +117,16 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         __builtin_amdgcn_sched_barrier(0);   // gate first, then the tiles, in order (see RegN)
         rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
         rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
-        rdo.load(static_cast<const TI*>(p.dout) + row0 * DVr + v0, DVr, valid);
+        rdo.load(static_cast<const TI*>(p.dout) + row0 * DVr + vcol, DVr, valid);
+        if (trans) rdo.valid_ = 0;   // stores as zero
         rP.load(static_cast<const TI*>(p.Pm) + cc, C, C);
         rT.load(static_cast<const TI*>(p.Tm) + cc, C, C);
     };
-    prefetch(p.NT - 1);
+    prefetch(n1 - 1);
 
     using TX = Tiles<C, BV>;    // dU  [t][v]
     using TL = Tiles<BV, C>;    // lambda^T [v][t]
-    for (int n = p.NT - 1; n >= 0; --n) {
+    for (int n = n1 - 1; n >= n0; --n) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
         // (a) dS1 of this chunk: operand copy (written to the workspace from LDS below)
@@ -128,17 +151,18 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         rP.store(Pl, LDC);
         rT.store(Tl, LDC);
         // lambda and dv of the chunk done last iteration (in Lb / Db until (d) below)
-        if (n + 1 < p.NT) {
+        if (!SUMMARY && n + 1 < n1) {
             const long rp = (long)bh * p.T + (n + 1) * C;
             lds_to_global<TI, C, BV>(static_cast<TI*>(p.lam) + ((long)bh * p.NT + n + 1) * C * DVr + v0, DVr, Lb,
                                      LDV, C);
             lds_to_global<TI, C, BV>(static_cast<TI*>(p.dv) + rp * DVr + v0, DVr, Db, LDV, min(C, p.T - (n + 1) * C));
         }
         __syncthreads();
-        lds_to_global<TI, BV, DK>(static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, dSs, LDK,
-                                  BV);
+        if (!SUMMARY)
+            lds_to_global<TI, BV, DK>(static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, dSs,
+                                      LDK, BV);
         // the next chunk's loads last and unconditional (see the forward state kernel)
-        prefetch(n > 0 ? n - 1 : 0);
+        prefetch(n > n0 ? n - 1 : n0);
 
         // (c) dU = P^T dO + Kd dS1^T  -> dU^T   (P and dO read as [k][m] / [k][n])
         {
@@ -188,14 +212,20 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         gemm<TI, DK, BV, C, true, true>(dS, VEC ? Kn : Kd, LDK, VEC ? Db : Dn, LDV);
         __syncthreads();
     }
-    if (p.NT > 0) {   // lambda and dv of chunk 0
-        lds_to_global<TI, C, BV>(static_cast<TI*>(p.lam) + (long)bh * p.NT * C * DVr + v0, DVr, Lb, LDV, C);
-        lds_to_global<TI, C, BV>(static_cast<TI*>(p.dv) + (long)bh * p.T * DVr + v0, DVr, Db, LDV, min(C, p.T));
+    if (!SUMMARY && n1 > n0) {   // lambda and dv of the segment's first chunk
+        lds_to_global<TI, C, BV>(static_cast<TI*>(p.lam) + ((long)bh * p.NT + n0) * C * DVr + v0, DVr, Lb, LDV, C);
+        lds_to_global<TI, C, BV>(static_cast<TI*>(p.dv) + ((long)bh * p.T + n0 * C) * DVr + v0, DVr, Db, LDV,
+                                 min(C, p.T - n0 * C));
     }
-    if (p.dh0 && TS::active()) {
+    if (!SUMMARY && seg == 0 && p.dh0 && TS::active()) {
 #pragma unroll
         for (int j = 0; j < TS::PER; ++j)
             st4<float>(p.dh0 + ((long)bh * DVr + v0 + TS::col(j)) * DK + TS::row(j, 0), dS[j]);
+    }
+    if (SUMMARY && TS::active()) {
+        float* out = p.seg_end + ((long)bh * p.nseg + seg) * rows * DK;
+#pragma unroll
+        for (int j = 0; j < TS::PER; ++j) st4<float>(out + (long)(v0 + TS::col(j)) * DK + TS::row(j, 0), dS[j]);
     }
 }
 

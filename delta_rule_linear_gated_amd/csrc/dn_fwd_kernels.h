@@ -383,13 +383,22 @@ template <int GATE, int C, int DK> struct GateLds {
 };
 
 // ---------------------------------------------------------------------------
-// fwd_state_kernel: grid (DV / BV, BH).  Walks the chunks of one head in order
-// for one block of BV state rows (rows of S are independent: each row only
-// mixes with itself through the key dimension).  The global tiles of chunk
-// n + 1 are loaded into registers while chunk n is computed.
+// fwd_state_kernel: grid (rows / BV) * nseg * BH.  Walks the chunks of one
+// segment of one head in order for one block of BV state rows (rows of S are
+// independent: each row only mixes with itself through the key dimension).  The
+// global tiles of chunk n + 1 are loaded into registers while chunk n is
+// computed.
 //   SAVE    : write the state entering each chunk (I/O type) to p.states
 //   OUTPUT  : write O and hT.  Off for the recompute pass of the backward (P is
 //             not needed there).
+//   neither : segment summary of the chunk-parallel scan (exact affine chunk
+//             transfer, SFDA summary): the segment's rows of S from a zero state
+//             (the first segment from h0), plus DK rows that start as the
+//             identity and see V = 0, so that they end as the segment's
+//             transition matrix P_s (S_end = S_start P_s + S_end|zero start);
+//             the end states go to p.seg_end.
+// With segments (p.nseg > 1) and SAVE or OUTPUT, a segment starts from the
+// boundary state the combine left in p.seg_start (the first from h0).
 // Static LDS of fwd_state_kernel (bytes), mirrored from its declarations.
 template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_state_lds() {
     constexpr size_t E = sizeof(TI);
@@ -430,19 +439,34 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     TI* const Ub = Vb;                           // V is dead once R is formed
     __shared__ __align__(16) TI Ud[SCA ? C * LDV : 8];   // U Gam_C / Gam (scalar gate) [t][v]
 
+    constexpr bool SUMMARY = !SAVE && !OUTPUT;
     const int DVr = p.DVr;
-    int bh, vblk;
-    head_and_block(DVr / BV, p.BH, bh, vblk);
+    const int rows = DVr + (SUMMARY ? DK : 0);
+    const int nblk = rows / BV;
+    int bh, sb;
+    head_and_block(nblk * p.nseg, p.BH, bh, sb);
+    const int seg = sb / nblk, vblk = sb - seg * nblk;
     const int v0 = vblk * BV;
+    const bool trans = SUMMARY && v0 >= DVr;   // rows of the transition matrix
+    // only the inner segments' transitions enter the combine
+    if (trans && (seg == 0 || seg == p.nseg - 1)) return;
+    const int n0 = seg * p.seg_len, n1 = min(p.NT, n0 + p.seg_len);
     // the state is held transposed, S^T [c][v] tiles: a lane's 4 values are 4
     // consecutive keys c of one row v of S (one vector store into S0's [v][c] copy)
     using TS = Tiles<DK, BV>;
     f32x4 S[TS::PER];
+    const float* init = seg == 0 ? (trans ? nullptr : (p.h0 ? p.h0 + (long)bh * DVr * DK : nullptr))
+                                 : (SUMMARY ? nullptr : p.seg_start + ((long)bh * p.nseg + seg) * DVr * DK);
 #pragma unroll
     for (int j = 0; j < TS::PER; ++j) {
         S[j] = zero4();
-        if (p.h0 && TS::active()) S[j] = ld4<float>(p.h0 + ((long)bh * DVr + v0 + TS::col(j)) * DK + TS::row(j, 0));
+        if (init && TS::active()) S[j] = ld4<float>(init + (long)(v0 + TS::col(j)) * DK + TS::row(j, 0));
+        if (trans && TS::active()) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[j][i] = TS::row(j, i) == v0 - DVr + TS::col(j) ? 1.f : 0.f;
+        }
     }
+    const int vcol = trans ? 0 : v0;   // (transition rows load a valid V block and zero it)
 
     // registers of the next chunk
     RegN<TI, C, DK> rq, rk;
@@ -459,16 +483,17 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         __builtin_amdgcn_sched_barrier(0);   // gate first, then the tiles, in order (see RegN)
         rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
         rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
-        rv.load(static_cast<const TI*>(p.v) + row0 * DVr + v0, DVr, valid);
+        rv.load(static_cast<const TI*>(p.v) + row0 * DVr + vcol, DVr, valid);
+        if (trans) rv.valid_ = 0;   // stores as zero
         rT.load(static_cast<const TI*>(p.Tm) + cc, C, C);
         if constexpr (OUTPUT) rP.load(static_cast<const TI*>(p.Pm) + cc, C, C);
     };
-    prefetch(0);
+    prefetch(n0);
 
     // X^T, U^T and O^T tiles [v][t]: a lane holds 4 consecutive v of one row t of
     // R, U and O (one vector LDS access each)
     using TX = Tiles<BV, C>;
-    for (int n = 0; n < p.NT; ++n) {
+    for (int n = n0; n < n1; ++n) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
         const long row0 = (long)bh * p.T + t0;
@@ -493,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         rT.store(Tl, LDC);
         if constexpr (OUTPUT) rP.store(Pl, LDC);
         // the previous chunk's O (in Rb until (c) below overwrites it)
-        if (OUTPUT && n > 0)
+        if (OUTPUT && n > n0)
             lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + (row0 - C) * DVr + v0, DVr, Rb, LDV, C);
         __syncthreads();
         if (SAVE)
@@ -504,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         // head are merged over the first entry (the loads alone) and the back edge,
         // and only with the loads last on both do they stay exact instead of waiting
         // for every outstanding load and store.
-        prefetch(n + 1 < p.NT ? n + 1 : n);
+        prefetch(n + 1 < n1 ? n + 1 : n);
 
         // (c) X^T = S0 (K Gam)^T ;  R = diag(beta) (V - X)
         {
@@ -564,15 +589,20 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         gemm<TI, DK, BV, C, true, true>(S, VEC ? Kd : Kg, LDK, SCA ? Ud : Ub, LDV);
         __syncthreads();
     }
-    if (OUTPUT && p.NT > 0) {
-        const int t0 = (p.NT - 1) * C;
+    if (OUTPUT && n1 > n0) {
+        const int t0 = (n1 - 1) * C;
         lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + ((long)bh * p.T + t0) * DVr + v0, DVr, Rb, LDV,
                                  min(C, p.T - t0));
     }
-    if (OUTPUT && p.hT && TS::active()) {
+    if (OUTPUT && p.hT && n1 == p.NT && TS::active()) {
 #pragma unroll
         for (int j = 0; j < TS::PER; ++j)
             st4<float>(p.hT + ((long)bh * DVr + v0 + TS::col(j)) * DK + TS::row(j, 0), S[j]);
+    }
+    if (SUMMARY && TS::active()) {
+        float* out = p.seg_end + ((long)bh * p.nseg + seg) * rows * DK;
+#pragma unroll
+        for (int j = 0; j < TS::PER; ++j) st4<float>(out + (long)(v0 + TS::col(j)) * DK + TS::row(j, 0), S[j]);
     }
 }
 

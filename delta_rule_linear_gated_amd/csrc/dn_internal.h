@@ -56,6 +56,16 @@ struct Params {
     float* krn;
     float eps;
     int kz;       // 1: Kaczmarz step (beta from eta and the keys)
+    // chunk-parallel scan of the state passes (nseg == 1: one sequential pass).
+    // Segment s covers chunks [s * seg_len, min(NT, (s + 1) * seg_len)).
+    //   seg_end   [BH][nseg][DVr + DKr][DKr] fp32: each segment's state pass from a
+    //             zero state (rows < DVr) and from the identity with zero V / dO
+    //             (rows >= DVr: the segment's transition matrix)
+    //   seg_start [BH][nseg][DVr][DKr] fp32: the true state entering each segment
+    //             (forward) or leaving it (backward), from the combine
+    int nseg, seg_len;
+    float* seg_end;
+    float* seg_start;
 };
 
 struct Problem {
@@ -63,13 +73,23 @@ struct Problem {
     int bf16;   // 1: bf16 I/O, 0: fp32 I/O
     int gate;   // Gate
     int kz;     // Kaczmarz step flag
+    int no_scan;   // force one sequential state pass
 };
+
+// Segments of the chunk-parallel state scan for this problem: 1 (a plain
+// sequential pass) unless the sequential kernels would leave most compute units
+// idle (few heads); then about enough segments to fill the device, each of at
+// least two chunks.  seg_len = chunks per segment.
+struct ScanPlan {
+    int nseg, seg_len;
+};
+ScanPlan scan_plan(const Problem& pr);
 
 // Workspace carving per pass (0 forward, 1 backward with saved data, 2 backward
 // recomputing it).  Offsets in bytes from the workspace base; every region
 // starts on a 256-byte boundary; regions a pass does not use have size 0.
 struct WsLayout {
-    size_t gam, Tm, Pm, lam, dS1, states, kz, total;
+    size_t gam, Tm, Pm, lam, dS1, states, kz, seg_end, seg_start, total;
 };
 WsLayout ws_layout(const Problem& pr, int pass);
 
@@ -83,6 +103,9 @@ SavedLayout saved_layout(const Problem& pr);
 // Kernel launch sequences (all enqueue on `stream`, none synchronises).
 hipError_t launch_forward(const Problem& pr, const Params& p, bool save_states, hipStream_t stream);
 hipError_t launch_backward(const Problem& pr, const Params& p, bool have_states, hipStream_t stream);
+// Combine of the chunk-parallel state scan (p.nseg > 1): p.seg_end -> p.seg_start,
+// segments walked first to last (forward) or last to first (backward).
+hipError_t launch_scan_combine(const Params& p, int DK, bool forward, hipStream_t stream);
 // Recurrent form: T steps per head, state p.hT (fp32, in place), outputs p.o.
 hipError_t launch_recurrent(const Problem& pr, const Params& p, hipStream_t stream);
 bool supported(const Problem& pr);

@@ -85,39 +85,67 @@ template <typename TI, int GATE, int C, int D> int state_block(int BH) {
 
 // OUTPUT is a template argument so that the forward and the backward units each
 // instantiate only the variants they launch.
+// Sequential state kernels: MODE 0 = the pass itself (forward: OUTPUT selects
+// O / hT, `save` the chunk states; with segments each segment starts from the
+// combine's boundary state), MODE 1 = segment summaries of the scan (DK more
+// rows, the transition matrix).  The grid covers every (row block, segment,
+// head); the d_v block is chosen for BH * nseg heads' worth of chains.
 template <typename TI, int GATE, int C, int D, int BV, bool OUTPUT>
-void launch_fwd_state(const Params& p, int BH, bool save, hipStream_t stream) {
-    const dim3 grid((D / BV) * BH), block(kThreads);
-    if (!OUTPUT || save)
+void launch_fwd_state(const Params& p, int BH, bool save, int mode, hipStream_t stream) {
+    const int rows = D + (mode ? D : 0);
+    const dim3 grid((rows / BV) * BH * p.nseg), block(kThreads);
+    if (mode)
+        hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, false>), grid, block, 0, stream, p);
+    else if (!OUTPUT || save)
         hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, true, OUTPUT>), grid, block, 0, stream, p);
     else
         hipLaunchKernelGGL((fwd_state_kernel<TI, GATE, C, D, BV, false, true>), grid, block, 0, stream, p);
 }
 
 template <typename TI, int GATE, int C, int D, bool OUTPUT>
-void fwd_state(const Params& p, int BH, bool save, hipStream_t stream) {
-    const int bv = state_block<TI, GATE, C, D>(BH);
+void fwd_state(const Params& p, int BH, bool save, int mode, hipStream_t stream) {
+    const int bv = state_block<TI, GATE, C, D>(BH * p.nseg);
     if constexpr (state_fits<TI, GATE, C, D, 64>())
-        if (bv == 64) return launch_fwd_state<TI, GATE, C, D, 64, OUTPUT>(p, BH, save, stream);
+        if (bv == 64) return launch_fwd_state<TI, GATE, C, D, 64, OUTPUT>(p, BH, save, mode, stream);
     if constexpr (state_fits<TI, GATE, C, D, 32>())
-        if (bv == 32) return launch_fwd_state<TI, GATE, C, D, 32, OUTPUT>(p, BH, save, stream);
+        if (bv == 32) return launch_fwd_state<TI, GATE, C, D, 32, OUTPUT>(p, BH, save, mode, stream);
     if constexpr (state_fits<TI, GATE, C, D, 16>())
-        launch_fwd_state<TI, GATE, C, D, 16, OUTPUT>(p, BH, save, stream);
+        launch_fwd_state<TI, GATE, C, D, 16, OUTPUT>(p, BH, save, mode, stream);
 }
 
-template <typename TI, int GATE, int C, int D, int BV> void launch_bwd_state(const Params& p, int BH, hipStream_t stream) {
-    hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV>), dim3((D / BV) * BH), dim3(kThreads), 0, stream, p);
+template <typename TI, int GATE, int C, int D, int BV>
+void launch_bwd_state(const Params& p, int BH, int mode, hipStream_t stream) {
+    const int rows = D + (mode ? D : 0);
+    const dim3 grid((rows / BV) * BH * p.nseg), block(kThreads);
+    if (mode)
+        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_state_kernel<TI, GATE, C, D, BV, false>), grid, block, 0, stream, p);
 }
 
 template <typename TI, int GATE, int C, int D>
-void bwd_state(const Params& p, int BH, hipStream_t stream) {
-    const int bv = state_block<TI, GATE, C, D>(BH);
+void bwd_state(const Params& p, int BH, int mode, hipStream_t stream) {
+    const int bv = state_block<TI, GATE, C, D>(BH * p.nseg);
     if constexpr (state_fits<TI, GATE, C, D, 64>())
-        if (bv == 64) return launch_bwd_state<TI, GATE, C, D, 64>(p, BH, stream);
+        if (bv == 64) return launch_bwd_state<TI, GATE, C, D, 64>(p, BH, mode, stream);
     if constexpr (state_fits<TI, GATE, C, D, 32>())
-        if (bv == 32) return launch_bwd_state<TI, GATE, C, D, 32>(p, BH, stream);
+        if (bv == 32) return launch_bwd_state<TI, GATE, C, D, 32>(p, BH, mode, stream);
     if constexpr (state_fits<TI, GATE, C, D, 16>())
-        launch_bwd_state<TI, GATE, C, D, 16>(p, BH, stream);
+        launch_bwd_state<TI, GATE, C, D, 16>(p, BH, mode, stream);
+}
+
+// The forward state pass, through the scan when the plan has segments.
+template <typename TI, int GATE, int C, int D, bool OUTPUT>
+void fwd_state_pass(const Params& p, int BH, bool save, const char* name, const char* sname, hipStream_t stream) {
+    if (p.nseg > 1) {
+        prof_begin(stream, sname);
+        fwd_state<TI, GATE, C, D, OUTPUT>(p, BH, false, 1, stream);
+        prof_end(stream);
+        launch_scan_combine(p, D, true, stream);
+    }
+    prof_begin(stream, name);
+    fwd_state<TI, GATE, C, D, OUTPUT>(p, BH, save, 0, stream);
+    prof_end(stream);
 }
 
 template <typename TI, int GATE, int C, int D>
@@ -129,9 +157,7 @@ hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t s
         prof_begin(stream, "prep");
         hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
         prof_end(stream);
-        prof_begin(stream, "fwd_state");
-        fwd_state<TI, GATE, C, D, true>(p, BH, save, stream);
-        prof_end(stream);
+        fwd_state_pass<TI, GATE, C, D, true>(p, BH, save, "fwd_state", "fwd_summary", stream);
         return hipGetLastError();
     }
 }
@@ -146,12 +172,16 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
             prof_begin(stream, "prep_recompute");
             hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
             prof_end(stream);
-            prof_begin(stream, "fwd_state_recompute");
-            fwd_state<TI, GATE, C, D, false>(p, BH, true, stream);
+            fwd_state_pass<TI, GATE, C, D, false>(p, BH, true, "fwd_state_recompute", "fwd_summary_recompute", stream);
+        }
+        if (p.nseg > 1) {   // the reverse scan: segment summaries of dS, then the combine
+            prof_begin(stream, "bwd_summary");
+            bwd_state<TI, GATE, C, D>(p, BH, 1, stream);
             prof_end(stream);
+            launch_scan_combine(p, D, false, stream);
         }
         prof_begin(stream, "bwd_state");
-        bwd_state<TI, GATE, C, D>(p, BH, stream);
+        bwd_state<TI, GATE, C, D>(p, BH, 0, stream);
         prof_end(stream);
         prof_begin(stream, "bwd_chunk");
         hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);

@@ -41,12 +41,17 @@ def kernel_key(name: str) -> str:
     """Map a demangled rocprofv3 kernel name to the names dn_profile_collect uses."""
     if "prep_kernel" in name:
         return "prep"
-    if "fwd_state_kernel" in name:
+    if "fwd_state_kernel" in name:   # <..., SAVE, OUTPUT>
+        if re.search(r"false, false>\(", name):
+            return "fwd_summary"
         return "fwd_state" if re.search(r"true, true>\(", name) or re.search(r"false, true>\(", name) \
             else "fwd_state_recompute"
-    for k in ("bwd_state", "bwd_chunk"):
-        if k + "_kernel" in name:
-            return k
+    if "bwd_state_kernel" in name:   # <..., SUMMARY>
+        return "bwd_summary" if re.search(r"true>\(", name) else "bwd_state"
+    if "scan_combine_kernel" in name:
+        return "scan_combine"
+    if "bwd_chunk_kernel" in name:
+        return "bwd_chunk"
     if "copyBuffer" in name or "elementwise" in name:
         return "copy"
     return name

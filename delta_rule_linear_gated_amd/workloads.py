@@ -78,6 +78,13 @@ CONFIGS = {
                                  "bf16", 0.0, True, "recompute", 5),
 }
 CONFIG_ORDER = ["deltanet_fp32", "gdn_fp32", "gdn_bf16", "kda_bf16", "kla_gdn_bf16_32k"]
+# Few heads, long sequence (one sequence of a 4-head layer): the sequential state
+# passes alone would occupy 32 compute units, so the chunk-parallel scan runs.
+EXTRA = {
+    "gdn_bf16_4h_32k": Workload("gdn_bf16_4h_32k", 1, 4, 32768, 128, 128, 64, "scalar", "bf16", 0.5, False,
+                                "save", 6),
+}
+CONFIGS.update(EXTRA)
 HEADLINE = "gdn_bf16"
 
 

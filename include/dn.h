@@ -105,10 +105,24 @@ typedef enum {
 #define DN_FLAG_KACZMARZ 1u
 
 /*
+ * Chunk-parallel state scan (exact affine chunk transfer, SFDA summary, "Exakter
+ * Affiner Chunk-Transfer"; chunk-WY theorem): when the sequential state passes
+ * would occupy few compute units (few heads: (dv / 16) * B * H < 128) and the
+ * sequence has at least 32 chunks, the forward and backward split the chunks
+ * into segments, run every segment from a zero state together with its d_k x
+ * d_k transition matrix, compose the segments' boundary states in fp32, and
+ * rerun each segment from its true boundary state.  Results equal the
+ * sequential pass up to rounding (the transition is formed with the same
+ * matrix-core operands).  This flag forces the sequential pass.
+ */
+#define DN_FLAG_NO_SCAN 2u
+
+/*
  * Problem shape.  Supported: B, H, T >= 0 with B*H <= 65535; dk == dv in
  * {16, 32, 64, 128} (fp32: dk <= 64); C in {16, 32, 64}; any T (a last,
  * shorter chunk is handled exactly); fp32 with a vector gate needs C <= 32 at
- * dk = 64.  flags: 0 or DN_FLAG_KACZMARZ (other bits: DN_ERR_INVALID); eps:
+ * dk = 64.  flags: DN_FLAG_KACZMARZ and / or DN_FLAG_NO_SCAN (other bits:
+ * DN_ERR_INVALID; dn_recurrent_fwd ignores DN_FLAG_NO_SCAN); eps:
  * read only with DN_FLAG_KACZMARZ, finite and >= 0.  Anything else returns
  * DN_ERR_UNSUPPORTED.
  */
@@ -194,12 +208,14 @@ const char* dn_last_error(void);
  * Diagnostics: byte offsets of the workspace regions a pass uses, in the order
  * {cumulative log-decay, (I+A)^{-1} per chunk, intra-chunk scores per chunk,
  * triangular-residual adjoint, state cotangent per chunk, recomputed states,
- * Kaczmarz step data (as in the saved buffer), total}; a region the pass does
+ * Kaczmarz step data (as in the saved buffer), scan segment summaries
+ * [B][H][nseg][dv + dk][dk] fp32, scan boundary states [B][H][nseg][dv][dk] fp32
+ * (both only when the scan is used), total}; a region the pass does
  * not use has zero size (the next offset is equal).  DN_PASS_FWD places the
  * per-chunk data there only when the forward saves nothing; DN_PASS_BWD takes
  * it from the saved buffer.  Returns DN_OK or an error for a bad shape / pass.
  */
-dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[8]);
+dn_status dn_workspace_layout(const dn_shape* shape, int pass, size_t offsets[10]);
 
 /*
  * Diagnostics: per-kernel timing.  dn_profile_enable(1) makes every later

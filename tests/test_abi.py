@@ -56,15 +56,63 @@ def test_sizes_of_the_workloads(name):
     assert 0 < f and 0 < b < r
     lay = B.dn_workspace_layout(sh, B.DN_PASS_BWD_RECOMPUTE)
     assert lay["total"] == r
-    offs = [lay[k] for k in ("gam", "T", "P", "lam", "dS1", "states", "kz", "total")]
+    offs = [lay[k] for k in ("gam", "T", "P", "lam", "dS1", "states", "kz", "seg_end", "seg_start", "total")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     # the recomputing backward holds in its workspace what the saved buffer carries
     assert r - b == B.dn_states_bytes(sh)
-    # with a saved buffer the backward's workspace holds only lambda and dS1
+    # with a saved buffer the backward's workspace holds only lambda and dS1 (and the
+    # scan buffers, when the scan is used)
     lb = B.dn_workspace_layout(sh, B.DN_PASS_BWD)
-    assert lb["gam"] == lb["T"] == lb["P"] == lb["lam"] == 0 and lb["states"] == lb["kz"] == lb["total"] == b
+    scan = lb["total"] - lb["seg_end"]
+    assert scan == scan_bytes(w.B, w.H, w.T, w.dk, w.dv, w.C)
+    assert lb["gam"] == lb["T"] == lb["P"] == lb["lam"] == 0 and lb["states"] == lb["kz"] == lb["seg_end"]
     # the forward's workspace holds gam, T, P (used when it saves nothing)
-    assert f == sl["total"] - sl["T"]
+    assert f == sl["total"] - sl["T"] + scan
+
+
+def expected_segments(B_, H, T, dv, C):
+    """The scan's segment count, restated: sequential unless (dv/16) * B * H < 128
+    and at least 32 chunks; then min(512 // grid, 32, NT // 4) segments of equal
+    length (the last shorter), at least 2."""
+    NT = -(-T // C) if T > 0 else 0
+    grid = (dv // 16) * B_ * H
+    if NT < 32 or grid == 0 or 2 * grid >= 256:
+        return 1
+    g = min(512 // grid, 32, NT // 4)
+    if g < 2:
+        return 1
+    ln = -(-NT // g)
+    return -(-NT // ln)
+
+
+def scan_bytes(B_, H, T, dk, dv, C):
+    G = expected_segments(B_, H, T, dv, C)
+    if G == 1:
+        return 0
+    al = lambda x: -(-x // 256) * 256
+    return al(B_ * H * G * (dv + dk) * dk * 4) + al(B_ * H * G * dv * dk * 4)
+
+
+@pytest.mark.parametrize("B_,H,T,d,C,nseg", [
+    (1, 4, 32768, 128, 64, 16),     # few heads, long sequence: 16 segments of 32 chunks
+    (2, 4, 1024, 64, 64, 1),        # 16 chunks: sequential
+    (2, 4, 2048, 64, 64, 8),        # 8 heads at d = 64, 32 chunks: 8 segments of 4
+    (1, 1, 64, 16, 16, 1),          # 4 chunks: sequential
+    (8, 16, 4096, 128, 64, 1),      # 128 heads fill the device: sequential
+    (1, 32, 32768, 128, 64, 1),     # 32 heads x 8 row blocks = 256: sequential
+    (1, 8, 8192, 128, 64, 8),       # 64 blocks: 8 segments of 16 chunks
+    (1, 1, 100 * 64 + 5, 128, 64, 21),   # 101 chunks, at most 101 // 4 = 25 -> segments of 5 -> 21
+    (1, 1, 37 * 64, 64, 64, 8),     # 37 chunks: 9 asked, segments of 5 -> 8
+])
+def test_scan_plan_and_workspace(B_, H, T, d, C, nseg):
+    assert expected_segments(B_, H, T, d, C) == nseg
+    sh = B.make_shape(B_, H, T, d, d, C, "bf16", "scalar")
+    for pass_ in (B.DN_PASS_FWD, B.DN_PASS_BWD, B.DN_PASS_BWD_RECOMPUTE):
+        lay = B.dn_workspace_layout(sh, pass_)
+        assert lay["total"] - lay["seg_end"] == scan_bytes(B_, H, T, d, d, C)
+    off = B.make_shape(B_, H, T, d, d, C, "bf16", "scalar", no_scan=True)
+    lay = B.dn_workspace_layout(off, B.DN_PASS_FWD)
+    assert lay["total"] == lay["seg_end"]
 
 
 FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation first
@@ -135,7 +183,7 @@ def test_validation_errors_kaczmarz():
         assert bwd(sh_of(kaczmarz_eps=eps)) == B.DN_ERR_INVALID
         assert rec(sh_of(kaczmarz_eps=eps)) == B.DN_ERR_INVALID
     sh = sh_of()
-    sh.flags = 2
+    sh.flags = 4   # no such flag
     assert fwd(sh) == B.DN_ERR_INVALID and "flags" in B.dn_last_error()
     assert B.dn_states_bytes(sh) == 0
     # eps is ignored without the flag; with it the saved buffer gains the step data
