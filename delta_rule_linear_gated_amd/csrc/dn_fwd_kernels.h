@@ -142,8 +142,16 @@ template <typename TI, int GATE, int C, int DK> struct PrepSmem {
 // ---------------------------------------------------------------------------
 // prep_kernel: grid (NT, BH), one chunk per workgroup: gam, P and T of the
 // chunk (T and P row-major; the reverse pass transposes them while staging).
+// Waves per SIMD prep_kernel is compiled for: three workgroups per compute unit
+// (registers capped at 80) where three fit in LDS, else the default two.  Not
+// below d = 64, where the cap would spill (C = 64, bf16).
+template <typename TI, int GATE, int C, int DK> constexpr int prep_waves() {
+    return DK >= 64 && 3 * PrepSmem<TI, GATE, C, DK>::TOTAL <= 160 * 1024 ? 3 * kWaves / 4 : kWaves / 4;
+}
+
 template <typename TI, int GATE, int C, int DK>
-__global__ __launch_bounds__(kThreads) void prep_kernel(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prep_waves<TI, GATE, C, DK>())))
+void prep_kernel(Params p) {
     using L = PrepSmem<TI, GATE, C, DK>;
     constexpr int LDK = L::LDK, LDA = L::LDA, LC = L::LC;
     constexpr bool VEC = L::VEC;
