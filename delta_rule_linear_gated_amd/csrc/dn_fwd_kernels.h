@@ -539,11 +539,17 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         // for every outstanding load and store.
         prefetch(n + 1 < n1 ? n + 1 : n);
 
-        // (c) X^T = S0 (K Gam)^T ;  R = diag(beta) (V - X)
+        // (c) X^T = S0 (K Gam)^T ;  R = diag(beta) (V - X); with the output, the
+        //     S0 (Q Gam)^T part of O^T in the same pass over S0's fragments
+        f32x4 OT[TX::PER];
+        zero_acc<BV, C>(OT);
         {
             f32x4 X[TX::PER];
             zero_acc<BV, C>(X);
-            gemm<TI, BV, C, DK, false, false>(X, Ss, LDK, Kg, LDK);
+            if constexpr (OUTPUT)
+                gemm2<TI, BV, C, DK, false, false>(X, OT, Ss, LDK, Kg, Qg, LDK);
+            else
+                gemm<TI, BV, C, DK, false, false>(X, Ss, LDK, Kg, LDK);
             if (TX::active()) {
                 f32x4 r[TX::PER];   // all LDS reads, then all LDS writes (see RegN::store)
 #pragma unroll
@@ -571,11 +577,9 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             }
         }
         __syncthreads();
-        // (e) O^T = S0 (Q Gam)^T + U^T P^T   (O into Rb, dead since (d); written back next iteration)
+        // (e) O^T = S0 (Q Gam)^T (from (c)) + U^T P^T   (O into Rb, dead since (d); written back
+        //     next iteration)
         if (OUTPUT) {
-            f32x4 OT[TX::PER];
-            zero_acc<BV, C>(OT);
-            gemm<TI, BV, C, DK, false, false>(OT, Ss, LDK, Qg, LDK);
             if (SCA && TX::active()) {
 #pragma unroll
                 for (int j = 0; j < TX::PER; ++j) OT[j] *= rowf[TX::col(j)];
