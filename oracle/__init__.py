@@ -13,6 +13,11 @@ Contents
   chunk-transfer form, in numpy fp64 (pinned to the sequential form for every
   chunk size).
 * ``brute``: the explicit product of d_k x d_k transition matrices.
+* ``sfda``: the phase-controlled gate of the SFDA summary (complex state,
+  per-channel rotation-decay, real inputs, real-part readout), recurrent form,
+  in three evaluations pinned against each other and the above.
+* ``kaczmarz_*``: the Kaczmarz step size of the KLA abstract on top of
+  ``forward`` / ``backward``.
 
 Operator (per head, state S in R^{d_v x d_k}):
     S_t = S_{t-1} Diag(exp(g_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t

@@ -1,0 +1,131 @@
+"""Phase-controlled gate (SFDA), recurrent form, fp64 -- TEST INFRASTRUCTURE ONLY.
+
+Reading of the SFDA technical summary (gist.science), "Kernarchitektur" and
+"Reelle Implementierung", transposed to the d_v x d_k orientation of this
+operator, with real inputs:
+  * the state is complex, S = A + i B (d_v x d_k);
+  * step t applies the complex diagonal gate Lambda_t = diag(exp(g_t) exp(i theta_t))
+    (one log-decay and one phase per key channel; a scalar g is shared by all
+    channels, no g means no decay), then the rank-one erase with the real key,
+    then the write of the real value:
+        S_t = S_{t-1} Lambda_t (I - beta_t k_t k_t^T) + beta_t v_t k_t^T;
+  * the output is the real part, o_t = Re(S_t q_t).
+With theta = 0 and a real initial state B stays zero and this is KDA ("KDA als
+Spezialfall", "Zentrale Beitraege").  In real arithmetic each key channel's pair
+(A_c, B_c) is turned by a 2 x 2 rotation-decay block and the erase and write act
+on A and B separately.
+
+Three evaluations, pinned against each other and against closed forms in
+tests/test_oracle_sfda.py:
+  forward           the recurrence in complex numpy, vectorised over heads;
+  forward_products  explicit complex transition matrices and their products
+                    (brute force, O(T^2 d_k^3));
+  forward_blocks    the real 2 x 2 rotation-decay form (A, B real).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import brute
+
+
+def _f64(x):
+    return None if x is None else np.asarray(x, np.float64)
+
+
+def _gate(g, theta, T, dk, lead):
+    """Complex per-channel gates [..., T, dk]: exp(g) exp(i theta)."""
+    theta = _f64(theta)
+    if g is None:
+        mag = np.ones(lead + (T, dk))
+    else:
+        g = _f64(g)
+        mag = np.exp(g)[..., None] * np.ones(dk) if g.ndim == len(lead) + 1 else np.exp(g)
+    return mag * np.exp(1j * theta)
+
+
+def _beta(beta, k, eps):
+    beta = _f64(beta)
+    if eps is None:
+        return beta
+    return beta / (np.sum(_f64(k) ** 2, axis=-1) + eps)   # Kaczmarz step (KLA abstract)
+
+
+def forward(q, k, v, beta, g, theta, h0_re=None, h0_im=None, eps=None):
+    """Inputs [B, H, T, .]: q, k [dk]; v [dv]; beta [B,H,T]; g None, [B,H,T] or
+    [B,H,T,dk]; theta [B,H,T,dk]; h0_re / h0_im [B,H,dv,dk] or None (zero).
+    ``eps`` not None: beta is eta of the Kaczmarz step.
+    Returns o [B,H,T,dv] (real) and the final state [B,H,dv,dk] (complex)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Bn, H, T, dk = q.shape
+    dv = v.shape[-1]
+    lam = _gate(g, theta, T, dk, (Bn, H))
+    b = _beta(beta, k, eps)
+    S = np.zeros((Bn, H, dv, dk), np.complex128)
+    if h0_re is not None:
+        S += _f64(h0_re)
+    if h0_im is not None:
+        S += 1j * _f64(h0_im)
+    o = np.zeros((Bn, H, T, dv))
+    for t in range(T):
+        S = S * lam[:, :, t, None, :]                        # gate the key channels
+        p = np.einsum("bhvc,bhc->bhv", S, k[:, :, t])        # S k
+        u = b[:, :, t, None] * (v[:, :, t] - p)              # beta (v - S k)
+        S = S + u[..., :, None] * k[:, :, t, None, :]        # + u k^T
+        o[:, :, t] = np.einsum("bhvc,bhc->bhv", S, q[:, :, t]).real
+    return o, S
+
+
+def forward_products(q, k, v, beta, g, theta, h0=None, eps=None):
+    """One head, brute force: complex M_t = Lambda_t (I - beta_t k_t k_t^T) as
+    explicit matrices, S_t = h0 M_1..M_t + sum_j beta_j v_j k_j^T M_{j+1}..M_t.
+    q, k [T, dk]; v [T, dv]; beta [T]; g None, [T] or [T, dk]; theta [T, dk];
+    h0 complex [dv, dk] or None.  Returns (o [T, dv] real, S_T complex)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, dk = q.shape
+    dv = v.shape[1]
+    lam = _gate(g, theta, T, dk, ())
+    b = _beta(beta, k, eps)
+    Ms = [brute.transition(k[t], b[t], lam[t]) for t in range(T)]
+    S0 = np.zeros((dv, dk), np.complex128) if h0 is None else np.asarray(h0, np.complex128)
+    o = np.zeros((T, dv))
+    S = S0
+    for t in range(T):
+        P = brute.product(Ms[: t + 1])
+        S = S0 @ P
+        for j in range(t + 1):
+            W = np.outer(b[j] * v[j], k[j]).astype(np.complex128)
+            tail = brute.product(Ms[j + 1: t + 1])
+            S = S + (W if tail is None else W @ tail)
+        o[t] = (S @ q[t]).real
+    return o, S
+
+
+def forward_blocks(q, k, v, beta, g, theta, h0_re=None, h0_im=None, eps=None):
+    """The real form: A, B [.., dv, dk] real; per key channel c the pair
+    (A[:, c], B[:, c]) is turned by exp(g) [[cos, -sin], [sin, cos]](theta); then
+    the erase with k acts on A and B, the write of v on A; o = A q."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Bn, H, T, dk = q.shape
+    dv = v.shape[-1]
+    b = _beta(beta, k, eps)
+    theta = _f64(theta)
+    if g is None:
+        mag = np.ones((Bn, H, T, dk))
+    else:
+        g = _f64(g)
+        mag = np.exp(g)[..., None] * np.ones(dk) if g.ndim == 3 else np.exp(g)
+    A = np.zeros((Bn, H, dv, dk)) if h0_re is None else _f64(h0_re).copy()
+    Bm = np.zeros((Bn, H, dv, dk)) if h0_im is None else _f64(h0_im).copy()
+    o = np.zeros((Bn, H, T, dv))
+    for t in range(T):
+        c, s, m = np.cos(theta[:, :, t]), np.sin(theta[:, :, t]), mag[:, :, t]
+        A, Bm = (m * c)[:, :, None, :] * A - (m * s)[:, :, None, :] * Bm, \
+                (m * s)[:, :, None, :] * A + (m * c)[:, :, None, :] * Bm
+        kt = k[:, :, t]
+        pa = np.einsum("bhvc,bhc->bhv", A, kt)
+        pb = np.einsum("bhvc,bhc->bhv", Bm, kt)
+        A = A + (b[:, :, t, None] * (v[:, :, t] - pa))[..., None] * kt[:, :, None, :]
+        Bm = Bm - (b[:, :, t, None] * pb)[..., None] * kt[:, :, None, :]
+        o[:, :, t] = np.einsum("bhvc,bhc->bhv", A, q[:, :, t])
+    return o, A + 1j * Bm

@@ -1,0 +1,106 @@
+"""Pins of the phase-controlled gate's oracle (oracle/sfda.py, SFDA technical
+summary, "Kernarchitektur", real inputs, transposed orientation): against the
+independent C oracle at zero phase (KDA), against explicit products of complex
+transition matrices, between the complex and the real 2 x 2 rotation-decay
+forms, and against closed forms (pure rotation, decay of the magnitudes, the
+Kaczmarz projection)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import sfda
+
+
+def rel(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    den = np.max(np.abs(b))
+    return np.max(np.abs(a - b)) / (den if den > 0 else 1.0)
+
+
+def case(seed, Bn=2, H=2, T=7, dk=6, dv=5, gate="vector", phase=0.7, complex_h0=True):
+    r = np.random.default_rng(seed)
+    c = dict(q=r.standard_normal((Bn, H, T, dk)), k=r.standard_normal((Bn, H, T, dk)) * 0.5,
+             v=r.standard_normal((Bn, H, T, dv)), beta=1 / (1 + np.exp(-r.standard_normal((Bn, H, T)))),
+             theta=phase * r.standard_normal((Bn, H, T, dk)),
+             h0_re=r.standard_normal((Bn, H, dv, dk)),
+             h0_im=r.standard_normal((Bn, H, dv, dk)) if complex_h0 else None)
+    c["g"] = {"none": None, "scalar": -np.abs(r.standard_normal((Bn, H, T))) / 4,
+              "vector": -np.abs(r.standard_normal((Bn, H, T, dk))) / 4}[gate]
+    return c
+
+
+def run(c, **over):
+    d = dict(c)
+    d.update(over)
+    return sfda.forward(d["q"], d["k"], d["v"], d["beta"], d["g"], d["theta"], d["h0_re"], d["h0_im"])
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "vector"])
+def test_zero_phase_is_the_c_oracle(gate):
+    """theta = 0, real h0: the complex recurrence is the KDA / GDN / DeltaNet one."""
+    c = case(1, gate=gate, complex_h0=False)
+    o, S = run(c, theta=np.zeros_like(c["theta"]))
+    o_ref, h_ref = oracle.forward(c["q"], c["k"], c["v"], c["beta"], c["g"], c["h0_re"])
+    assert rel(o, o_ref) < 1e-12 and rel(S.real, h_ref) < 1e-12
+    assert np.max(np.abs(S.imag)) == 0.0
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "vector"])
+def test_recurrence_equals_transition_products(gate):
+    c = case(2, Bn=1, H=2, T=5, dk=4, dv=3, gate=gate)
+    o, S = run(c)
+    for h in range(2):
+        g = None if c["g"] is None else c["g"][0, h]
+        h0 = c["h0_re"][0, h] + 1j * c["h0_im"][0, h]
+        ob, Sb = sfda.forward_products(c["q"][0, h], c["k"][0, h], c["v"][0, h], c["beta"][0, h], g,
+                                       c["theta"][0, h], h0)
+        assert rel(o[0, h], ob) < 1e-12 and rel(S[0, h], Sb) < 1e-12
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "vector"])
+def test_complex_form_equals_real_rotation_blocks(gate):
+    c = case(3, gate=gate)
+    o, S = run(c)
+    ob, Sb = sfda.forward_blocks(c["q"], c["k"], c["v"], c["beta"], c["g"], c["theta"], c["h0_re"], c["h0_im"])
+    assert rel(o, ob) < 1e-12 and rel(S, Sb) < 1e-12
+
+
+def test_pure_rotation_closed_form():
+    """beta = 0, g = 0: every key channel of the state turns by the summed phase."""
+    c = case(4, gate="none")
+    o, S = run(c, beta=np.zeros_like(c["beta"]))
+    S0 = c["h0_re"] + 1j * c["h0_im"]
+    expect = S0 * np.exp(1j * np.sum(c["theta"], axis=2))[:, :, None, :]
+    assert rel(S, expect) < 1e-13
+    # and the readout of the last step is the real part of S_T q_T
+    assert rel(o[:, :, -1], np.einsum("bhvc,bhc->bhv", expect, c["q"][:, :, -1]).real) < 1e-13
+
+
+def test_decay_of_magnitudes():
+    """beta = 0: |S_T| = |S_0| exp(sum_t g_t) element by element, whatever the phases."""
+    c = case(5, gate="vector")
+    _, S = run(c, beta=np.zeros_like(c["beta"]))
+    S0 = c["h0_re"] + 1j * c["h0_im"]
+    assert rel(np.abs(S), np.abs(S0) * np.exp(np.sum(c["g"], axis=2))[:, :, None, :]) < 1e-13
+
+
+def test_kaczmarz_projection_with_phases():
+    """With the Kaczmarz step and eta = 1 the last step solves S_T k_T = v_T exactly:
+    the erase removes the gated state's whole component along k_T, real and
+    imaginary, and the write puts v_T there (KLA abstract's projection)."""
+    c = case(6, gate="vector")
+    eta = np.ones_like(c["beta"])
+    _, S = sfda.forward(c["q"], c["k"], c["v"], eta, c["g"], c["theta"], c["h0_re"], c["h0_im"], eps=0.0)
+    Sk = np.einsum("bhvc,bhc->bhv", S, c["k"][:, :, -1])
+    assert rel(Sk, c["v"][:, :, -1]) < 1e-12
+
+
+def test_a_plausible_mistake_is_caught():
+    """A planted mistake -- the phase applied with the opposite sign -- fails the
+    pins above (the transition-product comparison catches it)."""
+    c = case(7, Bn=1, H=1, T=4, dk=4, dv=3)
+    o_wrong, _ = run(c, theta=-c["theta"])
+    h0 = c["h0_re"][0, 0] + 1j * c["h0_im"][0, 0]
+    ob, _ = sfda.forward_products(c["q"][0, 0], c["k"][0, 0], c["v"][0, 0], c["beta"][0, 0], c["g"][0, 0],
+                                  c["theta"][0, 0], h0)
+    assert rel(o_wrong[0, 0], ob) > 1e-3
