@@ -87,6 +87,9 @@ def parse():
                     help="instead of fwd+bwd, time the recurrent (decode) entry point: --decode-batch "
                          "sequences with the workload's heads and dims, --decode-tokens tokens per "
                          "sequence and call, the fp32 state updated in place")
+    ap.add_argument("--phase", action="store_true",
+                    help="with --decode: the phase-controlled gate (dn_recurrent_phase_fwd, complex state, "
+                         "per-channel decay and phase)")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--decode-tokens", type=int, default=1)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -272,20 +275,26 @@ def decode_bench(args, w0):
     from delta_rule_linear_gated_amd import binding as B
     from delta_rule_linear_gated_amd import workloads as W
 
-    w = W.custom(args.decode_batch, w0.H, args.decode_tokens, w0.dk, w0.dv, w0.C, w0.gate, w0.dtype,
-                 h0_std=0.5, kla=w0.kla, seed=w0.seed, name=f"decode_{w0.name}", kz_eps=w0.kz_eps)
+    gate = "vector" if args.phase else w0.gate   # the phase-controlled gate decays per channel
+    w = W.custom(args.decode_batch, w0.H, args.decode_tokens, w0.dk, w0.dv, w0.C, gate, w0.dtype,
+                 h0_std=0.5, kla=w0.kla, seed=w0.seed, name=f"decode_{w0.name}", kz_eps=w0.kz_eps,
+                 phase=args.phase)
     dev = torch.device("cuda:0")
     print(f"[bench] decode: generating {w.describe()}", file=sys.stderr, flush=True)
     inp_cpu = W.make_inputs(w, cotangents=False)
     inp = {n: (None if t is None else t.to(dev)) for n, t in inp_cpu.items()}
     q, k, v, beta, g = (inp[n] for n in ("q", "k", "v", "beta", "g"))
     state = inp["h0"].clone()
+    state_im = inp["h0_im"].clone() if args.phase else None
     o = torch.empty_like(v)
     sh = B.make_shape(w.B, w.H, w.T, w.dk, w.dv, w.C, w.dtype, w.gate, w.kaczmarz_eps)
     stream = torch.cuda.current_stream(dev)
 
     def call():
-        st = B.dn_recurrent_fwd(sh, q, k, v, beta, g, state, o, stream)
+        if args.phase:
+            st = B.dn_recurrent_phase_fwd(sh, q, k, v, beta, g, inp["theta"], state, state_im, o, stream)
+        else:
+            st = B.dn_recurrent_fwd(sh, q, k, v, beta, g, state, o, stream)
         if st != B.DN_OK:
             raise B.DnError(st, B.dn_last_error())
 
@@ -304,14 +313,17 @@ def decode_bench(args, w0):
     E = 2 if w.dtype == "bf16" else 4
     gw = w.dk if w.gate == "vector" else (0 if w.gate == "none" else 1)
     heads = w.B * w.H
-    by = heads * (2 * w.dv * w.dk * 4 + w.T * ((2 * w.dk + 2 * w.dv) * E + 4 * (1 + gw)))
-    fl = heads * w.T * 8 * w.dv * w.dk     # decay, S k, rank-one update, S q
-    tot, n = kern.get("recurrent", (0.0, 0))
+    nst = 2 if args.phase else 1           # real (and imaginary) state, read and written once
+    by = heads * (nst * 2 * w.dv * w.dk * 4 + w.T * ((2 * w.dk + 2 * w.dv) * E + 4 * (1 + gw)
+                                                  + (4 * w.dk if args.phase else 0)))
+    fl = heads * w.T * (8 if not args.phase else 16) * w.dv * w.dk   # decay, S k, rank-one update, S q
+    kname = "recurrent_phase" if args.phase else "recurrent"
+    tot, n = kern.get(kname, (0.0, 0))
     roofline = None
     if n:
         avg_s = tot / n / 1e3
         ach = by / avg_s / 1e9
-        roofline = {"kernel": "recurrent", "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
                     "algorithmic_bytes_per_launch": int(by), "algorithmic_flops_per_launch": int(fl),
                     "avg_launch_ms": round(avg_s * 1e3, 4)}
@@ -325,7 +337,11 @@ def decode_bench(args, w0):
         t0 = time.perf_counter()
         reps = 0
         while True:
-            if w.kla:
+            if args.phase:
+                from oracle import sfda
+                sfda.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["theta"], f["h0"], f["h0_im"],
+                             eps=w.kaczmarz_eps)
+            elif w.kla:
                 oracle.kaczmarz_forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"], eps=w.kaczmarz_eps,
                                         nthreads=threads)
             else:
@@ -334,13 +350,18 @@ def decode_bench(args, w0):
             if time.perf_counter() - t0 > 2.0:
                 break
         dt = (time.perf_counter() - t0) / reps
+        if args.phase:
+            threads = 1   # the phase-controlled gate's oracle is numpy, one thread
         cpu = {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole batch ({w.B * w.H} heads x {w.T} token(s)), fp64, {reps} repetitions"}
     line = {
-        "metric": "decode tokens/s (recurrent form, state in place)", "value": round(tokens / (ms / 1e3), 1),
+        "metric": "decode tokens/s (recurrent form, state in place" + (", phase-controlled gate)" if args.phase
+                                                                         else ")"),
+        "value": round(tokens / (ms / 1e3), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"decode: gate={w.gate} B={w.B} H={w.H} dk={w.dk} dv={w.dv}, {w.T} token(s) "
+        "config": {"workload": f"decode{' (phase-controlled gate)' if args.phase else ''}: gate={w.gate} "
+                               f"B={w.B} H={w.H} dk={w.dk} dv={w.dv}, {w.T} token(s) "
                                f"per sequence and call", "global_batch": w.B, "seq_len": w.T, "heads": w.H,
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu,

@@ -28,8 +28,8 @@ DN_PASS_FWD, DN_PASS_BWD, DN_PASS_BWD_RECOMPUTE = 0, 1, 2
 DN_FLAG_KACZMARZ, DN_FLAG_NO_SCAN = 1, 2
 
 EXPORTS = ("dn_states_bytes", "dn_states_layout", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
-           "dn_chunk_bwd", "dn_recurrent_fwd", "dn_status_string", "dn_last_error", "dn_profile_enable",
-           "dn_profile_collect")
+           "dn_chunk_bwd", "dn_recurrent_fwd", "dn_recurrent_phase_fwd", "dn_status_string", "dn_last_error",
+           "dn_profile_enable", "dn_profile_collect")
 
 
 class DnError(RuntimeError):
@@ -68,6 +68,8 @@ def lib():
     L.dn_states_layout.restype = i32
     L.dn_recurrent_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.dn_recurrent_fwd.restype = i32
+    L.dn_recurrent_phase_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.dn_recurrent_phase_fwd.restype = i32
     L.dn_chunk_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dn_chunk_fwd.restype = i32
     L.dn_chunk_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -190,6 +192,12 @@ def dn_recurrent_fwd(shape, q, k, v, beta, g, state, o, stream=None) -> int:
                                   _ptr(state), _ptr(o), _stream(stream))
 
 
+def dn_recurrent_phase_fwd(shape, q, k, v, beta, g, theta, state_re, state_im, o, stream=None) -> int:
+    """Raw call; returns the dn_status (no exception)."""
+    return lib().dn_recurrent_phase_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                        _ptr(theta), _ptr(state_re), _ptr(state_im), _ptr(o), _stream(stream))
+
+
 # ------------------------------------------------------------------ convenience
 
 
@@ -292,6 +300,19 @@ def recurrent_fwd(q, k, v, beta, g, state, stream=None, kaczmarz_eps=None):
     sh = make_shape(B, H, T, dk, v.shape[-1], 64, q.dtype, _gate_kind(g, dk), kaczmarz_eps)
     o = torch.empty_like(v)
     _check(dn_recurrent_fwd(sh, q, k, v, beta, g, state, o, stream))
+    return o
+
+
+def recurrent_phase_fwd(q, k, v, beta, g, theta, state_re, state_im, gate=None, stream=None, kaczmarz_eps=None):
+    """T recurrent steps with the phase-controlled gate; the complex state
+    (state_re, state_im, fp32 [B,H,dv,dk]) is updated in place.  ``gate`` names
+    how g is laid out when it is 4-D or 3-D (default: from g's rank).  Returns o."""
+    _contig(q, k, v, beta, g, theta, state_re, state_im)
+    B, H, T, dk = q.shape
+    sh = make_shape(B, H, T, dk, v.shape[-1], 64, q.dtype, gate if gate is not None else _gate_kind(g, dk),
+                    kaczmarz_eps)
+    o = torch.empty_like(v)
+    _check(dn_recurrent_phase_fwd(sh, q, k, v, beta, g, theta, state_re, state_im, o, stream))
     return o
 
 

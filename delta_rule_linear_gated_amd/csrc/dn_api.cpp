@@ -336,8 +336,16 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
     return DN_OK;
 }
 
-dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
-                           const float* beta, const float* g, float* state, void* o, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both recurrent entry points: theta == nullptr is the plain recurrence (then
+// state_im must be NULL too), else the phase-controlled gate with the complex
+// state (state, state_im).
+dn_status recurrent_call(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
+                         const float* g, const float* theta, float* state, float* state_im, void* o, void* stream,
+                         bool phase) {
     g_err[0] = '\0';
     if (!shape) return fail(DN_ERR_INVALID, "shape is NULL");
     const dn_shape* s = shape;
@@ -353,20 +361,25 @@ dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, 
     const size_t gw = s->gate == DN_GATE_VECTOR ? (size_t)s->dk : 1;
     const size_t nk = BH * T * s->dk * E, nv = BH * T * s->dv * E, nb = BH * T * 4;
     const size_t ng = s->gate == DN_GATE_NONE ? 0 : BH * T * gw * 4, ns = BH * s->dv * s->dk * 4;
+    const size_t nth = phase ? BH * T * s->dk * 4 : 0, nsi = phase ? ns : 0;
     if (s->gate == DN_GATE_NONE && g) return fail(DN_ERR_INVALID, "g must be NULL without a gate");
     DN_TRY(need(q, nk, "q"));
     DN_TRY(need(k, nk, "k"));
     DN_TRY(need(v, nv, "v"));
     DN_TRY(need(beta, nb, "beta"));
     DN_TRY(need(g, ng, "g"));
+    DN_TRY(need(theta, nth, "theta"));
     DN_TRY(need(state, ns, "state"));
+    DN_TRY(need(state_im, nsi, "state_im"));
     DN_TRY(need(o, nv, "o"));
     DN_TRY(check_buffers({{"q", q, nk, false},
                           {"k", k, nk, false},
                           {"v", v, nv, false},
                           {"beta", beta, nb, false},
                           {"g", g, ng, false},
+                          {"theta", theta, nth, false},
                           {"state", state, ns, true},
+                          {"state_im", state_im, nsi, true},
                           {"o", o, nv, true}}));
     dn::Problem pr{};
     pr.B = s->B;
@@ -390,6 +403,10 @@ dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, 
     p.g = g;
     p.hT = state;
     p.o = o;
+    if (phase) {
+        p.theta = theta;
+        p.hT_im = state_im;
+    }
     if (pr.kz) {   // the step size is formed per step in the kernel
         p.eta = beta;
         p.eps = s->eps;
@@ -398,6 +415,21 @@ dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, 
     const hipError_t e = dn::launch_recurrent(pr, p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, float* state, void* o, void* stream) {
+    return recurrent_call(shape, q, k, v, beta, g, nullptr, state, nullptr, o, stream, false);
+}
+
+dn_status dn_recurrent_phase_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
+                                 const float* beta, const float* g, const float* theta, float* state_re,
+                                 float* state_im, void* o, void* stream) {
+    return recurrent_call(shape, q, k, v, beta, g, theta, state_re, state_im, o, stream, true);
 }
 
 const char* dn_status_string(dn_status status) {

@@ -66,6 +66,10 @@ struct Params {
     int nseg, seg_len;
     float* seg_end;
     float* seg_start;
+    // phase-controlled gate (recurrent form only): theta [BH][T][DK] fp32 and the
+    // imaginary part of the state [BH][DV][DK] fp32 (the real part is hT)
+    const float* theta;
+    float* hT_im;
 };
 
 struct Problem {

@@ -4,6 +4,12 @@
 // with the fp32 state updated in place (the decode workload; the recurrent form
 // of the Fast Weight Attention abstract, the KLA abstract's decode setting).
 //
+// Phase-controlled gate (SFDA summary, "Kernarchitektur" and its real
+// implementation, real inputs): the state is complex, S = A + i B, the gate of
+// key channel c is exp(g) exp(i theta), i.e. a 2 x 2 rotation-decay of the pair
+// (A[:, c], B[:, c]); the erase with k acts on A and B, the write of v on A, and
+// the output is Re(S q) = A q.  theta = 0 with B = 0 is the plain recurrence.
+//
 // Rows of S are independent (row v only mixes with itself through the keys), so
 // a workgroup takes 16 rows of one head: a wave holds 4 rows, 16 lanes per row,
 // E = DK / 16 consecutive keys per lane, and both row sums of a step (S k and
@@ -19,9 +25,9 @@ namespace {
 constexpr int kRecThreads = 256;
 constexpr int kRecRows = 16;   // state rows per workgroup: 4 waves x 4 rows
 
-template <typename TI, int GATE, int DK> struct StepIn {
+template <typename TI, int GATE, int DK, bool PHASE> struct StepIn {
     static constexpr int E = DK / 16;
-    float k[E], q[E], a[GATE == kGateVector ? E : 1];
+    float k[E], q[E], a[GATE == kGateVector ? E : 1], th[PHASE ? E : 1];
     float v = 0.f, beta = 0.f;
     __device__ __forceinline__ void load(const Params& p, long tok, int v_row, int c0) {
         const TI* kp = static_cast<const TI*>(p.k) + tok * DK + c0;
@@ -38,10 +44,14 @@ template <typename TI, int GATE, int DK> struct StepIn {
 #pragma unroll
             for (int e = 0; e < E; ++e) a[e] = p.g[tok * DK + c0 + e];
         }
+        if (PHASE) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) th[e] = p.theta[tok * DK + c0 + e];
+        }
     }
 };
 
-template <typename TI, int GATE, int DK>
+template <typename TI, int GATE, int DK, bool PHASE>
 __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(Params p) {
     constexpr int E = DK / 16;
     const int DV = p.DVr;
@@ -64,13 +74,31 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < E; ++e) s[e] = srow[e];
     }
-    StepIn<TI, GATE, DK> cur, nxt;
+    // imaginary part of the state rows (phase-controlled gate only)
+    float* irow = PHASE ? p.hT_im + ((long)bh * DV + v) * DK + c0 : nullptr;
+    float sb[PHASE ? E : 1];
+    if constexpr (PHASE) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) sb[e] = irow[e];
+    }
+    StepIn<TI, GATE, DK, PHASE> cur, nxt;
     const long tok0 = (long)bh * p.T;
     if (p.T > 0) cur.load(p, tok0, v, c0);
     for (int t = 0; t < p.T; ++t) {
         nxt.load(p, tok0 + (t + 1 < p.T ? t + 1 : t), v, c0);   // next step's inputs (in bounds)
-        // decay, then the erase / write of the delta rule, then the read-out
-        if (GATE == kGateScalar) {
+        // decay (with the phase: rotation-decay), then the erase / write of the
+        // delta rule, then the read-out
+        if constexpr (PHASE) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float m = GATE == kGateScalar ? fexp(cur.a[0]) : (GATE == kGateVector ? fexp(cur.a[e]) : 1.f);
+                float sn, cs;
+                sincosf(cur.th[e], &sn, &cs);
+                const float ar = s[e], ai = sb[e];
+                s[e] = m * (cs * ar - sn * ai);
+                sb[e] = m * (sn * ar + cs * ai);
+            }
+        } else if (GATE == kGateScalar) {
             const float a = fexp(cur.a[0]);
 #pragma unroll
             for (int e = 0; e < E; ++e) s[e] *= a;
@@ -82,6 +110,12 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < E; ++e) pk += s[e] * cur.k[e];
         pk = row16_sum(pk);
+        float pkb = 0.f;   // imaginary part of S k
+        if constexpr (PHASE) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) pkb += sb[e] * cur.k[e];
+            pkb = row16_sum(pkb);
+        }
         float beta = cur.beta;
         if (p.kz) {   // Kaczmarz step (KLA abstract): beta_t = eta_t / (||k_t||^2 + eps)
             float kk = 0.f;
@@ -96,6 +130,11 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(Params p) {
             s[e] += u * cur.k[e];
             oq += s[e] * cur.q[e];
         }
+        if constexpr (PHASE) {   // the imaginary part is only erased
+            const float w = -beta * pkb;
+#pragma unroll
+            for (int e = 0; e < E; ++e) sb[e] += w * cur.k[e];
+        }
         oq = row16_sum(oq);
         if (j == 0) static_cast<TI*>(p.o)[(tok0 + t) * DV + v] = from_f<TI>(oq);
         cur = nxt;
@@ -107,11 +146,18 @@ __global__ __launch_bounds__(kRecThreads) void recurrent_kernel(Params p) {
 #pragma unroll
         for (int e = 0; e < E; ++e) srow[e] = s[e];
     }
+    if constexpr (PHASE) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) irow[e] = sb[e];
+    }
 }
 
 template <typename TI, int GATE, int DK> hipError_t launch_rec(const Problem& pr, const Params& p, hipStream_t s) {
     const long blocks = (long)pr.B * pr.H * (pr.dv / kRecRows);
-    hipLaunchKernelGGL((recurrent_kernel<TI, GATE, DK>), dim3((unsigned)blocks), dim3(kRecThreads), 0, s, p);
+    if (p.theta)
+        hipLaunchKernelGGL((recurrent_kernel<TI, GATE, DK, true>), dim3((unsigned)blocks), dim3(kRecThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<TI, GATE, DK, false>), dim3((unsigned)blocks), dim3(kRecThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -138,7 +184,7 @@ template <typename TI> hipError_t rec_gate(const Problem& pr, const Params& p, h
 
 hipError_t launch_recurrent(const Problem& pr, const Params& p, hipStream_t stream) {
     if ((long)pr.B * pr.H * pr.dv == 0 || pr.T == 0) return hipSuccess;
-    prof_begin(stream, "recurrent");
+    prof_begin(stream, p.theta ? "recurrent_phase" : "recurrent");
     const hipError_t e = pr.bf16 ? rec_gate<bf16>(pr, p, stream) : rec_gate<float>(pr, p, stream);
     prof_end(stream);
     return e;

@@ -13,6 +13,7 @@ Distributions (per head, per step):
                                                      or per channel [B,H,T,dk]
   h0    = h0_std * N(0, 1)  (None when h0_std == 0)  fp32 [B,H,dv,dk]
   dO    ~ N(0, 1) in the I/O dtype; dhT ~ N(0, 1) fp32
+  theta = 0.5 N(0, 1) fp32 [B,H,T,dk] and h0_im like h0 (phase-controlled gate only)
 The long-context workload uses the Kaczmarz step of the KLA abstract: keys are
 left unnormalised and the step input is eta = sigmoid(N(0, 1)) (fp32, returned
 under "beta"), which the operator turns into beta_t = eta_t / (||k_t||^2 + eps)
@@ -48,6 +49,7 @@ class Workload:
     policy: str = "save"          # "save": forward keeps per-chunk states; "recompute"
     seed: int = 1
     kz_eps: float = 1e-6          # eps of the Kaczmarz step (kla workloads)
+    phase: bool = False           # phase-controlled gate: draw theta (and an imaginary h0)
 
     @property
     def kaczmarz_eps(self):
@@ -149,6 +151,10 @@ def make_inputs(w: Workload, seed: int | None = None, cotangents: bool = True,
         out["h0"] = _round(w.h0_std * _rng(s, 5).standard_normal((B, H, dv, dk)), "fp32")
     else:
         out["h0"] = None
+    if w.phase:   # phases in radians, per step and key channel; the state's imaginary part
+        out["theta"] = _round(0.5 * _rng(s, 8).standard_normal((B, H, T, dk)), "fp32")
+        out["h0_im"] = _round(w.h0_std * _rng(s, 9).standard_normal((B, H, dv, dk)), "fp32") \
+            if w.h0_std > 0 else None
     if cotangents:
         out["do"] = _round(_rng(s + 100, 6).standard_normal((B, H, T, dv)), w.dtype)
         out["dhT"] = _round(_rng(s + 100, 7).standard_normal((B, H, dv, dk)), "fp32")
@@ -158,9 +164,9 @@ def make_inputs(w: Workload, seed: int | None = None, cotangents: bool = True,
 
 
 def custom(B, H, T, dk, dv, C, gate="scalar", dtype="bf16", h0_std=0.0, kla=False,
-           policy="save", seed=7, name="custom", kz_eps=1e-6) -> Workload:
+           policy="save", seed=7, name="custom", kz_eps=1e-6, phase=False) -> Workload:
     """A workload of any shape, with the same distributions."""
-    return Workload(name, B, H, T, dk, dv, C, gate, dtype, h0_std, kla, policy, seed, kz_eps)
+    return Workload(name, B, H, T, dk, dv, C, gate, dtype, h0_std, kla, policy, seed, kz_eps, phase)
 
 
 def to_f64(t, heads=None) -> np.ndarray | None:

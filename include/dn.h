@@ -198,6 +198,29 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
 dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
                            const float* beta, const float* g, float* state, void* o, void* stream);
 
+/*
+ * Recurrent evaluation with the phase-controlled gate (SFDA summary,
+ * "Kernarchitektur" and its real implementation with 2 x 2 rotation-decay
+ * blocks; read with real inputs): the state is complex, S = S_re + i S_im, and
+ * every step applies per key channel c the gate exp(g_t[c]) exp(i theta_t[c]),
+ * then the erase with the real key and the write of the real value:
+ *     S_t = S_{t-1} diag(exp(g_t + i theta_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = Re(S_t q_t).
+ * With theta = 0 and S_im = 0 this is dn_recurrent_fwd (KDA for a vector g).
+ * Only the recurrent form exists for this gate (no chunkwise form, no backward).
+ *   shape  : as for dn_recurrent_fwd; the gate type says how g is laid out (none:
+ *            no decay; scalar: one log-decay per step; vector: one per channel)
+ *   inputs : q, k, v, beta (eta with DN_FLAG_KACZMARZ), g as for dn_recurrent_fwd;
+ *            theta fp32 [B][H][T][dk] (radians)
+ *   state  : state_re, state_im fp32 [B][H][dv][dk], in place (neither may
+ *            overlap any other argument)
+ *   outputs: o [B][H][T][dv] (io)
+ * Validation and errors as for dn_recurrent_fwd; no workspace.
+ */
+dn_status dn_recurrent_phase_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
+                                 const float* beta, const float* g, const float* theta, float* state_re,
+                                 float* state_im, void* o, void* stream);
+
 /* Static description of a status code. */
 const char* dn_status_string(dn_status status);
 

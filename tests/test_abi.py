@@ -220,3 +220,24 @@ def test_validation_errors_recurrent():
     assert rec(sh_of(), o=FAKE * 6) == B.DN_ERR_INVALID                # o aliases the state
     assert rec(sh_of(), state=FAKE + 8) == B.DN_ERR_INVALID            # misaligned
     assert "state" in B.dn_last_error() or "aligned" in B.dn_last_error()
+
+
+def recp(sh, **over):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, theta=FAKE * 6, state_re=FAKE * 7,
+             state_im=FAKE * 8, o=FAKE * 9)
+    a.update(over)
+    return B.dn_recurrent_phase_fwd(sh, *(a[n] for n in ("q", "k", "v", "beta", "g", "theta", "state_re",
+                                                         "state_im", "o")), 0)
+
+
+def test_validation_errors_recurrent_phase():
+    sh = sh_of(gate="vector", T=3, dk=32, dv=32)
+    assert recp(sh, theta=None) == B.DN_ERR_INVALID and "theta" in B.dn_last_error()
+    assert recp(sh, state_im=None) == B.DN_ERR_INVALID and "state_im" in B.dn_last_error()
+    assert recp(sh, state_im=FAKE * 7) == B.DN_ERR_INVALID and "overlaps" in B.dn_last_error()
+    assert recp(sh, o=FAKE * 8) == B.DN_ERR_INVALID
+    assert recp(sh, theta=FAKE * 6 + 4) == B.DN_ERR_INVALID                     # misaligned
+    assert recp(sh_of(gate="none", T=3), theta=FAKE * 6) == B.DN_ERR_INVALID    # g given without a gate
+    assert recp(sh_of(gate="vector", T=3, dk=48, dv=48)) == B.DN_ERR_UNSUPPORTED
+    assert recp(sh_of(gate="vector", T=3, dv=24)) == B.DN_ERR_UNSUPPORTED
+    assert recp(sh_of(gate="vector", T=3, kaczmarz_eps=-1.0)) == B.DN_ERR_INVALID
