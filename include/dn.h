@@ -17,7 +17,9 @@
  *     S_t = (I - beta k k*) Lambda_t S_{t-1} + beta k v*, which with zero phase is
  *     KDA; this header uses its transpose (S is d_v x d_k, o = S q).
  *     "Der konstruktive Chunk-WY-Theorem" / "Zentrale Beitraege": chunk products
- *     in WY form and the exact affine chunk transfer used by the forward.
+ *     in WY form and the exact affine chunk transfer used by the forward and by
+ *     the chunk-parallel scan (DN_FLAG_NO_SCAN); the phase-controlled gate and
+ *     its real 2 x 2 rotation-decay form (dn_recurrent_phase_fwd).
  *   - KLA abstract (thelatestinai): GDN as gated decay plus delta-rule residual
  *     write; the Kaczmarz step beta_t = eta_t / (||k_t||^2 + eps) changes only
  *     the step size.  Callers either pass beta themselves or set
@@ -48,8 +50,8 @@
  *     beta, dbeta        fp32 [B][H][T]
  *     g, dg              fp32 [B][H][T] (DN_GATE_SCALAR) or [B][H][T][dk] (DN_GATE_VECTOR)
  *     h0, hT, dh0, dhT   fp32 [B][H][dv][dk]
- *     states             the forward's saved buffer, four regions at the byte
- *                        offsets dn_states_layout() gives (each 256-byte aligned):
+ *     states             the forward's saved buffer, regions at the byte offsets
+ *                        dn_states_layout() gives (each 256-byte aligned):
  *                          io   [B][H][NT][dv][dk]  state entering each chunk
  *                          io   [B][H][NT][C][C]    (I + A)^{-1} of each chunk
  *                          io   [B][H][NT][C][C]    causal intra-chunk scores
@@ -122,7 +124,7 @@ typedef enum {
  * {16, 32, 64, 128} (fp32: dk <= 64); C in {16, 32, 64}; any T (a last,
  * shorter chunk is handled exactly); fp32 with a vector gate needs C <= 32 at
  * dk = 64.  flags: DN_FLAG_KACZMARZ and / or DN_FLAG_NO_SCAN (other bits:
- * DN_ERR_INVALID; dn_recurrent_fwd ignores DN_FLAG_NO_SCAN); eps:
+ * DN_ERR_INVALID; the recurrent entry points ignore DN_FLAG_NO_SCAN); eps:
  * read only with DN_FLAG_KACZMARZ, finite and >= 0.  Anything else returns
  * DN_ERR_UNSUPPORTED.
  */
