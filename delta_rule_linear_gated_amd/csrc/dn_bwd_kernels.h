@@ -139,9 +139,13 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         __syncthreads();
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (VEC) {
-            rk.store(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
-            rk.store(Kn, LDK, [&](int r, int c, float x) { return -x * gf.G(r, c); });
-            rq.store(Qg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
+            // K e^{gam_C - gam}, -K e^{gam} and Q e^{gam} (one exp for the last two)
+            rk.store3(rq, Kd, Kn, Qg, LDK, [&](int r, int c, float k, float q, float* y) {
+                const float e = gf.G(r, c);
+                y[0] = k * gf.Gd(r, c);
+                y[1] = -k * e;
+                y[2] = q * e;
+            });
         } else {
             rk.store(Kd, LDK);
             rq.store(Qg, LDK);
@@ -525,9 +529,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             }
         };
         if (VEC) {
-            rk.store(Kr, LD, [&](int r, int c, float x) { return x / fpl(r, c); });
-            rk.store(Kl, LD, [&](int r, int c, float x) { return x * fpl(r, c); });
-            rq.store(Ql, LD, [&](int r, int c, float x) { return x * fpl(r, c); });
+            // K e^{c - gam}, K e^{gam - c}, Q e^{gam - c}: one exp per element
+            rk.store3(rq, Kr, Kl, Ql, LD, [&](int r, int c, float k, float q, float* y) {
+                const float e = fpl(r, c);
+                y[0] = __fdividef(k, e);
+                y[1] = k * e;
+                y[2] = q * e;
+            });
         } else {
             rq.store(Ql, LD);
         }

@@ -259,9 +259,13 @@ void prep_kernel(Params p) {
     // -- stage K and Q (centred per-channel factors for the vector gate)
     if (VEC) {
         const float* gl = gam_s + (valid - 1) * DK;  // gam_C
-        rk.store(Kp, LDK, [&](int r, int c, float x) { return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]); });
-        rk.store(Km, LDK, [&](int r, int c, float x) { return x * fexp(0.5f * gl[c] - gam_s[r * DK + c]); });
-        rq.store(Qp, LDK, [&](int r, int c, float x) { return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]); });
+        // K e^{gam - centre}, K e^{centre - gam}, Q e^{gam - centre}: one exp per element
+        rk.store3(rq, Kp, Km, Qp, LDK, [&](int r, int c, float k, float q, float* y) {
+            const float e = fexp(gam_s[r * DK + c] - 0.5f * gl[c]);
+            y[0] = k * e;
+            y[1] = __fdividef(k, e);
+            y[2] = q * e;
+        });
     } else {
         rk.store(Kp, LDK);
         rq.store(Qp, LDK);
@@ -515,9 +519,13 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         __syncthreads();
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (VEC) {
-            rq.store(Qg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
-            rk.store(Kg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
-            rk.store(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
+            // Q e^{gam}, K e^{gam} (one exp) and K e^{gam_C - gam}
+            rq.store3(rk, Qg, Kg, Kd, LDK, [&](int r, int c, float q, float k, float* y) {
+                const float e = gf.G(r, c);
+                y[0] = q * e;
+                y[1] = k * e;
+                y[2] = k * gf.Gd(r, c);
+            });
         } else {
             rq.store(Qg, LDK);
             rk.store(Kg, LDK);
