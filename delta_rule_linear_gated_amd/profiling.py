@@ -37,17 +37,30 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+def _trailing_bools(name: str) -> list:
+    """The bool template arguments at the end of a kernel name, demangled
+    ("..., true, false>(") or mangled ("...Lb1ELb0EEEv")."""
+    m = re.search(r"((?:(?:true|false), )*(?:true|false))>\(", name)
+    if m:
+        return [x == "true" for x in m.group(1).split(", ")]
+    m = re.search(r"((?:Lb[01]E)+)EEv", name)
+    if m:
+        return [x == "1" for x in re.findall(r"Lb([01])E", m.group(1))]
+    return []
+
+
 def kernel_key(name: str) -> str:
-    """Map a demangled rocprofv3 kernel name to the names dn_profile_collect uses."""
+    """Map a rocprofv3 kernel name (demangled or mangled) to the names
+    dn_profile_collect uses."""
     if "prep_kernel" in name:
         return "prep"
     if "fwd_state_kernel" in name:   # <..., SAVE, OUTPUT>
-        if re.search(r"false, false>\(", name):
+        b = _trailing_bools(name)[-2:]
+        if b == [False, False]:
             return "fwd_summary"
-        return "fwd_state" if re.search(r"true, true>\(", name) or re.search(r"false, true>\(", name) \
-            else "fwd_state_recompute"
+        return "fwd_state" if b[-1:] == [True] else "fwd_state_recompute"
     if "bwd_state_kernel" in name:   # <..., SUMMARY>
-        return "bwd_summary" if re.search(r"true>\(", name) else "bwd_state"
+        return "bwd_summary" if _trailing_bools(name)[-1:] == [True] else "bwd_state"
     if "scan_combine_kernel" in name:
         return "scan_combine"
     if "bwd_chunk_kernel" in name:
