@@ -416,7 +416,7 @@ template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_sta
     constexpr size_t E = sizeof(TI);
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
     constexpr int G = GATE == kGateVector ? C * DK : C;
-    constexpr int NK = GATE == kGateVector ? 3 : 2;   // Q, K (+ K Gam_C / Gam)
+    constexpr int NK = GATE == kGateVector ? 3 : 2;   // Q, K (+ K Gam_C / Gam); an upper bound without output
     constexpr int NV = GATE == kGateScalar ? 3 : 2;   // V (then U), R (+ U Gam_C / Gam)
     return 4 * (G + 3 * C) + E * (BV * LDK + NK * C * LDK + NV * C * LDV + 2 * C * LDC) + 96;
 }
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     __shared__ float rowf[2 * C];
     __shared__ __align__(16) float beta_s[C];
     __shared__ __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
-    __shared__ __align__(16) TI Qg[C * LDK];     // Q (vector gate: Q Gam)            [t][c]
+    __shared__ __align__(16) TI Qg[OUTPUT ? C * LDK : 8];   // Q (vector gate: Q Gam)  [t][c]
     __shared__ __align__(16) TI Kg[C * LDK];     // K (vector gate: K Gam)            [t][c]
     __shared__ __align__(16) TI Kd[VEC ? C * LDK : 8];   // K Gam_C / Gam (vector gate) [t][c]
     __shared__ __align__(16) TI Vb[C * LDV];     // V block [t][v]; after (c) U [t][v]
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         const long cc = ((long)bh * p.NT + n) * C * C;
         rg.load(p.gam + row0 * GW, p.beta + row0, valid);
         __builtin_amdgcn_sched_barrier(0);   // gate first, then the tiles, in order (see RegN)
-        rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
+        if constexpr (OUTPUT) rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);   // Q only feeds O
         rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
         rv.load(static_cast<const TI*>(p.v) + row0 * DVr + vcol, DVr, valid);
         if (trans) rv.valid_ = 0;   // stores as zero
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
         rg.commit(rowf, gam_s, beta_s);
         __syncthreads();
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
-        if (VEC) {
+        if (VEC && OUTPUT) {
             // Q e^{gam}, K e^{gam} (one exp) and K e^{gam_C - gam}
             rq.store3(rk, Qg, Kg, Kd, LDK, [&](int r, int c, float q, float k, float* y) {
                 const float e = gf.G(r, c);
@@ -526,8 +526,11 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
                 y[1] = k * e;
                 y[2] = k * gf.Gd(r, c);
             });
+        } else if (VEC) {
+            rk.store(Kg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
+            rk.store(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
         } else {
-            rq.store(Qg, LDK);
+            if constexpr (OUTPUT) rq.store(Qg, LDK);
             rk.store(Kg, LDK);
         }
         rv.store(Vb, LDV);
