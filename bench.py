@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--phase", action="store_true",
                     help="with --decode: the phase-controlled gate (dn_recurrent_phase_fwd, complex state, "
                          "per-channel decay and phase)")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --decode: also time the calls captured in a HIP graph and replayed")
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--decode-tokens", type=int, default=1)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -291,6 +293,7 @@ def decode_bench(args, w0):
     stream = torch.cuda.current_stream(dev)
 
     def call():
+        stream = torch.cuda.current_stream(dev)   # (the capture stream while a graph is captured)
         if args.phase:
             st = B.dn_recurrent_phase_fwd(sh, q, k, v, beta, g, inp["theta"], state, state_im, o, stream)
         else:
@@ -301,15 +304,41 @@ def decode_bench(args, w0):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    B.dn_profile_collect()
-    B.dn_profile_enable(True)
-    t0 = time.perf_counter()
+    t0 = time.perf_counter()           # the timed calls, without timing events
     for _ in range(args.steps):
         call()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    B.dn_profile_collect()              # then the kernel's own duration, from HIP events
+    B.dn_profile_enable(True)
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
     B.dn_profile_enable(False)
     kern = B.dn_profile_collect()
+    graph = None
+    if args.graph:   # calls captured once in a HIP graph and replayed (no per-call launch cost)
+        per = 16
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(per):
+                call()
+        gr.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // per)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            gr.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) * 1e3 / (reps * per)
+        graph = {"calls_per_replay": per, "replays": reps, "ms_per_call": round(gms, 5),
+                 "tokens_per_s": round(w.B * w.T / (gms / 1e3), 1)}
     E = 2 if w.dtype == "bf16" else 4
     gw = w.dk if w.gate == "vector" else (0 if w.gate == "none" else 1)
     heads = w.B * w.H
@@ -364,7 +393,7 @@ def decode_bench(args, w0):
                                f"B={w.B} H={w.H} dk={w.dk} dv={w.dv}, {w.T} token(s) "
                                f"per sequence and call", "global_batch": w.B, "seq_len": w.T, "heads": w.H,
                    "parallelism": "none (1 GPU)"},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "graph_replay": graph, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
