@@ -136,16 +136,18 @@ void bwd_state(const Params& p, int BH, int mode, hipStream_t stream) {
 
 // The forward state pass, through the scan when the plan has segments.
 template <typename TI, int GATE, int C, int D, bool OUTPUT>
-void fwd_state_pass(const Params& p, int BH, bool save, const char* name, const char* sname, hipStream_t stream) {
+hipError_t fwd_state_pass(const Params& p, int BH, bool save, const char* name, const char* sname, hipStream_t stream) {
     if (p.nseg > 1) {
         prof_begin(stream, sname);
         fwd_state<TI, GATE, C, D, OUTPUT>(p, BH, false, 1, stream);
         prof_end(stream);
-        launch_scan_combine(p, D, true, stream);
+        const hipError_t e = launch_scan_combine(p, D, true, stream);
+        if (e != hipSuccess) return e;
     }
     prof_begin(stream, name);
     fwd_state<TI, GATE, C, D, OUTPUT>(p, BH, save, 0, stream);
     prof_end(stream);
+    return hipSuccess;
 }
 
 template <typename TI, int GATE, int C, int D>
@@ -157,8 +159,8 @@ hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t s
         prof_begin(stream, "prep");
         hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
         prof_end(stream);
-        fwd_state_pass<TI, GATE, C, D, true>(p, BH, save, "fwd_state", "fwd_summary", stream);
-        return hipGetLastError();
+        const hipError_t e = fwd_state_pass<TI, GATE, C, D, true>(p, BH, save, "fwd_state", "fwd_summary", stream);
+        return e != hipSuccess ? e : hipGetLastError();
     }
 }
 
@@ -172,13 +174,16 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
             prof_begin(stream, "prep_recompute");
             hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
             prof_end(stream);
-            fwd_state_pass<TI, GATE, C, D, false>(p, BH, true, "fwd_state_recompute", "fwd_summary_recompute", stream);
+            const hipError_t e = fwd_state_pass<TI, GATE, C, D, false>(p, BH, true, "fwd_state_recompute",
+                                                                      "fwd_summary_recompute", stream);
+            if (e != hipSuccess) return e;
         }
         if (p.nseg > 1) {   // the reverse scan: segment summaries of dS, then the combine
             prof_begin(stream, "bwd_summary");
             bwd_state<TI, GATE, C, D>(p, BH, 1, stream);
             prof_end(stream);
-            launch_scan_combine(p, D, false, stream);
+            const hipError_t e = launch_scan_combine(p, D, false, stream);
+            if (e != hipSuccess) return e;
         }
         prof_begin(stream, "bwd_state");
         bwd_state<TI, GATE, C, D>(p, BH, 0, stream);
