@@ -66,6 +66,10 @@ struct Params {
     int nseg, seg_len;
     float* seg_end;
     float* seg_start;
+    // workgroups of the chunk backward resident on the device at once (the
+    // distance, in workgroup ids, to the one that most likely starts next on
+    // the same XCD)
+    int resident;
     // phase-controlled gate (recurrent form only): theta [BH][T][DK] fp32 and the
     // imaginary part of the state [BH][DV][DK] fp32 (the real part is hT)
     const float* theta;

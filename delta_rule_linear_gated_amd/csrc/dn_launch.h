@@ -65,6 +65,18 @@ inline int device_cus() {
     return v;
 }
 
+// Workgroups of kernel f (kThreads threads, static LDS only) resident on one
+// compute unit at once (cached per kernel).
+template <typename F> int resident_per_cu(F* f) {
+    static std::atomic<int> cache{0};
+    int v = cache.load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, f, kThreads, 0) != hipSuccess || v <= 0) v = 1;
+        cache.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 // d_v block of the sequential kernels: the widest of 64, 32, 16 (at most D, and
 // fitting in LDS) whose grid of (D / BV) * BH workgroups still gives every
 // compute unit one; the narrowest when none does (few heads: more, shorter
@@ -188,8 +200,10 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
         prof_begin(stream, "bwd_state");
         bwd_state<TI, GATE, C, D>(p, BH, 0, stream);
         prof_end(stream);
+        Params pc = p;
+        pc.resident = device_cus() * resident_per_cu(bwd_chunk_kernel<TI, GATE, C, D>);
         prof_begin(stream, "bwd_chunk");
-        hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, pc);
         prof_end(stream);
         return hipGetLastError();
     }
