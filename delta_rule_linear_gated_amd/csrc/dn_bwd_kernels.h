@@ -291,8 +291,7 @@ struct BwdChunkSmem {
     static constexpr size_t RED_B = RED_G + al((D / 16) * C * 4);                 // [VB/16][C] row partials (dbeta_R)
     static constexpr size_t RED_C = RED_B + al((VB / 16) * C * 4);                // [C/16][D] column partials
     static constexpr size_t LASTS = RED_C + al((C / 16) * D * 4);                 // [D]
-    static constexpr size_t PART = LASTS + al(D * 4);                             // [D/64 rounded up]
-    static constexpr size_t KCO = PART + 256;                                     // [C] Kaczmarz dk coefficients
+    static constexpr size_t KCO = LASTS + al(D * 4);                              // [C] Kaczmarz dk coefficients
     static constexpr size_t TOTAL = KCO + al(C * 4);
     // dq / dk write-back tiles [C][LD] each at offset 0; d gam of the vector gate
     // [C][D] fp32 after them, written once every phase-C tile is dead
@@ -326,7 +325,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     float* red_r = reinterpret_cast<float*>(smem + L::RED_R);
     float* red_g = reinterpret_cast<float*>(smem + L::RED_G);
     float* red_b = reinterpret_cast<float*>(smem + L::RED_B);
-    float* part_s = reinterpret_cast<float*>(smem + L::PART);
     float* red_c = reinterpret_cast<float*>(smem + L::RED_C);
     float* lastS = reinterpret_cast<float*>(smem + L::LASTS);
     float* dgb = reinterpret_cast<float*>(smem + L::DGB);
@@ -667,12 +665,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                     const f32x4 x = dgm[im * TO::RN + in];
                     sg += x[0] + x[1] + x[2] + x[3];
                 }
-                sb += __shfl_xor(sb, 16);
-                sb += __shfl_xor(sb, 32);
-                if (SCA) {
-                    sg += __shfl_xor(sg, 16);
-                    sg += __shfl_xor(sg, 32);
-                }
+                sb = sum_lane_groups(sb);
+                if (SCA) sg = sum_lane_groups(sg);
                 if (lane_id() < 16) {
                     red_r[TO::rg() * C + TO::col(in)] = sb;
                     if (SCA) red_g[TO::rg() * C + TO::col(in)] = sg;
@@ -683,9 +677,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         if (TX::active()) {
 #pragma unroll
             for (int j = 0; j < TX::PER; ++j) {
-                float sr = dbr_part[j];
-                sr += __shfl_xor(sr, 16);
-                sr += __shfl_xor(sr, 32);
+                const float sr = sum_lane_groups(dbr_part[j]);
                 if (lane_id() < 16) red_b[(TX::m0(j) / 16) * C + TX::col(j)] = sr;
             }
         }
@@ -727,32 +719,20 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         lds_to_global<TI, C, D>(static_cast<TI*>(p.dq) + row0 * D, D, dqs, LD, valid);
         lds_to_global<TI, C, D>(static_cast<TI*>(p.dk) + row0 * D, D, dks, LD, valid);
         if constexpr (GATE != kGateNone) {
-            // gam_C terms: lastS[c] = sum_v S0 dS1 and the Kd dKd column sums; for the
-            // scalar gate their total over c, one partial per wave
-            if (wave_id() < (D + 63) / 64) {
-                const int c = threadIdx.x;
-                float x = 0.f;
-                if (c < D) {
-                    float ssum = 0.f;
-                    for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * D + c];
-                    float cs = 0.f;
-                    for (int b = 0; b < TO::WN; ++b) cs += red_c[b * D + c];
-                    lastS[c] = ssum;
-                    x = gf.GC(c) * ssum + cs;
-                    if (VEC) lastS[c] = fexp(gl[c]) * ssum + cs;   // the whole last-row term of channel c
+            // gam_C terms from sum_v S0 dS1 and the Kd dKd column sums: per channel
+            // (vector gate, lastS), or their total over the channels (scalar gate)
+            if constexpr (VEC) {
+                if (wave_id() < (D + 63) / 64) {
+                    const int c = threadIdx.x;
+                    if (c < D) {
+                        float ssum = 0.f;
+                        for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * D + c];
+                        float cs = 0.f;
+                        for (int b = 0; b < TO::WN; ++b) cs += red_c[b * D + c];
+                        lastS[c] = fexp(gl[c]) * ssum + cs;   // the whole last-row term of channel c
+                    }
                 }
-                if (SCA) {
-                    x = row16_sum(x);
-                    const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0)) +
-                                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16)) +
-                                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32)) +
-                                      __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-                    if (lane_id() == 0) part_s[wave_id()] = tot;
-                }
-            }
-            __syncthreads();
-            // d gam: elementwise terms + the gam_C terms on the last valid row
-            if (VEC) {
+                // d gam: elementwise terms + the gam_C terms on the last valid row
                 if (TO::active()) {
 #pragma unroll
                     for (int j = 0; j < TO::PER; ++j) st4<float>(dgb + TO::col(j) * D + TO::row(j, 0), dgm[j]);
@@ -767,16 +747,31 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                     }
                 }
             } else if (wave_id() == 0) {
+                // one wave, no barrier: the gam_C term summed over the channels
+                // (e^{gam_C} sum_v S0 dS1 + the Kd dKd column sums), then
+                // d gam_t = sum_{s >= t} x_s with that term on the last valid row
+                float xc = 0.f;
+                for (int c = lane_id(); c < D; c += 64) {
+                    float ssum = 0.f;
+                    for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * D + c];
+                    float cs = 0.f;
+                    for (int b = 0; b < TO::WN; ++b) cs += red_c[b * D + c];
+                    xc += gf.GC(c) * ssum + cs;
+                }
+                xc = row16_sum(xc);
+                const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xc), 0)) +
+                                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xc), 16)) +
+                                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xc), 32)) +
+                                  __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xc), 48));
                 const int t = lane_id();
                 float x = 0.f;
                 if (t < valid) {
                     for (int b = 0; b < TO::WM; ++b) x += red_g[b * C + t];
-                    if (t == valid - 1)
-                        for (int w = 0; w < (D + 63) / 64; ++w) x += part_s[w];
+                    if (t == valid - 1) x += tot;
                 }
-                // reverse inclusive scan over the 64 lanes, dg_t = sum_{s >= t} x_s: within
-                // each row of 16 lanes by DPP row shifts (lane i adds lane i + n of its row,
-                // 0 past the row end), then the totals of the later rows
+                // reverse inclusive scan over the 64 lanes: within each row of 16
+                // lanes by DPP row shifts (lane i adds lane i + n of its row, 0 past
+                // the row end), then the totals of the later rows
                 x += dpp_f<0x101>(x);
                 x += dpp_f<0x102>(x);
                 x += dpp_f<0x104>(x);

@@ -702,6 +702,22 @@ __device__ __forceinline__ void head_and_block(int nblk, int BH, int& bh, int& b
     }
 }
 
+// Sum of x over the lanes l, l ^ 16, l ^ 32, l ^ 48 (one column of the four
+// lane groups), in every lane.  v_permlane16_swap (v_permlane32_swap) given x
+// twice returns, in each lane, its own x and that of lane l ^ 16 (l ^ 32): the
+// partner's value is the first result in the upper half of each pair of lane
+// groups, the second in the lower half.  VALU only; a __shfl_xor is an LDS round
+// trip.
+__device__ __forceinline__ float sum_lane_groups(float x) {
+    const int l = lane_id();
+    unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x += __builtin_bit_cast(float, (l & 16) ? a[0] : a[1]);
+    u = __builtin_bit_cast(unsigned, x);
+    const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return x + __builtin_bit_cast(float, (l & 32) ? b[0] : b[1]);
+}
+
 // x as seen from another lane of the same row of 16 lanes, by a DPP control:
 // quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2),
 // row_half_mirror = 0x141 (lane i of 8 <- 7 - i), row_mirror = 0x140 (i of 16 <- 15 - i).
