@@ -546,9 +546,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         // and consumed only at the end, so nothing waits for them.
         int warm[2];
         {
-            const int ids = gridDim.x * gridDim.y;
-            const int nid = min((int)(blockIdx.y * gridDim.x + blockIdx.x) + p.resident, ids - 1);
-            const int nbh = nid / gridDim.x, nn = nid - nbh * gridDim.x;
+            const long ids = (long)gridDim.x * gridDim.y;
+            const long nid = min((long)blockIdx.y * gridDim.x + blockIdx.x + p.resident, ids - 1);
+            const int nbh = (int)(nid / gridDim.x), nn = (int)(nid - (long)nbh * gridDim.x);
             const int nvalid = min(C, p.T - nn * C);
             const long nrow0 = (long)nbh * p.T + (long)nn * C;
             const long nchunk = (long)nbh * p.NT + nn;
