@@ -514,9 +514,11 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
 #pragma unroll
             for (int j = 0; j < TS::PER; ++j) st4<TI>(Ss + TS::col(j) * LDK + TS::row(j, 0), S[j]);
         }
-        // (b) commit this chunk's tiles to LDS
+        // (b) commit this chunk's tiles to LDS (the barrier ending the previous
+        // chunk ordered these writes after its reads; only the vector gate's
+        // scaling below reads the gate just committed)
         rg.commit(rowf, gam_s, beta_s);
-        __syncthreads();
+        if constexpr (VEC) __syncthreads();
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (VEC && OUTPUT) {
             // Q e^{gam}, K e^{gam} (one exp) and K e^{gam_C - gam}
