@@ -173,7 +173,19 @@ void prep_kernel(Params p) {
     const TI* __restrict__ q = static_cast<const TI*>(p.q) + row0 * DK;
     const TI* __restrict__ k = static_cast<const TI*>(p.k) + row0 * DK;
     const float* __restrict__ beta = p.beta + row0;
+    // the chunk's gate and beta first (lane t, every wave, branch-free): the scan
+    // below waits for them, the K / Q tiles are needed only after it
+    const int tl = min(lane_id(), valid - 1);
+    const float g_in = GATE == kGateScalar ? p.g[row0 + tl] : 0.f;
+    const float b_in = beta[tl];
     RegN<TI, C, DK> rq, rk;
+    // Kaczmarz step: eta of the rows whose key norms this thread finishes (below);
+    // branch-free, from beta (a valid array) when there is no Kaczmarz step
+    float eta_in[RegN<TI, C, DK>::PER];
+    const float* __restrict__ eta = (p.kz ? p.eta : p.beta) + row0;
+#pragma unroll
+    for (int i = 0; i < RegN<TI, C, DK>::PER; ++i)
+        eta_in[i] = eta[min(RegN<TI, C, DK>::idx_of(i) / RegN<TI, C, DK>::VPR, valid - 1)];
     rq.load(q, DK, valid);
     rk.load(k, DK, valid);
 
@@ -181,13 +193,19 @@ void prep_kernel(Params p) {
     if (GATE == kGateScalar) {
         if (wave_id() == 0) {
             const int t = lane_id();
-            const float g = p.g[row0 + (t < valid ? t : valid - 1)];
-            float x = t < valid ? g : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (t >= off) x += y;
-            }
+            float x = t < valid ? g_in : 0.f;
+            // inclusive prefix sum over the 64 lanes: within each row of 16 lanes by
+            // DPP row shifts (lane i adds lane i - n of its row, 0 before the row
+            // start), then the totals of the earlier rows
+            x += dpp_f<0x111>(x);
+            x += dpp_f<0x112>(x);
+            x += dpp_f<0x114>(x);
+            x += dpp_f<0x118>(x);
+            const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+            const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+            const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+            const int row = t >> 4;
+            x += (row > 0 ? r0 : 0.f) + (row > 1 ? r1 : 0.f) + (row > 2 ? r2 : 0.f);
             if (t < C) {
                 gam_s[t] = x;
                 if (t < valid) p.gam[row0 + t] = x;
@@ -243,7 +261,7 @@ void prep_kernel(Params p) {
             const int idx = threadIdx.x + i * kThreads, row = idx / RK::VPR;
             if (idx < RK::NV && idx % RK::VPR == 0) {
                 const float rn = 1.f / (ss + p.eps);
-                const float b = row < valid ? p.eta[row0 + row] * rn : 0.f;
+                const float b = row < valid ? eta_in[i] * rn : 0.f;
                 beta_s[row] = b;
                 if (row < valid) {
                     p.kb[row0 + row] = b;
@@ -252,7 +270,7 @@ void prep_kernel(Params p) {
             }
         }
     } else {
-        for (int t = threadIdx.x; t < C; t += kThreads) beta_s[t] = beta[t < valid ? t : valid - 1] * (t < valid ? 1.f : 0.f);
+        if ((int)threadIdx.x < C) beta_s[threadIdx.x] = (int)threadIdx.x < valid ? b_in : 0.f;
     }
     __syncthreads();
 
