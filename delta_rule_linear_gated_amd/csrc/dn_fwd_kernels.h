@@ -178,6 +178,15 @@ void prep_kernel(Params p) {
     const int tl = min(lane_id(), valid - 1);
     const float g_in = GATE == kGateScalar ? p.g[row0 + tl] : 0.f;
     const float b_in = beta[tl];
+    // vector gate: the RS rows of one channel this thread's cumsum segment covers
+    // (see below), also loaded ahead of the K / Q tiles
+    constexpr int RSV = VEC ? C / L::NSEG : 1;
+    float gx[RSV];
+    if constexpr (VEC) {
+        const int c = threadIdx.x % DK, seg = min((int)threadIdx.x / DK, L::NSEG - 1);
+#pragma unroll
+        for (int r = 0; r < RSV; ++r) gx[r] = p.g[(row0 + min(seg * RSV + r, valid - 1)) * DK + c];
+    }
     RegN<TI, C, DK> rq, rk;
     // Kaczmarz step: eta of the rows whose key norms this thread finishes (below);
     // branch-free, from beta (a valid array) when there is no Kaczmarz step
@@ -211,21 +220,18 @@ void prep_kernel(Params p) {
                 if (t < valid) p.gam[row0 + t] = x;
             }
         }
-    } else if (GATE == kGateVector) {
+    } else if constexpr (GATE == kGateVector) {
         // per-channel cumsum in two levels: NSEG segments of RS rows per channel, one
-        // thread each (branch-free loads of its RS rows, a local prefix sum), then the
+        // thread each (its RS rows, loaded above, and a local prefix sum), then the
         // totals of the earlier segments
         constexpr int NSEG = L::NSEG, RS = C / NSEG;
         float* tot = reinterpret_cast<float*>(smem + L::TOT);
         const int c = threadIdx.x % DK, seg = threadIdx.x / DK;
         float x[RS];
+        static_assert(RS == RSV, "segment rows");
         if (seg < NSEG) {
 #pragma unroll
-            for (int r = 0; r < RS; ++r) {
-                const int t = seg * RS + r;
-                const float gv = p.g[(row0 + (t < valid ? t : valid - 1)) * DK + c];
-                x[r] = t < valid ? gv : 0.f;
-            }
+            for (int r = 0; r < RS; ++r) x[r] = seg * RS + r < valid ? gx[r] : 0.f;
 #pragma unroll
             for (int r = 1; r < RS; ++r) x[r] += x[r - 1];
             tot[seg * DK + c] = x[RS - 1];
