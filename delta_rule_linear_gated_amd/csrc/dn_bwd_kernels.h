@@ -105,15 +105,23 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     const int vcol = trans ? 0 : v0;   // (transition rows load a valid dO block and zero it)
 
     RegN<TI, C, DK> rq, rk;
-    RegN<TI, C, BV> rdo;
+    using RDO = RegN<TI, C, BV>;
+    RDO rdo;
     RegN<TI, C, C> rP, rT;
     GateRegs<GATE, C, DK> rg;
+    // scalar gate: gam of the rows of this thread's dO vectors (dO e^{gam} is formed
+    // from registers, so the commit needs no barrier between the gate and the tiles)
+    float gdo[SCA ? RDO::PER : 1];
     auto prefetch = [&](int n) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
         const long row0 = (long)bh * p.T + t0;
         const long cc = ((long)bh * p.NT + n) * C * C;
         rg.load(p.gam + row0 * GW, p.beta + row0, valid);
+        if constexpr (SCA) {
+#pragma unroll
+            for (int i = 0; i < RDO::PER; ++i) gdo[i] = p.gam[row0 + min(RDO::idx_of(i) / RDO::VPR, valid - 1)];
+        }
         __builtin_amdgcn_sched_barrier(0);   // gate first, then the tiles, in order (see RegN)
         rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
         rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
@@ -134,9 +142,11 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
 #pragma unroll
             for (int j = 0; j < TS::PER; ++j) st4<TI>(dSs + TS::col(j) * LDK + TS::row(j, 0), dS[j]);
         }
-        // (b) commit this chunk's tiles
+        // (b) commit this chunk's tiles (the barrier ending the previous chunk ordered
+        // these writes after its reads; only the vector gate's scaling below reads the
+        // gate just committed)
         rg.commit(rowf, gam_s, beta_s);
-        __syncthreads();
+        if constexpr (VEC) __syncthreads();
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (VEC) {
             // K e^{gam_C - gam}, -K e^{gam} and Q e^{gam} (one exp for the last two)
@@ -151,7 +161,12 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
             rq.store(Qg, LDK);
         }
         rdo.store(dOb, LDV);
-        if (SCA) rdo.store(dOg, LDV, [&](int r, int, float x) { return x * rowf[r]; });
+        if constexpr (SCA) {
+            float eg[RDO::PER];
+#pragma unroll
+            for (int i = 0; i < RDO::PER; ++i) eg[i] = fexp(gdo[i]);
+            rdo.store_scaled(dOg, LDV, eg);
+        }
         rP.store(Pl, LDC);
         rT.store(Tl, LDC);
         // lambda and dv of the chunk done last iteration (in Lb / Db until (d) below)

@@ -506,6 +506,27 @@ template <typename T, int ROWS, int COLS> struct RegN {
             *reinterpret_cast<uint4*>(lds + row * ldl + c0) = row < valid_ ? pin(r[i]) : zero_u4();
         }
     }
+    // Every vector times a factor of its own, s[i] (rows >= valid as zero).
+    __device__ __forceinline__ void store_scaled(T* lds, int ldl, const float (&s)[PER]) const {
+        uint4 outv[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = idx_of(i);
+            const int row = idx / VPR;
+            const uint4 ri = pin(r[i]);
+            const T* src = reinterpret_cast<const T*>(&ri);
+            T* out = reinterpret_cast<T*>(&outv[i]);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) out[e] = from_f<T>(row < valid_ ? to_f(src[e]) * s[i] : 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            if (idx >= NV) continue;
+            const int row = idx / VPR, c0 = (idx % VPR) * VW;
+            *reinterpret_cast<uint4*>(lds + row * ldl + c0) = outv[i];
+        }
+    }
     // Three tiles from this one (a) and another of the same shape (b) in one
     // two-phase pass: f(row, col, a, b, y) fills y[0..2] for tiles l0, l1, l2, so
     // a factor the three share (a per-element gate) is computed once.
