@@ -753,12 +753,33 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                     for (int j = 0; j < TO::PER; ++j) st4<float>(dgb + TO::col(j) * D + TO::row(j, 0), dgm[j]);
                 }
                 __syncthreads();
-                for (int c = threadIdx.x; c < D; c += kThreads) {
+                // d gam_t = sum_{s >= t} per channel, in NSG segments of RSG rows (one
+                // thread each: the suffix sums of its rows), then the totals of the
+                // later segments (through red_c, dead since lastS was formed)
+                constexpr int NSG = kThreads / D < C / 16 ? kThreads / D : C / 16;
+                constexpr int RSG = C / NSG;
+                static_assert(NSG >= 1 && NSG * D <= kThreads && C % NSG == 0, "segments");
+                const int c = threadIdx.x % D, sg = threadIdx.x / D;
+                float sfx[RSG];
+                if (sg < NSG) {
                     const float last = lastS[c];
                     float acc = 0.f;
-                    for (int t = valid - 1; t >= 0; --t) {
-                        acc += dgb[t * D + c] + (t == valid - 1 ? last : 0.f);
-                        p.dg[(row0 + t) * D + c] = acc;
+#pragma unroll
+                    for (int r = RSG - 1; r >= 0; --r) {
+                        const int t = sg * RSG + r;
+                        acc += t < valid ? dgb[t * D + c] + (t == valid - 1 ? last : 0.f) : 0.f;
+                        sfx[r] = acc;
+                    }
+                    red_c[sg * D + c] = acc;
+                }
+                __syncthreads();
+                if (sg < NSG) {
+                    float off = 0.f;
+                    for (int s2 = sg + 1; s2 < NSG; ++s2) off += red_c[s2 * D + c];
+#pragma unroll
+                    for (int r = 0; r < RSG; ++r) {
+                        const int t = sg * RSG + r;
+                        if (t < valid) p.dg[(row0 + t) * D + c] = sfx[r] + off;
                     }
                 }
             } else if (wave_id() == 0) {
