@@ -556,9 +556,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         // Warm the caches for the workgroup that most likely starts next on this
         // XCD: workgroups start in id order and go to the XCDs round-robin, so it
         // is this id plus the number resident at once.  One dword of every
-        // 128-byte line of its prologue tiles (K, T and the first two d_v blocks of
-        // S0, dS1, lambda, dO and V; up to 2 lines per thread), held in registers
-        // and consumed only at the end, so nothing waits for them.
+        // 128-byte line of its prologue tiles (K, T, the first two d_v blocks of
+        // S0, dS1, lambda, dO and V, the gate and beta rows; up to 2 lines per
+        // thread), held in registers and consumed only at the end, so nothing
+        // waits for them.
         int warm[2];
         {
             const long ids = (long)gridDim.x * gridDim.y;
@@ -571,8 +572,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             constexpr int LPR = (NB * VB * E + 127) / 128;   // lines per row of the lambda / dO / V blocks
             const int nK = (nvalid * D * E + 127) / 128;
             constexpr int nT = (C * C * E + 127) / 128, nS = (NB * VB * D * E + 127) / 128;
+            const int nG = (nvalid * GW * 4 + 127) / 128, nB = (nvalid * 4 + 127) / 128;   // gate and beta rows
             const int b1 = nK, b2 = b1 + nT, b3 = b2 + nS, b4 = b3 + nS, b5 = b4 + C * LPR, b6 = b5 + nvalid * LPR,
-                      nl = b6 + nvalid * LPR;
+                      b7 = b6 + nvalid * LPR, b8 = b7 + (GATE != kGateNone ? nG : 0), nl = b8 + nB;
             const char* kb = reinterpret_cast<const char*>(static_cast<const TI*>(p.k) + nrow0 * D);
             const char* tb = reinterpret_cast<const char*>(static_cast<const TI*>(p.Tm) + nchunk * C * C);
             const char* sb = reinterpret_cast<const char*>(static_cast<const TI*>(p.states) + nchunk * D * D);
@@ -580,17 +582,24 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             const char* lb = reinterpret_cast<const char*>(static_cast<const TI*>(p.lam) + nchunk * C * D);
             const char* ob = reinterpret_cast<const char*>(static_cast<const TI*>(p.dout) + nrow0 * D);
             const char* vb = reinterpret_cast<const char*>(static_cast<const TI*>(p.v) + nrow0 * D);
+            const char* gb = reinterpret_cast<const char*>(p.gam + nrow0 * GW);
+            const char* bb = reinterpret_cast<const char*>(p.beta + nrow0);
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int i = min((int)threadIdx.x + r * kThreads, nl - 1);
-                const int s = i < b4 ? 0 : (i < b5 ? 1 : (i < b6 ? 2 : 3));
+                const int s = i < b4 ? 0 : (i < b5 ? 1 : (i < b6 ? 2 : (i < b7 ? 3 : 4)));
                 const int j = i - (s == 0 ? 0 : (s == 1 ? b4 : (s == 2 ? b5 : b6)));
-                // contiguous segments (K, T, S0, dS1) by line; row segments by row and line
+                // contiguous segments (K, T, S0, dS1, gate, beta) by line; row segments by
+                // row and line
                 const char* base = s == 1 ? lb : (s == 2 ? ob : vb);
                 long off = (long)(j / LPR) * D * E + (j % LPR) * 128;
                 if (s == 0) {
                     base = i < b1 ? kb : (i < b2 ? tb : (i < b3 ? sb : db));
                     off = (long)(i - (i < b1 ? 0 : (i < b2 ? b1 : (i < b3 ? b2 : b3)))) * 128;
+                }
+                if (s == 4) {
+                    base = i < b8 ? gb : bb;
+                    off = (long)(i - (i < b8 ? b7 : b8)) * 128;
                 }
                 warm[r] = *reinterpret_cast<const int*>(base + off);
             }
