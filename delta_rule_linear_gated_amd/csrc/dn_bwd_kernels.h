@@ -309,13 +309,14 @@ struct BwdChunkSmem {
     static constexpr size_t KCO = LASTS + al(D * 4);                              // [C] Kaczmarz dk coefficients
     static constexpr size_t TOTAL = KCO + al(C * 4);
     // dq / dk write-back tiles [C][LD] each at offset 0; d gam of the vector gate
-    // [C][D] fp32 after them, written once every phase-C tile is dead
+    // [C][LDG] fp32 after them, written once every phase-C tile is dead
     static constexpr size_t DGB = al(2 * C * LD * E);
-    static_assert(!VEC || DGB + C * D * 4 <= BIG_END, "d gam buffer");
+    static constexpr int LDG = D + 4;   // d gam rows (fp32, padded: its accumulator stores stay conflict-free)
+    static_assert(!VEC || DGB + C * LDG * 4 <= BIG_END, "d gam buffer");
     // per-thread partials of sum_v S0 dS1 [row blocks of the S0 register tile][D] fp32,
     // beside the write-back tiles (and d gam)
     using RS = RegB<TI, VB, D>;
-    static constexpr size_t LSRED = VEC ? DGB + al(C * D * 4) : DGB;
+    static constexpr size_t LSRED = VEC ? DGB + al(C * LDG * 4) : DGB;
     static_assert(LSRED + RS::BR * D * 4 <= BIG_END, "S0 dS1 partials");
     static_assert(2 * C * LD * E <= BIG_END, "write-back tiles");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
@@ -759,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 // d gam: elementwise terms + the gam_C terms on the last valid row
                 if (TO::active()) {
 #pragma unroll
-                    for (int j = 0; j < TO::PER; ++j) st4<float>(dgb + TO::col(j) * D + TO::row(j, 0), dgm[j]);
+                    for (int j = 0; j < TO::PER; ++j) st4<float>(dgb + TO::col(j) * L::LDG + TO::row(j, 0), dgm[j]);
                 }
                 __syncthreads();
                 // d gam_t = sum_{s >= t} per channel, in NSG segments of RSG rows (one
@@ -776,7 +777,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
 #pragma unroll
                     for (int r = RSG - 1; r >= 0; --r) {
                         const int t = sg * RSG + r;
-                        acc += t < valid ? dgb[t * D + c] + (t == valid - 1 ? last : 0.f) : 0.f;
+                        acc += t < valid ? dgb[t * L::LDG + c] + (t == valid - 1 ? last : 0.f) : 0.f;
                         sfx[r] = acc;
                     }
                     red_c[sg * D + c] = acc;
