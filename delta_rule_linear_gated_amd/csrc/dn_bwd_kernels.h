@@ -297,9 +297,11 @@ struct BwdChunkSmem {
     static constexpr size_t KL = KR + al(C * LD * E);                // K e^{gam-c}    [C][LD] (vector)
     static constexpr size_t C_END = VEC ? KL + al(C * LD * E) : KR;
     static constexpr size_t BIG_END = LOOP_END > C_END ? LOOP_END : C_END;
-    // small fp32 arrays
-    static constexpr size_t GAM = al(BIG_END);                                    // gam [C][D] or [C]
-    static constexpr size_t ROWF = GAM + al(VEC ? C * D * 4 : C * 4);             // [2][C] (scalar)
+    // small fp32 arrays; the vector gate's gam rows padded (LDGM floats): its
+    // per-element factors are read a column of 16 rows at a time
+    static constexpr int LDGM = D + 4;
+    static constexpr size_t GAM = al(BIG_END);                                    // gam [C][LDGM] or [C]
+    static constexpr size_t ROWF = GAM + al(VEC ? C * LDGM * 4 : C * 4);          // [2][C] (scalar)
     static constexpr size_t BETA = ROWF + al(2 * C * 4);                          // [C]
     static constexpr size_t RED_R = BETA + al(C * 4);                             // [D/16][C] row partials (dbeta_A)
     static constexpr size_t RED_G = RED_R + al((D / 16) * C * 4);                 // [D/16][C] row partials (d gam)
@@ -388,9 +390,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     if (NVB > 1) load_block(rb[1], 1);
     // sum_v S0[v][c] dS1[v][c] over this thread's rows of every block
     float ls[L::RS::PER][L::RS::VW] = {};
-    rg.commit(rowf, gam_s, beta_s);
+    rg.commit(rowf, gam_s, beta_s, L::LDGM);
     __syncthreads();
-    const GateLds<GATE, C, D> gf{rowf, gam_s, valid - 1};
+    const GateLds<GATE, C, D, L::LDGM> gf{rowf, gam_s, valid - 1};
     if (VEC)
         rK.store(KG, LD, [&](int r, int c, float x) { return x * gf.G(r, c); });
     else
@@ -530,12 +532,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         // K rows: the loop's K tile without a vector gate, else K e^{c - gam} / K e^{gam - c}
         TI* Kr = VEC ? reinterpret_cast<TI*>(smem + L::KR) : KG;
         TI* Kl = VEC ? reinterpret_cast<TI*>(smem + L::KL) : KG;
-        const float* gl = gam_s + (valid - 1) * GW;
+        const float* gl = gam_s + (valid - 1) * (VEC ? L::LDGM : GW);
         // fp = e^{gam - centre} (vector gate; 1 otherwise), centre = gam_C / 2
-        auto fpl = [&](int t, int c) -> float { return VEC ? fexp(gam_s[t * D + c] - 0.5f * gl[c]) : 1.f; };
+        auto fpl = [&](int t, int c) -> float { return VEC ? fexp(gam_s[t * L::LDGM + c] - 0.5f * gl[c]) : 1.f; };
         auto fp4 = [&](int t, int c0) -> f32x4 {
             if constexpr (VEC) {
-                const f32x4 g4 = ld4<float>(gam_s + t * D + c0), c4 = ld4<float>(gl + c0);
+                const f32x4 g4 = ld4<float>(gam_s + t * L::LDGM + c0), c4 = ld4<float>(gl + c0);
                 return f32x4{fexp(g4[0] - 0.5f * c4[0]), fexp(g4[1] - 0.5f * c4[1]), fexp(g4[2] - 0.5f * c4[2]),
                              fexp(g4[3] - 0.5f * c4[3])};
             } else {

@@ -380,7 +380,8 @@ template <int GATE, int C, int DK> struct GateRegs {
         }
         if (VEC) gv.load_clamped(gam, DK, valid);
     }
-    __device__ __forceinline__ void commit(float* rowf, float* gam_s, float* beta_s) const {
+    // ldg: row stride of gam_s (vector gate)
+    __device__ __forceinline__ void commit(float* rowf, float* gam_s, float* beta_s, int ldg = DK) const {
         const int t = threadIdx.x;
         if (t < C) beta_s[t] = t < valid_ ? b : 0.f;
         if (GATE == kGateScalar && t < C) {
@@ -388,12 +389,12 @@ template <int GATE, int C, int DK> struct GateRegs {
             rowf[C + t] = fexp(gC - gs);
             gam_s[t] = gs;
         }
-        if (VEC) gv.store(gam_s, DK);
+        if (VEC) gv.store(gam_s, ldg);
     }
 };
 
 // Decay factors read back from LDS after GateRegs::commit.
-template <int GATE, int C, int DK> struct GateLds {
+template <int GATE, int C, int DK, int LDG = DK> struct GateLds {   // LDG: row stride of gam_s (vector gate)
     const float* rowf;
     const float* gam_s;
     int last;                  // valid - 1
@@ -402,19 +403,19 @@ template <int GATE, int C, int DK> struct GateLds {
     __device__ __forceinline__ float G(int t, int c) const {
         if (GATE == kGateNone) return 1.f;
         if (GATE == kGateScalar) return rowf[t];
-        return fexp(gam_s[t * DK + c]);
+        return fexp(gam_s[t * LDG + c]);
     }
     // e^{gam_C[c] - gam[t][c]}
     __device__ __forceinline__ float Gd(int t, int c) const {
         if (GATE == kGateNone) return 1.f;
         if (GATE == kGateScalar) return rowf[C + t];
-        return fexp(gam_s[last * DK + c] - gam_s[t * DK + c]);
+        return fexp(gam_s[last * LDG + c] - gam_s[t * LDG + c]);
     }
     // e^{gam_C[c]}
     __device__ __forceinline__ float GC(int c) const {
         if (GATE == kGateNone) return 1.f;
         if (GATE == kGateScalar) return rowf[last];
-        return fexp(gl ? gl[c] : gam_s[last * DK + c]);
+        return fexp(gl ? gl[c] : gam_s[last * LDG + c]);
     }
 };
 
