@@ -315,11 +315,12 @@ struct BwdChunkSmem {
     static constexpr size_t DGB = al(2 * C * LD * E);
     static constexpr int LDG = D + 4;   // d gam rows (fp32, padded: its accumulator stores stay conflict-free)
     static_assert(!VEC || DGB + C * LDG * 4 <= BIG_END, "d gam buffer");
-    // per-thread partials of sum_v S0 dS1 [row blocks of the S0 register tile][D] fp32,
+    // per-thread partials of sum_v S0 dS1 [row blocks of the S0 register tile][LDS_] fp32,
     // beside the write-back tiles (and d gam)
     using RS = RegB<TI, VB, D>;
+    static constexpr int LDS_ = D + 4;   // rows of the partials (padded: eight lanes store to eight rows)
     static constexpr size_t LSRED = VEC ? DGB + al(C * LDG * 4) : DGB;
-    static_assert(LSRED + RS::BR * D * 4 <= BIG_END, "S0 dS1 partials");
+    static_assert(LSRED + RS::BR * LDS_ * 4 <= BIG_END, "S0 dS1 partials");
     static_assert(2 * C * LD * E <= BIG_END, "write-back tiles");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -715,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 if (L::RS::owns(i)) {
 #pragma unroll
                     for (int kk = 0; kk < L::RS::VW; kk += 4)
-                        st4<float>(lsred + L::RS::rowblk(i) * D + L::RS::col0(i) + kk,
+                        st4<float>(lsred + L::RS::rowblk(i) * L::LDS_ + L::RS::col0(i) + kk,
                                    f32x4{ls[i][kk], ls[i][kk + 1], ls[i][kk + 2], ls[i][kk + 3]});
                 }
             }
@@ -753,7 +754,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                     const int c = threadIdx.x;
                     if (c < D) {
                         float ssum = 0.f;
-                        for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * D + c];
+                        for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * L::LDS_ + c];
                         float cs = 0.f;
                         for (int b = 0; b < TO::WN; ++b) cs += red_c[b * D + c];
                         lastS[c] = fexp(gl[c]) * ssum + cs;   // the whole last-row term of channel c
@@ -801,7 +802,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 float xc = 0.f;
                 for (int c = lane_id(); c < D; c += 64) {
                     float ssum = 0.f;
-                    for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * D + c];
+                    for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * L::LDS_ + c];
                     float cs = 0.f;
                     for (int b = 0; b < TO::WN; ++b) cs += red_c[b * D + c];
                     xc += gf.GC(c) * ssum + cs;
