@@ -337,6 +337,35 @@ void prep_kernel(Params p) {
     const long cc = ((long)bh * p.NT + n) * C * C;
     lds_to_global<TI, C, C>(static_cast<TI*>(p.Pm) + cc, C, Ps, LC, C);
 
+    // Per-channel gate: warm the caches for the workgroup that most likely starts
+    // next on this XCD (workgroups start in id order and go to the XCDs
+    // round-robin: this id plus the number resident at once): one dword of every
+    // 128-byte line of its K, Q, gate and beta rows, while this one's inverse
+    // runs, consumed only at the end. With a scalar gate or none the three
+    // workgroups resident per CU already hide the loads and warming costs time.
+    int warm[2] = {0, 0};
+    if constexpr (GATE == kGateVector) {
+        const long ids = (long)gridDim.x * gridDim.y;
+        const long nid = min((long)blockIdx.y * gridDim.x + blockIdx.x + p.resident, ids - 1);
+        const int nbh = (int)(nid / gridDim.x), nn = (int)(nid - (long)nbh * gridDim.x);
+        const int nvalid = min(C, p.T - nn * C);
+        const long nrow0 = (long)nbh * p.T + (long)nn * C;
+        constexpr int E = sizeof(TI);
+        const int nK = (nvalid * DK * E + 127) / 128, nG = (nvalid * DK * 4 + 127) / 128;
+        const int b1 = nK, b2 = b1 + nK, b3 = b2 + nG, nl = b3 + (nvalid * 4 + 127) / 128;
+        const char* kb = reinterpret_cast<const char*>(static_cast<const TI*>(p.k) + nrow0 * DK);
+        const char* qb = reinterpret_cast<const char*>(static_cast<const TI*>(p.q) + nrow0 * DK);
+        const char* gb = reinterpret_cast<const char*>(p.g + nrow0 * DK);
+        const char* bb = reinterpret_cast<const char*>((p.kz ? p.eta : p.beta) + nrow0);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int i = min((int)threadIdx.x + r * kThreads, nl - 1);
+            const char* base = i < b1 ? kb : (i < b2 ? qb : (i < b3 ? gb : bb));
+            const long off = (long)(i - (i < b1 ? 0 : (i < b2 ? b1 : (i < b3 ? b2 : b3)))) * 128;
+            warm[r] = *reinterpret_cast<const int*>(base + off);
+        }
+    }
+
     // -- T = (I + A)^{-1}
     unit_lower_inverse<C>(A_s, Ts, LDA, Ysc);
 
@@ -352,6 +381,7 @@ void prep_kernel(Params p) {
             *reinterpret_cast<uint4*>(Tout + r * C + c0) = *reinterpret_cast<const uint4*>(out);
         }
     }
+    asm volatile("" ::"v"(warm[0]), "v"(warm[1]));   // the warming loads' only use
 }
 
 // ---------------------------------------------------------------------------

@@ -65,13 +65,14 @@ inline int device_cus() {
     return v;
 }
 
-// Workgroups of kernel f (kThreads threads, static LDS only) resident on one
-// compute unit at once (cached per kernel).
-template <typename F> int resident_per_cu(F* f) {
+// Workgroups of kernel K (kThreads threads, static LDS only) resident on one
+// compute unit at once. The kernel is a template argument so that each kernel
+// keeps a cache of its own: every kernel here has the same function type.
+template <auto K> int resident_per_cu() {
     static std::atomic<int> cache{0};
     int v = cache.load(std::memory_order_relaxed);
     if (v == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, f, kThreads, 0) != hipSuccess || v <= 0) v = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, K, kThreads, 0) != hipSuccess || v <= 0) v = 1;
         cache.store(v, std::memory_order_relaxed);
     }
     return v;
@@ -168,8 +169,10 @@ hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t s
         return hipErrorInvalidConfiguration;
     } else {
         const int BH = pr.B * pr.H;
+        Params pp = p;   // resident: used by the per-channel gate's cache warming
+        pp.resident = device_cus() * resident_per_cu<prep_kernel<TI, GATE, C, D>>();
         prof_begin(stream, "prep");
-        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, pp);
         prof_end(stream);
         const hipError_t e = fwd_state_pass<TI, GATE, C, D, true>(p, BH, save, "fwd_state", "fwd_summary", stream);
         return e != hipSuccess ? e : hipGetLastError();
@@ -183,8 +186,10 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
     } else {
         const int BH = pr.B * pr.H;
         if (!have_states) {   // recomputation policy: gam, T, P and the states into the workspace
+            Params pp = p;
+            pp.resident = device_cus() * resident_per_cu<prep_kernel<TI, GATE, C, D>>();
             prof_begin(stream, "prep_recompute");
-            hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, pp);
             prof_end(stream);
             const hipError_t e = fwd_state_pass<TI, GATE, C, D, false>(p, BH, true, "fwd_state_recompute",
                                                                       "fwd_summary_recompute", stream);
@@ -201,7 +206,7 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
         bwd_state<TI, GATE, C, D>(p, BH, 0, stream);
         prof_end(stream);
         Params pc = p;
-        pc.resident = device_cus() * resident_per_cu(bwd_chunk_kernel<TI, GATE, C, D>);
+        pc.resident = device_cus() * resident_per_cu<bwd_chunk_kernel<TI, GATE, C, D>>();
         prof_begin(stream, "bwd_chunk");
         hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, pc);
         prof_end(stream);
