@@ -423,8 +423,16 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     zero_acc<C, C>(dA);
     zero_acc<C, C>(dP);
     float dbr_part[TX::PER] = {};   // sum over this lane's 4 v of lambda (V - X) at row t = TX::col(j)
+    // q (and k for the vector gate) for the key-gradient products, loaded at the
+    // start of the last d_v block (whose second register set is free by then; q
+    // is not among the cache-warmed tiles, so it comes from far away)
+    RegN<TI, C, D> rq, rk;
 #pragma unroll
     for (int b = 0; b < NVB; ++b) {
+        if (b == NVB - 1) {
+            rq.load(q, D, valid);
+            if (VEC) rk.load(k, D, valid);
+        }
         TI* S0B = blk(b & 1, L::S0B);
         TI* DS1B = blk(b & 1, L::DS1B);
         TI* LAMB = blk(b & 1, L::LAMB);
@@ -473,11 +481,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         // b + 2) and into RB come after the next block's first barrier
     }
 
-    // q (and k for the vector gate) for the key-gradient products (loads in flight
-    // during the epilogues below)
-    RegN<TI, C, D> rq, rk;
-    rq.load(q, D, valid);
-    if (VEC) rk.load(k, D, valid);
 
     // dq = Gam dQg ; dk+ = -beta Gam dKg ; dk- = Gd dKd   (element c = row, t = col)
     if (TO::active()) {
