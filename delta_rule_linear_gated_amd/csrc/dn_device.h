@@ -527,6 +527,37 @@ template <typename T, int ROWS, int COLS> struct RegN {
             *reinterpret_cast<uint4*>(lds + row * ldl + c0) = outv[i];
         }
     }
+    // Two tiles from this one in one two-phase pass: f(row, col, a, y) fills y[0]
+    // for l0 and y[1] for l1, so a factor both share is computed once.
+    template <class F>
+    __device__ __forceinline__ void store2(T* l0, T* l1, int ldl, F f) const {
+        uint4 o[2][PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = idx_of(i);
+            const int row = idx / VPR, c0 = (idx % VPR) * VW;
+            const uint4 ra = pin(r[i]);
+            const T* sa = reinterpret_cast<const T*>(&ra);
+            T* d0 = reinterpret_cast<T*>(&o[0][i]);
+            T* d1 = reinterpret_cast<T*>(&o[1][i]);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                float y[2];
+                f(row, c0 + e, to_f(sa[e]), y);   // unconditional (see store)
+                const bool ok = row < valid_;
+                d0[e] = from_f<T>(ok ? y[0] : 0.f);
+                d1[e] = from_f<T>(ok ? y[1] : 0.f);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            if (idx >= NV) continue;
+            const int row = idx / VPR, c0 = (idx % VPR) * VW;
+            *reinterpret_cast<uint4*>(l0 + row * ldl + c0) = o[0][i];
+            *reinterpret_cast<uint4*>(l1 + row * ldl + c0) = o[1][i];
+        }
+    }
     // Three tiles from this one (a) and another of the same shape (b) in one
     // two-phase pass: f(row, col, a, b, y) fills y[0..2] for tiles l0, l1, l2, so
     // a factor the three share (a per-element gate) is computed once.

@@ -121,32 +121,45 @@ template <typename TI, int GATE, int C, int DK> struct PrepSmem {
     static constexpr int LC = C + Pad<TI>::value;       // I/O-type C x C rows
     static constexpr int GW = GateLayout<GATE, DK>::GW;
     static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+    // K (or K e^{gam - centre}) and Q; the vector gate's K e^{centre - gam} in KM,
+    // and its Q e^{gam - centre} staged into KP's space once the Gram product
+    // has read KP
     static constexpr size_t KP = 0;
     static constexpr size_t KM = KP + al(C * LDK * sizeof(TI));
-    static constexpr size_t QP = KM + (VEC ? al(C * LDK * sizeof(TI)) : 0);
-    static constexpr size_t R0_END = QP + al(C * LDK * sizeof(TI));
+    static constexpr size_t QP = VEC ? KP : KM;
+    static constexpr size_t R0_END = KM + al(C * LDK * sizeof(TI));
     static constexpr size_t TS = 0;                     // fp32 [C][LDA]
     static constexpr size_t YSC = TS + al(C * LDA * 4); // fp32 [C/16][256]
     static constexpr size_t PS = YSC + al((C / 16) * 256 * 4);   // TI [C][LC]
     static constexpr size_t R0B_END = PS + al(C * LC * sizeof(TI));
     static constexpr size_t R0 = R0_END > R0B_END ? R0_END : R0B_END;
     static constexpr size_t AS = R0;                    // fp32 [C][LDA]
-    // vector gate: segment totals of the per-channel cumsum [NSEG][DK] fp32
+    // gam [C][GW] fp32; the vector gate's shares A's space (dead once the scaled
+    // tiles are staged, before A is written), so that two workgroups fit per CU
+    static constexpr size_t GAM = VEC ? AS : AS + al(C * LDA * 4);
+    static constexpr size_t GAM_END =
+        VEC ? AS + al(C * LDA * 4 > C * GW * 4 ? C * LDA * 4 : C * GW * 4) : GAM + al(C * GW * 4);
+    static constexpr size_t BETA = GAM_END;
+    // vector gate: segment totals of the per-channel cumsum [NSEG][DK] fp32, in
+    // the K tiles' space (dead before K is staged)
     static constexpr int NSEG = (kThreads / DK) < C ? (kThreads / DK) : C;
-    static constexpr size_t GAM = AS + al(C * LDA * 4);
-    static constexpr size_t BETA = GAM + al(C * GW * 4);
-    static constexpr size_t TOT = BETA + al(C * 4);
-    static constexpr size_t TOTAL = TOT + (VEC ? al(NSEG * DK * 4) : 0);
+    static constexpr size_t TOT = KP;
+    static_assert(!VEC || NSEG * DK * 4 <= R0_END, "cumsum totals");
+    static constexpr size_t TOTAL = BETA + al(C * 4);
 };
 
 // ---------------------------------------------------------------------------
 // prep_kernel: grid (NT, BH), one chunk per workgroup: gam, P and T of the
 // chunk (T and P row-major; the reverse pass transposes them while staging).
 // Waves per SIMD prep_kernel is compiled for: three workgroups per compute unit
-// (registers capped at 80) where three fit in LDS, else the default two.  Not
-// below d = 64, where the cap would spill (C = 64, bf16).
+// (registers capped at 80) where three fit in LDS, not below d = 64, where the
+// cap would spill (C = 64, bf16); with the vector gate two (128) where two fit;
+// else the default two waves.
 template <typename TI, int GATE, int C, int DK> constexpr int prep_waves() {
-    return DK >= 64 && 3 * PrepSmem<TI, GATE, C, DK>::TOTAL <= 160 * 1024 ? 3 * kWaves / 4 : kWaves / 4;
+    constexpr size_t T = PrepSmem<TI, GATE, C, DK>::TOTAL;
+    if (DK >= 64 && 3 * T <= 160 * 1024) return 3 * kWaves / 4;
+    if (GATE == kGateVector && 2 * T <= 160 * 1024) return 2 * kWaves / 4;
+    return kWaves / 4;
 }
 
 template <typename TI, int GATE, int C, int DK>
@@ -280,15 +293,15 @@ void prep_kernel(Params p) {
     }
     __syncthreads();
 
-    // -- stage K and Q (centred per-channel factors for the vector gate)
+    // -- stage K and Q (centred per-channel factors for the vector gate; its Q
+    //    after the Gram product, below)
+    const float* gl = gam_s + (valid - 1) * DK;  // gam_C (vector gate)
     if (VEC) {
-        const float* gl = gam_s + (valid - 1) * DK;  // gam_C
-        // K e^{gam - centre}, K e^{centre - gam}, Q e^{gam - centre}: one exp per element
-        rk.store3(rq, Kp, Km, Qp, LDK, [&](int r, int c, float k, float q, float* y) {
+        // K e^{gam - centre}, K e^{centre - gam}: one exp per element
+        rk.store2(Kp, Km, LDK, [&](int r, int c, float k, float* y) {
             const float e = fexp(gam_s[r * DK + c] - 0.5f * gl[c]);
             y[0] = k * e;
             y[1] = __fdividef(k, e);
-            y[2] = q * e;
         });
     } else {
         rk.store(Kp, LDK);
@@ -307,7 +320,18 @@ void prep_kernel(Params p) {
             accp[j] = zero4();
             if (!TL::valid(j) || TL::n0(j) > TL::m0(j)) continue;   // strictly upper tiles are zero
             acc[j] = tile_nt<TI, DK>(Kp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, acc[j]);
-            accp[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, accp[j]);
+            if (!VEC) accp[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, accp[j]);
+        }
+        if constexpr (VEC) {
+            // Q e^{gam - centre} into KP's space once every wave has read KP
+            __syncthreads();
+            rq.store(Qp, LDK, [&](int r, int c, float x) { return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]); });
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < TL::PER; ++j) {
+                if (!TL::valid(j) || TL::n0(j) > TL::m0(j)) continue;
+                accp[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, accp[j]);
+            }
         }
         // gate factors and masks (LDS reads only)
         if (TL::active()) {
