@@ -6,11 +6,20 @@ one batch of synthetic input already resident in HBM, through the C ABI.
 Default workload: Gated DeltaNet, bf16 q/k/v/dO with fp32 gate / beta / state,
 B=8, H=16, T=4096, d_k=d_v=128, chunk 64, states saved by the forward.
 
+Timing: W untimed warmup steps, then K steps bracketed by synchronisations,
+each step bracketed by HIP events on the launch stream (three per step:
+before the forward, between forward and backward, after the backward; no
+events inside the library).  ms_per_step and value use the median step; the
+fwd and bwd medians and the wall-clock mean are reported beside it.  A second
+pass of K steps records events around every kernel launch inside the library
+(dn_profile_enable) for the per-kernel durations behind the roofline.
+
 Prints ONE JSON line: tokens/s (B*T per second, all heads), algorithmic
-TFLOP/s and its fraction of the bf16 dense MFMA peak, the roofline of the
-dominant kernel (algorithmic bytes per launch / average launch time from HIP
-events recorded around each launch on the launch stream), the recomputation
-policy's step time, and the fp64 CPU oracle timed on the host.
+TFLOP/s and its fraction of the dense MFMA peak, the whole step against the
+HBM roof (minimum bytes of the operator), the roofline of the dominant kernel
+(the minimum bytes of the pass it belongs to / its average launch time; its
+own tensor budget beside it), the recomputation policy's step time, and the
+fp64 CPU oracle timed on the host (threaded, and one thread on a smaller sample).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--policy save|recompute]
                     [--no-cpu-baseline] [--gpus 1]
@@ -37,6 +46,22 @@ def algorithmic_flops_per_token_head(C: int, dk: int, dv: int) -> float:
     as triangles, recomputation excluded: forward 2C(dk+dv) + 6 dk dv + C^2/3,
     backward 4C(dk+dv) + 12 dk dv."""
     return (2 * C * (dk + dv) + 6 * dk * dv + C * C / 3) + (4 * C * (dk + dv) + 12 * dk * dv)
+
+
+def algorithmic_bytes_per_token_head(dk: int, dv: int, E: int, gw: int):
+    """Minimum HBM bytes per token and head of (forward, backward): every input
+    read once and every output written once, nothing else (no saved states, no
+    per-chunk intermediates).  E = bytes per I/O element, gw = gate values per
+    step (0 none, 1 scalar, dk per-channel), 4 bytes each.
+      forward : q, k, v read, o written, beta, g read
+      backward: q, k, v, dO read, dq, dk, dv written, beta read, dbeta written,
+                g read, dg written"""
+    fwd = (2 * dk + dv) * E + dv * E + 4 + 4 * gw
+    bwd = (2 * dk + dv) * E + dv * E + (2 * dk + dv) * E + 8 + 8 * gw
+    return fwd, bwd
+
+
+FWD_KERNELS = ("prep", "fwd_state", "fwd_summary")
 
 
 def kernel_budget(name: str, C: int, d: int, E: int, gw: int, saved: bool, kz: bool = False):
@@ -74,8 +99,8 @@ def kernel_budget(name: str, C: int, d: int, E: int, gw: int, saved: bool, kz: b
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gdn_bf16")
     ap.add_argument("--policy", default=None, choices=[None, "save", "recompute"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -158,76 +183,106 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(b):
+    def fwd(b):
         st = B.dn_chunk_fwd(sh, q, k, v, beta, g, h0, b["o"], b["hT"], b["states"], b["wsf"],
                             b["wsf"].numel(), stream)
         if st != B.DN_OK:
             raise B.DnError(st, B.dn_last_error())
+
+    def bwd(b):
         st = B.dn_chunk_bwd(sh, q, k, v, beta, g, h0, do, dhT, b["states"], b["dq"], b["dk"], b["dv"],
                             b["dbeta"], b["dg"], b["dh0"], b["wsb"], b["wsb"].numel(), stream)
         if st != B.DN_OK:
             raise B.DnError(st, B.dn_last_error())
 
-    def timed(pol, steps, warmup, events):
+    def median(xs):
+        s = sorted(xs)
+        m = len(s) // 2
+        return s[m] if len(s) % 2 else 0.5 * (s[m - 1] + s[m])
+
+    def timed(pol, steps, warmup, kernels):
+        """Median step / fwd / bwd ms from per-step HIP events, the wall-clock mean,
+        and (kernels=True) a second pass with per-launch events inside the library."""
         b = buffers(pol)
         for _ in range(warmup):
-            step(b)
+            fwd(b)
+            bwd(b)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
-        if events:
-            B.dn_profile_collect()
-            B.dn_profile_enable(True)
         t0 = time.perf_counter()
-        for _ in range(steps):
-            step(b)
+        for i in range(steps):
+            ev[i][0].record(stream)
+            fwd(b)
+            ev[i][1].record(stream)
+            bwd(b)
+            ev[i][2].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        res = {"median_ms": median([e[0].elapsed_time(e[2]) for e in ev]),
+               "fwd_ms": median([e[0].elapsed_time(e[1]) for e in ev]),
+               "bwd_ms": median([e[1].elapsed_time(e[2]) for e in ev]),
+               "wall_mean_ms": (t1 - t0) * 1e3 / steps}
         kern = {}
-        if events:
+        if kernels:
+            B.dn_profile_collect()
+            B.dn_profile_enable(True)
+            for _ in range(steps):
+                fwd(b)
+                bwd(b)
+            torch.cuda.synchronize()
             B.dn_profile_enable(False)
             kern = B.dn_profile_collect()
         del b
-        return (t1 - t0) * 1e3 / steps, kern
+        return res, kern
 
     print(f"[bench] warmup {args.warmup}, timing {args.steps} steps ({policy})", file=sys.stderr, flush=True)
-    ms, kern = timed(policy, args.steps, args.warmup, events=True)
+    res, kern = timed(policy, args.steps, args.warmup, kernels=True)
+    ms = res["median_ms"]
     tokens = w.B * w.T
     value = tokens / (ms / 1e3)
     fl_th = algorithmic_flops_per_token_head(w.C, w.dk, w.dv)
     tflops = fl_th * w.token_heads / (ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-
-    # roofline of the dominant kernel
     gw = w.dk if w.gate == "vector" else (0 if w.gate == "none" else 1)
+    by_fwd, by_bwd = algorithmic_bytes_per_token_head(w.dk, w.dv, E, gw)
+    step_bytes = (by_fwd + by_bwd) * w.token_heads
+    step_roof = {"algorithmic_bytes": int(step_bytes), "achieved_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1),
+                 "hbm_frac": round(step_bytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                 "fwd_bytes_per_token_head": by_fwd, "bwd_bytes_per_token_head": by_bwd}
+
     per_kernel = {}
     for name, (tot, n) in kern.items():
-        avg_ms = tot / max(n, 1)
-        per_kernel[name] = {"avg_ms": round(avg_ms, 4), "launches": n, "share": None}
+        per_kernel[name] = {"avg_ms": round(tot / max(n, 1), 4), "launches": n, "share": None}
     total_k = sum(t for t, _ in kern.values()) or 1.0
     for name, (tot, n) in kern.items():
         per_kernel[name]["share"] = round(tot / total_k, 3)
+
+    # roofline of the dominant kernel: the minimum bytes of the pass it belongs to
+    # (per token-head, times the token-heads one launch covers) over its average
+    # launch time; the kernel's own tensor budget (which counts the saved states
+    # and per-chunk intermediates it reads and writes) is reported beside it
     roofline = None
     budgeted = [n for n in kern if kernel_budget(n, w.C, w.dk, E, gw, policy == "save", w.kla)]
-    if budgeted:   # the costliest kernel with an algorithmic budget (not the scan's small combine)
+    if budgeted:   # the costliest kernel with a budget (not the scan's small combine)
         dom = max(budgeted, key=lambda n: kern[n][0])
         fl, by = kernel_budget(dom, w.C, w.dk, E, gw, policy == "save", w.kla)
-        units = w.B * w.H * NT                      # chunk-heads per launch
+        chunks = w.B * w.H * NT                      # chunk-heads per launch
+        units = w.token_heads                        # token-heads per launch
         avg_s = kern[dom][0] / kern[dom][1] / 1e3
-        ach_gbs = by * units / avg_s / 1e9
-        ach_tf = fl * units / avg_s / 1e12
-        intensity = fl / by
-        ridge = peak * 1e3 / PEAK_HBM_GBS
-        if intensity < ridge:
-            roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                        "algorithmic_bytes_per_launch": int(by * units),
-                        "algorithmic_flops_per_launch": int(fl * units),
-                        "achieved_tflops": round(ach_tf, 2), "avg_launch_ms": round(avg_s * 1e3, 4)}
-        else:
-            roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach_tf, 2), "peak": peak,
-                        "unit": "TFLOP/s", "frac": round(ach_tf / peak, 4), "traffic": None,
-                        "algorithmic_bytes_per_launch": int(by * units),
-                        "algorithmic_flops_per_launch": int(fl * units),
-                        "achieved_gbs": round(ach_gbs, 1), "avg_launch_ms": round(avg_s * 1e3, 4)}
+        alg_per_unit = by_fwd if dom in FWD_KERNELS else by_bwd
+        alg = alg_per_unit * units
+        ach_gbs = alg / avg_s / 1e9
+        kb_gbs = by * chunks / avg_s / 1e9
+        ach_tf = fl * chunks / avg_s / 1e12
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                    "algorithmic_bytes_per_launch": int(alg),
+                    "algorithmic_bytes_per_token_head": alg_per_unit, "token_heads_per_launch": units,
+                    "avg_launch_ms": round(avg_s * 1e3, 4),
+                    "kernel_budget": {"bytes_per_launch": int(by * chunks), "achieved_gbs": round(kb_gbs, 1),
+                                      "frac": round(kb_gbs / PEAK_HBM_GBS, 4)},
+                    "kernel_flops_per_launch": int(fl * chunks), "achieved_tflops": round(ach_tf, 2),
+                    "mfma_frac": round(ach_tf / peak, 4)}
 
     # measured HBM traffic of the dominant kernel, from the committed rocprofv3
     # summary of this workload -- only while the kernel sources are unchanged
@@ -243,8 +298,10 @@ def main():
     other = None
     if not args.no_recompute_leg and w.B * w.H * w.T > 0:
         pol2 = "recompute" if policy == "save" else "save"
-        ms2, _ = timed(pol2, max(1, args.steps // 2), 2, events=False)
-        other = {"policy": pol2, "ms_per_step": round(ms2, 4), "tokens_per_s": round(tokens / (ms2 / 1e3), 1)}
+        r2, _ = timed(pol2, max(10, args.steps // 2), 3, kernels=False)
+        ms2 = r2["median_ms"]
+        other = {"policy": pol2, "ms_per_step": round(ms2, 4), "fwd_ms": round(r2["fwd_ms"], 4),
+                 "bwd_ms": round(r2["bwd_ms"], 4), "tokens_per_s": round(tokens / (ms2 / 1e3), 1)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -253,6 +310,8 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "fwd_ms": round(res["fwd_ms"], 4), "bwd_ms": round(res["bwd_ms"], 4),
+        "wall_mean_ms": round(res["wall_mean_ms"], 4), "timing": "median of per-step HIP events",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"{w.name}: gate={w.gate} B={w.B} H={w.H} T={w.T} dk={w.dk} dv={w.dv} "
@@ -261,7 +320,7 @@ def main():
                                + (f", Kaczmarz step in-kernel (eps={w.kaczmarz_eps:g})" if w.kla else ""),
                    "global_batch": w.B, "seq_len": w.T, "heads": w.H, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / peak, 4),
-        "algorithmic_gflop_per_step": round(fl_th * w.token_heads / 1e9, 2),
+        "algorithmic_gflop_per_step": round(fl_th * w.token_heads / 1e9, 2), "step_hbm": step_roof,
         "roofline": roofline, "kernels": per_kernel, "other_policy": other, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -414,19 +473,27 @@ def cpu_baseline(w, inp_cpu):
     f = {n: W.to_f64(t, heads) for n, t in inp_cpu.items()}
     print(f"[bench] cpu baseline: oracle on {nheads} heads x T={w.T}, {threads} threads", file=sys.stderr,
           flush=True)
-    args = (f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"])
-    t0 = time.perf_counter()
-    if w.kla:   # Kaczmarz step: beta carries eta
-        oracle.kaczmarz_forward(*args, eps=w.kaczmarz_eps, nthreads=threads)
-        oracle.kaczmarz_backward(*args, f["do"], f["dhT"], eps=w.kaczmarz_eps, nthreads=threads)
-    else:
-        oracle.forward(*args, nthreads=threads)
-        oracle.backward(*args, f["do"], f["dhT"], nthreads=threads)
-    dt = time.perf_counter() - t0
+    def run(f, nthreads):
+        args = (f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"])
+        t0 = time.perf_counter()
+        if w.kla:   # Kaczmarz step: beta carries eta
+            oracle.kaczmarz_forward(*args, eps=w.kaczmarz_eps, nthreads=nthreads)
+            oracle.kaczmarz_backward(*args, f["do"], f["dhT"], eps=w.kaczmarz_eps, nthreads=nthreads)
+        else:
+            oracle.forward(*args, nthreads=nthreads)
+            oracle.backward(*args, f["do"], f["dhT"], nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    dt = run(f, threads)
     tok = nheads * w.T / w.H  # tokens of all heads: the sample covers nheads/H batch rows
+    # one thread on the first head alone
+    f1 = {n: W.to_f64(t, heads[:1]) for n, t in inp_cpu.items()}
+    dt1 = run(f1, 1)
     return {"value": round(tok / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{nheads} of {nheads_all} heads, full length T={w.T}, fwd+bwd, fp64 "
-                      f"({dt:.1f} s wall)"}
+                      f"({dt:.1f} s wall)",
+            "single_thread": {"value": round(w.T / w.H / dt1, 1), "unit": "tokens/s", "cores": 1,
+                              "sample": f"1 head, full length T={w.T}, fwd+bwd, fp64 ({dt1:.1f} s wall)"}}
 
 
 if __name__ == "__main__":

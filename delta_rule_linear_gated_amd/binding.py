@@ -213,6 +213,55 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+_IO_DTYPES = (torch.float32, torch.bfloat16)
+
+
+def _validate(q, k, v, beta, g, h0=None, do=None, dhT=None, states=None, state=None, theta=None,
+              state_im=None):
+    """Check what the C ABI cannot: element types, shapes and devices of the
+    tensors (it sizes every buffer from q's shape and the dtype field, so a
+    mismatched tensor would be read past its end).  Raises ValueError.
+      q, k [B,H,T,dk], v and do [B,H,T,dv]: one I/O type (fp32 or bf16)
+      beta [B,H,T]; g [B,H,T] or [B,H,T,dk]; theta [B,H,T,dk]: fp32
+      h0, dhT, state, state_im [B,H,dv,dk]: fp32;  states: uint8
+    Every tensor contiguous and on q's CUDA device."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B,H,T,dk], got shape {tuple(q.shape)}")
+    Bq, Hq, Tq, dk = q.shape
+    if q.dtype not in _IO_DTYPES:
+        raise ValueError(f"q must be float32 or bfloat16, got {q.dtype}")
+    if v.dim() != 4:
+        raise ValueError(f"v must be [B,H,T,dv], got shape {tuple(v.shape)}")
+    dv = v.shape[-1]
+    want = {"k": (k, q.dtype, (Bq, Hq, Tq, dk)), "v": (v, q.dtype, (Bq, Hq, Tq, dv)),
+            "beta": (beta, torch.float32, (Bq, Hq, Tq)), "do": (do, q.dtype, (Bq, Hq, Tq, dv)),
+            "h0": (h0, torch.float32, (Bq, Hq, dv, dk)), "dhT": (dhT, torch.float32, (Bq, Hq, dv, dk)),
+            "state": (state, torch.float32, (Bq, Hq, dv, dk)),
+            "state_im": (state_im, torch.float32, (Bq, Hq, dv, dk)),
+            "theta": (theta, torch.float32, (Bq, Hq, Tq, dk))}
+    for name, (t, dt, shp) in want.items():
+        if t is None:
+            continue
+        if t.dtype != dt:
+            raise ValueError(f"{name} must be {dt} (q is {q.dtype}), got {t.dtype}")
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} must have shape {shp}, got {tuple(t.shape)}")
+    if g is not None:
+        if g.dtype != torch.float32:
+            raise ValueError(f"g must be torch.float32, got {g.dtype}")
+        if tuple(g.shape) not in ((Bq, Hq, Tq), (Bq, Hq, Tq, dk)):
+            raise ValueError(f"g must have shape {(Bq, Hq, Tq)} or {(Bq, Hq, Tq, dk)}, got {tuple(g.shape)}")
+    if states is not None and states.dtype != torch.uint8:
+        raise ValueError(f"states must be the uint8 buffer chunk_fwd returns, got {states.dtype}")
+    ts = [q, k, v, beta, g, h0, do, dhT, states, state, theta, state_im]
+    _contig(*ts)
+    if q.device.type != "cuda":
+        raise ValueError(f"tensors must be on a CUDA device, q is on {q.device}")
+    for t in ts:
+        if t is not None and t.device != q.device:
+            raise ValueError(f"every tensor must be on {q.device}, found one on {t.device}")
+
+
 def shape_of(q, v, g, C, kaczmarz_eps=None, no_scan=False) -> Shape:
     B, H, T, dk = q.shape
     return make_shape(B, H, T, dk, v.shape[-1], C, q.dtype, _gate_kind(g, dk), kaczmarz_eps, no_scan)
@@ -260,7 +309,7 @@ def chunk_fwd(q, k, v, beta, g=None, h0=None, C=64, save_states=True, want_hT=Tr
               stream=None, kaczmarz_eps=None, no_scan=False):
     """Returns (o, hT or None, saved buffer or None); saved_regions() views the buffer.
     With ``kaczmarz_eps`` set, ``beta`` is eta (Kaczmarz step)."""
-    _contig(q, k, v, beta, g, h0)
+    _validate(q, k, v, beta, g, h0)
     sh = shape_of(q, v, g, C, kaczmarz_eps, no_scan)
     o = torch.empty_like(v)
     hT = torch.empty(q.shape[0], q.shape[1], v.shape[-1], q.shape[-1], dtype=torch.float32,
@@ -276,8 +325,10 @@ def chunk_bwd(q, k, v, beta, g, h0, do, dhT=None, states=None, C=64, want_dh0=Tr
               stream=None, kaczmarz_eps=None, no_scan=False):
     """Returns dict dq, dk, dv, dbeta, dg (None without a gate), dh0 (or None).  With
     ``kaczmarz_eps`` set, ``beta`` is eta and "dbeta" holds d eta."""
-    _contig(q, k, v, beta, g, h0, do, dhT, states)
+    _validate(q, k, v, beta, g, h0, do, dhT, states)
     sh = shape_of(q, v, g, C, kaczmarz_eps, no_scan)
+    if states is not None and states.numel() < dn_states_bytes(sh):
+        raise ValueError(f"states holds {states.numel()} bytes, this shape saves {dn_states_bytes(sh)}")
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -295,7 +346,7 @@ def chunk_bwd(q, k, v, beta, g, h0, do, dhT=None, states=None, C=64, want_dh0=Tr
 def recurrent_fwd(q, k, v, beta, g, state, stream=None, kaczmarz_eps=None):
     """T recurrent steps (decode); `state` (fp32 [B,H,dv,dk]) is updated in place.
     Returns o.  With ``kaczmarz_eps`` set, ``beta`` is eta."""
-    _contig(q, k, v, beta, g, state)
+    _validate(q, k, v, beta, g, state=state)
     B, H, T, dk = q.shape
     sh = make_shape(B, H, T, dk, v.shape[-1], 64, q.dtype, _gate_kind(g, dk), kaczmarz_eps)
     o = torch.empty_like(v)
@@ -307,7 +358,7 @@ def recurrent_phase_fwd(q, k, v, beta, g, theta, state_re, state_im, gate=None, 
     """T recurrent steps with the phase-controlled gate; the complex state
     (state_re, state_im, fp32 [B,H,dv,dk]) is updated in place.  ``gate`` names
     how g is laid out when it is 4-D or 3-D (default: from g's rank).  Returns o."""
-    _contig(q, k, v, beta, g, theta, state_re, state_im)
+    _validate(q, k, v, beta, g, state=state_re, theta=theta, state_im=state_im)
     B, H, T, dk = q.shape
     sh = make_shape(B, H, T, dk, v.shape[-1], 64, q.dtype, gate if gate is not None else _gate_kind(g, dk),
                     kaczmarz_eps)

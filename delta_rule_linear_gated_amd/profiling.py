@@ -10,6 +10,15 @@ and only while the kernel sources still hash to the digest recorded in it.
 Counter scaling: each counter is divided by what it reads for the reference
 copy (bytes moved / counter value), so a kernel's traffic is
 ``FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale`` (KiB -> bytes).
+
+``python -m delta_rule_linear_gated_amd.profiling counters ...`` summarises
+``--pmc`` runs of the matrix-core and LDS counters per kernel:
+  MFMA busy      SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * CUs * 4 SIMDs)
+  executed MFMA  SQ_INSTS_VALU_MFMA_MOPS_{BF16,F32} * 512 flops per dispatch,
+                 and those flops over the dispatch's duration against the peak
+  LDS conflicts  SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles)
+GRBM_GUI_ACTIVE counts GPU-busy cycles once per XCD on this part; the busy
+fraction divides by the per-XCD value (the counter divided by --xcds).
 """
 from __future__ import annotations
 
@@ -157,6 +166,74 @@ def summarize(args) -> str:
     return "\n".join(lines)
 
 
+def counter_table(d):
+    """{kernel key: {counter: mean value per dispatch}} plus the dispatch fields
+    (duration ns, VGPRs, AGPRs, LDS bytes) of one --pmc run."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _csv(_find(d, "counter_collection.csv")):
+        k = kernel_key(r["Kernel_Name"])
+        acc[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for f, name in (("Start_Timestamp", None), ("VGPR_Count", "vgpr"), ("Accum_VGPR_Count", "agpr"),
+                        ("LDS_Block_Size", "lds_bytes")):
+            if name and f in r and r[f] not in ("", None):
+                acc[k]["_" + name].append(float(r[f]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def counters(args) -> str:
+    tab = collections.defaultdict(dict)
+    for d in args.run:
+        for k, cs in counter_table(d).items():
+            tab[k].update(cs)
+    timed = {}
+    if args.summary:
+        s = load_summary(args.summary)
+        if s:
+            timed = {k: r.get("timed_avg_us", r.get("avg_us")) for k, r in s["kernels"].items()}
+    rows = []
+    data = {"workload": args.workload, "source_sha256": source_digest(), "cus": args.cus, "xcds": args.xcds,
+            "clock_ghz": args.clock_ghz, "kernels": {}}
+    for k in sorted(tab, key=lambda x: -(timed.get(x) or 0)):
+        if k == "copy":
+            continue
+        c = tab[k]
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        grbm = c.get("GRBM_GUI_ACTIVE")
+        mfma_busy = busy / (grbm / args.xcds * args.cus * 4) if busy is not None and grbm else None
+        fl_bf16 = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        fl_f32 = c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) * 512
+        us = timed.get(k)
+        tf_bf16 = fl_bf16 / (us * 1e-6) / 1e12 if us else None
+        tf_f32 = fl_f32 / (us * 1e-6) / 1e12 if us else None
+        conf = c.get("SQ_LDS_BANK_CONFLICT")
+        act = c.get("SQ_LDS_IDX_ACTIVE")
+        rec = {"avg_us": us, "mfma_busy": mfma_busy, "mfma_flops_bf16": fl_bf16, "mfma_flops_f32": fl_f32,
+               "mfma_tflops_bf16": tf_bf16, "mfma_tflops_f32": tf_f32,
+               "mfma_peak_frac_bf16": tf_bf16 / args.peak_bf16 if tf_bf16 is not None else None,
+               "mfma_peak_frac_f32": tf_f32 / args.peak_f32 if tf_f32 is not None else None,
+               "lds_conflict_frac": conf / act if conf is not None and act else None,
+               "raw": {n: v for n, v in c.items()}}
+        data["kernels"][k] = rec
+
+        def f(x, fmt):
+            return "-" if x is None else format(x, fmt)
+        rows.append(f"| {k} | {f(us, '.1f')} | {f(mfma_busy, '.1%')} | {fl_bf16 / 1e9:.2f} | {f(tf_bf16, '.1f')} | "
+                    f"{f(rec['mfma_peak_frac_bf16'], '.2%')} | {fl_f32 / 1e9:.3f} | {f(rec['lds_conflict_frac'], '.1%')} | "
+                    f"{f(c.get('_vgpr'), '.0f')} / {f(c.get('_agpr'), '.0f')} | {f(c.get('_lds_bytes'), '.0f')} |")
+    lines = [f"# {args.title}", "", "Commands (from /tmp, TMPDIR=/tmp):", ""]
+    for cmd in args.command:
+        lines.append(f"    {cmd}")
+    lines += ["", "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x CUs x 4); executed flops = "
+              "SQ_INSTS_VALU_MFMA_MOPS_* x 512 per dispatch; TFLOP/s = executed flops / the kernel's average "
+              "duration in the timed steps (kernel-trace summary); LDS conflicts = SQ_LDS_BANK_CONFLICT / "
+              "SQ_LDS_IDX_ACTIVE.", "",
+              "| kernel | avg us | MFMA busy | bf16 MFMA GFLOP / launch | bf16 TFLOP/s | of bf16 peak | "
+              "fp32 MFMA GFLOP / launch | LDS conflict cycles | VGPR / AGPR | LDS bytes |",
+              "|---|---|---|---|---|---|---|---|---|---|", *rows, "",
+              "```json", json.dumps(data, indent=1), "```", ""]
+    return "\n".join(lines)
+
+
 def load_summary(path):
     """The JSON block of a summary written by ``summarize`` (None if absent)."""
     if not os.path.exists(path):
@@ -182,12 +259,24 @@ def main():
     s.add_argument("--steps", type=int, default=0, help="timed steps of the traced bench run")
     s.add_argument("--warmup", type=int, default=0, help="warmup steps of the traced bench run")
     s.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--run", action="append", required=True, help="a --pmc output directory (repeatable)")
+    c.add_argument("--summary", help="the kernel-trace summary of the same workload (for durations)")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", action="append", default=[])
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--clock-ghz", type=float, default=2.4)
+    c.add_argument("--peak-bf16", type=float, default=2516.6)
+    c.add_argument("--peak-f32", type=float, default=157.3)
+    c.add_argument("--out", required=True)
     sub.add_parser("digest")
     a = ap.parse_args()
     if a.cmd == "digest":
         print(source_digest())
         return
-    txt = summarize(a)
+    txt = summarize(a) if a.cmd == "summarize" else counters(a)
     with open(a.out, "w") as f:
         f.write(txt)
     print(txt)

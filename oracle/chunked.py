@@ -3,9 +3,10 @@
 This is a second, independent evaluation of the operator that the C oracle
 computes step by step.  It follows the chunkwise form the pages describe:
 
-* ReWY abstract: chunkwise implementations expose matrix parallelism; the chunk
-  correction is one triangular residual system, and differentiating it needs a
-  single transposed solve (no adjoint of an explicit inverse).
+* ReWY abstract: the chunked evaluation turns the recurrence into dense matrix
+  work per chunk; its backward treats the per-chunk correction as a single
+  triangular system, solved once transposed, with no explicit inverse to
+  differentiate.
 * SFDA summary, "Der konstruktive Chunk-WY-Theorem": within a chunk the product
   of transitions is the decay product minus a rank <= C correction with a
   triangular core; "Zentrale Beitraege": the chunk's write summary B_chunk is the
