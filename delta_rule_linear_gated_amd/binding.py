@@ -26,9 +26,10 @@ DN_F32, DN_BF16 = 0, 1
 DN_GATE_NONE, DN_GATE_SCALAR, DN_GATE_VECTOR = 0, 1, 2
 DN_PASS_FWD, DN_PASS_BWD, DN_PASS_BWD_RECOMPUTE = 0, 1, 2
 DN_FLAG_KACZMARZ, DN_FLAG_NO_SCAN = 1, 2
+DN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("dn_states_bytes", "dn_states_layout", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
-           "dn_chunk_bwd", "dn_recurrent_fwd", "dn_recurrent_phase_fwd", "dn_status_string", "dn_last_error",
+           "dn_chunk_fwd_noalloc", "dn_chunk_bwd", "dn_recurrent_fwd", "dn_recurrent_phase_fwd", "dn_status_string", "dn_last_error",
            "dn_profile_enable", "dn_profile_collect")
 
 
@@ -72,6 +73,8 @@ def lib():
     L.dn_recurrent_phase_fwd.restype = i32
     L.dn_chunk_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dn_chunk_fwd.restype = i32
+    L.dn_chunk_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.dn_chunk_fwd_noalloc.restype = i32
     L.dn_chunk_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dn_chunk_bwd.restype = i32
     L.dn_status_string.argtypes = [i32]
@@ -175,6 +178,13 @@ def dn_chunk_fwd(shape, q, k, v, beta, g, h0, o, hT, states, ws, ws_bytes, strea
     return lib().dn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
                               _ptr(h0), _ptr(o), _ptr(hT), _ptr(states), _ptr(ws), int(ws_bytes),
                               _stream(stream))
+
+
+def dn_chunk_fwd_noalloc(shape, q, k, v, beta, g, h0, o, hT, stream=None) -> int:
+    """Raw call; returns the dn_status (no exception).  The forward without saved
+    states, its scratch in the library's per-device array (no workspace)."""
+    return lib().dn_chunk_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                      _ptr(h0), _ptr(o), _ptr(hT), _stream(stream))
 
 
 def dn_chunk_bwd(shape, q, k, v, beta, g, h0, dout, dhT, states, dq, dk, dv, dbeta, dg, dh0, ws,

@@ -247,6 +247,26 @@ dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, cons
     return DN_OK;
 }
 
+dn_status dn_chunk_fwd_noalloc(const dn_shape* shape, const void* q, const void* k, const void* v,
+                               const float* beta, const float* g, const float* h0, void* o, float* hT,
+                               void* stream) {
+    g_err[0] = '\0';
+    // a bad shape needs no scratch: dn_chunk_fwd reports it
+    const size_t need = dn_workspace_bytes(shape, DN_PASS_FWD);
+    if (need > DN_NOALLOC_SCRATCH_BYTES)
+        return fail(DN_ERR_WORKSPACE,
+                    "this shape needs %zu bytes of scratch; the allocation-free forward holds %zu (use "
+                    "dn_chunk_fwd with a workspace)",
+                    need, (size_t)DN_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (need > 0) {
+        const hipError_t e = dn::noalloc_scratch(&ws, &ws_bytes);
+        if (e != hipSuccess) return fail(DN_ERR_HIP, "scratch array not found: %s", hipGetErrorString(e));
+    }
+    return dn_chunk_fwd(shape, q, k, v, beta, g, h0, o, hT, nullptr, ws, ws_bytes, stream);
+}
+
 dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, const void* v,
                        const float* beta, const float* g, const float* h0, const void* dout,
                        const float* dhT, const void* states, void* dq, void* dk, void* dv,

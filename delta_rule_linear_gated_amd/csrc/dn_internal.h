@@ -117,6 +117,9 @@ hipError_t launch_scan_combine(const Params& p, int DK, bool forward, hipStream_
 // Recurrent form: T steps per head, state p.hT (fp32, in place), outputs p.o.
 hipError_t launch_recurrent(const Problem& pr, const Params& p, hipStream_t stream);
 bool supported(const Problem& pr);
+// Scratch array of dn_chunk_fwd_noalloc (dn_noalloc.hip): the current device's
+// address of it, looked up once per device.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 
 // Optional per-kernel timing (dn_profile.cpp); no-ops unless enabled.
 void prof_begin(hipStream_t stream, const char* name);

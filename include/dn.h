@@ -38,10 +38,11 @@
  *   - On any error nothing is enqueued, a negative dn_status is returned and
  *     dn_last_error() describes it.  No C++ exception crosses this boundary.
  *   - NaN / Inf in the inputs propagate to the outputs; they are not errors.
- *   - The library keeps no state between calls except the per-thread error text
- *     and, while dn_profile_enable(1) is in effect, the recorded timing events;
- *     calls from several host threads are safe.  Two calls that share a
- *     workspace must be ordered on one stream.
+ *   - The library keeps no state between calls except the per-thread error text,
+ *     while dn_profile_enable(1) is in effect the recorded timing events, and
+ *     the per-device scratch array of dn_chunk_fwd_noalloc; calls from several
+ *     host threads are safe.  Two calls that share a workspace (or, for
+ *     dn_chunk_fwd_noalloc, a GPU) must be ordered on one stream.
  *
  * Layouts (BH = B * H, NT = ceil(T / C)); "io" is the element type chosen by
  * dn_shape.dtype (fp32 or bf16), everything marked fp32 is always fp32:
@@ -181,6 +182,29 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
                        const float* dhT, const void* states, void* dq, void* dk, void* dv,
                        float* dbeta, float* dg, float* dh0, void* ws, size_t ws_bytes,
                        void* stream);
+
+/*
+ * The forward without saved states (as dn_chunk_fwd with states == NULL), for
+ * callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes no workspace: its scratch
+ * (the per-chunk log-decay, (I + A)^{-1} and scores, the Kaczmarz step data and
+ * the scan's segment buffers -- what dn_workspace_bytes(shape, DN_PASS_FWD)
+ * counts) lives in a device array of the library, DN_NOALLOC_SCRATCH_BYTES
+ * bytes, one per GPU, set up on the first call on each device (the current
+ * device must be the one the pointers and the stream belong to) and held until
+ * the process ends.  The call allocates nothing and frees nothing.
+ *   arguments, layouts, validation and errors: as for dn_chunk_fwd
+ *   DN_ERR_WORKSPACE when dn_workspace_bytes(shape, DN_PASS_FWD) exceeds
+ *   DN_NOALLOC_SCRATCH_BYTES (nothing is enqueued); DN_ERR_HIP when the
+ *   device's array cannot be located
+ * Every call on one GPU uses the same array, and nothing in it is carried from
+ * one call to the next: calls that overlap on one GPU (on different streams,
+ * or from several host threads without ordering) race.
+ */
+#define DN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dn_status dn_chunk_fwd_noalloc(const dn_shape* shape, const void* q, const void* k, const void* v,
+                               const float* beta, const float* g, const float* h0, void* o, float* hT,
+                               void* stream);
 
 /*
  * Recurrent evaluation (decode): the T steps of the recurrence for every batch

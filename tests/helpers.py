@@ -53,19 +53,23 @@ def gpu_run(w: W.Workload, inp: dict, policy: str | None = None, dhT=True):
     return {n: (None if t is None else t.cpu()) for n, t in out.items()}
 
 
-def oracle_run(inp: dict, heads=None, dhT=True, kaczmarz_eps=None):
+def oracle_run(inp: dict, heads=None, dhT=True, kaczmarz_eps=None, backward=True):
     """fp64 oracle on the same rounded inputs (optionally only some (b, h) heads).
-    With ``kaczmarz_eps``, inp["beta"] is eta and "dbeta" holds d eta."""
+    With ``kaczmarz_eps``, inp["beta"] is eta and "dbeta" holds d eta;
+    ``backward=False`` returns o and hT only."""
     f = {n: W.to_f64(t, heads) for n, t in inp.items()}
     args = (f["q"], f["k"], f["v"], f["beta"], f["g"], f["h0"])
-    dh = f["dhT"] if dhT else None
+    dh = f.get("dhT") if dhT else None
+    gr = {}
     if kaczmarz_eps is None:
         o, hT = oracle.forward(*args, nthreads=nthreads())
-        gr = oracle.backward(*args, f["do"], dh, nthreads=nthreads())
+        if backward:
+            gr = oracle.backward(*args, f["do"], dh, nthreads=nthreads())
     else:
         o, hT = oracle.kaczmarz_forward(*args, eps=kaczmarz_eps, nthreads=nthreads())
-        gr = oracle.kaczmarz_backward(*args, f["do"], dh, eps=kaczmarz_eps, nthreads=nthreads())
-        gr["dbeta"] = gr.pop("deta")
+        if backward:
+            gr = oracle.kaczmarz_backward(*args, f["do"], dh, eps=kaczmarz_eps, nthreads=nthreads())
+            gr["dbeta"] = gr.pop("deta")
     return {"o": o, "hT": hT, **gr}
 
 
