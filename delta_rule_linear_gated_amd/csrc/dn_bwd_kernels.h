@@ -58,8 +58,10 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     // A scalar gate is a row scaling: Q and K stay unscaled (K staged once) and the
     // decays go to the C x BV operands -- e^{gam_C - gam_t} to the K dS1^T part of
     // dU, e^{gam_t} to copies of dO and of -beta lambda for the dS update.  The
-    // vector gate scales Q and K per element.
-    __shared__ float gam_s[VEC ? C * DK : C];
+    // vector gate scales Q and K per element, from gate values held in registers
+    // in the layout of the K / Q register tiles (VecGate).
+    __shared__ float gam_s[C];
+    __shared__ __align__(16) float egc[VEC ? DK : 4];   // e^{gam_C} per channel (vector gate)
     __shared__ __align__(16) float rowf[2 * C];
     __shared__ __align__(16) float beta_s[C];
     __shared__ __align__(16) TI dSs[BV * LDK];   // dS1 operand     [v][c]
@@ -108,7 +110,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     using RDO = RegN<TI, C, BV>;
     RDO rdo;
     RegN<TI, C, C> rP, rT;
-    GateRegs<GATE, C, DK> rg;
+    GateRegs<GATE, C, DK, false> rg;
+    VecGate<TI, C, DK> vg;   // vector gate
     // scalar gate: gam of the rows of this thread's dO vectors (dO e^{gam} is formed
     // from registers, so the commit needs no barrier between the gate and the tiles)
     float gdo[SCA ? RDO::PER : 1];
@@ -118,6 +121,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         const long row0 = (long)bh * p.T + t0;
         const long cc = ((long)bh * p.NT + n) * C * C;
         rg.load(p.gam + row0 * GW, p.beta + row0, valid);
+        if constexpr (VEC) vg.load(p.gam + row0 * GW, valid);
         if constexpr (SCA) {
 #pragma unroll
             for (int i = 0; i < RDO::PER; ++i) gdo[i] = p.gam[row0 + min(RDO::idx_of(i) / RDO::VPR, valid - 1)];
@@ -143,18 +147,20 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
             for (int j = 0; j < TS::PER; ++j) st4<TI>(dSs + TS::col(j) * LDK + TS::row(j, 0), dS[j]);
         }
         // (b) commit this chunk's tiles (the barrier ending the previous chunk ordered
-        // these writes after its reads; only the vector gate's scaling below reads the
-        // gate just committed)
+        // these writes after its reads; nothing below reads the gate just committed
+        // before the next barrier)
         rg.commit(rowf, gam_s, beta_s);
-        if constexpr (VEC) __syncthreads();
+        if constexpr (VEC) vg.commit_last(egc);
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (VEC) {
-            // K e^{gam_C - gam}, -K e^{gam} and Q e^{gam} (one exp for the last two)
-            rk.store3(rq, Kd, Kn, Qg, LDK, [&](int r, int c, float k, float q, float* y) {
-                const float e = gf.G(r, c);
-                y[0] = k * gf.Gd(r, c);
-                y[1] = -k * e;
-                y[2] = q * e;
+            // K e^{gam_C - gam}, -K e^{gam} and Q e^{gam} (one exp for the last two),
+            // from the gate registers
+            rk.store3i(rq, Kd, Kn, Qg, LDK, [&](int i, int e, float k, float q, float* y) {
+                const float ge = vg.g[i][e];
+                const float f = fexp(ge);
+                y[0] = k * fexp(vg.gc[e] - ge);
+                y[1] = -k * f;
+                y[2] = q * f;
             });
         } else {
             rk.store(Kd, LDK);
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
 #pragma unroll
             for (int j = 0; j < TS::PER; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dS[j][i] *= gf.GC(TS::row(j, i));
+                for (int i = 0; i < 4; ++i) dS[j][i] *= VEC ? egc[TS::row(j, i)] : gf.GC(TS::row(j, i));
             }
         }
         gemm<TI, DK, BV, C, true, true>(dS, Qg, LDK, SCA ? dOg : dOb, LDV);

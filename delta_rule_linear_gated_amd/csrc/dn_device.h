@@ -558,6 +558,74 @@ template <typename T, int ROWS, int COLS> struct RegN {
             *reinterpret_cast<uint4*>(l1 + row * ldl + c0) = o[1][i];
         }
     }
+    // Two tiles from this one whose factors come from per-element registers of
+    // the caller: f(i, e, a, y) gets the vector index i (0 .. PER-1) and the
+    // element e (0 .. VW-1) of the value a and fills y[0] for l0, y[1] for l1.
+    template <class F>
+    __device__ __forceinline__ void store2i(T* l0, T* l1, int ldl, F f) const {
+        uint4 o[2][PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = idx_of(i);
+            const int row = idx / VPR;
+            const uint4 ra = pin(r[i]);
+            const T* sa = reinterpret_cast<const T*>(&ra);
+            T* d0 = reinterpret_cast<T*>(&o[0][i]);
+            T* d1 = reinterpret_cast<T*>(&o[1][i]);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                float y[2];
+                f(i, e, to_f(sa[e]), y);
+                const bool ok = row < valid_;
+                d0[e] = from_f<T>(ok ? y[0] : 0.f);
+                d1[e] = from_f<T>(ok ? y[1] : 0.f);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            if (idx >= NV) continue;
+            const int row = idx / VPR, c0 = (idx % VPR) * VW;
+            *reinterpret_cast<uint4*>(l0 + row * ldl + c0) = o[0][i];
+            *reinterpret_cast<uint4*>(l1 + row * ldl + c0) = o[1][i];
+        }
+    }
+    // Three tiles from this one (a) and another of the same shape (b), factors
+    // from per-element registers of the caller: f(i, e, a, b, y) fills y[0..2]
+    // for l0, l1, l2 (i, e as in store2i).
+    template <class F>
+    __device__ __forceinline__ void store3i(const RegN& b, T* l0, T* l1, T* l2, int ldl, F f) const {
+        uint4 o[3][PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = idx_of(i);
+            const int row = idx / VPR;
+            const uint4 ra = pin(r[i]), rb = pin(b.r[i]);
+            const T* sa = reinterpret_cast<const T*>(&ra);
+            const T* sb = reinterpret_cast<const T*>(&rb);
+            T* d0 = reinterpret_cast<T*>(&o[0][i]);
+            T* d1 = reinterpret_cast<T*>(&o[1][i]);
+            T* d2 = reinterpret_cast<T*>(&o[2][i]);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                float y[3];
+                f(i, e, to_f(sa[e]), to_f(sb[e]), y);
+                const bool ok = row < valid_;
+                d0[e] = from_f<T>(ok ? y[0] : 0.f);
+                d1[e] = from_f<T>(ok ? y[1] : 0.f);
+                d2[e] = from_f<T>(ok ? y[2] : 0.f);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = threadIdx.x + i * kThreads;
+            if (idx >= NV) continue;
+            const int row = idx / VPR, c0 = (idx % VPR) * VW;
+            *reinterpret_cast<uint4*>(l0 + row * ldl + c0) = o[0][i];
+            *reinterpret_cast<uint4*>(l1 + row * ldl + c0) = o[1][i];
+            *reinterpret_cast<uint4*>(l2 + row * ldl + c0) = o[2][i];
+        }
+    }
     // Three tiles from this one (a) and another of the same shape (b) in one
     // two-phase pass: f(row, col, a, b, y) fills y[0..2] for tiles l0, l1, l2, so
     // a factor the three share (a per-element gate) is computed once.

@@ -413,8 +413,10 @@ void prep_kernel(Params p) {
 // decay factors it leaves in LDS:
 //   scalar gate: rowf[t] = e^{gam_t}, rowf[C + t] = e^{gam_C - gam_t}, gam_s[t]
 //   vector gate: gam_s[t][c] (factors computed per element from it)
-template <int GATE, int C, int DK> struct GateRegs {
-    static constexpr bool VEC = GATE == kGateVector;
+// VT = false leaves the vector gate's tile out (the state kernels hold it in a
+// VecGate instead, see below).
+template <int GATE, int C, int DK, bool VT = true> struct GateRegs {
+    static constexpr bool VEC = GATE == kGateVector && VT;
     RegN<float, VEC ? C : 4, VEC ? DK : 4> gv;   // vector gate: the chunk's gam rows
     float gs = 0.f, gC = 0.f, b = 0.f;          // scalar gate: gam_t, gam_C; beta_t (thread t < C)
     int valid_ = C;
@@ -444,6 +446,56 @@ template <int GATE, int C, int DK> struct GateRegs {
             gam_s[t] = gs;
         }
         if (VEC) gv.store(gam_s, ldg);
+    }
+};
+
+// Per-channel gate of one chunk in registers, laid out like the elements of a
+// RegN<TI, C, DK> tile (a K or Q tile): g[i][e] is gam at element e of the
+// thread's vector i of that tile (row clamped into the chunk like the tile's
+// own loads), gc[e] gam_C at the same columns.  A thread's vectors all start at
+// the same column (kThreads is a multiple of the vectors per row), so one set
+// of gam_C values serves all of them; for the vectors past the tile's end (not
+// stored) the values are in-bounds duplicates.  The scaled tiles are then formed
+// straight from registers: no gate tile in LDS, no barrier between the gate and
+// the tiles.
+template <typename TI, int C, int DK> struct VecGate {
+    using RT = RegN<TI, C, DK>;
+    static constexpr int VW = RT::VW, VPR = RT::VPR, PER = RT::PER;
+    static_assert(VW % 4 == 0 && kThreads % VPR == 0, "gate vectors");
+    float g[PER][VW];
+    float gc[VW];
+    __device__ __forceinline__ static int col0() { return ((int)threadIdx.x % VPR) * VW; }
+    __device__ __forceinline__ void load(const float* __restrict__ gam, int valid) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = RT::idx_of(i);
+            const int row = min(idx / VPR, valid - 1), c0 = (idx % VPR) * VW;
+#pragma unroll
+            for (int v = 0; v < VW / 4; ++v) {
+                const float4 x = *reinterpret_cast<const float4*>(gam + (long)row * DK + c0 + 4 * v);
+                g[i][4 * v] = x.x;
+                g[i][4 * v + 1] = x.y;
+                g[i][4 * v + 2] = x.z;
+                g[i][4 * v + 3] = x.w;
+                __builtin_amdgcn_sched_barrier(0);   // fixed issue order (see RegN)
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < VW / 4; ++v) {
+            const float4 x = *reinterpret_cast<const float4*>(gam + (long)(valid - 1) * DK + col0() + 4 * v);
+            gc[4 * v] = x.x;
+            gc[4 * v + 1] = x.y;
+            gc[4 * v + 2] = x.z;
+            gc[4 * v + 3] = x.w;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // e^{gam_C} per channel into egc[DK] (the threads of the first row of vectors)
+    __device__ __forceinline__ void commit_last(float* egc) const {
+        if ((int)threadIdx.x < VPR) {
+#pragma unroll
+            for (int e = 0; e < VW; ++e) egc[col0() + e] = fexp(gc[e]);
+        }
     }
 };
 
@@ -494,7 +546,7 @@ template <int GATE, int C, int DK, int LDG = DK> struct GateLds {   // LDG: row 
 template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_state_lds() {
     constexpr size_t E = sizeof(TI);
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
-    constexpr int G = GATE == kGateVector ? C * DK : C;
+    constexpr int G = GATE == kGateVector ? C + DK : C;   // gam (+ e^{gam_C} per channel)
     constexpr int NK = GATE == kGateVector ? 3 : 2;   // Q, K (+ K Gam_C / Gam); an upper bound without output
     constexpr int NV = GATE == kGateScalar ? 3 : 2;   // V (then U), R (+ U Gam_C / Gam)
     return 4 * (G + 3 * C) + E * (BV * LDK + NK * C * LDK + NV * C * LDV + 2 * C * LDC) + 96;
@@ -514,8 +566,10 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     // scaling, so Q and K stay unscaled (staged once) and the decays are applied
     // to the C x BV results instead: e^{gam_t} to X and to the Q S0^T part of O,
     // e^{gam_C - gam_t} to a second copy of U that feeds the state update.  The
-    // per-channel vector gate scales Q and K per element.
-    __shared__ float gam_s[VEC ? C * DK : C];
+    // per-channel vector gate scales Q and K per element, from gate values held
+    // in registers in the layout of the K / Q register tiles (VecGate).
+    __shared__ float gam_s[C];
+    __shared__ __align__(16) float egc[VEC ? DK : 4];   // e^{gam_C} per channel (vector gate)
     __shared__ float rowf[2 * C];
     __shared__ __align__(16) float beta_s[C];
     __shared__ __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
@@ -564,13 +618,15 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     RegN<TI, C, BV> rv;
     RegN<TI, C, C> rT;
     RegN<TI, OUTPUT ? C : 16, OUTPUT ? C : 16> rP;
-    GateRegs<GATE, C, DK> rg;
+    GateRegs<GATE, C, DK, false> rg;
+    VecGate<TI, C, DK> vg;   // vector gate
     auto prefetch = [&](int n) {
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
         const long row0 = (long)bh * p.T + t0;
         const long cc = ((long)bh * p.NT + n) * C * C;
         rg.load(p.gam + row0 * GW, p.beta + row0, valid);
+        if constexpr (VEC) vg.load(p.gam + row0 * GW, valid);
         __builtin_amdgcn_sched_barrier(0);   // gate first, then the tiles, in order (see RegN)
         if constexpr (OUTPUT) rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);   // Q only feeds O
         rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
@@ -594,22 +650,26 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
             for (int j = 0; j < TS::PER; ++j) st4<TI>(Ss + TS::col(j) * LDK + TS::row(j, 0), S[j]);
         }
         // (b) commit this chunk's tiles to LDS (the barrier ending the previous
-        // chunk ordered these writes after its reads; only the vector gate's
-        // scaling below reads the gate just committed)
+        // chunk ordered these writes after its reads; nothing below reads the gate
+        // just committed before the next barrier)
         rg.commit(rowf, gam_s, beta_s);
-        if constexpr (VEC) __syncthreads();
+        if constexpr (VEC) vg.commit_last(egc);
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
         if (VEC && OUTPUT) {
-            // Q e^{gam}, K e^{gam} (one exp) and K e^{gam_C - gam}
-            rq.store3(rk, Qg, Kg, Kd, LDK, [&](int r, int c, float q, float k, float* y) {
-                const float e = gf.G(r, c);
-                y[0] = q * e;
-                y[1] = k * e;
-                y[2] = k * gf.Gd(r, c);
+            // Q e^{gam}, K e^{gam} (one exp) and K e^{gam_C - gam}, from the gate registers
+            rq.store3i(rk, Qg, Kg, Kd, LDK, [&](int i, int e, float q, float k, float* y) {
+                const float ge = vg.g[i][e];
+                const float f = fexp(ge);
+                y[0] = q * f;
+                y[1] = k * f;
+                y[2] = k * fexp(vg.gc[e] - ge);
             });
         } else if (VEC) {
-            rk.store(Kg, LDK, [&](int r, int c, float x) { return x * gf.G(r, c); });
-            rk.store(Kd, LDK, [&](int r, int c, float x) { return x * gf.Gd(r, c); });
+            rk.store2i(Kg, Kd, LDK, [&](int i, int e, float k, float* y) {
+                const float ge = vg.g[i][e];
+                y[0] = k * fexp(ge);
+                y[1] = k * fexp(vg.gc[e] - ge);
+            });
         } else {
             if constexpr (OUTPUT) rq.store(Qg, LDK);
             rk.store(Kg, LDK);
@@ -687,7 +747,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
 #pragma unroll
             for (int j = 0; j < TS::PER; ++j) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[j][i] *= gf.GC(TS::row(j, i));
+                for (int i = 0; i < 4; ++i) S[j][i] *= VEC ? egc[TS::row(j, i)] : gf.GC(TS::row(j, i));
             }
         }
         gemm<TI, DK, BV, C, true, true>(S, VEC ? Kd : Kg, LDK, SCA ? Ud : Ub, LDV);

@@ -30,7 +30,7 @@ template <typename TI, int GATE, int C, int DK> constexpr size_t prep_lds() {
 template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t bwd_state_lds() {
     constexpr size_t E = sizeof(TI);
     constexpr int P = Pad<TI>::value, LDK = DK + P, LDC = C + P, LDV = BV + P;
-    constexpr int G = GATE == kGateVector ? C * DK : C;
+    constexpr int G = GATE == kGateVector ? C + DK : C;   // gam (+ e^{gam_C} per channel)
     constexpr int NK = GATE == kGateVector ? 3 : 2;   // K, Q (+ -K Gam)
     // dO, lambda, dv, then -beta lambda (Gam) without a vector gate, dO Gam with a scalar one
     constexpr int NV = GATE == kGateVector ? 3 : (GATE == kGateScalar ? 5 : 4);
