@@ -20,8 +20,10 @@
 //     is read off those same products (sum_c k (dA~ K) etc.) instead of
 //     re-forming the K K^T / Q K^T Gram matrices (the scalar-gate reduction of
 //     the ReWY abstract);
-//   * for the vector gate the same products run on the centred factors
-//     K e^{gam - c}, K e^{c - gam}, Q e^{gam - c} (centred contraction), and the
+//   * for the vector gate the same products run block by block over 16-step
+//     blocks of the contraction, on keys and queries scaled relative to the gate
+//     at a block boundary and with each block's partial rescaled (the centred
+//     contraction, centred per 16-row block: vec_key_products), and the
 //     per-channel gate gradient is elementwise;
 //   * dg is the reverse cumulative sum of d gam inside the chunk.
 #pragma once
@@ -319,7 +321,8 @@ struct BwdChunkSmem {
     static constexpr size_t RED_C = RED_B + al((VB / 16) * C * 4);                // [C/16][D] column partials
     static constexpr size_t LASTS = RED_C + al((C / 16) * D * 4);                 // [D]
     static constexpr size_t KCO = LASTS + al(D * 4);                              // [C] Kaczmarz dk coefficients
-    static constexpr size_t TOTAL = KCO + al(C * 4);
+    static constexpr size_t DIAGP = KCO + al(C * 4);                              // [C] diagonal of dP (vector gate)
+    static constexpr size_t TOTAL = DIAGP + al(VEC ? C * 4 : 0);
     // dq / dk write-back tiles [C][LD] each at offset 0; d gam of the vector gate
     // [C][LDG] fp32 after them, written once every phase-C tile is dead
     static constexpr size_t DGB = al(2 * C * LD * E);
@@ -334,6 +337,84 @@ struct BwdChunkSmem {
     static_assert(2 * C * LD * E <= BIG_END, "write-back tiles");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
+
+// Key-gradient products of the per-channel gate for the wave's tiles of the
+// D x C outputs, all transposed ([c][t] / [c][s]):
+//     Y^T [c][t] = sum_{s} dA~[t][s] k_sc e^{gam_tc - gam_sc}
+//     DQ^T[c][t] = sum_{s} dP~[t][s] k_sc e^{gam_tc - gam_sc}
+//     Z^T [c][s] = sum_{t} (beta dA~)[t][s] k_tc e^{gam_tc - gam_sc} + sum_{t} dP~[t][s] q_tc e^{gam_tc - gam_sc}
+// (dA~, beta dA~, dP~ stored [t][s] and masked; their rows and columns are
+// the chunk's steps).  The contraction is split into 16-step blocks b, with
+// rho_b = gam at the last row of block b (rho_{-1} = 0):
+//   Y, DQ: Kc = k e^{rho_b - gam} (b = the row's own block) is the operand, and
+//          each block's partial is scaled by e^{gam_t - rho_b} on the accumulator;
+//   Z:     Kr = k e^{gam - rho_{b-1}}, Qr = q e^{gam - rho_{b-1}} (b = the row's
+//          block) are the operands, each block's partial scaled by e^{rho_{b-1} - gam_s}.
+// For g <= 0 every factor is at most 1 except on the partial of the output's own
+// block, where it grows at most by the decay of 16 steps (the centred
+// contraction of the ReWY abstract, centred per 16-row block).
+// gam_s: [C][LDG] fp32; Kc, Kr, Qr: [C][ld]; DA, DAB, DP: [C][lc].
+// The results go straight into the caller's accumulators: dkp += beta_t Y,
+// dq += DQ, dkm += Z, and dbA[j] = sum over the lane's 4 channels of k Y (kraw:
+// k at the lane's elements of each tile, as given).
+template <typename TI, int C, int D, int LDG, int NACC>
+__device__ __forceinline__ void vec_key_products(f32x4 (&dkp)[NACC], f32x4 (&dq)[NACC], f32x4 (&dkm)[NACC],
+                                                 float (&dbA)[NACC], const typename Vec4<TI>::type (&kraw)[NACC],
+                                                 const float* beta_s, const TI* Kc, const TI* Kr, const TI* Qr,
+                                                 int ld, const TI* DA, const TI* DAB, const TI* DP, int lc,
+                                                 const float* gam_s) {
+    using TO = Tiles<D, C>;
+    using MM = typename MmaFor<TI, 16>::type;   // one 16-step block per partial
+    static_assert(NACC == TO::PER, "accumulator count");
+    constexpr int NB = C / 16;
+    if (!TO::active()) return;
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) {
+        const int m0 = TO::m0(j), n0 = TO::n0(j), ob = n0 / 16;   // channels m0.., steps n0.. (block ob)
+        const int c = TO::row(j, 0), t = TO::col(j);              // this lane's 4 channels c.., step t
+        const f32x4 gt = ld4<float>(gam_s + t * LDG + c);
+        f32x4 y = zero4(), dqp = zero4(), z = zero4();
+        // Y, DQ: blocks b <= ob
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b > ob) break;
+            f32x4 py = zero4(), pq = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < 16; k0 += MM::kStep) {
+                const auto fa = MM::load_t(Kc + (16 * b + k0) * ld + m0, ld);
+                py = MM::op(fa, MM::load(DA + n0 * lc + 16 * b + k0, lc), py);
+                pq = MM::op(fa, MM::load(DP + n0 * lc + 16 * b + k0, lc), pq);
+            }
+            const f32x4 rb = ld4<float>(gam_s + (16 * b + 15) * LDG + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float fct = fexp(gt[i] - rb[i]);
+                y[i] += fct * py[i];
+                dqp[i] += fct * pq[i];
+            }
+        }
+        // Z: blocks b >= ob (here t is the output's step s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b < ob) continue;
+            f32x4 pz = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < 16; k0 += MM::kStep) {
+                pz = MM::op(MM::load_t(Kr + (16 * b + k0) * ld + m0, ld), MM::load_t(DAB + (16 * b + k0) * lc + n0, lc), pz);
+                pz = MM::op(MM::load_t(Qr + (16 * b + k0) * ld + m0, ld), MM::load_t(DP + (16 * b + k0) * lc + n0, lc), pz);
+            }
+            const f32x4 rp = b > 0 ? ld4<float>(gam_s + (16 * b - 1) * LDG + c) : zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[i] += fexp(rp[i] - gt[i]) * pz[i];
+        }
+        const f32x4 kv = f32x4{to_f(kraw[j][0]), to_f(kraw[j][1]), to_f(kraw[j][2]), to_f(kraw[j][3])};
+        const f32x4 d4 = kv * y;
+        dbA[j] = d4[0] + d4[1] + d4[2] + d4[3];
+        dkp[j] += beta_s[t] * y;
+        dq[j] += dqp;
+        dkm[j] += z;
+    }
+}
 
 template <typename TI, int GATE, int C, int D>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
@@ -358,6 +439,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     float* lastS = reinterpret_cast<float*>(smem + L::LASTS);
     float* dgb = reinterpret_cast<float*>(smem + L::DGB);
     float* kco = reinterpret_cast<float*>(smem + L::KCO);
+    float* diagp = reinterpret_cast<float*>(smem + L::DIAGP);
 
     const int n = blockIdx.x, bh = blockIdx.y;
     const int t0 = n * C;
@@ -411,6 +493,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     rT.store(TLs, LC);
     auto commit_block = [&](BlockRegs& r, int i) {
         r.S0.dot_rows(r.dS1, ls);
+        // the sums are formed here: left to their use at the finish, the compiler
+        // sinks the products there and keeps both register tiles alive until then
+#pragma unroll
+        for (int x = 0; x < L::RS::PER; ++x)
+#pragma unroll
+            for (int y = 0; y < L::RS::VW; ++y) asm volatile("" : "+v"(ls[x][y]));
         r.S0.store_n(blk(i, L::S0B), LD, Identity());
         r.dS1.store_n(blk(i, L::DS1B), LD, Identity());
         r.lam.store(blk(i, L::LAMB), LVB);
@@ -522,7 +610,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 for (int i = 0; i < 4; ++i) {
                     const int s2 = TCC::row(j, i);
                     const float e = (SCA && s2 <= t) ? fexp(gt - gam_s[s2]) : 1.f;
-                    pp[j][i] = s2 <= t ? dP[j][i] * e : 0.f;
+                    // the vector gate's key products leave out the diagonal of dP: it is
+                    // added in fp32 in phase C (see there)
+                    pp[j][i] = (VEC ? s2 < t : s2 <= t) ? dP[j][i] * e : 0.f;
+                    if (VEC && s2 == t) diagp[t] = dP[j][i];
                     a[j][i] = s2 < t ? -dA[j][i] * e : 0.f;   // dA = -lambda U^T
                     ab[j][i] = bt * a[j][i];
                 }
@@ -547,27 +638,40 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         TI* Kr = VEC ? reinterpret_cast<TI*>(smem + L::KR) : KG;
         TI* Kl = VEC ? reinterpret_cast<TI*>(smem + L::KL) : KG;
         const float* gl = gam_s + (valid - 1) * (VEC ? L::LDGM : GW);
-        // fp = e^{gam - centre} (vector gate; 1 otherwise), centre = gam_C / 2
-        auto fpl = [&](int t, int c) -> float { return VEC ? fexp(gam_s[t * L::LDGM + c] - 0.5f * gl[c]) : 1.f; };
-        auto fp4 = [&](int t, int c0) -> f32x4 {
-            if constexpr (VEC) {
-                const f32x4 g4 = ld4<float>(gam_s + t * L::LDGM + c0), c4 = ld4<float>(gl + c0);
-                return f32x4{fexp(g4[0] - 0.5f * c4[0]), fexp(g4[1] - 0.5f * c4[1]), fexp(g4[2] - 0.5f * c4[2]),
-                             fexp(g4[3] - 0.5f * c4[3])};
-            } else {
-                return f32x4{1.f, 1.f, 1.f, 1.f};
-            }
-        };
         if (VEC) {
-            // K e^{c - gam}, K e^{gam - c}, Q e^{gam - c}: one exp per element
+            // K e^{rho_b - gam}, K e^{gam - rho_{b-1}}, Q e^{gam - rho_{b-1}} with rho_b the
+            // gate at the last row of the row's 16-row block b (see vec_key_products)
             rk.store3(rq, Kr, Kl, Ql, LD, [&](int r, int c, float k, float q, float* y) {
-                const float e = fpl(r, c);
-                y[0] = __fdividef(k, e);
-                y[1] = k * e;
-                y[2] = q * e;
+                const int b = r >> 4;
+                const float g = gam_s[r * L::LDGM + c];
+                const float rb = gam_s[(16 * b + 15) * L::LDGM + c];
+                const float rp = b > 0 ? gam_s[(16 * b - 1) * L::LDGM + c] : 0.f;
+                const float fr = fexp(g - rp);
+                y[0] = k * fexp(rb - g);
+                y[1] = k * fr;
+                y[2] = q * fr;
             });
         } else {
             rq.store(Ql, LD);
+        }
+        // vector gate: k at this lane's elements of the output tiles (4 consecutive c of
+        // row t), as given and kept packed (cache hits: the chunk's rows were just
+        // loaded); rows past the sequence read row valid - 1 and count as zero
+        typedef typename Vec4<TI>::type V4;
+        V4 kraw[TO::PER], qraw[TO::PER];
+        if (VEC && TO::active()) {
+            // the pointers pass through an empty asm so that these loads are issued here:
+            // k and q are read-only, and hoisted to the prologue they would hold registers
+            // through the d_v loop, where the kernel has none to spare
+            const TI* kk = k;
+            const TI* qq = q;
+            asm volatile("" : "+s"(kk), "+s"(qq));
+#pragma unroll
+            for (int j = 0; j < TO::PER; ++j) {
+                const int t = TO::col(j), tt = min(t, valid - 1);
+                kraw[j] = *reinterpret_cast<const V4*>(kk + (long)tt * D + TO::row(j, 0));
+                qraw[j] = *reinterpret_cast<const V4*>(qq + (long)tt * D + TO::row(j, 0));
+            }
         }
         __syncthreads();
         // Warm the caches for the workgroup that most likely starts next on this
@@ -622,15 +726,28 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             }
         }
         // k and q at this lane's elements (4 consecutive c of row t), read back from the
-        // staged tiles; the gam_C column sums of Kd dKd (dk- holds only the Kd path so far)
-        f32x4 kv[TO::PER], qv[TO::PER];
+        // staged tiles without a vector gate; the gam_C column sums of Kd dKd (dk- holds
+        // only the Kd path so far)
+        // without a vector gate k and q come from the staged tiles (dead before the
+        // finish, so held in registers); with it from the packed loads above
+        f32x4 kv_[TO::PER], qv_[TO::PER];
+        auto cvt = [](const V4& x) { return f32x4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])}; };
+        auto kv = [&](int j) -> f32x4 {
+            if constexpr (VEC) return cvt(kraw[j]); else return kv_[j];
+        };
         if (TO::active()) {
 #pragma unroll
             for (int j = 0; j < TO::PER; ++j) {
                 const int t = TO::col(j), c0 = TO::row(j, 0);
-                const f32x4 fp = fp4(t, c0);
-                kv[j] = ld4<TI>(Kr + t * LD + c0) * fp;
-                qv[j] = ld4<TI>(Ql + t * LD + c0) / fp;
+                if constexpr (VEC) {
+                    if (t >= valid) {
+                        kraw[j] = V4{};
+                        qraw[j] = V4{};
+                    }
+                } else {
+                    kv_[j] = ld4<TI>(Kr + t * LD + c0);
+                    qv_[j] = ld4<TI>(Ql + t * LD + c0);
+                }
             }
             // column sums over t (the 16 lanes of a tile row, the wave's RN tiles) per c
 #pragma unroll
@@ -640,41 +757,59 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                     float colp = 0.f;
 #pragma unroll
                     for (int in = 0; in < TO::RN; ++in)
-                        colp += kv[im * TO::RN + in][i] * dkm[im * TO::RN + in][i];
+                        colp += kv(im * TO::RN + in)[i] * dkm[im * TO::RN + in][i];
                     colp = row16_sum(colp);
                     if ((lane_id() & 15) == 0) red_c[TO::cg() * D + TO::row(im * TO::RN, i)] = colp;
                 }
         }
-        float dbA[TO::PER];   // sum over this lane's 4 c of K+ Y at row t = TO::col(j)
-        f32x4 tmp[TO::PER];
-        // Y^T = Kr^T dA~^T :  dK+ = beta Y, dbeta_A = sum_c K+ Y
-        zero_acc<D, C>(tmp);
-        gemm<TI, D, C, C, true, false>(tmp, Kr, LD, DAs, LC);
-        if (TO::active()) {
+        float dbA[TO::PER];   // sum over this lane's 4 c of k Y at row t = TO::col(j)
+        if constexpr (VEC) {
+            // Y, dQ+ and Z + W tile by tile, block by block (see vec_key_products)
+            vec_key_products<TI, C, D, L::LDGM>(dkp, dq, dkm, dbA, kraw, beta_s, Kr, Kl, Ql, LD, DAs, DABs, DPs, LC,
+                                                gam_s);
+            // The diagonal of dP (a score with no decay) enters dq as dP_tt k_t and dk- as
+            // dP_tt q_t; its two terms of d gam, q (dP_tt k) - k (dP_tt q), cancel exactly.
+            // Added here in fp32 from the same k and q, they cancel to rounding, where
+            // through the scaled bf16 operands of the products they would not (with strong
+            // decay they dominate the small d gam)
+            if (TO::active()) {
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j) {
-                const int t = TO::col(j);
-                const f32x4 fp = fp4(t, TO::row(j, 0));
-                const f32x4 yf = tmp[j] * fp;
-                const f32x4 d4 = kv[j] * yf;
-                dbA[j] = d4[0] + d4[1] + d4[2] + d4[3];
-                dkp[j] += beta_s[t] * yf;
+                for (int j = 0; j < TO::PER; ++j) {
+                    const float dpt = TO::col(j) < valid ? diagp[TO::col(j)] : 0.f;
+                    qv_[j] = cvt(qraw[j]);
+                    dq[j] += dpt * kv(j);
+                    dkm[j] += dpt * qv_[j];
+                }
             }
-        }
-        // Z^T = Kl^T (beta dA~) and W^T = Ql^T dP~ : both reach k through e^{-gam}
-        zero_acc<D, C>(tmp);
-        gemm<TI, D, C, C, true, true>(tmp, Kl, LD, DABs, LC);
-        gemm<TI, D, C, C, true, true>(tmp, Ql, LD, DPs, LC);
-        if (TO::active()) {
+        } else {
+            f32x4 tmp[TO::PER];
+            // Y^T = Kr^T dA~^T :  dK+ = beta Y, dbeta_A = sum_c K Y
+            zero_acc<D, C>(tmp);
+            gemm<TI, D, C, C, true, false>(tmp, Kr, LD, DAs, LC);
+            if (TO::active()) {
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j) dkm[j] += tmp[j] / fp4(TO::col(j), TO::row(j, 0));
-        }
-        // dQ+^T = Kr^T dP~^T
-        zero_acc<D, C>(tmp);
-        gemm<TI, D, C, C, true, false>(tmp, Kr, LD, DPs, LC);
-        if (TO::active()) {
+                for (int j = 0; j < TO::PER; ++j) {
+                    const int t = TO::col(j);
+                    const f32x4 d4 = kv(j) * tmp[j];
+                    dbA[j] = d4[0] + d4[1] + d4[2] + d4[3];
+                    dkp[j] += beta_s[t] * tmp[j];
+                }
+            }
+            // Z^T = Kl^T (beta dA~) and W^T = Ql^T dP~ : both reach k through e^{-gam}
+            zero_acc<D, C>(tmp);
+            gemm<TI, D, C, C, true, true>(tmp, Kl, LD, DABs, LC);
+            gemm<TI, D, C, C, true, true>(tmp, Ql, LD, DPs, LC);
+            if (TO::active()) {
 #pragma unroll
-            for (int j = 0; j < TO::PER; ++j) dq[j] += tmp[j] * fp4(TO::col(j), TO::row(j, 0));
+                for (int j = 0; j < TO::PER; ++j) dkm[j] += tmp[j];
+            }
+            // dQ+^T = Kr^T dP~^T
+            zero_acc<D, C>(tmp);
+            gemm<TI, D, C, C, true, false>(tmp, Kr, LD, DPs, LC);
+            if (TO::active()) {
+#pragma unroll
+                for (int j = 0; j < TO::PER; ++j) dq[j] += tmp[j];
+            }
         }
 
         // -------- finish: dq, dk = dk+ + dk-, dbeta, d gam = q.dq + k.(dk+ - dk-)
@@ -693,7 +828,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 dkt[j] = dkp[j] + dkm[j];
                 st4<TI>(dqs + off, dq[j]);
                 if (!kz) st4<TI>(dks + off, dkt[j]);
-                dgm[j] = qv[j] * dq[j] + kv[j] * (dkp[j] - dkm[j]);
+                dgm[j] = qv_[j] * dq[j] + kv(j) * (dkp[j] - dkm[j]);
             }
             // row partials over c (4 per lane, 4 lane groups, RM tiles) of K+ Y (dbeta)
             // and, for the scalar gate, of d gam
@@ -752,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
 #pragma unroll
                 for (int j = 0; j < TO::PER; ++j) {
                     const int t = TO::col(j);
-                    st4<TI>(dks + t * LD + TO::row(j, 0), dkt[j] + (t < valid ? kco[t] : 0.f) * kv[j]);
+                    st4<TI>(dks + t * LD + TO::row(j, 0), dkt[j] + (t < valid ? kco[t] : 0.f) * kv(j));
                 }
             }
             __syncthreads();

@@ -45,6 +45,11 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Four consecutive elements of T as one vector (see st4 / ld4 below).
+template <typename T> struct Vec4;
+template <> struct Vec4<float> { typedef f32x4 type; };
+template <> struct Vec4<bf16> { typedef __attribute__((ext_vector_type(4))) __bf16 type; };
+
 // ---------------------------------------------------------------------------
 // One K-step of a 16x16 tile: load() fetches this lane's fragment of a tile
 // whose first row is at p (row stride ld, at column k0 already), op() is the
@@ -127,6 +132,58 @@ template <> struct Mma<float, 4> {
 template <typename T, int K> struct MmaFor {
     static constexpr int ks = sizeof(T) == 4 ? 4 : (K % 32 == 0 ? 32 : 16);
     using type = Mma<T, ks>;
+};
+
+// The elements of an MFMA operand fragment as floats, for operands that are
+// scaled per element in registers before the product: for Mma<T, KS> lane l
+// holds NE = KS / 4 consecutive K values of row (l & 15), starting NE * (l >> 4)
+// into the K step (the layout Mma::load reads from a K-contiguous tile).
+template <typename T, int KS> struct FragF {
+    static constexpr int NE = KS / 4;
+    float x[NE];
+    // p at the tile's first row and the K step's first column, row stride ld
+    __device__ __forceinline__ static int off(int ld) { return (lane_id() & 15) * ld + NE * (lane_id() >> 4); }
+    __device__ __forceinline__ void load(const T* p, int ld) {
+        const T* q = p + off(ld);
+        if constexpr (sizeof(T) == 2 && NE == 8) {
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+        } else if constexpr (sizeof(T) == 2 && NE == 4) {
+            const typename Vec4<bf16>::type v = *reinterpret_cast<const typename Vec4<bf16>::type*>(q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
+        } else {
+            static_assert(sizeof(T) == 4 && NE == 1, "fragment shape");
+            x[0] = to_f(q[0]);
+        }
+    }
+    // the same positions of an fp32 array (row stride ld floats, 16-byte aligned rows for NE >= 4)
+    __device__ __forceinline__ static void load_f(const float* p, int ld, float (&y)[NE]) {
+        const float* q = p + off(ld);
+#pragma unroll
+        for (int v = 0; v < NE; v += 4) {
+            if constexpr (NE >= 4) {
+                const f32x4 w = *reinterpret_cast<const f32x4*>(q + v);
+                y[v] = w[0];
+                y[v + 1] = w[1];
+                y[v + 2] = w[2];
+                y[v + 3] = w[3];
+            }
+        }
+        if constexpr (NE < 4) y[0] = q[0];
+    }
+    __device__ __forceinline__ typename Mma<T, KS>::Frag pack() const {
+        if constexpr (sizeof(T) == 2 && NE == 8) {
+            return bf16x8{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3],
+                          (bf16)x[4], (bf16)x[5], (bf16)x[6], (bf16)x[7]};
+        } else if constexpr (sizeof(T) == 2 && NE == 4) {
+            const typename Vec4<bf16>::type v = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+            return __builtin_bit_cast(i16x4, v);
+        } else {
+            return x[0];
+        }
+    }
 };
 
 // acc += A[16 x K] * B[16 x K]^T for one tile (A, B at the tile's first rows).
@@ -318,9 +375,6 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NACC]) {
 // one vector store / load.  An accumulator tile gives each lane 4 consecutive
 // rows of one column, so these move a lane's 4 values of a tile whose LDS (or
 // global) layout is transposed with respect to the tile.
-template <typename T> struct Vec4;
-template <> struct Vec4<float> { typedef f32x4 type; };
-template <> struct Vec4<bf16> { typedef __attribute__((ext_vector_type(4))) __bf16 type; };
 
 template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d) {
     typename Vec4<T>::type v = {from_f<T>(a), from_f<T>(b), from_f<T>(c), from_f<T>(d)};

@@ -21,9 +21,10 @@
 //
 // Gates: kGateNone (DeltaNet), kGateScalar (GDN: pairwise decays applied as
 // e^{gam_t - gam_s} on the C x C scores, never above 1 for g <= 0), kGateVector
-// (KDA: per-channel decays, factored through a per-chunk centre gam_C / 2 so
-// that K e^{gam - centre} and K e^{centre - gam} stay within e^{+-|gam_C|/2} --
-// the centred contraction of the ReWY abstract).
+// (KDA: per-channel decays; the C x C products split each pair's decay at a
+// per-channel reference, the gate at the last row of a 16-row block, so that
+// no factor exceeds the decay of 16 steps -- the centred contraction of the
+// ReWY abstract, centred per 16-row block).
 #pragma once
 
 #include <type_traits>
@@ -120,13 +121,14 @@ template <typename TI, int GATE, int C, int DK> struct PrepSmem {
     static constexpr int LDA = C + 4;                   // fp32 C x C rows
     static constexpr int LC = C + Pad<TI>::value;       // I/O-type C x C rows
     static constexpr int GW = GateLayout<GATE, DK>::GW;
+    // vector gate: gam rows padded to DK + 8 floats, so that 16 rows read 16 bytes
+    // each at one column hit distinct banks
+    static constexpr int LDG = VEC ? DK + 8 : 1;
     static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
-    // K (or K e^{gam - centre}) and Q; the vector gate's K e^{centre - gam} in KM,
-    // and its Q e^{gam - centre} staged into KP's space once the Gram product
-    // has read KP
+    // K and Q as loaded
     static constexpr size_t KP = 0;
     static constexpr size_t KM = KP + al(C * LDK * sizeof(TI));
-    static constexpr size_t QP = VEC ? KP : KM;
+    static constexpr size_t QP = KM;
     static constexpr size_t R0_END = KM + al(C * LDK * sizeof(TI));
     static constexpr size_t TS = 0;                     // fp32 [C][LDA]
     static constexpr size_t YSC = TS + al(C * LDA * 4); // fp32 [C/16][256]
@@ -134,11 +136,12 @@ template <typename TI, int GATE, int C, int DK> struct PrepSmem {
     static constexpr size_t R0B_END = PS + al(C * LC * sizeof(TI));
     static constexpr size_t R0 = R0_END > R0B_END ? R0_END : R0B_END;
     static constexpr size_t AS = R0;                    // fp32 [C][LDA]
-    // gam [C][GW] fp32; the vector gate's shares A's space (dead once the scaled
-    // tiles are staged, before A is written), so that two workgroups fit per CU
+    // gam [C][GW] fp32 ([C][LDG] for the vector gate, whose gam shares A's
+    // space: it is dead once the Gram products are done, before A is written),
+    // so that two workgroups fit per CU
     static constexpr size_t GAM = VEC ? AS : AS + al(C * LDA * 4);
     static constexpr size_t GAM_END =
-        VEC ? AS + al(C * LDA * 4 > C * GW * 4 ? C * LDA * 4 : C * GW * 4) : GAM + al(C * GW * 4);
+        VEC ? AS + al(C * LDA * 4 > C * LDG * 4 ? C * LDA * 4 : C * LDG * 4) : GAM + al(C * GW * 4);
     static constexpr size_t BETA = GAM_END;
     // vector gate: segment totals of the per-channel cumsum [NSEG][DK] fp32, in
     // the K tiles' space (dead before K is staged)
@@ -147,6 +150,61 @@ template <typename TI, int GATE, int C, int DK> struct PrepSmem {
     static_assert(!VEC || NSEG * DK * 4 <= R0_END, "cumsum totals");
     static constexpr size_t TOTAL = BETA + al(C * 4);
 };
+
+// Gram products of the per-channel gate (KDA) for the wave's tiles of the C x C
+// output:
+//     acc  (t, s) = sum_c k_tc k_sc e^{gam_tc - gam_sc}
+//     accp (t, s) = sum_c q_tc k_sc e^{gam_tc - gam_sc}
+// over the lower tiles (row block i >= column block j; the caller masks).  The
+// decay of a pair is split at a per-channel reference, rho_j = gam at the last
+// row of the column block: the column operand is k_s e^{rho_j - gam_s} and the
+// row operands k_t e^{gam_t - rho_j}, q_t e^{gam_t - rho_j}, both formed in
+// registers from the loaded tiles.  For g <= 0 both factors are at most 1 below
+// the diagonal blocks; on a diagonal block the row factor grows at most by the
+// decay of the block's 16 rows (the centred contraction of the ReWY abstract,
+// centred per 16-row block instead of per chunk, so its range is set by 16
+// steps, not C).  K, Q: [C][ldk] as loaded; gam_s: [C][LDG] fp32.
+template <typename TI, int C, int DK, int LDG, int NACC>
+__device__ __forceinline__ void vec_gram(f32x4 (&acc)[NACC], f32x4 (&accp)[NACC], const TI* K, const TI* Q,
+                                         int ldk, const float* gam_s) {
+    using TL = Tiles<C, C>;
+    using MM = typename MmaFor<TI, DK>::type;
+    using FF = FragF<TI, MM::kStep>;
+    constexpr int NE = FF::NE;
+    static_assert(TL::RN == 1, "one column block per wave");
+    if (!TL::active()) return;
+    const int s0 = TL::n0(0);                     // the wave's column block
+    const float* rho = gam_s + (s0 + 15) * LDG;   // its last row
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += MM::kStep) {
+        float r[NE], gs[NE];
+        FF::load_f(rho + k0, 0, r);   // row rho at this lane's columns
+        FF::load_f(gam_s + s0 * LDG + k0, LDG, gs);
+        FF b;
+        b.load(K + s0 * ldk + k0, ldk);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) b.x[e] *= fexp(r[e] - gs[e]);
+        const typename MM::Frag fb = b.pack();
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) {
+            const int t0 = TL::m0(j);
+            if (s0 > t0) continue;   // strictly upper tile: zero
+            float gt[NE];
+            FF::load_f(gam_s + t0 * LDG + k0, LDG, gt);
+            FF a, q;
+            a.load(K + t0 * ldk + k0, ldk);
+            q.load(Q + t0 * ldk + k0, ldk);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                const float f = fexp(gt[e] - r[e]);
+                a.x[e] *= f;
+                q.x[e] *= f;
+            }
+            acc[j] = MM::op(a.pack(), fb, acc[j]);
+            accp[j] = MM::op(q.pack(), fb, accp[j]);
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // prep_kernel: grid (NT, BH), one chunk per workgroup: gam, P and T of the
@@ -169,9 +227,8 @@ void prep_kernel(Params p) {
     constexpr int LDK = L::LDK, LDA = L::LDA, LC = L::LC;
     constexpr bool VEC = L::VEC;
     __shared__ __align__(16) char smem[L::TOTAL];
-    TI* Kp = reinterpret_cast<TI*>(smem + L::KP);   // K, or K e^{gam - centre}
-    TI* Km = reinterpret_cast<TI*>(smem + L::KM);   // K e^{centre - gam} (vector gate)
-    TI* Qp = reinterpret_cast<TI*>(smem + L::QP);   // Q, or Q e^{gam - centre}
+    TI* Kp = reinterpret_cast<TI*>(smem + L::KP);   // K
+    TI* Qp = reinterpret_cast<TI*>(smem + L::QP);   // Q
     float* Ts = reinterpret_cast<float*>(smem + L::TS);
     float* Ysc = reinterpret_cast<float*>(smem + L::YSC);
     TI* Ps = reinterpret_cast<TI*>(smem + L::PS);
@@ -257,7 +314,7 @@ void prep_kernel(Params p) {
             for (int r = 0; r < RS; ++r) {
                 const int t = seg * RS + r;
                 const float y = x[r] + off;
-                gam_s[t * DK + c] = y;
+                gam_s[t * L::LDG + c] = y;
                 if (t < valid) p.gam[(row0 + t) * DK + c] = y;
             }
         }
@@ -293,24 +350,13 @@ void prep_kernel(Params p) {
     }
     __syncthreads();
 
-    // -- stage K and Q (centred per-channel factors for the vector gate; its Q
-    //    after the Gram product, below)
-    const float* gl = gam_s + (valid - 1) * DK;  // gam_C (vector gate)
-    if (VEC) {
-        // K e^{gam - centre}, K e^{centre - gam}: one exp per element
-        rk.store2(Kp, Km, LDK, [&](int r, int c, float k, float* y) {
-            const float e = fexp(gam_s[r * DK + c] - 0.5f * gl[c]);
-            y[0] = k * e;
-            y[1] = __fdividef(k, e);
-        });
-    } else {
-        rk.store(Kp, LDK);
-        rq.store(Qp, LDK);
-    }
+    // -- stage K and Q as loaded (the per-channel gate scales the operand
+    //    fragments in registers, below)
+    rk.store(Kp, LDK);
+    rq.store(Qp, LDK);
     __syncthreads();
 
     // -- gated Gram matrices: A (strict lower, scaled by beta_t) and P (lower)
-    const TI* KmP = VEC ? Km : Kp;
     {
         using TL = Tiles<C, C>;
         f32x4 acc[TL::PER], accp[TL::PER];
@@ -318,20 +364,16 @@ void prep_kernel(Params p) {
         for (int j = 0; j < TL::PER; ++j) {
             acc[j] = zero4();
             accp[j] = zero4();
-            if (!TL::valid(j) || TL::n0(j) > TL::m0(j)) continue;   // strictly upper tiles are zero
-            acc[j] = tile_nt<TI, DK>(Kp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, acc[j]);
-            if (!VEC) accp[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, accp[j]);
         }
-        if constexpr (VEC) {
-            // Q e^{gam - centre} into KP's space once every wave has read KP
-            __syncthreads();
-            rq.store(Qp, LDK, [&](int r, int c, float x) { return x * fexp(gam_s[r * DK + c] - 0.5f * gl[c]); });
-            __syncthreads();
+        if constexpr (!VEC) {
 #pragma unroll
             for (int j = 0; j < TL::PER; ++j) {
-                if (!TL::valid(j) || TL::n0(j) > TL::m0(j)) continue;
-                accp[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, KmP + TL::n0(j) * LDK, LDK, accp[j]);
+                if (!TL::valid(j) || TL::n0(j) > TL::m0(j)) continue;   // strictly upper tiles are zero
+                acc[j] = tile_nt<TI, DK>(Kp + TL::m0(j) * LDK, LDK, Kp + TL::n0(j) * LDK, LDK, acc[j]);
+                accp[j] = tile_nt<TI, DK>(Qp + TL::m0(j) * LDK, LDK, Kp + TL::n0(j) * LDK, LDK, accp[j]);
             }
+        } else {
+            vec_gram<TI, C, DK, L::LDG>(acc, accp, Kp, Qp, LDK, gam_s);
         }
         // gate factors and masks (LDS reads only)
         if (TL::active()) {

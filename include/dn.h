@@ -121,6 +121,12 @@ typedef enum {
 #define DN_FLAG_NO_SCAN 2u
 
 /*
+ * Per-channel gate (DN_GATE_VECTOR): the C x C products split each pair's decay
+ * at the gate of a 16-step block boundary (the centred contraction, ReWY
+ * abstract), so every factor is finite while a channel's log-decay summed over
+ * any 16 consecutive steps stays above -87 (e.g. g >= -5.4 per step); beyond
+ * that the factors overflow and the results are Inf / NaN, with DN_OK.
+ *
  * Problem shape.  Supported: B, H, T >= 0 with B*H <= 65535; dk == dv in
  * {16, 32, 64, 128} (fp32: dk <= 64); C in {16, 32, 64}; any T (a last,
  * shorter chunk is handled exactly); fp32 with a vector gate needs C <= 32 at
