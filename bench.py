@@ -27,6 +27,7 @@ fp64 CPU oracle timed on the host (threaded, and one thread on a smaller sample)
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -108,6 +109,9 @@ def parse():
     ap.add_argument("--no-scan", action="store_true",
                     help="force one sequential state pass (DN_FLAG_NO_SCAN) where the chunk-parallel scan "
                          "would run")
+    ap.add_argument("--fp32-work", action="store_true",
+                    help="the precision option with fp32 working matrices: the workload's bf16 data, upcast "
+                         "exactly to fp32, through the fp32 path (fp32 tiles and fp32 matrix-core operands)")
     ap.add_argument("--decode", action="store_true",
                     help="instead of fwd+bwd, time the recurrent (decode) entry point: --decode-batch "
                          "sequences with the workload's heads and dims, --decode-tokens tokens per "
@@ -161,6 +165,12 @@ def main():
     torch.cuda.set_device(dev)
     print(f"[bench] generating {w.describe()}", file=sys.stderr, flush=True)
     inp_cpu = W.make_inputs(w)
+    if args.fp32_work:   # the same bf16 values, held and computed in fp32
+        if w.dtype != "bf16":
+            print("--fp32-work takes a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        inp_cpu = {n: (t.float() if t is not None and t.dtype == torch.bfloat16 else t) for n, t in inp_cpu.items()}
+        w = dataclasses.replace(w, dtype="fp32")
     inp = {n: (None if t is None else t.to(dev)) for n, t in inp_cpu.items()}
     q, k, v, beta, g, h0, do, dhT = (inp[n] for n in ("q", "k", "v", "beta", "g", "h0", "do", "dhT"))
     sh = B.shape_of(q, v, g, w.C, w.kaczmarz_eps, args.no_scan)   # Kaczmarz workloads: beta carries eta
@@ -313,11 +323,13 @@ def main():
         "fwd_ms": round(res["fwd_ms"], 4), "bwd_ms": round(res["bwd_ms"], 4),
         "wall_mean_ms": round(res["wall_mean_ms"], 4), "timing": "median of per-step HIP events",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
+        "dtype": w.dtype, "data": "synthetic" + (" (bf16 values, held in fp32)" if args.fp32_work else ""),
         "config": {"workload": f"{w.name}: gate={w.gate} B={w.B} H={w.H} T={w.T} dk={w.dk} dv={w.dv} "
                                f"C={w.C} policy={policy}, fwd+bwd"
                                + (", state passes by the chunk-parallel scan" if uses_scan else "")
-                               + (f", Kaczmarz step in-kernel (eps={w.kaczmarz_eps:g})" if w.kla else ""),
+                               + (f", Kaczmarz step in-kernel (eps={w.kaczmarz_eps:g})" if w.kla else "")
+                               + (", fp32 working matrices" if args.fp32_work else ", bf16 matrix-core operands, "
+                                  "fp32 accumulation" if w.dtype == "bf16" else ""),
                    "global_batch": w.B, "seq_len": w.T, "heads": w.H, "parallelism": "none (1 GPU)"},
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / peak, 4),
         "algorithmic_gflop_per_step": round(fl_th * w.token_heads / 1e9, 2), "step_hbm": step_roof,

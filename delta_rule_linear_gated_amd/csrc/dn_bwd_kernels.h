@@ -277,7 +277,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
 template <typename TI, int GATE, int C, int D>
 struct BwdChunkSmem {
     static constexpr int PAD = Pad<TI>::value;
-    static constexpr int VB = D >= 32 ? 32 : D;   // d_v block
+    // d_v block (16 for fp32 at D = 128, whose tiles are twice the bytes)
+    static constexpr int VB = D >= 32 ? (sizeof(TI) == 4 && D > 64 ? 16 : 32) : D;
     static constexpr int NVB = D / VB;
     static constexpr int LD = D + PAD;            // rows of D elements
     static constexpr int LC = C + PAD;            // rows of C elements

@@ -912,14 +912,20 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8 or 16), every
-// lane of a group getting the total (the DPP steps of row16_sum).
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16 or 32), every
+// lane of a group getting the total (the DPP steps of row16_sum, then for 32 the
+// partner row's sum by v_permlane16_swap, as in sum_lane_groups).
 template <int N> __device__ __forceinline__ float group_sum(float x) {
-    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group");
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "group");
     if (N >= 2) x += dpp_f<0xB1>(x);
     if (N >= 4) x += dpp_f<0x4E>(x);
     if (N >= 8) x += dpp_f<0x141>(x);
     if (N >= 16) x += dpp_f<0x140>(x);
+    if (N >= 32) {
+        const unsigned u = __builtin_bit_cast(unsigned, x);
+        const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        x += __builtin_bit_cast(float, (lane_id() & 16) ? a[0] : a[1]);
+    }
     return x;
 }
 

@@ -47,8 +47,9 @@ template <typename TI, int GATE, int C, int D, int BV> constexpr bool state_fits
 template <typename TI, int GATE, int C, int D> struct Fits {
     static constexpr int BVMIN = D < 16 ? D : 16;
     static constexpr bool small = prep_lds<TI, GATE, C, D>() <= kLdsMax && state_fits<TI, GATE, C, D, BVMIN>();
-    // fp32 at D = 128 cannot hold the backward's tiles
-    static constexpr bool value = small && !(sizeof(TI) == 4 && D > 64) &&
+    // fp32 with the per-channel gate cannot hold the chunk backward's tiles at D = 128,
+    // nor at D = 64 with C = 64
+    static constexpr bool value = small && !(sizeof(TI) == 4 && D > 64 && GATE == kGateVector) &&
                                   !(sizeof(TI) == 4 && D == 64 && GATE == kGateVector && C == 64);
 };
 

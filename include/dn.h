@@ -128,9 +128,11 @@ typedef enum {
  * that the factors overflow and the results are Inf / NaN, with DN_OK.
  *
  * Problem shape.  Supported: B, H, T >= 0 with B*H <= 65535; dk == dv in
- * {16, 32, 64, 128} (fp32: dk <= 64); C in {16, 32, 64}; any T (a last,
- * shorter chunk is handled exactly); fp32 with a vector gate needs C <= 32 at
- * dk = 64.  flags: DN_FLAG_KACZMARZ and / or DN_FLAG_NO_SCAN (other bits:
+ * {16, 32, 64, 128}; C in {16, 32, 64}; any T (a last, shorter chunk is
+ * handled exactly); fp32 with a vector gate needs dk <= 64, and C <= 32 at
+ * dk = 64.  fp32 I/O keeps every working matrix in fp32 (the matrix-core
+ * operands too); bf16 I/O uses bf16 operands with fp32 accumulation -- a caller
+ * who wants fp32 working matrices for bf16 data passes its exact fp32 copy.  flags: DN_FLAG_KACZMARZ and / or DN_FLAG_NO_SCAN (other bits:
  * DN_ERR_INVALID; the recurrent entry points ignore DN_FLAG_NO_SCAN); eps:
  * read only with DN_FLAG_KACZMARZ, finite and >= 0.  Anything else returns
  * DN_ERR_UNSUPPORTED.

@@ -152,7 +152,8 @@ def test_validation_errors_forward():
     assert fwd(sh_of(C=48)) == B.DN_ERR_UNSUPPORTED
     assert fwd(sh_of(dk=16, dv=32)) == B.DN_ERR_UNSUPPORTED
     assert fwd(sh_of(dk=96, dv=96)) == B.DN_ERR_UNSUPPORTED
-    assert fwd(sh_of(dk=128, dv=128, C=64, dtype="fp32")) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh_of(dk=128, dv=128, C=64, dtype="fp32", gate="vector")) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh_of(dk=64, dv=64, C=64, dtype="fp32", gate="vector")) == B.DN_ERR_UNSUPPORTED
     assert fwd(sh_of(B=300, H=300)) == B.DN_ERR_UNSUPPORTED
     assert fwd(sh_of(), q=None) == B.DN_ERR_INVALID
     assert fwd(sh_of(), g=None) == B.DN_ERR_INVALID
