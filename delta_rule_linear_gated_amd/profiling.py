@@ -35,10 +35,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 
+# The sources the chunkwise kernels are built from (the measured path): the
+# device headers, the launch code and the per-variant units.  Other files under
+# csrc/ (the C ABI, the recurrent and phase-gate kernels, the scratch array) do
+# not change these kernels.
+KERNEL_SOURCES = ("dn_device.h", "dn_fwd_kernels.h", "dn_bwd_kernels.h", "dn_internal.h", "dn_launch.h",
+                  "dn_launch.hip")
+
+
 def source_digest() -> str:
-    """sha256 over the kernel sources (csrc/*), in name order."""
+    """sha256 over the sources of the chunkwise kernels, in name order."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    names = set(KERNEL_SOURCES) | {os.path.basename(x) for x in glob.glob(os.path.join(CSRC, "dn_[fb]wd_*_g*.hip"))}
+    for path in sorted(os.path.join(CSRC, n) for n in names):
         if os.path.isfile(path):
             h.update(os.path.basename(path).encode())
             with open(path, "rb") as f:
@@ -228,7 +237,7 @@ def counters(args) -> str:
               "duration in the timed steps (kernel-trace summary); LDS conflicts = SQ_LDS_BANK_CONFLICT / "
               "SQ_LDS_IDX_ACTIVE.", "",
               "| kernel | avg us | MFMA busy | bf16 MFMA GFLOP / launch | bf16 TFLOP/s | of bf16 peak | "
-              "fp32 MFMA GFLOP / launch | LDS conflict cycles | VGPR / AGPR | LDS bytes |",
+              "fp32 MFMA GFLOP / launch | LDS conflict cycles | VGPR_Count / Accum_VGPR_Count fields | LDS bytes |",
               "|---|---|---|---|---|---|---|---|---|---|", *rows, "",
               "```json", json.dumps(data, indent=1), "```", ""]
     return "\n".join(lines)
