@@ -20,7 +20,9 @@ tests/test_oracle_sfda.py:
   forward           the recurrence in complex numpy, vectorised over heads;
   forward_products  explicit complex transition matrices and their products
                     (brute force, O(T^2 d_k^3));
-  forward_blocks    the real 2 x 2 rotation-decay form (A, B real).
+  forward_blocks    the real 2 x 2 rotation-decay form (A, B real);
+and the reverse mode of the recurrence, ``backward``, pinned by central
+differences and, at zero phase, by the C oracle's reverse mode.
 """
 from __future__ import annotations
 
@@ -129,3 +131,84 @@ def forward_blocks(q, k, v, beta, g, theta, h0_re=None, h0_im=None, eps=None):
         Bm = Bm - (b[:, :, t, None] * pb)[..., None] * kt[:, :, None, :]
         o[:, :, t] = np.einsum("bhvc,bhc->bhv", A, q[:, :, t])
     return o, A + 1j * Bm
+
+
+def backward(q, k, v, beta, g, theta, h0_re=None, h0_im=None, dout=None, dhT_re=None, dhT_im=None, eps=None):
+    """Reverse mode of ``forward``: the vector-Jacobian products of
+        L = <o, dout> + <Re S_T, dhT_re> + <Im S_T, dhT_im>
+    with respect to every input.  Shapes as for ``forward``; dout [B,H,T,dv] or
+    None (zero), dhT_re / dhT_im [B,H,dv,dk] or None.  With ``eps`` the beta
+    argument is eta of the Kaczmarz step and "dbeta" holds d eta (dk then
+    includes the path through the step size).
+
+    Each step is taken back in the order it was taken forward.  A complex
+    quantity Z carries the cotangent Zb = dL/dRe Z + i dL/dIm Z; a real input x
+    that enters as x w gets Re(conj(w) Zb); through the holomorphic exp of the
+    gate, lb = conj(lam) lamb; g and theta are the real and imaginary parts of
+    the gate's logarithm, so dg = Re lb (summed over the channels for a scalar
+    g) and dtheta = Im lb.
+
+    Returns a dict: dq, dk, dv [B,H,T,.], dbeta [B,H,T], dg (None / like g),
+    dtheta [B,H,T,dk], dh0_re, dh0_im [B,H,dv,dk]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Bn, H, T, dk = q.shape
+    dv = v.shape[-1]
+    lam = _gate(g, theta, T, dk, (Bn, H))
+    b = _beta(beta, k, eps)
+    S = np.zeros((Bn, H, dv, dk), np.complex128)
+    if h0_re is not None:
+        S += _f64(h0_re)
+    if h0_im is not None:
+        S += 1j * _f64(h0_im)
+    prev = np.empty((T, Bn, H, dv, dk), np.complex128)   # the state entering each step
+    for t in range(T):
+        prev[t] = S
+        St = S * lam[:, :, t, None, :]
+        u = b[:, :, t, None] * (v[:, :, t] - np.einsum("bhvc,bhc->bhv", St, k[:, :, t]))
+        S = St + u[..., :, None] * k[:, :, t, None, :]
+    do = np.zeros((Bn, H, T, dv)) if dout is None else _f64(dout)
+    Sb = np.zeros((Bn, H, dv, dk), np.complex128)
+    if dhT_re is not None:
+        Sb += _f64(dhT_re)
+    if dhT_im is not None:
+        Sb += 1j * _f64(dhT_im)
+    dq = np.zeros_like(q)
+    dkk = np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    db = np.zeros((Bn, H, T))
+    lb = np.zeros((Bn, H, T, dk), np.complex128)
+    for t in range(T - 1, -1, -1):
+        kt, qt, lt = k[:, :, t], q[:, :, t], lam[:, :, t]
+        Sp = prev[t]
+        St = Sp * lt[:, :, None, :]                          # gated state
+        p = np.einsum("bhvc,bhc->bhv", St, kt)
+        u = b[:, :, t, None] * (v[:, :, t] - p)
+        Sn = St + u[..., :, None] * kt[:, :, None, :]        # state after the step
+        # o_t = Re(Sn q_t)
+        Sb = Sb + do[:, :, t, :, None] * qt[:, :, None, :]
+        dq[:, :, t] = np.einsum("bhvc,bhv->bhc", Sn.real, do[:, :, t])
+        # Sn = St + u k^T
+        ub = np.einsum("bhvc,bhc->bhv", Sb, kt)
+        dkk[:, :, t] = np.einsum("bhv,bhvc->bhc", np.conj(u), Sb).real
+        # u = b (v - p)
+        dvv[:, :, t] = b[:, :, t, None] * ub.real
+        db[:, :, t] = np.einsum("bhv,bhv->bh", np.conj(ub), v[:, :, t] - p).real
+        pb = -b[:, :, t, None] * ub
+        # p = St k
+        Stb = Sb + pb[..., :, None] * kt[:, :, None, :]
+        dkk[:, :, t] += np.einsum("bhvc,bhv->bhc", np.conj(St), pb).real
+        # St = Sp diag(lam_t)
+        lamb = np.einsum("bhvc,bhvc->bhc", Stb, np.conj(Sp))
+        lb[:, :, t] = np.conj(lt) * lamb
+        Sb = Stb * np.conj(lt)[:, :, None, :]
+    out = {"dq": dq, "dk": dkk, "dv": dvv, "dtheta": lb.imag.copy(), "dh0_re": Sb.real.copy(),
+           "dh0_im": Sb.imag.copy(), "dg": None}
+    if g is not None:
+        out["dg"] = lb.real.sum(axis=-1) if _f64(g).ndim == 3 else lb.real.copy()
+    if eps is None:
+        out["dbeta"] = db
+    else:   # beta = eta / n, n = ||k||^2 + eps
+        n = np.sum(k ** 2, axis=-1) + eps
+        out["dbeta"] = db / n
+        out["dk"] = dkk - 2.0 * (db * b / n)[..., None] * k
+    return out

@@ -3,7 +3,9 @@ summary, "Kernarchitektur", real inputs, transposed orientation): against the
 independent C oracle at zero phase (KDA), against explicit products of complex
 transition matrices, between the complex and the real 2 x 2 rotation-decay
 forms, and against closed forms (pure rotation, decay of the magnitudes, the
-Kaczmarz projection)."""
+Kaczmarz projection); its reverse mode against central differences of the
+forward for every input and against the C oracle's reverse mode at zero
+phase."""
 import numpy as np
 import pytest
 
@@ -104,3 +106,70 @@ def test_a_plausible_mistake_is_caught():
     ob, _ = sfda.forward_products(c["q"][0, 0], c["k"][0, 0], c["v"][0, 0], c["beta"][0, 0], c["g"][0, 0],
                                   c["theta"][0, 0], h0)
     assert rel(o_wrong[0, 0], ob) > 1e-3
+
+
+def _loss(c, do, dr, di, eps=None, **over):
+    d = dict(c)
+    d.update(over)
+    o, S = sfda.forward(d["q"], d["k"], d["v"], d["beta"], d["g"], d["theta"], d["h0_re"], d["h0_im"], eps=eps)
+    return np.sum(o * do) + np.sum(S.real * dr) + np.sum(S.imag * di)
+
+
+def _central_differences(c, do, dr, di, name, eps=None, h=1e-6):
+    x = c[name]
+    fd = np.zeros_like(x)
+    for i in np.ndindex(x.shape):
+        a = x.copy()
+        a[i] += h
+        lp = _loss(c, do, dr, di, eps, **{name: a})
+        a[i] -= 2 * h
+        lm = _loss(c, do, dr, di, eps, **{name: a})
+        fd[i] = (lp - lm) / (2 * h)
+    return fd
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "vector"])
+@pytest.mark.parametrize("kz", [None, 1e-3])
+def test_backward_central_differences(gate, kz):
+    c = case(11, Bn=1, H=2, T=6, dk=4, dv=3, gate=gate)
+    r = np.random.default_rng(12)
+    do, dr, di = r.standard_normal((1, 2, 6, 3)), r.standard_normal((1, 2, 3, 4)), r.standard_normal((1, 2, 3, 4))
+    gr = sfda.backward(c["q"], c["k"], c["v"], c["beta"], c["g"], c["theta"], c["h0_re"], c["h0_im"], do, dr, di,
+                       eps=kz)
+    names = {"q": "dq", "k": "dk", "v": "dv", "beta": "dbeta", "theta": "dtheta", "h0_re": "dh0_re",
+             "h0_im": "dh0_im"}
+    if gate != "none":
+        names["g"] = "dg"
+    for name, key in names.items():
+        fd = _central_differences(c, do, dr, di, name, kz)
+        assert rel(gr[key], fd) < 1e-7, (name, rel(gr[key], fd))
+    if gate == "none":
+        assert gr["dg"] is None
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "vector"])
+def test_backward_zero_phase_is_the_c_oracle(gate):
+    """theta = 0, real h0 and dhT: the reverse mode is the C oracle's (KDA / GDN /
+    DeltaNet), and dh0 has no imaginary part."""
+    c = case(13, gate=gate, complex_h0=False)
+    r = np.random.default_rng(14)
+    do, dr = r.standard_normal(c["v"].shape), r.standard_normal(c["h0_re"].shape)
+    gr = sfda.backward(c["q"], c["k"], c["v"], c["beta"], c["g"], np.zeros_like(c["theta"]), c["h0_re"], None, do, dr)
+    ref = oracle.backward(c["q"], c["k"], c["v"], c["beta"], c["g"], c["h0_re"], do, dr)
+    for key in ("dq", "dk", "dv", "dbeta", "dg"):
+        if ref[key] is None:
+            assert gr[key] is None
+            continue
+        assert rel(gr[key], ref[key]) < 1e-12, key
+    assert rel(gr["dh0_re"], ref["dh0"]) < 1e-12
+    assert np.max(np.abs(gr["dh0_im"])) == 0.0
+
+
+def test_a_plausible_reverse_mode_mistake_is_caught():
+    """The phase gradient taken through the gate without its conjugate (the
+    reverse mode run at the opposite phases) disagrees with central differences."""
+    c = case(15, Bn=1, H=1, T=4, dk=3, dv=2)
+    r = np.random.default_rng(16)
+    do, dr, di = r.standard_normal((1, 1, 4, 2)), r.standard_normal((1, 1, 2, 3)), r.standard_normal((1, 1, 2, 3))
+    wrong = sfda.backward(c["q"], c["k"], c["v"], c["beta"], c["g"], -c["theta"], c["h0_re"], c["h0_im"], do, dr, di)
+    assert rel(wrong["dtheta"], _central_differences(c, do, dr, di, "theta")) > 1e-3
