@@ -112,6 +112,10 @@ def parse():
     ap.add_argument("--fp32-work", action="store_true",
                     help="the precision option with fp32 working matrices: the workload's bf16 data, upcast "
                          "exactly to fp32, through the fp32 path (fp32 tiles and fp32 matrix-core operands)")
+    ap.add_argument("--phase-chunk", action="store_true",
+                    help="instead of the real gates, time the chunkwise phase-controlled gate "
+                         "(dn_chunk_phase_fwd + dn_chunk_phase_bwd, chunks of 16) on the workload's batch, heads, "
+                         "length and gate at d = min(dk, 64), with phases theta = 0.5 N(0, 1)")
     ap.add_argument("--decode", action="store_true",
                     help="instead of fwd+bwd, time the recurrent (decode) entry point: --decode-batch "
                          "sequences with the workload's heads and dims, --decode-tokens tokens per "
@@ -159,6 +163,9 @@ def main():
     w = W.CONFIGS[args.workload]
     if args.decode:
         decode_bench(args, w)
+        return
+    if args.phase_chunk:
+        phase_chunk_bench(args, w)
         return
     policy = args.policy or w.policy
     dev = torch.device("cuda:0")
@@ -465,6 +472,81 @@ def decode_bench(args, w0):
                                f"per sequence and call", "global_batch": w.B, "seq_len": w.T, "heads": w.H,
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline, "graph_replay": graph, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def phase_chunk_bench(args, w0):
+    """fwd + bwd of the chunkwise phase-controlled gate: median of per-step HIP
+    events, like the main bench; the per-kernel durations from a second pass."""
+    import torch
+
+    from delta_rule_linear_gated_amd import binding as B
+    from delta_rule_linear_gated_amd import workloads as W
+
+    d = min(w0.dk, 64)
+    w = W.custom(w0.B, w0.H, w0.T, d, d, 16, w0.gate, w0.dtype, h0_std=0.5, seed=w0.seed, name=f"phase_{w0.name}",
+                 phase=True)
+    dev = torch.device("cuda:0")
+    print(f"[bench] phase: generating {w.describe()}", file=sys.stderr, flush=True)
+    inp_cpu = W.make_inputs(w)
+    x = {n: (None if t is None else t.to(dev)) for n, t in inp_cpu.items()}
+    sh = B.make_shape(w.B, w.H, w.T, d, d, 16, w.dtype, w.gate)
+    stream = torch.cuda.current_stream(dev)
+    o = torch.empty_like(x["v"])
+    hr = torch.empty(w.B, w.H, d, d, device=dev)
+    hi = torch.empty_like(hr)
+    st = torch.empty(max(B.dn_phase_states_bytes(sh) // 4, 1), device=dev)
+    gr = {n: torch.empty_like(x[m]) for n, m in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dbeta", "beta"),
+                                                  ("dtheta", "theta"))}
+    gr["dg"] = None if x["g"] is None else torch.empty_like(x["g"])
+    gr["dh0_re"], gr["dh0_im"] = torch.empty_like(hr), torch.empty_like(hr)
+
+    def fwd():
+        st_ = B.dn_chunk_phase_fwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["h0"], x["h0_im"], o,
+                                   hr, hi, st, stream)
+        if st_ != B.DN_OK:
+            raise B.DnError(st_, B.dn_last_error())
+
+    def bwd():
+        st_ = B.dn_chunk_phase_bwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["do"], x["dhT"],
+                                   x["dhT_im"], st, gr["dq"], gr["dk"], gr["dv"], gr["dbeta"], gr["dg"], gr["dtheta"],
+                                   gr["dh0_re"], gr["dh0_im"], stream)
+        if st_ != B.DN_OK:
+            raise B.DnError(st_, B.dn_last_error())
+
+    steps = max(5, args.steps // 5)   # a step takes milliseconds here
+    for _ in range(max(1, args.warmup // 5)):
+        fwd()
+        bwd()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    ms = med([e[0].elapsed_time(e[2]) for e in ev])
+    fms = med([e[0].elapsed_time(e[1]) for e in ev])
+    bms = med([e[1].elapsed_time(e[2]) for e in ev])
+    E = 2 if w.dtype == "bf16" else 4
+    gw = d if w.gate == "vector" else (0 if w.gate == "none" else 1)
+    by_f, by_b = algorithmic_bytes_per_token_head(d, d, E, gw)
+    by = (by_f + by_b + 3 * 4 * d) * w.token_heads   # + theta read, dtheta written (fp32 per channel)
+    line = {
+        "metric": "chunkwise phase-controlled gate fwd+bwd tokens/s", "value": round(w.B * w.T / (ms / 1e3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": steps, "ms_per_step": round(ms, 4), "fwd_ms": round(fms, 4),
+        "bwd_ms": round(bms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"phase-controlled gate, chunks of 16: gate={w.gate} B={w.B} H={w.H} T={w.T} d={d}, "
+                               f"fp32 arithmetic, one workgroup per (batch, head)", "global_batch": w.B,
+                   "seq_len": w.T, "heads": w.H, "parallelism": "none (1 GPU)"},
+        "step_hbm": {"algorithmic_bytes": int(by), "achieved_gbs": round(by / (ms / 1e3) / 1e9, 1),
+                     "hbm_frac": round(by / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 5)},
+        "workgroups": w.B * w.H,
     }
     print(json.dumps(line), flush=True)
 

@@ -29,7 +29,8 @@ DN_FLAG_KACZMARZ, DN_FLAG_NO_SCAN = 1, 2
 DN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("dn_states_bytes", "dn_states_layout", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
-           "dn_chunk_fwd_noalloc", "dn_chunk_bwd", "dn_recurrent_fwd", "dn_recurrent_phase_fwd", "dn_status_string", "dn_last_error",
+           "dn_chunk_fwd_noalloc", "dn_chunk_bwd", "dn_recurrent_fwd", "dn_recurrent_phase_fwd", "dn_phase_states_bytes",
+           "dn_chunk_phase_fwd", "dn_chunk_phase_bwd", "dn_status_string", "dn_last_error",
            "dn_profile_enable", "dn_profile_collect")
 
 
@@ -77,6 +78,12 @@ def lib():
     L.dn_chunk_fwd_noalloc.restype = i32
     L.dn_chunk_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dn_chunk_bwd.restype = i32
+    L.dn_phase_states_bytes.argtypes = [sp]
+    L.dn_phase_states_bytes.restype = sz
+    L.dn_chunk_phase_fwd.argtypes = [sp] + [vp] * 13
+    L.dn_chunk_phase_fwd.restype = i32
+    L.dn_chunk_phase_bwd.argtypes = [sp] + [vp] * 19
+    L.dn_chunk_phase_bwd.restype = i32
     L.dn_status_string.argtypes = [i32]
     L.dn_status_string.restype = ctypes.c_char_p
     L.dn_last_error.argtypes = []
@@ -206,6 +213,25 @@ def dn_recurrent_phase_fwd(shape, q, k, v, beta, g, theta, state_re, state_im, o
     """Raw call; returns the dn_status (no exception)."""
     return lib().dn_recurrent_phase_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
                                         _ptr(theta), _ptr(state_re), _ptr(state_im), _ptr(o), _stream(stream))
+
+
+def dn_phase_states_bytes(shape: Shape) -> int:
+    return lib().dn_phase_states_bytes(ctypes.byref(shape))
+
+
+def dn_chunk_phase_fwd(shape, q, k, v, beta, g, theta, h0_re, h0_im, o, hT_re, hT_im, states, stream=None) -> int:
+    """Raw call; returns the dn_status (no exception)."""
+    return lib().dn_chunk_phase_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(theta),
+                                    _ptr(h0_re), _ptr(h0_im), _ptr(o), _ptr(hT_re), _ptr(hT_im), _ptr(states),
+                                    _stream(stream))
+
+
+def dn_chunk_phase_bwd(shape, q, k, v, beta, g, theta, dout, dhT_re, dhT_im, states, dq, dk, dv, dbeta, dg, dtheta,
+                       dh0_re, dh0_im, stream=None) -> int:
+    """Raw call; returns the dn_status (no exception)."""
+    return lib().dn_chunk_phase_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(theta),
+                                    _ptr(dout), _ptr(dhT_re), _ptr(dhT_im), _ptr(states), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _ptr(dbeta), _ptr(dg), _ptr(dtheta), _ptr(dh0_re), _ptr(dh0_im), _stream(stream))
 
 
 # ------------------------------------------------------------------ convenience
@@ -375,6 +401,40 @@ def recurrent_phase_fwd(q, k, v, beta, g, theta, state_re, state_im, gate=None, 
     o = torch.empty_like(v)
     _check(dn_recurrent_phase_fwd(sh, q, k, v, beta, g, theta, state_re, state_im, o, stream))
     return o
+
+
+def chunk_phase_fwd(q, k, v, beta, g, theta, h0_re=None, h0_im=None, gate=None, save_states=True, stream=None):
+    """Chunkwise forward of the phase-controlled gate (chunks of 16).  ``gate``
+    names how g is laid out (default: from its rank).  Returns (o, hT_re, hT_im,
+    states or None)."""
+    _validate(q, k, v, beta, g, h0=h0_re, state_im=h0_im, theta=theta)
+    B, H, T, dk = q.shape
+    sh = make_shape(B, H, T, dk, v.shape[-1], 16, q.dtype, gate if gate is not None else _gate_kind(g, dk))
+    o = torch.empty_like(v)
+    hT_re = torch.empty(B, H, v.shape[-1], dk, dtype=torch.float32, device=q.device)
+    hT_im = torch.empty_like(hT_re)
+    states = (torch.empty(max(dn_phase_states_bytes(sh) // 4, 1), dtype=torch.float32, device=q.device)
+              if save_states else None)
+    _check(dn_chunk_phase_fwd(sh, q, k, v, beta, g, theta, h0_re, h0_im, o, hT_re, hT_im, states, stream))
+    return o, hT_re, hT_im, states
+
+
+def chunk_phase_bwd(q, k, v, beta, g, theta, do, dhT_re, dhT_im, states, gate=None, stream=None):
+    """Backward of chunk_phase_fwd from its saved states.  Returns a dict dq, dk,
+    dv, dbeta, dg (None without a gate), dtheta, dh0_re, dh0_im."""
+    _validate(q, k, v, beta, g, do=do, dhT=dhT_re, state_im=dhT_im, theta=theta)
+    B, H, T, dk = q.shape
+    sh = make_shape(B, H, T, dk, v.shape[-1], 16, q.dtype, gate if gate is not None else _gate_kind(g, dk))
+    if states is None or states.dtype != torch.float32 or states.numel() * 4 < dn_phase_states_bytes(sh):
+        raise ValueError("states must be the float32 buffer chunk_phase_fwd saved")
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dbeta": torch.empty_like(beta), "dg": None if g is None else torch.empty_like(g),
+           "dtheta": torch.empty_like(theta),
+           "dh0_re": torch.empty(B, H, v.shape[-1], dk, dtype=torch.float32, device=q.device)}
+    out["dh0_im"] = torch.empty_like(out["dh0_re"])
+    _check(dn_chunk_phase_bwd(sh, q, k, v, beta, g, theta, do, dhT_re, dhT_im, states, out["dq"], out["dk"], out["dv"],
+                              out["dbeta"], out["dg"], out["dtheta"], out["dh0_re"], out["dh0_im"], stream))
+    return out
 
 
 class DeltaRule(torch.autograd.Function):

@@ -360,6 +360,177 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
 
 namespace {
 
+// Shape checks of the chunkwise phase-controlled gate (chunks of 16, d <= 64).
+dn_status phase_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
+    if (!s) return fail(DN_ERR_INVALID, "shape is NULL");
+    if (s->B < 0 || s->H < 0 || s->T < 0) return fail(DN_ERR_SHAPE, "B, H, T must be >= 0");
+    if (s->dtype != DN_F32 && s->dtype != DN_BF16) return fail(DN_ERR_DTYPE, "unknown dtype %d", s->dtype);
+    if (s->gate < DN_GATE_NONE || s->gate > DN_GATE_VECTOR) return fail(DN_ERR_INVALID, "unknown gate %d", s->gate);
+    DN_TRY(check_flags(s));
+    if (s->flags & DN_FLAG_KACZMARZ) return fail(DN_ERR_UNSUPPORTED, "the chunkwise phase gate has no Kaczmarz step");
+    if ((long long)s->B * s->H > 65535) return fail(DN_ERR_UNSUPPORTED, "B*H must be <= 65535");
+    if (s->C != 16) return fail(DN_ERR_UNSUPPORTED, "the chunkwise phase gate runs chunks of 16 (C must be 16)");
+    if (s->dk != s->dv) return fail(DN_ERR_UNSUPPORTED, "dk must equal dv");
+    if (s->dk != 16 && s->dk != 32 && s->dk != 64) return fail(DN_ERR_UNSUPPORTED, "dk must be 16, 32 or 64");
+    *pr = dn::Problem{};
+    pr->B = s->B;
+    pr->H = s->H;
+    pr->T = s->T;
+    pr->dk = s->dk;
+    pr->dv = s->dv;
+    pr->C = 16;
+    pr->bf16 = s->dtype == DN_BF16;
+    pr->gate = s->gate;
+    d->BH = (size_t)s->B * s->H;
+    d->T = (size_t)s->T;
+    d->NT = s->T > 0 ? ((size_t)s->T + 15) / 16 : 0;
+    d->dk = (size_t)s->dk;
+    d->dv = (size_t)s->dv;
+    d->E = pr->bf16 ? 2 : 4;
+    d->gw = s->gate == DN_GATE_VECTOR ? (size_t)s->dk : 1;
+    return DN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dn_phase_states_bytes(const dn_shape* shape) {
+    dn::Problem pr;
+    Dims d;
+    if (phase_shape(shape, &pr, &d) != DN_OK) return 0;
+    return d.BH * d.NT * 2 * d.dv * d.dk * 4;
+}
+
+dn_status dn_chunk_phase_fwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
+                             const float* g, const float* theta, const float* h0_re, const float* h0_im, void* o,
+                             float* hT_re, float* hT_im, float* states, void* stream) {
+    g_err[0] = '\0';
+    dn::Problem pr;
+    Dims d;
+    DN_TRY(phase_shape(shape, &pr, &d));
+    const size_t nk = d.BH * d.T * d.dk * d.E, nv = d.BH * d.T * d.dv * d.E, nb = d.BH * d.T * 4;
+    const size_t ng = pr.gate == DN_GATE_NONE ? 0 : d.BH * d.T * d.gw * 4, nth = d.BH * d.T * d.dk * 4;
+    const size_t ns = d.BH * d.dv * d.dk * 4, nst = d.BH * d.NT * 2 * d.dv * d.dk * 4;
+    if (pr.gate == DN_GATE_NONE && g) return fail(DN_ERR_INVALID, "g must be NULL without a gate");
+    DN_TRY(need(q, nk, "q"));
+    DN_TRY(need(k, nk, "k"));
+    DN_TRY(need(v, nv, "v"));
+    DN_TRY(need(beta, nb, "beta"));
+    DN_TRY(need(g, ng, "g"));
+    DN_TRY(need(theta, nth, "theta"));
+    DN_TRY(need(o, nv, "o"));
+    DN_TRY(check_buffers({{"q", q, nk, false},
+                          {"k", k, nk, false},
+                          {"v", v, nv, false},
+                          {"beta", beta, nb, false},
+                          {"g", g, ng, false},
+                          {"theta", theta, nth, false},
+                          {"h0_re", h0_re, ns, false},
+                          {"h0_im", h0_im, ns, false},
+                          {"o", o, nv, true},
+                          {"hT_re", hT_re, ns, true},
+                          {"hT_im", hT_im, ns, true},
+                          {"states", states, nst, true}}));
+    dn::Params p{};
+    p.BH = (int)d.BH;
+    p.T = (int)d.T;
+    p.NT = (int)d.NT;
+    p.DKr = (int)d.dk;
+    p.DVr = (int)d.dv;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.beta = beta;
+    p.g = g;
+    p.theta = theta;
+    p.h0 = h0_re;
+    p.h0_im = h0_im;
+    p.o = o;
+    p.hT = hT_re;
+    p.hT_im = hT_im;
+    const hipError_t e = dn::launch_phase(pr, p, states, false, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return DN_OK;
+}
+
+dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
+                             const float* g, const float* theta, const void* dout, const float* dhT_re,
+                             const float* dhT_im, const float* states, void* dq, void* dk, void* dv, float* dbeta,
+                             float* dg, float* dtheta, float* dh0_re, float* dh0_im, void* stream) {
+    g_err[0] = '\0';
+    dn::Problem pr;
+    Dims d;
+    DN_TRY(phase_shape(shape, &pr, &d));
+    const size_t nk = d.BH * d.T * d.dk * d.E, nv = d.BH * d.T * d.dv * d.E, nb = d.BH * d.T * 4;
+    const size_t ng = pr.gate == DN_GATE_NONE ? 0 : d.BH * d.T * d.gw * 4, nth = d.BH * d.T * d.dk * 4;
+    const size_t ns = d.BH * d.dv * d.dk * 4, nst = d.BH * d.NT * 2 * d.dv * d.dk * 4;
+    if (pr.gate == DN_GATE_NONE && (g || dg)) return fail(DN_ERR_INVALID, "g and dg must be NULL without a gate");
+    DN_TRY(need(q, nk, "q"));
+    DN_TRY(need(k, nk, "k"));
+    DN_TRY(need(v, nv, "v"));
+    DN_TRY(need(beta, nb, "beta"));
+    DN_TRY(need(g, ng, "g"));
+    DN_TRY(need(theta, nth, "theta"));
+    DN_TRY(need(dout, nv, "dout"));
+    DN_TRY(need(states, nst, "states"));
+    DN_TRY(need(dq, nk, "dq"));
+    DN_TRY(need(dk, nk, "dk"));
+    DN_TRY(need(dv, nv, "dv"));
+    DN_TRY(need(dbeta, nb, "dbeta"));
+    DN_TRY(need(dg, ng, "dg"));
+    DN_TRY(need(dtheta, nth, "dtheta"));
+    DN_TRY(check_buffers({{"q", q, nk, false},
+                          {"k", k, nk, false},
+                          {"v", v, nv, false},
+                          {"beta", beta, nb, false},
+                          {"g", g, ng, false},
+                          {"theta", theta, nth, false},
+                          {"dout", dout, nv, false},
+                          {"dhT_re", dhT_re, ns, false},
+                          {"dhT_im", dhT_im, ns, false},
+                          {"states", states, nst, false},
+                          {"dq", dq, nk, true},
+                          {"dk", dk, nk, true},
+                          {"dv", dv, nv, true},
+                          {"dbeta", dbeta, nb, true},
+                          {"dg", dg, ng, true},
+                          {"dtheta", dtheta, nth, true},
+                          {"dh0_re", dh0_re, ns, true},
+                          {"dh0_im", dh0_im, ns, true}}));
+    dn::Params p{};
+    p.BH = (int)d.BH;
+    p.T = (int)d.T;
+    p.NT = (int)d.NT;
+    p.DKr = (int)d.dk;
+    p.DVr = (int)d.dv;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.beta = beta;
+    p.g = g;
+    p.theta = theta;
+    p.dout = dout;
+    p.dhT = dhT_re;
+    p.dhT_im = dhT_im;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dbeta = dbeta;
+    p.dg = dg;
+    p.dtheta = dtheta;
+    p.dh0 = dh0_re;
+    p.dh0_im = dh0_im;
+    const hipError_t e =
+        dn::launch_phase(pr, p, const_cast<float*>(states), true, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return DN_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
 // Both recurrent entry points: theta == nullptr is the plain recurrence (then
 // state_im must be NULL too), else the phase-controlled gate with the complex
 // state (state, state_im).

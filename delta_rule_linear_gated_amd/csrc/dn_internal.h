@@ -70,10 +70,15 @@ struct Params {
     // distance, in workgroup ids, to the one that most likely starts next on
     // the same XCD)
     int resident;
-    // phase-controlled gate (recurrent form only): theta [BH][T][DK] fp32 and the
-    // imaginary part of the state [BH][DV][DK] fp32 (the real part is hT)
+    // phase-controlled gate: theta [BH][T][DK] fp32 and the imaginary parts of the
+    // state [BH][DV][DK] fp32 (the real parts are h0 / hT and dh0 / dhT); the
+    // backward of the chunkwise form writes dtheta like theta
     const float* theta;
     float* hT_im;
+    const float* h0_im;
+    const float* dhT_im;
+    float* dh0_im;
+    float* dtheta;
 };
 
 struct Problem {
@@ -116,6 +121,10 @@ hipError_t launch_backward(const Problem& pr, const Params& p, bool have_states,
 hipError_t launch_scan_combine(const Params& p, int DK, bool forward, hipStream_t stream);
 // Recurrent form: T steps per head, state p.hT (fp32, in place), outputs p.o.
 hipError_t launch_recurrent(const Problem& pr, const Params& p, hipStream_t stream);
+// Chunkwise form of the phase-controlled gate (dn_phase.hip): forward (o, hT /
+// hT_im; the complex state entering each chunk to `states` when not NULL) or
+// backward (from those states), one workgroup per head, chunks of 16.
+hipError_t launch_phase(const Problem& pr, const Params& p, float* states, bool backward, hipStream_t stream);
 bool supported(const Problem& pr);
 // Scratch array of dn_chunk_fwd_noalloc (dn_noalloc.hip): the current device's
 // address of it, looked up once per device.

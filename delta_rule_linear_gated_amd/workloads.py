@@ -13,7 +13,8 @@ Distributions (per head, per step):
                                                      or per channel [B,H,T,dk]
   h0    = h0_std * N(0, 1)  (None when h0_std == 0)  fp32 [B,H,dv,dk]
   dO    ~ N(0, 1) in the I/O dtype; dhT ~ N(0, 1) fp32
-  theta = 0.5 N(0, 1) fp32 [B,H,T,dk] and h0_im like h0 (phase-controlled gate only)
+  theta = 0.5 N(0, 1) fp32 [B,H,T,dk], h0_im like h0 and dhT_im like dhT
+                                                     (phase-controlled gate only)
 The long-context workload uses the Kaczmarz step of the KLA abstract: keys are
 left unnormalised and the step input is eta = sigmoid(N(0, 1)) (fp32, returned
 under "beta"), which the operator turns into beta_t = eta_t / (||k_t||^2 + eps)
@@ -158,6 +159,8 @@ def make_inputs(w: Workload, seed: int | None = None, cotangents: bool = True,
     if cotangents:
         out["do"] = _round(_rng(s + 100, 6).standard_normal((B, H, T, dv)), w.dtype)
         out["dhT"] = _round(_rng(s + 100, 7).standard_normal((B, H, dv, dk)), "fp32")
+        if w.phase:   # cotangent of the final state's imaginary part
+            out["dhT_im"] = _round(_rng(s + 100, 10).standard_normal((B, H, dv, dk)), "fp32")
     if str(device) != "cpu":
         out = {n: (None if t is None else t.to(device)) for n, t in out.items()}
     return out

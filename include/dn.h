@@ -241,7 +241,7 @@ dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, 
  *     S_t = S_{t-1} diag(exp(g_t + i theta_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
  *     o_t = Re(S_t q_t).
  * With theta = 0 and S_im = 0 this is dn_recurrent_fwd (KDA for a vector g).
- * Only the recurrent form exists for this gate (no chunkwise form, no backward).
+ * The chunkwise form with its backward is dn_chunk_phase_fwd / dn_chunk_phase_bwd.
  *   shape  : as for dn_recurrent_fwd; the gate type says how g is laid out (none:
  *            no decay; scalar: one log-decay per step; vector: one per channel)
  *   inputs : q, k, v, beta (eta with DN_FLAG_KACZMARZ), g as for dn_recurrent_fwd;
@@ -254,6 +254,42 @@ dn_status dn_recurrent_fwd(const dn_shape* shape, const void* q, const void* k, 
 dn_status dn_recurrent_phase_fwd(const dn_shape* shape, const void* q, const void* k, const void* v,
                                  const float* beta, const float* g, const float* theta, float* state_re,
                                  float* state_im, void* o, void* stream);
+
+/*
+ * Chunkwise form of the phase-controlled gate, forward and backward (SFDA
+ * summary, "Der konstruktive Chunk-WY-Theorem" with the gate of "Kernarchitektur",
+ * read as for dn_recurrent_phase_fwd: real q, k, v, beta, a complex state and
+ * per key channel the gate exp(g_t + i theta_t)):
+ *     S_t = S_{t-1} diag(exp(g_t + i theta_t)) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = Re(S_t q_t),  S_0 = h0_re + i h0_im,  S_T = hT_re + i hT_im.
+ * In chunks of 16 steps: per chunk the complex UT / WY construction (pairwise
+ * complex decays in the C x C products, so any g <= 0 is safe), the exact
+ * chunk transfer of the state and the intra-chunk output; the backward takes
+ * the chunks back in reverse with one transposed (conjugated) triangular solve
+ * per chunk.  One workgroup per (batch, head); fp32 arithmetic throughout.
+ *   shape  : dk == dv in {16, 32, 64}; C == 16; dtype fp32 or bf16 (q, k, v, o,
+ *            dout, dq, dk, dv); gate as for dn_chunk_fwd; DN_FLAG_KACZMARZ is not
+ *            supported here (DN_ERR_UNSUPPORTED); DN_FLAG_NO_SCAN is ignored
+ *   inputs : q, k, v, beta, g as for dn_chunk_fwd; theta fp32 [B][H][T][dk]
+ *            (radians); h0_re, h0_im fp32 [B][H][dv][dk] (NULL = zero)
+ *   outputs: o; hT_re, hT_im (NULL = not wanted); states: the complex state
+ *            entering each chunk, fp32 [B][H][NT][2][dv][dk] (real part, then
+ *            imaginary; NT = ceil(T / 16); dn_phase_states_bytes bytes), written
+ *            by the forward when not NULL and required by the backward
+ *   backward: the vector-Jacobian products of
+ *            L = <o, dout> + <hT_re, dhT_re> + <hT_im, dhT_im>  (dhT_* NULL = zero):
+ *            dq, dk, dv (io), dbeta, dg (NULL iff no gate; layout of g), dtheta
+ *            (like theta) fp32; dh0_re, dh0_im (NULL = not wanted)
+ * Validation and errors as for dn_chunk_fwd; no workspace.
+ */
+size_t dn_phase_states_bytes(const dn_shape* shape);
+dn_status dn_chunk_phase_fwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
+                             const float* g, const float* theta, const float* h0_re, const float* h0_im, void* o,
+                             float* hT_re, float* hT_im, float* states, void* stream);
+dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
+                             const float* g, const float* theta, const void* dout, const float* dhT_re,
+                             const float* dhT_im, const float* states, void* dq, void* dk, void* dv, float* dbeta,
+                             float* dg, float* dtheta, float* dh0_re, float* dh0_im, void* stream);
 
 /* Static description of a status code. */
 const char* dn_status_string(dn_status status);

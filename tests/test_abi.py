@@ -242,3 +242,44 @@ def test_validation_errors_recurrent_phase():
     assert recp(sh_of(gate="vector", T=3, dk=48, dv=48)) == B.DN_ERR_UNSUPPORTED
     assert recp(sh_of(gate="vector", T=3, dv=24)) == B.DN_ERR_UNSUPPORTED
     assert recp(sh_of(gate="vector", T=3, kaczmarz_eps=-1.0)) == B.DN_ERR_INVALID
+
+
+def test_validation_errors_chunk_phase():
+    """The chunkwise phase-controlled gate: chunks of 16, d <= 64, no Kaczmarz step,
+    theta required, the backward needs the forward's states."""
+    def sh(**over):
+        d = dict(B=1, H=2, T=40, dk=32, dv=32, C=16, dtype="fp32", gate="vector")
+        d.update(over)
+        return B.make_shape(**d)
+
+    def fwd(s, **over):
+        a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, theta=FAKE * 6, h0_re=None, h0_im=None,
+                 o=FAKE * 7, hT_re=None, hT_im=None, states=None)
+        a.update(over)
+        return B.dn_chunk_phase_fwd(s, a["q"], a["k"], a["v"], a["beta"], a["g"], a["theta"], a["h0_re"],
+                                    a["h0_im"], a["o"], a["hT_re"], a["hT_im"], a["states"], 0)
+
+    def bwd(s, **over):
+        a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, theta=FAKE * 6, dout=FAKE * 8,
+                 dhT_re=None, dhT_im=None, states=FAKE * 9, dq=FAKE * 10, dk=FAKE * 11, dv=FAKE * 12,
+                 dbeta=FAKE * 13, dg=FAKE * 14, dtheta=FAKE * 15, dh0_re=None, dh0_im=None)
+        a.update(over)
+        return B.dn_chunk_phase_bwd(s, *(a[n] for n in ("q", "k", "v", "beta", "g", "theta", "dout", "dhT_re",
+                                                        "dhT_im", "states", "dq", "dk", "dv", "dbeta", "dg",
+                                                        "dtheta", "dh0_re", "dh0_im")), 0)
+
+    assert B.dn_phase_states_bytes(sh()) == 1 * 2 * 3 * 2 * 32 * 32 * 4   # NT = ceil(40 / 16) = 3
+    assert B.dn_phase_states_bytes(sh(C=64)) == 0
+    assert fwd(sh(C=64)) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh(dk=128, dv=128)) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh(dk=32, dv=16)) == B.DN_ERR_UNSUPPORTED
+    assert fwd(B.make_shape(1, 2, 40, 32, 32, 16, "fp32", "vector", kaczmarz_eps=1e-6)) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh(), theta=None) == B.DN_ERR_INVALID
+    assert fwd(sh(gate="none")) == B.DN_ERR_INVALID                     # g given without a gate
+    assert fwd(sh(), o=FAKE * 3) == B.DN_ERR_INVALID                    # output aliases v
+    assert fwd(sh(), hT_re=FAKE * 20, hT_im=FAKE * 20) == B.DN_ERR_INVALID
+    assert bwd(sh(), states=None) == B.DN_ERR_INVALID
+    assert bwd(sh(), dtheta=None) == B.DN_ERR_INVALID
+    assert bwd(sh(), dg=None) == B.DN_ERR_INVALID
+    assert bwd(sh(), dq=FAKE * 11) == B.DN_ERR_INVALID                  # dq aliases dk
+    assert "overlaps" in B.dn_last_error()
