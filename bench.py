@@ -63,6 +63,25 @@ def algorithmic_bytes_per_token_head(dk: int, dv: int, E: int, gw: int):
 
 
 FWD_KERNELS = ("prep", "fwd_state", "fwd_summary")
+PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector ALUs (256 CUs x 128 lanes x 2 flops x 2.4 GHz)
+
+
+def phase_flops_per_chunk(name: str, C: int, D: int) -> int:
+    """Algorithmic fp32 flops of one chunk-head of the phase-controlled gate's
+    kernels: a complex multiply-add counts 8, a real-by-complex one 4, a complex
+    exponential 10 (turn reduction, exp, sin, cos, scaling); pairs (t, u <= t)
+    number C (C + 1) / 2.  Recomputation counts as work here: these kernels are
+    bound by the vector ALUs, not by HBM."""
+    pairs = C * (C + 1) // 2
+    if name == "phase_prep":        # pairwise G, H per channel; T by forward substitution
+        return pairs * D * 20 + 4 * C * C * (C - 1)
+    if name == "phase_fwd_state":   # X, Y; U, O; S1; the gated tiles
+        return 24 * C * D * D + 8 * pairs * D * 2 + 6 * D * D + 29 * C * D
+    if name == "phase_bwd_state":   # Ub; P^H dO; lambda; dS0; the gated tiles
+        return 20 * C * D * D + 6 * pairs * D * 2 + 6 * D * D + 27 * C * D
+    if name == "phase_bwd_chunk":   # X, U; Ab, Pb; dS1.S0; the three row sums; pair terms per element
+        return 28 * C * D * D + 10 * pairs * D * 2 + 32 * C * C * D + 8 * D * D + 60 * C * D
+    return 0
 
 
 def kernel_budget(name: str, C: int, d: int, E: int, gw: int, saved: bool, kz: bool = False):
@@ -497,6 +516,8 @@ def phase_chunk_bench(args, w0):
     hr = torch.empty(w.B, w.H, d, d, device=dev)
     hi = torch.empty_like(hr)
     st = torch.empty(max(B.dn_phase_states_bytes(sh) // 4, 1), device=dev)
+    nws = B.dn_phase_workspace_bytes(sh, B.DN_PASS_BWD)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     gr = {n: torch.empty_like(x[m]) for n, m in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dbeta", "beta"),
                                                   ("dtheta", "theta"))}
     gr["dg"] = None if x["g"] is None else torch.empty_like(x["g"])
@@ -504,14 +525,14 @@ def phase_chunk_bench(args, w0):
 
     def fwd():
         st_ = B.dn_chunk_phase_fwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["h0"], x["h0_im"], o,
-                                   hr, hi, st, stream)
+                                   hr, hi, st, None, 0, stream)
         if st_ != B.DN_OK:
             raise B.DnError(st_, B.dn_last_error())
 
     def bwd():
         st_ = B.dn_chunk_phase_bwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["do"], x["dhT"],
                                    x["dhT_im"], st, gr["dq"], gr["dk"], gr["dv"], gr["dbeta"], gr["dg"], gr["dtheta"],
-                                   gr["dh0_re"], gr["dh0_im"], stream)
+                                   gr["dh0_re"], gr["dh0_im"], ws, nws, stream)
         if st_ != B.DN_OK:
             raise B.DnError(st_, B.dn_last_error())
 
@@ -532,23 +553,73 @@ def phase_chunk_bench(args, w0):
     ms = med([e[0].elapsed_time(e[2]) for e in ev])
     fms = med([e[0].elapsed_time(e[1]) for e in ev])
     bms = med([e[1].elapsed_time(e[2]) for e in ev])
+    B.dn_profile_collect()              # per-kernel durations from HIP events, a pass of their own
+    B.dn_profile_enable(True)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    B.dn_profile_enable(False)
+    kern = B.dn_profile_collect()
+    chunks = w.B * w.H * ((w.T + 15) // 16)
+    per_kernel = {n: {"avg_ms": round(t / max(c, 1), 4), "launches": c,
+                      "tflops": round(phase_flops_per_chunk(n, 16, d) * chunks / (t / max(c, 1) / 1e3) / 1e12, 2)}
+                  for n, (t, c) in kern.items()}
+    roofline = None
+    if kern:
+        dom = max(kern, key=lambda n: kern[n][0])
+        avg_s = kern[dom][0] / kern[dom][1] / 1e3
+        fl = phase_flops_per_chunk(dom, 16, d) * chunks
+        roofline = {"kernel": dom, "bound": "alu", "achieved": round(fl / avg_s / 1e12, 2),
+                    "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(fl / avg_s / 1e12 / PEAK_FP32_VALU_TFLOPS, 4), "traffic": None,
+                    "algorithmic_flops_per_launch": int(fl), "chunk_heads_per_launch": chunks,
+                    "avg_launch_ms": round(avg_s * 1e3, 4)}
     E = 2 if w.dtype == "bf16" else 4
     gw = d if w.gate == "vector" else (0 if w.gate == "none" else 1)
     by_f, by_b = algorithmic_bytes_per_token_head(d, d, E, gw)
     by = (by_f + by_b + 3 * 4 * d) * w.token_heads   # + theta read, dtheta written (fp32 per channel)
+    cpu = None if args.no_cpu_baseline else phase_cpu_baseline(w, inp_cpu)
     line = {
         "metric": "chunkwise phase-controlled gate fwd+bwd tokens/s", "value": round(w.B * w.T / (ms / 1e3), 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": steps, "ms_per_step": round(ms, 4), "fwd_ms": round(fms, 4),
         "bwd_ms": round(bms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"phase-controlled gate, chunks of 16: gate={w.gate} B={w.B} H={w.H} T={w.T} d={d}, "
-                               f"fp32 arithmetic, one workgroup per (batch, head)", "global_batch": w.B,
+                               f"fp32 arithmetic on the vector ALUs", "global_batch": w.B,
                    "seq_len": w.T, "heads": w.H, "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "kernels": per_kernel,
         "step_hbm": {"algorithmic_bytes": int(by), "achieved_gbs": round(by / (ms / 1e3) / 1e9, 1),
                      "hbm_frac": round(by / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 5)},
-        "workgroups": w.B * w.H,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def phase_cpu_baseline(w, inp_cpu):
+    """The phase-controlled gate's fp64 oracle (oracle/sfda.py: the complex
+    recurrence and its reverse mode, numpy) on a bounded sample of the workload:
+    the first heads of the first sequence over the first steps."""
+    from oracle import sfda
+    from delta_rule_linear_gated_amd import workloads as W
+
+    nh, Ts = min(w.H, 4), min(w.T, 4096)
+    heads = [(0, h) for h in range(nh)]
+    f = {}
+    for n, t in inp_cpu.items():
+        x = W.to_f64(t, heads)
+        if x is not None and n not in ("h0", "h0_im", "dhT", "dhT_im"):
+            x = x[:, :, :Ts]
+        f[n] = x
+    print(f"[bench] cpu baseline: phase oracle on {nh} heads x T={Ts}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    sfda.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["theta"], f["h0"], f["h0_im"])
+    sfda.backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["theta"], f["h0"], f["h0_im"], f["do"], f["dhT"],
+                  f["dhT_im"])
+    dt = time.perf_counter() - t0
+    tok = nh * Ts / w.H   # tokens of whole sequences: the sample covers nh / H of a sequence's heads
+    return {"value": round(tok / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nh} heads of sequence 0, steps 0..{Ts - 1}, fwd+bwd, fp64 numpy ({dt:.1f} s wall)"}
 
 
 def cpu_baseline(w, inp_cpu):

@@ -30,7 +30,7 @@ DN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("dn_states_bytes", "dn_states_layout", "dn_workspace_bytes", "dn_workspace_layout", "dn_chunk_fwd",
            "dn_chunk_fwd_noalloc", "dn_chunk_bwd", "dn_recurrent_fwd", "dn_recurrent_phase_fwd", "dn_phase_states_bytes",
-           "dn_chunk_phase_fwd", "dn_chunk_phase_bwd", "dn_status_string", "dn_last_error",
+           "dn_phase_workspace_bytes", "dn_chunk_phase_fwd", "dn_chunk_phase_bwd", "dn_status_string", "dn_last_error",
            "dn_profile_enable", "dn_profile_collect")
 
 
@@ -80,9 +80,11 @@ def lib():
     L.dn_chunk_bwd.restype = i32
     L.dn_phase_states_bytes.argtypes = [sp]
     L.dn_phase_states_bytes.restype = sz
-    L.dn_chunk_phase_fwd.argtypes = [sp] + [vp] * 13
+    L.dn_phase_workspace_bytes.argtypes = [sp, i32]
+    L.dn_phase_workspace_bytes.restype = sz
+    L.dn_chunk_phase_fwd.argtypes = [sp] + [vp] * 13 + [sz, vp]
     L.dn_chunk_phase_fwd.restype = i32
-    L.dn_chunk_phase_bwd.argtypes = [sp] + [vp] * 19
+    L.dn_chunk_phase_bwd.argtypes = [sp] + [vp] * 19 + [sz, vp]
     L.dn_chunk_phase_bwd.restype = i32
     L.dn_status_string.argtypes = [i32]
     L.dn_status_string.restype = ctypes.c_char_p
@@ -219,19 +221,25 @@ def dn_phase_states_bytes(shape: Shape) -> int:
     return lib().dn_phase_states_bytes(ctypes.byref(shape))
 
 
-def dn_chunk_phase_fwd(shape, q, k, v, beta, g, theta, h0_re, h0_im, o, hT_re, hT_im, states, stream=None) -> int:
+def dn_phase_workspace_bytes(shape: Shape, pass_: int) -> int:
+    return lib().dn_phase_workspace_bytes(ctypes.byref(shape), pass_)
+
+
+def dn_chunk_phase_fwd(shape, q, k, v, beta, g, theta, h0_re, h0_im, o, hT_re, hT_im, states, ws=None, ws_bytes=0,
+                       stream=None) -> int:
     """Raw call; returns the dn_status (no exception)."""
     return lib().dn_chunk_phase_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(theta),
                                     _ptr(h0_re), _ptr(h0_im), _ptr(o), _ptr(hT_re), _ptr(hT_im), _ptr(states),
-                                    _stream(stream))
+                                    _ptr(ws), ws_bytes, _stream(stream))
 
 
 def dn_chunk_phase_bwd(shape, q, k, v, beta, g, theta, dout, dhT_re, dhT_im, states, dq, dk, dv, dbeta, dg, dtheta,
-                       dh0_re, dh0_im, stream=None) -> int:
+                       dh0_re, dh0_im, ws=None, ws_bytes=0, stream=None) -> int:
     """Raw call; returns the dn_status (no exception)."""
     return lib().dn_chunk_phase_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(theta),
                                     _ptr(dout), _ptr(dhT_re), _ptr(dhT_im), _ptr(states), _ptr(dq), _ptr(dk), _ptr(dv),
-                                    _ptr(dbeta), _ptr(dg), _ptr(dtheta), _ptr(dh0_re), _ptr(dh0_im), _stream(stream))
+                                    _ptr(dbeta), _ptr(dg), _ptr(dtheta), _ptr(dh0_re), _ptr(dh0_im), _ptr(ws),
+                                    ws_bytes, _stream(stream))
 
 
 # ------------------------------------------------------------------ convenience
@@ -415,7 +423,9 @@ def chunk_phase_fwd(q, k, v, beta, g, theta, h0_re=None, h0_im=None, gate=None, 
     hT_im = torch.empty_like(hT_re)
     states = (torch.empty(max(dn_phase_states_bytes(sh) // 4, 1), dtype=torch.float32, device=q.device)
               if save_states else None)
-    _check(dn_chunk_phase_fwd(sh, q, k, v, beta, g, theta, h0_re, h0_im, o, hT_re, hT_im, states, stream))
+    nws = 0 if save_states else dn_phase_workspace_bytes(sh, DN_PASS_FWD)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device) if nws else None
+    _check(dn_chunk_phase_fwd(sh, q, k, v, beta, g, theta, h0_re, h0_im, o, hT_re, hT_im, states, ws, nws, stream))
     return o, hT_re, hT_im, states
 
 
@@ -432,8 +442,10 @@ def chunk_phase_bwd(q, k, v, beta, g, theta, do, dhT_re, dhT_im, states, gate=No
            "dtheta": torch.empty_like(theta),
            "dh0_re": torch.empty(B, H, v.shape[-1], dk, dtype=torch.float32, device=q.device)}
     out["dh0_im"] = torch.empty_like(out["dh0_re"])
+    nws = dn_phase_workspace_bytes(sh, DN_PASS_BWD)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
     _check(dn_chunk_phase_bwd(sh, q, k, v, beta, g, theta, do, dhT_re, dhT_im, states, out["dq"], out["dk"], out["dv"],
-                              out["dbeta"], out["dg"], out["dtheta"], out["dh0_re"], out["dh0_im"], stream))
+                              out["dbeta"], out["dg"], out["dtheta"], out["dh0_re"], out["dh0_im"], ws, nws, stream))
     return out
 
 

@@ -391,6 +391,18 @@ dn_status phase_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
     return DN_OK;
 }
 
+// Regions of the phase gate's buffers (fp32, each rounded up to 256 bytes):
+// saved = chunk states, then the per-chunk T, P, G; backward workspace = lambda,
+// then the state cotangent leaving each chunk.
+struct PhaseSizes {
+    size_t st, mats, lam, ds1;
+};
+PhaseSizes phase_sizes(const Dims& d) {
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    return {al(d.BH * d.NT * 2 * d.dv * d.dk * 4), al(d.BH * d.NT * 6 * 16 * 16 * 4), al(d.BH * d.NT * 2 * d.dv * 16 * 4),
+            al(d.BH * d.NT * 2 * d.dv * d.dk * 4)};
+}
+
 }  // namespace
 
 extern "C" {
@@ -399,20 +411,36 @@ size_t dn_phase_states_bytes(const dn_shape* shape) {
     dn::Problem pr;
     Dims d;
     if (phase_shape(shape, &pr, &d) != DN_OK) return 0;
-    return d.BH * d.NT * 2 * d.dv * d.dk * 4;
+    const PhaseSizes z = phase_sizes(d);
+    return z.st + z.mats;
+}
+
+size_t dn_phase_workspace_bytes(const dn_shape* shape, int pass) {
+    dn::Problem pr;
+    Dims d;
+    if (phase_shape(shape, &pr, &d) != DN_OK) return 0;
+    const PhaseSizes z = phase_sizes(d);
+    if (pass == DN_PASS_FWD) return z.mats;
+    if (pass == DN_PASS_BWD) return z.lam + z.ds1;
+    return 0;
 }
 
 dn_status dn_chunk_phase_fwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
                              const float* g, const float* theta, const float* h0_re, const float* h0_im, void* o,
-                             float* hT_re, float* hT_im, float* states, void* stream) {
+                             float* hT_re, float* hT_im, float* states, void* ws, size_t ws_bytes,
+                             void* stream) {
     g_err[0] = '\0';
     dn::Problem pr;
     Dims d;
     DN_TRY(phase_shape(shape, &pr, &d));
     const size_t nk = d.BH * d.T * d.dk * d.E, nv = d.BH * d.T * d.dv * d.E, nb = d.BH * d.T * 4;
     const size_t ng = pr.gate == DN_GATE_NONE ? 0 : d.BH * d.T * d.gw * 4, nth = d.BH * d.T * d.dk * 4;
-    const size_t ns = d.BH * d.dv * d.dk * 4, nst = d.BH * d.NT * 2 * d.dv * d.dk * 4;
+    const PhaseSizes z = phase_sizes(d);
+    const size_t ns = d.BH * d.dv * d.dk * 4, nst = z.st + z.mats;
+    const size_t nws = states ? 0 : z.mats;   // with saved states the matrices go there
     if (pr.gate == DN_GATE_NONE && g) return fail(DN_ERR_INVALID, "g must be NULL without a gate");
+    if (ws_bytes < nws) return fail(DN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, nws);
+    DN_TRY(need(ws, nws, "workspace"));
     DN_TRY(need(q, nk, "q"));
     DN_TRY(need(k, nk, "k"));
     DN_TRY(need(v, nv, "v"));
@@ -431,7 +459,8 @@ dn_status dn_chunk_phase_fwd(const dn_shape* shape, const void* q, const void* k
                           {"o", o, nv, true},
                           {"hT_re", hT_re, ns, true},
                           {"hT_im", hT_im, ns, true},
-                          {"states", states, nst, true}}));
+                          {"states", states, nst, true},
+                          {"workspace", ws, nws, true}}));
     dn::Params p{};
     p.BH = (int)d.BH;
     p.T = (int)d.T;
@@ -449,7 +478,10 @@ dn_status dn_chunk_phase_fwd(const dn_shape* shape, const void* q, const void* k
     p.o = o;
     p.hT = hT_re;
     p.hT_im = hT_im;
-    const hipError_t e = dn::launch_phase(pr, p, states, false, static_cast<hipStream_t>(stream));
+    dn::PhaseBufs f{};
+    f.states = states;
+    f.mats = states ? reinterpret_cast<float*>(reinterpret_cast<char*>(states) + z.st) : static_cast<float*>(ws);
+    const hipError_t e = dn::launch_phase(pr, p, f, false, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;
 }
@@ -457,15 +489,19 @@ dn_status dn_chunk_phase_fwd(const dn_shape* shape, const void* q, const void* k
 dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
                              const float* g, const float* theta, const void* dout, const float* dhT_re,
                              const float* dhT_im, const float* states, void* dq, void* dk, void* dv, float* dbeta,
-                             float* dg, float* dtheta, float* dh0_re, float* dh0_im, void* stream) {
+                             float* dg, float* dtheta, float* dh0_re, float* dh0_im, void* ws, size_t ws_bytes,
+                             void* stream) {
     g_err[0] = '\0';
     dn::Problem pr;
     Dims d;
     DN_TRY(phase_shape(shape, &pr, &d));
     const size_t nk = d.BH * d.T * d.dk * d.E, nv = d.BH * d.T * d.dv * d.E, nb = d.BH * d.T * 4;
     const size_t ng = pr.gate == DN_GATE_NONE ? 0 : d.BH * d.T * d.gw * 4, nth = d.BH * d.T * d.dk * 4;
-    const size_t ns = d.BH * d.dv * d.dk * 4, nst = d.BH * d.NT * 2 * d.dv * d.dk * 4;
+    const PhaseSizes z = phase_sizes(d);
+    const size_t ns = d.BH * d.dv * d.dk * 4, nst = z.st + z.mats, nws = z.lam + z.ds1;
     if (pr.gate == DN_GATE_NONE && (g || dg)) return fail(DN_ERR_INVALID, "g and dg must be NULL without a gate");
+    if (ws_bytes < nws) return fail(DN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, nws);
+    DN_TRY(need(ws, nws, "workspace"));
     DN_TRY(need(q, nk, "q"));
     DN_TRY(need(k, nk, "k"));
     DN_TRY(need(v, nv, "v"));
@@ -497,7 +533,8 @@ dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k
                           {"dg", dg, ng, true},
                           {"dtheta", dtheta, nth, true},
                           {"dh0_re", dh0_re, ns, true},
-                          {"dh0_im", dh0_im, ns, true}}));
+                          {"dh0_im", dh0_im, ns, true},
+                          {"workspace", ws, nws, true}}));
     dn::Params p{};
     p.BH = (int)d.BH;
     p.T = (int)d.T;
@@ -521,8 +558,12 @@ dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k
     p.dtheta = dtheta;
     p.dh0 = dh0_re;
     p.dh0_im = dh0_im;
-    const hipError_t e =
-        dn::launch_phase(pr, p, const_cast<float*>(states), true, static_cast<hipStream_t>(stream));
+    dn::PhaseBufs f{};
+    f.states = const_cast<float*>(states);
+    f.mats = reinterpret_cast<float*>(reinterpret_cast<char*>(f.states) + z.st);
+    f.lam = static_cast<float*>(ws);
+    f.dS1 = reinterpret_cast<float*>(static_cast<char*>(ws) + z.lam);
+    const hipError_t e = dn::launch_phase(pr, p, f, true, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;
 }

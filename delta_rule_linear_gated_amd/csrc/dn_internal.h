@@ -121,10 +121,20 @@ hipError_t launch_backward(const Problem& pr, const Params& p, bool have_states,
 hipError_t launch_scan_combine(const Params& p, int DK, bool forward, hipStream_t stream);
 // Recurrent form: T steps per head, state p.hT (fp32, in place), outputs p.o.
 hipError_t launch_recurrent(const Problem& pr, const Params& p, hipStream_t stream);
-// Chunkwise form of the phase-controlled gate (dn_phase.hip): forward (o, hT /
-// hT_im; the complex state entering each chunk to `states` when not NULL) or
-// backward (from those states), one workgroup per head, chunks of 16.
-hipError_t launch_phase(const Problem& pr, const Params& p, float* states, bool backward, hipStream_t stream);
+// Chunkwise form of the phase-controlled gate (dn_phase.hip), chunks of 16, fp32:
+//   states [BH][NT][2][DV][DK]  complex state entering each chunk (forward: written
+//                               when not NULL; backward: read)
+//   mats   [BH][NT][6][16][16]  T re, T im, P re, P im, G re, G im per chunk (written
+//                               by the forward, read by the backward)
+//   lam    [BH][NT][2][DV][16]  lambda of each chunk, row v then step (backward scratch)
+//   dS1    [BH][NT][2][DV][DK]  state cotangent leaving each chunk (backward scratch)
+struct PhaseBufs {
+    float* states;
+    float* mats;
+    float* lam;
+    float* dS1;
+};
+hipError_t launch_phase(const Problem& pr, const Params& p, const PhaseBufs& f, bool backward, hipStream_t stream);
 bool supported(const Problem& pr);
 // Scratch array of dn_chunk_fwd_noalloc (dn_noalloc.hip): the current device's
 // address of it, looked up once per device.

@@ -24,11 +24,21 @@
 // each exp as Eb conj(E), and dg, dtheta are the real and imaginary parts of
 // its reverse cumulative sum.
 //
-// One workgroup per head walks the chunks in order (forward) or in reverse.
-// The state (and its cotangent) lives in registers: a group of PG = 256 / D
-// consecutive lanes owns one state row v, each lane NC = D / PG consecutive key
-// channels of it; sums over the key channels are lane-group sums.  All
-// arithmetic is fp32 on the vector ALUs.
+// Four kernels, all fp32 on the vector ALUs:
+//   phase_prep       grid (chunk, head), every chunk at once: gam, the pairwise
+//                    G and H, T by forward substitution; T, P, G per chunk out.
+//   phase_fwd_state  grid (head, block of 16 state rows), chunks in order: the
+//                    state recurrence, O, the chunk-entry states.
+//   phase_bwd_state  grid (head, block of 16 rows), chunks last to first: Ub,
+//                    lambda = T^H Ub, dv and the state cotangent; lambda and the
+//                    cotangent leaving each chunk out.
+//   phase_bwd_chunk  grid (chunk, head), every chunk at once: X and U again, the
+//                    pair cotangents, dq, dk, dbeta, dg, dtheta.
+// Row v of S1 depends only on row v of S0 (and row v of dS0 only on row v of
+// dS1), so the sequential kernels split the state into blocks of 16 rows.  There
+// a row belongs to 16 consecutive lanes (one DPP row), each lane D / 16
+// consecutive key channels, and lane j also holds step j of the row's per-step
+// values: sums over the key channels are 16-lane DPP sums.
 #include <hip/hip_runtime.h>
 
 #include "dn.h"
@@ -39,7 +49,11 @@ namespace dn {
 
 namespace {
 
-constexpr int kPT = 256;   // threads per workgroup
+constexpr int kPT = 256;           // threads per workgroup
+constexpr int kC = 16;             // chunk length
+constexpr int kBV = 16;            // state rows per workgroup of the sequential kernels
+constexpr int kCC = kC * kC;
+constexpr int kMats = 6 * kCC;     // per chunk: T re, T im, P re, P im, G re, G im
 
 struct cf {
     float r, i;
@@ -59,124 +73,77 @@ __device__ __forceinline__ cf cexp_(float re, float im) {
     return {m * __builtin_amdgcn_cosf(fr), m * __builtin_amdgcn_sinf(fr)};
 }
 
-// LDS of the parts both passes share: the chunk's rows and per-chunk matrices.
-template <int D, int C> struct PhaseTiles {
-    float K[C][D], Q[C][D], V[C][D];
-    float gr[C][D], gi[C][D];          // cumulative log gate (re, im)
-    float kgr[C][D], kgi[C][D];        // K E
-    float qgr[C][D], qgi[C][D];        // Q E
-    float kdr[C][D], kdi[C][D];        // K exp(gam_L - gam)
-    float Gr[C][C + 1], Gi[C][C + 1];  // G (without beta)
-    float Tr[C][C + 1], Ti[C][C + 1];  // A, then T = (I + A)^{-1}
-    float Pr[C][C + 1], Pi[C][C + 1];  // P
-    float beta[C];
+// ---------------------------------------------------------------------------
+// A chunk's K, Q and log gate l = g + i theta in registers: thread (channel
+// c = tid % D, row group tid / D) holds NR consecutive rows, so the in-chunk
+// cumulative sum is a prefix over its own rows plus the totals of the earlier
+// row groups.  Rows at or past `valid` read row 0 (branch-free loads) and count
+// as zero, gate included: they leave the state unchanged.
+template <typename TI, int GATE, int D> struct ChunkIn {
+    static constexpr int RG = kPT / D, NR = kC / RG;
+    static_assert(RG * NR == kC, "rows");
+    float k[NR], q[NR], lr[NR], li[NR];
+    static __device__ __forceinline__ int chan() { return threadIdx.x % D; }
+    static __device__ __forceinline__ int grp() { return threadIdx.x / D; }
+    static __device__ __forceinline__ int row(int r) { return grp() * NR + r; }
+    __device__ __forceinline__ void load(const Params& p, long row0, int valid) {
+        const TI* __restrict__ kp = static_cast<const TI*>(p.k);
+        const TI* __restrict__ qp = static_cast<const TI*>(p.q);
+        const int c = chan();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int t = row(r);
+            const bool ok = t < valid;
+            const long rr = row0 + (ok ? t : 0);
+            const long e = rr * D + c;
+            const float kk = to_f(kp[e]), qq = to_f(qp[e]), th = p.theta[e];
+            float g = 0.f;
+            if (GATE == kGateScalar) g = p.g[rr];
+            if (GATE == kGateVector) g = p.g[e];
+            k[r] = ok ? kk : 0.f;
+            q[r] = ok ? qq : 0.f;
+            lr[r] = ok ? g : 0.f;
+            li[r] = ok ? th : 0.f;
+        }
+    }
+    // Inclusive prefix over the thread's rows, in place; the totals to tr / ti.
+    __device__ __forceinline__ void prefix(float (*tr)[D], float (*ti)[D]) {
+#pragma unroll
+        for (int r = 1; r < NR; ++r) {
+            lr[r] += lr[r - 1];
+            li[r] += li[r - 1];
+        }
+        tr[grp()][chan()] = lr[NR - 1];
+        ti[grp()][chan()] = li[NR - 1];
+    }
+    // After a barrier: the earlier groups' totals are added (lr, li become gam);
+    // returns gam at the chunk's last row, summed in the same order as the last
+    // row's own value (the rows past `valid` add zeros), so exp(gam_L - gam_L) = 1.
+    __device__ __forceinline__ cf finish(const float (*tr)[D], const float (*ti)[D]) {
+        const int c = chan(), g0 = grp();
+        float orr = 0.f, oi = 0.f, ar = 0.f, ai = 0.f;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const float xr = tr[g][c], xi = ti[g][c];
+            if (g < g0) {
+                orr += xr;
+                oi += xi;
+            }
+            ar += xr;
+            ai += xi;
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            lr[r] += orr;
+            li[r] += oi;
+        }
+        return {ar, ai};
+    }
 };
 
-// Load the chunk's rows, form gam, the scaled tiles, G, P and T.  Rows past
-// `valid` are zero (their gate too), which leaves the state unchanged.  Begins
-// writing LDS at once (the caller's previous barrier ordered it after the last
-// reads) and ends with a barrier.
-template <typename TI, int GATE, int D, int C>
-__device__ void chunk_setup(const Params& p, PhaseTiles<D, C>& s, long row0, int valid) {
-    const int tid = threadIdx.x;
-    const TI* __restrict__ k = static_cast<const TI*>(p.k);
-    const TI* __restrict__ q = static_cast<const TI*>(p.q);
-    const TI* __restrict__ v = static_cast<const TI*>(p.v);
-    for (int idx = tid; idx < C * D; idx += kPT) {
-        const int t = idx / D, c = idx % D;
-        const bool ok = t < valid;
-        const long e = (row0 + (ok ? t : 0)) * D + c;
-        s.K[t][c] = ok ? to_f(k[e]) : 0.f;
-        s.Q[t][c] = ok ? to_f(q[e]) : 0.f;
-        s.V[t][c] = ok ? to_f(v[e]) : 0.f;
-        float g = 0.f;
-        if (GATE == kGateScalar) g = p.g[row0 + (ok ? t : 0)];
-        if (GATE == kGateVector) g = p.g[e];
-        s.gr[t][c] = ok ? g : 0.f;
-        s.gi[t][c] = ok ? p.theta[e] : 0.f;
-    }
-    if (tid < C) s.beta[tid] = tid < valid ? p.beta[row0 + tid] : 0.f;
-    __syncthreads();
-    if (tid < D) {   // in-chunk cumulative sum, one channel per thread
-        float ar = 0.f, ai = 0.f;
-        for (int t = 0; t < C; ++t) {
-            ar += s.gr[t][tid];
-            ai += s.gi[t][tid];
-            s.gr[t][tid] = ar;
-            s.gi[t][tid] = ai;
-        }
-    }
-    __syncthreads();
-    const int L = valid - 1;
-    for (int idx = tid; idx < C * D; idx += kPT) {
-        const int t = idx / D, c = idx % D;
-        const cf E = cexp_(s.gr[t][c], s.gi[t][c]);
-        const cf Ed = cexp_(s.gr[L][c] - s.gr[t][c], s.gi[L][c] - s.gi[t][c]);
-        const float kk = s.K[t][c], qq = s.Q[t][c];
-        s.kgr[t][c] = kk * E.r;
-        s.kgi[t][c] = kk * E.i;
-        s.qgr[t][c] = qq * E.r;
-        s.qgi[t][c] = qq * E.i;
-        s.kdr[t][c] = kk * Ed.r;
-        s.kdi[t][c] = kk * Ed.i;
-    }
-    // pairwise Gram products (u <= t), each factor exp(gam_t - gam_u) formed per channel
-    for (int pr = tid; pr < C * C; pr += kPT) {
-        const int t = pr / C, u = pr % C;
-        cf Gs = {0.f, 0.f}, Hs = {0.f, 0.f};
-        if (u <= t) {
-            #pragma unroll 4
-            for (int c = 0; c < D; ++c) {
-                const cf f = cexp_(s.gr[t][c] - s.gr[u][c], s.gi[t][c] - s.gi[u][c]);
-                const float ku = s.K[u][c];
-                Gs = cadd(Gs, cscale(f, s.K[t][c] * ku));
-                Hs = cadd(Hs, cscale(f, s.Q[t][c] * ku));
-            }
-        }
-        s.Gr[t][u] = Gs.r;
-        s.Gi[t][u] = Gs.i;
-        const float b = s.beta[t];
-        s.Tr[t][u] = u < t ? b * Gs.r : 0.f;   // A
-        s.Ti[t][u] = u < t ? b * Gs.i : 0.f;
-        s.Pr[t][u] = Hs.r;                     // P (zero above the diagonal)
-        s.Pi[t][u] = Hs.i;
-    }
-    __syncthreads();
-    // T = (I + A)^{-1}: column u by forward substitution, one thread per column,
-    // every column formed from A before any is written back over it
-    cf x[C];
-    if (tid < C) {
-        const int u = tid;
-#pragma unroll
-        for (int i = 0; i < C; ++i) x[i] = {i == u ? 1.f : 0.f, 0.f};
-#pragma unroll
-        for (int i = 1; i < C; ++i) {
-            cf acc = x[i];
-#pragma unroll
-            for (int j = 0; j < i; ++j) acc = csub(acc, cmul({s.Tr[i][j], s.Ti[i][j]}, x[j]));
-            x[i] = acc;
-        }
-    }
-    __syncthreads();
-    if (tid < C) {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            s.Tr[i][tid] = x[i].r;
-            s.Ti[i][tid] = x[i].i;
-        }
-    }
-    __syncthreads();
-}
-
-// Sum of x over the PG consecutive lanes of a state row's group.
-template <int PG> __device__ __forceinline__ float row_sum(float x) { return group_sum<PG>(x); }
-
-// ---------------------------------------------------------------------------
-// Per-row complex vectors over the chunk's steps, [C][D + 1] (column v for row v
-// of the state).  A row's lanes are one lane group of one wave: what one lane
-// stores there the others read back in program order, with no barrier.
-template <int D, int C> struct RowVecs {
-    float r[C][D + 1], i[C][D + 1];
+// Per-step complex values of W state rows, [C][W + 1] (column v for row v).
+template <int W> struct Rows {
+    float r[kC][W + 1], i[kC][W + 1];
     __device__ __forceinline__ cf get(int t, int v) const { return {r[t][v], i[t][v]}; }
     __device__ __forceinline__ void set(int t, int v, cf x) {
         r[t][v] = x.r;
@@ -184,35 +151,176 @@ template <int D, int C> struct RowVecs {
     }
 };
 
-// The row's sums over the key channels of (A_t . S_row) for every step t, A one
-// or two [C][D] complex tiles given by pointers; lane 0 of the group stores them.
-template <int D, int C, int PG, int NC>
-__device__ __forceinline__ void row_products(const float (*ar)[D], const float (*ai)[D], const float* sr, const float* si,
-                                             int v, int c0, bool conj_a, RowVecs<D, C>& out) {
-#pragma unroll 1
-    for (int t = 0; t < C; ++t) {
-        cf x = {0.f, 0.f};
+// ---------------------------------------------------------------------------
+// phase_prep: gam, G, P and T of one chunk; out: the chunk's record of mats.
+template <int D> struct PrepLds {
+    float K[kC][D + 1], Q[kC][D + 1], gr[kC][D + 1], gi[kC][D + 1];   // rows of D + 1: the pair
+    float tr[kPT / D][D], ti[kPT / D][D];                              // loop reads a column of 16 rows
+    float Ar[kC][kC + 1], Ai[kC][kC + 1];
+    float beta[kC];
+};
+
+template <typename TI, int GATE, int D>
+__global__ __launch_bounds__(kPT) void phase_prep_kernel(Params p, float* __restrict__ mats) {
+    using CI = ChunkIn<TI, GATE, D>;
+    __shared__ PrepLds<D> s;
+    const int tid = threadIdx.x, n = blockIdx.x, bh = blockIdx.y;
+    const int t0 = n * kC, valid = min(kC, p.T - t0);
+    const long row0 = (long)bh * p.T + t0;
+    CI in;
+    in.load(p, row0, valid);
+    const float bt = p.beta[row0 + min(tid % kC, valid - 1)];
+    in.prefix(s.tr, s.ti);
+    if (tid < kC) s.beta[tid] = tid < valid ? bt : 0.f;
+    __syncthreads();
+    in.finish(s.tr, s.ti);
+    {
+        const int c = CI::chan();
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const cf A = {ar[t][c0 + c], conj_a ? -ai[t][c0 + c] : ai[t][c0 + c]};
-            x = cadd(x, cmul(A, {sr[c], si[c]}));
+        for (int r = 0; r < CI::NR; ++r) {
+            const int t = CI::row(r);
+            s.K[t][c] = in.k[r];
+            s.Q[t][c] = in.q[r];
+            s.gr[t][c] = in.lr[r];
+            s.gi[t][c] = in.li[r];
         }
-        x = {row_sum<PG>(x.r), row_sum<PG>(x.i)};
-        if (threadIdx.x % PG == 0) out.set(t, v, x);
+    }
+    __syncthreads();
+    float* __restrict__ m = mats + ((long)bh * p.NT + n) * kMats;
+    {   // pair (t, u), u <= t, one per thread
+        const int t = tid / kC, u = tid % kC;
+        cf Gs = {0.f, 0.f}, Hs = {0.f, 0.f};
+        if (u <= t) {
+#pragma unroll 4
+            for (int c = 0; c < D; ++c) {
+                const cf f = cexp_(s.gr[t][c] - s.gr[u][c], s.gi[t][c] - s.gi[u][c]);
+                const float ku = s.K[u][c];
+                Gs = cadd(Gs, cscale(f, s.K[t][c] * ku));
+                Hs = cadd(Hs, cscale(f, s.Q[t][c] * ku));
+            }
+        }
+        const float b = s.beta[t];
+        s.Ar[t][u] = u < t ? b * Gs.r : 0.f;
+        s.Ai[t][u] = u < t ? b * Gs.i : 0.f;
+        m[2 * kCC + tid] = Hs.r;   // P (zero above the diagonal)
+        m[3 * kCC + tid] = Hs.i;
+        m[4 * kCC + tid] = Gs.r;
+        m[5 * kCC + tid] = Gs.i;
+    }
+    __syncthreads();
+    if (tid < kC) {   // T = (I + A)^{-1}: column u by forward substitution
+        const int u = tid;
+        cf x[kC];
+#pragma unroll
+        for (int i = 0; i < kC; ++i) x[i] = {i == u ? 1.f : 0.f, 0.f};
+#pragma unroll
+        for (int i = 1; i < kC; ++i) {
+            cf acc = x[i];
+#pragma unroll
+            for (int j = 0; j < i; ++j) acc = csub(acc, cmul({s.Ar[i][j], s.Ai[i][j]}, x[j]));
+            x[i] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+            m[i * kC + u] = x[i].r;
+            m[kCC + i * kC + u] = x[i].i;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Forward: one workgroup per head.  states (if not NULL): the complex state
-// entering each chunk, [BH][NT][2][D][D] fp32 (real part, then imaginary).
-template <typename TI, int GATE, int D, int C>
-__global__ __launch_bounds__(kPT) void phase_fwd_kernel(Params p, float* states) {
-    constexpr int PG = kPT / D, NC = D / PG;
-    __shared__ PhaseTiles<D, C> s;
-    __shared__ RowVecs<D, C> X, Y, U;
-    __shared__ float Os[C][D];
-    const int tid = threadIdx.x, v = tid / PG, j = tid % PG, c0 = j * NC;
-    const int bh = blockIdx.x;
+// Register staging of the sequential kernels: the chunk's K, Q, gate, one
+// 16-column block of a [T][D] tile (V forward, dO backward), T and P, beta.
+template <typename TI, int GATE, int D> struct SeqIn {
+    ChunkIn<TI, GATE, D> in;
+    float blk;    // element (tid / 16, tid % 16) of the block
+    float m[4];   // element tid of T re, T im, P re, P im
+    float bt;     // beta of step tid % 16
+    __device__ __forceinline__ void load(const Params& p, const void* tile, const float* __restrict__ mats, int bh,
+                                         int col0, int n) {
+        const int tid = threadIdx.x, t0 = n * kC, valid = min(kC, p.T - t0);
+        const long row0 = (long)bh * p.T + t0;
+        in.load(p, row0, valid);
+        const int t = tid / kBV, v = tid % kBV;
+        const float x = to_f(static_cast<const TI*>(tile)[(row0 + min(t, valid - 1)) * D + col0 + v]);
+        blk = t < valid ? x : 0.f;
+        const float* mc = mats + ((long)bh * p.NT + n) * kMats;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = mc[j * kCC + tid];
+        const int s = tid % kC;
+        const float b = p.beta[row0 + min(s, valid - 1)];
+        bt = s < valid ? b : 0.f;
+    }
+};
+
+// LDS of the sequential kernels: the gated tiles (rows of D: lane j of a row
+// reads D / 16 consecutive channels, the tiles are written a row at a time),
+// the block tile, T, P, beta and the rows' per-step vectors.
+template <int D> struct SeqLds {
+    float kgr[kC][D], kgi[kC][D];   // K E
+    float qgr[kC][D], qgi[kC][D];   // Q E
+    float kdr[kC][D], kdi[kC][D];   // K exp(gam_L - gam)
+    float elr[D], eli[D];           // E at the last row
+    float tr[kPT / D][D], ti[kPT / D][D];
+    float B[kC][kBV + 1];           // V (forward) or dO (backward) block
+    float Tr[kC][kC + 1], Ti[kC][kC + 1], Pr[kC][kC + 1], Pi[kC][kC + 1];
+    float beta[kC];
+    Rows<kBV> Ra, Rb;               // forward: R, U; backward: Ub, lambda
+    float Os[kC][kBV + 1];          // O (forward) or dv (backward) block, for the write-back
+};
+
+// Commit of the staged registers (phase A of a chunk): the gate's partial sums,
+// the block tile, T, P, beta.
+template <typename TI, int GATE, int D>
+__device__ __forceinline__ void seq_commit(SeqIn<TI, GATE, D>& x, SeqLds<D>& s) {
+    const int tid = threadIdx.x;
+    x.in.prefix(s.tr, s.ti);
+    s.B[tid / kBV][tid % kBV] = x.blk;
+    const int t = tid / kC, u = tid % kC;
+    s.Tr[t][u] = x.m[0];
+    s.Ti[t][u] = x.m[1];
+    s.Pr[t][u] = x.m[2];
+    s.Pi[t][u] = x.m[3];
+    if (tid < kC) s.beta[tid] = x.bt;
+}
+
+// Phase B: gam, then the gated tiles and E_L from the thread's own rows.
+template <typename TI, int GATE, int D>
+__device__ __forceinline__ void seq_tiles(SeqIn<TI, GATE, D>& x, SeqLds<D>& s) {
+    using CI = ChunkIn<TI, GATE, D>;
+    const cf gl = x.in.finish(s.tr, s.ti);
+    const int c = CI::chan();
+#pragma unroll
+    for (int r = 0; r < CI::NR; ++r) {
+        const int t = CI::row(r);
+        const cf E = cexp_(x.in.lr[r], x.in.li[r]);
+        const cf Ed = cexp_(gl.r - x.in.lr[r], gl.i - x.in.li[r]);
+        const float kk = x.in.k[r], qq = x.in.q[r];
+        s.kgr[t][c] = kk * E.r;
+        s.kgi[t][c] = kk * E.i;
+        s.qgr[t][c] = qq * E.r;
+        s.qgi[t][c] = qq * E.i;
+        s.kdr[t][c] = kk * Ed.r;
+        s.kdi[t][c] = kk * Ed.i;
+    }
+    if (CI::grp() == 0) {
+        const cf EL = cexp_(gl.r, gl.i);
+        s.elr[c] = EL.r;
+        s.eli[c] = EL.i;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// phase_fwd_state: one workgroup per (head, block of 16 state rows).  states
+// (if not NULL): the complex state entering each chunk, [BH][NT][2][D][D] fp32.
+template <typename TI, int GATE, int D>
+__global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const float* __restrict__ mats,
+                                                              float* __restrict__ states) {
+    constexpr int NB = D / kBV, NC = D / kC;
+    __shared__ __align__(16) SeqLds<D> s;
+    int bh, blk;
+    head_and_block(NB, p.BH, bh, blk);
+    const int tid = threadIdx.x, vl = tid / kC, j = tid % kC, c0 = j * NC, v = blk * kBV + vl;
     float sr[NC], si[NC];   // S[v][c0 .. c0 + NC)
     {
         const long o0 = ((long)bh * D + v) * D + c0;
@@ -223,10 +331,16 @@ __global__ __launch_bounds__(kPT) void phase_fwd_kernel(Params p, float* states)
         }
     }
     TI* __restrict__ out = static_cast<TI*>(p.o);
+    SeqIn<TI, GATE, D> x;
+    x.load(p, p.v, mats, bh, blk * kBV, 0);
     for (int n = 0; n < p.NT; ++n) {
-        const int t0 = n * C, valid = min(C, p.T - t0), L = valid - 1;
-        const long row0 = (long)bh * p.T + t0;
-        chunk_setup<TI, GATE, D, C>(p, s, row0, valid);
+        const int valid = min(kC, p.T - n * kC);
+        const long row0 = (long)bh * p.T + n * kC;
+        seq_commit(x, s);
+        __syncthreads();
+        seq_tiles(x, s);
+        x.load(p, p.v, mats, bh, blk * kBV, n + 1 < p.NT ? n + 1 : n);   // the next chunk, during this one
+        __syncthreads();
         if (states) {
             float* st = states + (((long)bh * p.NT + n) * 2 * D + v) * D + c0;
 #pragma unroll
@@ -235,45 +349,56 @@ __global__ __launch_bounds__(kPT) void phase_fwd_kernel(Params p, float* states)
                 st[(long)D * D + c] = si[c];
             }
         }
-        // X_t = (K E)_t . S_v and Y_t = (Q E)_t . S_v
-        row_products<D, C, PG, NC>(s.kgr, s.kgi, sr, si, v, c0, false, X);
-        row_products<D, C, PG, NC>(s.qgr, s.qgi, sr, si, v, c0, false, Y);
-        // U = T R with R = beta (V - X): the row's lanes take every PG-th step
-        for (int t = j; t < C; t += PG) {
-            cf u = {0.f, 0.f};
-            for (int w = 0; w <= t; ++w)
-                u = cadd(u, cmul({s.Tr[t][w], s.Ti[t][w]}, cscale(csub({s.V[w][v], 0.f}, X.get(w, v)), s.beta[w])));
-            U.set(t, v, u);
+        // X_t = (K E)_t . S_v and Y_t = (Q E)_t . S_v; lane j keeps step j
+        cf xj = {0.f, 0.f}, yj = {0.f, 0.f};
+#pragma unroll 4
+        for (int t = 0; t < kC; ++t) {
+            cf a = {0.f, 0.f}, b = {0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const cf S = {sr[c], si[c]};
+                a = cadd(a, cmul({s.kgr[t][c0 + c], s.kgi[t][c0 + c]}, S));
+                b = cadd(b, cmul({s.qgr[t][c0 + c], s.qgi[t][c0 + c]}, S));
+            }
+            a = {group_sum<kC>(a.r), group_sum<kC>(a.i)};
+            b = {group_sum<kC>(b.r), group_sum<kC>(b.i)};
+            if (t == j) {
+                xj = a;
+                yj = b;
+            }
         }
-        // O = Re(Y + P U)
-        for (int t = j; t < C; t += PG) {
-            cf o = Y.get(t, v);
-            for (int w = 0; w <= t; ++w) o = cadd(o, cmul({s.Pr[t][w], s.Pi[t][w]}, U.get(w, v)));
-            Os[t][v] = o.r;
-        }
-        // S1 = S0 diag(E_L) + U^T (K exp(gam_L - gam)), step by step over the lane's channels
+        // R_j = beta_j (V_j - X_j); U_j = sum_{w <= j} T_jw R_w; O_j = Re(Y_j + sum_{w <= j} P_jw U_w).
+        // A row's lanes are 16 lanes of one wave: what one stores, the others read back in
+        // program order with no barrier.
+        s.Ra.set(j, vl, cscale(csub({s.B[j][vl], 0.f}, xj), s.beta[j]));
+        cf u = {0.f, 0.f};
+        for (int w = 0; w <= j; ++w) u = cadd(u, cmul({s.Tr[j][w], s.Ti[j][w]}, s.Ra.get(w, vl)));
+        s.Rb.set(j, vl, u);
+        cf o = yj;
+        for (int w = 0; w <= j; ++w) o = cadd(o, cmul({s.Pr[j][w], s.Pi[j][w]}, s.Rb.get(w, vl)));
+        s.Os[j][vl] = o.r;
+        // S1 = S0 diag(E_L) + U^T (K exp(gam_L - gam))
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const cf S = cmul({sr[c], si[c]}, cexp_(s.gr[L][c0 + c], s.gi[L][c0 + c]));
+            const cf S = cmul({sr[c], si[c]}, {s.elr[c0 + c], s.eli[c0 + c]});
             sr[c] = S.r;
             si[c] = S.i;
         }
-#pragma unroll 1
-        for (int t = 0; t < C; ++t) {
-            const cf u = U.get(t, v);
+#pragma unroll 4
+        for (int t = 0; t < kC; ++t) {
+            const cf ut = s.Rb.get(t, vl);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const cf x = cmul(u, {s.kdr[t][c0 + c], s.kdi[t][c0 + c]});
-                sr[c] += x.r;
-                si[c] += x.i;
+                const cf y = cmul(ut, {s.kdr[t][c0 + c], s.kdi[t][c0 + c]});
+                sr[c] += y.r;
+                si[c] += y.i;
             }
         }
         __syncthreads();
-        for (int idx = tid; idx < C * D; idx += kPT) {
-            const int t = idx / D, c = idx % D;
-            if (t < valid) out[(row0 + t) * D + c] = from_f<TI>(Os[t][c]);
+        {
+            const int t = tid / kBV, vv = tid % kBV;
+            if (t < valid) out[(row0 + t) * D + blk * kBV + vv] = from_f<TI>(s.Os[t][vv]);
         }
-        __syncthreads();
     }
     const long o0 = ((long)bh * D + v) * D + c0;
 #pragma unroll
@@ -284,33 +409,21 @@ __global__ __launch_bounds__(kPT) void phase_fwd_kernel(Params p, float* states)
 }
 
 // ---------------------------------------------------------------------------
-// Reverse: one workgroup per head, chunks last to first, from the states the
-// forward saved.  Per chunk, with the cotangents dO (real) and dS1 (complex):
-//     Ub = conj(Kd) dS1^T + P^H dO          lambda = T^H Ub
-//     Ab = -strictly-lower(lambda U^H)      Pb = lower(dO U^H)
-//     dv = Re(diag(beta) lambda)            dbeta = Re rowsum(conj(lambda) (V - X)) + Re rowsum(conj(Ab) G)
+// phase_bwd_state: one workgroup per (head, block of 16 rows of the state
+// cotangent), chunks last to first.  Per chunk, with dS1 the cotangent leaving it:
+//     Ub = conj(Kd) dS1^T + P^H dO,   lambda = T^H Ub,   dv = Re(diag(beta) lambda)
 //     dS0 = dS1 diag(conj(E_L)) + dO^T conj(Q E) - (diag(beta) lambda)^T conj(K E)
-// and K, Q, gam get the cotangents of the scaled tiles and of the pairwise G, H.
-template <int D, int C> struct PhaseBwdLds {
-    float S0r[D][D + 1], S0i[D][D + 1];   // state entering the chunk
-    float S1r[D][D + 1], S1i[D][D + 1];   // cotangent of the state leaving it
-    float dO[C][D];
-    RowVecs<D, C> U, LB, X;               // U; Ub, then lambda over it; X
-    float Gbr[C][C + 1], Gbi[C][C + 1];   // cotangent of G (beta Ab)
-    float Hbr[C][C + 1], Hbi[C][C + 1];   // cotangent of H (Pb)
-    float dbA[C][C + 1];                  // Re(conj(Ab) G) per pair
-    float red[2 * (kPT / D)][D];          // per-channel partial sums over rows
-    float glr[D], gli[D];                 // cotangent of gam_L from the state's decay
-};
-
-template <typename TI, int GATE, int D, int C>
-__global__ __launch_bounds__(kPT) void phase_bwd_kernel(Params p, const float* states) {
-    constexpr int PG = kPT / D, NC = D / PG;
-    __shared__ PhaseTiles<D, C> s;
-    __shared__ PhaseBwdLds<D, C> b;
-    const int tid = threadIdx.x, v = tid / PG, c0 = (tid % PG) * NC;
-    const int bh = blockIdx.x;
-    float br[NC], bi[NC];   // dS[v][c0 .. c0 + NC), the running state cotangent
+// Out per chunk: lambda [BH][NT][2][D][C] (row v, then step) and dS1
+// [BH][NT][2][D][D], which the per-chunk backward reads.
+template <typename TI, int GATE, int D>
+__global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const float* __restrict__ mats,
+                                                              float* __restrict__ lam, float* __restrict__ dS1) {
+    constexpr int NB = D / kBV, NC = D / kC;
+    __shared__ __align__(16) SeqLds<D> s;
+    int bh, blk;
+    head_and_block(NB, p.BH, bh, blk);
+    const int tid = threadIdx.x, vl = tid / kC, j = tid % kC, c0 = j * NC, v = blk * kBV + vl;
+    float br[NC], bi[NC];   // dS[v][c0 .. c0 + NC)
     {
         const long o0 = ((long)bh * D + v) * D + c0;
 #pragma unroll
@@ -319,212 +432,72 @@ __global__ __launch_bounds__(kPT) void phase_bwd_kernel(Params p, const float* s
             bi[c] = p.dhT_im ? p.dhT_im[o0 + c] : 0.f;
         }
     }
-    const TI* __restrict__ dout = static_cast<const TI*>(p.dout);
-    TI* __restrict__ dq = static_cast<TI*>(p.dq);
-    TI* __restrict__ dk = static_cast<TI*>(p.dk);
-    TI* __restrict__ dvv = static_cast<TI*>(p.dv);
+    TI* __restrict__ dvp = static_cast<TI*>(p.dv);
+    SeqIn<TI, GATE, D> x;
+    x.load(p, p.dout, mats, bh, blk * kBV, p.NT - 1);
     for (int n = p.NT - 1; n >= 0; --n) {
-        const int t0 = n * C, valid = min(C, p.T - t0), L = valid - 1;
-        const long row0 = (long)bh * p.T + t0;
-        // (a) the chunk's state and the cotangent leaving it into LDS, dO rows
+        const int valid = min(kC, p.T - n * kC);
+        const long row0 = (long)bh * p.T + n * kC;
+        const long chunk = (long)bh * p.NT + n;
+        seq_commit(x, s);
+        __syncthreads();
+        seq_tiles(x, s);
+        x.load(p, p.dout, mats, bh, blk * kBV, n > 0 ? n - 1 : n);   // the previous chunk, during this one
+        __syncthreads();
         {
-            const float* st = states + ((long)bh * p.NT + n) * 2 * D * D;
-            for (int idx = tid; idx < D * D; idx += kPT) {
-                const int r = idx / D, c = idx % D;
-                b.S0r[r][c] = st[idx];
-                b.S0i[r][c] = st[(long)D * D + idx];
-            }
+            float* d1 = dS1 + (chunk * 2 * D + v) * D + c0;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                b.S1r[v][c0 + c] = br[c];
-                b.S1i[v][c0 + c] = bi[c];
-            }
-            for (int idx = tid; idx < C * D; idx += kPT) {
-                const int t = idx / D, c = idx % D;
-                b.dO[t][c] = t < valid ? to_f(dout[(row0 + t) * D + c]) : 0.f;
+                d1[c] = br[c];
+                d1[(long)D * D + c] = bi[c];
             }
         }
-        chunk_setup<TI, GATE, D, C>(p, s, row0, valid);   // (its barriers order the stores above)
-        // (b) the row's X, U, Ub, lambda; dv; the new state cotangent dS0 (the row's lanes
-        //     take every PG-th step of the triangular products)
+        // Ub_t = sum_c conj(Kd_tc) dS_vc (lane j keeps step j) + sum_{w >= j} conj(P_wj) dO_wv
+        cf ub = {0.f, 0.f};
+#pragma unroll 4
+        for (int t = 0; t < kC; ++t) {
+            cf a = {0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) a = cadd(a, cmulc({br[c], bi[c]}, {s.kdr[t][c0 + c], s.kdi[t][c0 + c]}));
+            a = {group_sum<kC>(a.r), group_sum<kC>(a.i)};
+            if (t == j) ub = a;
+        }
+        for (int w = j; w < kC; ++w) ub = cadd(ub, cscale({s.Pr[w][j], -s.Pi[w][j]}, s.B[w][vl]));
+        s.Ra.set(j, vl, ub);
+        // lambda_j = sum_{w >= j} conj(T_wj) Ub_w (the row's lanes: one wave, program order)
+        cf lm = {0.f, 0.f};
+        for (int w = j; w < kC; ++w) lm = cadd(lm, cmul({s.Tr[w][j], -s.Ti[w][j]}, s.Ra.get(w, vl)));
+        s.Rb.set(j, vl, lm);
         {
-            const int j = tid % PG;
-            float sr[NC], si[NC];
+            float* lp = lam + (chunk * 2 * D + v) * kC + j;
+            lp[0] = lm.r;
+            lp[(long)D * kC] = lm.i;
+        }
+        s.Os[j][vl] = s.beta[j] * lm.r;
+        // dS0, step by step over the lane's channels
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const cf y = cmulc({br[c], bi[c]}, {s.elr[c0 + c], s.eli[c0 + c]});
+            br[c] = y.r;
+            bi[c] = y.i;
+        }
+#pragma unroll 4
+        for (int t = 0; t < kC; ++t) {
+            const float o = s.B[t][vl];
+            const cf l = cscale(s.Rb.get(t, vl), s.beta[t]);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                sr[c] = b.S0r[v][c0 + c];
-                si[c] = b.S0i[v][c0 + c];
-            }
-            row_products<D, C, PG, NC>(s.kgr, s.kgi, sr, si, v, c0, false, b.X);   // X = (K E) S0^T
-            row_products<D, C, PG, NC>(s.kdr, s.kdi, br, bi, v, c0, true, b.LB);   // conj(Kd) dS1^T
-            for (int t = j; t < C; t += PG) {
-                cf u = {0.f, 0.f};
-                for (int w = 0; w <= t; ++w)
-                    u = cadd(u, cmul({s.Tr[t][w], s.Ti[t][w]}, cscale(csub({s.V[w][v], 0.f}, b.X.get(w, v)), s.beta[w])));
-                b.U.set(t, v, u);
-                // + P^H dO:  Ub_t += sum_{w >= t} conj(P_wt) dO_wv
-                cf acc = b.LB.get(t, v);
-                for (int w = t; w < C; ++w) acc = cadd(acc, cscale({s.Pr[w][t], -s.Pi[w][t]}, b.dO[w][v]));
-                b.LB.set(t, v, acc);
-            }
-            // lambda = T^H Ub, in place: lambda_t = sum_{w >= t} conj(T_wt) Ub_w.  Round r of the
-            // loop writes steps [r PG, (r + 1) PG) after all of its reads, and later rounds read
-            // only steps beyond those
-            for (int t = j; t < C; t += PG) {
-                cf acc = {0.f, 0.f};
-                for (int w = t; w < C; ++w) acc = cadd(acc, cmul({s.Tr[w][t], -s.Ti[w][t]}, b.LB.get(w, v)));
-                b.LB.set(t, v, acc);
-                if (t < valid) dvv[(row0 + t) * D + v] = from_f<TI>(s.beta[t] * acc.r);
-            }
-            // dS0 = dS1 diag(conj(E_L)) + dO^T conj(Q E) - (diag(beta) lambda)^T conj(K E), step by
-            // step over the lane's channels
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const cf x = cmulc({br[c], bi[c]}, cexp_(s.gr[L][c0 + c], s.gi[L][c0 + c]));
-                br[c] = x.r;
-                bi[c] = x.i;
-            }
-#pragma unroll 1
-            for (int t = 0; t < C; ++t) {
-                const float o = b.dO[t][v];
-                const cf l = cscale(b.LB.get(t, v), s.beta[t]);
-#pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const int cc = c0 + c;
-                    const cf x = csub(cscale({s.qgr[t][cc], -s.qgi[t][cc]}, o), cmulc(l, {s.kgr[t][cc], s.kgi[t][cc]}));
-                    br[c] += x.r;
-                    bi[c] += x.i;
-                }
+                const int cc = c0 + c;
+                const cf y = csub(cscale({s.qgr[t][cc], -s.qgi[t][cc]}, o), cmulc(l, {s.kgr[t][cc], s.kgi[t][cc]}));
+                br[c] += y.r;
+                bi[c] += y.i;
             }
         }
         __syncthreads();
-        // (c) pairs: Ab = -lambda U^H (strictly lower), Pb = dO U^H (lower); per channel the
-        //     cotangent of gam_L through the state's decay, sum_v dS1 conj(S0 E_L)
-        for (int pr = tid; pr < C * C; pr += kPT) {
-            const int t = pr / C, u = pr % C;
-            cf ab = {0.f, 0.f}, pb = {0.f, 0.f};
-            if (u <= t) {
-                #pragma unroll 4
-                for (int w = 0; w < D; ++w) {
-                    const cf Uc = b.U.get(u, w);
-                    ab = csub(ab, cmulc(b.LB.get(t, w), Uc));
-                    pb = cadd(pb, cmulc({b.dO[t][w], 0.f}, Uc));
-                }
-            }
-            if (u == t) ab = {0.f, 0.f};
-            b.Gbr[t][u] = s.beta[t] * ab.r;
-            b.Gbi[t][u] = s.beta[t] * ab.i;
-            b.Hbr[t][u] = pb.r;
-            b.Hbi[t][u] = pb.i;
-            b.dbA[t][u] = ab.r * s.Gr[t][u] + ab.i * s.Gi[t][u];   // Re(conj(Ab) G)
-        }
-        if (tid < D) {
-            const int c = tid;
-            cf acc = {0.f, 0.f};
-            #pragma unroll 4
-            for (int w = 0; w < D; ++w) acc = cadd(acc, cmulc({b.S1r[w][c], b.S1i[w][c]}, {b.S0r[w][c], b.S0i[w][c]}));
-            const cf EL = cexp_(s.gr[L][c], s.gi[L][c]);
-            const cf gl = cmulc(acc, EL);
-            b.glr[c] = gl.r;
-            b.gli[c] = gl.i;
-        }
-        __syncthreads();
-        // (d) elements (t, c): the scaled tiles' cotangents from sums over the rows v, the
-        //     pairwise G / H terms; dq, dk; gam's cotangent, stored over (K E) at the same
-        //     element (each element of K E is read only by the thread that replaces it)
-        constexpr int TS = kPT / D;   // threads sharing a channel (rows t = tid / D + TS j)
         {
-            const int c = tid % D, tg = tid / D;
-            cf kdsum = {0.f, 0.f};
-            for (int t = tg; t < C; t += TS) {
-                cf Kgb = {0.f, 0.f}, Qgb = {0.f, 0.f}, Kdb = {0.f, 0.f};
-                #pragma unroll 4
-                for (int w = 0; w < D; ++w) {
-                    const cf S = {b.S0r[w][c], b.S0i[w][c]};
-                    Kgb = csub(Kgb, cmulc(b.LB.get(t, w), S));
-                    Qgb = cadd(Qgb, cmulc({b.dO[t][w], 0.f}, S));
-                    Kdb = cadd(Kdb, cmulc({b.S1r[w][c], b.S1i[w][c]}, b.U.get(t, w)));
-                }
-                Kgb = cscale(Kgb, s.beta[t]);
-                const cf E = cexp_(s.gr[t][c], s.gi[t][c]);
-                const cf Ed = cexp_(s.gr[L][c] - s.gr[t][c], s.gi[L][c] - s.gi[t][c]);
-                const float kt = s.K[t][c], qt = s.Q[t][c];
-                // Re(conj(w) Zb) for the real inputs, Zb conj(Z) for gam
-                float dkv = Kgb.r * E.r + Kgb.i * E.i + Kdb.r * Ed.r + Kdb.i * Ed.i;
-                float dqv = Qgb.r * E.r + Qgb.i * E.i;
-                cf gb = cadd(cmulc(Kgb, {s.kgr[t][c], s.kgi[t][c]}), cmulc(Qgb, {s.qgr[t][c], s.qgi[t][c]}));
-                const cf kdc = cmulc(Kdb, {s.kdr[t][c], s.kdi[t][c]});
-                gb = csub(gb, kdc);
-                kdsum = cadd(kdsum, kdc);
-                // pairs with t as the row (u <= t) and as the column (w >= t)
-                #pragma unroll 4
-                for (int u = 0; u < C; ++u) {
-                    const int r = u <= t ? t : u, cl = u <= t ? u : t;   // the pair (row, column)
-                    const cf f = cexp_(s.gr[r][c] - s.gr[cl][c], s.gi[r][c] - s.gi[cl][c]);
-                    const cf Gb = {b.Gbr[r][cl], b.Gbi[r][cl]}, Hb = {b.Hbr[r][cl], b.Hbi[r][cl]};
-                    if (u <= t) {   // t is the row: G_tu, H_tu
-                        const float ku = s.K[u][c];
-                        const cf wg = cscale(f, ku);       // dG_tu / dk_tc
-                        dkv += Gb.r * wg.r + Gb.i * wg.i;
-                        dqv += Hb.r * wg.r + Hb.i * wg.i;
-                        gb = cadd(gb, cadd(cmulc(Gb, cscale(f, kt * ku)), cmulc(Hb, cscale(f, qt * ku))));
-                    }
-                    if (u >= t) {   // t is the column: G_ut, H_ut
-                        const cf wg = cscale(f, s.K[u][c]), wh = cscale(f, s.Q[u][c]);
-                        dkv += Gb.r * wg.r + Gb.i * wg.i + Hb.r * wh.r + Hb.i * wh.i;
-                        gb = csub(gb, cadd(cmulc(Gb, cscale(f, s.K[u][c] * kt)), cmulc(Hb, cscale(f, s.Q[u][c] * kt))));
-                    }
-                }
-                if (t < valid) {
-                    dq[(row0 + t) * D + c] = from_f<TI>(dqv);
-                    dk[(row0 + t) * D + c] = from_f<TI>(dkv);
-                }
-                s.kgr[t][c] = gb.r;
-                s.kgi[t][c] = gb.i;
-            }
-            b.red[2 * tg][c] = kdsum.r;
-            b.red[2 * tg + 1][c] = kdsum.i;
+            const int t = tid / kBV, vv = tid % kBV;
+            if (t < valid) dvp[(row0 + t) * D + blk * kBV + vv] = from_f<TI>(s.Os[t][vv]);
         }
-        __syncthreads();
-        // (e) per channel: gam_L's cotangent (the state's decay and the Kd terms), then the
-        //     reverse cumulative sum; dtheta, dg (the scalar gate sums its channels per row,
-        //     from the real parts kept over U, which nothing reads any more)
-        float (*dgs)[D + 1] = b.U.r;
-        if (tid < D) {
-            const int c = tid;
-            float lr = b.glr[c], li = b.gli[c];
-            for (int g2 = 0; g2 < TS; ++g2) {
-                lr += b.red[2 * g2][c];
-                li += b.red[2 * g2 + 1][c];
-            }
-            float ar = 0.f, ai = 0.f;
-            for (int t = L; t >= 0; --t) {
-                ar += s.kgr[t][c] + (t == L ? lr : 0.f);
-                ai += s.kgi[t][c] + (t == L ? li : 0.f);
-                p.dtheta[(row0 + t) * D + c] = ai;
-                if (GATE == kGateVector) p.dg[(row0 + t) * D + c] = ar;
-                dgs[t][c] = ar;
-            }
-        }
-        // dbeta_t = Re sum_v conj(lambda_tv) (V - X)_tv + sum_u Re(conj(Ab_tu) G_tu)
-        if (tid >= kPT - C) {
-            const int t = tid - (kPT - C);
-            if (t < valid) {
-                float acc = 0.f;
-                #pragma unroll 4
-                for (int w = 0; w < D; ++w)
-                    acc += b.LB.r[t][w] * (s.V[t][w] - b.X.r[t][w]) - b.LB.i[t][w] * b.X.i[t][w];
-                for (int u = 0; u < t; ++u) acc += b.dbA[t][u];
-                p.dbeta[row0 + t] = acc;
-            }
-        }
-        __syncthreads();
-        if (GATE == kGateScalar && tid < valid) {
-            float acc = 0.f;
-            for (int c = 0; c < D; ++c) acc += dgs[tid][c];
-            p.dg[row0 + tid] = acc;
-        }
-        __syncthreads();
     }
     const long o0 = ((long)bh * D + v) * D + c0;
 #pragma unroll
@@ -534,44 +507,303 @@ __global__ __launch_bounds__(kPT) void phase_bwd_kernel(Params p, const float* s
     }
 }
 
+// ---------------------------------------------------------------------------
+// phase_bwd_chunk: one workgroup per (chunk, head), from the chunk's entry state
+// S0, the cotangent dS1 leaving it, lambda and the forward's T, P, G:
+//     X = (K E) S0^T,  U = T diag(beta) (V - X)
+//     Ab = -strictly-lower(lambda U^H)      Pb = lower(dO U^H)
+//     dbeta = Re rowsum(conj(lambda) (V - X)) + Re rowsum(conj(Ab) G)
+// and K, Q, gam get the cotangents of the scaled tiles and of the pairwise G, H.
+template <int D> struct ChunkBwdLds {
+    float K[kC][D + 1], Q[kC][D + 1], V[kC][D + 1];
+    float gr[kC][D + 1], gi[kC][D + 1];     // gam
+    float kgr[kC][D + 1], kgi[kC][D + 1];   // K E, then the cotangent of gam
+    float Gr[kC][kC + 1], Gi[kC][kC + 1], Tr[kC][kC + 1], Ti[kC][kC + 1], Pr[kC][kC + 1], Pi[kC][kC + 1];
+    float beta[kC];
+    float tr[kPT / D][D], ti[kPT / D][D];
+    float S0r[D][D + 1], S0i[D][D + 1];   // state entering the chunk
+    float S1r[D][D + 1], S1i[D][D + 1];   // cotangent of the state leaving it
+    float dO[kC][D + 1];
+    Rows<D> U, LB, X;                     // U; lambda; X
+    float Gbr[kC][kC + 1], Gbi[kC][kC + 1];   // cotangent of G (beta Ab)
+    float Hbr[kC][kC + 1], Hbi[kC][kC + 1];   // cotangent of H (Pb)
+    float dbA[kC][kC + 1];                    // Re(conj(Ab) G) per pair
+    float red[2 * (kPT / D)][D];              // per-channel partial sums over rows
+    float glr[D], gli[D];                     // cotangent of gam_L from the state's decay
+};
+
 template <typename TI, int GATE, int D>
-hipError_t phase_launch_d(const Params& p, float* states, bool backward, hipStream_t stream) {
-    constexpr int C = 16;
-    const dim3 grid(p.BH), block(kPT);
-    if (backward) {
-        prof_begin(stream, "phase_bwd");
-        hipLaunchKernelGGL((phase_bwd_kernel<TI, GATE, D, C>), grid, block, 0, stream, p, states);
-    } else {
-        prof_begin(stream, "phase_fwd");
-        hipLaunchKernelGGL((phase_fwd_kernel<TI, GATE, D, C>), grid, block, 0, stream, p, states);
+__global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const float* __restrict__ states,
+                                                              const float* __restrict__ mats,
+                                                              const float* __restrict__ lam,
+                                                              const float* __restrict__ dS1) {
+    using CI = ChunkIn<TI, GATE, D>;
+    constexpr int PG = kPT / D, NC = D / PG;
+    __shared__ ChunkBwdLds<D> b;
+    const int tid = threadIdx.x, n = blockIdx.x, bh = blockIdx.y;
+    const int t0 = n * kC, valid = min(kC, p.T - t0), L = valid - 1;
+    const long row0 = (long)bh * p.T + t0, chunk = (long)bh * p.NT + n;
+    const TI* __restrict__ dout = static_cast<const TI*>(p.dout);
+    const TI* __restrict__ vin = static_cast<const TI*>(p.v);
+    TI* __restrict__ dq = static_cast<TI*>(p.dq);
+    TI* __restrict__ dk = static_cast<TI*>(p.dk);
+    // (a) the chunk's data into LDS
+    CI in;
+    in.load(p, row0, valid);
+    {
+        const float* st = states + chunk * 2 * D * D;
+        const float* d1 = dS1 + chunk * 2 * D * D;
+        for (int idx = tid; idx < D * D; idx += kPT) {
+            const int r = idx / D, c = idx % D;
+            b.S0r[r][c] = st[idx];
+            b.S0i[r][c] = st[(long)D * D + idx];
+            b.S1r[r][c] = d1[idx];
+            b.S1i[r][c] = d1[(long)D * D + idx];
+        }
+        const float* lm = lam + chunk * 2 * D * kC;
+        for (int idx = tid; idx < D * kC; idx += kPT) {
+            const int vv = idx / kC, t = idx % kC;
+            b.LB.r[t][vv] = lm[idx];
+            b.LB.i[t][vv] = lm[(long)D * kC + idx];
+        }
+        for (int idx = tid; idx < kC * D; idx += kPT) {
+            const int t = idx / D, c = idx % D;
+            const bool ok = t < valid;
+            const long e = (row0 + (ok ? t : 0)) * D + c;
+            const float o = to_f(dout[e]), vv = to_f(vin[e]);
+            b.dO[t][c] = ok ? o : 0.f;
+            b.V[t][c] = ok ? vv : 0.f;
+        }
+        const float* mc = mats + chunk * kMats;
+        {
+            const int t = tid / kC, u = tid % kC;
+            b.Tr[t][u] = mc[tid];
+            b.Ti[t][u] = mc[kCC + tid];
+            b.Pr[t][u] = mc[2 * kCC + tid];
+            b.Pi[t][u] = mc[3 * kCC + tid];
+            b.Gr[t][u] = mc[4 * kCC + tid];
+            b.Gi[t][u] = mc[5 * kCC + tid];
+        }
+        const float bt = p.beta[row0 + min(tid % kC, valid - 1)];
+        if (tid < kC) b.beta[tid] = tid < valid ? bt : 0.f;
     }
-    prof_end(stream);
+    in.prefix(b.tr, b.ti);
+    __syncthreads();
+    in.finish(b.tr, b.ti);
+    {
+        const int c = CI::chan();
+#pragma unroll
+        for (int r = 0; r < CI::NR; ++r) {
+            const int t = CI::row(r);
+            b.K[t][c] = in.k[r];
+            b.Q[t][c] = in.q[r];
+            b.gr[t][c] = in.lr[r];
+            b.gi[t][c] = in.li[r];
+            const cf E = cexp_(in.lr[r], in.li[r]);
+            b.kgr[t][c] = in.k[r] * E.r;
+            b.kgi[t][c] = in.k[r] * E.i;
+        }
+    }
+    __syncthreads();
+    // (b) X = (K E) S0^T and U = T beta (V - X): rows v of the state by groups of PG
+    //     lanes, NC channels each; the row's lanes take every PG-th step of U
+    {
+        const int v = tid / PG, j = tid % PG, c0 = j * NC;
+        float sr[NC], si[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            sr[c] = b.S0r[v][c0 + c];
+            si[c] = b.S0i[v][c0 + c];
+        }
+#pragma unroll 1
+        for (int t = 0; t < kC; ++t) {
+            cf x = {0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) x = cadd(x, cmul({b.kgr[t][c0 + c], b.kgi[t][c0 + c]}, {sr[c], si[c]}));
+            x = {group_sum<PG>(x.r), group_sum<PG>(x.i)};
+            if (j == 0) b.X.set(t, v, x);
+        }
+        for (int t = j; t < kC; t += PG) {
+            cf u = {0.f, 0.f};
+            for (int w = 0; w <= t; ++w)
+                u = cadd(u, cmul({b.Tr[t][w], b.Ti[t][w]}, cscale(csub({b.V[w][v], 0.f}, b.X.get(w, v)), b.beta[w])));
+            b.U.set(t, v, u);
+        }
+    }
+    __syncthreads();
+    // (c) pairs: Ab = -lambda U^H (strictly lower), Pb = dO U^H (lower); per channel the
+    //     cotangent of gam_L through the state's decay, sum_v dS1 conj(S0 E_L)
+    {
+        const int t = tid / kC, u = tid % kC;
+        cf ab = {0.f, 0.f}, pb = {0.f, 0.f};
+        if (u <= t) {
+#pragma unroll 4
+            for (int w = 0; w < D; ++w) {
+                const cf Uc = b.U.get(u, w);
+                ab = csub(ab, cmulc(b.LB.get(t, w), Uc));
+                pb = cadd(pb, cmulc({b.dO[t][w], 0.f}, Uc));
+            }
+        }
+        if (u == t) ab = {0.f, 0.f};
+        b.Gbr[t][u] = b.beta[t] * ab.r;
+        b.Gbi[t][u] = b.beta[t] * ab.i;
+        b.Hbr[t][u] = pb.r;
+        b.Hbi[t][u] = pb.i;
+        b.dbA[t][u] = ab.r * b.Gr[t][u] + ab.i * b.Gi[t][u];   // Re(conj(Ab) G)
+    }
+    if (tid < D) {
+        const int c = tid;
+        cf acc = {0.f, 0.f};
+#pragma unroll 4
+        for (int w = 0; w < D; ++w) acc = cadd(acc, cmulc({b.S1r[w][c], b.S1i[w][c]}, {b.S0r[w][c], b.S0i[w][c]}));
+        const cf EL = cexp_(b.gr[L][c], b.gi[L][c]);
+        const cf gl = cmulc(acc, EL);
+        b.glr[c] = gl.r;
+        b.gli[c] = gl.i;
+    }
+    __syncthreads();
+    // (d) elements (t, c): the scaled tiles' cotangents from sums over the rows v, the
+    //     pairwise G / H terms; dq, dk; gam's cotangent, stored over (K E) at the same
+    //     element (each element of K E is read here only by the thread that replaces it)
+    constexpr int TS = kPT / D;   // threads sharing a channel (rows t = tid / D + TS j)
+    {
+        const int c = tid % D, tg = tid / D;
+        cf kdsum = {0.f, 0.f};
+        for (int t = tg; t < kC; t += TS) {
+            cf Kgb = {0.f, 0.f}, Qgb = {0.f, 0.f}, Kdb = {0.f, 0.f};
+#pragma unroll 4
+            for (int w = 0; w < D; ++w) {
+                const cf S = {b.S0r[w][c], b.S0i[w][c]};
+                Kgb = csub(Kgb, cmulc(b.LB.get(t, w), S));
+                Qgb = cadd(Qgb, cmulc({b.dO[t][w], 0.f}, S));
+                Kdb = cadd(Kdb, cmulc({b.S1r[w][c], b.S1i[w][c]}, b.U.get(t, w)));
+            }
+            Kgb = cscale(Kgb, b.beta[t]);
+            const cf E = cexp_(b.gr[t][c], b.gi[t][c]);
+            const cf Ed = cexp_(b.gr[L][c] - b.gr[t][c], b.gi[L][c] - b.gi[t][c]);
+            const float kt = b.K[t][c], qt = b.Q[t][c];
+            // Re(conj(w) Zb) for the real inputs, Zb conj(Z) for gam
+            float dkv = Kgb.r * E.r + Kgb.i * E.i + Kdb.r * Ed.r + Kdb.i * Ed.i;
+            float dqv = Qgb.r * E.r + Qgb.i * E.i;
+            cf gb = cadd(cmulc(Kgb, cscale(E, kt)), cmulc(Qgb, cscale(E, qt)));
+            const cf kdc = cmulc(Kdb, cscale(Ed, kt));
+            gb = csub(gb, kdc);
+            kdsum = cadd(kdsum, kdc);
+            // pairs with t as the row (u <= t) and as the column (u >= t)
+#pragma unroll 4
+            for (int u = 0; u < kC; ++u) {
+                const int r = u <= t ? t : u, cl = u <= t ? u : t;   // the pair (row, column)
+                const cf f = cexp_(b.gr[r][c] - b.gr[cl][c], b.gi[r][c] - b.gi[cl][c]);
+                const cf Gb = {b.Gbr[r][cl], b.Gbi[r][cl]}, Hb = {b.Hbr[r][cl], b.Hbi[r][cl]};
+                if (u <= t) {   // t is the row: G_tu, H_tu
+                    const float ku = b.K[u][c];
+                    const cf wg = cscale(f, ku);   // dG_tu / dk_tc
+                    dkv += Gb.r * wg.r + Gb.i * wg.i;
+                    dqv += Hb.r * wg.r + Hb.i * wg.i;
+                    gb = cadd(gb, cadd(cmulc(Gb, cscale(f, kt * ku)), cmulc(Hb, cscale(f, qt * ku))));
+                }
+                if (u >= t) {   // t is the column: G_ut, H_ut
+                    const cf wg = cscale(f, b.K[u][c]), wh = cscale(f, b.Q[u][c]);
+                    dkv += Gb.r * wg.r + Gb.i * wg.i + Hb.r * wh.r + Hb.i * wh.i;
+                    gb = csub(gb, cadd(cmulc(Gb, cscale(f, b.K[u][c] * kt)), cmulc(Hb, cscale(f, b.Q[u][c] * kt))));
+                }
+            }
+            if (t < valid) {
+                dq[(row0 + t) * D + c] = from_f<TI>(dqv);
+                dk[(row0 + t) * D + c] = from_f<TI>(dkv);
+            }
+            b.kgr[t][c] = gb.r;
+            b.kgi[t][c] = gb.i;
+        }
+        b.red[2 * tg][c] = kdsum.r;
+        b.red[2 * tg + 1][c] = kdsum.i;
+    }
+    __syncthreads();
+    // (e) per channel: gam_L's cotangent (the state's decay and the Kd terms), then the
+    //     reverse cumulative sum; dtheta, dg (the scalar gate sums its channels per row,
+    //     from the real parts kept over U, which nothing reads any more)
+    float (*dgs)[D + 1] = b.U.r;
+    if (tid < D) {
+        const int c = tid;
+        float lr = b.glr[c], li = b.gli[c];
+        for (int g2 = 0; g2 < TS; ++g2) {
+            lr += b.red[2 * g2][c];
+            li += b.red[2 * g2 + 1][c];
+        }
+        float ar = 0.f, ai = 0.f;
+        for (int t = L; t >= 0; --t) {
+            ar += b.kgr[t][c] + (t == L ? lr : 0.f);
+            ai += b.kgi[t][c] + (t == L ? li : 0.f);
+            p.dtheta[(row0 + t) * D + c] = ai;
+            if (GATE == kGateVector) p.dg[(row0 + t) * D + c] = ar;
+            dgs[t][c] = ar;
+        }
+    }
+    // dbeta_t = Re sum_v conj(lambda_tv) (V - X)_tv + sum_u Re(conj(Ab_tu) G_tu)
+    if (tid >= kPT - kC) {
+        const int t = tid - (kPT - kC);
+        if (t < valid) {
+            float acc = 0.f;
+#pragma unroll 4
+            for (int w = 0; w < D; ++w)
+                acc += b.LB.r[t][w] * (b.V[t][w] - b.X.r[t][w]) - b.LB.i[t][w] * b.X.i[t][w];
+            for (int u = 0; u < t; ++u) acc += b.dbA[t][u];
+            p.dbeta[row0 + t] = acc;
+        }
+    }
+    if (GATE == kGateScalar) {
+        __syncthreads();
+        if (tid < valid) {
+            float acc = 0.f;
+            for (int c = 0; c < D; ++c) acc += dgs[tid][c];
+            p.dg[row0 + tid] = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <typename TI, int GATE, int D>
+hipError_t phase_launch_d(const Params& p, const PhaseBufs& f, bool backward, hipStream_t stream) {
+    const dim3 chunks(p.NT, p.BH), seq(p.BH * (D / kBV)), block(kPT);
+    if (!backward) {
+        prof_begin(stream, "phase_prep");
+        hipLaunchKernelGGL((phase_prep_kernel<TI, GATE, D>), chunks, block, 0, stream, p, f.mats);
+        prof_end(stream);
+        prof_begin(stream, "phase_fwd_state");
+        hipLaunchKernelGGL((phase_fwd_state_kernel<TI, GATE, D>), seq, block, 0, stream, p, f.mats, f.states);
+        prof_end(stream);
+    } else {
+        prof_begin(stream, "phase_bwd_state");
+        hipLaunchKernelGGL((phase_bwd_state_kernel<TI, GATE, D>), seq, block, 0, stream, p, f.mats, f.lam, f.dS1);
+        prof_end(stream);
+        prof_begin(stream, "phase_bwd_chunk");
+        hipLaunchKernelGGL((phase_bwd_chunk_kernel<TI, GATE, D>), chunks, block, 0, stream, p, f.states, f.mats,
+                           f.lam, f.dS1);
+        prof_end(stream);
+    }
     return hipGetLastError();
 }
 
 template <typename TI, int GATE>
-hipError_t phase_launch_g(const Params& p, float* states, bool backward, hipStream_t stream) {
+hipError_t phase_launch_g(const Params& p, const PhaseBufs& f, bool backward, hipStream_t stream) {
     switch (p.DKr) {
-        case 16: return phase_launch_d<TI, GATE, 16>(p, states, backward, stream);
-        case 32: return phase_launch_d<TI, GATE, 32>(p, states, backward, stream);
-        case 64: return phase_launch_d<TI, GATE, 64>(p, states, backward, stream);
+        case 16: return phase_launch_d<TI, GATE, 16>(p, f, backward, stream);
+        case 32: return phase_launch_d<TI, GATE, 32>(p, f, backward, stream);
+        case 64: return phase_launch_d<TI, GATE, 64>(p, f, backward, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename TI>
-hipError_t phase_launch_t(const Problem& pr, const Params& p, float* states, bool backward, hipStream_t stream) {
+hipError_t phase_launch_t(const Problem& pr, const Params& p, const PhaseBufs& f, bool backward, hipStream_t stream) {
     switch (pr.gate) {
-        case kGateNone: return phase_launch_g<TI, kGateNone>(p, states, backward, stream);
-        case kGateScalar: return phase_launch_g<TI, kGateScalar>(p, states, backward, stream);
-        case kGateVector: return phase_launch_g<TI, kGateVector>(p, states, backward, stream);
+        case kGateNone: return phase_launch_g<TI, kGateNone>(p, f, backward, stream);
+        case kGateScalar: return phase_launch_g<TI, kGateScalar>(p, f, backward, stream);
+        case kGateVector: return phase_launch_g<TI, kGateVector>(p, f, backward, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-}  // namespace
-
-namespace {
 __global__ void phase_copy_kernel(const float* __restrict__ src, float* __restrict__ dst, long n) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) dst[i] = src ? src[i] : 0.f;
@@ -581,9 +813,10 @@ hipError_t phase_copy(const float* src, float* dst, long n, hipStream_t stream) 
     hipLaunchKernelGGL(phase_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, src, dst, n);
     return hipGetLastError();
 }
+
 }  // namespace
 
-hipError_t launch_phase(const Problem& pr, const Params& p, float* states, bool backward, hipStream_t stream) {
+hipError_t launch_phase(const Problem& pr, const Params& p, const PhaseBufs& f, bool backward, hipStream_t stream) {
     if (pr.B * pr.H == 0) return hipSuccess;
     if (pr.T == 0) {   // no steps: the state (or its cotangent) passes through
         const long n = (long)pr.B * pr.H * pr.dv * pr.dk;
@@ -591,8 +824,8 @@ hipError_t launch_phase(const Problem& pr, const Params& p, float* states, bool 
         if (e != hipSuccess) return e;
         return backward ? phase_copy(p.dhT_im, p.dh0_im, n, stream) : phase_copy(p.h0_im, p.hT_im, n, stream);
     }
-    return pr.bf16 ? phase_launch_t<bf16>(pr, p, states, backward, stream)
-                   : phase_launch_t<float>(pr, p, states, backward, stream);
+    return pr.bf16 ? phase_launch_t<bf16>(pr, p, f, backward, stream)
+                   : phase_launch_t<float>(pr, p, f, backward, stream);
 }
 
 }  // namespace dn

@@ -266,30 +266,39 @@ dn_status dn_recurrent_phase_fwd(const dn_shape* shape, const void* q, const voi
  * complex decays in the C x C products, so any g <= 0 is safe), the exact
  * chunk transfer of the state and the intra-chunk output; the backward takes
  * the chunks back in reverse with one transposed (conjugated) triangular solve
- * per chunk.  One workgroup per (batch, head); fp32 arithmetic throughout.
+ * per chunk.  The per-chunk products run for all chunks at once, the state
+ * recurrences over (head, block of 16 state rows); fp32 arithmetic throughout.
  *   shape  : dk == dv in {16, 32, 64}; C == 16; dtype fp32 or bf16 (q, k, v, o,
  *            dout, dq, dk, dv); gate as for dn_chunk_fwd; DN_FLAG_KACZMARZ is not
  *            supported here (DN_ERR_UNSUPPORTED); DN_FLAG_NO_SCAN is ignored
  *   inputs : q, k, v, beta, g as for dn_chunk_fwd; theta fp32 [B][H][T][dk]
  *            (radians); h0_re, h0_im fp32 [B][H][dv][dk] (NULL = zero)
- *   outputs: o; hT_re, hT_im (NULL = not wanted); states: the complex state
- *            entering each chunk, fp32 [B][H][NT][2][dv][dk] (real part, then
- *            imaginary; NT = ceil(T / 16); dn_phase_states_bytes bytes), written
- *            by the forward when not NULL and required by the backward
+ *   outputs: o; hT_re, hT_im (NULL = not wanted); states (dn_phase_states_bytes
+ *            bytes, fp32; NULL = not saved): the complex state entering each
+ *            chunk [B][H][NT][2][dv][dk] (real part, then imaginary; NT =
+ *            ceil(T / 16)), then, from the next 256-byte boundary, per chunk
+ *            [B][H][NT][6][16][16] the matrices (I + A)^{-1}, P and G (real,
+ *            imaginary, each); written by the forward, required by the backward
  *   backward: the vector-Jacobian products of
  *            L = <o, dout> + <hT_re, dhT_re> + <hT_im, dhT_im>  (dhT_* NULL = zero):
  *            dq, dk, dv (io), dbeta, dg (NULL iff no gate; layout of g), dtheta
  *            (like theta) fp32; dh0_re, dh0_im (NULL = not wanted)
- * Validation and errors as for dn_chunk_fwd; no workspace.
+ *   ws     : device scratch of ws_bytes >= dn_phase_workspace_bytes(shape, pass):
+ *            the forward needs it only when states is NULL (DN_PASS_FWD: the
+ *            per-chunk matrices), the backward always (DN_PASS_BWD: lambda and
+ *            the state cotangent of each chunk)
+ * Validation and errors as for dn_chunk_fwd.
  */
 size_t dn_phase_states_bytes(const dn_shape* shape);
+size_t dn_phase_workspace_bytes(const dn_shape* shape, int pass);
 dn_status dn_chunk_phase_fwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
                              const float* g, const float* theta, const float* h0_re, const float* h0_im, void* o,
-                             float* hT_re, float* hT_im, float* states, void* stream);
+                             float* hT_re, float* hT_im, float* states, void* ws, size_t ws_bytes, void* stream);
 dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
                              const float* g, const float* theta, const void* dout, const float* dhT_re,
                              const float* dhT_im, const float* states, void* dq, void* dk, void* dv, float* dbeta,
-                             float* dg, float* dtheta, float* dh0_re, float* dh0_im, void* stream);
+                             float* dg, float* dtheta, float* dh0_re, float* dh0_im, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* Static description of a status code. */
 const char* dn_status_string(dn_status status);

@@ -254,22 +254,29 @@ def test_validation_errors_chunk_phase():
 
     def fwd(s, **over):
         a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, theta=FAKE * 6, h0_re=None, h0_im=None,
-                 o=FAKE * 7, hT_re=None, hT_im=None, states=None)
+                 o=FAKE * 7, hT_re=None, hT_im=None, states=None, ws=FAKE * 16, ws_bytes=1 << 30)
         a.update(over)
         return B.dn_chunk_phase_fwd(s, a["q"], a["k"], a["v"], a["beta"], a["g"], a["theta"], a["h0_re"],
-                                    a["h0_im"], a["o"], a["hT_re"], a["hT_im"], a["states"], 0)
+                                    a["h0_im"], a["o"], a["hT_re"], a["hT_im"], a["states"], a["ws"], a["ws_bytes"], 0)
 
     def bwd(s, **over):
         a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, theta=FAKE * 6, dout=FAKE * 8,
                  dhT_re=None, dhT_im=None, states=FAKE * 9, dq=FAKE * 10, dk=FAKE * 11, dv=FAKE * 12,
-                 dbeta=FAKE * 13, dg=FAKE * 14, dtheta=FAKE * 15, dh0_re=None, dh0_im=None)
+                 dbeta=FAKE * 13, dg=FAKE * 14, dtheta=FAKE * 15, dh0_re=None, dh0_im=None, ws=FAKE * 16,
+                 ws_bytes=1 << 30)
         a.update(over)
         return B.dn_chunk_phase_bwd(s, *(a[n] for n in ("q", "k", "v", "beta", "g", "theta", "dout", "dhT_re",
                                                         "dhT_im", "states", "dq", "dk", "dv", "dbeta", "dg",
-                                                        "dtheta", "dh0_re", "dh0_im")), 0)
+                                                        "dtheta", "dh0_re", "dh0_im", "ws", "ws_bytes")), 0)
 
-    assert B.dn_phase_states_bytes(sh()) == 1 * 2 * 3 * 2 * 32 * 32 * 4   # NT = ceil(40 / 16) = 3
+    al = lambda x: (x + 255) // 256 * 256
+    # NT = ceil(40 / 16) = 3: chunk states, then T, P, G per chunk (complex, 16 x 16)
+    assert B.dn_phase_states_bytes(sh()) == al(1 * 2 * 3 * 2 * 32 * 32 * 4) + al(1 * 2 * 3 * 6 * 16 * 16 * 4)
+    assert B.dn_phase_workspace_bytes(sh(), B.DN_PASS_FWD) == al(1 * 2 * 3 * 6 * 16 * 16 * 4)
+    assert B.dn_phase_workspace_bytes(sh(), B.DN_PASS_BWD) == al(2 * 3 * 2 * 32 * 16 * 4) + al(2 * 3 * 2 * 32 * 32 * 4)
+    assert B.dn_phase_workspace_bytes(sh(), B.DN_PASS_BWD_RECOMPUTE) == 0
     assert B.dn_phase_states_bytes(sh(C=64)) == 0
+    assert B.dn_phase_workspace_bytes(sh(C=64), B.DN_PASS_BWD) == 0
     assert fwd(sh(C=64)) == B.DN_ERR_UNSUPPORTED
     assert fwd(sh(dk=128, dv=128)) == B.DN_ERR_UNSUPPORTED
     assert fwd(sh(dk=32, dv=16)) == B.DN_ERR_UNSUPPORTED
@@ -279,6 +286,11 @@ def test_validation_errors_chunk_phase():
     assert fwd(sh(), o=FAKE * 3) == B.DN_ERR_INVALID                    # output aliases v
     assert fwd(sh(), hT_re=FAKE * 20, hT_im=FAKE * 20) == B.DN_ERR_INVALID
     assert bwd(sh(), states=None) == B.DN_ERR_INVALID
+    assert fwd(sh(), ws=None) == B.DN_ERR_INVALID                       # no states: the matrices need a workspace
+    assert fwd(sh(), ws_bytes=100) == B.DN_ERR_WORKSPACE
+    assert fwd(sh(), o=FAKE * 16) == B.DN_ERR_INVALID                   # output aliases the workspace
+    assert bwd(sh(), ws=None) == B.DN_ERR_INVALID
+    assert bwd(sh(), ws_bytes=100) == B.DN_ERR_WORKSPACE
     assert bwd(sh(), dtheta=None) == B.DN_ERR_INVALID
     assert bwd(sh(), dg=None) == B.DN_ERR_INVALID
     assert bwd(sh(), dq=FAKE * 11) == B.DN_ERR_INVALID                  # dq aliases dk

@@ -124,3 +124,17 @@ def test_zero_steps_pass_the_state_through():
     assert np.array_equal(gpu["hT_im"], inp["h0_im"].double().numpy())
     assert np.array_equal(gpu["dh0_re"], inp["dhT"].double().numpy())
     assert np.array_equal(gpu["dh0_im"], inp["dhT_im"].double().numpy())
+
+
+def test_forward_without_states_matches():
+    """Without a saved buffer the per-chunk matrices go to the workspace: o and the
+    final state are bitwise those of the saving forward."""
+    w, inp = _case("vector", "bf16", 2, 2, 16 * 4 + 3, 64, seed=79)
+    d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
+    a = B.chunk_phase_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["theta"], d["h0"], d["h0_im"])
+    b = B.chunk_phase_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["theta"], d["h0"], d["h0_im"],
+                          save_states=False)
+    torch.cuda.synchronize()
+    assert b[3] is None
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
