@@ -78,9 +78,9 @@ __device__ __forceinline__ cf cexp_(float re, float im) {
 // c = tid % D, row group tid / D) holds NR consecutive rows, so the in-chunk
 // cumulative sum is a prefix over its own rows plus the totals of the earlier
 // row groups.  Rows at or past `valid` read row 0 (branch-free loads) and count
-// as zero, gate included: they leave the state unchanged.
-template <typename TI, int GATE, int D> struct ChunkIn {
-    static constexpr int RG = kPT / D, NR = kC / RG;
+// as zero, gate included: they leave the state unchanged.  NTH threads.
+template <typename TI, int GATE, int D, int NTH = kPT> struct ChunkIn {
+    static constexpr int RG = NTH / D, NR = kC / RG;
     static_assert(RG * NR == kC, "rows");
     float k[NR], q[NR], lr[NR], li[NR];
     static __device__ __forceinline__ int chan() { return threadIdx.x % D; }
@@ -367,15 +367,19 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
                 yj = b;
             }
         }
-        // R_j = beta_j (V_j - X_j); U_j = sum_{w <= j} T_jw R_w; O_j = Re(Y_j + sum_{w <= j} P_jw U_w).
-        // A row's lanes are 16 lanes of one wave: what one stores, the others read back in
-        // program order with no barrier.
+        // R_j = beta_j (V_j - X_j); U_j = sum_w T_jw R_w; O_j = Re(Y_j + sum_w P_jw U_w).  T and
+        // P are stored with zeros above the diagonal, so every lane runs all 16 steps (no
+        // divergent loop: the reads of a row are issued together).  A row's lanes are 16
+        // lanes of one wave: what one stores, the others read back in program order with
+        // no barrier.
         s.Ra.set(j, vl, cscale(csub({s.B[j][vl], 0.f}, xj), s.beta[j]));
         cf u = {0.f, 0.f};
-        for (int w = 0; w <= j; ++w) u = cadd(u, cmul({s.Tr[j][w], s.Ti[j][w]}, s.Ra.get(w, vl)));
+#pragma unroll
+        for (int w = 0; w < kC; ++w) u = cadd(u, cmul({s.Tr[j][w], s.Ti[j][w]}, s.Ra.get(w, vl)));
         s.Rb.set(j, vl, u);
         cf o = yj;
-        for (int w = 0; w <= j; ++w) o = cadd(o, cmul({s.Pr[j][w], s.Pi[j][w]}, s.Rb.get(w, vl)));
+#pragma unroll
+        for (int w = 0; w < kC; ++w) o = cadd(o, cmul({s.Pr[j][w], s.Pi[j][w]}, s.Rb.get(w, vl)));
         s.Os[j][vl] = o.r;
         // S1 = S0 diag(E_L) + U^T (K exp(gam_L - gam))
 #pragma unroll
@@ -462,11 +466,14 @@ __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const fl
             a = {group_sum<kC>(a.r), group_sum<kC>(a.i)};
             if (t == j) ub = a;
         }
-        for (int w = j; w < kC; ++w) ub = cadd(ub, cscale({s.Pr[w][j], -s.Pi[w][j]}, s.B[w][vl]));
+        // (T and P are zero above the diagonal: all 16 steps, no divergent loop)
+#pragma unroll
+        for (int w = 0; w < kC; ++w) ub = cadd(ub, cscale({s.Pr[w][j], -s.Pi[w][j]}, s.B[w][vl]));
         s.Ra.set(j, vl, ub);
-        // lambda_j = sum_{w >= j} conj(T_wj) Ub_w (the row's lanes: one wave, program order)
+        // lambda_j = sum_w conj(T_wj) Ub_w (the row's lanes: one wave, program order)
         cf lm = {0.f, 0.f};
-        for (int w = j; w < kC; ++w) lm = cadd(lm, cmul({s.Tr[w][j], -s.Ti[w][j]}, s.Ra.get(w, vl)));
+#pragma unroll
+        for (int w = 0; w < kC; ++w) lm = cadd(lm, cmul({s.Tr[w][j], -s.Ti[w][j]}, s.Ra.get(w, vl)));
         s.Rb.set(j, vl, lm);
         {
             float* lp = lam + (chunk * 2 * D + v) * kC + j;
@@ -514,13 +521,13 @@ __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const fl
 //     Ab = -strictly-lower(lambda U^H)      Pb = lower(dO U^H)
 //     dbeta = Re rowsum(conj(lambda) (V - X)) + Re rowsum(conj(Ab) G)
 // and K, Q, gam get the cotangents of the scaled tiles and of the pairwise G, H.
-template <int D> struct ChunkBwdLds {
+template <int D, int NTH> struct ChunkBwdLds {
     float K[kC][D + 1], Q[kC][D + 1], V[kC][D + 1];
     float gr[kC][D + 1], gi[kC][D + 1];     // gam
     float kgr[kC][D + 1], kgi[kC][D + 1];   // K E, then the cotangent of gam
     float Gr[kC][kC + 1], Gi[kC][kC + 1], Tr[kC][kC + 1], Ti[kC][kC + 1], Pr[kC][kC + 1], Pi[kC][kC + 1];
     float beta[kC];
-    float tr[kPT / D][D], ti[kPT / D][D];
+    float tr[NTH / D][D], ti[NTH / D][D];
     float S0r[D][D + 1], S0i[D][D + 1];   // state entering the chunk
     float S1r[D][D + 1], S1i[D][D + 1];   // cotangent of the state leaving it
     float dO[kC][D + 1];
@@ -528,18 +535,22 @@ template <int D> struct ChunkBwdLds {
     float Gbr[kC][kC + 1], Gbi[kC][kC + 1];   // cotangent of G (beta Ab)
     float Hbr[kC][kC + 1], Hbi[kC][kC + 1];   // cotangent of H (Pb)
     float dbA[kC][kC + 1];                    // Re(conj(Ab) G) per pair
-    float red[2 * (kPT / D)][D];              // per-channel partial sums over rows
+    float red[2 * (NTH / D)][D];              // per-channel partial sums over rows
     float glr[D], gli[D];                     // cotangent of gam_L from the state's decay
 };
 
+// Threads of phase_bwd_chunk: 512 (two waves per SIMD) where every phase has work
+// for them (d >= 32).
+template <int D> constexpr int bwd_chunk_threads() { return D >= 32 ? 512 : 256; }
+
 template <typename TI, int GATE, int D>
-__global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const float* __restrict__ states,
-                                                              const float* __restrict__ mats,
-                                                              const float* __restrict__ lam,
-                                                              const float* __restrict__ dS1) {
-    using CI = ChunkIn<TI, GATE, D>;
-    constexpr int PG = kPT / D, NC = D / PG;
-    __shared__ ChunkBwdLds<D> b;
+__global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel(
+    Params p, const float* __restrict__ states, const float* __restrict__ mats, const float* __restrict__ lam,
+    const float* __restrict__ dS1) {
+    constexpr int NTH = bwd_chunk_threads<D>();
+    using CI = ChunkIn<TI, GATE, D, NTH>;
+    constexpr int PG = NTH / D <= D ? NTH / D : D, NC = D / PG;   // lanes per state row in (b)
+    __shared__ ChunkBwdLds<D, NTH> b;
     const int tid = threadIdx.x, n = blockIdx.x, bh = blockIdx.y;
     const int t0 = n * kC, valid = min(kC, p.T - t0), L = valid - 1;
     const long row0 = (long)bh * p.T + t0, chunk = (long)bh * p.NT + n;
@@ -553,7 +564,7 @@ __global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const fl
     {
         const float* st = states + chunk * 2 * D * D;
         const float* d1 = dS1 + chunk * 2 * D * D;
-        for (int idx = tid; idx < D * D; idx += kPT) {
+        for (int idx = tid; idx < D * D; idx += NTH) {
             const int r = idx / D, c = idx % D;
             b.S0r[r][c] = st[idx];
             b.S0i[r][c] = st[(long)D * D + idx];
@@ -561,12 +572,12 @@ __global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const fl
             b.S1i[r][c] = d1[(long)D * D + idx];
         }
         const float* lm = lam + chunk * 2 * D * kC;
-        for (int idx = tid; idx < D * kC; idx += kPT) {
+        for (int idx = tid; idx < D * kC; idx += NTH) {
             const int vv = idx / kC, t = idx % kC;
             b.LB.r[t][vv] = lm[idx];
             b.LB.i[t][vv] = lm[(long)D * kC + idx];
         }
-        for (int idx = tid; idx < kC * D; idx += kPT) {
+        for (int idx = tid; idx < kC * D; idx += NTH) {
             const int t = idx / D, c = idx % D;
             const bool ok = t < valid;
             const long e = (row0 + (ok ? t : 0)) * D + c;
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const fl
             b.V[t][c] = ok ? vv : 0.f;
         }
         const float* mc = mats + chunk * kMats;
-        {
+        if (tid < kCC) {
             const int t = tid / kC, u = tid % kC;
             b.Tr[t][u] = mc[tid];
             b.Ti[t][u] = mc[kCC + tid];
@@ -607,7 +618,7 @@ __global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const fl
     __syncthreads();
     // (b) X = (K E) S0^T and U = T beta (V - X): rows v of the state by groups of PG
     //     lanes, NC channels each; the row's lanes take every PG-th step of U
-    {
+    if (tid < D * PG) {
         const int v = tid / PG, j = tid % PG, c0 = j * NC;
         float sr[NC], si[NC];
 #pragma unroll
@@ -631,9 +642,10 @@ __global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const fl
         }
     }
     __syncthreads();
-    // (c) pairs: Ab = -lambda U^H (strictly lower), Pb = dO U^H (lower); per channel the
-    //     cotangent of gam_L through the state's decay, sum_v dS1 conj(S0 E_L)
-    {
+    // (c) pairs: Ab = -lambda U^H (strictly lower), Pb = dO U^H (lower), one per thread
+    //     of the first 256; per channel, by the threads after them, the cotangent of
+    //     gam_L through the state's decay, sum_v dS1 conj(S0 E_L)
+    if (tid < kCC) {
         const int t = tid / kC, u = tid % kC;
         cf ab = {0.f, 0.f}, pb = {0.f, 0.f};
         if (u <= t) {
@@ -651,8 +663,8 @@ __global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const fl
         b.Hbi[t][u] = pb.i;
         b.dbA[t][u] = ab.r * b.Gr[t][u] + ab.i * b.Gi[t][u];   // Re(conj(Ab) G)
     }
-    if (tid < D) {
-        const int c = tid;
+    if (tid >= NTH - D) {
+        const int c = tid - (NTH - D);
         cf acc = {0.f, 0.f};
 #pragma unroll 4
         for (int w = 0; w < D; ++w) acc = cadd(acc, cmulc({b.S1r[w][c], b.S1i[w][c]}, {b.S0r[w][c], b.S0i[w][c]}));
@@ -665,20 +677,34 @@ __global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const fl
     // (d) elements (t, c): the scaled tiles' cotangents from sums over the rows v, the
     //     pairwise G / H terms; dq, dk; gam's cotangent, stored over (K E) at the same
     //     element (each element of K E is read here only by the thread that replaces it)
-    constexpr int TS = kPT / D;   // threads sharing a channel (rows t = tid / D + TS j)
+    constexpr int TS = NTH / D;                         // threads sharing a channel
+    constexpr int NRD = TS < kC ? kC / TS : 1;          // their rows t = tid / D + TS r
     {
         const int c = tid % D, tg = tid / D;
         cf kdsum = {0.f, 0.f};
-        for (int t = tg; t < kC; t += TS) {
-            cf Kgb = {0.f, 0.f}, Qgb = {0.f, 0.f}, Kdb = {0.f, 0.f};
+        // the three sums over the rows v for all of the thread's steps at once: each
+        // S0 / dS1 element is read once for them
+        cf Kgs[NRD], Qgs[NRD], Kds[NRD];
+#pragma unroll
+        for (int r = 0; r < NRD; ++r) Kgs[r] = Qgs[r] = Kds[r] = {0.f, 0.f};
+        if (tg < kC) {
 #pragma unroll 4
             for (int w = 0; w < D; ++w) {
-                const cf S = {b.S0r[w][c], b.S0i[w][c]};
-                Kgb = csub(Kgb, cmulc(b.LB.get(t, w), S));
-                Qgb = cadd(Qgb, cmulc({b.dO[t][w], 0.f}, S));
-                Kdb = cadd(Kdb, cmulc({b.S1r[w][c], b.S1i[w][c]}, b.U.get(t, w)));
+                const cf S = {b.S0r[w][c], b.S0i[w][c]}, S1 = {b.S1r[w][c], b.S1i[w][c]};
+#pragma unroll
+                for (int r = 0; r < NRD; ++r) {
+                    const int t = tg + TS * r;
+                    Kgs[r] = csub(Kgs[r], cmulc(b.LB.get(t, w), S));
+                    Qgs[r] = cadd(Qgs[r], cmulc({b.dO[t][w], 0.f}, S));
+                    Kds[r] = cadd(Kds[r], cmulc(S1, b.U.get(t, w)));
+                }
             }
-            Kgb = cscale(Kgb, b.beta[t]);
+        }
+#pragma unroll
+        for (int r = 0; r < NRD; ++r) {
+            const int t = tg + TS * r;
+            if (t >= kC) break;
+            const cf Kgb = cscale(Kgs[r], b.beta[t]), Qgb = Qgs[r], Kdb = Kds[r];
             const cf E = cexp_(b.gr[t][c], b.gi[t][c]);
             const cf Ed = cexp_(b.gr[L][c] - b.gr[t][c], b.gi[L][c] - b.gi[t][c]);
             const float kt = b.K[t][c], qt = b.Q[t][c];
@@ -740,8 +766,8 @@ __global__ __launch_bounds__(kPT) void phase_bwd_chunk_kernel(Params p, const fl
         }
     }
     // dbeta_t = Re sum_v conj(lambda_tv) (V - X)_tv + sum_u Re(conj(Ab_tu) G_tu)
-    if (tid >= kPT - kC) {
-        const int t = tid - (kPT - kC);
+    if (tid >= NTH - kC) {
+        const int t = tid - (NTH - kC);
         if (t < valid) {
             float acc = 0.f;
 #pragma unroll 4
@@ -777,8 +803,8 @@ hipError_t phase_launch_d(const Params& p, const PhaseBufs& f, bool backward, hi
         hipLaunchKernelGGL((phase_bwd_state_kernel<TI, GATE, D>), seq, block, 0, stream, p, f.mats, f.lam, f.dS1);
         prof_end(stream);
         prof_begin(stream, "phase_bwd_chunk");
-        hipLaunchKernelGGL((phase_bwd_chunk_kernel<TI, GATE, D>), chunks, block, 0, stream, p, f.states, f.mats,
-                           f.lam, f.dS1);
+        hipLaunchKernelGGL((phase_bwd_chunk_kernel<TI, GATE, D>), chunks, dim3(bwd_chunk_threads<D>()), 0, stream, p,
+                           f.states, f.mats, f.lam, f.dS1);
         prof_end(stream);
     }
     return hipGetLastError();
