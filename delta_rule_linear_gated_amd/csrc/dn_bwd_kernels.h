@@ -48,8 +48,40 @@ namespace dn {
 //            p.seg_end, nothing else written.
 // Otherwise, with segments, a segment starts from the dS the combine left in
 // p.seg_start (the last from dhT) and writes lambda, dv and dS1 of its chunks.
-template <typename TI, int GATE, int C, int DK, int BV, bool SUMMARY = false>
-__global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
+// LDS arrays of the backward state pass (see FwdStateArrays).
+template <typename TI, int GATE, int C, int DK, int BV> struct BwdStateArrays {
+    static constexpr int PAD = Pad<TI>::value, LDK = DK + PAD, LDC = C + PAD, LDV = BV + PAD;
+    static constexpr bool VEC = GATE == kGateVector, SCA = GATE == kGateScalar;
+    float gam_s[C];
+    __align__(16) float egc[VEC ? DK : 4];   // e^{gam_C} per channel (vector gate)
+    __align__(16) float rowf[2 * C];
+    __align__(16) float beta_s[C];
+    __align__(16) TI dSs[BV * LDK];   // dS1 operand     [v][c]
+    __align__(16) TI Kd[C * LDK];     // K (vector gate: K Gam_C / Gam)  [t][c]
+    __align__(16) TI Kn[VEC ? C * LDK : 8];   // -K Gam (vector gate)    [t][c]
+    __align__(16) TI Qg[C * LDK];     // Q (vector gate: Q Gam)          [t][c]
+    __align__(16) TI Pl[C * LDC];     // P               [s][t]
+    __align__(16) TI Tl[C * LDC];     // T               [s][t]
+    __align__(16) TI dOb[C * LDV];    // dO block        [t][v]
+    __align__(16) TI dOg[SCA ? C * LDV : 8];  // dO Gam (scalar gate)    [t][v]
+    __align__(16) TI dUT[BV * LDC];   // dU^T            [v][t]
+    // lambda and dv = beta lambda [t][v], written back a chunk later; without a
+    // vector gate the dS update takes -beta lambda (Gam) from Dn, else dv itself
+    __align__(16) TI Lb[C * LDV];
+    __align__(16) TI Db[C * LDV];
+    __align__(16) TI Dn[VEC ? 8 : C * LDV];
+};
+
+// The pass for workgroup `wg` of its grid (LDS arrays as restrict pointers, as
+// for fwd_state_body).
+template <typename TI, int GATE, int C, int DK, int BV, bool SUMMARY>
+__device__ __forceinline__ void bwd_state_body(const Params& p, int wg, float* __restrict__ gam_s,
+                                               float* __restrict__ egc, float* __restrict__ rowf,
+                                               float* __restrict__ beta_s, TI* __restrict__ dSs,
+                                               TI* __restrict__ Kd, TI* __restrict__ Kn, TI* __restrict__ Qg,
+                                               TI* __restrict__ Pl, TI* __restrict__ Tl, TI* __restrict__ dOb,
+                                               TI* __restrict__ dOg, TI* __restrict__ dUT, TI* __restrict__ Lb,
+                                               TI* __restrict__ Db, TI* __restrict__ Dn) {
     constexpr int PAD = Pad<TI>::value;
     constexpr int LDK = DK + PAD;
     constexpr int LDC = C + PAD;
@@ -62,30 +94,12 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
     // dU, e^{gam_t} to copies of dO and of -beta lambda for the dS update.  The
     // vector gate scales Q and K per element, from gate values held in registers
     // in the layout of the K / Q register tiles (VecGate).
-    __shared__ float gam_s[C];
-    __shared__ __align__(16) float egc[VEC ? DK : 4];   // e^{gam_C} per channel (vector gate)
-    __shared__ __align__(16) float rowf[2 * C];
-    __shared__ __align__(16) float beta_s[C];
-    __shared__ __align__(16) TI dSs[BV * LDK];   // dS1 operand     [v][c]
-    __shared__ __align__(16) TI Kd[C * LDK];     // K (vector gate: K Gam_C / Gam)  [t][c]
-    __shared__ __align__(16) TI Kn[VEC ? C * LDK : 8];   // -K Gam (vector gate)    [t][c]
-    __shared__ __align__(16) TI Qg[C * LDK];     // Q (vector gate: Q Gam)          [t][c]
-    __shared__ __align__(16) TI Pl[C * LDC];     // P               [s][t]
-    __shared__ __align__(16) TI Tl[C * LDC];     // T               [s][t]
-    __shared__ __align__(16) TI dOb[C * LDV];    // dO block        [t][v]
-    __shared__ __align__(16) TI dOg[SCA ? C * LDV : 8];  // dO Gam (scalar gate)    [t][v]
-    __shared__ __align__(16) TI dUT[BV * LDC];   // dU^T            [v][t]
-    // lambda and dv = beta lambda [t][v], written back a chunk later; without a
-    // vector gate the dS update takes -beta lambda (Gam) from Dn, else dv itself
-    __shared__ __align__(16) TI Lb[C * LDV];
-    __shared__ __align__(16) TI Db[C * LDV];
-    __shared__ __align__(16) TI Dn[VEC ? 8 : C * LDV];
 
     const int DVr = p.DVr;
     const int rows = DVr + (SUMMARY ? DK : 0);
     const int nblk = rows / BV;
     int bh, sb;
-    head_and_block(nblk * p.nseg, p.BH, bh, sb);
+    head_and_block(nblk * p.nseg, p.BH, bh, sb, wg);
     const int seg = sb / nblk, vblk = sb - seg * nblk;
     const int v0 = vblk * BV;
     const bool trans = SUMMARY && v0 >= DVr;   // rows of the transposed transition
@@ -257,6 +271,36 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
         float* out = p.seg_end + ((long)bh * p.nseg + seg) * rows * DK;
 #pragma unroll
         for (int j = 0; j < TS::PER; ++j) st4<float>(out + (long)(v0 + TS::col(j)) * DK + TS::row(j, 0), dS[j]);
+    }
+}
+
+template <typename TI, int GATE, int C, int DK, int BV, bool SUMMARY = false>
+__global__ __launch_bounds__(kThreads) void bwd_state_kernel(Params p) {
+    __shared__ BwdStateArrays<TI, GATE, C, DK, BV> a;
+    bwd_state_body<TI, GATE, C, DK, BV, SUMMARY>(p, blockIdx.x, a.gam_s, a.egc, a.rowf, a.beta_s, a.dSs, a.Kd, a.Kn,
+                                                 a.Qg, a.Pl, a.Tl, a.dOb, a.dOg, a.dUT, a.Lb, a.Db, a.Dn);
+}
+
+// The recomputing backward's forward state pass (chunk states into the
+// workspace) and the backward state pass in one launch.  The reverse pass needs
+// no chunk state, so the two chains are independent: workgroups [0, nf) walk the
+// forward chains, the others the reverse ones, and the two kinds overlay their
+// LDS arrays, so that one of each shares a compute unit where LDS and registers
+// allow.  Both chains are latency-bound; side by side each hides the other's waits.
+template <typename TI, int GATE, int C, int DK, int BV>
+__global__ __launch_bounds__(kThreads) void recompute_bwd_state_kernel(Params p, int nf) {
+    __shared__ union {
+        FwdStateArrays<TI, GATE, C, DK, BV, false> f;
+        BwdStateArrays<TI, GATE, C, DK, BV> b;
+    } u;
+    if ((int)blockIdx.x < nf) {
+        auto& a = u.f;
+        fwd_state_body<TI, GATE, C, DK, BV, true, false>(p, blockIdx.x, a.gam_s, a.egc, a.rowf, a.beta_s, a.Ss, a.Qg,
+                                                         a.Kg, a.Kd, a.Vb, a.Tl, a.Pl, a.Rb, a.Ud);
+    } else {
+        auto& a = u.b;
+        bwd_state_body<TI, GATE, C, DK, BV, false>(p, blockIdx.x - nf, a.gam_s, a.egc, a.rowf, a.beta_s, a.dSs, a.Kd,
+                                                   a.Kn, a.Qg, a.Pl, a.Tl, a.dOb, a.dOg, a.dUT, a.Lb, a.Db, a.Dn);
     }
 }
 

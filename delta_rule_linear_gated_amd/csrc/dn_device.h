@@ -864,8 +864,7 @@ __device__ __forceinline__ void lds_to_global(T* __restrict__ g, long gld, const
 // q / k / T / P tiles, so they are given ids that are equal mod 8 (same XCD,
 // shared L2).  Falls back to the plain order when BH is not a multiple of 8.
 constexpr int kXcds = 8;
-__device__ __forceinline__ void head_and_block(int nblk, int BH, int& bh, int& blk) {
-    const int id = blockIdx.x;
+__device__ __forceinline__ void head_and_block(int nblk, int BH, int& bh, int& blk, int id = blockIdx.x) {
     if (BH % kXcds == 0) {
         const int x = id % kXcds, k = id / kXcds;
         bh = (k / nblk) * kXcds + x;

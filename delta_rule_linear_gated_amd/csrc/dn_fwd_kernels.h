@@ -594,8 +594,37 @@ template <typename TI, int GATE, int C, int DK, int BV> constexpr size_t fwd_sta
     return 4 * (G + 3 * C) + E * (BV * LDK + NK * C * LDK + NV * C * LDV + 2 * C * LDC) + 96;
 }
 
+// LDS arrays of the forward state pass.  The kernel declares them one by one;
+// a launch that runs another pass in its other workgroups overlays both passes'
+// arrays in a union of these structs.
+template <typename TI, int GATE, int C, int DK, int BV, bool OUTPUT> struct FwdStateArrays {
+    static constexpr int PAD = Pad<TI>::value, LDK = DK + PAD, LDC = C + PAD, LDV = BV + PAD;
+    static constexpr bool VEC = GATE == kGateVector, SCA = GATE == kGateScalar;
+    float gam_s[C];
+    __align__(16) float egc[VEC ? DK : 4];   // e^{gam_C} per channel (vector gate)
+    float rowf[2 * C];
+    __align__(16) float beta_s[C];
+    __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
+    __align__(16) TI Qg[OUTPUT ? C * LDK : 8];   // Q (vector gate: Q Gam)  [t][c]
+    __align__(16) TI Kg[C * LDK];     // K (vector gate: K Gam)            [t][c]
+    __align__(16) TI Kd[VEC ? C * LDK : 8];   // K Gam_C / Gam (vector gate) [t][c]
+    __align__(16) TI Vb[C * LDV];     // V block [t][v]; after (c) U [t][v]
+    __align__(16) TI Tl[C * LDC];     // T                 [t][s]
+    __align__(16) TI Pl[OUTPUT ? C * LDC : 8];   // P (only with the output)  [t][s]
+    // R [t][v]; after (d) it holds the chunk's O [t][v] until the next iteration writes it back
+    __align__(16) TI Rb[C * LDV];
+    __align__(16) TI Ud[SCA ? C * LDV : 8];   // U Gam_C / Gam (scalar gate) [t][v]
+};
+
+// The pass for workgroup `wg` of its grid.  Each LDS array arrives as a restrict
+// pointer, so after inlining the compiler knows they do not overlap.
 template <typename TI, int GATE, int C, int DK, int BV, bool SAVE, bool OUTPUT>
-__global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
+__device__ __forceinline__ void fwd_state_body(const Params& p, int wg, float* __restrict__ gam_s,
+                                               float* __restrict__ egc, float* __restrict__ rowf,
+                                               float* __restrict__ beta_s, TI* __restrict__ Ss,
+                                               TI* __restrict__ Qg, TI* __restrict__ Kg, TI* __restrict__ Kd,
+                                               TI* __restrict__ Vb, TI* __restrict__ Tl, TI* __restrict__ Pl,
+                                               TI* __restrict__ Rb, TI* __restrict__ Ud) {
     constexpr int PAD = Pad<TI>::value;
     constexpr int LDK = DK + PAD;
     constexpr int LDC = C + PAD;
@@ -610,28 +639,14 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
     // e^{gam_C - gam_t} to a second copy of U that feeds the state update.  The
     // per-channel vector gate scales Q and K per element, from gate values held
     // in registers in the layout of the K / Q register tiles (VecGate).
-    __shared__ float gam_s[C];
-    __shared__ __align__(16) float egc[VEC ? DK : 4];   // e^{gam_C} per channel (vector gate)
-    __shared__ float rowf[2 * C];
-    __shared__ __align__(16) float beta_s[C];
-    __shared__ __align__(16) TI Ss[BV * LDK];    // S0 (operand copy) [v][c]
-    __shared__ __align__(16) TI Qg[OUTPUT ? C * LDK : 8];   // Q (vector gate: Q Gam)  [t][c]
-    __shared__ __align__(16) TI Kg[C * LDK];     // K (vector gate: K Gam)            [t][c]
-    __shared__ __align__(16) TI Kd[VEC ? C * LDK : 8];   // K Gam_C / Gam (vector gate) [t][c]
-    __shared__ __align__(16) TI Vb[C * LDV];     // V block [t][v]; after (c) U [t][v]
-    __shared__ __align__(16) TI Tl[C * LDC];     // T                 [t][s]
-    __shared__ __align__(16) TI Pl[C * LDC];     // P                 [t][s]
-    // R [t][v]; after (d) it holds the chunk's O [t][v] until the next iteration writes it back
-    __shared__ __align__(16) TI Rb[C * LDV];
     TI* const Ub = Vb;                           // V is dead once R is formed
-    __shared__ __align__(16) TI Ud[SCA ? C * LDV : 8];   // U Gam_C / Gam (scalar gate) [t][v]
 
     constexpr bool SUMMARY = !SAVE && !OUTPUT;
     const int DVr = p.DVr;
     const int rows = DVr + (SUMMARY ? DK : 0);
     const int nblk = rows / BV;
     int bh, sb;
-    head_and_block(nblk * p.nseg, p.BH, bh, sb);
+    head_and_block(nblk * p.nseg, p.BH, bh, sb, wg);
     const int seg = sb / nblk, vblk = sb - seg * nblk;
     const int v0 = vblk * BV;
     const bool trans = SUMMARY && v0 >= DVr;   // rows of the transition matrix
@@ -810,6 +825,13 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < TS::PER; ++j) st4<float>(out + (long)(v0 + TS::col(j)) * DK + TS::row(j, 0), S[j]);
     }
+}
+
+template <typename TI, int GATE, int C, int DK, int BV, bool SAVE, bool OUTPUT>
+__global__ __launch_bounds__(kThreads) void fwd_state_kernel(Params p) {
+    __shared__ FwdStateArrays<TI, GATE, C, DK, BV, OUTPUT> a;
+    fwd_state_body<TI, GATE, C, DK, BV, SAVE, OUTPUT>(p, blockIdx.x, a.gam_s, a.egc, a.rowf, a.beta_s, a.Ss, a.Qg,
+                                                      a.Kg, a.Kd, a.Vb, a.Tl, a.Pl, a.Rb, a.Ud);
 }
 
 }  // namespace dn

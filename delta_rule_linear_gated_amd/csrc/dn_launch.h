@@ -180,21 +180,51 @@ hipError_t fwd_impl(const Problem& pr, const Params& p, bool save, hipStream_t s
     }
 }
 
+// The recomputing backward without segments: its forward state pass and the
+// backward state pass in one launch (recompute_bwd_state_kernel), when two of its
+// workgroups fit on a compute unit; false (nothing launched) otherwise.
+template <typename TI, int GATE, int C, int D, int BV>
+bool launch_recompute_bwd_state(const Params& p, int BH, hipStream_t stream) {
+    if (resident_per_cu<recompute_bwd_state_kernel<TI, GATE, C, D, BV>>() < 2) return false;
+    const int nf = (p.DVr / BV) * BH;
+    prof_begin(stream, "fwd_state_recompute+bwd_state");
+    hipLaunchKernelGGL((recompute_bwd_state_kernel<TI, GATE, C, D, BV>), dim3(2 * nf), dim3(kThreads), 0, stream, p,
+                       nf);
+    prof_end(stream);
+    return true;
+}
+
+template <typename TI, int GATE, int C, int D>
+bool recompute_with_bwd_state(const Params& p, int BH, hipStream_t stream) {
+    const int bv = state_block<TI, GATE, C, D>(BH);
+    if constexpr (state_fits<TI, GATE, C, D, 64>())
+        if (bv == 64) return launch_recompute_bwd_state<TI, GATE, C, D, 64>(p, BH, stream);
+    if constexpr (state_fits<TI, GATE, C, D, 32>())
+        if (bv == 32) return launch_recompute_bwd_state<TI, GATE, C, D, 32>(p, BH, stream);
+    if constexpr (state_fits<TI, GATE, C, D, 16>())
+        if (bv == 16) return launch_recompute_bwd_state<TI, GATE, C, D, 16>(p, BH, stream);
+    return false;
+}
+
 template <typename TI, int GATE, int C, int D>
 hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStream_t stream) {
     if constexpr (!Fits<TI, GATE, C, D>::value) {
         return hipErrorInvalidConfiguration;
     } else {
         const int BH = pr.B * pr.H;
+        bool fused = false;   // the recomputed forward state pass and bwd_state in one launch
         if (!have_states) {   // recomputation policy: gam, T, P and the states into the workspace
             Params pp = p;
             pp.resident = device_cus() * resident_per_cu<prep_kernel<TI, GATE, C, D>>();
             prof_begin(stream, "prep_recompute");
             hipLaunchKernelGGL((prep_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, pp);
             prof_end(stream);
-            const hipError_t e = fwd_state_pass<TI, GATE, C, D, false>(p, BH, true, "fwd_state_recompute",
-                                                                      "fwd_summary_recompute", stream);
-            if (e != hipSuccess) return e;
+            fused = p.nseg == 1 && recompute_with_bwd_state<TI, GATE, C, D>(p, BH, stream);
+            if (!fused) {
+                const hipError_t e = fwd_state_pass<TI, GATE, C, D, false>(p, BH, true, "fwd_state_recompute",
+                                                                          "fwd_summary_recompute", stream);
+                if (e != hipSuccess) return e;
+            }
         }
         if (p.nseg > 1) {   // the reverse scan: segment summaries of dS, then the combine
             prof_begin(stream, "bwd_summary");
@@ -203,9 +233,11 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
             const hipError_t e = launch_scan_combine(p, D, false, stream);
             if (e != hipSuccess) return e;
         }
-        prof_begin(stream, "bwd_state");
-        bwd_state<TI, GATE, C, D>(p, BH, 0, stream);
-        prof_end(stream);
+        if (!fused) {
+            prof_begin(stream, "bwd_state");
+            bwd_state<TI, GATE, C, D>(p, BH, 0, stream);
+            prof_end(stream);
+        }
         Params pc = p;
         pc.resident = device_cus() * resident_per_cu<bwd_chunk_kernel<TI, GATE, C, D>>();
         prof_begin(stream, "bwd_chunk");
