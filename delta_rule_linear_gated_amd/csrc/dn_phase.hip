@@ -528,15 +528,16 @@ template <int D, int NTH> struct ChunkBwdLds {
     float Gr[kC][kC + 1], Gi[kC][kC + 1], Tr[kC][kC + 1], Ti[kC][kC + 1], Pr[kC][kC + 1], Pi[kC][kC + 1];
     float beta[kC];
     float tr[NTH / D][D], ti[NTH / D][D];
-    float S0r[D][D + 1], S0i[D][D + 1];   // state entering the chunk
-    float S1r[D][D + 1], S1i[D][D + 1];   // cotangent of the state leaving it
+    // the state entering the chunk (S0 re, im) and the cotangent of the state leaving
+    // it (dS1 re, im), D rows each; after the products of (c), the six [C][D] sums
+    float SS[4 * D > 6 * kC ? 4 * D : 6 * kC][D + 1];
     float dO[kC][D + 1];
     Rows<D> U, LB, X;                     // U; lambda; X
     float Gbr[kC][kC + 1], Gbi[kC][kC + 1];   // cotangent of G (beta Ab)
     float Hbr[kC][kC + 1], Hbi[kC][kC + 1];   // cotangent of H (Pb)
     float dbA[kC][kC + 1];                    // Re(conj(Ab) G) per pair
     float red[2 * (NTH / D)][D];              // per-channel partial sums over rows
-    float glr[D], gli[D];                     // cotangent of gam_L from the state's decay
+    float glp[2 * (NTH / D)][D];              // partials of sum_w dS1 conj(S0) per channel
 };
 
 // Threads of phase_bwd_chunk: 512 (two waves per SIMD) where every phase has work
@@ -551,6 +552,7 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
     using CI = ChunkIn<TI, GATE, D, NTH>;
     constexpr int PG = NTH / D <= D ? NTH / D : D, NC = D / PG;   // lanes per state row in (b)
     __shared__ ChunkBwdLds<D, NTH> b;
+    float(*S0r)[D + 1] = b.SS, (*S0i)[D + 1] = b.SS + D, (*S1r)[D + 1] = b.SS + 2 * D, (*S1i)[D + 1] = b.SS + 3 * D;
     const int tid = threadIdx.x, n = blockIdx.x, bh = blockIdx.y;
     const int t0 = n * kC, valid = min(kC, p.T - t0), L = valid - 1;
     const long row0 = (long)bh * p.T + t0, chunk = (long)bh * p.NT + n;
@@ -566,10 +568,10 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
         const float* d1 = dS1 + chunk * 2 * D * D;
         for (int idx = tid; idx < D * D; idx += NTH) {
             const int r = idx / D, c = idx % D;
-            b.S0r[r][c] = st[idx];
-            b.S0i[r][c] = st[(long)D * D + idx];
-            b.S1r[r][c] = d1[idx];
-            b.S1i[r][c] = d1[(long)D * D + idx];
+            S0r[r][c] = st[idx];
+            S0i[r][c] = st[(long)D * D + idx];
+            S1r[r][c] = d1[idx];
+            S1i[r][c] = d1[(long)D * D + idx];
         }
         const float* lm = lam + chunk * 2 * D * kC;
         for (int idx = tid; idx < D * kC; idx += NTH) {
@@ -616,95 +618,171 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
         }
     }
     __syncthreads();
-    // (b) X = (K E) S0^T and U = T beta (V - X): rows v of the state by groups of PG
-    //     lanes, NC channels each; the row's lanes take every PG-th step of U
-    if (tid < D * PG) {
-        const int v = tid / PG, j = tid % PG, c0 = j * NC;
-        float sr[NC], si[NC];
+    // Every product below runs on the fp32 matrix cores: a complex product is two
+    // or four real 16x16x4 MFMA products into one accumulator per real output
+    // (signs folded into the A fragment).  Fragments: lane l supplies A row l % 16
+    // and B row l % 16 at K slot l / 16; accumulator element i of lane l is
+    // output (4 (l / 16) + i, l % 16) of the 16 x 16 tile.  Work items go to the
+    // waves round-robin.
+    const int lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
+    constexpr int NW = NTH / 64, NTL = D / 16;   // waves; 16-wide column tiles of a D-wide output
+    auto mma = [](float a, float bb, f32x4 acc) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0); };
+    // (b) X = (K E) S0^T (kept for dbeta), then R = beta (V - X) over K E (dead once X
+    //     is formed) and U = T R; items (column tile of v, real or imaginary part)
+    for (int it = wave; it < 2 * NTL; it += NW) {
+        const int n0 = (it >> 1) * 16;
+        f32x4 acc = zero4();
+#pragma unroll 4
+        for (int k0 = 0; k0 < D; k0 += 4) {
+            const float ar = b.kgr[li][k0 + lk], ai = b.kgi[li][k0 + lk];
+            const float sr = S0r[n0 + li][k0 + lk], si = S0i[n0 + li][k0 + lk];
+            if (it & 1) acc = mma(ai, sr, mma(ar, si, acc));    // Xi = KEr S0i^T + KEi S0r^T
+            else acc = mma(-ai, si, mma(ar, sr, acc));          // Xr = KEr S0r^T - KEi S0i^T
+        }
+        float(*xo)[D + 1] = (it & 1) ? b.X.i : b.X.r;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            sr[c] = b.S0r[v][c0 + c];
-            si[c] = b.S0i[v][c0 + c];
-        }
-#pragma unroll 1
-        for (int t = 0; t < kC; ++t) {
-            cf x = {0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) x = cadd(x, cmul({b.kgr[t][c0 + c], b.kgi[t][c0 + c]}, {sr[c], si[c]}));
-            x = {group_sum<PG>(x.r), group_sum<PG>(x.i)};
-            if (j == 0) b.X.set(t, v, x);
-        }
-        for (int t = j; t < kC; t += PG) {
-            cf u = {0.f, 0.f};
-            for (int w = 0; w <= t; ++w)
-                u = cadd(u, cmul({b.Tr[t][w], b.Ti[t][w]}, cscale(csub({b.V[w][v], 0.f}, b.X.get(w, v)), b.beta[w])));
-            b.U.set(t, v, u);
-        }
+        for (int i = 0; i < 4; ++i) xo[4 * lk + i][n0 + li] = acc[i];
     }
     __syncthreads();
-    // (c) pairs: Ab = -lambda U^H (strictly lower), Pb = dO U^H (lower), one per thread
-    //     of the first 256; per channel, by the threads after them, the cotangent of
-    //     gam_L through the state's decay, sum_v dS1 conj(S0 E_L)
-    if (tid < kCC) {
-        const int t = tid / kC, u = tid % kC;
-        cf ab = {0.f, 0.f}, pb = {0.f, 0.f};
-        if (u <= t) {
-#pragma unroll 4
-            for (int w = 0; w < D; ++w) {
-                const cf Uc = b.U.get(u, w);
-                ab = csub(ab, cmulc(b.LB.get(t, w), Uc));
-                pb = cadd(pb, cmulc({b.dO[t][w], 0.f}, Uc));
-            }
-        }
-        if (u == t) ab = {0.f, 0.f};
-        b.Gbr[t][u] = b.beta[t] * ab.r;
-        b.Gbi[t][u] = b.beta[t] * ab.i;
-        b.Hbr[t][u] = pb.r;
-        b.Hbi[t][u] = pb.i;
-        b.dbA[t][u] = ab.r * b.Gr[t][u] + ab.i * b.Gi[t][u];   // Re(conj(Ab) G)
+    for (int idx = tid; idx < kC * D; idx += NTH) {
+        const int t = idx / D, v = idx % D;
+        b.kgr[t][v] = b.beta[t] * (b.V[t][v] - b.X.r[t][v]);
+        b.kgi[t][v] = -b.beta[t] * b.X.i[t][v];
     }
-    if (tid >= NTH - D) {
-        const int c = tid - (NTH - D);
+    __syncthreads();
+    for (int it = wave; it < 2 * NTL; it += NW) {
+        const int n0 = (it >> 1) * 16;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < kC; k0 += 4) {
+            const float tr = b.Tr[li][k0 + lk], ti = b.Ti[li][k0 + lk];
+            const float rr = b.kgr[k0 + lk][n0 + li], ri = b.kgi[k0 + lk][n0 + li];
+            if (it & 1) acc = mma(ti, rr, mma(tr, ri, acc));    // Ui = Tr Ri + Ti Rr
+            else acc = mma(-ti, ri, mma(tr, rr, acc));          // Ur = Tr Rr - Ti Ri
+        }
+        float(*uo)[D + 1] = (it & 1) ? b.U.i : b.U.r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) uo[4 * lk + i][n0 + li] = acc[i];
+    }
+    __syncthreads();
+    // (c) the three sums over the rows v per element (t, c), the pair products, and per
+    //     channel the state-decay term of gam_L:
+    //       Kgb = -sum_w lambda_tw conj(S0_wc)    Qgb = sum_w dO_tw conj(S0_wc)
+    //       Kdb = sum_w dS1_wc conj(U_tw)
+    //       Ab = -lambda U^H (strictly lower)      Pb = dO U^H (lower)
+    //       gl_c = sum_w dS1_wc conj(S0_wc E_L,c)
+    //     Items: Kgb and Qgb per column tile (waves 0 .. NTL - 1), Kdb per column tile
+    //     (the next NTL), Ab and Pb (one 16 x 16 tile each, on waves after those or
+    //     shared).  Kgb / Qgb / Kdb stay in registers until every wave has read S0 and
+    //     dS1, then go to LDS over them.
+    f32x4 res[4] = {zero4(), zero4(), zero4(), zero4()};
+    const int item = wave < 2 * NTL ? wave : -1;
+    if (item >= 0 && item < NTL) {
+        const int n0 = item * 16;
+#pragma unroll 4
+        for (int k0 = 0; k0 < D; k0 += 4) {
+            const float lr = b.LB.r[li][k0 + lk], lq = b.LB.i[li][k0 + lk], o = b.dO[li][k0 + lk];
+            const float sr = S0r[k0 + lk][n0 + li], si = S0i[k0 + lk][n0 + li];
+            res[0] = mma(lq, si, mma(lr, sr, res[0]));     // -Kgb_r = lr S0r + li S0i
+            res[1] = mma(-lr, si, mma(lq, sr, res[1]));    // -Kgb_i = li S0r - lr S0i
+            res[2] = mma(o, sr, res[2]);                   //  Qgb_r = dO S0r
+            res[3] = mma(-o, si, res[3]);                  //  Qgb_i = -dO S0i
+        }
+    } else if (item >= NTL) {
+        const int n0 = (item - NTL) * 16;
+#pragma unroll 4
+        for (int k0 = 0; k0 < D; k0 += 4) {
+            const float ur = b.U.r[li][k0 + lk], ui = b.U.i[li][k0 + lk];
+            const float sr = S1r[k0 + lk][n0 + li], si = S1i[k0 + lk][n0 + li];
+            res[0] = mma(ui, si, mma(ur, sr, res[0]));     // Kdb_r = Ur S1r + Ui S1i
+            res[1] = mma(-ui, sr, mma(ur, si, res[1]));    // Kdb_i = Ur S1i - Ui S1r
+        }
+    }
+    constexpr int AB_WAVE = 2 * NTL < NW ? 2 * NTL : NTL, PB_WAVE = 2 * NTL + 1 < NW ? 2 * NTL + 1 : NTL + 1;
+    if (wave == AB_WAVE) {
+        f32x4 ar = zero4(), ai = zero4();
+#pragma unroll 4
+        for (int k0 = 0; k0 < D; k0 += 4) {
+            const float lr = b.LB.r[li][k0 + lk], lq = b.LB.i[li][k0 + lk];
+            const float ur = b.U.r[li][k0 + lk], ui = b.U.i[li][k0 + lk];
+            ar = mma(lq, ui, mma(lr, ur, ar));     // -Ab_r = lr Ur + li Ui
+            ai = mma(-lr, ui, mma(lq, ur, ai));    // -Ab_i = li Ur - lr Ui
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * lk + i, u = li;
+            const float abr = u < t ? -ar[i] : 0.f, abi = u < t ? -ai[i] : 0.f;
+            b.Gbr[t][u] = b.beta[t] * abr;
+            b.Gbi[t][u] = b.beta[t] * abi;
+            b.dbA[t][u] = abr * b.Gr[t][u] + abi * b.Gi[t][u];   // Re(conj(Ab) G)
+        }
+    }
+    if (wave == PB_WAVE) {
+        f32x4 pr = zero4(), pi = zero4();
+#pragma unroll 4
+        for (int k0 = 0; k0 < D; k0 += 4) {
+            const float o = b.dO[li][k0 + lk];
+            pr = mma(o, b.U.r[li][k0 + lk], pr);     // Pb_r = dO Ur
+            pi = mma(-o, b.U.i[li][k0 + lk], pi);    // Pb_i = -dO Ui
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * lk + i, u = li;
+            b.Hbr[t][u] = u <= t ? pr[i] : 0.f;
+            b.Hbi[t][u] = u <= t ? pi[i] : 0.f;
+        }
+    }
+    {   // gl: channel c, rows w of this thread's part (partials over the parts in (e))
+        constexpr int NP = NTH / D, WP = D / NP > 0 ? D / NP : 1;
+        const int c = tid % D, part = tid / D;
         cf acc = {0.f, 0.f};
+        if (part * WP < D) {
 #pragma unroll 4
-        for (int w = 0; w < D; ++w) acc = cadd(acc, cmulc({b.S1r[w][c], b.S1i[w][c]}, {b.S0r[w][c], b.S0i[w][c]}));
-        const cf EL = cexp_(b.gr[L][c], b.gi[L][c]);
-        const cf gl = cmulc(acc, EL);
-        b.glr[c] = gl.r;
-        b.gli[c] = gl.i;
+            for (int w = part * WP; w < part * WP + WP; ++w)
+                acc = cadd(acc, cmulc({S1r[w][c], S1i[w][c]}, {S0r[w][c], S0i[w][c]}));
+        }
+        b.glp[2 * part][c] = acc.r;
+        b.glp[2 * part + 1][c] = acc.i;
     }
     __syncthreads();
-    // (d) elements (t, c): the scaled tiles' cotangents from sums over the rows v, the
-    //     pairwise G / H terms; dq, dk; gam's cotangent, stored over (K E) at the same
-    //     element (each element of K E is read here only by the thread that replaces it)
+    // S0 and dS1 are dead: the sums go over them, [t][c] each
+    float(*Kgr)[D + 1] = b.SS, (*Kgi)[D + 1] = b.SS + kC, (*Qgr)[D + 1] = b.SS + 2 * kC;
+    float(*Qgi)[D + 1] = b.SS + 3 * kC, (*Kdr)[D + 1] = b.SS + 4 * kC, (*Kdi)[D + 1] = b.SS + 5 * kC;
+
+    if (item >= 0 && item < NTL) {
+        const int n0 = item * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * lk + i, c = n0 + li;
+            Kgr[t][c] = -res[0][i];
+            Kgi[t][c] = -res[1][i];
+            Qgr[t][c] = res[2][i];
+            Qgi[t][c] = res[3][i];
+        }
+    } else if (item >= NTL) {
+        const int n0 = (item - NTL) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Kdr[4 * lk + i][n0 + li] = res[0][i];
+            Kdi[4 * lk + i][n0 + li] = res[1][i];
+        }
+    }
+    __syncthreads();
+    // (d) elements (t, c): the scaled tiles' cotangents, the pairwise G / H terms; dq, dk;
+    //     gam's cotangent, stored over K E (R since (b); dead).  Each pair's factor is
+    //     formed by both of its elements (as row and as column): accumulating the column
+    //     terms once per pair through LDS atomics instead measured 1.9x slower.
     constexpr int TS = NTH / D;                         // threads sharing a channel
     constexpr int NRD = TS < kC ? kC / TS : 1;          // their rows t = tid / D + TS r
     {
         const int c = tid % D, tg = tid / D;
         cf kdsum = {0.f, 0.f};
-        // the three sums over the rows v for all of the thread's steps at once: each
-        // S0 / dS1 element is read once for them
-        cf Kgs[NRD], Qgs[NRD], Kds[NRD];
-#pragma unroll
-        for (int r = 0; r < NRD; ++r) Kgs[r] = Qgs[r] = Kds[r] = {0.f, 0.f};
-        if (tg < kC) {
-#pragma unroll 4
-            for (int w = 0; w < D; ++w) {
-                const cf S = {b.S0r[w][c], b.S0i[w][c]}, S1 = {b.S1r[w][c], b.S1i[w][c]};
-#pragma unroll
-                for (int r = 0; r < NRD; ++r) {
-                    const int t = tg + TS * r;
-                    Kgs[r] = csub(Kgs[r], cmulc(b.LB.get(t, w), S));
-                    Qgs[r] = cadd(Qgs[r], cmulc({b.dO[t][w], 0.f}, S));
-                    Kds[r] = cadd(Kds[r], cmulc(S1, b.U.get(t, w)));
-                }
-            }
-        }
 #pragma unroll
         for (int r = 0; r < NRD; ++r) {
             const int t = tg + TS * r;
             if (t >= kC) break;
-            const cf Kgb = cscale(Kgs[r], b.beta[t]), Qgb = Qgs[r], Kdb = Kds[r];
+            const cf Kgb = cscale({Kgr[t][c], Kgi[t][c]}, b.beta[t]), Qgb = {Qgr[t][c], Qgi[t][c]};
+            const cf Kdb = {Kdr[t][c], Kdi[t][c]};
             const cf E = cexp_(b.gr[t][c], b.gi[t][c]);
             const cf Ed = cexp_(b.gr[L][c] - b.gr[t][c], b.gi[L][c] - b.gi[t][c]);
             const float kt = b.K[t][c], qt = b.Q[t][c];
@@ -718,9 +796,9 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
             // pairs with t as the row (u <= t) and as the column (u >= t)
 #pragma unroll 4
             for (int u = 0; u < kC; ++u) {
-                const int r = u <= t ? t : u, cl = u <= t ? u : t;   // the pair (row, column)
-                const cf f = cexp_(b.gr[r][c] - b.gr[cl][c], b.gi[r][c] - b.gi[cl][c]);
-                const cf Gb = {b.Gbr[r][cl], b.Gbi[r][cl]}, Hb = {b.Hbr[r][cl], b.Hbi[r][cl]};
+                const int r2 = u <= t ? t : u, cl = u <= t ? u : t;   // the pair (row, column)
+                const cf f = cexp_(b.gr[r2][c] - b.gr[cl][c], b.gi[r2][c] - b.gi[cl][c]);
+                const cf Gb = {b.Gbr[r2][cl], b.Gbi[r2][cl]}, Hb = {b.Hbr[r2][cl], b.Hbi[r2][cl]};
                 if (u <= t) {   // t is the row: G_tu, H_tu
                     const float ku = b.K[u][c];
                     const cf wg = cscale(f, ku);   // dG_tu / dk_tc
@@ -751,7 +829,10 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
     float (*dgs)[D + 1] = b.U.r;
     if (tid < D) {
         const int c = tid;
-        float lr = b.glr[c], li = b.gli[c];
+        cf acc = {0.f, 0.f};
+        for (int g2 = 0; g2 < NTH / D; ++g2) acc = cadd(acc, {b.glp[2 * g2][c], b.glp[2 * g2 + 1][c]});
+        const cf gl = cmulc(acc, cexp_(b.gr[L][c], b.gi[L][c]));   // sum_w dS1 conj(S0 E_L)
+        float lr = gl.r, li = gl.i;
         for (int g2 = 0; g2 < TS; ++g2) {
             lr += b.red[2 * g2][c];
             li += b.red[2 * g2 + 1][c];
@@ -765,17 +846,15 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
             dgs[t][c] = ar;
         }
     }
-    // dbeta_t = Re sum_v conj(lambda_tv) (V - X)_tv + sum_u Re(conj(Ab_tu) G_tu)
-    if (tid >= NTH - kC) {
-        const int t = tid - (NTH - kC);
-        if (t < valid) {
-            float acc = 0.f;
-#pragma unroll 4
-            for (int w = 0; w < D; ++w)
-                acc += b.LB.r[t][w] * (b.V[t][w] - b.X.r[t][w]) - b.LB.i[t][w] * b.X.i[t][w];
-            for (int u = 0; u < t; ++u) acc += b.dbA[t][u];
-            p.dbeta[row0 + t] = acc;
-        }
+    // dbeta_t = Re sum_v conj(lambda_tv) (V - X)_tv + sum_u Re(conj(Ab_tu) G_tu): step t
+    // by the 16 lanes of one DPP row of the last 256 threads
+    if (tid >= NTH - kCC) {
+        const int t = (tid - (NTH - kCC)) / 16, j = tid % 16;
+        float acc = j < t ? b.dbA[t][j] : 0.f;
+        for (int w = j; w < D; w += 16)
+            acc += b.LB.r[t][w] * (b.V[t][w] - b.X.r[t][w]) - b.LB.i[t][w] * b.X.i[t][w];
+        acc = group_sum<16>(acc);
+        if (j == 0 && t < valid) p.dbeta[row0 + t] = acc;
     }
     if (GATE == kGateScalar) {
         __syncthreads();
