@@ -34,6 +34,23 @@ def rel_err(x, ref):
     return num / den if den > 0 else num
 
 
+def rel_err_heads(x, ref, floor_frac=1e-2):
+    """Worst over the (b, h) heads of max |x - ref| / max |ref| within the head, so a
+    local error in a low-magnitude head is not hidden under another head's maximum
+    (a head's maximum is floored at floor_frac of the largest head's, so a head that
+    is zero up to rounding does not divide by its own noise)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.ndim < 3 or ref.size == 0:
+        return rel_err(x, ref)
+    nh = ref.shape[0] * ref.shape[1]
+    d = np.abs(x - ref).reshape(nh, -1).max(axis=1)
+    m = np.abs(ref).reshape(nh, -1).max(axis=1)
+    if m.max() == 0:
+        return float(d.max())
+    return float((d / np.maximum(m, floor_frac * m.max())).max())
+
+
 def gpu_run(w: W.Workload, inp: dict, policy: str | None = None, dhT=True):
     """fwd + bwd on the GPU through the C ABI (with the Kaczmarz flag when the
     workload has one: inp["beta"] is then eta).  Returns a dict of CPU tensors."""
@@ -80,15 +97,21 @@ def select(t, heads):
 
 
 def compare(gpu: dict, ref: dict, tol: float, heads=None, label=""):
-    errs = {}
+    """Every output within ``tol`` of the oracle, normalised over the whole tensor and
+    per head (rel_err_heads)."""
+    errs, herrs = {}, {}
     for n in OUTPUTS:
         if ref.get(n) is None:
             assert gpu.get(n) is None, n
             continue
         x = select(gpu[n], heads)
         assert torch.isfinite(x.float()).all(), f"{label} {n} has non-finite values"
-        errs[n] = rel_err(x.to(torch.float64).numpy(), ref[n])
+        xn = x.to(torch.float64).numpy()
+        errs[n] = rel_err(xn, ref[n])
+        herrs[n] = rel_err_heads(xn, ref[n])
     say(f"{label} errors: " + ", ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    say(f"{label} worst head: " + ", ".join(f"{n}={e:.2e}" for n, e in herrs.items()))
     bad = {n: e for n, e in errs.items() if not e <= tol}
+    bad.update({f"{n} (per head)": e for n, e in herrs.items() if not e <= tol})
     assert not bad, f"{label} over tolerance {tol}: {bad}"
     return errs

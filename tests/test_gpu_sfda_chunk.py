@@ -13,7 +13,7 @@ import torch
 from oracle import sfda
 from delta_rule_linear_gated_amd import binding as B
 from delta_rule_linear_gated_amd import workloads as W
-from helpers import TOL, rel_err, say
+from helpers import TOL, rel_err, rel_err_heads, say
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,7 @@ def _compare(gpu, ref, tol, label):
             continue
         assert np.isfinite(gpu[n]).all(), f"{label} {n} not finite"
         errs[n] = rel_err(gpu[n], ref[n])
+        errs[n + " (per head)"] = rel_err_heads(gpu[n], ref[n])
     say(f"{label} errors: " + ", ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     bad = {n: e for n, e in errs.items() if not e <= tol}
     assert not bad, f"{label} over tolerance {tol}: {bad}"
