@@ -253,26 +253,33 @@ template <typename TI, int GATE, int D> struct SeqIn {
     }
 };
 
-// LDS of the sequential kernels: the gated tiles (rows of D: lane j of a row
-// reads D / 16 consecutive channels, the tiles are written a row at a time),
-// the block tile, T, P, beta and the rows' per-step vectors.
-template <int D> struct SeqLds {
-    float kgr[kC][D], kgi[kC][D];   // K E
-    float qgr[kC][D], qgi[kC][D];   // Q E
-    float kdr[kC][D], kdi[kC][D];   // K exp(gam_L - gam)
-    float elr[D], eli[D];           // E at the last row
+// LDS of the sequential kernels (matrix-core form).  Tiles padded by 4 floats per row
+// (the fragment reads of 16 rows x 4 columns and 4 rows x 16 columns spread over
+// the banks); the state block lives here between chunks.
+template <int D> struct SeqLdsM {
+    static constexpr int LD = D + 4, LB = kBV + 4, LC = kC + 4;
+    float kgr[kC][LD], kgi[kC][LD];   // K E
+    float qgr[kC][LD], qgi[kC][LD];   // Q E
+    float kdr[kC][LD], kdi[kC][LD];   // K exp(gam_L - gam)
+    float elr[D], eli[D];             // E at the last row
     float tr[kPT / D][D], ti[kPT / D][D];
-    float B[kC][kBV + 1];           // V (forward) or dO (backward) block
-    float Tr[kC][kC + 1], Ti[kC][kC + 1], Pr[kC][kC + 1], Pi[kC][kC + 1];
+    float Sr[kBV][LD], Si[kBV][LD];   // the state block [v][c]
+    float B[kC][LB];                  // V (forward) or dO (backward) block [t][v]
+    float Tr[kC][LC], Ti[kC][LC], Pr[kC][LC], Pi[kC][LC];
     float beta[kC];
-    Rows<kBV> Ra, Rb;               // forward: R, U; backward: Ub, lambda
-    float Os[kC][kBV + 1];          // O (forward) or dv (backward) block, for the write-back
+    float Rr[kC][LB], Ri[kC][LB];     // R [t][v] (backward: Ub)
+    float Ur[kC][LB], Ui[kC][LB];     // U [t][v] (backward: lambda)
+    float Os[kC][LB];                 // O (backward: dv) block, for the write-back
 };
+
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
 
 // Commit of the staged registers (phase A of a chunk): the gate's partial sums,
 // the block tile, T, P, beta.
-template <typename TI, int GATE, int D>
-__device__ __forceinline__ void seq_commit(SeqIn<TI, GATE, D>& x, SeqLds<D>& s) {
+template <typename TI, int GATE, int D, class LDS>
+__device__ __forceinline__ void seq_commit(SeqIn<TI, GATE, D>& x, LDS& s) {
     const int tid = threadIdx.x;
     x.in.prefix(s.tr, s.ti);
     s.B[tid / kBV][tid % kBV] = x.blk;
@@ -285,8 +292,8 @@ __device__ __forceinline__ void seq_commit(SeqIn<TI, GATE, D>& x, SeqLds<D>& s) 
 }
 
 // Phase B: gam, then the gated tiles and E_L from the thread's own rows.
-template <typename TI, int GATE, int D>
-__device__ __forceinline__ void seq_tiles(SeqIn<TI, GATE, D>& x, SeqLds<D>& s) {
+template <typename TI, int GATE, int D, class LDS>
+__device__ __forceinline__ void seq_tiles(SeqIn<TI, GATE, D>& x, LDS& s) {
     using CI = ChunkIn<TI, GATE, D>;
     const cf gl = x.in.finish(s.tr, s.ti);
     const int c = CI::chan();
@@ -311,110 +318,154 @@ __device__ __forceinline__ void seq_tiles(SeqIn<TI, GATE, D>& x, SeqLds<D>& s) {
 }
 
 // ---------------------------------------------------------------------------
-// phase_fwd_state: one workgroup per (head, block of 16 state rows).  states
-// (if not NULL): the complex state entering each chunk, [BH][NT][2][D][D] fp32.
+// phase_fwd_state: one workgroup per (head, block of 16 state rows), on the fp32
+// matrix cores.  The state block S [16][D] stays in LDS; per chunk
+//     X = (K E) S^T,  Yr = Re((Q E) S^T)       (16 x 16, over the D channels)
+//     R = beta (V - X),  U = T R,  O = Yr + Re(P U)
+//     S1 = S diag(E_L) + U^T (K exp(gam_L - gam))
+// each a sum of real 16x16x4 products (fragments as in the per-chunk backward).
+// states (if not NULL): the complex state entering each chunk, [BH][NT][2][D][D].
 template <typename TI, int GATE, int D>
 __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const float* __restrict__ mats,
                                                               float* __restrict__ states) {
-    constexpr int NB = D / kBV, NC = D / kC;
-    __shared__ __align__(16) SeqLds<D> s;
+    constexpr int NB = D / kBV, NTL = D / 16, NW = kPT / 64;
+    __shared__ __align__(16) SeqLdsM<D> s;
     int bh, blk;
     head_and_block(NB, p.BH, bh, blk);
-    const int tid = threadIdx.x, vl = tid / kC, j = tid % kC, c0 = j * NC, v = blk * kBV + vl;
-    float sr[NC], si[NC];   // S[v][c0 .. c0 + NC)
-    {
-        const long o0 = ((long)bh * D + v) * D + c0;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            sr[c] = p.h0 ? p.h0[o0 + c] : 0.f;
-            si[c] = p.h0_im ? p.h0_im[o0 + c] : 0.f;
-        }
+    const int tid = threadIdx.x, v0 = blk * kBV;
+    const int lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
+    for (int idx = tid; idx < kBV * D; idx += kPT) {
+        const int v = idx / D, c = idx % D;
+        const long e = ((long)bh * D + v0 + v) * D + c;
+        s.Sr[v][c] = p.h0 ? p.h0[e] : 0.f;
+        s.Si[v][c] = p.h0_im ? p.h0_im[e] : 0.f;
     }
     TI* __restrict__ out = static_cast<TI*>(p.o);
     SeqIn<TI, GATE, D> x;
-    x.load(p, p.v, mats, bh, blk * kBV, 0);
+    x.load(p, p.v, mats, bh, v0, 0);
     for (int n = 0; n < p.NT; ++n) {
         const int valid = min(kC, p.T - n * kC);
         const long row0 = (long)bh * p.T + n * kC;
         seq_commit(x, s);
-        __syncthreads();
+        __syncthreads();   // (also orders the state block written at the end of the last chunk)
         seq_tiles(x, s);
-        x.load(p, p.v, mats, bh, blk * kBV, n + 1 < p.NT ? n + 1 : n);   // the next chunk, during this one
-        __syncthreads();
-        if (states) {
-            float* st = states + (((long)bh * p.NT + n) * 2 * D + v) * D + c0;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                st[c] = sr[c];
-                st[(long)D * D + c] = si[c];
-            }
-        }
-        // X_t = (K E)_t . S_v and Y_t = (Q E)_t . S_v; lane j keeps step j
-        cf xj = {0.f, 0.f}, yj = {0.f, 0.f};
-#pragma unroll 4
-        for (int t = 0; t < kC; ++t) {
-            cf a = {0.f, 0.f}, b = {0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const cf S = {sr[c], si[c]};
-                a = cadd(a, cmul({s.kgr[t][c0 + c], s.kgi[t][c0 + c]}, S));
-                b = cadd(b, cmul({s.qgr[t][c0 + c], s.qgi[t][c0 + c]}, S));
-            }
-            a = {group_sum<kC>(a.r), group_sum<kC>(a.i)};
-            b = {group_sum<kC>(b.r), group_sum<kC>(b.i)};
-            if (t == j) {
-                xj = a;
-                yj = b;
-            }
-        }
-        // R_j = beta_j (V_j - X_j); U_j = sum_w T_jw R_w; O_j = Re(Y_j + sum_w P_jw U_w).  T and
-        // P are stored with zeros above the diagonal, so every lane runs all 16 steps (no
-        // divergent loop: the reads of a row are issued together).  A row's lanes are 16
-        // lanes of one wave: what one stores, the others read back in program order with
-        // no barrier.
-        s.Ra.set(j, vl, cscale(csub({s.B[j][vl], 0.f}, xj), s.beta[j]));
-        cf u = {0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < kC; ++w) u = cadd(u, cmul({s.Tr[j][w], s.Ti[j][w]}, s.Ra.get(w, vl)));
-        s.Rb.set(j, vl, u);
-        cf o = yj;
-#pragma unroll
-        for (int w = 0; w < kC; ++w) o = cadd(o, cmul({s.Pr[j][w], s.Pi[j][w]}, s.Rb.get(w, vl)));
-        s.Os[j][vl] = o.r;
-        // S1 = S0 diag(E_L) + U^T (K exp(gam_L - gam))
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const cf S = cmul({sr[c], si[c]}, {s.elr[c0 + c], s.eli[c0 + c]});
-            sr[c] = S.r;
-            si[c] = S.i;
-        }
-#pragma unroll 4
-        for (int t = 0; t < kC; ++t) {
-            const cf ut = s.Rb.get(t, vl);
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const cf y = cmul(ut, {s.kdr[t][c0 + c], s.kdi[t][c0 + c]});
-                sr[c] += y.r;
-                si[c] += y.i;
+        x.load(p, p.v, mats, bh, v0, n + 1 < p.NT ? n + 1 : n);   // the next chunk, during this one
+        if (states) {   // the state entering this chunk
+            float* st = states + ((long)bh * p.NT + n) * 2 * D * D;
+            for (int idx = tid; idx < kBV * D; idx += kPT) {
+                const int v = idx / D, c = idx % D;
+                st[(long)(v0 + v) * D + c] = s.Sr[v][c];
+                st[(long)D * D + (long)(v0 + v) * D + c] = s.Si[v][c];
             }
         }
         __syncthreads();
+        // X and Yr: items Xr, Xi, Yr; R = beta (V - X) from the X items
+        f32x4 yr = zero4();
+        for (int it = wave; it < 3; it += NW) {
+            f32x4 acc = zero4();
+            const float(*ar)[SeqLdsM<D>::LD] = it < 2 ? s.kgr : s.qgr;
+            const float(*ai)[SeqLdsM<D>::LD] = it < 2 ? s.kgi : s.qgi;
+#pragma unroll 4
+            for (int k0 = 0; k0 < D; k0 += 4) {
+                const float a_r = ar[li][k0 + lk], a_i = ai[li][k0 + lk];
+                const float sr = s.Sr[li][k0 + lk], si = s.Si[li][k0 + lk];
+                if (it == 1) acc = mma4(a_i, sr, mma4(a_r, si, acc));   // Xi = Ar Si^T + Ai Sr^T
+                else acc = mma4(-a_i, si, mma4(a_r, sr, acc));          // Xr, Yr = Ar Sr^T - Ai Si^T
+            }
+            // acc[i] = (t = 4 lk + i, v = li)
+            if (it == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 4 * lk + i;
+                    s.Rr[t][li] = s.beta[t] * (s.B[t][li] - acc[i]);
+                }
+            } else if (it == 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s.Ri[4 * lk + i][li] = -s.beta[4 * lk + i] * acc[i];
+            } else {
+                yr = acc;
+            }
+        }
+        __syncthreads();
+        // U = T R: items Ur, Ui
+        for (int it = wave; it < 2; it += NW) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < kC; k0 += 4) {
+                const float tr = s.Tr[li][k0 + lk], ti = s.Ti[li][k0 + lk];
+                const float rr = s.Rr[k0 + lk][li], ri = s.Ri[k0 + lk][li];
+                if (it) acc = mma4(ti, rr, mma4(tr, ri, acc));   // Ui = Tr Ri + Ti Rr
+                else acc = mma4(-ti, ri, mma4(tr, rr, acc));     // Ur = Tr Rr - Ti Ri
+            }
+            float(*uo)[SeqLdsM<D>::LB] = it ? s.Ui : s.Ur;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) uo[4 * lk + i][li] = acc[i];
+        }
+        __syncthreads();
+        // O = Yr + Pr Ur - Pi Ui (the wave that holds Yr)
+        if (wave == 2 % NW) {
+            f32x4 acc = yr;
+#pragma unroll
+            for (int k0 = 0; k0 < kC; k0 += 4) {
+                const float pr = s.Pr[li][k0 + lk], pi = s.Pi[li][k0 + lk];
+                acc = mma4(-pi, s.Ui[k0 + lk][li], mma4(pr, s.Ur[k0 + lk][li], acc));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s.Os[4 * lk + i][li] = acc[i];
+        }
+        // S1 = S diag(E_L) + U^T Kd: items (column tile of c, real or imaginary part),
+        // held until every item has read S
+        constexpr int NI = (2 * NTL + NW - 1) / NW;
+        f32x4 s1[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int it = wave + j * NW;
+            s1[j] = zero4();
+            if (it >= 2 * NTL) continue;
+            const int n0 = (it >> 1) * 16, c = n0 + li;
+            const float er = s.elr[c], ei = s.eli[c];
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sr = s.Sr[4 * lk + i][c], si = s.Si[4 * lk + i][c];
+                acc[i] = (it & 1) ? sr * ei + si * er : sr * er - si * ei;
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < kC; k0 += 4) {
+                const float ur = s.Ur[k0 + lk][li], ui = s.Ui[k0 + lk][li];   // A = U^T [v][t]
+                const float kr = s.kdr[k0 + lk][c], ki = s.kdi[k0 + lk][c];     // B = Kd [t][c]
+                if (it & 1) acc = mma4(ui, kr, mma4(ur, ki, acc));   // + Ur Kdi + Ui Kdr
+                else acc = mma4(-ui, ki, mma4(ur, kr, acc));         // + Ur Kdr - Ui Kdi
+            }
+            s1[j] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int it = wave + j * NW;
+            if (it >= 2 * NTL) continue;
+            float(*so)[SeqLdsM<D>::LD] = (it & 1) ? s.Si : s.Sr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) so[4 * lk + i][(it >> 1) * 16 + li] = s1[j][i];
+        }
         {
             const int t = tid / kBV, vv = tid % kBV;
-            if (t < valid) out[(row0 + t) * D + blk * kBV + vv] = from_f<TI>(s.Os[t][vv]);
+            if (t < valid) out[(row0 + t) * D + v0 + vv] = from_f<TI>(s.Os[t][vv]);
         }
     }
-    const long o0 = ((long)bh * D + v) * D + c0;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        if (p.hT) p.hT[o0 + c] = sr[c];
-        if (p.hT_im) p.hT_im[o0 + c] = si[c];
+    __syncthreads();
+    for (int idx = tid; idx < kBV * D; idx += kPT) {
+        const int v = idx / D, c = idx % D;
+        const long e = ((long)bh * D + v0 + v) * D + c;
+        if (p.hT) p.hT[e] = s.Sr[v][c];
+        if (p.hT_im) p.hT_im[e] = s.Si[v][c];
     }
 }
 
 // ---------------------------------------------------------------------------
 // phase_bwd_state: one workgroup per (head, block of 16 rows of the state
-// cotangent), chunks last to first.  Per chunk, with dS1 the cotangent leaving it:
+// cotangent), chunks last to first, on the fp32 matrix cores (the block dS [16][D]
+// in LDS).  Per chunk, with dS1 the cotangent leaving it:
 //     Ub = conj(Kd) dS1^T + P^H dO,   lambda = T^H Ub,   dv = Re(diag(beta) lambda)
 //     dS0 = dS1 diag(conj(E_L)) + dO^T conj(Q E) - (diag(beta) lambda)^T conj(K E)
 // Out per chunk: lambda [BH][NT][2][D][C] (row v, then step) and dS1
@@ -422,95 +473,129 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
 template <typename TI, int GATE, int D>
 __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const float* __restrict__ mats,
                                                               float* __restrict__ lam, float* __restrict__ dS1) {
-    constexpr int NB = D / kBV, NC = D / kC;
-    __shared__ __align__(16) SeqLds<D> s;
+    constexpr int NB = D / kBV, NTL = D / 16, NW = kPT / 64;
+    __shared__ __align__(16) SeqLdsM<D> s;   // Sr / Si: dS; Rr / Ri: Ub; Ur / Ui: lambda
     int bh, blk;
     head_and_block(NB, p.BH, bh, blk);
-    const int tid = threadIdx.x, vl = tid / kC, j = tid % kC, c0 = j * NC, v = blk * kBV + vl;
-    float br[NC], bi[NC];   // dS[v][c0 .. c0 + NC)
-    {
-        const long o0 = ((long)bh * D + v) * D + c0;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            br[c] = p.dhT ? p.dhT[o0 + c] : 0.f;
-            bi[c] = p.dhT_im ? p.dhT_im[o0 + c] : 0.f;
-        }
+    const int tid = threadIdx.x, v0 = blk * kBV;
+    const int lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
+    for (int idx = tid; idx < kBV * D; idx += kPT) {
+        const int v = idx / D, c = idx % D;
+        const long e = ((long)bh * D + v0 + v) * D + c;
+        s.Sr[v][c] = p.dhT ? p.dhT[e] : 0.f;
+        s.Si[v][c] = p.dhT_im ? p.dhT_im[e] : 0.f;
     }
     TI* __restrict__ dvp = static_cast<TI*>(p.dv);
     SeqIn<TI, GATE, D> x;
-    x.load(p, p.dout, mats, bh, blk * kBV, p.NT - 1);
+    x.load(p, p.dout, mats, bh, v0, p.NT - 1);
     for (int n = p.NT - 1; n >= 0; --n) {
         const int valid = min(kC, p.T - n * kC);
         const long row0 = (long)bh * p.T + n * kC;
         const long chunk = (long)bh * p.NT + n;
-        seq_commit(x, s);
+        seq_commit(x, s);   // B: the dO block
         __syncthreads();
         seq_tiles(x, s);
-        x.load(p, p.dout, mats, bh, blk * kBV, n > 0 ? n - 1 : n);   // the previous chunk, during this one
-        __syncthreads();
-        {
-            float* d1 = dS1 + (chunk * 2 * D + v) * D + c0;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                d1[c] = br[c];
-                d1[(long)D * D + c] = bi[c];
-            }
-        }
-        // Ub_t = sum_c conj(Kd_tc) dS_vc (lane j keeps step j) + sum_{w >= j} conj(P_wj) dO_wv
-        cf ub = {0.f, 0.f};
-#pragma unroll 4
-        for (int t = 0; t < kC; ++t) {
-            cf a = {0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) a = cadd(a, cmulc({br[c], bi[c]}, {s.kdr[t][c0 + c], s.kdi[t][c0 + c]}));
-            a = {group_sum<kC>(a.r), group_sum<kC>(a.i)};
-            if (t == j) ub = a;
-        }
-        // (T and P are zero above the diagonal: all 16 steps, no divergent loop)
-#pragma unroll
-        for (int w = 0; w < kC; ++w) ub = cadd(ub, cscale({s.Pr[w][j], -s.Pi[w][j]}, s.B[w][vl]));
-        s.Ra.set(j, vl, ub);
-        // lambda_j = sum_w conj(T_wj) Ub_w (the row's lanes: one wave, program order)
-        cf lm = {0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < kC; ++w) lm = cadd(lm, cmul({s.Tr[w][j], -s.Ti[w][j]}, s.Ra.get(w, vl)));
-        s.Rb.set(j, vl, lm);
-        {
-            float* lp = lam + (chunk * 2 * D + v) * kC + j;
-            lp[0] = lm.r;
-            lp[(long)D * kC] = lm.i;
-        }
-        s.Os[j][vl] = s.beta[j] * lm.r;
-        // dS0, step by step over the lane's channels
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const cf y = cmulc({br[c], bi[c]}, {s.elr[c0 + c], s.eli[c0 + c]});
-            br[c] = y.r;
-            bi[c] = y.i;
-        }
-#pragma unroll 4
-        for (int t = 0; t < kC; ++t) {
-            const float o = s.B[t][vl];
-            const cf l = cscale(s.Rb.get(t, vl), s.beta[t]);
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int cc = c0 + c;
-                const cf y = csub(cscale({s.qgr[t][cc], -s.qgi[t][cc]}, o), cmulc(l, {s.kgr[t][cc], s.kgi[t][cc]}));
-                br[c] += y.r;
-                bi[c] += y.i;
+        x.load(p, p.dout, mats, bh, v0, n > 0 ? n - 1 : n);   // the previous chunk, during this one
+        {   // the cotangent leaving this chunk
+            float* d1 = dS1 + chunk * 2 * D * D;
+            for (int idx = tid; idx < kBV * D; idx += kPT) {
+                const int v = idx / D, c = idx % D;
+                d1[(long)(v0 + v) * D + c] = s.Sr[v][c];
+                d1[(long)D * D + (long)(v0 + v) * D + c] = s.Si[v][c];
             }
         }
         __syncthreads();
+        // Ub = conj(Kd) dS^T + P^H dO: items Ub re, Ub im
+        for (int it = wave; it < 2; it += NW) {
+            f32x4 acc = zero4();
+#pragma unroll 4
+            for (int k0 = 0; k0 < D; k0 += 4) {
+                const float kr = s.kdr[li][k0 + lk], ki = s.kdi[li][k0 + lk];
+                const float sr = s.Sr[li][k0 + lk], si = s.Si[li][k0 + lk];
+                if (it) acc = mma4(-ki, sr, mma4(kr, si, acc));   // Kdr dSi - Kdi dSr
+                else acc = mma4(ki, si, mma4(kr, sr, acc));       // Kdr dSr + Kdi dSi
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < kC; k0 += 4) {   // A = P^T [t][w], B = dO [w][v]
+                const float o = s.B[k0 + lk][li];
+                acc = it ? mma4(-s.Pi[k0 + lk][li], o, acc) : mma4(s.Pr[k0 + lk][li], o, acc);
+            }
+            float(*uo)[SeqLdsM<D>::LB] = it ? s.Ri : s.Rr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) uo[4 * lk + i][li] = acc[i];
+        }
+        __syncthreads();
+        // lambda = T^H Ub: items re, im; dv = beta Re(lambda); lambda out
+        for (int it = wave; it < 2; it += NW) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < kC; k0 += 4) {   // A = T^T [t][w] (conjugated), B = Ub [w][v]
+                const float tr = s.Tr[k0 + lk][li], ti = s.Ti[k0 + lk][li];
+                const float ur = s.Rr[k0 + lk][li], ui = s.Ri[k0 + lk][li];
+                if (it) acc = mma4(-ti, ur, mma4(tr, ui, acc));   // Tr Ubi - Ti Ubr
+                else acc = mma4(ti, ui, mma4(tr, ur, acc));       // Tr Ubr + Ti Ubi
+            }
+            float(*lo)[SeqLdsM<D>::LB] = it ? s.Ui : s.Ur;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lo[4 * lk + i][li] = acc[i];
+            // lambda [v][t]: this lane's 4 steps of row v are consecutive
+            float* lp = lam + (chunk * 2 * D + v0 + li) * kC + 4 * lk + (it ? (long)D * kC : 0);
+            *reinterpret_cast<f32x4*>(lp) = acc;
+            if (!it) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s.Os[4 * lk + i][li] = s.beta[4 * lk + i] * acc[i];
+            }
+        }
+        __syncthreads();
+        // dS0 = dS diag(conj(E_L)) + dO^T conj(Q E) - (beta lambda)^T conj(K E): items
+        // (column tile of c, real or imaginary part), held until every item has read dS
+        constexpr int NI = (2 * NTL + NW - 1) / NW;
+        f32x4 s1[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int it = wave + j * NW;
+            s1[j] = zero4();
+            if (it >= 2 * NTL) continue;
+            const int c = (it >> 1) * 16 + li;
+            const float er = s.elr[c], ei = s.eli[c];
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sr = s.Sr[4 * lk + i][c], si = s.Si[4 * lk + i][c];
+                acc[i] = (it & 1) ? si * er - sr * ei : sr * er + si * ei;
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < kC; k0 += 4) {
+                const int t = k0 + lk;
+                const float o = s.B[t][li];                                  // A = dO^T [v][t]
+                const float lr = s.beta[t] * s.Ur[t][li], lq = s.beta[t] * s.Ui[t][li];   // (beta lambda)^T
+                if (it & 1)   // - dO QEi - (bli KEr - blr KEi)
+                    acc = mma4(lr, s.kgi[t][c], mma4(-lq, s.kgr[t][c], mma4(-o, s.qgi[t][c], acc)));
+                else          // + dO QEr - (blr KEr + bli KEi)
+                    acc = mma4(-lq, s.kgi[t][c], mma4(-lr, s.kgr[t][c], mma4(o, s.qgr[t][c], acc)));
+            }
+            s1[j] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int it = wave + j * NW;
+            if (it >= 2 * NTL) continue;
+            float(*so)[SeqLdsM<D>::LD] = (it & 1) ? s.Si : s.Sr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) so[4 * lk + i][(it >> 1) * 16 + li] = s1[j][i];
+        }
         {
             const int t = tid / kBV, vv = tid % kBV;
-            if (t < valid) dvp[(row0 + t) * D + blk * kBV + vv] = from_f<TI>(s.Os[t][vv]);
+            if (t < valid) dvp[(row0 + t) * D + v0 + vv] = from_f<TI>(s.Os[t][vv]);
         }
     }
-    const long o0 = ((long)bh * D + v) * D + c0;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        if (p.dh0) p.dh0[o0 + c] = br[c];
-        if (p.dh0_im) p.dh0_im[o0 + c] = bi[c];
+    __syncthreads();
+    for (int idx = tid; idx < kBV * D; idx += kPT) {
+        const int v = idx / D, c = idx % D;
+        const long e = ((long)bh * D + v0 + v) * D + c;
+        if (p.dh0) p.dh0[e] = s.Sr[v][c];
+        if (p.dh0_im) p.dh0_im[e] = s.Si[v][c];
     }
 }
 
