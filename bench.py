@@ -586,7 +586,7 @@ def phase_chunk_bench(args, w0):
         "bwd_ms": round(bms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"phase-controlled gate, chunks of 16: gate={w.gate} B={w.B} H={w.H} T={w.T} d={d}, "
-                               f"fp32 arithmetic on the vector ALUs", "global_batch": w.B,
+                               f"fp32 arithmetic (fp32 matrix cores and vector ALUs)", "global_batch": w.B,
                    "seq_len": w.T, "heads": w.H, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "kernels": per_kernel,
         "step_hbm": {"algorithmic_bytes": int(by), "achieved_gbs": round(by / (ms / 1e3) / 1e9, 1),

@@ -276,6 +276,47 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+// Fragment of a 16 x K operand for K step j: row l % 16, column 4 j + l / 16 of a
+// [16][K] tile (T = false) or of the transposed [K][16] one (T = true), row stride L.
+template <int L, bool T> __device__ __forceinline__ float frag(const float* p, int j) {
+    const int l = threadIdx.x & 63, li = l & 15, k = 4 * j + (l >> 4);
+    return T ? p[k * L + li] : p[li * L + k];
+}
+
+// acc + s1 sum_k A1[m][k] B1[n][k] + s2 sum_k A2[m][k] B2[n][k] for one 16 x 16 tile,
+// K a multiple of 4 (operands at the tile's first row; LA / LB row strides; TA / TB:
+// stored transposed).  Fully unrolled, operands chosen before the loop, so the fragment
+// reads are issued ahead of the products.
+template <int K, int LA, int LB, bool TA, bool TB>
+__device__ __forceinline__ f32x4 mma_pair(f32x4 acc, const float* A1, const float* B1, float s1, const float* A2,
+                                          const float* B2, float s2) {
+    float a1[K / 4], b1[K / 4], a2[K / 4], b2[K / 4];
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j) {
+        a1[j] = frag<LA, TA>(A1, j);
+        a2[j] = frag<LA, TA>(A2, j);
+        b1[j] = frag<LB, TB>(B1, j);
+        b2[j] = frag<LB, TB>(B2, j);
+    }
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j) acc = mma4(s2 * a2[j], b2[j], mma4(s1 * a1[j], b1[j], acc));
+    return acc;
+}
+
+// acc + s1 sum_k A1[m][k] B1[n][k] (as mma_pair, one product).
+template <int K, int LA, int LB, bool TA, bool TB>
+__device__ __forceinline__ f32x4 mma_one(f32x4 acc, const float* A1, const float* B1, float s1) {
+    float a1[K / 4], b1[K / 4];
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j) {
+        a1[j] = frag<LA, TA>(A1, j);
+        b1[j] = frag<LB, TB>(B1, j);
+    }
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j) acc = mma4(s1 * a1[j], b1[j], acc);
+    return acc;
+}
+
 // Commit of the staged registers (phase A of a chunk): the gate's partial sums,
 // the block tile, T, P, beta.
 template <typename TI, int GATE, int D, class LDS>
@@ -362,16 +403,13 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
         // X and Yr: items Xr, Xi, Yr; R = beta (V - X) from the X items
         f32x4 yr = zero4();
         for (int it = wave; it < 3; it += NW) {
-            f32x4 acc = zero4();
-            const float(*ar)[SeqLdsM<D>::LD] = it < 2 ? s.kgr : s.qgr;
-            const float(*ai)[SeqLdsM<D>::LD] = it < 2 ? s.kgi : s.qgi;
-#pragma unroll 4
-            for (int k0 = 0; k0 < D; k0 += 4) {
-                const float a_r = ar[li][k0 + lk], a_i = ai[li][k0 + lk];
-                const float sr = s.Sr[li][k0 + lk], si = s.Si[li][k0 + lk];
-                if (it == 1) acc = mma4(a_i, sr, mma4(a_r, si, acc));   // Xi = Ar Si^T + Ai Sr^T
-                else acc = mma4(-a_i, si, mma4(a_r, sr, acc));          // Xr, Yr = Ar Sr^T - Ai Si^T
-            }
+            // Xr, Yr = Ar Sr^T - Ai Si^T; Xi = Ar Si^T + Ai Sr^T
+            constexpr int LD = SeqLdsM<D>::LD;
+            const float* ar = it < 2 ? &s.kgr[0][0] : &s.qgr[0][0];
+            const float* ai = it < 2 ? &s.kgi[0][0] : &s.qgi[0][0];
+            const float* b1 = it == 1 ? &s.Si[0][0] : &s.Sr[0][0];
+            const float* b2 = it == 1 ? &s.Sr[0][0] : &s.Si[0][0];
+            const f32x4 acc = mma_pair<D, LD, LD, false, false>(zero4(), ar, b1, 1.f, ai, b2, it == 1 ? 1.f : -1.f);
             // acc[i] = (t = 4 lk + i, v = li)
             if (it == 0) {
 #pragma unroll
@@ -389,14 +427,12 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
         __syncthreads();
         // U = T R: items Ur, Ui
         for (int it = wave; it < 2; it += NW) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < kC; k0 += 4) {
-                const float tr = s.Tr[li][k0 + lk], ti = s.Ti[li][k0 + lk];
-                const float rr = s.Rr[k0 + lk][li], ri = s.Ri[k0 + lk][li];
-                if (it) acc = mma4(ti, rr, mma4(tr, ri, acc));   // Ui = Tr Ri + Ti Rr
-                else acc = mma4(-ti, ri, mma4(tr, rr, acc));     // Ur = Tr Rr - Ti Ri
-            }
+            // Ur = Tr Rr - Ti Ri, Ui = Tr Ri + Ti Rr (R stored [w][v])
+            constexpr int LC = SeqLdsM<D>::LC, LBv = SeqLdsM<D>::LB;
+            const float* b1 = it ? &s.Ri[0][0] : &s.Rr[0][0];
+            const float* b2 = it ? &s.Rr[0][0] : &s.Ri[0][0];
+            const f32x4 acc = mma_pair<kC, LC, LBv, false, true>(zero4(), &s.Tr[0][0], b1, 1.f, &s.Ti[0][0], b2,
+                                                                  it ? 1.f : -1.f);
             float(*uo)[SeqLdsM<D>::LB] = it ? s.Ui : s.Ur;
 #pragma unroll
             for (int i = 0; i < 4; ++i) uo[4 * lk + i][li] = acc[i];
@@ -404,12 +440,9 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
         __syncthreads();
         // O = Yr + Pr Ur - Pi Ui (the wave that holds Yr)
         if (wave == 2 % NW) {
-            f32x4 acc = yr;
-#pragma unroll
-            for (int k0 = 0; k0 < kC; k0 += 4) {
-                const float pr = s.Pr[li][k0 + lk], pi = s.Pi[li][k0 + lk];
-                acc = mma4(-pi, s.Ui[k0 + lk][li], mma4(pr, s.Ur[k0 + lk][li], acc));
-            }
+            constexpr int LC = SeqLdsM<D>::LC, LBv = SeqLdsM<D>::LB;
+            const f32x4 acc =
+                mma_pair<kC, LC, LBv, false, true>(yr, &s.Pr[0][0], &s.Ur[0][0], 1.f, &s.Pi[0][0], &s.Ui[0][0], -1.f);
 #pragma unroll
             for (int i = 0; i < 4; ++i) s.Os[4 * lk + i][li] = acc[i];
         }
@@ -422,7 +455,7 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
             const int it = wave + j * NW;
             s1[j] = zero4();
             if (it >= 2 * NTL) continue;
-            const int n0 = (it >> 1) * 16, c = n0 + li;
+            const int c = (it >> 1) * 16 + li;
             const float er = s.elr[c], ei = s.eli[c];
             f32x4 acc;
 #pragma unroll
@@ -430,14 +463,12 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
                 const float sr = s.Sr[4 * lk + i][c], si = s.Si[4 * lk + i][c];
                 acc[i] = (it & 1) ? sr * ei + si * er : sr * er - si * ei;
             }
-#pragma unroll
-            for (int k0 = 0; k0 < kC; k0 += 4) {
-                const float ur = s.Ur[k0 + lk][li], ui = s.Ui[k0 + lk][li];   // A = U^T [v][t]
-                const float kr = s.kdr[k0 + lk][c], ki = s.kdi[k0 + lk][c];     // B = Kd [t][c]
-                if (it & 1) acc = mma4(ui, kr, mma4(ur, ki, acc));   // + Ur Kdi + Ui Kdr
-                else acc = mma4(-ui, ki, mma4(ur, kr, acc));         // + Ur Kdr - Ui Kdi
-            }
-            s1[j] = acc;
+            // + Ur Kdr - Ui Kdi (re), + Ur Kdi + Ui Kdr (im); A = U^T [v][t], B = Kd [t][c]
+            constexpr int LD = SeqLdsM<D>::LD, LBv = SeqLdsM<D>::LB;
+            const int n0 = (it >> 1) * 16;
+            const float* b1 = (it & 1) ? &s.kdi[0][n0] : &s.kdr[0][n0];
+            const float* b2 = (it & 1) ? &s.kdr[0][n0] : &s.kdi[0][n0];
+            s1[j] = mma_pair<kC, LBv, LD, true, true>(acc, &s.Ur[0][0], b1, 1.f, &s.Ui[0][0], b2, (it & 1) ? 1.f : -1.f);
         }
         __syncthreads();
 #pragma unroll
@@ -507,19 +538,13 @@ __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const fl
         __syncthreads();
         // Ub = conj(Kd) dS^T + P^H dO: items Ub re, Ub im
         for (int it = wave; it < 2; it += NW) {
-            f32x4 acc = zero4();
-#pragma unroll 4
-            for (int k0 = 0; k0 < D; k0 += 4) {
-                const float kr = s.kdr[li][k0 + lk], ki = s.kdi[li][k0 + lk];
-                const float sr = s.Sr[li][k0 + lk], si = s.Si[li][k0 + lk];
-                if (it) acc = mma4(-ki, sr, mma4(kr, si, acc));   // Kdr dSi - Kdi dSr
-                else acc = mma4(ki, si, mma4(kr, sr, acc));       // Kdr dSr + Kdi dSi
-            }
-#pragma unroll
-            for (int k0 = 0; k0 < kC; k0 += 4) {   // A = P^T [t][w], B = dO [w][v]
-                const float o = s.B[k0 + lk][li];
-                acc = it ? mma4(-s.Pi[k0 + lk][li], o, acc) : mma4(s.Pr[k0 + lk][li], o, acc);
-            }
+            // Kdr dSr + Kdi dSi + Pr^T dO (re), Kdr dSi - Kdi dSr - Pi^T dO (im)
+            constexpr int LD = SeqLdsM<D>::LD, LC = SeqLdsM<D>::LC, LBv = SeqLdsM<D>::LB;
+            const float* b1 = it ? &s.Si[0][0] : &s.Sr[0][0];
+            const float* b2 = it ? &s.Sr[0][0] : &s.Si[0][0];
+            f32x4 acc = mma_pair<D, LD, LD, false, false>(zero4(), &s.kdr[0][0], b1, 1.f, &s.kdi[0][0], b2,
+                                                          it ? -1.f : 1.f);
+            acc = mma_one<kC, LC, LBv, true, true>(acc, it ? &s.Pi[0][0] : &s.Pr[0][0], &s.B[0][0], it ? -1.f : 1.f);
             float(*uo)[SeqLdsM<D>::LB] = it ? s.Ri : s.Rr;
 #pragma unroll
             for (int i = 0; i < 4; ++i) uo[4 * lk + i][li] = acc[i];
@@ -527,17 +552,15 @@ __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const fl
         __syncthreads();
         // lambda = T^H Ub: items re, im; dv = beta Re(lambda); lambda out
         for (int it = wave; it < 2; it += NW) {
-            f32x4 acc = zero4();
+            // Tr Ubr + Ti Ubi (re), Tr Ubi - Ti Ubr (im); A = conj(T)^T, B = Ub [w][v]
+            constexpr int LC = SeqLdsM<D>::LC, LBv = SeqLdsM<D>::LB;
+            const float* b1 = it ? &s.Ri[0][0] : &s.Rr[0][0];
+            const float* b2 = it ? &s.Rr[0][0] : &s.Ri[0][0];
+            const f32x4 acc = mma_pair<kC, LC, LBv, true, true>(zero4(), &s.Tr[0][0], b1, 1.f, &s.Ti[0][0], b2,
+                                                                 it ? -1.f : 1.f);
+            float(*lo)[SeqLdsM<D>::LB] = it ? s.Ui : s.Ur;   // beta lambda, for dS0
 #pragma unroll
-            for (int k0 = 0; k0 < kC; k0 += 4) {   // A = T^T [t][w] (conjugated), B = Ub [w][v]
-                const float tr = s.Tr[k0 + lk][li], ti = s.Ti[k0 + lk][li];
-                const float ur = s.Rr[k0 + lk][li], ui = s.Ri[k0 + lk][li];
-                if (it) acc = mma4(-ti, ur, mma4(tr, ui, acc));   // Tr Ubi - Ti Ubr
-                else acc = mma4(ti, ui, mma4(tr, ur, acc));       // Tr Ubr + Ti Ubi
-            }
-            float(*lo)[SeqLdsM<D>::LB] = it ? s.Ui : s.Ur;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lo[4 * lk + i][li] = acc[i];
+            for (int i = 0; i < 4; ++i) lo[4 * lk + i][li] = s.beta[4 * lk + i] * acc[i];
             // lambda [v][t]: this lane's 4 steps of row v are consecutive
             float* lp = lam + (chunk * 2 * D + v0 + li) * kC + 4 * lk + (it ? (long)D * kC : 0);
             *reinterpret_cast<f32x4*>(lp) = acc;
@@ -564,17 +587,14 @@ __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const fl
                 const float sr = s.Sr[4 * lk + i][c], si = s.Si[4 * lk + i][c];
                 acc[i] = (it & 1) ? si * er - sr * ei : sr * er + si * ei;
             }
-#pragma unroll
-            for (int k0 = 0; k0 < kC; k0 += 4) {
-                const int t = k0 + lk;
-                const float o = s.B[t][li];                                  // A = dO^T [v][t]
-                const float lr = s.beta[t] * s.Ur[t][li], lq = s.beta[t] * s.Ui[t][li];   // (beta lambda)^T
-                if (it & 1)   // - dO QEi - (bli KEr - blr KEi)
-                    acc = mma4(lr, s.kgi[t][c], mma4(-lq, s.kgr[t][c], mma4(-o, s.qgi[t][c], acc)));
-                else          // + dO QEr - (blr KEr + bli KEi)
-                    acc = mma4(-lq, s.kgi[t][c], mma4(-lr, s.kgr[t][c], mma4(o, s.qgr[t][c], acc)));
-            }
-            s1[j] = acc;
+            // + dO QEr - (blr KEr + bli KEi) (re), - dO QEi - (bli KEr - blr KEi) (im);
+            // A = dO^T, (beta lambda)^T [v][t]; B = QE, KE [t][c]
+            constexpr int LD = SeqLdsM<D>::LD, LBv = SeqLdsM<D>::LB;
+            const int n0 = (it >> 1) * 16;
+            const bool im = it & 1;
+            acc = mma_one<kC, LBv, LD, true, true>(acc, &s.B[0][0], im ? &s.qgi[0][n0] : &s.qgr[0][n0], im ? -1.f : 1.f);
+            s1[j] = mma_pair<kC, LBv, LD, true, true>(acc, im ? &s.Ui[0][0] : &s.Ur[0][0], &s.kgr[0][n0], -1.f,
+                                                       im ? &s.Ur[0][0] : &s.Ui[0][0], &s.kgi[0][n0], im ? 1.f : -1.f);
         }
         __syncthreads();
 #pragma unroll
@@ -715,15 +735,12 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
     // (b) X = (K E) S0^T (kept for dbeta), then R = beta (V - X) over K E (dead once X
     //     is formed) and U = T R; items (column tile of v, real or imaginary part)
     for (int it = wave; it < 2 * NTL; it += NW) {
+        // Xr = KEr S0r^T - KEi S0i^T, Xi = KEr S0i^T + KEi S0r^T
         const int n0 = (it >> 1) * 16;
-        f32x4 acc = zero4();
-#pragma unroll 4
-        for (int k0 = 0; k0 < D; k0 += 4) {
-            const float ar = b.kgr[li][k0 + lk], ai = b.kgi[li][k0 + lk];
-            const float sr = S0r[n0 + li][k0 + lk], si = S0i[n0 + li][k0 + lk];
-            if (it & 1) acc = mma(ai, sr, mma(ar, si, acc));    // Xi = KEr S0i^T + KEi S0r^T
-            else acc = mma(-ai, si, mma(ar, sr, acc));          // Xr = KEr S0r^T - KEi S0i^T
-        }
+        const float* b1 = (it & 1) ? &S0i[n0][0] : &S0r[n0][0];
+        const float* b2 = (it & 1) ? &S0r[n0][0] : &S0i[n0][0];
+        const f32x4 acc = mma_pair<D, D + 1, D + 1, false, false>(zero4(), &b.kgr[0][0], b1, 1.f, &b.kgi[0][0], b2,
+                                                                  (it & 1) ? 1.f : -1.f);
         float(*xo)[D + 1] = (it & 1) ? b.X.i : b.X.r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) xo[4 * lk + i][n0 + li] = acc[i];
@@ -736,15 +753,12 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
     }
     __syncthreads();
     for (int it = wave; it < 2 * NTL; it += NW) {
+        // Ur = Tr Rr - Ti Ri, Ui = Tr Ri + Ti Rr (R stored [w][v] over K E)
         const int n0 = (it >> 1) * 16;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < kC; k0 += 4) {
-            const float tr = b.Tr[li][k0 + lk], ti = b.Ti[li][k0 + lk];
-            const float rr = b.kgr[k0 + lk][n0 + li], ri = b.kgi[k0 + lk][n0 + li];
-            if (it & 1) acc = mma(ti, rr, mma(tr, ri, acc));    // Ui = Tr Ri + Ti Rr
-            else acc = mma(-ti, ri, mma(tr, rr, acc));          // Ur = Tr Rr - Ti Ri
-        }
+        const float* b1 = (it & 1) ? &b.kgi[0][n0] : &b.kgr[0][n0];
+        const float* b2 = (it & 1) ? &b.kgr[0][n0] : &b.kgi[0][n0];
+        const f32x4 acc = mma_pair<kC, kC + 1, D + 1, false, true>(zero4(), &b.Tr[0][0], b1, 1.f, &b.Ti[0][0], b2,
+                                                                   (it & 1) ? 1.f : -1.f);
         float(*uo)[D + 1] = (it & 1) ? b.U.i : b.U.r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) uo[4 * lk + i][n0 + li] = acc[i];
@@ -764,35 +778,42 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
     const int item = wave < 2 * NTL ? wave : -1;
     if (item >= 0 && item < NTL) {
         const int n0 = item * 16;
-#pragma unroll 4
-        for (int k0 = 0; k0 < D; k0 += 4) {
-            const float lr = b.LB.r[li][k0 + lk], lq = b.LB.i[li][k0 + lk], o = b.dO[li][k0 + lk];
-            const float sr = S0r[k0 + lk][n0 + li], si = S0i[k0 + lk][n0 + li];
-            res[0] = mma(lq, si, mma(lr, sr, res[0]));     // -Kgb_r = lr S0r + li S0i
-            res[1] = mma(-lr, si, mma(lq, sr, res[1]));    // -Kgb_i = li S0r - lr S0i
-            res[2] = mma(o, sr, res[2]);                   //  Qgb_r = dO S0r
-            res[3] = mma(-o, si, res[3]);                  //  Qgb_i = -dO S0i
+        // -Kgb_r = lr S0r + li S0i, -Kgb_i = li S0r - lr S0i, Qgb_r = dO S0r, Qgb_i = -dO S0i
+        // (A = lambda, dO [t][w]; B = S0 [w][c]); fragments of 4 K steps read ahead
+#pragma unroll
+        for (int j0 = 0; j0 < D / 4; j0 += 4) {
+            float lr[4], lq[4], o[4], sr[4], si[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lr[j] = frag<D + 1, false>(&b.LB.r[0][0], j0 + j);
+                lq[j] = frag<D + 1, false>(&b.LB.i[0][0], j0 + j);
+                o[j] = frag<D + 1, false>(&b.dO[0][0], j0 + j);
+                sr[j] = frag<D + 1, true>(&S0r[0][n0], j0 + j);
+                si[j] = frag<D + 1, true>(&S0i[0][n0], j0 + j);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                res[0] = mma(lq[j], si[j], mma(lr[j], sr[j], res[0]));
+                res[1] = mma(-lr[j], si[j], mma(lq[j], sr[j], res[1]));
+                res[2] = mma(o[j], sr[j], res[2]);
+                res[3] = mma(-o[j], si[j], res[3]);
+            }
         }
     } else if (item >= NTL) {
         const int n0 = (item - NTL) * 16;
-#pragma unroll 4
-        for (int k0 = 0; k0 < D; k0 += 4) {
-            const float ur = b.U.r[li][k0 + lk], ui = b.U.i[li][k0 + lk];
-            const float sr = S1r[k0 + lk][n0 + li], si = S1i[k0 + lk][n0 + li];
-            res[0] = mma(ui, si, mma(ur, sr, res[0]));     // Kdb_r = Ur S1r + Ui S1i
-            res[1] = mma(-ui, sr, mma(ur, si, res[1]));    // Kdb_i = Ur S1i - Ui S1r
-        }
+        // Kdb_r = Ur S1r + Ui S1i, Kdb_i = Ur S1i - Ui S1r (A = U [t][w], B = dS1 [w][c])
+        res[0] = mma_pair<D, D + 1, D + 1, false, true>(res[0], &b.U.r[0][0], &S1r[0][n0], 1.f, &b.U.i[0][0],
+                                                        &S1i[0][n0], 1.f);
+        res[1] = mma_pair<D, D + 1, D + 1, false, true>(res[1], &b.U.r[0][0], &S1i[0][n0], 1.f, &b.U.i[0][0],
+                                                        &S1r[0][n0], -1.f);
     }
     constexpr int AB_WAVE = 2 * NTL < NW ? 2 * NTL : NTL, PB_WAVE = 2 * NTL + 1 < NW ? 2 * NTL + 1 : NTL + 1;
     if (wave == AB_WAVE) {
-        f32x4 ar = zero4(), ai = zero4();
-#pragma unroll 4
-        for (int k0 = 0; k0 < D; k0 += 4) {
-            const float lr = b.LB.r[li][k0 + lk], lq = b.LB.i[li][k0 + lk];
-            const float ur = b.U.r[li][k0 + lk], ui = b.U.i[li][k0 + lk];
-            ar = mma(lq, ui, mma(lr, ur, ar));     // -Ab_r = lr Ur + li Ui
-            ai = mma(-lr, ui, mma(lq, ur, ai));    // -Ab_i = li Ur - lr Ui
-        }
+        // -Ab_r = lr Ur + li Ui, -Ab_i = li Ur - lr Ui (A = lambda [t][w], B = U [u][w])
+        const f32x4 ar = mma_pair<D, D + 1, D + 1, false, false>(zero4(), &b.LB.r[0][0], &b.U.r[0][0], 1.f,
+                                                                 &b.LB.i[0][0], &b.U.i[0][0], 1.f);
+        const f32x4 ai = mma_pair<D, D + 1, D + 1, false, false>(zero4(), &b.LB.i[0][0], &b.U.r[0][0], 1.f,
+                                                                 &b.LB.r[0][0], &b.U.i[0][0], -1.f);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * lk + i, u = li;
@@ -803,13 +824,9 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
         }
     }
     if (wave == PB_WAVE) {
-        f32x4 pr = zero4(), pi = zero4();
-#pragma unroll 4
-        for (int k0 = 0; k0 < D; k0 += 4) {
-            const float o = b.dO[li][k0 + lk];
-            pr = mma(o, b.U.r[li][k0 + lk], pr);     // Pb_r = dO Ur
-            pi = mma(-o, b.U.i[li][k0 + lk], pi);    // Pb_i = -dO Ui
-        }
+        // Pb_r = dO Ur, Pb_i = -dO Ui (A = dO [t][w], B = U [u][w])
+        const f32x4 pr = mma_one<D, D + 1, D + 1, false, false>(zero4(), &b.dO[0][0], &b.U.r[0][0], 1.f);
+        const f32x4 pi = mma_one<D, D + 1, D + 1, false, false>(zero4(), &b.dO[0][0], &b.U.i[0][0], -1.f);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * lk + i, u = li;
