@@ -70,6 +70,11 @@ def _trailing_bools(name: str) -> list:
 def kernel_key(name: str) -> str:
     """Map a rocprofv3 kernel name (demangled or mangled) to the names
     dn_profile_collect uses."""
+    for k in ("phase_prep", "phase_fwd_state", "phase_bwd_state", "phase_bwd_chunk"):
+        if k + "_kernel" in name:
+            return k
+    if "recompute_bwd_state_kernel" in name:   # the recomputed forward chains and bwd_state, one launch
+        return "fwd_state_recompute+bwd_state"
     if "prep_kernel" in name:
         return "prep"
     if "fwd_state_kernel" in name:   # <..., SAVE, OUTPUT>
