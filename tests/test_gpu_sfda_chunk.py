@@ -139,3 +139,28 @@ def test_forward_without_states_matches():
     assert b[3] is None
     for x, y in zip(a[:3], b[:3]):
         assert torch.equal(x, y)
+
+
+def _phase_sweep(n=16, seed=2027):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for case in range(n):
+        gate = rng.choice(["none", "scalar", "vector"])
+        dtype = rng.choice(["bf16", "fp32"])
+        d = rng.choice([16, 32, 64])
+        T = rng.choice([1, 15, 16, 17, 16 * 3 + 5, 16 * 9, rng.randint(1, 200)])
+        Bn, H = rng.choice([(1, 1), (1, 3), (2, 2), (3, 1)])
+        h0 = rng.choice([0.0, 0.5])
+        out.append((gate, dtype, Bn, H, T, d, h0, 3000 + case))
+    return out
+
+
+@pytest.mark.parametrize("case", _phase_sweep(), ids=lambda c: "-".join(map(str, c[:6])))
+def test_chunk_phase_random_shapes(case):
+    """Seeded random shapes: gate, I/O type, d, length (one step, around one chunk,
+    ragged, whole multiples, arbitrary), batch and heads, zero or random initial state."""
+    gate, dtype, Bn, H, T, d, h0, seed = case
+    w = W.custom(Bn, H, T, d, d, 16, gate, dtype, h0_std=h0, seed=seed, phase=True)
+    inp = W.make_inputs(w)
+    _compare(_gpu(inp), _oracle(inp), TOL[dtype], f"phase sweep {case}")
