@@ -134,7 +134,10 @@ def parse():
     ap.add_argument("--phase-chunk", action="store_true",
                     help="instead of the real gates, time the chunkwise phase-controlled gate "
                          "(dn_chunk_phase_fwd + dn_chunk_phase_bwd, chunks of 16) on the workload's batch, heads, "
-                         "length and gate at d = min(dk, 64), with phases theta = 0.5 N(0, 1)")
+                         "length and gate at d = --phase-d (default: the workload's dk), with phases "
+                         "theta = 0.5 N(0, 1)")
+    ap.add_argument("--phase-d", type=int, default=None, choices=[16, 32, 64, 128],
+                    help="with --phase-chunk: the head size (dk = dv)")
     ap.add_argument("--decode", action="store_true",
                     help="instead of fwd+bwd, time the recurrent (decode) entry point: --decode-batch "
                          "sequences with the workload's heads and dims, --decode-tokens tokens per "
@@ -503,7 +506,7 @@ def phase_chunk_bench(args, w0):
     from delta_rule_linear_gated_amd import binding as B
     from delta_rule_linear_gated_amd import workloads as W
 
-    d = min(w0.dk, 64)
+    d = args.phase_d or w0.dk
     w = W.custom(w0.B, w0.H, w0.T, d, d, 16, w0.gate, w0.dtype, h0_std=0.5, seed=w0.seed, name=f"phase_{w0.name}",
                  phase=True)
     dev = torch.device("cuda:0")

@@ -360,7 +360,7 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
 
 namespace {
 
-// Shape checks of the chunkwise phase-controlled gate (chunks of 16, d <= 64).
+// Shape checks of the chunkwise phase-controlled gate (chunks of 16, d <= 128).
 dn_status phase_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
     if (!s) return fail(DN_ERR_INVALID, "shape is NULL");
     if (s->B < 0 || s->H < 0 || s->T < 0) return fail(DN_ERR_SHAPE, "B, H, T must be >= 0");
@@ -371,7 +371,8 @@ dn_status phase_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
     if ((long long)s->B * s->H > 65535) return fail(DN_ERR_UNSUPPORTED, "B*H must be <= 65535");
     if (s->C != 16) return fail(DN_ERR_UNSUPPORTED, "the chunkwise phase gate runs chunks of 16 (C must be 16)");
     if (s->dk != s->dv) return fail(DN_ERR_UNSUPPORTED, "dk must equal dv");
-    if (s->dk != 16 && s->dk != 32 && s->dk != 64) return fail(DN_ERR_UNSUPPORTED, "dk must be 16, 32 or 64");
+    if (s->dk != 16 && s->dk != 32 && s->dk != 64 && s->dk != 128)
+        return fail(DN_ERR_UNSUPPORTED, "dk must be 16, 32, 64 or 128");
     *pr = dn::Problem{};
     pr->B = s->B;
     pr->H = s->H;

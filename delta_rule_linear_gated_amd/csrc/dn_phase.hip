@@ -286,34 +286,44 @@ template <int L, bool T> __device__ __forceinline__ float frag(const float* p, i
 // acc + s1 sum_k A1[m][k] B1[n][k] + s2 sum_k A2[m][k] B2[n][k] for one 16 x 16 tile,
 // K a multiple of 4 (operands at the tile's first row; LA / LB row strides; TA / TB:
 // stored transposed).  Fully unrolled, operands chosen before the loop, so the fragment
-// reads are issued ahead of the products.
+// reads of up to 16 K steps are issued ahead of their products.
 template <int K, int LA, int LB, bool TA, bool TB>
 __device__ __forceinline__ f32x4 mma_pair(f32x4 acc, const float* A1, const float* B1, float s1, const float* A2,
                                           const float* B2, float s2) {
-    float a1[K / 4], b1[K / 4], a2[K / 4], b2[K / 4];
+    constexpr int KB = K / 4 < 16 ? K / 4 : 16;
+    static_assert(K % 4 == 0 && (K / 4) % KB == 0, "K");
 #pragma unroll
-    for (int j = 0; j < K / 4; ++j) {
-        a1[j] = frag<LA, TA>(A1, j);
-        a2[j] = frag<LA, TA>(A2, j);
-        b1[j] = frag<LB, TB>(B1, j);
-        b2[j] = frag<LB, TB>(B2, j);
+    for (int j0 = 0; j0 < K / 4; j0 += KB) {
+        float a1[KB], b1[KB], a2[KB], b2[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            a1[j] = frag<LA, TA>(A1, j0 + j);
+            a2[j] = frag<LA, TA>(A2, j0 + j);
+            b1[j] = frag<LB, TB>(B1, j0 + j);
+            b2[j] = frag<LB, TB>(B2, j0 + j);
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j) acc = mma4(s2 * a2[j], b2[j], mma4(s1 * a1[j], b1[j], acc));
     }
-#pragma unroll
-    for (int j = 0; j < K / 4; ++j) acc = mma4(s2 * a2[j], b2[j], mma4(s1 * a1[j], b1[j], acc));
     return acc;
 }
 
 // acc + s1 sum_k A1[m][k] B1[n][k] (as mma_pair, one product).
 template <int K, int LA, int LB, bool TA, bool TB>
 __device__ __forceinline__ f32x4 mma_one(f32x4 acc, const float* A1, const float* B1, float s1) {
-    float a1[K / 4], b1[K / 4];
+    constexpr int KB = K / 4 < 16 ? K / 4 : 16;
+    static_assert(K % 4 == 0 && (K / 4) % KB == 0, "K");
 #pragma unroll
-    for (int j = 0; j < K / 4; ++j) {
-        a1[j] = frag<LA, TA>(A1, j);
-        b1[j] = frag<LB, TB>(B1, j);
+    for (int j0 = 0; j0 < K / 4; j0 += KB) {
+        float a1[KB], b1[KB];
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            a1[j] = frag<LA, TA>(A1, j0 + j);
+            b1[j] = frag<LB, TB>(B1, j0 + j);
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j) acc = mma4(s1 * a1[j], b1[j], acc);
     }
-#pragma unroll
-    for (int j = 0; j < K / 4; ++j) acc = mma4(s1 * a1[j], b1[j], acc);
     return acc;
 }
 
@@ -621,93 +631,160 @@ __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const fl
 
 // ---------------------------------------------------------------------------
 // phase_bwd_chunk: one workgroup per (chunk, head), from the chunk's entry state
-// S0, the cotangent dS1 leaving it, lambda and the forward's T, P, G:
+// S0, the cotangent dS1 leaving it, lambda and the forward's T and G:
 //     X = (K E) S0^T,  U = T diag(beta) (V - X)
+//     Kgb = -lambda conj(S0),  Qgb = dO conj(S0),  Kdb_tc = sum_w dS1_wc conj(U_tw)
 //     Ab = -strictly-lower(lambda U^H)      Pb = lower(dO U^H)
 //     dbeta = Re rowsum(conj(lambda) (V - X)) + Re rowsum(conj(Ab) G)
 // and K, Q, gam get the cotangents of the scaled tiles and of the pairwise G, H.
+// Each term is either a block of 16 columns of X and U (from 16 rows of S0) or a
+// sum over the state rows, so S0, dS1, lambda and the dO / V columns go through
+// LDS one block of 16 state rows at a time (the next block in registers during
+// the current one) and the sums stay in matrix-core accumulators across blocks:
+// the LDS does not grow with D^2 (two workgroups per CU at d = 64; d = 128 fits).
 template <int D, int NTH> struct ChunkBwdLds {
-    float K[kC][D + 1], Q[kC][D + 1], V[kC][D + 1];
-    float gr[kC][D + 1], gi[kC][D + 1];     // gam
-    float kgr[kC][D + 1], kgi[kC][D + 1];   // K E, then the cotangent of gam
-    float Gr[kC][kC + 1], Gi[kC][kC + 1], Tr[kC][kC + 1], Ti[kC][kC + 1], Pr[kC][kC + 1], Pi[kC][kC + 1];
+    static constexpr int NQ = D / 16 < 4 ? D / 16 : 4;   // channel parts of X
+    // row strides: S0 is read with its rows as the output index (X) and as the
+    // reduction index (Kgb, Qgb), dS1 only as the reduction index
+    static constexpr int L0 = D + 4, L1 = D + 16, LT = kC + 1;
+    // (the arrays of the block loop and of the pair loop first: within the first
+    // 64 KB, a ds_read reaches them by its immediate offset from one address)
+    union {
+        struct {
+            float S0r[kBV][L0], S0i[kBV][L0];   // the block's rows w of S0, [w][c]
+            float S1r[kBV][L1], S1i[kBV][L1];   // and of dS1
+            float Lr[kBV][LT], Li[kBV][LT];     // lambda [w][t]
+            float dO[kC][LT], V[kC][LT];        // the block's columns of dO and V, [t][w]
+            float Xp[2 * NQ][kC][LT];           // X by channel part (re, im) [t][v]
+            float Ur[kC][LT], Ui[kC][LT];       // U [t][v]
+        } blk;
+        float sums[6][kC][D + 1];   // after the last block: -Kgb, Qgb, Kdb (re, im) [t][c]
+    } u2;
+    float Tr[kC][LT], Ti[kC][LT];
     float beta[kC];
-    float tr[NTH / D][D], ti[NTH / D][D];
-    // the state entering the chunk (S0 re, im) and the cotangent of the state leaving
-    // it (dS1 re, im), D rows each; after the products of (c), the six [C][D] sums
-    float SS[4 * D > 6 * kC ? 4 * D : 6 * kC][D + 1];
-    float dO[kC][D + 1];
-    Rows<D> U, LB, X;                     // U; lambda; X
-    float Gbr[kC][kC + 1], Gbi[kC][kC + 1];   // cotangent of G (beta Ab)
-    float Hbr[kC][kC + 1], Hbi[kC][kC + 1];   // cotangent of H (Pb)
-    float dbA[kC][kC + 1];                    // Re(conj(Ab) G) per pair
-    float red[2 * (NTH / D)][D];              // per-channel partial sums over rows
-    float glp[2 * (NTH / D)][D];              // partials of sum_w dS1 conj(S0) per channel
+    float K[kC][D + 1], Q[kC][D + 1];
+    float gr[kC][D + 1], gi[kC][D + 1];     // gam
+    float Gbr[kC][LT], Gbi[kC][LT];         // cotangent of G (beta Ab)
+    float Hbr[kC][LT], Hbi[kC][LT];         // cotangent of H (Pb)
+    float kgr[kC][D + 1], kgi[kC][D + 1];   // K E, then the cotangent of gam
+    float Gr[kC][LT], Gi[kC][LT];
+    float dbA[kC][LT];                      // Re(conj(Ab) G) per pair
+    union {
+        struct {
+            float tr[NTH / D][D], ti[NTH / D][D];   // the gate's prefix totals
+        } pre;
+        struct {
+            float red[2 * (NTH / D)][D];   // per-channel partials of the Kd terms of gam_L
+            float glp[2 * (NTH / 64)][D];  // per-wave partials of sum_w dS1 conj(S0)
+        } post;
+    } u1;
 };
 
 // Threads of phase_bwd_chunk: 512 (two waves per SIMD) where every phase has work
 // for them (d >= 32).
 template <int D> constexpr int bwd_chunk_threads() { return D >= 32 ? 512 : 256; }
 
+// Waves per SIMD that the registers must allow: at d = 64 the LDS holds two
+// workgroups of 512 threads per CU, four waves per SIMD.
+template <int D> constexpr int bwd_chunk_waves() { return D == 64 ? 4 : 1; }
+
 template <typename TI, int GATE, int D>
-__global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel(
+__global__ __launch_bounds__(bwd_chunk_threads<D>()) __attribute__((amdgpu_waves_per_eu(bwd_chunk_waves<D>())))
+void phase_bwd_chunk_kernel(
     Params p, const float* __restrict__ states, const float* __restrict__ mats, const float* __restrict__ lam,
     const float* __restrict__ dS1) {
     constexpr int NTH = bwd_chunk_threads<D>();
     using CI = ChunkIn<TI, GATE, D, NTH>;
-    constexpr int PG = NTH / D <= D ? NTH / D : D, NC = D / PG;   // lanes per state row in (b)
-    __shared__ ChunkBwdLds<D, NTH> b;
-    float(*S0r)[D + 1] = b.SS, (*S0i)[D + 1] = b.SS + D, (*S1r)[D + 1] = b.SS + 2 * D, (*S1i)[D + 1] = b.SS + 3 * D;
+    using LDS = ChunkBwdLds<D, NTH>;
+    constexpr int NQ = LDS::NQ, KQ = D / NQ, L0 = LDS::L0, L1 = LDS::L1, LT = LDS::LT;
+    constexpr int NW = NTH / 64, NTL = D / 16, NBLK = D / kBV;
+    constexpr int VEC = kBV * D / NTH, NX = 2 * kCC / NTH;   // per thread and block: state floats, others
+    static_assert(VEC >= 1 && VEC * NTH == kBV * D && NX * NTH == 2 * kCC && NTL <= NW, "block loads");
+    constexpr int KDI = (2 * NTL + NW - 1) / NW;             // Kdb items per wave
+    constexpr int AB_W = 2 % NW, PB_W = 3 % NW;              // the waves of Ab and Pb
+    __shared__ __align__(16) LDS b;
+    auto& bk = b.u2.blk;
     const int tid = threadIdx.x, n = blockIdx.x, bh = blockIdx.y;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), li = lane & 15, lk = lane >> 4;
     const int t0 = n * kC, valid = min(kC, p.T - t0), L = valid - 1;
     const long row0 = (long)bh * p.T + t0, chunk = (long)bh * p.NT + n;
     const TI* __restrict__ dout = static_cast<const TI*>(p.dout);
     const TI* __restrict__ vin = static_cast<const TI*>(p.v);
     TI* __restrict__ dq = static_cast<TI*>(p.dq);
     TI* __restrict__ dk = static_cast<TI*>(p.dk);
-    // (a) the chunk's data into LDS
+
+    // The block in registers: VEC consecutive floats of each state array from
+    // element tid VEC of the block's 16 x D (row ew, channels ec ..), and NX
+    // elements of lambda (re, then im: [w][t]) and of the dO and V columns ([t][w]).
+    const float* __restrict__ st0 = states + chunk * 2 * D * D;
+    const float* __restrict__ st1 = dS1 + chunk * 2 * D * D;
+    const float* __restrict__ lm = lam + chunk * 2 * D * kC;
+    const int ew = tid * VEC / D, ec = tid * VEC % D;
+    float s0r[VEC], s0i[VEC], s1r[VEC], s1i[VEC], lx[NX], ox[NX];
+    auto fetch = [&](int j) {
+        const long o = (long)j * kBV * D + tid * VEC;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            s0r[v] = st0[o + v];
+            s0i[v] = st0[(long)D * D + o + v];
+            s1r[v] = st1[o + v];
+            s1i[v] = st1[(long)D * D + o + v];
+        }
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+            const int idx = tid + NTH * x, e = idx % kCC, t = e / kBV, w = e % kBV;
+            const bool second = idx >= kCC;   // lambda im and V, else lambda re and dO
+            lx[x] = lm[(second ? (long)D * kC : 0) + j * kCC + e];
+            const bool ok = t < valid;
+            const float y = to_f((second ? vin : dout)[(row0 + (ok ? t : 0)) * D + j * kBV + w]);
+            ox[x] = ok ? y : 0.f;
+        }
+    };
+    float glr[VEC], gli[VEC];   // sum_w dS1_wc conj(S0_wc) for the thread's channels
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) glr[v] = gli[v] = 0.f;
+    auto commit = [&]() {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            bk.S0r[ew][ec + v] = s0r[v];
+            bk.S0i[ew][ec + v] = s0i[v];
+            bk.S1r[ew][ec + v] = s1r[v];
+            bk.S1i[ew][ec + v] = s1i[v];
+            glr[v] += s1r[v] * s0r[v] + s1i[v] * s0i[v];
+            gli[v] += s1i[v] * s0r[v] - s1r[v] * s0i[v];
+        }
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+            const int idx = tid + NTH * x, e = idx % kCC, r = e / kBV, c = e % kBV;
+            if (idx < kCC) {
+                bk.Lr[r][c] = lx[x];
+                bk.dO[r][c] = ox[x];
+            } else {
+                bk.Li[r][c] = lx[x];
+                bk.V[r][c] = ox[x];
+            }
+        }
+    };
+    fetch(0);
+
+    // (a) the chunk's K, Q, gam, K E, T, G, beta into LDS
     CI in;
     in.load(p, row0, valid);
     {
-        const float* st = states + chunk * 2 * D * D;
-        const float* d1 = dS1 + chunk * 2 * D * D;
-        for (int idx = tid; idx < D * D; idx += NTH) {
-            const int r = idx / D, c = idx % D;
-            S0r[r][c] = st[idx];
-            S0i[r][c] = st[(long)D * D + idx];
-            S1r[r][c] = d1[idx];
-            S1i[r][c] = d1[(long)D * D + idx];
-        }
-        const float* lm = lam + chunk * 2 * D * kC;
-        for (int idx = tid; idx < D * kC; idx += NTH) {
-            const int vv = idx / kC, t = idx % kC;
-            b.LB.r[t][vv] = lm[idx];
-            b.LB.i[t][vv] = lm[(long)D * kC + idx];
-        }
-        for (int idx = tid; idx < kC * D; idx += NTH) {
-            const int t = idx / D, c = idx % D;
-            const bool ok = t < valid;
-            const long e = (row0 + (ok ? t : 0)) * D + c;
-            const float o = to_f(dout[e]), vv = to_f(vin[e]);
-            b.dO[t][c] = ok ? o : 0.f;
-            b.V[t][c] = ok ? vv : 0.f;
-        }
         const float* mc = mats + chunk * kMats;
         if (tid < kCC) {
             const int t = tid / kC, u = tid % kC;
             b.Tr[t][u] = mc[tid];
             b.Ti[t][u] = mc[kCC + tid];
-            b.Pr[t][u] = mc[2 * kCC + tid];
-            b.Pi[t][u] = mc[3 * kCC + tid];
             b.Gr[t][u] = mc[4 * kCC + tid];
             b.Gi[t][u] = mc[5 * kCC + tid];
         }
         const float bt = p.beta[row0 + min(tid % kC, valid - 1)];
         if (tid < kC) b.beta[tid] = tid < valid ? bt : 0.f;
     }
-    in.prefix(b.tr, b.ti);
+    in.prefix(b.u1.pre.tr, b.u1.pre.ti);
     __syncthreads();
-    in.finish(b.tr, b.ti);
+    in.finish(b.u1.pre.tr, b.u1.pre.ti);
     {
         const int c = CI::chan();
 #pragma unroll
@@ -722,156 +799,186 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
             b.kgi[t][c] = in.k[r] * E.i;
         }
     }
-    __syncthreads();
+
     // Every product below runs on the fp32 matrix cores: a complex product is two
     // or four real 16x16x4 MFMA products into one accumulator per real output
     // (signs folded into the A fragment).  Fragments: lane l supplies A row l % 16
     // and B row l % 16 at K slot l / 16; accumulator element i of lane l is
-    // output (4 (l / 16) + i, l % 16) of the 16 x 16 tile.  Work items go to the
-    // waves round-robin.
-    const int lane = tid & 63, wave = tid >> 6, li = lane & 15, lk = lane >> 4;
-    constexpr int NW = NTH / 64, NTL = D / 16;   // waves; 16-wide column tiles of a D-wide output
-    auto mma = [](float a, float bb, f32x4 acc) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0); };
-    // (b) X = (K E) S0^T (kept for dbeta), then R = beta (V - X) over K E (dead once X
-    //     is formed) and U = T R; items (column tile of v, real or imaginary part)
-    for (int it = wave; it < 2 * NTL; it += NW) {
-        // Xr = KEr S0r^T - KEi S0i^T, Xi = KEr S0i^T + KEi S0r^T
-        const int n0 = (it >> 1) * 16;
-        const float* b1 = (it & 1) ? &S0i[n0][0] : &S0r[n0][0];
-        const float* b2 = (it & 1) ? &S0r[n0][0] : &S0i[n0][0];
-        const f32x4 acc = mma_pair<D, D + 1, D + 1, false, false>(zero4(), &b.kgr[0][0], b1, 1.f, &b.kgi[0][0], b2,
-                                                                  (it & 1) ? 1.f : -1.f);
-        float(*xo)[D + 1] = (it & 1) ? b.X.i : b.X.r;
+    // output (4 (l / 16) + i, l % 16) of the 16 x 16 tile.
+    f32x4 kq[4] = {zero4(), zero4(), zero4(), zero4()};   // wave < NTL: -Kgb re, im, Qgb re, im of tile `wave`
+    f32x4 kd[KDI];                                        // Kdb items wave + NW jj: (column tile, re / im)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xo[4 * lk + i][n0 + li] = acc[i];
-    }
-    __syncthreads();
-    for (int idx = tid; idx < kC * D; idx += NTH) {
-        const int t = idx / D, v = idx % D;
-        b.kgr[t][v] = b.beta[t] * (b.V[t][v] - b.X.r[t][v]);
-        b.kgi[t][v] = -b.beta[t] * b.X.i[t][v];
-    }
-    __syncthreads();
-    for (int it = wave; it < 2 * NTL; it += NW) {
-        // Ur = Tr Rr - Ti Ri, Ui = Tr Ri + Ti Rr (R stored [w][v] over K E)
-        const int n0 = (it >> 1) * 16;
-        const float* b1 = (it & 1) ? &b.kgi[0][n0] : &b.kgr[0][n0];
-        const float* b2 = (it & 1) ? &b.kgr[0][n0] : &b.kgi[0][n0];
-        const f32x4 acc = mma_pair<kC, kC + 1, D + 1, false, true>(zero4(), &b.Tr[0][0], b1, 1.f, &b.Ti[0][0], b2,
-                                                                   (it & 1) ? 1.f : -1.f);
-        float(*uo)[D + 1] = (it & 1) ? b.U.i : b.U.r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) uo[4 * lk + i][n0 + li] = acc[i];
-    }
-    __syncthreads();
-    // (c) the three sums over the rows v per element (t, c), the pair products, and per
-    //     channel the state-decay term of gam_L:
-    //       Kgb = -sum_w lambda_tw conj(S0_wc)    Qgb = sum_w dO_tw conj(S0_wc)
-    //       Kdb = sum_w dS1_wc conj(U_tw)
-    //       Ab = -lambda U^H (strictly lower)      Pb = dO U^H (lower)
-    //       gl_c = sum_w dS1_wc conj(S0_wc E_L,c)
-    //     Items: Kgb and Qgb per column tile (waves 0 .. NTL - 1), Kdb per column tile
-    //     (the next NTL), Ab and Pb (one 16 x 16 tile each, on waves after those or
-    //     shared).  Kgb / Qgb / Kdb stay in registers until every wave has read S0 and
-    //     dS1, then go to LDS over them.
-    f32x4 res[4] = {zero4(), zero4(), zero4(), zero4()};
-    const int item = wave < 2 * NTL ? wave : -1;
-    if (item >= 0 && item < NTL) {
-        const int n0 = item * 16;
-        // -Kgb_r = lr S0r + li S0i, -Kgb_i = li S0r - lr S0i, Qgb_r = dO S0r, Qgb_i = -dO S0i
-        // (A = lambda, dO [t][w]; B = S0 [w][c]); fragments of 4 K steps read ahead
-#pragma unroll
-        for (int j0 = 0; j0 < D / 4; j0 += 4) {
+    for (int jj = 0; jj < KDI; ++jj) kd[jj] = zero4();
+    f32x4 ap[2] = {zero4(), zero4()};   // -Ab re, im (wave AB_W) or Pb re, im (wave PB_W)
+    float db[4] = {0.f, 0.f, 0.f, 0.f};  // wave 0: dbeta partials of steps 4 jj + lk, column li
+    for (int j = 0; j < NBLK; ++j) {
+        commit();
+        __syncthreads();   // (the first time also orders the chunk's tiles of (a))
+        if (j + 1 < NBLK) fetch(j + 1);
+        // (1) the block's terms of Kgb and Qgb for column tile `wave` (sharing the S0
+        //     fragments): -Kgb_r += lr S0r + li S0i, -Kgb_i += li S0r - lr S0i,
+        //     Qgb_r += dO S0r, Qgb_i -= dO S0i (A = lambda [w][t] transposed, dO [t][w];
+        //     B = S0 [w][c] transposed); then the channel parts of X (items NTL ..)
+        if (wave < NTL) {
+            const int n0 = wave * 16;
             float lr[4], lq[4], o[4], sr[4], si[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                lr[j] = frag<D + 1, false>(&b.LB.r[0][0], j0 + j);
-                lq[j] = frag<D + 1, false>(&b.LB.i[0][0], j0 + j);
-                o[j] = frag<D + 1, false>(&b.dO[0][0], j0 + j);
-                sr[j] = frag<D + 1, true>(&S0r[0][n0], j0 + j);
-                si[j] = frag<D + 1, true>(&S0i[0][n0], j0 + j);
+            for (int jj = 0; jj < 4; ++jj) {
+                lr[jj] = frag<LT, true>(&bk.Lr[0][0], jj);
+                lq[jj] = frag<LT, true>(&bk.Li[0][0], jj);
+                o[jj] = frag<LT, false>(&bk.dO[0][0], jj);
+                sr[jj] = frag<L0, true>(&bk.S0r[0][n0], jj);
+                si[jj] = frag<L0, true>(&bk.S0i[0][n0], jj);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                res[0] = mma(lq[j], si[j], mma(lr[j], sr[j], res[0]));
-                res[1] = mma(-lr[j], si[j], mma(lq[j], sr[j], res[1]));
-                res[2] = mma(o[j], sr[j], res[2]);
-                res[3] = mma(-o[j], si[j], res[3]);
+            for (int jj = 0; jj < 4; ++jj) {
+                kq[0] = mma4(lq[jj], si[jj], mma4(lr[jj], sr[jj], kq[0]));
+                kq[1] = mma4(-lr[jj], si[jj], mma4(lq[jj], sr[jj], kq[1]));
+                kq[2] = mma4(o[jj], sr[jj], kq[2]);
+                kq[3] = mma4(-o[jj], si[jj], kq[3]);
             }
         }
-    } else if (item >= NTL) {
-        const int n0 = (item - NTL) * 16;
-        // Kdb_r = Ur S1r + Ui S1i, Kdb_i = Ur S1i - Ui S1r (A = U [t][w], B = dS1 [w][c])
-        res[0] = mma_pair<D, D + 1, D + 1, false, true>(res[0], &b.U.r[0][0], &S1r[0][n0], 1.f, &b.U.i[0][0],
-                                                        &S1i[0][n0], 1.f);
-        res[1] = mma_pair<D, D + 1, D + 1, false, true>(res[1], &b.U.r[0][0], &S1i[0][n0], 1.f, &b.U.i[0][0],
-                                                        &S1r[0][n0], -1.f);
+        for (int x = (wave + NW - NTL % NW) % NW; x < 2 * NQ; x += NW) {
+            // channels c0 .. c0 + KQ: Xr = KEr S0r^T - KEi S0i^T, Xi = KEr S0i^T + KEi S0r^T
+            const int c0 = (x >> 1) * KQ;
+            const bool im = x & 1;
+            const f32x4 acc = mma_pair<KQ, D + 1, L0, false, false>(
+                zero4(), &b.kgr[0][c0], im ? &bk.S0i[0][c0] : &bk.S0r[0][c0], 1.f, &b.kgi[0][c0],
+                im ? &bk.S0r[0][c0] : &bk.S0i[0][c0], im ? 1.f : -1.f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bk.Xp[x][4 * lk + i][li] = acc[i];
+        }
+        __syncthreads();
+        // (2) U = T R with R = diag(beta) (V - X), X the sum of its parts (waves 0, 1:
+        //     re, im; each forms the R fragments it needs); wave 0 adds the block's
+        //     Re(conj(lambda) (V - X)) to the dbeta partials
+        if (wave < 2) {
+            const bool im = wave == 1;
+            float rr[4], ri[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int s = 4 * jj + lk;
+                float xr = 0.f, xi = 0.f;
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    xr += bk.Xp[2 * q][s][li];
+                    xi += bk.Xp[2 * q + 1][s][li];
+                }
+                const float a = bk.V[s][li] - xr, bt = b.beta[s];
+                rr[jj] = bt * a;
+                ri[jj] = -bt * xi;
+                if (!im) db[jj] += bk.Lr[li][s] * a - bk.Li[li][s] * xi;
+            }
+            // Ur = Tr Rr - Ti Ri, Ui = Tr Ri + Ti Rr (A = T [t][s]; B = R at (s, v) = (4 jj + lk, li))
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float a1 = frag<LT, false>(&b.Tr[0][0], jj), a2 = frag<LT, false>(&b.Ti[0][0], jj);
+                acc = mma4(a1, im ? ri[jj] : rr[jj], acc);
+                acc = mma4(im ? a2 : -a2, im ? rr[jj] : ri[jj], acc);
+            }
+            float(*uo)[LT] = im ? bk.Ui : bk.Ur;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) uo[4 * lk + i][li] = acc[i];
+        }
+        __syncthreads();
+        // (3) the block's terms of Kdb (items: column tile, re / im), -Ab and Pb
+#pragma unroll
+        for (int jj = 0; jj < KDI; ++jj) {
+            const int it = wave + jj * NW;
+            if (it < 2 * NTL) {
+                // Kdb_r += Ur S1r + Ui S1i, Kdb_i += Ur S1i - Ui S1r (A = U [t][w]; B = dS1 [w][c] transposed)
+                const int n0 = (it >> 1) * 16;
+                const bool im = it & 1;
+                kd[jj] = mma_pair<kBV, LT, L1, false, true>(kd[jj], &bk.Ur[0][0],
+                                                            im ? &bk.S1i[0][n0] : &bk.S1r[0][n0], 1.f, &bk.Ui[0][0],
+                                                            im ? &bk.S1r[0][n0] : &bk.S1i[0][n0], im ? -1.f : 1.f);
+            }
+        }
+        if (wave == AB_W) {
+            // -Ab_r += lr Ur + li Ui, -Ab_i += li Ur - lr Ui (A = lambda transposed; B = U [u][w])
+            ap[0] = mma_pair<kBV, LT, LT, true, false>(ap[0], &bk.Lr[0][0], &bk.Ur[0][0], 1.f, &bk.Li[0][0],
+                                                       &bk.Ui[0][0], 1.f);
+            ap[1] = mma_pair<kBV, LT, LT, true, false>(ap[1], &bk.Li[0][0], &bk.Ur[0][0], 1.f, &bk.Lr[0][0],
+                                                       &bk.Ui[0][0], -1.f);
+        }
+        if (wave == PB_W) {
+            // Pb_r += dO Ur, Pb_i -= dO Ui (A = dO [t][w]; B = U [u][w])
+            ap[0] = mma_one<kBV, LT, LT, false, false>(ap[0], &bk.dO[0][0], &bk.Ur[0][0], 1.f);
+            ap[1] = mma_one<kBV, LT, LT, false, false>(ap[1], &bk.dO[0][0], &bk.Ui[0][0], -1.f);
+        }
+        __syncthreads();   // the block is consumed
     }
-    constexpr int AB_WAVE = 2 * NTL < NW ? 2 * NTL : NTL, PB_WAVE = 2 * NTL + 1 < NW ? 2 * NTL + 1 : NTL + 1;
-    if (wave == AB_WAVE) {
-        // -Ab_r = lr Ur + li Ui, -Ab_i = li Ur - lr Ui (A = lambda [t][w], B = U [u][w])
-        const f32x4 ar = mma_pair<D, D + 1, D + 1, false, false>(zero4(), &b.LB.r[0][0], &b.U.r[0][0], 1.f,
-                                                                 &b.LB.i[0][0], &b.U.i[0][0], 1.f);
-        const f32x4 ai = mma_pair<D, D + 1, D + 1, false, false>(zero4(), &b.LB.i[0][0], &b.U.r[0][0], 1.f,
-                                                                 &b.LB.r[0][0], &b.U.i[0][0], -1.f);
+    // The sums to LDS over the blocks' space; Gb, Hb, Re(conj(Ab) G); the gl partials
+    float(*Kgr)[D + 1] = b.u2.sums[0], (*Kgi)[D + 1] = b.u2.sums[1], (*Qgr)[D + 1] = b.u2.sums[2];
+    float(*Qgi)[D + 1] = b.u2.sums[3], (*Kdr)[D + 1] = b.u2.sums[4], (*Kdi)[D + 1] = b.u2.sums[5];
+    if (wave < NTL) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * lk + i, c = wave * 16 + li;
+            Kgr[t][c] = -kq[0][i];
+            Kgi[t][c] = -kq[1][i];
+            Qgr[t][c] = kq[2][i];
+            Qgi[t][c] = kq[3][i];
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < KDI; ++jj) {
+        const int it = wave + jj * NW;
+        if (it < 2 * NTL) {
+            float(*ko)[D + 1] = (it & 1) ? Kdi : Kdr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ko[4 * lk + i][(it >> 1) * 16 + li] = kd[jj][i];
+        }
+    }
+    if (wave == AB_W) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * lk + i, u = li;
-            const float abr = u < t ? -ar[i] : 0.f, abi = u < t ? -ai[i] : 0.f;
+            const float abr = u < t ? -ap[0][i] : 0.f, abi = u < t ? -ap[1][i] : 0.f;
             b.Gbr[t][u] = b.beta[t] * abr;
             b.Gbi[t][u] = b.beta[t] * abi;
             b.dbA[t][u] = abr * b.Gr[t][u] + abi * b.Gi[t][u];   // Re(conj(Ab) G)
         }
     }
-    if (wave == PB_WAVE) {
-        // Pb_r = dO Ur, Pb_i = -dO Ui (A = dO [t][w], B = U [u][w])
-        const f32x4 pr = mma_one<D, D + 1, D + 1, false, false>(zero4(), &b.dO[0][0], &b.U.r[0][0], 1.f);
-        const f32x4 pi = mma_one<D, D + 1, D + 1, false, false>(zero4(), &b.dO[0][0], &b.U.i[0][0], -1.f);
+    if (wave == PB_W) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * lk + i, u = li;
-            b.Hbr[t][u] = u <= t ? pr[i] : 0.f;
-            b.Hbi[t][u] = u <= t ? pi[i] : 0.f;
+            b.Hbr[t][u] = u <= t ? ap[0][i] : 0.f;
+            b.Hbi[t][u] = u <= t ? ap[1][i] : 0.f;
         }
     }
-    {   // gl: channel c, rows w of this thread's part (partials over the parts in (e))
-        constexpr int NP = NTH / D, WP = D / NP > 0 ? D / NP : 1;
-        const int c = tid % D, part = tid / D;
-        cf acc = {0.f, 0.f};
-        if (part * WP < D) {
-#pragma unroll 4
-            for (int w = part * WP; w < part * WP + WP; ++w)
-                acc = cadd(acc, cmulc({S1r[w][c], S1i[w][c]}, {S0r[w][c], S0i[w][c]}));
-        }
-        b.glp[2 * part][c] = acc.r;
-        b.glp[2 * part + 1][c] = acc.i;
-    }
-    __syncthreads();
-    // S0 and dS1 are dead: the sums go over them, [t][c] each
-    float(*Kgr)[D + 1] = b.SS, (*Kgi)[D + 1] = b.SS + kC, (*Qgr)[D + 1] = b.SS + 2 * kC;
-    float(*Qgi)[D + 1] = b.SS + 3 * kC, (*Kdr)[D + 1] = b.SS + 4 * kC, (*Kdi)[D + 1] = b.SS + 5 * kC;
-
-    if (item >= 0 && item < NTL) {
-        const int n0 = item * 16;
+    {   // lanes D / VEC apart hold the same channels: the wave's total, then one partial per wave
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * lk + i, c = n0 + li;
-            Kgr[t][c] = -res[0][i];
-            Kgi[t][c] = -res[1][i];
-            Qgr[t][c] = res[2][i];
-            Qgi[t][c] = res[3][i];
-        }
-    } else if (item >= NTL) {
-        const int n0 = (item - NTL) * 16;
+        for (int v = 0; v < VEC; ++v) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            Kdr[4 * lk + i][n0 + li] = res[0][i];
-            Kdi[4 * lk + i][n0 + li] = res[1][i];
+            for (int off = D / VEC; off < 64; off *= 2) {
+                glr[v] += __shfl_xor(glr[v], off);
+                gli[v] += __shfl_xor(gli[v], off);
+            }
+        }
+        if (lane < D / VEC) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                b.u1.post.glp[2 * wave][ec + v] = glr[v];
+                b.u1.post.glp[2 * wave + 1][ec + v] = gli[v];
+            }
         }
     }
     __syncthreads();
+    // dbeta_t = Re sum_v conj(lambda_tv) (V - X)_tv + sum_u Re(conj(Ab_tu) G_tu): the
+    // partials of wave 0, summed over the 16 lanes of a DPP row
+    if (wave == 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int s = 4 * jj + lk;
+            const float x = group_sum<16>(db[jj] + (li < s ? b.dbA[s][li] : 0.f));
+            if (li == 0 && s < valid) p.dbeta[row0 + s] = x;
+        }
+    }
     // (d) elements (t, c): the scaled tiles' cotangents, the pairwise G / H terms; dq, dk;
-    //     gam's cotangent, stored over K E (R since (b); dead).  Each pair's factor is
+    //     gam's cotangent, stored over K E (dead after the last block).  Each pair's factor is
     //     formed by both of its elements (as row and as column): accumulating the column
     //     terms once per pair through LDS atomics instead measured 1.9x slower.
     constexpr int TS = NTH / D;                         // threads sharing a channel
@@ -921,23 +1028,23 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
             b.kgr[t][c] = gb.r;
             b.kgi[t][c] = gb.i;
         }
-        b.red[2 * tg][c] = kdsum.r;
-        b.red[2 * tg + 1][c] = kdsum.i;
+        b.u1.post.red[2 * tg][c] = kdsum.r;
+        b.u1.post.red[2 * tg + 1][c] = kdsum.i;
     }
     __syncthreads();
     // (e) per channel: gam_L's cotangent (the state's decay and the Kd terms), then the
     //     reverse cumulative sum; dtheta, dg (the scalar gate sums its channels per row,
-    //     from the real parts kept over U, which nothing reads any more)
-    float (*dgs)[D + 1] = b.U.r;
+    //     from the real parts kept over the first of the sums, read by (d) only)
+    float(*dgs)[D + 1] = b.u2.sums[0];
     if (tid < D) {
         const int c = tid;
         cf acc = {0.f, 0.f};
-        for (int g2 = 0; g2 < NTH / D; ++g2) acc = cadd(acc, {b.glp[2 * g2][c], b.glp[2 * g2 + 1][c]});
+        for (int g2 = 0; g2 < NW; ++g2) acc = cadd(acc, {b.u1.post.glp[2 * g2][c], b.u1.post.glp[2 * g2 + 1][c]});
         const cf gl = cmulc(acc, cexp_(b.gr[L][c], b.gi[L][c]));   // sum_w dS1 conj(S0 E_L)
         float lr = gl.r, li = gl.i;
         for (int g2 = 0; g2 < TS; ++g2) {
-            lr += b.red[2 * g2][c];
-            li += b.red[2 * g2 + 1][c];
+            lr += b.u1.post.red[2 * g2][c];
+            li += b.u1.post.red[2 * g2 + 1][c];
         }
         float ar = 0.f, ai = 0.f;
         for (int t = L; t >= 0; --t) {
@@ -947,16 +1054,6 @@ __global__ __launch_bounds__(bwd_chunk_threads<D>()) void phase_bwd_chunk_kernel
             if (GATE == kGateVector) p.dg[(row0 + t) * D + c] = ar;
             dgs[t][c] = ar;
         }
-    }
-    // dbeta_t = Re sum_v conj(lambda_tv) (V - X)_tv + sum_u Re(conj(Ab_tu) G_tu): step t
-    // by the 16 lanes of one DPP row of the last 256 threads
-    if (tid >= NTH - kCC) {
-        const int t = (tid - (NTH - kCC)) / 16, j = tid % 16;
-        float acc = j < t ? b.dbA[t][j] : 0.f;
-        for (int w = j; w < D; w += 16)
-            acc += b.LB.r[t][w] * (b.V[t][w] - b.X.r[t][w]) - b.LB.i[t][w] * b.X.i[t][w];
-        acc = group_sum<16>(acc);
-        if (j == 0 && t < valid) p.dbeta[row0 + t] = acc;
     }
     if (GATE == kGateScalar) {
         __syncthreads();
@@ -997,6 +1094,7 @@ hipError_t phase_launch_g(const Params& p, const PhaseBufs& f, bool backward, hi
         case 16: return phase_launch_d<TI, GATE, 16>(p, f, backward, stream);
         case 32: return phase_launch_d<TI, GATE, 32>(p, f, backward, stream);
         case 64: return phase_launch_d<TI, GATE, 64>(p, f, backward, stream);
+        case 128: return phase_launch_d<TI, GATE, 128>(p, f, backward, stream);
         default: return hipErrorInvalidValue;
     }
 }

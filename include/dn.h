@@ -268,7 +268,7 @@ dn_status dn_recurrent_phase_fwd(const dn_shape* shape, const void* q, const voi
  * the chunks back in reverse with one transposed (conjugated) triangular solve
  * per chunk.  The per-chunk products run for all chunks at once, the state
  * recurrences over (head, block of 16 state rows); fp32 arithmetic throughout.
- *   shape  : dk == dv in {16, 32, 64}; C == 16; dtype fp32 or bf16 (q, k, v, o,
+ *   shape  : dk == dv in {16, 32, 64, 128}; C == 16; dtype fp32 or bf16 (q, k, v, o,
  *            dout, dq, dk, dv); gate as for dn_chunk_fwd; DN_FLAG_KACZMARZ is not
  *            supported here (DN_ERR_UNSUPPORTED); DN_FLAG_NO_SCAN is ignored
  *   inputs : q, k, v, beta, g as for dn_chunk_fwd; theta fp32 [B][H][T][dk]

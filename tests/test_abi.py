@@ -245,7 +245,7 @@ def test_validation_errors_recurrent_phase():
 
 
 def test_validation_errors_chunk_phase():
-    """The chunkwise phase-controlled gate: chunks of 16, d <= 64, no Kaczmarz step,
+    """The chunkwise phase-controlled gate: chunks of 16, d in {16, 32, 64, 128}, no Kaczmarz step,
     theta required, the backward needs the forward's states."""
     def sh(**over):
         d = dict(B=1, H=2, T=40, dk=32, dv=32, C=16, dtype="fp32", gate="vector")
@@ -278,7 +278,9 @@ def test_validation_errors_chunk_phase():
     assert B.dn_phase_states_bytes(sh(C=64)) == 0
     assert B.dn_phase_workspace_bytes(sh(C=64), B.DN_PASS_BWD) == 0
     assert fwd(sh(C=64)) == B.DN_ERR_UNSUPPORTED
-    assert fwd(sh(dk=128, dv=128)) == B.DN_ERR_UNSUPPORTED
+    assert B.dn_phase_states_bytes(sh(dk=128, dv=128)) == al(2 * 3 * 2 * 128 * 128 * 4) + al(2 * 3 * 6 * 16 * 16 * 4)
+    assert fwd(sh(dk=48, dv=48)) == B.DN_ERR_UNSUPPORTED
+    assert fwd(sh(dk=256, dv=256)) == B.DN_ERR_UNSUPPORTED
     assert fwd(sh(dk=32, dv=16)) == B.DN_ERR_UNSUPPORTED
     assert fwd(B.make_shape(1, 2, 40, 32, 32, 16, "fp32", "vector", kaczmarz_eps=1e-6)) == B.DN_ERR_UNSUPPORTED
     assert fwd(sh(), theta=None) == B.DN_ERR_INVALID

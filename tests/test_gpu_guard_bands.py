@@ -107,7 +107,8 @@ def test_allocation_free_forward_stays_in_bounds():
     g.check("allocation-free forward")
 
 
-@pytest.mark.parametrize("gate,dtype,d", [("vector", "bf16", 64), ("scalar", "fp32", 32), ("none", "bf16", 16)])
+@pytest.mark.parametrize("gate,dtype,d", [("vector", "bf16", 64), ("scalar", "fp32", 32), ("none", "bf16", 16),
+                                          ("vector", "fp32", 128)])
 def test_chunk_phase_stays_in_bounds(gate, dtype, d):
     w = W.custom(2, 2, 16 * 3 + 7, d, d, 16, gate, dtype, h0_std=0.5, seed=98, phase=True)
     x = _inputs(w)

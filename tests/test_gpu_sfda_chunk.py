@@ -3,7 +3,7 @@ dn_chunk_phase_bwd; SFDA summary, chunk-WY form of the complex recurrence with
 real inputs) with the fp64 oracle (oracle/sfda.py, the recurrence and its
 reverse mode): o, the complex final state and every gradient (q, k, v, beta,
 g, theta, the complex initial state) at nonzero phase, for every gate type, both
-I/O types, d in {16, 32, 64} and ragged sequences; strong decay; at zero phase
+I/O types, d in {16, 32, 64, 128} and ragged sequences; strong decay; at zero phase
 the chunkwise real path (KDA / GDN / DeltaNet); the recurrent phase entry point;
 zero steps."""
 import numpy as np
@@ -27,6 +27,9 @@ CASES = [
     ("none", "bf16", 2, 1, 16 * 3 + 15, 32),
     ("vector", "fp32", 3, 1, 7, 32),
     ("vector", "bf16", 1, 1, 1, 16),
+    ("vector", "fp32", 1, 2, 16 * 3 + 5, 128),
+    ("scalar", "bf16", 2, 1, 16 * 2 + 11, 128),
+    ("none", "fp32", 1, 1, 16 * 4, 128),
 ]
 
 
@@ -148,7 +151,7 @@ def _phase_sweep(n=16, seed=2027):
     for case in range(n):
         gate = rng.choice(["none", "scalar", "vector"])
         dtype = rng.choice(["bf16", "fp32"])
-        d = rng.choice([16, 32, 64])
+        d = rng.choice([16, 32, 64, 128])
         T = rng.choice([1, 15, 16, 17, 16 * 3 + 5, 16 * 9, rng.randint(1, 200)])
         Bn, H = rng.choice([(1, 1), (1, 3), (2, 2), (3, 1)])
         h0 = rng.choice([0.0, 0.5])
