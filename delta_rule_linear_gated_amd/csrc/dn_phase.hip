@@ -255,21 +255,29 @@ template <typename TI, int GATE, int D> struct SeqIn {
 
 // LDS of the sequential kernels (matrix-core form).  Tiles padded by 4 floats per row
 // (the fragment reads of 16 rows x 4 columns and 4 rows x 16 columns spread over
-// the banks); the state block lives here between chunks.
+// the banks; the 16-wide ones by 1 at d = 128, where the whole fits two workgroups
+// per CU); the state block lives here between chunks.  The small per-chunk arrays
+// come first, so ds_read immediates from one address reach them.
 template <int D> struct SeqLdsM {
-    static constexpr int LD = D + 4, LB = kBV + 4, LC = kC + 4;
-    float kgr[kC][LD], kgi[kC][LD];   // K E
-    float qgr[kC][LD], qgi[kC][LD];   // Q E
-    float kdr[kC][LD], kdi[kC][LD];   // K exp(gam_L - gam)
-    float elr[D], eli[D];             // E at the last row
-    float tr[kPT / D][D], ti[kPT / D][D];
-    float Sr[kBV][LD], Si[kBV][LD];   // the state block [v][c]
+    static constexpr int LD = D + 4, LB = kBV + (D >= 128 ? 1 : 4), LC = kC + (D >= 128 ? 1 : 4);
     float B[kC][LB];                  // V (forward) or dO (backward) block [t][v]
     float Tr[kC][LC], Ti[kC][LC], Pr[kC][LC], Pi[kC][LC];
     float beta[kC];
-    float Rr[kC][LB], Ri[kC][LB];     // R [t][v] (backward: Ub)
+    union {
+        struct {
+            float r[kC][LB], i[kC][LB];   // R [t][v] (backward: Ub), from the first product on
+        } R;
+        struct {
+            float r[kPT / D][D], i[kPT / D][D];   // the gate's prefix totals, until the tiles are formed
+        } tot;
+    } u;
     float Ur[kC][LB], Ui[kC][LB];     // U [t][v] (backward: lambda)
     float Os[kC][LB];                 // O (backward: dv) block, for the write-back
+    float elr[D], eli[D];             // E at the last row
+    float Sr[kBV][LD], Si[kBV][LD];   // the state block [v][c]
+    float kgr[kC][LD], kgi[kC][LD];   // K E
+    float qgr[kC][LD], qgi[kC][LD];   // Q E
+    float kdr[kC][LD], kdi[kC][LD];   // K exp(gam_L - gam)
 };
 
 __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 acc) {
@@ -332,7 +340,7 @@ __device__ __forceinline__ f32x4 mma_one(f32x4 acc, const float* A1, const float
 template <typename TI, int GATE, int D, class LDS>
 __device__ __forceinline__ void seq_commit(SeqIn<TI, GATE, D>& x, LDS& s) {
     const int tid = threadIdx.x;
-    x.in.prefix(s.tr, s.ti);
+    x.in.prefix(s.u.tot.r, s.u.tot.i);
     s.B[tid / kBV][tid % kBV] = x.blk;
     const int t = tid / kC, u = tid % kC;
     s.Tr[t][u] = x.m[0];
@@ -346,7 +354,7 @@ __device__ __forceinline__ void seq_commit(SeqIn<TI, GATE, D>& x, LDS& s) {
 template <typename TI, int GATE, int D, class LDS>
 __device__ __forceinline__ void seq_tiles(SeqIn<TI, GATE, D>& x, LDS& s) {
     using CI = ChunkIn<TI, GATE, D>;
-    const cf gl = x.in.finish(s.tr, s.ti);
+    const cf gl = x.in.finish(s.u.tot.r, s.u.tot.i);
     const int c = CI::chan();
 #pragma unroll
     for (int r = 0; r < CI::NR; ++r) {
@@ -425,11 +433,11 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = 4 * lk + i;
-                    s.Rr[t][li] = s.beta[t] * (s.B[t][li] - acc[i]);
+                    s.u.R.r[t][li] = s.beta[t] * (s.B[t][li] - acc[i]);
                 }
             } else if (it == 1) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s.Ri[4 * lk + i][li] = -s.beta[4 * lk + i] * acc[i];
+                for (int i = 0; i < 4; ++i) s.u.R.i[4 * lk + i][li] = -s.beta[4 * lk + i] * acc[i];
             } else {
                 yr = acc;
             }
@@ -439,8 +447,8 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
         for (int it = wave; it < 2; it += NW) {
             // Ur = Tr Rr - Ti Ri, Ui = Tr Ri + Ti Rr (R stored [w][v])
             constexpr int LC = SeqLdsM<D>::LC, LBv = SeqLdsM<D>::LB;
-            const float* b1 = it ? &s.Ri[0][0] : &s.Rr[0][0];
-            const float* b2 = it ? &s.Rr[0][0] : &s.Ri[0][0];
+            const float* b1 = it ? &s.u.R.i[0][0] : &s.u.R.r[0][0];
+            const float* b2 = it ? &s.u.R.r[0][0] : &s.u.R.i[0][0];
             const f32x4 acc = mma_pair<kC, LC, LBv, false, true>(zero4(), &s.Tr[0][0], b1, 1.f, &s.Ti[0][0], b2,
                                                                   it ? 1.f : -1.f);
             float(*uo)[SeqLdsM<D>::LB] = it ? s.Ui : s.Ur;
@@ -555,7 +563,7 @@ __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const fl
             f32x4 acc = mma_pair<D, LD, LD, false, false>(zero4(), &s.kdr[0][0], b1, 1.f, &s.kdi[0][0], b2,
                                                           it ? -1.f : 1.f);
             acc = mma_one<kC, LC, LBv, true, true>(acc, it ? &s.Pi[0][0] : &s.Pr[0][0], &s.B[0][0], it ? -1.f : 1.f);
-            float(*uo)[SeqLdsM<D>::LB] = it ? s.Ri : s.Rr;
+            float(*uo)[SeqLdsM<D>::LB] = it ? s.u.R.i : s.u.R.r;
 #pragma unroll
             for (int i = 0; i < 4; ++i) uo[4 * lk + i][li] = acc[i];
         }
@@ -564,8 +572,8 @@ __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const fl
         for (int it = wave; it < 2; it += NW) {
             // Tr Ubr + Ti Ubi (re), Tr Ubi - Ti Ubr (im); A = conj(T)^T, B = Ub [w][v]
             constexpr int LC = SeqLdsM<D>::LC, LBv = SeqLdsM<D>::LB;
-            const float* b1 = it ? &s.Ri[0][0] : &s.Rr[0][0];
-            const float* b2 = it ? &s.Rr[0][0] : &s.Ri[0][0];
+            const float* b1 = it ? &s.u.R.i[0][0] : &s.u.R.r[0][0];
+            const float* b2 = it ? &s.u.R.r[0][0] : &s.u.R.i[0][0];
             const f32x4 acc = mma_pair<kC, LC, LBv, true, true>(zero4(), &s.Tr[0][0], b1, 1.f, &s.Ti[0][0], b2,
                                                                  it ? -1.f : 1.f);
             float(*lo)[SeqLdsM<D>::LB] = it ? s.Ui : s.Ur;   // beta lambda, for dS0
@@ -666,7 +674,7 @@ template <int D, int NTH> struct ChunkBwdLds {
     float gr[kC][D + 1], gi[kC][D + 1];     // gam
     float Gbr[kC][LT], Gbi[kC][LT];         // cotangent of G (beta Ab)
     float Hbr[kC][LT], Hbi[kC][LT];         // cotangent of H (Pb)
-    float kgr[kC][D + 1], kgi[kC][D + 1];   // K E, then the cotangent of gam
+    float kgr[kC][D + 1], kgi[kC][D + 1];   // K E, then the per-step factors exp(gam_t - gam_{t-1})
     float Gr[kC][LT], Gi[kC][LT];
     float dbA[kC][LT];                      // Re(conj(Ab) G) per pair
     union {
@@ -949,6 +957,19 @@ void phase_bwd_chunk_kernel(
             b.Hbi[t][u] = u <= t ? ap[1][i] : 0.f;
         }
     }
+    constexpr int TS = NTH / D;                  // threads sharing a channel in (d)
+    constexpr int NRD = TS < kC ? kC / TS : 1;   // their rows t = tid / D + TS r
+    {   // per-step factors exp(gam_t - gam_{t-1}) over K E (dead), for the pair factors of (d)
+        const int c = tid % D, tg = tid / D;
+#pragma unroll
+        for (int r = 0; r < NRD; ++r) {
+            const int t = tg + TS * r;
+            if (t >= kC) break;
+            const cf e = cexp_(b.gr[t][c] - (t ? b.gr[t - 1][c] : 0.f), b.gi[t][c] - (t ? b.gi[t - 1][c] : 0.f));
+            b.kgr[t][c] = e.r;
+            b.kgi[t][c] = e.i;
+        }
+    }
     {   // lanes D / VEC apart hold the same channels: the wave's total, then one partial per wave
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
@@ -978,13 +999,15 @@ void phase_bwd_chunk_kernel(
         }
     }
     // (d) elements (t, c): the scaled tiles' cotangents, the pairwise G / H terms; dq, dk;
-    //     gam's cotangent, stored over K E (dead after the last block).  Each pair's factor is
-    //     formed by both of its elements (as row and as column): accumulating the column
-    //     terms once per pair through LDS atomics instead measured 1.9x slower.
-    constexpr int TS = NTH / D;                         // threads sharing a channel
-    constexpr int NRD = TS < kC ? kC / TS : 1;          // their rows t = tid / D + TS r
+    //     gam's cotangent, stored over the element's own Kgb (read first).  The pair
+    //     factors exp(gam_t - gam_u) are running products of the per-step factors
+    //     from the diagonal outwards (t as the row: u = t, t - 1, .., 0; as the
+    //     column: u = t, .., C - 1), so none exceeds 1 in magnitude for g <= 0.  Each
+    //     pair is formed by both of its elements: accumulating the column terms once
+    //     per pair through LDS atomics instead measured 1.9x slower.
     {
-        const int c = tid % D, tg = tid / D;
+        const int c = tid % D;
+        const int tg = D >= 64 ? __builtin_amdgcn_readfirstlane(tid / D) : tid / D;   // one per wave at D >= 64
         cf kdsum = {0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < NRD; ++r) {
@@ -1002,31 +1025,31 @@ void phase_bwd_chunk_kernel(
             const cf kdc = cmulc(Kdb, cscale(Ed, kt));
             gb = csub(gb, kdc);
             kdsum = cadd(kdsum, kdc);
-            // pairs with t as the row (u <= t) and as the column (u >= t)
-#pragma unroll 4
-            for (int u = 0; u < kC; ++u) {
-                const int r2 = u <= t ? t : u, cl = u <= t ? u : t;   // the pair (row, column)
-                const cf f = cexp_(b.gr[r2][c] - b.gr[cl][c], b.gi[r2][c] - b.gi[cl][c]);
-                const cf Gb = {b.Gbr[r2][cl], b.Gbi[r2][cl]}, Hb = {b.Hbr[r2][cl], b.Hbi[r2][cl]};
-                if (u <= t) {   // t is the row: G_tu, H_tu
-                    const float ku = b.K[u][c];
-                    const cf wg = cscale(f, ku);   // dG_tu / dk_tc
-                    dkv += Gb.r * wg.r + Gb.i * wg.i;
-                    dqv += Hb.r * wg.r + Hb.i * wg.i;
-                    gb = cadd(gb, cadd(cmulc(Gb, cscale(f, kt * ku)), cmulc(Hb, cscale(f, qt * ku))));
-                }
-                if (u >= t) {   // t is the column: G_ut, H_ut
-                    const cf wg = cscale(f, b.K[u][c]), wh = cscale(f, b.Q[u][c]);
-                    dkv += Gb.r * wg.r + Gb.i * wg.i + Hb.r * wh.r + Hb.i * wh.i;
-                    gb = csub(gb, cadd(cmulc(Gb, cscale(f, b.K[u][c] * kt)), cmulc(Hb, cscale(f, b.Q[u][c] * kt))));
-                }
+            // t as the row: G_tu, H_tu (dG_tu / dk_tc = f k_u)
+            cf f = {1.f, 0.f};
+            for (int u = t; u >= 0; --u) {
+                if (u < t) f = cmul(f, {b.kgr[u + 1][c], b.kgi[u + 1][c]});
+                const cf Gb = {b.Gbr[t][u], b.Gbi[t][u]}, Hb = {b.Hbr[t][u], b.Hbi[t][u]};
+                const cf wg = cscale(f, b.K[u][c]);
+                dkv += Gb.r * wg.r + Gb.i * wg.i;
+                dqv += Hb.r * wg.r + Hb.i * wg.i;
+                gb = cadd(gb, cmulc(cadd(cscale(Gb, kt), cscale(Hb, qt)), wg));
+            }
+            // t as the column: G_ut, H_ut
+            f = {1.f, 0.f};
+            for (int u = t; u < kC; ++u) {
+                if (u > t) f = cmul({b.kgr[u][c], b.kgi[u][c]}, f);
+                const cf Gb = {b.Gbr[u][t], b.Gbi[u][t]}, Hb = {b.Hbr[u][t], b.Hbi[u][t]};
+                const float ku = b.K[u][c], qu = b.Q[u][c];
+                dkv += ku * (Gb.r * f.r + Gb.i * f.i) + qu * (Hb.r * f.r + Hb.i * f.i);
+                gb = csub(gb, cscale(cmulc(cadd(cscale(Gb, ku), cscale(Hb, qu)), f), kt));
             }
             if (t < valid) {
                 dq[(row0 + t) * D + c] = from_f<TI>(dqv);
                 dk[(row0 + t) * D + c] = from_f<TI>(dkv);
             }
-            b.kgr[t][c] = gb.r;
-            b.kgi[t][c] = gb.i;
+            Kgr[t][c] = gb.r;
+            Kgi[t][c] = gb.i;
         }
         b.u1.post.red[2 * tg][c] = kdsum.r;
         b.u1.post.red[2 * tg + 1][c] = kdsum.i;
@@ -1034,8 +1057,8 @@ void phase_bwd_chunk_kernel(
     __syncthreads();
     // (e) per channel: gam_L's cotangent (the state's decay and the Kd terms), then the
     //     reverse cumulative sum; dtheta, dg (the scalar gate sums its channels per row,
-    //     from the real parts kept over the first of the sums, read by (d) only)
-    float(*dgs)[D + 1] = b.u2.sums[0];
+    //     from the real parts kept over Qgb, which only (d) read)
+    float(*dgs)[D + 1] = Qgr;
     if (tid < D) {
         const int c = tid;
         cf acc = {0.f, 0.f};
@@ -1048,8 +1071,8 @@ void phase_bwd_chunk_kernel(
         }
         float ar = 0.f, ai = 0.f;
         for (int t = L; t >= 0; --t) {
-            ar += b.kgr[t][c] + (t == L ? lr : 0.f);
-            ai += b.kgi[t][c] + (t == L ? li : 0.f);
+            ar += Kgr[t][c] + (t == L ? lr : 0.f);
+            ai += Kgi[t][c] + (t == L ? li : 0.f);
             p.dtheta[(row0 + t) * D + c] = ai;
             if (GATE == kGateVector) p.dg[(row0 + t) * D + c] = ar;
             dgs[t][c] = ar;
