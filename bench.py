@@ -80,7 +80,8 @@ def phase_flops_per_chunk(name: str, C: int, D: int) -> int:
     if name == "phase_bwd_state":   # Ub; P^H dO; lambda; dS0; the gated tiles
         return 20 * C * D * D + 6 * pairs * D * 2 + 6 * D * D + 27 * C * D
     if name == "phase_bwd_chunk":   # X, U; Ab, Pb; dS1.S0; the three row sums; pair terms per element
-        return 28 * C * D * D + 10 * pairs * D * 2 + 32 * C * C * D + 8 * D * D + 60 * C * D
+        # (each pair factor formed by both of its elements, one complex product each)
+        return 28 * C * D * D + 8 * pairs * D * 2 + 32 * C * C * D + 8 * D * D + 60 * C * D
     return 0
 
 
@@ -606,7 +607,7 @@ def phase_cpu_baseline(w, inp_cpu):
     from oracle import sfda
     from delta_rule_linear_gated_amd import workloads as W
 
-    nh, Ts = min(w.H, 4), min(w.T, 4096)
+    nh, Ts = min(w.H, 8 if w.dk <= 64 else 4), min(w.T, 8192)   # about 5-10 s of one core
     heads = [(0, h) for h in range(nh)]
     f = {}
     for n, t in inp_cpu.items():
