@@ -87,19 +87,21 @@ template <typename TI, int GATE, int D, int NTH = kPT> struct ChunkIn {
     static __device__ __forceinline__ int grp() { return threadIdx.x / D; }
     static __device__ __forceinline__ int row(int r) { return grp() * NR + r; }
     __device__ __forceinline__ void load(const Params& p, long row0, int valid) {
-        const TI* __restrict__ kp = static_cast<const TI*>(p.k);
-        const TI* __restrict__ qp = static_cast<const TI*>(p.q);
+        // the chunk's rows from uniform bases, per-lane 32-bit offsets
+        const TI* __restrict__ kp = static_cast<const TI*>(p.k) + row0 * D;
+        const TI* __restrict__ qp = static_cast<const TI*>(p.q) + row0 * D;
+        const float* __restrict__ thp = p.theta + row0 * D;
+        const float* __restrict__ gp = p.g + (GATE == kGateVector ? row0 * D : row0);
         const int c = chan();
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const int t = row(r);
             const bool ok = t < valid;
-            const long rr = row0 + (ok ? t : 0);
-            const long e = rr * D + c;
-            const float kk = to_f(kp[e]), qq = to_f(qp[e]), th = p.theta[e];
+            const int rr = ok ? t : 0, e = rr * D + c;
+            const float kk = to_f(kp[e]), qq = to_f(qp[e]), th = thp[e];
             float g = 0.f;
-            if (GATE == kGateScalar) g = p.g[rr];
-            if (GATE == kGateVector) g = p.g[e];
+            if (GATE == kGateScalar) g = gp[rr];
+            if (GATE == kGateVector) g = gp[e];
             k[r] = ok ? kk : 0.f;
             q[r] = ok ? qq : 0.f;
             lr[r] = ok ? g : 0.f;
@@ -242,13 +244,14 @@ template <typename TI, int GATE, int D> struct SeqIn {
         const long row0 = (long)bh * p.T + t0;
         in.load(p, row0, valid);
         const int t = tid / kBV, v = tid % kBV;
-        const float x = to_f(static_cast<const TI*>(tile)[(row0 + min(t, valid - 1)) * D + col0 + v]);
+        const TI* __restrict__ tp = static_cast<const TI*>(tile) + row0 * D + col0;
+        const float x = to_f(tp[min(t, valid - 1) * D + v]);
         blk = t < valid ? x : 0.f;
         const float* mc = mats + ((long)bh * p.NT + n) * kMats;
 #pragma unroll
         for (int j = 0; j < 4; ++j) m[j] = mc[j * kCC + tid];
         const int s = tid % kC;
-        const float b = p.beta[row0 + min(s, valid - 1)];
+        const float b = (p.beta + row0)[min(s, valid - 1)];
         bt = s < valid ? b : 0.f;
     }
 };
@@ -312,6 +315,34 @@ __device__ __forceinline__ f32x4 mma_pair(f32x4 acc, const float* A1, const floa
         }
 #pragma unroll
         for (int j = 0; j < KB; ++j) acc = mma4(s2 * a2[j], b2[j], mma4(s1 * a1[j], b1[j], acc));
+    }
+    return acc;
+}
+
+// As mma_pair for two operands stored [16][K] (neither transposed), with the K
+// slots dealt so that a lane's slots are consecutive: lane group l / 16 takes
+// k = (l / 16) K / 4 + j at step j (the sum does not depend on which step takes
+// which k), so each lane reads its part of a row with 16-byte LDS loads (rows and
+// operands 16-byte aligned: LA, LB multiples of 4).
+template <int K, int LA, int LB>
+__device__ __forceinline__ f32x4 mma_pair_rows(f32x4 acc, const float* A1, const float* B1, float s1,
+                                               const float* A2, const float* B2, float s2) {
+    constexpr int NS = K / 4, KB = NS < 16 ? NS : 16;
+    static_assert(NS % 4 == 0 && NS % KB == 0 && LA % 4 == 0 && LB % 4 == 0, "16-byte rows");
+    const int l = threadIdx.x & 63, li = l & 15, k0 = (l >> 4) * NS;
+#pragma unroll
+    for (int j0 = 0; j0 < NS; j0 += KB) {
+        f32x4 a1[KB / 4], b1[KB / 4], a2[KB / 4], b2[KB / 4];
+#pragma unroll
+        for (int q = 0; q < KB / 4; ++q) {
+            a1[q] = *reinterpret_cast<const f32x4*>(A1 + li * LA + k0 + j0 + 4 * q);
+            a2[q] = *reinterpret_cast<const f32x4*>(A2 + li * LA + k0 + j0 + 4 * q);
+            b1[q] = *reinterpret_cast<const f32x4*>(B1 + li * LB + k0 + j0 + 4 * q);
+            b2[q] = *reinterpret_cast<const f32x4*>(B2 + li * LB + k0 + j0 + 4 * q);
+        }
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+            acc = mma4(s2 * a2[j / 4][j % 4], b2[j / 4][j % 4], mma4(s1 * a1[j / 4][j % 4], b1[j / 4][j % 4], acc));
     }
     return acc;
 }
@@ -427,7 +458,7 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
             const float* ai = it < 2 ? &s.kgi[0][0] : &s.qgi[0][0];
             const float* b1 = it == 1 ? &s.Si[0][0] : &s.Sr[0][0];
             const float* b2 = it == 1 ? &s.Sr[0][0] : &s.Si[0][0];
-            const f32x4 acc = mma_pair<D, LD, LD, false, false>(zero4(), ar, b1, 1.f, ai, b2, it == 1 ? 1.f : -1.f);
+            const f32x4 acc = mma_pair_rows<D, LD, LD>(zero4(), ar, b1, 1.f, ai, b2, it == 1 ? 1.f : -1.f);
             // acc[i] = (t = 4 lk + i, v = li)
             if (it == 0) {
 #pragma unroll
@@ -560,8 +591,7 @@ __global__ __launch_bounds__(kPT) void phase_bwd_state_kernel(Params p, const fl
             constexpr int LD = SeqLdsM<D>::LD, LC = SeqLdsM<D>::LC, LBv = SeqLdsM<D>::LB;
             const float* b1 = it ? &s.Si[0][0] : &s.Sr[0][0];
             const float* b2 = it ? &s.Sr[0][0] : &s.Si[0][0];
-            f32x4 acc = mma_pair<D, LD, LD, false, false>(zero4(), &s.kdr[0][0], b1, 1.f, &s.kdi[0][0], b2,
-                                                          it ? -1.f : 1.f);
+            f32x4 acc = mma_pair_rows<D, LD, LD>(zero4(), &s.kdr[0][0], b1, 1.f, &s.kdi[0][0], b2, it ? -1.f : 1.f);
             acc = mma_one<kC, LC, LBv, true, true>(acc, it ? &s.Pi[0][0] : &s.Pr[0][0], &s.B[0][0], it ? -1.f : 1.f);
             float(*uo)[SeqLdsM<D>::LB] = it ? s.u.R.i : s.u.R.r;
 #pragma unroll
