@@ -504,6 +504,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     using TX = Tiles<VB, C>;   // X_b^T, U_b^T       [v][t]
 
     // ---------------- prologue: gate, K, T, the first d_v block
+    // (the Kaczmarz step's 1 / (||k_t||^2 + eps) of step t = thread index, used only
+    // by the finish: loaded first, branch-free (beta stands in without the step), so
+    // its latency hides behind the whole chunk)
+    const float krn_t = (p.kz ? p.krn + row0 : p.beta + row0)[min((int)threadIdx.x, valid - 1)];
     GateRegs<GATE, C, D> rg;
     rg.load(p.gam + row0 * GW, p.beta + row0, valid);
     RegN<TI, C, D> rK;
@@ -920,7 +924,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             for (int b = 0; b < VB / 16; ++b) s2 += red_b[b * C + t];
             for (int b = 0; b < TO::WM; ++b) s2 += red_r[b * C + t];
             if (kz) {
-                const float rn = p.krn[row0 + t];
+                const float rn = t == (int)threadIdx.x ? krn_t : p.krn[row0 + t];
                 kco[t] = -2.f * s2 * beta_s[t] * rn;
                 s2 *= rn;
             }
