@@ -14,7 +14,9 @@
 //     X = (K E) S0^T,  R = diag(beta) (V - X),  U = T R
 //     O = Re((Q E) S0^T + P U),   S1 = S0 diag(E_L) + U^T (K exp(gam_L - gam))
 // The pair factors exp(gam_t - gam_s) of G and H are formed per pair and
-// channel, so none exceeds 1 in magnitude for g <= 0, at any decay.
+// channel (the forward as exponentials of differences, the per-chunk backward as
+// running products of the per-step factors), so none exceeds 1 in magnitude for
+// g <= 0, at any decay.
 //
 // The reverse pass takes each chunk back with complex cotangents
 // Zb = dL/dRe Z + i dL/dIm Z: for Z = X Y^T, Xb = Zb conj(Y) and Yb = Zb^T conj(X);
@@ -24,7 +26,9 @@
 // each exp as Eb conj(E), and dg, dtheta are the real and imaginary parts of
 // its reverse cumulative sum.
 //
-// Four kernels, all fp32 on the vector ALUs:
+// Four kernels, complex fp32; every product of tiles runs on the fp32 matrix
+// cores as real 16x16x4 products of the real and imaginary parts, the
+// exponentials and the per-element pair terms on the vector ALUs:
 //   phase_prep       grid (chunk, head), every chunk at once: gam, the pairwise
 //                    G and H, T by forward substitution; T, P, G per chunk out.
 //   phase_fwd_state  grid (head, block of 16 state rows), chunks in order: the
@@ -33,12 +37,10 @@
 //                    lambda = T^H Ub, dv and the state cotangent; lambda and the
 //                    cotangent leaving each chunk out.
 //   phase_bwd_chunk  grid (chunk, head), every chunk at once: X and U again, the
-//                    pair cotangents, dq, dk, dbeta, dg, dtheta.
+//                    row sums and pair cotangents, dq, dk, dbeta, dg, dtheta.
 // Row v of S1 depends only on row v of S0 (and row v of dS0 only on row v of
-// dS1), so the sequential kernels split the state into blocks of 16 rows.  There
-// a row belongs to 16 consecutive lanes (one DPP row), each lane D / 16
-// consecutive key channels, and lane j also holds step j of the row's per-step
-// values: sums over the key channels are 16-lane DPP sums.
+// dS1), so the sequential kernels split the state into blocks of 16 rows, which
+// stay in LDS from chunk to chunk.
 #include <hip/hip_runtime.h>
 
 #include "dn.h"
@@ -140,16 +142,6 @@ template <typename TI, int GATE, int D, int NTH = kPT> struct ChunkIn {
             li[r] += oi;
         }
         return {ar, ai};
-    }
-};
-
-// Per-step complex values of W state rows, [C][W + 1] (column v for row v).
-template <int W> struct Rows {
-    float r[kC][W + 1], i[kC][W + 1];
-    __device__ __forceinline__ cf get(int t, int v) const { return {r[t][v], i[t][v]}; }
-    __device__ __forceinline__ void set(int t, int v, cf x) {
-        r[t][v] = x.r;
-        i[t][v] = x.i;
     }
 };
 
