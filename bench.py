@@ -519,8 +519,11 @@ def phase_chunk_bench(args, w0):
     o = torch.empty_like(x["v"])
     hr = torch.empty(w.B, w.H, d, d, device=dev)
     hi = torch.empty_like(hr)
-    st = torch.empty(max(B.dn_phase_states_bytes(sh) // 4, 1), device=dev)
-    nws = B.dn_phase_workspace_bytes(sh, B.DN_PASS_BWD)
+    recompute = args.policy == "recompute"   # the backward reruns the state pass instead of reading saved states
+    st = None if recompute else torch.empty(max(B.dn_phase_states_bytes(sh) // 4, 1), device=dev)
+    nwf = B.dn_phase_workspace_bytes(sh, B.DN_PASS_FWD) if recompute else 0
+    wsf = torch.empty(max(nwf, 1), dtype=torch.uint8, device=dev)
+    nws = B.dn_phase_workspace_bytes(sh, B.DN_PASS_BWD_RECOMPUTE if recompute else B.DN_PASS_BWD)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     gr = {n: torch.empty_like(x[m]) for n, m in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dbeta", "beta"),
                                                   ("dtheta", "theta"))}
@@ -529,14 +532,14 @@ def phase_chunk_bench(args, w0):
 
     def fwd():
         st_ = B.dn_chunk_phase_fwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["h0"], x["h0_im"], o,
-                                   hr, hi, st, None, 0, stream)
+                                   hr, hi, st, wsf if recompute else None, nwf, stream)
         if st_ != B.DN_OK:
             raise B.DnError(st_, B.dn_last_error())
 
     def bwd():
-        st_ = B.dn_chunk_phase_bwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["do"], x["dhT"],
-                                   x["dhT_im"], st, gr["dq"], gr["dk"], gr["dv"], gr["dbeta"], gr["dg"], gr["dtheta"],
-                                   gr["dh0_re"], gr["dh0_im"], ws, nws, stream)
+        st_ = B.dn_chunk_phase_bwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["h0"], x["h0_im"],
+                                   x["do"], x["dhT"], x["dhT_im"], st, gr["dq"], gr["dk"], gr["dv"], gr["dbeta"],
+                                   gr["dg"], gr["dtheta"], gr["dh0_re"], gr["dh0_im"], ws, nws, stream)
         if st_ != B.DN_OK:
             raise B.DnError(st_, B.dn_last_error())
 
@@ -590,7 +593,8 @@ def phase_chunk_bench(args, w0):
         "bwd_ms": round(bms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": f"phase-controlled gate, chunks of 16: gate={w.gate} B={w.B} H={w.H} T={w.T} d={d}, "
-                               f"fp32 arithmetic (fp32 matrix cores and vector ALUs)", "global_batch": w.B,
+                               f"fp32 arithmetic (fp32 matrix cores and vector ALUs), "
+                               f"{'recomputed' if recompute else 'saved'} states", "global_batch": w.B,
                    "seq_len": w.T, "heads": w.H, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "kernels": per_kernel,
         "step_hbm": {"algorithmic_bytes": int(by), "achieved_gbs": round(by / (ms / 1e3) / 1e9, 1),

@@ -84,7 +84,7 @@ def lib():
     L.dn_phase_workspace_bytes.restype = sz
     L.dn_chunk_phase_fwd.argtypes = [sp] + [vp] * 13 + [sz, vp]
     L.dn_chunk_phase_fwd.restype = i32
-    L.dn_chunk_phase_bwd.argtypes = [sp] + [vp] * 19 + [sz, vp]
+    L.dn_chunk_phase_bwd.argtypes = [sp] + [vp] * 21 + [sz, vp]
     L.dn_chunk_phase_bwd.restype = i32
     L.dn_status_string.argtypes = [i32]
     L.dn_status_string.restype = ctypes.c_char_p
@@ -233,13 +233,14 @@ def dn_chunk_phase_fwd(shape, q, k, v, beta, g, theta, h0_re, h0_im, o, hT_re, h
                                     _ptr(ws), ws_bytes, _stream(stream))
 
 
-def dn_chunk_phase_bwd(shape, q, k, v, beta, g, theta, dout, dhT_re, dhT_im, states, dq, dk, dv, dbeta, dg, dtheta,
-                       dh0_re, dh0_im, ws=None, ws_bytes=0, stream=None) -> int:
-    """Raw call; returns the dn_status (no exception)."""
+def dn_chunk_phase_bwd(shape, q, k, v, beta, g, theta, h0_re, h0_im, dout, dhT_re, dhT_im, states, dq, dk, dv, dbeta,
+                       dg, dtheta, dh0_re, dh0_im, ws=None, ws_bytes=0, stream=None) -> int:
+    """Raw call; returns the dn_status (no exception).  states NULL: recompute
+    (h0_re / h0_im used, workspace of DN_PASS_BWD_RECOMPUTE)."""
     return lib().dn_chunk_phase_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(theta),
-                                    _ptr(dout), _ptr(dhT_re), _ptr(dhT_im), _ptr(states), _ptr(dq), _ptr(dk), _ptr(dv),
-                                    _ptr(dbeta), _ptr(dg), _ptr(dtheta), _ptr(dh0_re), _ptr(dh0_im), _ptr(ws),
-                                    ws_bytes, _stream(stream))
+                                    _ptr(h0_re), _ptr(h0_im), _ptr(dout), _ptr(dhT_re), _ptr(dhT_im), _ptr(states),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbeta), _ptr(dg), _ptr(dtheta), _ptr(dh0_re),
+                                    _ptr(dh0_im), _ptr(ws), ws_bytes, _stream(stream))
 
 
 # ------------------------------------------------------------------ convenience
@@ -429,23 +430,28 @@ def chunk_phase_fwd(q, k, v, beta, g, theta, h0_re=None, h0_im=None, gate=None, 
     return o, hT_re, hT_im, states
 
 
-def chunk_phase_bwd(q, k, v, beta, g, theta, do, dhT_re, dhT_im, states, gate=None, stream=None):
-    """Backward of chunk_phase_fwd from its saved states.  Returns a dict dq, dk,
-    dv, dbeta, dg (None without a gate), dtheta, dh0_re, dh0_im."""
-    _validate(q, k, v, beta, g, do=do, dhT=dhT_re, state_im=dhT_im, theta=theta)
+def chunk_phase_bwd(q, k, v, beta, g, theta, do, dhT_re, dhT_im, states, h0_re=None, h0_im=None, gate=None,
+                    stream=None):
+    """Backward of chunk_phase_fwd from its saved states, or (states None) with the
+    states recomputed from h0_re / h0_im.  Returns a dict dq, dk, dv, dbeta, dg
+    (None without a gate), dtheta, dh0_re, dh0_im."""
+    _validate(q, k, v, beta, g, h0_re, do=do, dhT=dhT_re, state_im=dhT_im, theta=theta)
+    if h0_im is not None:
+        _validate(q, k, v, beta, g, h0_im)
     B, H, T, dk = q.shape
     sh = make_shape(B, H, T, dk, v.shape[-1], 16, q.dtype, gate if gate is not None else _gate_kind(g, dk))
-    if states is None or states.dtype != torch.float32 or states.numel() * 4 < dn_phase_states_bytes(sh):
+    if states is not None and (states.dtype != torch.float32 or states.numel() * 4 < dn_phase_states_bytes(sh)):
         raise ValueError("states must be the float32 buffer chunk_phase_fwd saved")
     out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
            "dbeta": torch.empty_like(beta), "dg": None if g is None else torch.empty_like(g),
            "dtheta": torch.empty_like(theta),
            "dh0_re": torch.empty(B, H, v.shape[-1], dk, dtype=torch.float32, device=q.device)}
     out["dh0_im"] = torch.empty_like(out["dh0_re"])
-    nws = dn_phase_workspace_bytes(sh, DN_PASS_BWD)
+    nws = dn_phase_workspace_bytes(sh, DN_PASS_BWD if states is not None else DN_PASS_BWD_RECOMPUTE)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
-    _check(dn_chunk_phase_bwd(sh, q, k, v, beta, g, theta, do, dhT_re, dhT_im, states, out["dq"], out["dk"], out["dv"],
-                              out["dbeta"], out["dg"], out["dtheta"], out["dh0_re"], out["dh0_im"], ws, nws, stream))
+    _check(dn_chunk_phase_bwd(sh, q, k, v, beta, g, theta, h0_re, h0_im, do, dhT_re, dhT_im, states, out["dq"],
+                              out["dk"], out["dv"], out["dbeta"], out["dg"], out["dtheta"], out["dh0_re"],
+                              out["dh0_im"], ws, nws, stream))
     return out
 
 

@@ -394,7 +394,8 @@ dn_status phase_shape(const dn_shape* s, dn::Problem* pr, Dims* d) {
 
 // Regions of the phase gate's buffers (fp32, each rounded up to 256 bytes):
 // saved = chunk states, then the per-chunk T, P, G; backward workspace = lambda,
-// then the state cotangent leaving each chunk.
+// then the state cotangent leaving each chunk (recomputing: then the saved
+// buffer's regions).
 struct PhaseSizes {
     size_t st, mats, lam, ds1;
 };
@@ -423,6 +424,7 @@ size_t dn_phase_workspace_bytes(const dn_shape* shape, int pass) {
     const PhaseSizes z = phase_sizes(d);
     if (pass == DN_PASS_FWD) return z.mats;
     if (pass == DN_PASS_BWD) return z.lam + z.ds1;
+    if (pass == DN_PASS_BWD_RECOMPUTE) return z.lam + z.ds1 + z.st + z.mats;
     return 0;
 }
 
@@ -488,10 +490,10 @@ dn_status dn_chunk_phase_fwd(const dn_shape* shape, const void* q, const void* k
 }
 
 dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
-                             const float* g, const float* theta, const void* dout, const float* dhT_re,
-                             const float* dhT_im, const float* states, void* dq, void* dk, void* dv, float* dbeta,
-                             float* dg, float* dtheta, float* dh0_re, float* dh0_im, void* ws, size_t ws_bytes,
-                             void* stream) {
+                             const float* g, const float* theta, const float* h0_re, const float* h0_im,
+                             const void* dout, const float* dhT_re, const float* dhT_im, const float* states, void* dq,
+                             void* dk, void* dv, float* dbeta, float* dg, float* dtheta, float* dh0_re, float* dh0_im,
+                             void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = '\0';
     dn::Problem pr;
     Dims d;
@@ -499,7 +501,9 @@ dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k
     const size_t nk = d.BH * d.T * d.dk * d.E, nv = d.BH * d.T * d.dv * d.E, nb = d.BH * d.T * 4;
     const size_t ng = pr.gate == DN_GATE_NONE ? 0 : d.BH * d.T * d.gw * 4, nth = d.BH * d.T * d.dk * 4;
     const PhaseSizes z = phase_sizes(d);
-    const size_t ns = d.BH * d.dv * d.dk * 4, nst = z.st + z.mats, nws = z.lam + z.ds1;
+    const size_t ns = d.BH * d.dv * d.dk * 4, nst = z.st + z.mats;
+    const bool recompute = states == nullptr;   // the states and matrices go to the workspace, after lambda, dS1
+    const size_t nws = z.lam + z.ds1 + (recompute ? nst : 0);
     if (pr.gate == DN_GATE_NONE && (g || dg)) return fail(DN_ERR_INVALID, "g and dg must be NULL without a gate");
     if (ws_bytes < nws) return fail(DN_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, nws);
     DN_TRY(need(ws, nws, "workspace"));
@@ -510,7 +514,6 @@ dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k
     DN_TRY(need(g, ng, "g"));
     DN_TRY(need(theta, nth, "theta"));
     DN_TRY(need(dout, nv, "dout"));
-    DN_TRY(need(states, nst, "states"));
     DN_TRY(need(dq, nk, "dq"));
     DN_TRY(need(dk, nk, "dk"));
     DN_TRY(need(dv, nv, "dv"));
@@ -523,6 +526,8 @@ dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k
                           {"beta", beta, nb, false},
                           {"g", g, ng, false},
                           {"theta", theta, nth, false},
+                          {"h0_re", h0_re, recompute ? ns : 0, false},
+                          {"h0_im", h0_im, recompute ? ns : 0, false},
                           {"dout", dout, nv, false},
                           {"dhT_re", dhT_re, ns, false},
                           {"dhT_im", dhT_im, ns, false},
@@ -560,10 +565,17 @@ dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k
     p.dh0 = dh0_re;
     p.dh0_im = dh0_im;
     dn::PhaseBufs f{};
-    f.states = const_cast<float*>(states);
+    f.states = recompute ? reinterpret_cast<float*>(static_cast<char*>(ws) + z.lam + z.ds1) : const_cast<float*>(states);
     f.mats = reinterpret_cast<float*>(reinterpret_cast<char*>(f.states) + z.st);
     f.lam = static_cast<float*>(ws);
     f.dS1 = reinterpret_cast<float*>(static_cast<char*>(ws) + z.lam);
+    if (recompute) {   // the forward's states and matrices again (no output)
+        dn::Params pf = p;
+        pf.h0 = h0_re;
+        pf.h0_im = h0_im;
+        const hipError_t e = dn::launch_phase(pr, pf, f, false, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    }
     const hipError_t e = dn::launch_phase(pr, p, f, true, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return DN_OK;

@@ -520,7 +520,7 @@ __global__ __launch_bounds__(kPT) void phase_fwd_state_kernel(Params p, const fl
 #pragma unroll
             for (int i = 0; i < 4; ++i) so[4 * lk + i][(it >> 1) * 16 + li] = s1[j][i];
         }
-        {
+        if (out) {   // (none when the backward recomputes the states)
             const int t = tid / kBV, vv = tid % kBV;
             if (t < valid) out[(row0 + t) * D + v0 + vv] = from_f<TI>(s.Os[t][vv]);
         }

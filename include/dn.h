@@ -278,7 +278,8 @@ dn_status dn_recurrent_phase_fwd(const dn_shape* shape, const void* q, const voi
  *            chunk [B][H][NT][2][dv][dk] (real part, then imaginary; NT =
  *            ceil(T / 16)), then, from the next 256-byte boundary, per chunk
  *            [B][H][NT][6][16][16] the matrices (I + A)^{-1}, P and G (real,
- *            imaginary, each); written by the forward, required by the backward
+ *            imaginary, each); written by the forward for the backward, which
+ *            recomputes them (from h0_re, h0_im) when it gets NULL
  *   backward: the vector-Jacobian products of
  *            L = <o, dout> + <hT_re, dhT_re> + <hT_im, dhT_im>  (dhT_* NULL = zero):
  *            dq, dk, dv (io), dbeta, dg (NULL iff no gate; layout of g), dtheta
@@ -286,7 +287,9 @@ dn_status dn_recurrent_phase_fwd(const dn_shape* shape, const void* q, const voi
  *   ws     : device scratch of ws_bytes >= dn_phase_workspace_bytes(shape, pass):
  *            the forward needs it only when states is NULL (DN_PASS_FWD: the
  *            per-chunk matrices), the backward always (DN_PASS_BWD: lambda and
- *            the state cotangent of each chunk)
+ *            the state cotangent of each chunk; DN_PASS_BWD_RECOMPUTE, when
+ *            states is NULL: those, then the recomputed states and matrices in
+ *            the layout of the saved buffer)
  * Validation and errors as for dn_chunk_fwd.
  */
 size_t dn_phase_states_bytes(const dn_shape* shape);
@@ -295,10 +298,10 @@ dn_status dn_chunk_phase_fwd(const dn_shape* shape, const void* q, const void* k
                              const float* g, const float* theta, const float* h0_re, const float* h0_im, void* o,
                              float* hT_re, float* hT_im, float* states, void* ws, size_t ws_bytes, void* stream);
 dn_status dn_chunk_phase_bwd(const dn_shape* shape, const void* q, const void* k, const void* v, const float* beta,
-                             const float* g, const float* theta, const void* dout, const float* dhT_re,
-                             const float* dhT_im, const float* states, void* dq, void* dk, void* dv, float* dbeta,
-                             float* dg, float* dtheta, float* dh0_re, float* dh0_im, void* ws, size_t ws_bytes,
-                             void* stream);
+                             const float* g, const float* theta, const float* h0_re, const float* h0_im,
+                             const void* dout, const float* dhT_re, const float* dhT_im, const float* states, void* dq,
+                             void* dk, void* dv, float* dbeta, float* dg, float* dtheta, float* dh0_re, float* dh0_im,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* dn_status_string(dn_status status);

@@ -246,7 +246,8 @@ def test_validation_errors_recurrent_phase():
 
 def test_validation_errors_chunk_phase():
     """The chunkwise phase-controlled gate: chunks of 16, d in {16, 32, 64, 128}, no Kaczmarz step,
-    theta required, the backward needs the forward's states."""
+    theta required; the backward takes the forward's states or (states NULL) recomputes them in a
+    larger workspace."""
     def sh(**over):
         d = dict(B=1, H=2, T=40, dk=32, dv=32, C=16, dtype="fp32", gate="vector")
         d.update(over)
@@ -260,21 +261,23 @@ def test_validation_errors_chunk_phase():
                                     a["h0_im"], a["o"], a["hT_re"], a["hT_im"], a["states"], a["ws"], a["ws_bytes"], 0)
 
     def bwd(s, **over):
-        a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, theta=FAKE * 6, dout=FAKE * 8,
-                 dhT_re=None, dhT_im=None, states=FAKE * 9, dq=FAKE * 10, dk=FAKE * 11, dv=FAKE * 12,
-                 dbeta=FAKE * 13, dg=FAKE * 14, dtheta=FAKE * 15, dh0_re=None, dh0_im=None, ws=FAKE * 16,
-                 ws_bytes=1 << 30)
+        a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, beta=FAKE * 4, g=FAKE * 5, theta=FAKE * 6, h0_re=None,
+                 h0_im=None, dout=FAKE * 8, dhT_re=None, dhT_im=None, states=FAKE * 9, dq=FAKE * 10, dk=FAKE * 11,
+                 dv=FAKE * 12, dbeta=FAKE * 13, dg=FAKE * 14, dtheta=FAKE * 15, dh0_re=None, dh0_im=None,
+                 ws=FAKE * 16, ws_bytes=1 << 30)
         a.update(over)
-        return B.dn_chunk_phase_bwd(s, *(a[n] for n in ("q", "k", "v", "beta", "g", "theta", "dout", "dhT_re",
-                                                        "dhT_im", "states", "dq", "dk", "dv", "dbeta", "dg",
-                                                        "dtheta", "dh0_re", "dh0_im", "ws", "ws_bytes")), 0)
+        return B.dn_chunk_phase_bwd(s, *(a[n] for n in ("q", "k", "v", "beta", "g", "theta", "h0_re", "h0_im",
+                                                        "dout", "dhT_re", "dhT_im", "states", "dq", "dk", "dv",
+                                                        "dbeta", "dg", "dtheta", "dh0_re", "dh0_im", "ws",
+                                                        "ws_bytes")), 0)
 
     al = lambda x: (x + 255) // 256 * 256
     # NT = ceil(40 / 16) = 3: chunk states, then T, P, G per chunk (complex, 16 x 16)
     assert B.dn_phase_states_bytes(sh()) == al(1 * 2 * 3 * 2 * 32 * 32 * 4) + al(1 * 2 * 3 * 6 * 16 * 16 * 4)
     assert B.dn_phase_workspace_bytes(sh(), B.DN_PASS_FWD) == al(1 * 2 * 3 * 6 * 16 * 16 * 4)
     assert B.dn_phase_workspace_bytes(sh(), B.DN_PASS_BWD) == al(2 * 3 * 2 * 32 * 16 * 4) + al(2 * 3 * 2 * 32 * 32 * 4)
-    assert B.dn_phase_workspace_bytes(sh(), B.DN_PASS_BWD_RECOMPUTE) == 0
+    nbwd = al(2 * 3 * 2 * 32 * 16 * 4) + al(2 * 3 * 2 * 32 * 32 * 4)
+    assert B.dn_phase_workspace_bytes(sh(), B.DN_PASS_BWD_RECOMPUTE) == nbwd + B.dn_phase_states_bytes(sh())
     assert B.dn_phase_states_bytes(sh(C=64)) == 0
     assert B.dn_phase_workspace_bytes(sh(C=64), B.DN_PASS_BWD) == 0
     assert fwd(sh(C=64)) == B.DN_ERR_UNSUPPORTED
@@ -287,7 +290,9 @@ def test_validation_errors_chunk_phase():
     assert fwd(sh(gate="none")) == B.DN_ERR_INVALID                     # g given without a gate
     assert fwd(sh(), o=FAKE * 3) == B.DN_ERR_INVALID                    # output aliases v
     assert fwd(sh(), hT_re=FAKE * 20, hT_im=FAKE * 20) == B.DN_ERR_INVALID
-    assert bwd(sh(), states=None) == B.DN_ERR_INVALID
+    # states NULL: the workspace must also hold the recomputed states and matrices
+    assert bwd(sh(), states=None, ws_bytes=nbwd) == B.DN_ERR_WORKSPACE
+    assert bwd(sh(), states=None, h0_re=FAKE * 10) == B.DN_ERR_INVALID   # h0 (read to recompute) aliases dq
     assert fwd(sh(), ws=None) == B.DN_ERR_INVALID                       # no states: the matrices need a workspace
     assert fwd(sh(), ws_bytes=100) == B.DN_ERR_WORKSPACE
     assert fwd(sh(), o=FAKE * 16) == B.DN_ERR_INVALID                   # output aliases the workspace

@@ -125,10 +125,16 @@ def test_chunk_phase_stays_in_bounds(gate, dtype, d):
     gr["dg"] = None if x["g"] is None else g.like("dg", x["g"])
     nws = B.dn_phase_workspace_bytes(sh, B.DN_PASS_BWD)
     ws = g.buf("ws", nws)
-    _ok(B.dn_chunk_phase_bwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["do"], x["dhT"],
-                             x["dhT_im"], states, gr["dq"], gr["dk"], gr["dv"], gr["dbeta"], gr["dg"], gr["dtheta"],
-                             gr["dh0_re"], gr["dh0_im"], ws, nws))
+    _ok(B.dn_chunk_phase_bwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["h0"], x["h0_im"],
+                             x["do"], x["dhT"], x["dhT_im"], states, gr["dq"], gr["dk"], gr["dv"], gr["dbeta"],
+                             gr["dg"], gr["dtheta"], gr["dh0_re"], gr["dh0_im"], ws, nws))
     g.check(f"phase {gate} {dtype} d={d} backward")
+    nwr = B.dn_phase_workspace_bytes(sh, B.DN_PASS_BWD_RECOMPUTE)   # the backward recomputing the states
+    wsr = g.buf("ws_recompute", nwr)
+    _ok(B.dn_chunk_phase_bwd(sh, x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["h0"], x["h0_im"],
+                             x["do"], x["dhT"], x["dhT_im"], None, gr["dq"], gr["dk"], gr["dv"], gr["dbeta"],
+                             gr["dg"], gr["dtheta"], gr["dh0_re"], gr["dh0_im"], wsr, nwr))
+    g.check(f"phase {gate} {dtype} d={d} backward, recomputed states")
     _same_inputs(x, ref, f"phase {gate}")
 
 

@@ -5,7 +5,8 @@ reverse mode): o, the complex final state and every gradient (q, k, v, beta,
 g, theta, the complex initial state) at nonzero phase, for every gate type, both
 I/O types, d in {16, 32, 64, 128} and ragged sequences; strong decay; at zero phase
 the chunkwise real path (KDA / GDN / DeltaNet); the recurrent phase entry point;
-zero steps."""
+zero steps; the backward recomputing the states equals the one from the saved
+buffer bitwise."""
 import numpy as np
 import pytest
 import torch
@@ -167,3 +168,24 @@ def test_chunk_phase_random_shapes(case):
     w = W.custom(Bn, H, T, d, d, 16, gate, dtype, h0_std=h0, seed=seed, phase=True)
     inp = W.make_inputs(w)
     _compare(_gpu(inp), _oracle(inp), TOL[dtype], f"phase sweep {case}")
+
+
+@pytest.mark.parametrize("gate,dtype,T,d", [("vector", "bf16", 16 * 5 + 3, 64), ("scalar", "fp32", 16 * 2 + 9, 128),
+                                             ("none", "bf16", 16 * 3, 32), ("vector", "fp32", 1, 16)])
+def test_backward_recomputing_the_states_matches(gate, dtype, T, d):
+    """Without the saved buffer the backward reruns the forward's per-chunk products and
+    state pass from h0 into its workspace: every gradient is bitwise the one from the
+    saved states."""
+    w, inp = _case(gate, dtype, 2, 2, T, d, seed=83 + T)
+    x = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
+    o, hr, hi, st = B.chunk_phase_fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["h0"], x["h0_im"])
+    a = B.chunk_phase_bwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["do"], x["dhT"], x["dhT_im"], st)
+    b = B.chunk_phase_bwd(x["q"], x["k"], x["v"], x["beta"], x["g"], x["theta"], x["do"], x["dhT"], x["dhT_im"], None,
+                          h0_re=x["h0"], h0_im=x["h0_im"])
+    torch.cuda.synchronize()
+    for n in a:
+        if a[n] is None:
+            assert b[n] is None
+            continue
+        assert torch.equal(a[n], b[n]), n
+    say(f"phase recompute {gate} {dtype} T={T} d={d}: bitwise equal")
