@@ -6,7 +6,7 @@ g, theta, the complex initial state) at nonzero phase, for every gate type, both
 I/O types, d in {16, 32, 64, 128} and ragged sequences; strong decay; at zero phase
 the chunkwise real path (KDA / GDN / DeltaNet); the recurrent phase entry point;
 zero steps; the backward recomputing the states equals the one from the saved
-buffer bitwise."""
+buffer bitwise; sampled heads at the benchmark's full shape."""
 import numpy as np
 import pytest
 import torch
@@ -189,3 +189,28 @@ def test_backward_recomputing_the_states_matches(gate, dtype, T, d):
             continue
         assert torch.equal(a[n], b[n]), n
     say(f"phase recompute {gate} {dtype} T={T} d={d}: bitwise equal")
+
+
+def test_chunk_phase_full_size_sampled_heads():
+    """The benchmark's shape and launch configuration (bench.py --phase-chunk on the KDA
+    workload: B=4, H=16, T=8192, d=128, per-channel gate, bf16, saved states): o, the
+    final state and every gradient of two sampled heads (the first and the last) against
+    the oracle run on those heads alone (heads are independent)."""
+    w0 = W.CONFIGS["kda_bf16"]
+    w = W.custom(w0.B, w0.H, w0.T, w0.dk, w0.dk, 16, w0.gate, w0.dtype, h0_std=0.5, seed=w0.seed, phase=True)
+    say(f"[phase full size] {w.describe()}")
+    inp = W.make_inputs(w)
+    d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
+    o, hr, hi, st = B.chunk_phase_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["theta"], d["h0"], d["h0_im"])
+    gr = B.chunk_phase_bwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["theta"], d["do"], d["dhT"], d["dhT_im"], st)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    out = {"o": o, "hT_re": hr, "hT_im": hi, **gr}
+    gpu = {n: W.to_f64(t, heads) for n, t in out.items()}
+    del d, st, out, gr
+    f = {n: W.to_f64(t, heads) for n, t in inp.items()}
+    ob, S = sfda.forward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["theta"], f["h0"], f["h0_im"])
+    ref = {"o": ob, "hT_re": S.real, "hT_im": S.imag,
+           **sfda.backward(f["q"], f["k"], f["v"], f["beta"], f["g"], f["theta"], f["h0"], f["h0_im"], f["do"],
+                           f["dhT"], f["dhT_im"])}
+    _compare(gpu, ref, TOL[w.dtype], f"phase full size, heads {heads}")
