@@ -680,6 +680,49 @@ template <typename T, int ROWS, int COLS> struct RegN {
             *reinterpret_cast<uint4*>(l2 + row * ldl + c0) = o[2][i];
         }
     }
+    // As store2i / store3i, into register tiles of the same shape instead of LDS
+    // (rows >= valid as zero; the outputs then store as they are).
+    template <class F> __device__ __forceinline__ void form2i(RegN& o0, RegN& o1, F f) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int row = idx_of(i) / VPR;
+            const uint4 ra = pin(r[i]);
+            const T* sa = reinterpret_cast<const T*>(&ra);
+            T* d0 = reinterpret_cast<T*>(&o0.r[i]);
+            T* d1 = reinterpret_cast<T*>(&o1.r[i]);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                float y[2];
+                f(i, e, to_f(sa[e]), y);
+                const bool ok = row < valid_;
+                d0[e] = from_f<T>(ok ? y[0] : 0.f);
+                d1[e] = from_f<T>(ok ? y[1] : 0.f);
+            }
+        }
+        o0.valid_ = o1.valid_ = ROWS;
+    }
+    template <class F> __device__ __forceinline__ void form3i(const RegN& b, RegN& o0, RegN& o1, RegN& o2, F f) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int row = idx_of(i) / VPR;
+            const uint4 ra = pin(r[i]), rb = pin(b.r[i]);
+            const T* sa = reinterpret_cast<const T*>(&ra);
+            const T* sb = reinterpret_cast<const T*>(&rb);
+            T* d0 = reinterpret_cast<T*>(&o0.r[i]);
+            T* d1 = reinterpret_cast<T*>(&o1.r[i]);
+            T* d2 = reinterpret_cast<T*>(&o2.r[i]);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) {
+                float y[3];
+                f(i, e, to_f(sa[e]), to_f(sb[e]), y);
+                const bool ok = row < valid_;
+                d0[e] = from_f<T>(ok ? y[0] : 0.f);
+                d1[e] = from_f<T>(ok ? y[1] : 0.f);
+                d2[e] = from_f<T>(ok ? y[2] : 0.f);
+            }
+        }
+        o0.valid_ = o1.valid_ = o2.valid_ = ROWS;
+    }
     // Three tiles from this one (a) and another of the same shape (b) in one
     // two-phase pass: f(row, col, a, b, y) fills y[0..2] for tiles l0, l1, l2, so
     // a factor the three share (a per-element gate) is computed once.

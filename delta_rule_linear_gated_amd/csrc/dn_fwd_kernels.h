@@ -677,22 +677,65 @@ __device__ __forceinline__ void fwd_state_body(const Params& p, int wg, float* _
     RegN<TI, OUTPUT ? C : 16, OUTPUT ? C : 16> rP;
     GateRegs<GATE, C, DK, false> rg;
     VecGate<TI, C, DK> vg;   // vector gate
-    auto prefetch = [&](int n) {
+    // Vector gate: the chunk's gated tiles K Gam, Q Gam, K Gam_C / Gam and e^{gam_C}
+    // are formed in registers at the end of the previous iteration (beside its
+    // matrix-core work, the exponentials off the commit's path), from K, Q and the
+    // gate loaded one chunk before that; the commit only stores them.
+    using VG = VecGate<TI, C, DK>;
+    RegN<TI, C, VEC ? DK : 8> pkg, pqg, pkd;
+    float pec[VEC ? VG::VW : 1];
+    auto prefetch_kq = [&](int n) {   // vector gate: K, Q and the gate of chunk n
+        if constexpr (VEC) {
+            const int t0 = n * C;
+            const int valid = min(C, p.T - t0);
+            const long row0 = (long)bh * p.T + t0;
+            vg.load(p.gam + row0 * GW, valid);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (OUTPUT) rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
+            rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
+        }
+    };
+    auto form = [&]() {   // vector gate: the tiles of the chunk in rq / rk / vg
+        if constexpr (VEC) {
+            if constexpr (OUTPUT) {
+                rq.form3i(rk, pqg, pkg, pkd, [&](int i, int e, float q, float k, float* y) {
+                    const float ge = vg.g[i][e];
+                    const float f = fexp(ge);
+                    y[0] = q * f;
+                    y[1] = k * f;
+                    y[2] = k * fexp(vg.gc[e] - ge);
+                });
+            } else {
+                rk.form2i(pkg, pkd, [&](int i, int e, float k, float* y) {
+                    const float ge = vg.g[i][e];
+                    y[0] = k * fexp(ge);
+                    y[1] = k * fexp(vg.gc[e] - ge);
+                });
+            }
+#pragma unroll
+            for (int e = 0; e < VG::VW; ++e) pec[e] = fexp(vg.gc[e]);
+        }
+    };
+    auto prefetch = [&](int n) {   // the rest of chunk n (everything without a vector gate)
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
         const long row0 = (long)bh * p.T + t0;
         const long cc = ((long)bh * p.NT + n) * C * C;
         rg.load(p.gam + row0 * GW, p.beta + row0, valid);
-        if constexpr (VEC) vg.load(p.gam + row0 * GW, valid);
         __builtin_amdgcn_sched_barrier(0);   // gate first, then the tiles, in order (see RegN)
-        if constexpr (OUTPUT) rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);   // Q only feeds O
-        rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
+        if constexpr (!VEC) {
+            if constexpr (OUTPUT) rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);   // Q only feeds O
+            rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
+        }
         rv.load(static_cast<const TI*>(p.v) + row0 * DVr + vcol, DVr, valid);
         if (trans) rv.valid_ = 0;   // stores as zero
         rT.load(static_cast<const TI*>(p.Tm) + cc, C, C);
         if constexpr (OUTPUT) rP.load(static_cast<const TI*>(p.Pm) + cc, C, C);
     };
+    prefetch_kq(n0);
     prefetch(n0);
+    form();
+    prefetch_kq(n0 + 1 < n1 ? n0 + 1 : n0);
 
     // X^T, U^T and O^T tiles [v][t]: a lane holds 4 consecutive v of one row t of
     // R, U and O (one vector LDS access each)
@@ -710,23 +753,15 @@ __device__ __forceinline__ void fwd_state_body(const Params& p, int wg, float* _
         // chunk ordered these writes after its reads; nothing below reads the gate
         // just committed before the next barrier)
         rg.commit(rowf, gam_s, beta_s);
-        if constexpr (VEC) vg.commit_last(egc);
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
-        if (VEC && OUTPUT) {
-            // Q e^{gam}, K e^{gam} (one exp) and K e^{gam_C - gam}, from the gate registers
-            rq.store3i(rk, Qg, Kg, Kd, LDK, [&](int i, int e, float q, float k, float* y) {
-                const float ge = vg.g[i][e];
-                const float f = fexp(ge);
-                y[0] = q * f;
-                y[1] = k * f;
-                y[2] = k * fexp(vg.gc[e] - ge);
-            });
-        } else if (VEC) {
-            rk.store2i(Kg, Kd, LDK, [&](int i, int e, float k, float* y) {
-                const float ge = vg.g[i][e];
-                y[0] = k * fexp(ge);
-                y[1] = k * fexp(vg.gc[e] - ge);
-            });
+        if constexpr (VEC) {   // the tiles formed last iteration (Q e^{gam}, K e^{gam}, K e^{gam_C - gam})
+            if ((int)threadIdx.x < VG::VPR) {
+#pragma unroll
+                for (int e = 0; e < VG::VW; ++e) egc[VG::col0() + e] = pec[e];
+            }
+            if constexpr (OUTPUT) pqg.store(Qg, LDK);
+            pkg.store(Kg, LDK);
+            pkd.store(Kd, LDK);
         } else {
             if constexpr (OUTPUT) rq.store(Qg, LDK);
             rk.store(Kg, LDK);
@@ -808,6 +843,10 @@ __device__ __forceinline__ void fwd_state_body(const Params& p, int wg, float* _
             }
         }
         gemm<TI, DK, BV, C, true, true>(S, VEC ? Kd : Kg, LDK, SCA ? Ud : Ub, LDV);
+        if constexpr (VEC) {   // the next chunk's tiles, then the inputs of the one after
+            form();
+            prefetch_kq(n + 2 < n1 ? n + 2 : n1 - 1);
+        }
         __syncthreads();
     }
     if (OUTPUT && n1 > n0) {
