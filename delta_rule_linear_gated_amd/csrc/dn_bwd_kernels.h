@@ -131,26 +131,60 @@ __device__ __forceinline__ void bwd_state_body(const Params& p, int wg, float* _
     // scalar gate: gam of the rows of this thread's dO vectors (dO e^{gam} is formed
     // from registers, so the commit needs no barrier between the gate and the tiles)
     float gdo[SCA ? RDO::PER : 1];
-    auto prefetch = [&](int n) {
+    // Vector gate: the chunk's gated tiles K e^{gam_C - gam}, -K e^{gam}, Q e^{gam}
+    // and e^{gam_C}, formed in registers at the end of the previous iteration from
+    // K, Q and the gate loaded one chunk before that (as in the forward state pass).
+    using VG = VecGate<TI, C, DK>;
+    RegN<TI, C, VEC ? DK : 8> pkd, pkn, pqg;
+    float pec[VEC ? VG::VW : 1];
+    auto prefetch_kq = [&](int n) {   // vector gate: K, Q and the gate of chunk n
+        if constexpr (VEC) {
+            const int t0 = n * C;
+            const int valid = min(C, p.T - t0);
+            const long row0 = (long)bh * p.T + t0;
+            vg.load(p.gam + row0 * GW, valid);
+            __builtin_amdgcn_sched_barrier(0);
+            rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
+            rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
+        }
+    };
+    auto form = [&]() {   // vector gate: the tiles of the chunk in rq / rk / vg
+        if constexpr (VEC) {
+            rk.form3i(rq, pkd, pkn, pqg, [&](int i, int e, float k, float q, float* y) {
+                const float ge = vg.g[i][e];
+                const float f = fexp(ge);
+                y[0] = k * fexp(vg.gc[e] - ge);
+                y[1] = -k * f;
+                y[2] = q * f;
+            });
+#pragma unroll
+            for (int e = 0; e < VG::VW; ++e) pec[e] = fexp(vg.gc[e]);
+        }
+    };
+    auto prefetch = [&](int n) {   // the rest of chunk n (everything without a vector gate)
         const int t0 = n * C;
         const int valid = min(C, p.T - t0);
         const long row0 = (long)bh * p.T + t0;
         const long cc = ((long)bh * p.NT + n) * C * C;
         rg.load(p.gam + row0 * GW, p.beta + row0, valid);
-        if constexpr (VEC) vg.load(p.gam + row0 * GW, valid);
         if constexpr (SCA) {
 #pragma unroll
             for (int i = 0; i < RDO::PER; ++i) gdo[i] = p.gam[row0 + min(RDO::idx_of(i) / RDO::VPR, valid - 1)];
         }
         __builtin_amdgcn_sched_barrier(0);   // gate first, then the tiles, in order (see RegN)
-        rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
-        rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
+        if constexpr (!VEC) {
+            rq.load(static_cast<const TI*>(p.q) + row0 * DK, DK, valid);
+            rk.load(static_cast<const TI*>(p.k) + row0 * DK, DK, valid);
+        }
         rdo.load(static_cast<const TI*>(p.dout) + row0 * DVr + vcol, DVr, valid);
         if (trans) rdo.valid_ = 0;   // stores as zero
         rP.load(static_cast<const TI*>(p.Pm) + cc, C, C);
         rT.load(static_cast<const TI*>(p.Tm) + cc, C, C);
     };
+    prefetch_kq(n1 - 1);
     prefetch(n1 - 1);
+    form();
+    prefetch_kq(n1 - 2 >= n0 ? n1 - 2 : n0);
 
     using TX = Tiles<C, BV>;    // dU  [t][v]
     using TL = Tiles<BV, C>;    // lambda^T [v][t]
@@ -166,18 +200,15 @@ __device__ __forceinline__ void bwd_state_body(const Params& p, int wg, float* _
         // these writes after its reads; nothing below reads the gate just committed
         // before the next barrier)
         rg.commit(rowf, gam_s, beta_s);
-        if constexpr (VEC) vg.commit_last(egc);
         const GateLds<GATE, C, DK> gf{rowf, gam_s, valid - 1};
-        if (VEC) {
-            // K e^{gam_C - gam}, -K e^{gam} and Q e^{gam} (one exp for the last two),
-            // from the gate registers
-            rk.store3i(rq, Kd, Kn, Qg, LDK, [&](int i, int e, float k, float q, float* y) {
-                const float ge = vg.g[i][e];
-                const float f = fexp(ge);
-                y[0] = k * fexp(vg.gc[e] - ge);
-                y[1] = -k * f;
-                y[2] = q * f;
-            });
+        if constexpr (VEC) {   // the tiles formed last iteration (K e^{gam_C - gam}, -K e^{gam}, Q e^{gam})
+            if ((int)threadIdx.x < VG::VPR) {
+#pragma unroll
+                for (int e = 0; e < VG::VW; ++e) egc[VG::col0() + e] = pec[e];
+            }
+            pkd.store(Kd, LDK);
+            pkn.store(Kn, LDK);
+            pqg.store(Qg, LDK);
         } else {
             rk.store(Kd, LDK);
             rq.store(Qg, LDK);
@@ -255,6 +286,10 @@ __device__ __forceinline__ void bwd_state_body(const Params& p, int wg, float* _
         // (e) dS0^T = Diag(Gam_C) dS1^T + (Q Gam)^T dO - (K Gam)^T (beta lambda),
         //     the first two terms already added in (c)
         gemm<TI, DK, BV, C, true, true>(dS, VEC ? Kn : Kd, LDK, VEC ? Db : Dn, LDV);
+        if constexpr (VEC) {   // the previous chunk's tiles, then the inputs of the one before
+            form();
+            prefetch_kq(n - 2 >= n0 ? n - 2 : n0);
+        }
         __syncthreads();
     }
     if (!SUMMARY && n1 > n0) {   // lambda and dv of the segment's first chunk

@@ -532,13 +532,6 @@ template <typename TI, int C, int DK> struct VecGate {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // e^{gam_C} per channel into egc[DK] (the threads of the first row of vectors)
-    __device__ __forceinline__ void commit_last(float* egc) const {
-        if ((int)threadIdx.x < VPR) {
-#pragma unroll
-            for (int e = 0; e < VW; ++e) egc[col0() + e] = fexp(gc[e]);
-        }
-    }
 };
 
 // Decay factors read back from LDS after GateRegs::commit.
