@@ -866,10 +866,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 }
             }
         } else {
-            f32x4 tmp[TO::PER];
-            // Y^T = Kr^T dA~^T :  dK+ = beta Y, dbeta_A = sum_c K Y
+            f32x4 tmp[TO::PER], dqp[TO::PER];
+            // Y^T = Kr^T dA~^T :  dK+ = beta Y, dbeta_A = sum_c K Y; and dQ+^T = Kr^T dP~^T
+            // from the same Kr fragments
             zero_acc<D, C>(tmp);
-            gemm<TI, D, C, C, true, false>(tmp, Kr, LD, DAs, LC);
+            zero_acc<D, C>(dqp);
+            gemm2<TI, D, C, C, true, false>(tmp, dqp, Kr, LD, DAs, DPs, LC);
             if (TO::active()) {
 #pragma unroll
                 for (int j = 0; j < TO::PER; ++j) {
@@ -885,14 +887,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             gemm<TI, D, C, C, true, true>(tmp, Ql, LD, DPs, LC);
             if (TO::active()) {
 #pragma unroll
-                for (int j = 0; j < TO::PER; ++j) dkm[j] += tmp[j];
-            }
-            // dQ+^T = Kr^T dP~^T
-            zero_acc<D, C>(tmp);
-            gemm<TI, D, C, C, true, false>(tmp, Kr, LD, DPs, LC);
-            if (TO::active()) {
-#pragma unroll
-                for (int j = 0; j < TO::PER; ++j) dq[j] += tmp[j];
+                for (int j = 0; j < TO::PER; ++j) {
+                    dkm[j] += tmp[j];
+                    dq[j] += dqp[j];
+                }
             }
         }
 
