@@ -605,11 +605,24 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     // start of the last d_v block (whose second register set is free by then; q
     // is not among the cache-warmed tiles, so it comes from far away)
     RegN<TI, C, D> rq, rk;
+    // vector gate: k and q at this lane's elements of the output tiles (4 consecutive
+    // c of row t), as given and kept packed, loaded with them (rows past the
+    // sequence read row valid - 1 and count as zero)
+    typedef typename Vec4<TI>::type V4;
+    V4 kraw[TO::PER], qraw[TO::PER];
 #pragma unroll
     for (int b = 0; b < NVB; ++b) {
         if (b == NVB - 1) {
             rq.load(q, D, valid);
             if (VEC) rk.load(k, D, valid);
+            if (VEC && TO::active()) {
+#pragma unroll
+                for (int j = 0; j < TO::PER; ++j) {
+                    const int t = TO::col(j), tt = min(t, valid - 1);
+                    kraw[j] = *reinterpret_cast<const V4*>(k + (long)tt * D + TO::row(j, 0));
+                    qraw[j] = *reinterpret_cast<const V4*>(q + (long)tt * D + TO::row(j, 0));
+                }
+            }
         }
         TI* S0B = blk(b & 1, L::S0B);
         TI* DS1B = blk(b & 1, L::DS1B);
@@ -737,25 +750,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             });
         } else {
             rq.store(Ql, LD);
-        }
-        // vector gate: k at this lane's elements of the output tiles (4 consecutive c of
-        // row t), as given and kept packed (cache hits: the chunk's rows were just
-        // loaded); rows past the sequence read row valid - 1 and count as zero
-        typedef typename Vec4<TI>::type V4;
-        V4 kraw[TO::PER], qraw[TO::PER];
-        if (VEC && TO::active()) {
-            // the pointers pass through an empty asm so that these loads are issued here:
-            // k and q are read-only, and hoisted to the prologue they would hold registers
-            // through the d_v loop, where the kernel has none to spare
-            const TI* kk = k;
-            const TI* qq = q;
-            asm volatile("" : "+s"(kk), "+s"(qq));
-#pragma unroll
-            for (int j = 0; j < TO::PER; ++j) {
-                const int t = TO::col(j), tt = min(t, valid - 1);
-                kraw[j] = *reinterpret_cast<const V4*>(kk + (long)tt * D + TO::row(j, 0));
-                qraw[j] = *reinterpret_cast<const V4*>(qq + (long)tt * D + TO::row(j, 0));
-            }
         }
         __syncthreads();
         // Warm the caches for the workgroup that most likely starts next on this
