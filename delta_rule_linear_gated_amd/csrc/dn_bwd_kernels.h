@@ -446,53 +446,89 @@ __device__ __forceinline__ void vec_key_products(f32x4 (&dkp)[NACC], f32x4 (&dq)
     using TO = Tiles<D, C>;
     using MM = typename MmaFor<TI, 16>::type;   // one 16-step block per partial
     static_assert(NACC == TO::PER, "accumulator count");
-    constexpr int NB = C / 16;
+    constexpr int NB = C / 16, RM = TO::RM, RN = TO::RN;
     if (!TO::active()) return;
+    // The RM tiles of one column group share their steps (n0, block ob), so each
+    // dA~ / beta dA~ / dP~ fragment is read once for all of them; each tile still
+    // sums its blocks in ascending order.
 #pragma unroll
-    for (int j = 0; j < NACC; ++j) {
-        const int m0 = TO::m0(j), n0 = TO::n0(j), ob = n0 / 16;   // channels m0.., steps n0.. (block ob)
-        const int c = TO::row(j, 0), t = TO::col(j);              // this lane's 4 channels c.., step t
-        const f32x4 gt = ld4<float>(gam_s + t * LDG + c);
-        f32x4 y = zero4(), dqp = zero4(), z = zero4();
+    for (int in = 0; in < RN; ++in) {
+        const int n0 = TO::n0(in), ob = n0 / 16, t = TO::col(in);   // steps n0.. (block ob); this lane's t
+        f32x4 gt[RM], y[RM], dqp[RM], z[RM];
+#pragma unroll
+        for (int im = 0; im < RM; ++im) {
+            gt[im] = ld4<float>(gam_s + t * LDG + TO::row(im * RN + in, 0));   // this lane's 4 channels c..
+            y[im] = zero4();
+            dqp[im] = zero4();
+            z[im] = zero4();
+        }
         // Y, DQ: blocks b <= ob
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (b > ob) break;
-            f32x4 py = zero4(), pq = zero4();
+            f32x4 py[RM], pq[RM];
+#pragma unroll
+            for (int im = 0; im < RM; ++im) {
+                py[im] = zero4();
+                pq[im] = zero4();
+            }
 #pragma unroll
             for (int k0 = 0; k0 < 16; k0 += MM::kStep) {
-                const auto fa = MM::load_t(Kc + (16 * b + k0) * ld + m0, ld);
-                py = MM::op(fa, MM::load(DA + n0 * lc + 16 * b + k0, lc), py);
-                pq = MM::op(fa, MM::load(DP + n0 * lc + 16 * b + k0, lc), pq);
-            }
-            const f32x4 rb = ld4<float>(gam_s + (16 * b + 15) * LDG + c);
+                const auto fda = MM::load(DA + n0 * lc + 16 * b + k0, lc);
+                const auto fdp = MM::load(DP + n0 * lc + 16 * b + k0, lc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float fct = fexp(gt[i] - rb[i]);
-                y[i] += fct * py[i];
-                dqp[i] += fct * pq[i];
+                for (int im = 0; im < RM; ++im) {
+                    const auto fa = MM::load_t(Kc + (16 * b + k0) * ld + TO::m0(im * RN + in), ld);
+                    py[im] = MM::op(fa, fda, py[im]);
+                    pq[im] = MM::op(fa, fdp, pq[im]);
+                }
+            }
+#pragma unroll
+            for (int im = 0; im < RM; ++im) {
+                const f32x4 rb = ld4<float>(gam_s + (16 * b + 15) * LDG + TO::row(im * RN + in, 0));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float fct = fexp(gt[im][i] - rb[i]);
+                    y[im][i] += fct * py[im][i];
+                    dqp[im][i] += fct * pq[im][i];
+                }
             }
         }
         // Z: blocks b >= ob (here t is the output's step s)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (b < ob) continue;
-            f32x4 pz = zero4();
+            f32x4 pz[RM];
+#pragma unroll
+            for (int im = 0; im < RM; ++im) pz[im] = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < 16; k0 += MM::kStep) {
-                pz = MM::op(MM::load_t(Kr + (16 * b + k0) * ld + m0, ld), MM::load_t(DAB + (16 * b + k0) * lc + n0, lc), pz);
-                pz = MM::op(MM::load_t(Qr + (16 * b + k0) * ld + m0, ld), MM::load_t(DP + (16 * b + k0) * lc + n0, lc), pz);
-            }
-            const f32x4 rp = b > 0 ? ld4<float>(gam_s + (16 * b - 1) * LDG + c) : zero4();
+                const auto fab = MM::load_t(DAB + (16 * b + k0) * lc + n0, lc);
+                const auto fpt = MM::load_t(DP + (16 * b + k0) * lc + n0, lc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) z[i] += fexp(rp[i] - gt[i]) * pz[i];
+                for (int im = 0; im < RM; ++im) {
+                    const int m0 = TO::m0(im * RN + in);
+                    pz[im] = MM::op(MM::load_t(Kr + (16 * b + k0) * ld + m0, ld), fab, pz[im]);
+                    pz[im] = MM::op(MM::load_t(Qr + (16 * b + k0) * ld + m0, ld), fpt, pz[im]);
+                }
+            }
+#pragma unroll
+            for (int im = 0; im < RM; ++im) {
+                const f32x4 rp = b > 0 ? ld4<float>(gam_s + (16 * b - 1) * LDG + TO::row(im * RN + in, 0)) : zero4();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) z[im][i] += fexp(rp[i] - gt[im][i]) * pz[im][i];
+            }
         }
-        const f32x4 kv = f32x4{to_f(kraw[j][0]), to_f(kraw[j][1]), to_f(kraw[j][2]), to_f(kraw[j][3])};
-        const f32x4 d4 = kv * y;
-        dbA[j] = d4[0] + d4[1] + d4[2] + d4[3];
-        dkp[j] += beta_s[t] * y;
-        dq[j] += dqp;
-        dkm[j] += z;
+#pragma unroll
+        for (int im = 0; im < RM; ++im) {
+            const int j = im * RN + in;
+            const f32x4 kv = f32x4{to_f(kraw[j][0]), to_f(kraw[j][1]), to_f(kraw[j][2]), to_f(kraw[j][3])};
+            const f32x4 d4 = kv * y[im];
+            dbA[j] = d4[0] + d4[1] + d4[2] + d4[3];
+            dkp[j] += beta_s[t] * y[im];
+            dq[j] += dqp[im];
+            dkm[j] += z[im];
+        }
     }
 }
 
