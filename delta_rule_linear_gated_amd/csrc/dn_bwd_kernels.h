@@ -403,16 +403,11 @@ struct BwdChunkSmem {
     static constexpr size_t KCO = LASTS + al(D * 4);                              // [C] Kaczmarz dk coefficients
     static constexpr size_t DIAGP = KCO + al(C * 4);                              // [C] diagonal of dP (vector gate)
     static constexpr size_t TOTAL = DIAGP + al(VEC ? C * 4 : 0);
-    // dq / dk write-back tiles [C][LD] each at offset 0; d gam of the vector gate
-    // [C][LDG] fp32 after them, written once every phase-C tile is dead
-    static constexpr size_t DGB = al(2 * C * LD * E);
-    static constexpr int LDG = D + 4;   // d gam rows (fp32, padded: its accumulator stores stay conflict-free)
-    static_assert(!VEC || DGB + C * LDG * 4 <= BIG_END, "d gam buffer");
-    // per-thread partials of sum_v S0 dS1 [row blocks of the S0 register tile][LDS_] fp32,
-    // beside the write-back tiles (and d gam)
+    // dq / dk write-back tiles [C][LD] each at offset 0; after them the per-thread
+    // partials of sum_v S0 dS1 [row blocks of the S0 register tile][LDS_] fp32
     using RS = RegB<TI, VB, D>;
     static constexpr int LDS_ = D + 4;   // rows of the partials (padded: eight lanes store to eight rows)
-    static constexpr size_t LSRED = VEC ? DGB + al(C * LDG * 4) : DGB;
+    static constexpr size_t LSRED = al(2 * C * LD * E);
     static_assert(LSRED + RS::BR * LDS_ * 4 <= BIG_END, "S0 dS1 partials");
     static_assert(2 * C * LD * E <= BIG_END, "write-back tiles");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
@@ -553,7 +548,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     float* red_b = reinterpret_cast<float*>(smem + L::RED_B);
     float* red_c = reinterpret_cast<float*>(smem + L::RED_C);
     float* lastS = reinterpret_cast<float*>(smem + L::LASTS);
-    float* dgb = reinterpret_cast<float*>(smem + L::DGB);
     float* kco = reinterpret_cast<float*>(smem + L::KCO);
     float* diagp = reinterpret_cast<float*>(smem + L::DIAGP);
 
@@ -1020,39 +1014,52 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                         lastS[c] = fexp(gl[c]) * ssum + cs;   // the whole last-row term of channel c
                     }
                 }
-                // d gam: elementwise terms + the gam_C terms on the last valid row
+                // d gam_t = sum_{s >= t} of the elementwise terms (rows past the sequence
+                // count as zero), plus the gam_C term lastS, which enters at the last valid
+                // row and so reaches every valid row.  In registers, per 16-step tile: a
+                // suffix scan over its 16 lanes (DPP row shifts: lane i adds lane i + n of
+                // its row, 0 past the row end) and the tile's total; then the totals of the
+                // later tiles, of this wave directly and of the later column groups of
+                // waves through LDS (red_g: [WN][D], unused by this gate).
+                float* tl = red_g;
+                static_assert(TO::WN * D <= (D / 16) * C, "tile totals");
+                f32x4 tot[TO::PER];
                 if (TO::active()) {
 #pragma unroll
-                    for (int j = 0; j < TO::PER; ++j) st4<float>(dgb + TO::col(j) * L::LDG + TO::row(j, 0), dgm[j]);
-                }
-                __syncthreads();
-                // d gam_t = sum_{s >= t} per channel, in NSG segments of RSG rows (one
-                // thread each: the suffix sums of its rows), then the totals of the
-                // later segments (through red_c, dead since lastS was formed)
-                constexpr int NSG = kThreads / D < C / 16 ? kThreads / D : C / 16;
-                constexpr int RSG = C / NSG;
-                static_assert(NSG >= 1 && NSG * D <= kThreads && C % NSG == 0, "segments");
-                const int c = threadIdx.x % D, sg = threadIdx.x / D;
-                float sfx[RSG];
-                if (sg < NSG) {
-                    const float last = lastS[c];
-                    float acc = 0.f;
+                    for (int j = 0; j < TO::PER; ++j) {
+                        const bool in_seq = TO::col(j) < valid;
 #pragma unroll
-                    for (int r = RSG - 1; r >= 0; --r) {
-                        const int t = sg * RSG + r;
-                        acc += t < valid ? dgb[t * L::LDG + c] + (t == valid - 1 ? last : 0.f) : 0.f;
-                        sfx[r] = acc;
+                        for (int i = 0; i < 4; ++i) {
+                            float x = in_seq ? dgm[j][i] : 0.f;
+                            tot[j][i] = row16_sum(x);
+                            x += dpp_f<0x101>(x);
+                            x += dpp_f<0x102>(x);
+                            x += dpp_f<0x104>(x);
+                            x += dpp_f<0x108>(x);
+                            dgm[j][i] = x;
+                        }
                     }
-                    red_c[sg * D + c] = acc;
+#pragma unroll
+                    for (int im = 0; im < TO::RM; ++im) {
+                        f32x4 sw = zero4();
+#pragma unroll
+                        for (int in = 0; in < TO::RN; ++in) sw += tot[im * TO::RN + in];
+                        if ((lane_id() & 15) == 0) st4<float>(tl + TO::cg() * D + TO::row(im * TO::RN, 0), sw);
+                    }
                 }
                 __syncthreads();
-                if (sg < NSG) {
-                    float off = 0.f;
-                    for (int s2 = sg + 1; s2 < NSG; ++s2) off += red_c[s2 * D + c];
+                if (TO::active()) {
 #pragma unroll
-                    for (int r = 0; r < RSG; ++r) {
-                        const int t = sg * RSG + r;
-                        if (t < valid) p.dg[(row0 + t) * D + c] = sfx[r] + off;
+                    for (int im = 0; im < TO::RM; ++im) {
+                        const int c = TO::row(im * TO::RN, 0);
+                        f32x4 off = ld4<float>(lastS + c);
+                        for (int g = TO::cg() + 1; g < TO::WN; ++g) off += ld4<float>(tl + g * D + c);
+#pragma unroll
+                        for (int in = TO::RN - 1; in >= 0; --in) {
+                            const int j = im * TO::RN + in, t = TO::col(j);
+                            if (t < valid) st4<float>(p.dg + (row0 + t) * D + c, dgm[j] + off);
+                            off += tot[j];
+                        }
                     }
                 }
             } else if (wave_id() == 0) {
