@@ -141,9 +141,9 @@ def dn_states_bytes(shape: Shape) -> int:
 
 
 def dn_states_layout(shape: Shape):
-    out = (ctypes.c_size_t * 6)()
+    out = (ctypes.c_size_t * 7)()
     _check(lib().dn_states_layout(ctypes.byref(shape), out))
-    return dict(zip(("states", "T", "P", "gam", "kz", "total"), list(out)))
+    return dict(zip(("states", "T", "P", "U", "gam", "kz", "total"), list(out)))
 
 
 def dn_workspace_bytes(shape: Shape, pass_: int) -> int:
@@ -318,13 +318,13 @@ def workspace(shape: Shape, pass_: int, device) -> torch.Tensor:
 
 
 def saved_buffer(shape: Shape, device) -> torch.Tensor:
-    """Byte buffer for the forward's saved states, T, P and log-decay."""
+    """Byte buffer for the forward's saved states, T, P, U and log-decay."""
     return torch.empty(max(dn_states_bytes(shape), 1), dtype=torch.uint8, device=device)
 
 
 def saved_regions(buf: torch.Tensor, shape: Shape) -> dict:
-    """Views of a saved buffer: states [B,H,NT,dv,dk], T and P [B,H,NT,C,C] (io
-    type), gam like g (fp32; None without a gate), and with the Kaczmarz flag
+    """Views of a saved buffer: states [B,H,NT,dv,dk], T and P [B,H,NT,C,C], U
+    [B,H,NT,C,dv] (io type), gam like g (fp32; None without a gate), and with the Kaczmarz flag
     kz_beta and kz_rn [B,H,T] (fp32; else None)."""
     lay = dn_states_layout(shape)
     io = torch.bfloat16 if shape.dtype == DN_BF16 else torch.float32
@@ -340,7 +340,8 @@ def saved_regions(buf: torch.Tensor, shape: Shape) -> dict:
 
     out = {"states": view(lay["states"], (B, H, NT, dv, dk), io, E),
            "T": view(lay["T"], (B, H, NT, C, C), io, E),
-           "P": view(lay["P"], (B, H, NT, C, C), io, E), "gam": None, "kz_beta": None, "kz_rn": None}
+           "P": view(lay["P"], (B, H, NT, C, C), io, E), "U": view(lay["U"], (B, H, NT, C, dv), io, E),
+           "gam": None, "kz_beta": None, "kz_rn": None}
     if shape.gate != DN_GATE_NONE:
         gw = (dk,) if shape.gate == DN_GATE_VECTOR else ()
         out["gam"] = view(lay["gam"], (B, H, T) + gw, torch.float32, 4)

@@ -144,7 +144,7 @@ size_t dn_states_bytes(const dn_shape* shape) {
     return dn::saved_layout(pr).total;
 }
 
-dn_status dn_states_layout(const dn_shape* shape, size_t offsets[6]) {
+dn_status dn_states_layout(const dn_shape* shape, size_t offsets[7]) {
     dn::Problem pr;
     Dims d;
     if (!offsets) return fail(DN_ERR_INVALID, "offsets is NULL");
@@ -153,9 +153,10 @@ dn_status dn_states_layout(const dn_shape* shape, size_t offsets[6]) {
     offsets[0] = l.states;
     offsets[1] = l.Tm;
     offsets[2] = l.Pm;
-    offsets[3] = l.gam;
-    offsets[4] = l.kz;
-    offsets[5] = l.total;
+    offsets[3] = l.Um;
+    offsets[4] = l.gam;
+    offsets[5] = l.kz;
+    offsets[6] = l.total;
     return DN_OK;
 }
 
@@ -240,6 +241,7 @@ dn_status dn_chunk_fwd(const dn_shape* shape, const void* q, const void* k, cons
     p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(wb + (states ? sl.gam : w.gam));
     p.Tm = wb + (states ? sl.Tm : w.Tm);
     p.Pm = wb + (states ? sl.Pm : w.Pm);
+    p.Um = states ? wb + sl.Um : nullptr;   // written only with the saved states
     if (pr.kz) set_kaczmarz(&p, wb + (states ? sl.kz : w.kz), d, shape->eps);
     set_scan(&p, pr, static_cast<char*>(ws), w);
     const hipError_t e = dn::launch_forward(pr, p, states != nullptr, static_cast<hipStream_t>(stream));
@@ -342,6 +344,7 @@ dn_status dn_chunk_bwd(const dn_shape* shape, const void* q, const void* k, cons
         p.gam = pr.gate == DN_GATE_NONE ? nullptr : reinterpret_cast<float*>(sb + sl.gam);
         p.Tm = sb + sl.Tm;
         p.Pm = sb + sl.Pm;
+        p.Um = sb + sl.Um;
         if (pr.kz) set_kaczmarz(&p, sb + sl.kz, d, shape->eps);
     } else {             // recomputed into the workspace
         p.states = wb + w.states;

@@ -342,18 +342,22 @@ __global__ __launch_bounds__(kThreads) void recompute_bwd_state_kernel(Params p,
 // ---------------------------------------------------------------------------
 // bwd_chunk_kernel: grid (NT, BH); every chunk finished independently.
 // D = d_k = d_v.  The d_v dimension is streamed in blocks of VB columns: the
-// block's S0 rows, dS1 rows, lambda, dO and V columns are loaded into registers
-// one block ahead and committed to LDS while the previous block computes
-//     X_b = (K Gam) S0_b^T,  R_b = beta (V_b - X_b),  U_b = T R_b
+// block's S0 rows, dS1 rows, lambda, dO, V and U columns (US: U = T R of the
+// chunk as the forward saved it) are loaded into registers two blocks ahead and
+// committed to LDS while the previous block computes
+//     (without US: X_b = (K Gam) S0_b^T,  R_b = beta (V_b - X_b),  U_b = T R_b)
 //     dQg += dO_b S0_b,  dKg += lambda_b S0_b,  dKd += U_b dS1_b
 //     dA  += lambda_b U_b^T,  dP += dO_b U_b^T
 // after which the key-gradient products (phase C) finish dq, dk, dbeta, dg.
+// The residual's part of dbeta, sum_v lambda (V - X) with X = (K Gam) S0^T,
+// needs no X: sum_v lambda X = sum_c (K Gam) (lambda S0), and lambda S0 is dKg;
+// sum_v lambda V is formed from the V and lambda registers at each commit.
 // Every LDS tile keeps its natural (global) layout; operands contracted over
 // their leading index are read with the transposing LDS load.  The products are
 // accumulated transposed where that gives a lane 4 consecutive elements of a
-// row of the stored result (X^T, U^T, dq^T, dk^T, dA^T, dP^T), so results go
-// to LDS with one vector store per tile.
-template <typename TI, int GATE, int C, int D>
+// row of the stored result (dq^T, dk^T, dA^T, dP^T), so results go to LDS with
+// one vector store per tile.
+template <typename TI, int GATE, int C, int D, bool US>
 struct BwdChunkSmem {
     static constexpr int PAD = Pad<TI>::value;
     // d_v block (16 for fp32 at D = 128, whose tiles are twice the bytes)
@@ -368,18 +372,18 @@ struct BwdChunkSmem {
     static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
     // persistent through the d_v loop (K also through phase C without a vector gate)
     static constexpr size_t KG = 0;                                  // K (or K Gam)   [C][LD]
-    static constexpr size_t TL = KG + al(C * LD * E);                // T              [C][LC]
-    static constexpr size_t LOOP = TL + al(C * LC * E);
+    static constexpr size_t TL = KG + al(C * LD * E);                // T (without US) [C][LC]
+    static constexpr size_t LOOP = TL + (US ? 0 : al(C * LC * E));
     // d_v loop: two buffers of one block's tiles (offsets within a buffer), so the
     // next block is committed while this one computes
     static constexpr size_t S0B = 0;                                 // S0 rows        [VB][LD]
     static constexpr size_t DS1B = S0B + al(VB * LD * E);            // dS1 rows       [VB][LD]
     static constexpr size_t LAMB = DS1B + al(VB * LD * E);           // lambda block   [C][LVB]
     static constexpr size_t DOB = LAMB + al(C * LVB * E);            // dO block       [C][LVB]
-    static constexpr size_t VBL = DOB + al(C * LVB * E);             // V block, then U block [C][LVB]
-    static constexpr size_t BLK = VBL + al(C * LVB * E);
-    static constexpr size_t RB = LOOP + 2 * BLK;                     // R block        [C][LVB]
-    static constexpr size_t LOOP_END = RB + al(C * LVB * E);
+    static constexpr size_t UBL = DOB + al(C * LVB * E);             // U block (without US: V, then U) [C][LVB]
+    static constexpr size_t BLK = UBL + al(C * LVB * E);
+    static constexpr size_t RB = LOOP + 2 * BLK;                     // R block (without US) [C][LVB]
+    static constexpr size_t LOOP_END = RB + (US ? 0 : al(C * LVB * E));
     // phase C (over the d_v-loop tiles)
     static constexpr size_t DA = LOOP;                               // dA~            [C][LC]
     static constexpr size_t DAB = DA + al(C * LC * E);               // beta_t dA~     [C][LC]
@@ -397,8 +401,9 @@ struct BwdChunkSmem {
     static constexpr size_t BETA = ROWF + al(2 * C * 4);                          // [C]
     static constexpr size_t RED_R = BETA + al(C * 4);                             // [D/16][C] row partials (dbeta_A)
     static constexpr size_t RED_G = RED_R + al((D / 16) * C * 4);                 // [D/16][C] row partials (d gam)
-    static constexpr size_t RED_B = RED_G + al((D / 16) * C * 4);                 // [VB/16][C] row partials (dbeta_R)
-    static constexpr size_t RED_C = RED_B + al((VB / 16) * C * 4);                // [C/16][D] column partials
+    using RV = RegN<TI, C, VB>;   // register tiles of the lambda / dO / U / V blocks
+    static constexpr size_t RED_V = RED_G + al((D / 16) * C * 4);                 // [RV::VPR][C] row partials (lambda . V)
+    static constexpr size_t RED_C = RED_V + al(RV::VPR * C * 4);                  // [C/16][D] column partials
     static constexpr size_t LASTS = RED_C + al((C / 16) * D * 4);                 // [D]
     static constexpr size_t KCO = LASTS + al(D * 4);                              // [C] Kaczmarz dk coefficients
     static constexpr size_t DIAGP = KCO + al(C * 4);                              // [C] diagonal of dP (vector gate)
@@ -527,9 +532,9 @@ __device__ __forceinline__ void vec_key_products(f32x4 (&dkp)[NACC], f32x4 (&dq)
     }
 }
 
-template <typename TI, int GATE, int C, int D>
+template <typename TI, int GATE, int C, int D, bool US>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
-    using L = BwdChunkSmem<TI, GATE, C, D>;
+    using L = BwdChunkSmem<TI, GATE, C, D, US>;
     constexpr int LD = L::LD, LC = L::LC, LVB = L::LVB, GW = L::GW;
     constexpr int VB = L::VB, NVB = L::NVB;
     constexpr bool VEC = GATE == kGateVector;
@@ -537,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     __shared__ __align__(16) char smem[L::TOTAL];
     TI* KG = reinterpret_cast<TI*>(smem + L::KG);
     TI* TLs = reinterpret_cast<TI*>(smem + L::TL);
-    // tiles of block-buffer i (V and then U share a slot: V is dead once R is formed)
+    // tiles of block-buffer i
     auto blk = [&](int i, size_t off) { return reinterpret_cast<TI*>(smem + L::LOOP + i * L::BLK + off); };
     TI* RB = reinterpret_cast<TI*>(smem + L::RB);
     float* gam_s = reinterpret_cast<float*>(smem + L::GAM);
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     float* beta_s = reinterpret_cast<float*>(smem + L::BETA);
     float* red_r = reinterpret_cast<float*>(smem + L::RED_R);
     float* red_g = reinterpret_cast<float*>(smem + L::RED_G);
-    float* red_b = reinterpret_cast<float*>(smem + L::RED_B);
+    float* red_v = reinterpret_cast<float*>(smem + L::RED_V);
     float* red_c = reinterpret_cast<float*>(smem + L::RED_C);
     float* lastS = reinterpret_cast<float*>(smem + L::LASTS);
     float* kco = reinterpret_cast<float*>(smem + L::KCO);
@@ -563,12 +568,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     const TI* __restrict__ S0g = static_cast<const TI*>(p.states) + chunk * D * D;
     const TI* __restrict__ dS1g = static_cast<const TI*>(p.dS1) + chunk * D * D;
     const TI* __restrict__ lamg = static_cast<const TI*>(p.lam) + chunk * C * D;
+    const TI* __restrict__ Ug = static_cast<const TI*>(p.Um) + chunk * C * D;
 
     using TO = Tiles<D, C>;    // dq^T, dk^T         [c][t]
     using TCC = Tiles<C, C>;   // dA^T, dP^T         [s][t]
-    using TX = Tiles<VB, C>;   // X_b^T, U_b^T       [v][t]
+    using TX = Tiles<VB, C>;   // X_b^T, U_b^T       [v][t]  (without US)
 
-    // ---------------- prologue: gate, K, T, the first d_v block
+    // ---------------- prologue: gate, K, the first d_v blocks
     // (the Kaczmarz step's 1 / (||k_t||^2 + eps) of step t = thread index, used only
     // by the finish: loaded first, branch-free (beta stands in without the step), so
     // its latency hides behind the whole chunk)
@@ -578,18 +584,20 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     RegN<TI, C, D> rK;
     rK.load(k, D, valid);
     RegN<TI, C, C> rT;
-    rT.load(static_cast<const TI*>(p.Tm) + chunk * C * C, C, C);
+    if (!US) rT.load(static_cast<const TI*>(p.Tm) + chunk * C * C, C, C);
     // two register sets: the loads of block b + 2 are issued when block b is
     // committed, so two blocks of loads are in flight during the loop
+    using RV = typename L::RV;
     struct BlockRegs {
         RegB<TI, VB, D> S0, dS1;
-        RegN<TI, C, VB> lam, dO, V;
+        RV lam, dO, U, V;
     } rb[2];
     auto load_block = [&](BlockRegs& r, int b) {
         const int v0 = b * VB;
         r.S0.load(S0g + (long)v0 * D, D, VB);
         r.dS1.load(dS1g + (long)v0 * D, D, VB);
         r.lam.load(lamg + v0, D, C);
+        if (US) r.U.load(Ug + v0, D, C);
         r.dO.load(dO + v0, D, valid);
         r.V.load(v + v0, D, valid);
     };
@@ -603,10 +611,23 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     if (VEC)
         rK.store(KG, LD, [&](int r, int c, float x) { return x * gf.G(r, c); });
     else
-        rK.store(KG, LD);   // scalar: Gam_t is applied to X's rows
-    rT.store(TLs, LC);
+        rK.store(KG, LD);   // scalar: Gam_t is applied on the C x D results
+    if (!US) rT.store(TLs, LC);
+    // sum_v lambda V over this thread's vectors of the block tiles (rows past the
+    // sequence excluded: V is loaded clamped there)
+    float lv[RV::PER] = {};
     auto commit_block = [&](BlockRegs& r, int i) {
         r.S0.dot_rows(r.dS1, ls);
+#pragma unroll
+        for (int x = 0; x < RV::PER; ++x) {
+            const uint4 la = pin(r.lam.r[x]), va = pin(r.V.r[x]);
+            const TI* le = reinterpret_cast<const TI*>(&la);
+            const TI* ve = reinterpret_cast<const TI*>(&va);
+            float s2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < RV::VW; ++e) s2 += to_f(le[e]) * to_f(ve[e]);
+            lv[x] += RV::idx_of(x) / RV::VPR < valid ? s2 : 0.f;
+        }
         // the sums are formed here: left to their use at the finish, the compiler
         // sinks the products there and keeps both register tiles alive until then
 #pragma unroll
@@ -617,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         r.dS1.store_n(blk(i, L::DS1B), LD, Identity());
         r.lam.store(blk(i, L::LAMB), LVB);
         r.dO.store(blk(i, L::DOB), LVB);
-        r.V.store(blk(i, L::VBL), LVB);
+        (US ? r.U : r.V).store(blk(i, L::UBL), LVB);
     };
     commit_block(rb[0], 0);
     __syncthreads();
@@ -630,7 +651,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     zero_acc<D, C>(dkm);
     zero_acc<C, C>(dA);
     zero_acc<C, C>(dP);
-    float dbr_part[TX::PER] = {};   // sum over this lane's 4 v of lambda (V - X) at row t = TX::col(j)
     // q (and k for the vector gate) for the key-gradient products, loaded at the
     // start of the last d_v block (whose second register set is free by then; q
     // is not among the cache-warmed tiles, so it comes from far away)
@@ -658,53 +678,76 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         TI* DS1B = blk(b & 1, L::DS1B);
         TI* LAMB = blk(b & 1, L::LAMB);
         TI* DOB = blk(b & 1, L::DOB);
-        TI* VBL = blk(b & 1, L::VBL);
-        TI* UB = VBL;
-        // X_b^T = S0_b (K Gam)^T and the two S0 contractions (S0 rows read as [k][m])
-        f32x4 X[TX::PER];
-        zero_acc<VB, C>(X);
-        gemm<TI, VB, C, D, false, false>(X, S0B, LD, KG, LD);
-        gemm2<TI, D, C, VB, true, false>(dq, dkp, S0B, LD, DOB, LAMB, LVB);
-        if (TX::active()) {
-            f32x4 rr[TX::PER];   // LDS reads first, then the writes
-#pragma unroll
-            for (int j = 0; j < TX::PER; ++j) {
-                const int t = TX::col(j), c = TX::row(j, 0);
-                const f32x4 xr = ld4<TI>(VBL + t * LVB + c) - (SCA ? rowf[t] : 1.f) * X[j];
-                const f32x4 lm = ld4<TI>(LAMB + t * LVB + c);
-                dbr_part[j] += lm[0] * xr[0] + lm[1] * xr[1] + lm[2] * xr[2] + lm[3] * xr[3];
-                rr[j] = beta_s[t] * xr;
+        TI* UB = blk(b & 1, L::UBL);
+        if constexpr (US) {
+            // the two S0 contractions (S0 rows read as [k][m]), then the two over U
+            gemm2<TI, D, C, VB, true, false>(dq, dkp, S0B, LD, DOB, LAMB, LVB);
+            gemm<TI, D, C, VB, true, false>(dkm, DS1B, LD, UB, LVB);
+            gemm2<TI, C, C, VB, false, false>(dA, dP, UB, LVB, LAMB, DOB, LVB);
+            // block b + 1 into the other buffer (its last reader, block b - 1, ended at
+            // the previous barrier), read after the barrier below; then the loads of
+            // block b + 3 into the registers it leaves free
+            if (b + 1 < NVB) {
+                commit_block(rb[(b + 1) & 1], (b + 1) & 1);
+                if (b + 3 < NVB) load_block(rb[(b + 1) & 1], b + 3);
+                __syncthreads();
             }
-#pragma unroll
-            for (int j = 0; j < TX::PER; ++j) st4<TI>(RB + TX::col(j) * LVB + TX::row(j, 0), rr[j]);
-        }
-        __syncthreads();
-        // block b + 1 into the other buffer (free since block b - 1 ended), read after
-        // the two barriers below
-        if (b + 1 < NVB) {
-            commit_block(rb[(b + 1) & 1], (b + 1) & 1);
-            if (b + 3 < NVB) load_block(rb[(b + 1) & 1], b + 3);
-        }
-        // U_b^T = R_b^T T^T  (R rows read as [k][m])
-        {
-            f32x4 U[TX::PER];
-            zero_acc<VB, C>(U);
-            gemm<TI, VB, C, C, true, false>(U, RB, LVB, TLs, LC);
+        } else {
+            // X_b^T = S0_b (K Gam)^T and the two S0 contractions (S0 rows read as [k][m])
+            f32x4 X[TX::PER];
+            zero_acc<VB, C>(X);
+            gemm<TI, VB, C, D, false, false>(X, S0B, LD, KG, LD);
+            gemm2<TI, D, C, VB, true, false>(dq, dkp, S0B, LD, DOB, LAMB, LVB);
             if (TX::active()) {
+                f32x4 rr[TX::PER];   // LDS reads first, then the writes
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) st4<TI>(UB + TX::col(j) * LVB + TX::row(j, 0), U[j]);
+                for (int j = 0; j < TX::PER; ++j) {
+                    const int t = TX::col(j), c = TX::row(j, 0);
+                    rr[j] = beta_s[t] * (ld4<TI>(UB + t * LVB + c) - (SCA ? rowf[t] : 1.f) * X[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < TX::PER; ++j) st4<TI>(RB + TX::col(j) * LVB + TX::row(j, 0), rr[j]);
             }
+            __syncthreads();
+            // block b + 1 into the other buffer (free since block b - 1 ended), read after
+            // the two barriers below
+            if (b + 1 < NVB) {
+                commit_block(rb[(b + 1) & 1], (b + 1) & 1);
+                if (b + 3 < NVB) load_block(rb[(b + 1) & 1], b + 3);
+            }
+            // U_b^T = R_b^T T^T  (R rows read as [k][m]) over the V block
+            {
+                f32x4 U[TX::PER];
+                zero_acc<VB, C>(U);
+                gemm<TI, VB, C, C, true, false>(U, RB, LVB, TLs, LC);
+                if (TX::active()) {
+#pragma unroll
+                    for (int j = 0; j < TX::PER; ++j) st4<TI>(UB + TX::col(j) * LVB + TX::row(j, 0), U[j]);
+                }
+            }
+            __syncthreads();
+            gemm<TI, D, C, VB, true, false>(dkm, DS1B, LD, UB, LVB);
+            gemm2<TI, C, C, VB, false, false>(dA, dP, UB, LVB, LAMB, DOB, LVB);
+            // no barrier here: the next writes into this buffer (the commit of block
+            // b + 2) and into RB come after the next block's first barrier
         }
-        __syncthreads();
-        gemm<TI, D, C, VB, true, false>(dkm, DS1B, LD, UB, LVB);
-        gemm2<TI, C, C, VB, false, false>(dA, dP, UB, LVB, LAMB, DOB, LVB);
-        // no barrier here: the next writes into this buffer (the commit of block
-        // b + 2) and into RB come after the next block's first barrier
     }
 
 
+    // sum_v lambda X at row t as sum_c (K Gam)[t][c] dKg[t][c] (over this lane's 4 c;
+    // K Gam with the operand values X was formed from), then
     // dq = Gam dQg ; dk+ = -beta Gam dKg ; dk- = Gd dKd   (element c = row, t = col)
+    float xdot[TO::PER];
     if (TO::active()) {
+#pragma unroll
+        for (int j = 0; j < TO::PER; ++j) {
+            const int t = TO::col(j);
+            const f32x4 kg = ld4<TI>(KG + t * LD + TO::row(j, 0));
+            float x = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x += kg[i] * (VEC ? 1.f : gf.G(t, TO::row(j, i))) * dkp[j][i];
+            xdot[j] = x;
+        }
 #pragma unroll
         for (int j = 0; j < TO::PER; ++j) {
             const int t = TO::col(j);
@@ -785,10 +828,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         // Warm the caches for the workgroup that most likely starts next on this
         // XCD: workgroups start in id order and go to the XCDs round-robin, so it
         // is this id plus the number resident at once.  One dword of every
-        // 128-byte line of its prologue tiles (K, T, the first two d_v blocks of
-        // S0, dS1, lambda, dO and V, the gate and beta rows; up to 2 lines per
-        // thread), held in registers and consumed only at the end, so nothing
-        // waits for them.
+        // 128-byte line of its prologue tiles (K, the first two d_v blocks of S0,
+        // dS1, lambda, U (or T without US), dO and V, the gate and beta rows; up
+        // to 2 lines per thread), held in registers and consumed only at the end,
+        // so nothing waits for them.
         int warm[2];
         {
             const long ids = (long)gridDim.x * gridDim.y;
@@ -798,17 +841,22 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             const long nrow0 = (long)nbh * p.T + (long)nn * C;
             const long nchunk = (long)nbh * p.NT + nn;
             constexpr int E = sizeof(TI), NB = NVB < 2 ? NVB : 2;
-            constexpr int LPR = (NB * VB * E + 127) / 128;   // lines per row of the lambda / dO / V blocks
+            constexpr int LPR = (NB * VB * E + 127) / 128;   // lines per row of the lambda / U / dO / V blocks
             const int nK = (nvalid * D * E + 127) / 128;
-            constexpr int nT = (C * C * E + 127) / 128, nS = (NB * VB * D * E + 127) / 128;
+            constexpr int nS = (NB * VB * D * E + 127) / 128;
+            constexpr int nU = US ? C * LPR : (C * C * E + 127) / 128;   // U by row, or T by line
             const int nG = (nvalid * GW * 4 + 127) / 128, nB = (nvalid * 4 + 127) / 128;   // gate and beta rows
-            const int b1 = nK, b2 = b1 + nT, b3 = b2 + nS, b4 = b3 + nS, b5 = b4 + C * LPR, b6 = b5 + nvalid * LPR,
-                      b7 = b6 + nvalid * LPR, b8 = b7 + (GATE != kGateNone ? nG : 0), nl = b8 + nB;
+            // contiguous: K, S0, dS1; by row: lambda (C rows), U (C rows; T contiguous
+            // without US), dO, V; then gate, beta
+            const int b1 = nK, b2 = b1 + nS, b3 = b2 + nS, b4 = b3 + C * LPR, b5 = b4 + nU,
+                      b6 = b5 + nvalid * LPR, b7 = b6 + nvalid * LPR, b8 = b7 + (GATE != kGateNone ? nG : 0),
+                      nl = b8 + nB;
             const char* kb = reinterpret_cast<const char*>(static_cast<const TI*>(p.k) + nrow0 * D);
-            const char* tb = reinterpret_cast<const char*>(static_cast<const TI*>(p.Tm) + nchunk * C * C);
             const char* sb = reinterpret_cast<const char*>(static_cast<const TI*>(p.states) + nchunk * D * D);
             const char* db = reinterpret_cast<const char*>(static_cast<const TI*>(p.dS1) + nchunk * D * D);
             const char* lb = reinterpret_cast<const char*>(static_cast<const TI*>(p.lam) + nchunk * C * D);
+            const char* ub = US ? reinterpret_cast<const char*>(static_cast<const TI*>(p.Um) + nchunk * C * D)
+                                : reinterpret_cast<const char*>(static_cast<const TI*>(p.Tm) + nchunk * C * C);
             const char* ob = reinterpret_cast<const char*>(static_cast<const TI*>(p.dout) + nrow0 * D);
             const char* vb = reinterpret_cast<const char*>(static_cast<const TI*>(p.v) + nrow0 * D);
             const char* gb = reinterpret_cast<const char*>(p.gam + nrow0 * GW);
@@ -816,17 +864,18 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
                 const int i = min((int)threadIdx.x + r * kThreads, nl - 1);
-                const int s = i < b4 ? 0 : (i < b5 ? 1 : (i < b6 ? 2 : (i < b7 ? 3 : 4)));
-                const int j = i - (s == 0 ? 0 : (s == 1 ? b4 : (s == 2 ? b5 : b6)));
-                // contiguous segments (K, T, S0, dS1, gate, beta) by line; row segments by
-                // row and line
-                const char* base = s == 1 ? lb : (s == 2 ? ob : vb);
+                const int s = i < b3 ? 0 : (i < b4 ? 1 : (i < b5 ? 2 : (i < b6 ? 3 : (i < b7 ? 4 : 5))));
+                const int j = i - (s == 1 ? b3 : (s == 2 ? b4 : (s == 3 ? b5 : b6)));
+                // row segments by row and line; contiguous segments (K, S0, dS1, gate,
+                // beta) by line
+                const char* base = s == 1 ? lb : (s == 2 ? ub : (s == 3 ? ob : vb));
                 long off = (long)(j / LPR) * D * E + (j % LPR) * 128;
+                if (!US && s == 2) off = (long)j * 128;
                 if (s == 0) {
-                    base = i < b1 ? kb : (i < b2 ? tb : (i < b3 ? sb : db));
-                    off = (long)(i - (i < b1 ? 0 : (i < b2 ? b1 : (i < b3 ? b2 : b3)))) * 128;
+                    base = i < b1 ? kb : (i < b2 ? sb : db);
+                    off = (long)(i - (i < b1 ? 0 : (i < b2 ? b1 : b2))) * 128;
                 }
-                if (s == 4) {
+                if (s == 5) {
                     base = i < b8 ? gb : bb;
                     off = (long)(i - (i < b8 ? b7 : b8)) * 128;
                 }
@@ -943,7 +992,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 float sb = 0.f, sg = 0.f;
 #pragma unroll
                 for (int im = 0; im < TO::RM; ++im) {
-                    sb += dbA[im * TO::RN + in];
+                    sb += dbA[im * TO::RN + in] - xdot[im * TO::RN + in];
                     const f32x4 x = dgm[im * TO::RN + in];
                     sg += x[0] + x[1] + x[2] + x[3];
                 }
@@ -955,13 +1004,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 }
             }
         }
-        // dbeta_R row partials over v (X^T tiles: 4 v per lane, 4 lane groups)
-        if (TX::active()) {
+        // sum_v lambda V: the row partials of the block tiles' owners
 #pragma unroll
-            for (int j = 0; j < TX::PER; ++j) {
-                const float sr = sum_lane_groups(dbr_part[j]);
-                if (lane_id() < 16) red_b[(TX::m0(j) / 16) * C + TX::col(j)] = sr;
-            }
+        for (int x = 0; x < RV::PER; ++x) {
+            const int idx = threadIdx.x + x * kThreads;
+            if (idx < RV::NV) red_v[(idx % RV::VPR) * C + idx / RV::VPR] = lv[x];
         }
         // per-thread partials of sum_v S0 dS1 (gate terms only)
         if (GATE != kGateNone) {
@@ -978,7 +1025,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         __syncthreads();
         for (int t = threadIdx.x; t < valid; t += kThreads) {
             float s2 = 0.f;
-            for (int b = 0; b < VB / 16; ++b) s2 += red_b[b * C + t];
+            for (int b = 0; b < RV::VPR; ++b) s2 += red_v[b * C + t];
             for (int b = 0; b < TO::WM; ++b) s2 += red_r[b * C + t];
             if (kz) {
                 const float rn = t == (int)threadIdx.x ? krn_t : p.krn[row0 + t];

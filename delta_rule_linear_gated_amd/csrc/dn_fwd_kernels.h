@@ -566,7 +566,8 @@ template <int GATE, int C, int DK, int LDG = DK> struct GateLds {   // LDG: row 
 // independent: each row only mixes with itself through the key dimension).  The
 // global tiles of chunk n + 1 are loaded into registers while chunk n is
 // computed.
-//   SAVE    : write the state entering each chunk (I/O type) to p.states
+//   SAVE    : write the state entering each chunk (I/O type) to p.states (with
+//             OUTPUT also U = T R of each chunk to p.Um)
 //   OUTPUT  : write O and hT.  Off for the recompute pass of the backward (P is
 //             not needed there).
 //   neither : segment summary of the chunk-parallel scan (exact affine chunk
@@ -814,6 +815,11 @@ __device__ __forceinline__ void fwd_state_body(const Params& p, int wg, float* _
             }
         }
         __syncthreads();
+        // U of this chunk (all C rows: rows past the sequence are zero), beside the
+        // products that read it; saved by the forward proper only (the backward's
+        // recomputing pass leaves U to the chunk backward)
+        if (SAVE && OUTPUT)
+            lds_to_global<TI, C, BV>(static_cast<TI*>(p.Um) + ((long)bh * p.NT + n) * C * DVr + v0, DVr, Ub, LDV, C);
         // (e) O^T = S0 (Q Gam)^T (from (c)) + U^T P^T   (O into Rb, dead since (d); written back
         //     next iteration)
         if (OUTPUT) {

@@ -22,6 +22,10 @@ enum Gate { kGateNone = 0, kGateScalar = 1, kGateVector = 2 };
 //   gam   fp32 in-chunk cumulative log-decay, same layout as g
 //   Tm    [BH][NT][C][C]   (I + A)^{-1} of each chunk
 //   Pm    [BH][NT][C][C]   causal intra-chunk score matrix of each chunk
+//   Um    [BH][NT][C][DV]  U = T R of each chunk, the forward's matrix-core
+//                          operand (saved buffer only: written by a forward that
+//                          saves states; the chunk backward then reads it instead
+//                          of recomputing it)
 //   kb    [BH][T] fp32     Kaczmarz step beta_t = eta_t / (||k_t||^2 + eps)
 //   krn   [BH][T] fp32     1 / (||k_t||^2 + eps)   (both only with the flag)
 // workspace of the backward:
@@ -50,6 +54,7 @@ struct Params {
     float* gam;
     void* Tm;
     void* Pm;
+    void* Um;
     void* lam;
     void* dS1;
     float* kb;    // Kaczmarz flag: written by prep, read through `beta` afterwards
@@ -106,10 +111,10 @@ struct WsLayout {
 };
 WsLayout ws_layout(const Problem& pr, int pass);
 
-// The forward's saved buffer: chunk-entry states, T, P, gam, Kaczmarz data
+// The forward's saved buffer: chunk-entry states, T, P, U, gam, Kaczmarz data
 // (kb then krn) (same alignment).
 struct SavedLayout {
-    size_t states, Tm, Pm, gam, kz, total;
+    size_t states, Tm, Pm, Um, gam, kz, total;
 };
 SavedLayout saved_layout(const Problem& pr);
 

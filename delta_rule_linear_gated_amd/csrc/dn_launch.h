@@ -238,10 +238,17 @@ hipError_t bwd_impl(const Problem& pr, const Params& p, bool have_states, hipStr
             bwd_state<TI, GATE, C, D>(p, BH, 0, stream);
             prof_end(stream);
         }
+        // with saved states the forward also saved U; recomputed, U is formed again here
         Params pc = p;
-        pc.resident = device_cus() * resident_per_cu<bwd_chunk_kernel<TI, GATE, C, D>>();
         prof_begin(stream, "bwd_chunk");
-        hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D>), dim3(p.NT, BH), dim3(kThreads), 0, stream, pc);
+        if (have_states) {
+            pc.resident = device_cus() * resident_per_cu<bwd_chunk_kernel<TI, GATE, C, D, true>>();
+            hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D, true>), dim3(p.NT, BH), dim3(kThreads), 0, stream, pc);
+        } else {
+            pc.resident = device_cus() * resident_per_cu<bwd_chunk_kernel<TI, GATE, C, D, false>>();
+            hipLaunchKernelGGL((bwd_chunk_kernel<TI, GATE, C, D, false>), dim3(p.NT, BH), dim3(kThreads), 0, stream,
+                               pc);
+        }
         prof_end(stream);
         return hipGetLastError();
     }

@@ -228,7 +228,8 @@ SavedLayout saved_layout(const Problem& pr) {
     l.states = 0;
     l.Tm = z.st;
     l.Pm = l.Tm + z.cc;
-    l.gam = l.Pm + z.cc;
+    l.Um = l.Pm + z.cc;
+    l.gam = l.Um + z.lam;
     l.kz = l.gam + z.gam;
     l.total = l.kz + z.kz;
     return l;

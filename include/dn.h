@@ -56,6 +56,10 @@
  *                          io   [B][H][NT][dv][dk]  state entering each chunk
  *                          io   [B][H][NT][C][C]    (I + A)^{-1} of each chunk
  *                          io   [B][H][NT][C][C]    causal intra-chunk scores
+ *                          io   [B][H][NT][C][dv]   U = (I + A)^{-1} R of each chunk
+ *                                                   (R = diag(beta)(V - X), the
+ *                                                   chunk's residual; rows past T
+ *                                                   zero)
  *                          fp32 like g              in-chunk cumulative log-decay
  *                                                   (absent without a gate)
  *                          fp32 [2][B][H][T]        DN_FLAG_KACZMARZ only: beta_t,
@@ -150,9 +154,9 @@ typedef struct {
 size_t dn_states_bytes(const dn_shape* shape);
 
 /* Byte offsets of the regions of `states`: {chunk-entry states, (I + A)^{-1},
- * intra-chunk scores, cumulative log-decay, Kaczmarz step data, total}; an
+ * intra-chunk scores, U, cumulative log-decay, Kaczmarz step data, total}; an
  * absent region has zero size.  DN_OK or a shape error. */
-dn_status dn_states_layout(const dn_shape* shape, size_t offsets[6]);
+dn_status dn_states_layout(const dn_shape* shape, size_t offsets[7]);
 
 /* Workspace bytes the given pass needs (0 on bad shape).  Workspace contents
  * are scratch: nothing is carried from one call to the next. */

@@ -38,9 +38,9 @@ int main() {
                     for (int T : Ts)
                         for (unsigned flags = 0; flags <= 3; ++flags) {
                             const dn_shape s = shape(2, 3, T, d, C, dtype, gate, flags, 1e-6f);
-                            size_t so[6], wo[10];
+                            size_t so[7], wo[10];
                             const size_t sb = dn_states_bytes(&s);
-                            if (dn_states_layout(&s, so) == DN_OK) EXPECT(so[5] == sb);
+                            if (dn_states_layout(&s, so) == DN_OK) EXPECT(so[6] == sb);
                             for (int pass = 0; pass <= 2; ++pass) {
                                 const size_t wb = dn_workspace_bytes(&s, pass);
                                 if (dn_workspace_layout(&s, pass, wo) == DN_OK) EXPECT(wo[9] == wb);

@@ -42,10 +42,11 @@ def test_sizes_of_the_workloads(name):
     gw = 0 if w.gate == "none" else (w.dk if w.gate == "vector" else 1)
     al = lambda x: -(-x // 256) * 256
     sl = B.dn_states_layout(sh)
-    # saved buffer: chunk-entry states, T, P (io type), cumulative log-decay (fp32)
+    # saved buffer: chunk-entry states, T, P, U (io type), cumulative log-decay (fp32)
     assert sl["states"] == 0
     assert sl["T"] == al(w.B * w.H * NT * w.dv * w.dk * E)
-    assert sl["P"] - sl["T"] == sl["gam"] - sl["P"] == al(w.B * w.H * NT * w.C * w.C * E)
+    assert sl["P"] - sl["T"] == sl["U"] - sl["P"] == al(w.B * w.H * NT * w.C * w.C * E)
+    assert sl["gam"] - sl["U"] == al(w.B * w.H * NT * w.C * w.dv * E)
     assert sl["kz"] - sl["gam"] == al(w.B * w.H * w.T * gw * 4)
     # Kaczmarz step: beta and 1 / (||k||^2 + eps) per token (fp32)
     assert sl["total"] - sl["kz"] == (al(2 * w.B * w.H * w.T * 4) if w.kla else 0)
@@ -58,16 +59,18 @@ def test_sizes_of_the_workloads(name):
     assert lay["total"] == r
     offs = [lay[k] for k in ("gam", "T", "P", "lam", "dS1", "states", "kz", "seg_end", "seg_start", "total")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    # the recomputing backward holds in its workspace what the saved buffer carries
-    assert r - b == B.dn_states_bytes(sh)
+    # the recomputing backward holds in its workspace what the saved buffer carries,
+    # except U (the chunk backward forms it again there)
+    assert r - b == B.dn_states_bytes(sh) - (sl["gam"] - sl["U"])
     # with a saved buffer the backward's workspace holds only lambda and dS1 (and the
     # scan buffers, when the scan is used)
     lb = B.dn_workspace_layout(sh, B.DN_PASS_BWD)
     scan = lb["total"] - lb["seg_end"]
     assert scan == scan_bytes(w.B, w.H, w.T, w.dk, w.dv, w.C)
     assert lb["gam"] == lb["T"] == lb["P"] == lb["lam"] == 0 and lb["states"] == lb["kz"] == lb["seg_end"]
-    # the forward's workspace holds gam, T, P (used when it saves nothing)
-    assert f == sl["total"] - sl["T"] + scan
+    # the forward's workspace holds gam, T, P (used when it saves nothing; U is
+    # written only beside saved states)
+    assert f == sl["total"] - sl["T"] - (sl["gam"] - sl["U"]) + scan
 
 
 def expected_segments(B_, H, T, dv, C):
@@ -198,8 +201,10 @@ def test_validation_errors_kaczmarz():
 
 def test_workspace_grows_with_recompute():
     sh = sh_of(T=4096, dk=128, dv=128, C=64)
+    sl = B.dn_states_layout(sh)
+    # everything the saved buffer carries except U, which the recomputing chunk backward forms itself
     assert B.dn_workspace_bytes(sh, B.DN_PASS_BWD_RECOMPUTE) - B.dn_workspace_bytes(sh, B.DN_PASS_BWD) \
-        == B.dn_states_bytes(sh)
+        == B.dn_states_bytes(sh) - (sl["gam"] - sl["U"])
     assert B.dn_workspace_bytes(sh, 9) == 0
 
 

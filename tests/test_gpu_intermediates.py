@@ -1,5 +1,5 @@
 """Parity of the per-chunk intermediates the HIP path leaves in the forward's
-saved buffer (cumulative log-decay, (I + A)^{-1}, intra-chunk scores, chunk-entry
+saved buffer (cumulative log-decay, (I + A)^{-1}, intra-chunk scores, U, chunk-entry
 states) and in the backward's workspace (the triangular-residual adjoint lambda
 and the state cotangent per chunk) with the fp64 chunked evaluation of the
 oracle.  A mismatch here names the stage that
@@ -64,14 +64,16 @@ def test_workspace_intermediates(case):
         # T and P as the forward saved them (row-major), lambda and dS1 from the backward's workspace
         Tm = sv["T"][0, h].cpu().to(torch.float64).numpy()
         Pm = sv["P"][0, h].cpu().to(torch.float64).numpy()
+        Um = sv["U"][0, h].cpu().to(torch.float64).numpy()
         lam = region(lay["lam"], 2 * NT * C * d, et).reshape(2, NT, C, d)[h]
         dS1 = region(lay["dS1"], 2 * NT * d * d, et).reshape(2, NT, d, d)[h]
         st = sv["states"][0, h].cpu().to(torch.float64).numpy()
         for n in range(NT):
             L = tr[n]["T"].shape[0]
             errs = dict(T=rel_err(Tm[n, :L, :L], tr[n]["T"]), P=rel_err(Pm[n, :L, :L], tr[n]["Pm"]),
-                        S0=rel_err(st[n], st_ref[n]), lam=rel_err(lam[n, :L], trb["lam"][n]),
+                        U=rel_err(Um[n, :L], tr[n]["U"]), S0=rel_err(st[n], st_ref[n]), lam=rel_err(lam[n, :L], trb["lam"][n]),
                         dS1=rel_err(dS1[n], trb["dS1"][n]))
             say(f"  head {h} chunk {n}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
             bad = {k: v for k, v in errs.items() if not v <= tol}
             assert not bad, (h, n, bad)
+            assert not Um[n, L:].any(), (h, n, "U rows past the sequence")
