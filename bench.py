@@ -98,12 +98,14 @@ def kernel_budget(name: str, C: int, d: int, E: int, gw: int, saved: bool, kz: b
         fl = 2 * (3 * C * d * d + C * C * d)
         by = (3 if name == "fwd_state" else 2) * C * d * E + 2 * C * C * E + sc
         by += (C * d * E if name == "fwd_state" else 0) + (d * d * E if (saved or name != "fwd_state") else 0)
+        by += C * d * E if (saved and name == "fwd_state") else 0   # U beside the saved states
     elif name == "bwd_state":
         fl = 2 * (3 * C * d * d + C * C * d)
         by = 3 * C * d * E + 2 * C * C * E + sc + d * d * E + 2 * C * d * E
     elif name == "bwd_chunk":
-        fl = 2 * (4 * C * d * d + 3.5 * C * C * d)
-        by = 4 * C * d * E + 2 * d * d * E + C * d * E + C * C * E + sc + 2 * C * d * E + sc
+        # with saved states U is read (not X, R, U = T R formed again, which needs T)
+        fl = 2 * (3 * C * d * d + 2.5 * C * C * d) if saved else 2 * (4 * C * d * d + 3.5 * C * C * d)
+        by = 4 * C * d * E + 2 * d * d * E + C * d * E + (C * d * E if saved else C * C * E) + sc + 2 * C * d * E + sc
         by += C * 4 if kz else 0
     elif name in ("fwd_summary", "fwd_summary_recompute"):
         # scan segment summaries: the state recurrence (no output) over d_v + d_k rows
