@@ -632,6 +632,25 @@ def phase_cpu_baseline(w, inp_cpu):
             "sample": f"{nh} heads of sequence 0, steps 0..{Ts - 1}, fwd+bwd, fp64 numpy ({dt:.1f} s wall)"}
 
 
+def host_info() -> dict:
+    """The host the CPU baseline ran on: CPU model and the logical CPUs this
+    process may use (the oracle's thread count is capped at 16 beside it)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(w, inp_cpu):
     """The fp64 oracle (sequential recurrence + reverse mode, C, threads over
     heads) on the same workload, timed on the host.  Sample: every head of the
@@ -668,7 +687,8 @@ def cpu_baseline(w, inp_cpu):
             "sample": f"{nheads} of {nheads_all} heads, full length T={w.T}, fwd+bwd, fp64 "
                       f"({dt:.1f} s wall)",
             "single_thread": {"value": round(w.T / w.H / dt1, 1), "unit": "tokens/s", "cores": 1,
-                              "sample": f"1 head, full length T={w.T}, fwd+bwd, fp64 ({dt1:.1f} s wall)"}}
+                              "sample": f"1 head, full length T={w.T}, fwd+bwd, fp64 ({dt1:.1f} s wall)"},
+            "host": host_info()}
 
 
 if __name__ == "__main__":
