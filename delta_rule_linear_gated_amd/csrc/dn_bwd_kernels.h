@@ -851,10 +851,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         // Warm the caches for the workgroup that most likely starts next on this
         // XCD: workgroups start in id order and go to the XCDs round-robin, so it
         // is this id plus the number resident at once.  One dword of every
-        // 128-byte line of its prologue tiles (K, the first two d_v blocks of S0,
-        // dS1, lambda, U (or T without US), dO and V, the gate and beta rows; up
-        // to 2 lines per thread), held in registers and consumed only at the end,
-        // so nothing waits for them.
+        // 128-byte line of its prologue tiles (K, the first 64 rows of S0 and dS1
+        // and columns of lambda, U (or T without US), dO and V -- the first two
+        // 32-wide d_v blocks or one 64-wide --, the gate and beta rows; up to 2
+        // lines per thread), held in registers and consumed only at the end, so
+        // nothing waits for them.
         int warm[2];
         {
             const long ids = (long)gridDim.x * gridDim.y;
