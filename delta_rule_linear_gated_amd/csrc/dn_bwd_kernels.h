@@ -613,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         r.V.load(v + v0, D, valid);
     };
     load_block(rb[0], 0);
-    if (NVB > 1) load_block(rb[1], 1);
+    if (NVB > 2) load_block(rb[1], 1);
     // sum_v S0[v][c] dS1[v][c] over this thread's rows of every block
     float ls[L::RS::PER][L::RS::VW] = {};
     rg.commit(rowf, gam_s, beta_s, L::LDGM);
@@ -665,6 +665,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     };
     commit_block(rb[0], 0);
     __syncthreads();
+    // with two (64-wide) blocks, block 1's loads only now: they arrive during block
+    // 0's products, where issued in the prologue they held its barriers back (with
+    // four blocks the prologue's are half the bytes and block 1 is best loaded
+    // there); then block 2's into the set just committed
+    if (NVB == 2) load_block(rb[1], 1);
     if (NVB > 2) load_block(rb[0], 2);
 
     // ---------------- d_v loop
