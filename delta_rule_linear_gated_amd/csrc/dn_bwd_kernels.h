@@ -233,14 +233,18 @@ __device__ __forceinline__ void bwd_state_body(const Params& p, int wg, float* _
         if (!SUMMARY)
             lds_to_global<TI, BV, DK>(static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, dSs,
                                       LDK, BV);
-        // the next chunk's loads last and unconditional (see the forward state kernel)
-        prefetch(n > n0 ? n - 1 : n0);
+        // the next chunk's loads after the dS1 save and unconditional (see the
+        // forward state kernel); with the per-channel gate only once the first
+        // product below is issued (its reverse pass 2 % faster, the scalar gate's
+        // 3.5 % slower)
+        if (!VEC) prefetch(n > n0 ? n - 1 : n0);
 
         // (c) dU = P^T dO + Kd dS1^T  -> dU^T   (P and dO read as [k][m] / [k][n])
         {
             f32x4 dU[TX::PER];
             zero_acc<C, BV>(dU);
             gemm<TI, C, BV, DK, false, false>(dU, Kd, LDK, dSs, LDK);
+            if (VEC) prefetch(n > n0 ? n - 1 : n0);
             if (SCA && TX::active()) {   // rows t of K dS1^T times e^{gam_C - gam_t}
 #pragma unroll
                 for (int j = 0; j < TX::PER; ++j) dU[j] *= ld4<float>(rowf + C + TX::row(j, 0));
