@@ -767,14 +767,18 @@ __device__ __forceinline__ void fwd_state_body(const Params& p, int wg, float* _
         if (OUTPUT && n > n0)
             lds_to_global<TI, C, BV>(static_cast<TI*>(p.o) + (row0 - C) * DVr + v0, DVr, Rb, LDV, C);
         __syncthreads();
-        if (SAVE)
+        // the state entering the chunk (Ss is not written again before the next
+        // chunk); the per-channel gate's after (d) instead, beside U (its forward
+        // pass 1 % faster, the scalar gate's 1 % slower)
+        if (SAVE && !VEC)
             lds_to_global<TI, BV, DK>(static_cast<TI*>(p.states) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, Ss,
                                       LDK, BV);
-        // The next chunk's loads come after every global store of the iteration and
+        // The next chunk's loads come after the stores issued so far and
         // unconditionally (the last chunk reloads itself): the wait counts at the loop
         // head are merged over the first entry (the loads alone) and the back edge,
-        // and only with the loads last on both do they stay exact instead of waiting
-        // for every outstanding load and store.
+        // and with the loads behind the stores there they stay close to exact instead
+        // of waiting for every outstanding load and store (the saves of U, and with
+        // the per-channel gate of the state, come later in the chunk: measured).
         prefetch(n + 1 < n1 ? n + 1 : n);
 
         // (c) X^T = S0 (K Gam)^T ;  R = diag(beta) (V - X); with the output, the
@@ -820,6 +824,9 @@ __device__ __forceinline__ void fwd_state_body(const Params& p, int wg, float* _
         // recomputing pass leaves U to the chunk backward)
         if (SAVE && OUTPUT)
             lds_to_global<TI, C, BV>(static_cast<TI*>(p.Um) + ((long)bh * p.NT + n) * C * DVr + v0, DVr, Ub, LDV, C);
+        if (SAVE && VEC)
+            lds_to_global<TI, BV, DK>(static_cast<TI*>(p.states) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, Ss,
+                                      LDK, BV);
         // (e) O^T = S0 (Q Gam)^T (from (c)) + U^T P^T   (O into Rb, dead since (d); written back
         //     next iteration)
         if (OUTPUT) {
