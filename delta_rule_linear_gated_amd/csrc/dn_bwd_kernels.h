@@ -230,7 +230,7 @@ __device__ __forceinline__ void bwd_state_body(const Params& p, int wg, float* _
             lds_to_global<TI, C, BV>(static_cast<TI*>(p.dv) + rp * DVr + v0, DVr, Db, LDV, min(C, p.T - (n + 1) * C));
         }
         __syncthreads();
-        if (!SUMMARY)
+        if (!SUMMARY && !VEC)
             lds_to_global<TI, BV, DK>(static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, dSs,
                                       LDK, BV);
         // the next chunk's loads after the dS1 save and unconditional (see the
@@ -267,6 +267,11 @@ __device__ __forceinline__ void bwd_state_body(const Params& p, int wg, float* _
         }
         gemm<TI, DK, BV, C, true, true>(dS, Qg, LDK, SCA ? dOg : dOb, LDV);
         __syncthreads();
+        // the per-channel gate saves dS1 here (dSs is next written at the next
+        // chunk's start)
+        if (!SUMMARY && VEC)
+            lds_to_global<TI, BV, DK>(static_cast<TI*>(p.dS1) + (((long)bh * p.NT + n) * DVr + v0) * DK, DK, dSs,
+                                      LDK, BV);
         // (d) lambda^T = dU^T T ; dv = beta lambda.  lambda^T tiles give a lane 4
         //     consecutive v of one row t of lambda and dv
         {
@@ -365,13 +370,10 @@ template <typename TI, int GATE, int C, int D, bool US>
 struct BwdChunkSmem {
     static constexpr int PAD = Pad<TI>::value;
     // d_v block: 32 (16 for fp32 at D = 128, whose tiles are twice the bytes), or 64
-    // where the saved U leaves room for it in LDS (WIDE: bf16, no per-channel gate
-    // tile, D = 128, C = 64).  The recomputing variant of such a shape keeps 32, and
-    // sums over v in the 64-wide order instead (PAIRED: two accumulators, one for
-    // the even and one for the odd 32-wide blocks), so that both policies give
-    // bitwise the same dbeta and dg
-    static constexpr bool WIDE_SHAPE = GATE != kGateVector && sizeof(TI) == 2 && D == 128 && C == 64;
-    static constexpr bool WIDE = US && WIDE_SHAPE, PAIRED = !US && WIDE_SHAPE;
+    // where LDS has room for two such blocks (WIDE: bf16, no per-channel gate tile,
+    // D = 128, C = 64; without US only with R formed in place over V, no R buffer)
+    static constexpr bool WIDE = GATE != kGateVector && sizeof(TI) == 2 && D == 128 && C == 64;
+    static constexpr bool RINPLACE = !US && WIDE;
     static constexpr int VB = WIDE ? 64 : (D >= 32 ? (sizeof(TI) == 4 && D > 64 ? 16 : 32) : D);
     static constexpr int NVB = D / VB;
     static constexpr int LD = D + PAD;            // rows of D elements
@@ -393,8 +395,8 @@ struct BwdChunkSmem {
     static constexpr size_t DOB = LAMB + al(C * LVB * E);            // dO block       [C][LVB]
     static constexpr size_t UBL = DOB + al(C * LVB * E);             // U block (without US: V, then U) [C][LVB]
     static constexpr size_t BLK = UBL + al(C * LVB * E);
-    static constexpr size_t RB = LOOP + 2 * BLK;                     // R block (without US) [C][LVB]
-    static constexpr size_t LOOP_END = RB + (US ? 0 : al(C * LVB * E));
+    static constexpr size_t RB = LOOP + 2 * BLK;                     // R block (without US, 32 wide) [C][LVB]
+    static constexpr size_t LOOP_END = RB + (US || RINPLACE ? 0 : al(C * LVB * E));
     // phase C (over the d_v-loop tiles)
     static constexpr size_t DA = LOOP;                               // dA~            [C][LC]
     static constexpr size_t DAB = DA + al(C * LC * E);               // beta_t dA~     [C][LC]
@@ -413,22 +415,18 @@ struct BwdChunkSmem {
     static constexpr size_t RED_R = BETA + al(C * 4);                             // [D/16][C] row partials (dbeta_A)
     static constexpr size_t RED_G = RED_R + al((D / 16) * C * 4);                 // [D/16][C] row partials (d gam)
     using RV = RegN<TI, C, VB>;   // register tiles of the lambda / dO / U / V blocks
-    static constexpr int VPRC = PAIRED ? 2 * RV::VPR : RV::VPR;                    // lambda . V partials per row
-    static constexpr size_t RED_V = RED_G + al((D / 16) * C * 4);                 // [VPRC][C] row partials (lambda . V)
-    static constexpr size_t RED_C = RED_V + al(VPRC * C * 4);                     // [C/16][D] column partials
+    static constexpr size_t RED_V = RED_G + al((D / 16) * C * 4);                 // [RV::VPR][C] row partials (lambda . V)
+    static constexpr size_t RED_C = RED_V + al(RV::VPR * C * 4);                  // [C/16][D] column partials
     static constexpr size_t LASTS = RED_C + al((C / 16) * D * 4);                 // [D]
     static constexpr size_t KCO = LASTS + al(D * 4);                              // [C] Kaczmarz dk coefficients
     static constexpr size_t DIAGP = KCO + al(C * 4);                              // [C] diagonal of dP (vector gate)
     static constexpr size_t TOTAL = DIAGP + al(VEC ? C * 4 : 0);
     // dq / dk write-back tiles [C][LD] each at offset 0; after them the per-thread
-    // partials of sum_v S0 dS1 [LSBR row blocks of the S0 register tile][LDS_] fp32
+    // partials of sum_v S0 dS1 [row blocks of the S0 register tile][LDS_] fp32
     using RS = RegB<TI, VB, D>;
-    static constexpr int LSBR = PAIRED ? 2 * RS::BR : RS::BR;
-    static_assert(!WIDE_SHAPE || (RS::BRW == 2 && RS::PER == 1 && RV::PER == 1 && RV::VPR == VB / 8),
-                  "64-wide and paired block layouts");
     static constexpr int LDS_ = D + 4;   // rows of the partials (padded: eight lanes store to eight rows)
     static constexpr size_t LSRED = al(2 * C * LD * E);
-    static_assert(LSRED + LSBR * LDS_ * 4 <= BIG_END, "S0 dS1 partials");
+    static_assert(LSRED + RS::BR * LDS_ * 4 <= BIG_END, "S0 dS1 partials");
     static_assert(2 * C * LD * E <= BIG_END, "write-back tiles");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -629,15 +627,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         rK.store(KG, LD);   // scalar: Gam_t is applied on the C x D results
     if (!US) rT.store(TLs, LC);
     // sum_v lambda V over this thread's vectors of the block tiles (rows past the
-    // sequence excluded: V is loaded clamped there); PAIRED: the odd blocks' part in
-    // lv2 (and the S0 dS1 sums in ls2), as 64-wide blocks hold those rows
-    float lv[RV::PER] = {}, lv2[L::PAIRED ? RV::PER : 1] = {};
-    float ls2[L::PAIRED ? L::RS::PER : 1][L::RS::VW] = {};
+    // sequence excluded: V is loaded clamped there)
+    float lv[RV::PER] = {};
     auto commit_block = [&](BlockRegs& r, int i) {
-        if (L::PAIRED && i == 1)
-            r.S0.dot_rows(r.dS1, ls2);
-        else
-            r.S0.dot_rows(r.dS1, ls);
+        r.S0.dot_rows(r.dS1, ls);
 #pragma unroll
         for (int x = 0; x < RV::PER; ++x) {
             const uint4 la = pin(r.lam.r[x]), va = pin(r.V.r[x]);
@@ -646,21 +639,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             float s2 = 0.f;
 #pragma unroll
             for (int e = 0; e < RV::VW; ++e) s2 += to_f(le[e]) * to_f(ve[e]);
-            s2 = RV::idx_of(x) / RV::VPR < valid ? s2 : 0.f;
-            if (L::PAIRED && i == 1)
-                lv2[x] += s2;
-            else
-                lv[x] += s2;
+            lv[x] += RV::idx_of(x) / RV::VPR < valid ? s2 : 0.f;
         }
         // the sums are formed here: left to their use at the finish, the compiler
         // sinks the products there and keeps both register tiles alive until then
 #pragma unroll
         for (int x = 0; x < L::RS::PER; ++x)
 #pragma unroll
-            for (int y = 0; y < L::RS::VW; ++y) {
-                asm volatile("" : "+v"(ls[x][y]));
-                if (L::PAIRED) asm volatile("" : "+v"(ls2[x][y]));
-            }
+            for (int y = 0; y < L::RS::VW; ++y) asm volatile("" : "+v"(ls[x][y]));
         r.S0.store_n(blk(i, L::S0B), LD, Identity());
         r.dS1.store_n(blk(i, L::DS1B), LD, Identity());
         r.lam.store(blk(i, L::LAMB), LVB);
@@ -738,7 +724,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                     rr[j] = beta_s[t] * (ld4<TI>(UB + t * LVB + c) - (SCA ? rowf[t] : 1.f) * X[j]);
                 }
 #pragma unroll
-                for (int j = 0; j < TX::PER; ++j) st4<TI>(RB + TX::col(j) * LVB + TX::row(j, 0), rr[j]);
+                for (int j = 0; j < TX::PER; ++j)
+                    st4<TI>((L::RINPLACE ? UB : RB) + TX::col(j) * LVB + TX::row(j, 0), rr[j]);
             }
             __syncthreads();
             // block b + 1 into the other buffer (free since block b - 1 ended), read after
@@ -751,7 +738,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             {
                 f32x4 U[TX::PER];
                 zero_acc<VB, C>(U);
-                gemm<TI, VB, C, C, true, false>(U, RB, LVB, TLs, LC);
+                gemm<TI, VB, C, C, true, false>(U, L::RINPLACE ? UB : RB, LVB, TLs, LC);
+                if (L::RINPLACE) __syncthreads();   // every wave has read R before U overwrites it
                 if (TX::active()) {
 #pragma unroll
                     for (int j = 0; j < TX::PER; ++j) st4<TI>(UB + TX::col(j) * LVB + TX::row(j, 0), U[j]);
@@ -761,7 +749,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             gemm<TI, D, C, VB, true, false>(dkm, DS1B, LD, UB, LVB);
             gemm2<TI, C, C, VB, false, false>(dA, dP, UB, LVB, LAMB, DOB, LVB);
             // no barrier here: the next writes into this buffer (the commit of block
-            // b + 2) and into RB come after the next block's first barrier
+            // b + 2) and into RB come after the next block's first barrier (with R in
+            // place, block b + 1's R goes to the other buffer)
         }
     }
 
@@ -1041,10 +1030,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
 #pragma unroll
         for (int x = 0; x < RV::PER; ++x) {
             const int idx = threadIdx.x + x * kThreads;
-            if (idx < RV::NV) {
-                red_v[(idx % RV::VPR) * C + idx / RV::VPR] = lv[x];
-                if (L::PAIRED) red_v[(RV::VPR + idx % RV::VPR) * C + idx / RV::VPR] = lv2[x];
-            }
+            if (idx < RV::NV) red_v[(idx % RV::VPR) * C + idx / RV::VPR] = lv[x];
         }
         // per-thread partials of sum_v S0 dS1 (gate terms only)
         if (GATE != kGateNone) {
@@ -1052,20 +1038,16 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
             for (int i = 0; i < L::RS::PER; ++i) {
                 if (L::RS::owns(i)) {
 #pragma unroll
-                    for (int kk = 0; kk < L::RS::VW; kk += 4) {
+                    for (int kk = 0; kk < L::RS::VW; kk += 4)
                         st4<float>(lsred + L::RS::rowblk(i) * L::LDS_ + L::RS::col0(i) + kk,
                                    f32x4{ls[i][kk], ls[i][kk + 1], ls[i][kk + 2], ls[i][kk + 3]});
-                        if (L::PAIRED)
-                            st4<float>(lsred + (L::RS::BR + L::RS::rowblk(i)) * L::LDS_ + L::RS::col0(i) + kk,
-                                       f32x4{ls2[i][kk], ls2[i][kk + 1], ls2[i][kk + 2], ls2[i][kk + 3]});
-                    }
                 }
             }
         }
         __syncthreads();
         for (int t = threadIdx.x; t < valid; t += kThreads) {
             float s2 = 0.f;
-            for (int b = 0; b < L::VPRC; ++b) s2 += red_v[b * C + t];
+            for (int b = 0; b < RV::VPR; ++b) s2 += red_v[b * C + t];
             for (int b = 0; b < TO::WM; ++b) s2 += red_r[b * C + t];
             if (kz) {
                 const float rn = t == (int)threadIdx.x ? krn_t : p.krn[row0 + t];
@@ -1095,7 +1077,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                     const int c = threadIdx.x;
                     if (c < D) {
                         float ssum = 0.f;
-                        for (int h = 0; h < L::LSBR; ++h) ssum += lsred[h * L::LDS_ + c];
+                        for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * L::LDS_ + c];
                         float cs = 0.f;
                         for (int b = 0; b < TO::WN; ++b) cs += red_c[b * D + c];
                         lastS[c] = fexp(gl[c]) * ssum + cs;   // the whole last-row term of channel c
@@ -1156,7 +1138,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
                 float xc = 0.f;
                 for (int c = lane_id(); c < D; c += 64) {
                     float ssum = 0.f;
-                    for (int h = 0; h < L::LSBR; ++h) ssum += lsred[h * L::LDS_ + c];
+                    for (int h = 0; h < L::RS::BR; ++h) ssum += lsred[h * L::LDS_ + c];
                     float cs = 0.f;
                     for (int b = 0; b < TO::WN; ++b) cs += red_c[b * D + c];
                     xc += gf.GC(c) * ssum + cs;
