@@ -615,11 +615,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         r.V.load(v + v0, D, valid);
     };
     load_block(rb[0], 0);
-    if (NVB > 2) load_block(rb[1], 1);
     // sum_v S0[v][c] dS1[v][c] over this thread's rows of every block
     float ls[L::RS::PER][L::RS::VW] = {};
     rg.commit(rowf, gam_s, beta_s, L::LDGM);
     __syncthreads();
+    if (NVB > 2) load_block(rb[1], 1);   // after the gate's barrier: it waits for fewer loads
     const GateLds<GATE, C, D, L::LDGM> gf{rowf, gam_s, valid - 1};
     if (VEC)
         rK.store(KG, LD, [&](int r, int c, float x) { return x * gf.G(r, c); });
