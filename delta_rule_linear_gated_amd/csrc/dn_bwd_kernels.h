@@ -594,8 +594,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     const float krn_t = (p.kz ? p.krn + row0 : p.beta + row0)[min((int)threadIdx.x, valid - 1)];
     GateRegs<GATE, C, D> rg;
     rg.load(p.gam + row0 * GW, p.beta + row0, valid);
+    // K: with two (64-wide) blocks loaded after the gate's barrier and staged after
+    // block 0's commit, so that barrier waits for fewer loads
+    constexpr bool KLATE = NVB == 2 && !VEC;
     RegN<TI, C, D> rK;
-    rK.load(k, D, valid);
+    if (!KLATE) rK.load(k, D, valid);
     RegN<TI, C, C> rT;
     if (!US) rT.load(static_cast<const TI*>(p.Tm) + chunk * C * C, C, C);
     // two register sets: the loads of block b + 2 are issued when block b is
@@ -620,10 +623,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
     rg.commit(rowf, gam_s, beta_s, L::LDGM);
     __syncthreads();
     if (NVB > 2) load_block(rb[1], 1);   // after the gate's barrier: it waits for fewer loads
+    if (KLATE) rK.load(k, D, valid);
     const GateLds<GATE, C, D, L::LDGM> gf{rowf, gam_s, valid - 1};
     if (VEC)
         rK.store(KG, LD, [&](int r, int c, float x) { return x * gf.G(r, c); });
-    else
+    else if (!KLATE)
         rK.store(KG, LD);   // scalar: Gam_t is applied on the C x D results
     if (!US) rT.store(TLs, LC);
     // sum_v lambda V over this thread's vectors of the block tiles (rows past the
@@ -654,6 +658,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(Params p) {
         (US ? r.U : r.V).store(blk(i, L::UBL), LVB);
     };
     commit_block(rb[0], 0);
+    if (KLATE) rK.store(KG, LD);
     __syncthreads();
     // with two (64-wide) blocks, block 1's loads only now: they arrive during block
     // 0's products, where issued in the prologue they held its barriers back (with
